@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle to values and facts it does not compute itself.
+
+Each test checks the oracle against something fixed outside it: numbers the
+pages print (tests/golden/), closed forms, invariants of the forward pass that
+follow from the pages' description, library routines for special cases, or a
+brute-force NumPy implementation built the way the pages describe candle's
+non-fused attention branch.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.np_reference import NumpyLlama, build_causal_mask, repeat_kv
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+# ---------------------------------------------------------------- sizes / layout
+
+def test_model_bytes_match_printed_file(golden_printed):
+    """Tensor bytes of the 135M shape = file size - data offset (Q8_0 = 34 B per 32)."""
+    g = golden_printed
+    s = synth.SMOL135M
+    specs = s.tensor_specs()
+    assert len(specs) == g["gguf_tensor_count"] == 30 * 9 + 2
+    assert s.total_bytes() == g["gguf_file_bytes"] - g["gguf_data_offset"]
+    q8 = sum(s.tensor_nbytes(d, r, c) for _, d, r, c in specs if d == "q8_0")
+    assert round(q8 / 2**20, 1) == g["q8_0_weight_mib"]
+    params = sum(r * c for _, _, r, c in specs)
+    assert int(params * 4 / 2**20) == g["f32_weight_mib"]
+    assert "output.weight" not in {n for n, *_ in specs}
+
+
+def test_generator_draws_the_stated_distributions():
+    m = synth.random_model(synth.micro_shape(n_vocab=512, n_embd=256), 0, keep_parts=True)
+    t = m["token_embd.weight"]
+    assert t.q.min() >= -127 and t.q.max() <= 127
+    s = t.scales.astype(np.float64)
+    assert (s >= 0).all()
+    assert 0.25 < (s < 2.0**-14).mean() < 0.35     # f16 subnormal share
+    w = m["blk.0.attn_norm.weight"].data
+    assert w.dtype == np.float32 and abs(w.mean() - 1.0) < 0.05
+
+
+def test_f16_decode_matches_library_for_every_bit_pattern():
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_f64(int(b)) for b in bits])
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    assert np.isnan(got[np.isnan(ref)]).all()
+    assert oracle.f16_to_f64(0x0001) == 2.0**-24
+    assert oracle.f16_to_f64(0x7BFF) == 65504.0
+
+
+def test_dequant_hand_block():
+    blk = np.zeros(34, dtype=np.uint8)
+    blk[0:2] = [0x00, 0x3C]                                   # f16 1.0
+    blk[2:] = np.arange(-16, 16, dtype=np.int8).view(np.uint8)
+    assert np.array_equal(oracle.dequant_q8_0(blk, 1, 32)[0], np.arange(-16, 16))
+    blk[0:2] = [0x01, 0x00]                                   # smallest subnormal
+    blk[2:] = 127
+    assert np.all(oracle.dequant_q8_0(blk, 1, 32)[0] == 127 * 2.0**-24)
+    blk[0:2] = 0                                              # d = 0
+    assert np.all(oracle.dequant_q8_0(blk, 1, 32)[0] == 0)
+
+
+def test_dequant_agrees_with_drawn_parts():
+    rng = np.random.default_rng(5)
+    scales, q = synth.draw_q8_0(rng, 7, 96)
+    raw = synth.pack_q8_0(scales, q)
+    ref = np.repeat(scales.astype(np.float64), 32, axis=1) * q
+    assert np.array_equal(oracle.dequant_q8_0(raw, 7, 96), ref)
+
+
+# ---------------------------------------------------------------- GEMV
+
+def test_matmul_single_nonzero_block():
+    rows, cols = 5, 128
+    raw = np.zeros((rows, cols // 32 * 34), dtype=np.uint8)
+    r, b = 3, 2
+    raw[r, b * 34:b * 34 + 2] = [0x00, 0x38]                  # f16 0.5
+    qv = np.arange(1, 33, dtype=np.int8)
+    raw[r, b * 34 + 2:b * 34 + 34] = qv.view(np.uint8)
+    x = np.linspace(-1, 1, cols)
+    y = oracle.matmul_q8(raw, rows, cols, x)[0]
+    expect = np.zeros(rows)
+    expect[r] = 0.5 * np.dot(qv.astype(np.float64), x[32 * b:32 * b + 32])
+    assert np.allclose(y, expect, rtol=1e-15, atol=0)
+    assert np.count_nonzero(y) == 1
+
+
+def test_matmul_matches_library_matmul():
+    rng = np.random.default_rng(11)
+    scales, q = synth.draw_q8_0(rng, 33, 192)
+    raw = synth.pack_q8_0(scales, q)
+    X = rng.standard_normal((4, 192))
+    W = np.repeat(scales.astype(np.float64), 32, axis=1) * q
+    got = oracle.matmul_q8(raw, 33, 192, X)
+    assert np.allclose(got, X @ W.T, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------- norm / rope / silu / attention
+
+def test_rmsnorm_constant_input_closed_form():
+    H, eps, c = 64, 1e-5, 0.37
+    w = np.random.default_rng(2).normal(1, 0.1, H).astype(np.float32)
+    y = oracle.rmsnorm(np.full(H, c), w, eps)
+    assert np.allclose(y, c / math.sqrt(c * c + eps) * w.astype(np.float64), rtol=1e-14)
+
+
+def test_rope_pairs_adjacent_dims_and_rotates_counterclockwise():
+    hd, theta = 64, 10000.0
+    for p in (0, 1, 7, 100):
+        e0 = np.zeros(hd); e0[0] = 1.0
+        r = oracle.rope_i(e0, p, theta)
+        assert r[0] == pytest.approx(math.cos(p), abs=1e-15)
+        assert r[1] == pytest.approx(math.sin(p), abs=1e-15)
+        assert np.all(r[2:] == 0)
+        e2 = np.zeros(hd); e2[2] = 1.0                       # pair j = 1
+        r = oracle.rope_i(e2, p, theta)
+        ang = float(np.float32(p) * np.float32(theta ** (-2.0 / hd)))
+        assert r[2] == pytest.approx(math.cos(ang), abs=1e-15)
+        assert r[3] == pytest.approx(math.sin(ang), abs=1e-15)
+        assert np.count_nonzero(r) <= 2
+
+
+def test_rope_angle_table_first_column_is_the_position():
+    for p in (0, 1, 33, 4095):
+        assert oracle.rope_angle(p, 0, 64, 10000.0) == float(p)
+
+
+def test_rope_identity_at_zero_and_norm_preserving():
+    v = np.random.default_rng(3).standard_normal(64)
+    assert np.array_equal(oracle.rope_i(v, 0, 1e4), v)
+    r = oracle.rope_i(v, 1234, 1e4)
+    assert np.allclose(np.hypot(r[0::2], r[1::2]), np.hypot(v[0::2], v[1::2]), rtol=1e-14)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(4)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    base = oracle.rope_i(q, 9, 1e4) @ oracle.rope_i(k, 4, 1e4)
+    for shift in (1, 3, 20):
+        s = oracle.rope_i(q, 9 + shift, 1e4) @ oracle.rope_i(k, 4 + shift, 1e4)
+        assert s == pytest.approx(base, rel=1e-5)
+
+
+def test_silu_identities():
+    assert oracle.silu(0.0) == 0.0
+    for z in (-3.0, -0.5, 0.25, 2.0):
+        assert oracle.silu(z) - oracle.silu(-z) == pytest.approx(z, rel=1e-14)
+    assert oracle.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(6)
+    hd = 16
+    K, V = rng.standard_normal((5, hd)), rng.standard_normal((5, hd))
+    q = rng.standard_normal(hd)
+    assert np.allclose(oracle.attend(q, K[:1], V[:1]), V[0], rtol=1e-15)       # one key: o = v
+    assert np.allclose(oracle.attend(np.zeros(hd), K, V), V.mean(axis=0), rtol=1e-14)
+    assert np.allclose(oracle.attend(q, K, V, last_visible=0), V[0], rtol=1e-15)
+    perm = rng.permutation(5)
+    assert np.allclose(oracle.attend(q, K[perm], V[perm]), oracle.attend(q, K, V), rtol=1e-13)
+
+
+def test_attention_two_keys_hand_values():
+    hd = 4
+    q = np.array([1.0, 0, 0, 0])
+    K = np.array([[2.0, 0, 0, 0], [0, 0, 0, 0]])            # scores 2/sqrt(4) = 1 and 0
+    V = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0]])
+    w0 = math.e / (math.e + 1.0)
+    assert np.allclose(oracle.attend(q, K, V), [w0, 1 - w0, 0, 0], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- NumPy brute-force reference pins
+
+def test_np_reference_mask_and_repeat_kv_match_printed_shapes(golden_printed):
+    g = golden_printed
+    m = build_causal_mask(5, 5)
+    assert m.shape == g["misuse_mask_shape"]
+    m = build_causal_mask(13, 33)
+    assert m.shape == g["clear_mask_shape"]
+    assert m[:, :33].sum() == 0 and np.array_equal(m[:, 33:], np.triu(np.ones((13, 13), np.uint8), 1))
+    x = np.arange(3 * 2 * 1).reshape(3, 2, 1).astype(float)
+    r = repeat_kv(x, 3)
+    assert r.shape == (9, 2, 1)
+    assert [int(r[h, 0, 0]) for h in range(9)] == [0, 0, 0, 2, 2, 2, 4, 4, 4]
+
+
+def test_np_reference_fails_like_the_pages_on_misuse(golden_printed):
+    g = golden_printed
+    s = synth.micro_shape(n_head=9, n_head_kv=3, head_dim=32, n_embd=64)
+    n = NumpyLlama(synth.random_model(s, 0))
+    toks = synth.prompt_ids(s.n_vocab, 13, 1)
+    n.forward(toks[:8], 0)
+    with pytest.raises(ValueError) as e:
+        n.forward(toks[8:], 5)
+    assert str(list(g["misuse_mask_shape"])) in str(e.value)
+    assert str(list(g["misuse_scores_shape"])) in str(e.value)
+
+
+# ---------------------------------------------------------------- whole forward
+
+MICRO_SHAPES = [
+    synth.micro_shape(),
+    synth.micro_shape(n_head=4, n_head_kv=1, name="mqa"),
+    synth.micro_shape(n_head=4, n_head_kv=4, name="mha"),
+    synth.micro_shape(n_layer=1, n_embd=96, n_head=6, n_head_kv=3, head_dim=16, n_ff=96,
+                      n_vocab=37, tied_output=False, name="odd-untied"),
+]
+
+
+@pytest.mark.parametrize("shape", MICRO_SHAPES, ids=lambda s: s.name)
+def test_brute_force_numpy_agrees(shape):
+    m = synth.random_model(shape, 3)
+    o, n = oracle.OracleModel(m), NumpyLlama(m)
+    toks = synth.prompt_ids(shape.n_vocab, 12, 7)
+    # prefill 8, chunked prefill 3 at p=8, then decode steps
+    for chunk, p in ((toks[:8], 0), (toks[8:11], 8), (toks[11:12], 11), ([5], 12), ([1], 13)):
+        st, _, lg64 = o.forward(chunk, p)
+        assert st == oracle.OK
+        ref = n.forward(chunk, p)
+        assert np.allclose(lg64, ref, rtol=1e-11, atol=1e-13)
+    # decode misuse (T = 1, stale counter) follows candle: not an error
+    st, _, lg64 = o.forward([2], 3)
+    assert st == oracle.OK
+    assert np.allclose(lg64, n.forward([2], 3), rtol=1e-11, atol=1e-13)
+
+
+def test_brute_force_tiny_config():
+    w, m, prompt = synth.workload_inputs("C1")
+    o, n = oracle.OracleModel(m), NumpyLlama(m)
+    st, _, lg64 = o.forward(prompt, 0)
+    assert np.allclose(lg64, n.forward(prompt, 0), rtol=1e-11, atol=1e-13)
+    for k in range(3):
+        tok = int(np.argmax(lg64))
+        st, _, lg64 = o.forward([tok], len(prompt) + k)
+        assert np.allclose(lg64, n.forward([tok], len(prompt) + k), rtol=1e-11, atol=1e-13)
+
+
+@pytest.fixture(scope="module")
+def micro():
+    s = synth.micro_shape(n_layer=2, n_head=4, n_head_kv=2, max_seq_len=64)
+    return s, synth.random_model(s, 1)
+
+
+def test_prefill_equals_token_by_token_decode(micro):
+    """T == 1 needs no mask: feeding tokens one at a time = one causal prefill."""
+    s, m = micro
+    toks = synth.prompt_ids(s.n_vocab, 10, 2)
+    a = oracle.OracleModel(m)
+    _, _, full = a.forward(toks, 0)
+    b = oracle.OracleModel(m)
+    for i, t in enumerate(toks):
+        _, _, step = b.forward([t], i)
+    assert np.allclose(full, step, rtol=1e-12, atol=1e-14)
+
+
+def test_chunked_prefill_equals_single(micro):
+    s, m = micro
+    toks = synth.prompt_ids(s.n_vocab, 13, 3)
+    a = oracle.OracleModel(m)
+    _, _, one = a.forward(toks, 0)
+    b = oracle.OracleModel(m)
+    assert b.forward(toks[:8], 0)[0] == oracle.OK
+    st, _, two = b.forward(toks[8:], 8)
+    assert st == oracle.OK and np.allclose(one, two, rtol=1e-12, atol=1e-14)
+    c = oracle.OracleModel(m)
+    c.forward(toks[:8], 0)
+    assert c.forward(toks[8:], 5)[0] == oracle.E_POS_MISMATCH
+    assert c.cache_len == 8                       # nothing changed
+
+
+def test_index_pos_zero_drops_cache_exactly(micro):
+    s, m = micro
+    p1, p2 = synth.prompt_ids(s.n_vocab, 9, 4), synth.prompt_ids(s.n_vocab, 7, 5)
+    fresh = oracle.OracleModel(m)
+    _, ref, _ = fresh.forward(p2, 0)
+    a = oracle.OracleModel(m)
+    a.forward(p1, 0)
+    a.forward([3], 9)
+    _, got, _ = a.forward(p2, 0)
+    assert np.array_equal(got, ref)
+    assert a.cache_len == 7
+
+
+def test_clear_then_stale_counter(micro):
+    s, m = micro
+    p1 = synth.prompt_ids(s.n_vocab, 9, 4)
+    a = oracle.OracleModel(m)
+    a.forward(p1, 0)
+    a.clear_kv_cache()
+    assert a.cache_len == 0
+    assert a.forward(p1, 9)[0] == oracle.E_POS_MISMATCH      # T > 1 with a stale counter
+    assert a.cache_len == 0
+    # one token after a clear sees only itself: q and k share the rotation
+    _, at_p, _ = a.forward([7], 9)
+    b = oracle.OracleModel(m)
+    _, at_0, _ = b.forward([7], 0)
+    assert np.allclose(at_p, at_0, rtol=1e-12, atol=1e-14)
+
+
+def test_index_pos_zero_every_step_sees_one_token(micro):
+    s, m = micro
+    a = oracle.OracleModel(m)
+    a.forward(synth.prompt_ids(s.n_vocab, 5, 6), 0)
+    for t in (4, 9, 2):
+        _, got, _ = a.forward([t], 0)
+        _, ref, _ = oracle.OracleModel(m).forward([t], 0)
+        assert np.array_equal(got, ref)
+
+
+def test_position_bounds(golden_printed):
+    s = synth.micro_shape(max_seq_len=golden_printed["rope_table_rows"])
+    m = synth.random_model(s, 2)
+    a = oracle.OracleModel(m)
+    assert a.forward([1], golden_printed["rope_error_index_pos"])[0] == oracle.E_POS_RANGE
+    assert a.forward([1], s.max_seq_len - 1)[0] == oracle.OK
+    assert a.forward([1, 2], s.max_seq_len - 1)[0] == oracle.E_POS_RANGE
+
+
+def test_error_codes_and_kv_full():
+    s = synth.micro_shape(max_seq_len=16)
+    m = synth.random_model(s, 2)
+    a = oracle.OracleModel(m)
+    assert a.forward([], 0)[0] == oracle.E_INVALID_ARG
+    assert a.forward([s.n_vocab], 0)[0] == oracle.E_INVALID_ARG
+    assert a.forward([1], -1)[0] == oracle.E_INVALID_ARG
+    assert a.forward(list(range(16)), 0)[0] == oracle.OK
+    assert a.cache_len == 16
+    assert a.forward([1], 3)[0] == oracle.E_KV_FULL          # T == 1 misuse into a full cache
+    assert a.cache_len == 16
+
+
+def test_call_counts_match_printed_spans(golden_printed):
+    g = golden_printed
+    s = synth.micro_shape(n_layer=30)
+    a = oracle.OracleModel(synth.random_model(s, 0))
+    for toks, p in ((synth.prompt_ids(s.n_vocab, 13, 1), 0), ([3], 13)):
+        a.forward(toks, p)
+        assert a.counts() == (g["qmatmul_calls"], g["rms_norm_calls"], g["rope_calls"])
+
+
+def test_only_last_position_logits(micro):
+    s, m = micro
+    _, lg, _ = oracle.OracleModel(m).forward(synth.prompt_ids(s.n_vocab, 13, 1), 0)
+    assert lg.shape == (s.n_vocab,)
+
+
+def test_untied_with_copied_embedding_equals_tied():
+    s_t = synth.micro_shape(tied_output=True)
+    s_u = synth.micro_shape(tied_output=False)
+    mt = synth.random_model(s_t, 8)
+    mu = synth.random_model(s_u, 8)
+    mu = mu.replace("output.weight", mt["token_embd.weight"].data.copy())
+    for name in (t.name for t in mt.tensors):
+        mu = mu.replace(name, mt[name].data)
+    toks = synth.prompt_ids(s_t.n_vocab, 6, 1)
+    _, a, _ = oracle.OracleModel(mt).forward(toks, 0)
+    _, b, _ = oracle.OracleModel(mu).forward(toks, 0)
+    assert np.array_equal(a, b)
+
+
+def test_zero_gate_or_down_removes_the_mlp(micro):
+    s, m = micro
+    toks = synth.prompt_ids(s.n_vocab, 6, 1)
+    outs = []
+    for which in ("ffn_gate", "ffn_up", "ffn_down"):
+        mm = m
+        for l in range(s.n_layer):
+            name = f"blk.{l}.{which}.weight"
+            raw = mm[name].data.copy().reshape(-1, 34)
+            raw[:, 0:2] = 0                                    # every block scale = 0
+            mm = mm.replace(name, raw.reshape(mm[name].data.shape))
+        outs.append(oracle.OracleModel(mm).forward(toks, 0)[1])
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    assert not np.array_equal(outs[0], oracle.OracleModel(m).forward(toks, 0)[1])
+
+
+def test_argmax_lowest_index_on_ties():
+    assert oracle.argmax(np.array([1.0, 3.0, 3.0, 2.0], np.float32)) == 1
+    assert oracle.argmax(np.array([5.0], np.float32)) == 0
