@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark: batch-1 greedy generation with the Q8_0 Llama forward on one GPU.
+
+One step = one generation of the workload as the pages time it ("生成一个
+token", section 实验程序): a prompt prefill at position 0, then `decode_steps`
+single-token forwards, each followed by the greedy argmax read back to the
+host. Default workload: the SmolLM2-135M-shaped model (30 layers, hidden 576,
+9/3 heads, vocab 49152 tied), 13-token prompt + 20 decode steps, random-init
+Q8_0 weights and uniform random prompt ids (no trained weights are used).
+
+Printed JSON line:
+  value            decode tokens/s of the host loop (forward + argmax readback per token)
+  prefill_tok_s    prompt tokens / prefill wall time (to the argmax readback)
+  device_loop      decode on the device (q8l_generate: argmax feeds the next step
+                   without host round trips), per-token time and HBM fraction
+                   = algorithmic bytes per token (Q8_0 weights + norms + one
+                   embedding row + KV cache read/written) / time / 8 TB/s
+  roofline         the decode kernel with the most time per step, its algorithmic
+                   bytes per launch over its mean launch time (HIP events)
+  cpu_baseline     the CPU oracle timed on a bounded sample of the same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+# The pages' Metal figure for this workload ("生成一个 token", section "Metal：热缓存"):
+# 20 decode steps after a 13-token prompt, 2.6 ms mean per step incl. the argmax
+# readback, on an Apple M2 Max -- another machine, quoted as context.
+PAGES_DECODE_MS = {"C2": 2.6}
+KIND_NAMES = ["embed", "qkv_rope_kv", "attn_decode", "oproj_residual", "gateup_silu",
+              "down_residual", "lmhead_argmax"]
+KERNEL_SYMBOLS = ["k_embed", "k_qkv<1>", "k_attn_decode", "k_matmul<1>", "k_gateup<1>",
+                  "k_matmul<1>", "k_lmhead"]
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def q8_bytes(rows, cols):
+    return rows * cols // 32 * 34
+
+
+def per_token_weight_bytes(s):
+    """Q8_0 projections + output layer + f32 norm weights + one embedding row."""
+    H, QD, KVD, F, V = s.n_embd, s.q_dim, s.kv_dim, s.n_ff, s.n_vocab
+    layer = (q8_bytes(QD, H) + 2 * q8_bytes(KVD, H) + q8_bytes(H, QD) + 2 * q8_bytes(F, H)
+             + q8_bytes(H, F) + 2 * H * 4)
+    return s.n_layer * layer + q8_bytes(V, H) + H * 4 + q8_bytes(1, H)
+
+
+def kv_bytes_per_position(s):
+    return s.n_layer * 2 * s.n_head_kv * s.head_dim * 4
+
+
+def kernel_bytes(s, kv_len):
+    """Algorithmic bytes of one launch of each decode kernel kind (layer 0)."""
+    H, QD, KVD, F, V = s.n_embd, s.q_dim, s.kv_dim, s.n_ff, s.n_vocab
+    return [
+        q8_bytes(1, H) + H * 4,
+        q8_bytes(QD + 2 * KVD, H) + 2 * H * 4 + (QD + 2 * KVD) * 4,
+        kv_len * s.n_head_kv * s.head_dim * 4 * 2 + 2 * QD * 4,
+        q8_bytes(H, QD) + QD * 4 + 2 * H * 4,
+        2 * q8_bytes(F, H) + 2 * H * 4 + F * 4,
+        q8_bytes(H, F) + F * 4 + 2 * H * 4,
+        q8_bytes(V, H) + 2 * H * 4 + V * 4,
+    ]
+
+
+def cpu_baseline(model, prompt, steps, seconds):
+    """The oracle, as it stands, on the same workload: repeat the generation
+    until `seconds` of CPU work; report decode tokens/s."""
+    import oracle
+
+    oracle.build(force=False)
+    om = oracle.OracleModel(model)
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    t_dec, n_dec, reps, t_all0 = 0.0, 0, 0, time.perf_counter()
+    while True:
+        st, lg, _ = om.forward(prompt, 0)
+        nxt = oracle.argmax(lg)
+        t0 = time.perf_counter()
+        for k in range(steps):
+            st, lg, _ = om.forward([nxt], len(prompt) + k)
+            nxt = oracle.argmax(lg)
+        t_dec += time.perf_counter() - t0
+        n_dec += steps
+        reps += 1
+        if time.perf_counter() - t_all0 >= seconds:
+            break
+    return {"value": n_dec / t_dec, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x (prefill {len(prompt)} + {steps} decode steps) of the same model; "
+                      f"decode tokens/s over {t_dec:.1f} s of decode"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="C2", help="workload key in synth.WORKLOADS")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        eprint(f"bench.py runs on one GPU: this build has no multi-GPU path (--gpus {args.gpus}).")
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from quantized_q8_gemv_amd import q8l as C
+    from quantized_q8_gemv_amd.model import Q8Model
+
+    w, model, prompt = synth.workload_inputs(args.config)
+    s = model.shape
+    steps = w.decode_steps
+    eprint(f"[bench] {w.name}: generating done, uploading {model.total_bytes / 1e6:.1f} MB")
+    gm = Q8Model(synth.shape_fields(s), model.tensors, device="cuda:0")
+    torch.cuda.synchronize()
+
+    def generation():
+        t0 = time.perf_counter()
+        st = gm.forward_async(prompt, 0)
+        assert st == C.Q8L_OK, st
+        nxt = int(gm.argmax.item())
+        t1 = time.perf_counter()
+        for k in range(steps):
+            st = gm.forward_async([nxt], len(prompt) + k)
+            assert st == C.Q8L_OK, st
+            nxt = int(gm.argmax.item())
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1
+
+    for _ in range(args.warmup):
+        generation()
+    torch.cuda.synchronize()
+    eprint(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    t_start = time.perf_counter()
+    pre, dec = [], []
+    for _ in range(args.steps):
+        a, b = generation()
+        pre.append(a)
+        dec.append(b)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) / args.steps * 1e3
+    value = args.steps * steps / sum(dec)
+    prefill_tok_s = len(prompt) / statistics.median(pre)
+    eprint(f"[bench] host loop: {value:.1f} decode tok/s, prefill {prefill_tok_s:.1f} tok/s")
+
+    # Decode on the device: argmax feeds the next step, no host round trip.
+    ids = torch.zeros(steps, dtype=torch.int32, device="cuda:0")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dl = []
+    for r in range(12):
+        assert gm.forward_async(prompt, 0) == C.Q8L_OK
+        ev0.record()
+        assert gm.generate_async(gm.argmax, len(prompt), steps, ids) == C.Q8L_OK
+        ev1.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            dl.append(ev0.elapsed_time(ev1) / steps)
+    dev_ms = statistics.median(dl)
+    W = per_token_weight_bytes(s)
+    kvb = kv_bytes_per_position(s)
+    mean_kv = len(prompt) + (steps + 1) / 2.0
+    b_tok = W + kvb * mean_kv
+    dev_gbs = b_tok / (dev_ms * 1e-3) / 1e9
+    eprint(f"[bench] device loop: {dev_ms * 1e3:.1f} us/token, {dev_gbs:.0f} GB/s algorithmic")
+
+    # Per-kernel launch times (HIP events on the stream the kernels run on).
+    assert gm.forward_async(prompt, 0) == C.Q8L_OK
+    torch.cuda.synchronize()
+    ms = (ctypes.c_float * 7)()
+    st = C.lib().q8l_time_decode_kernels(gm.handle, args.kernel_reps, ms,
+                                         torch.cuda.current_stream().cuda_stream)
+    assert st == C.Q8L_OK, C.q8l_last_error(gm.handle)
+    kv_len = len(prompt) + 1
+    kb = kernel_bytes(s, kv_len)
+    launches = [1, s.n_layer, s.n_layer, s.n_layer, s.n_layer, s.n_layer, 1]
+    per_step = [ms[i] * launches[i] for i in range(7)]
+    dom = max(range(7), key=lambda i: per_step[i])
+    kernels = {KIND_NAMES[i]: {"us": round(ms[i] * 1e3, 2), "bytes": kb[i],
+                               "gbs": round(kb[i] / (ms[i] * 1e-3) / 1e9, 1),
+                               "launches_per_token": launches[i]} for i in range(7)}
+    achieved = kb[dom] / (ms[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": KIND_NAMES[dom], "symbol": KERNEL_SYMBOLS[dom],
+                "bytes_per_launch": kb[dom], "us_per_launch": round(ms[dom] * 1e3, 2)}
+    eprint(f"[bench] kernels: " + ", ".join(f"{k} {v['us']}us" for k, v in kernels.items()))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        eprint(f"[bench] cpu baseline (oracle) ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(model, prompt, steps, args.cpu_seconds)
+
+    out = {
+        "metric": "decode tokens/s (batch 1) + achieved HBM GB/s vs peak; prefill tokens/s",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(value / (1e3 / PAGES_DECODE_MS[args.config]), 2)
+                        if args.config in PAGES_DECODE_MS else None),
+        "dtype": "f32 (Q8_0 int8 x f16-scale weights, f32 activations and accumulation)",
+        "data": "synthetic: random-init Q8_0 weights, uniform random prompt ids",
+        "config": {"workload": w.name, "model": s.name, "layers": s.n_layer, "hidden": s.n_embd,
+                   "heads": s.n_head, "kv_heads": s.n_head_kv, "vocab": s.n_vocab,
+                   "prompt_len": len(prompt), "decode_steps": steps, "batch": 1,
+                   "parallelism": "single GPU"},
+        "prefill_tok_s": round(prefill_tok_s, 1),
+        "decode_ms_per_token_host_loop": round(sum(dec) / (args.steps * steps) * 1e3, 4),
+        "device_loop": {"us_per_token": round(dev_ms * 1e3, 2),
+                        "tok_s": round(1e3 / dev_ms, 1),
+                        "bytes_per_token": int(b_tok),
+                        "hbm_gbs": round(dev_gbs, 1),
+                        "hbm_frac": round(dev_gbs / PEAK_HBM_GBS, 4)},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

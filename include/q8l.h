@@ -1,0 +1,246 @@
+/*
+ * q8l.h -- C ABI of the MI355X (gfx950) quantized Llama forward library.
+ *
+ * The library runs the forward pass of a Llama-shaped model whose projection
+ * weights are Q8_0 blocks, as the page "量化 llama 的一次前向" (one forward of
+ * quantized llama) traces it through candle's quantized_llama:
+ *   token embedding -> per layer [RMSNorm -> q/k/v projections -> interleaved
+ *   rope at index_pos -> KV-cache append -> grouped-query attention ->
+ *   o-projection + residual -> RMSNorm -> gate/up projections, SiLU(gate)*up,
+ *   down projection + residual] -> final RMSNorm -> last position ->
+ *   output layer (the embedding when output.weight is absent).
+ * Its calls follow the interface that page and "生成一个 token" (generating one
+ * token) describe: build a model from named tensors (section "建模型：按名字取
+ * 张量"), forward(tokens, index_pos) -> logits of the last position (section
+ * "forward：mask 什么时候建"), and clear_kv_cache (section "换 prompt 要不要
+ * clear_kv_cache").
+ *
+ * Conventions for every call:
+ *   - Device pointers are HIP device memory on the current device. The
+ *     library never frees memory it did not allocate; bound tensors and the
+ *     workspace are BORROWED and must outlive the model.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls that take a stream enqueue work and return without waiting;
+ *     results are valid after the stream is synchronized.
+ *   - Errors are returned as q8l_status; q8l_last_error() gives a message.
+ *     An error found by argument or state checks leaves the model unchanged
+ *     and enqueues nothing. A HIP launch failure returns Q8L_E_HIP.
+ *   - A model is not re-entrant: a forward mutates its KV cache. Two models
+ *     may be used from different threads.
+ *
+ * Q8_0 layout: a row of K weights (K a multiple of 64 for this library) is
+ * K/32 blocks of 34 bytes, each an IEEE binary16 scale d (little-endian)
+ * followed by 32 signed 8-bit values q; weight = d * q. Matrices are
+ * row-major [out, in] with blocks along `in`. The pages fix the block size
+ * through the model file's byte count ("生成一个 token", sections 实验程序
+ * and 读 GGUF); the field order is the GGUF convention.
+ */
+#ifndef Q8L_H
+#define Q8L_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q8L_OK = 0,
+    Q8L_E_INVALID_ARG = 1,    /* bad pointer, size, count, token id, or index_pos < 0 */
+    Q8L_E_MISSING_TENSOR = 2, /* finalize: a required tensor was never bound */
+    Q8L_E_SHAPE = 3,          /* bind: rows/cols/nbytes do not match the config */
+    Q8L_E_POS_RANGE = 4,      /* index_pos + T > max_seq_len (the rope table bound) */
+    Q8L_E_POS_MISMATCH = 5,   /* T > 1 and index_pos != cached positions */
+    Q8L_E_KV_FULL = 6,        /* cached positions + T > max_seq_len */
+    Q8L_E_NOT_FINALIZED = 7,  /* forward before finalize, or bind after it */
+    Q8L_E_HIP = 8             /* a HIP call failed (message has the HIP error) */
+} q8l_status;
+
+typedef enum { Q8L_F32 = 0, Q8L_Q8_0 = 1 } q8l_dtype;
+
+/*
+ * Model hyper-parameters: the llama.* metadata keys the page "生成一个 token"
+ * (section 读 GGUF) prints, plus the rope table length (4096 in candle, page
+ * "量化 llama 的一次前向", section "from_gguf：键名写死了 llama."), the norm eps
+ * and the rope base. Requirements: n_head % n_head_kv == 0 with at most 16
+ * query heads per KV head, head_dim a multiple of 8 and <= 128, n_embd, n_ff
+ * and n_head*head_dim multiples of 64, max_seq_len >= 1.
+ */
+typedef struct q8l_config {
+    int32_t n_layer;      /* llama.block_count */
+    int32_t n_embd;       /* llama.embedding_length (H) */
+    int32_t n_head;       /* llama.attention.head_count */
+    int32_t n_head_kv;    /* llama.attention.head_count_kv */
+    int32_t head_dim;     /* per-head width */
+    int32_t n_ff;         /* llama.feed_forward_length */
+    int32_t n_vocab;      /* rows of token_embd */
+    int32_t max_seq_len;  /* rope table rows = KV cache slots (4096) */
+    double rms_eps;       /* RMSNorm epsilon (1e-5) */
+    double rope_theta;    /* rope base (10000) */
+    int32_t tied_output;  /* 1: the output layer is token_embd */
+} q8l_config;
+
+typedef struct q8l_model q8l_model;
+
+/* Bytes of device workspace the model needs: KV cache
+ * [n_layer][2][n_head_kv][max_seq_len][head_dim] f32, the rope table,
+ * activations for up to max_seq_len tokens, attention partials and counters.
+ * Returns 0 for an invalid config. */
+size_t q8l_workspace_bytes(const q8l_config *cfg);
+
+/* Create a host-side model object; no HIP calls. Q8L_E_INVALID_ARG for a bad
+ * config. The object is owned by the caller and freed with q8l_destroy. */
+q8l_status q8l_create(const q8l_config *cfg, q8l_model **out);
+
+/*
+ * Bind one tensor by its GGUF name (page "生成一个 token", section 建模型):
+ *   token_embd.weight              Q8_0 [n_vocab, n_embd]
+ *   blk.{i}.attn_norm.weight       F32  [1, n_embd]
+ *   blk.{i}.attn_q.weight          Q8_0 [n_head*head_dim, n_embd]
+ *   blk.{i}.attn_k.weight          Q8_0 [n_head_kv*head_dim, n_embd]
+ *   blk.{i}.attn_v.weight          Q8_0 [n_head_kv*head_dim, n_embd]
+ *   blk.{i}.attn_output.weight     Q8_0 [n_embd, n_head*head_dim]
+ *   blk.{i}.ffn_norm.weight        F32  [1, n_embd]
+ *   blk.{i}.ffn_gate.weight        Q8_0 [n_ff, n_embd]
+ *   blk.{i}.ffn_up.weight          Q8_0 [n_ff, n_embd]
+ *   blk.{i}.ffn_down.weight        Q8_0 [n_embd, n_ff]
+ *   output_norm.weight             F32  [1, n_embd]
+ *   output.weight                  Q8_0 [n_vocab, n_embd]  (untied models only)
+ * `dev_ptr` holds the raw bytes (Q8_0 blocks exactly as in the file; F32
+ * little-endian), 16-byte aligned, borrowed. Q8L_E_SHAPE when rows, cols or
+ * nbytes (rows*cols/32*34 for Q8_0, rows*cols*4 for F32) do not match;
+ * Q8L_E_INVALID_ARG for an unknown name, NULL or misaligned pointer;
+ * Q8L_E_NOT_FINALIZED after finalize (weights are fixed once finalized).
+ * Binding a name twice replaces the earlier pointer.
+ */
+q8l_status q8l_bind_tensor(q8l_model *m, const char *name, q8l_dtype dtype, int64_t rows,
+                           int64_t cols, const void *dev_ptr, size_t nbytes);
+
+/* Bind the device workspace (>= q8l_workspace_bytes, 256-byte aligned,
+ * borrowed). Q8L_E_INVALID_ARG if too small, NULL or misaligned. */
+q8l_status q8l_bind_workspace(q8l_model *m, void *dev_ptr, size_t nbytes);
+
+/*
+ * Check that every required tensor (9 per layer + token_embd + output_norm,
+ * + output.weight when untied) and the workspace are bound -- else
+ * Q8L_E_MISSING_TENSOR naming the first missing one -- then build the rope
+ * table on the device, set the cached-position count to 0 and prepare the
+ * decode graphs. Enqueued on `stream`.
+ */
+q8l_status q8l_finalize(q8l_model *m, void *stream);
+
+/*
+ * forward(tokens, index_pos): run T = n_tokens tokens starting at position
+ * index_pos and write the logits of the LAST position to logits_dev
+ * (f32[n_vocab], device) and, if argmax_dev is not NULL, the index of the
+ * largest logit (lowest index on ties) to *argmax_dev (device uint32).
+ * `tokens_host` is host memory (read before the call returns).
+ * Checks, in this order, before anything is enqueued or changed:
+ *   1. n_tokens >= 1, tokens < n_vocab, index_pos >= 0, logits_dev != NULL
+ *                                                        else Q8L_E_INVALID_ARG
+ *   2. index_pos + T <= max_seq_len                      else Q8L_E_POS_RANGE
+ *   3. index_pos == 0 drops the cache (cached positions := 0), as candle does
+ *   4. T > 1 requires index_pos == cached positions      else Q8L_E_POS_MISMATCH
+ *      (candle fails these as a broadcast error; page "量化 llama 的一次前向",
+ *      section "index_pos 传错"). T == 1 is NOT checked, as in candle: rope
+ *      uses index_pos, the new key/value go to the next free slot and the
+ *      single query attends to every cached position without a mask.
+ *   5. cached positions + T <= max_seq_len               else Q8L_E_KV_FULL
+ * Then enqueue the forward; cached positions += T.
+ */
+q8l_status q8l_forward(q8l_model *m, const uint32_t *tokens_host, int32_t n_tokens,
+                       int32_t index_pos, float *logits_dev, uint32_t *argmax_dev,
+                       void *stream);
+
+/*
+ * Greedy generation on the device: starting from the token at *token_dev
+ * (device uint32), run `n_steps` single-token forwards at positions
+ * index_pos, index_pos+1, ..., each feeding its argmax to the next step
+ * without a host round trip, and write the n_steps picked ids to ids_dev
+ * (device uint32[n_steps]). logits_dev (optional, f32[n_vocab]) receives the
+ * last step's logits. This is the caller's loop of single-token forwards and
+ * argmax readbacks (page "生成一个 token", section 实验程序), with each step's
+ * checks (as in q8l_forward with T == 1) done up front for all steps.
+ */
+q8l_status q8l_generate(q8l_model *m, const uint32_t *token_dev, int32_t index_pos,
+                        int32_t n_steps, uint32_t *ids_dev, float *logits_dev, void *stream);
+
+/* Drop the KV cache: cached positions := 0 (page "量化 llama 的一次前向",
+ * section "换 prompt 要不要 clear_kv_cache"). No memory is freed or cleared. */
+q8l_status q8l_clear_kv_cache(q8l_model *m);
+
+/* Number of cached positions (-1 for NULL). */
+int32_t q8l_cache_len(const q8l_model *m);
+
+/* Message for the last error on this model ("" if none; static string for NULL). */
+const char *q8l_last_error(const q8l_model *m);
+
+/* Free the host object and the graphs it owns (not bound memory). */
+void q8l_destroy(q8l_model *m);
+
+/* ------------------------------------------------------------------------
+ * Single-op entry points: the hot path's building blocks on caller buffers,
+ * for tests and microbenchmarks. All pointers are device memory; all enqueue
+ * on `stream`.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Q8_0 matrix-vector / small matrix product (the decode projection; page
+ * "生成一个 token", section "prefill 和 decode：同一个 forward，不同的路":
+ * one input row uses the matrix-vector kernel):
+ *   Y[t][n] = sum_k W[n][k] * U[t][k],  t < T, n < N,
+ * with U = X (norm_w NULL) or U[t] = X[t] / sqrt(mean(X[t]^2) + eps) * norm_w
+ * (RMSNorm fused in front). W is Q8_0 [N][K] (16-byte aligned), X f32 [T][K],
+ * Y f32 [T][N]. When `accumulate` is 1, Y += the product (residual add).
+ * K must be a multiple of 64; 1 <= T <= max(T) for which the multi-token
+ * path is used (any T >= 1 is accepted; large T uses the matrix-matrix path).
+ */
+q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *X, int64_t T,
+                              const float *norm_w, double eps, int32_t accumulate, float *Y,
+                              void *stream);
+
+/*
+ * Attention of T queries over kv_len cached keys with grouped heads:
+ *   Q f32 [T][n_head][hd]; K, V f32 [n_head_kv][kv_stride][hd] (slot j of
+ *   group g at (g*kv_stride + j)*hd); O f32 [T][n_head][hd].
+ * Query head h reads KV group h / (n_head/n_head_kv). Scores are
+ * q.k / sqrt(hd); when T > 1, query t sees keys j <= kv_len - T + t (the
+ * causal mask offset by the cached prefix); when T == 1 it sees all kv_len.
+ */
+q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int32_t T,
+                            int32_t kv_len, int32_t kv_stride, int32_t n_head,
+                            int32_t n_head_kv, int32_t hd, float *O, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace q8l_op_attention needs for these sizes. */
+size_t q8l_op_attention_workspace(int32_t T, int32_t kv_len, int32_t n_head, int32_t n_head_kv,
+                                  int32_t hd);
+
+/* Largest element of x (f32[n], device), lowest index on ties, to *out. */
+q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
+ * Measurement: launch each kernel of one decode step on its own, `reps`
+ * times, each launch between two HIP events on `stream`, and write the mean
+ * duration in milliseconds to ms_out[kind], kinds
+ *   0 embedding, 1 q/k/v (+norm, rope, KV write), 2 attention,
+ *   3 o-projection (+residual), 4 gate/up (+norm, SiLU*up),
+ *   5 down (+residual), 6 output layer (+norm, argmax).
+ * Layer 0's weights are used, at the current cache length (attention over
+ * cache_len + 1 keys). The residual stream, the next KV slot and the logits
+ * buffer are scratch afterwards: the next forward rewrites them before use.
+ * The cache length is unchanged. Blocks until the timings are read back.
+ * Q8L_E_INVALID_ARG if reps < 1 or the cache is full.
+ */
+q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, void *stream);
+
+/* Version string of the library build. */
+const char *q8l_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8L_H */

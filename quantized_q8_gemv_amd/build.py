@@ -1,0 +1,59 @@
+"""Build libq8l.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+Usage: python -m quantized_q8_gemv_amd.build   (or call build()).
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libq8l.so")
+SOURCES = ["k_gemv.hip", "k_attn.hip", "k_misc.hip", "runtime.cpp"]
+ARCH = os.environ.get("Q8L_OFFLOAD_ARCH", "gfx950")
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+
+# -packed-fp32-ops: keep the compiler from forming packed FP32 instructions.
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
+          "-Wno-unused-variable"]
+
+
+def _compile(src: str, obj: str) -> None:
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libq8l.so; returns its path."""
+    with tempfile.TemporaryDirectory(prefix="q8l_build_") as tmp:
+        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+            futs = [ex.submit(_compile, s, o) for s, o in zip(SOURCES, objs)]
+            for s, f in zip(SOURCES, futs):
+                try:
+                    f.result()
+                except subprocess.CalledProcessError as e:
+                    sys.stderr.write(e.stdout.decode(errors="replace"))
+                    raise RuntimeError(f"hipcc failed on {s}") from None
+        tmp_lib = LIB + ".tmp"
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib] + objs
+        subprocess.run(cmd, check=True)
+        os.replace(tmp_lib, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,108 @@
+// device_common.h -- device helpers shared by the kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q8l_internal.h"
+
+namespace q8l {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// IEEE binary16 bit pattern -> f32 (exact; subnormal scales stay subnormal in
+// f16 and become normal f32 values).
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+    return __half2float(__ushort_as_half(static_cast<unsigned short>(bits & 0xffffu)));
+}
+
+__device__ __forceinline__ float sbyte(uint32_t v, int b) {
+    return static_cast<float>(static_cast<int>(static_cast<int8_t>((v >> (8 * b)) & 0xffu)));
+}
+
+// Decode one pair of Q8_0 blocks (68 bytes = 17 dwords at a 4-byte aligned
+// address): block A = bytes [0, 34), block B = bytes [34, 68). The int8
+// payload of A starts at byte 2, so its dwords are re-aligned with alignbyte;
+// B's payload starts at byte 36 and is dword-aligned.
+struct PairQ {
+    float dA, dB;
+    float q[64];
+};
+
+__device__ __forceinline__ void decode_pair(const uint32_t *w, PairQ &o) {
+    uint32_t r[17];
+#pragma unroll
+    for (int i = 0; i < 17; ++i) r[i] = w[i];
+    o.dA = half_bits_to_float(r[0]);
+    o.dB = half_bits_to_float(r[8] >> 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t a = __builtin_amdgcn_alignbyte(r[j + 1], r[j], 2);
+        uint32_t b = r[9 + j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o.q[4 * j + e] = sbyte(a, e);
+            o.q[32 + 4 * j + e] = sbyte(b, e);
+        }
+    }
+}
+
+// d * sum_i q[i] x[i] over one 32-weight block, in a fixed order: four
+// interleaved partial sums, then (s0 + s1) + (s2 + s3).
+__device__ __forceinline__ float block_dot(const float *q, const float *x) {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+        float4 xv = *reinterpret_cast<const float4 *>(x + i);
+        s0 = fmaf(q[i + 0], xv.x, s0);
+        s1 = fmaf(q[i + 1], xv.y, s1);
+        s2 = fmaf(q[i + 2], xv.z, s2);
+        s3 = fmaf(q[i + 3], xv.w, s3);
+    }
+    return (s0 + s1) + (s2 + s3);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Sum of v over the 256-thread workgroup in a fixed order; every thread gets
+// the result. `red` is 4 floats of LDS.
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Larger value wins; on equal values the lower index wins.
+__device__ __forceinline__ void argmax_merge(float &v, uint32_t &i, float ov, uint32_t oi) {
+    if (ov > v || (ov == v && oi < i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
+__device__ __forceinline__ void wave_argmax(float &v, uint32_t &i) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        float ov = __shfl_xor(v, off, 64);
+        uint32_t oi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(i), off, 64));
+        argmax_merge(v, i, ov, oi);
+    }
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace q8l

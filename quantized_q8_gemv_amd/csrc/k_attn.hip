@@ -1,0 +1,263 @@
+// k_attn.hip -- grouped-query attention over the preallocated KV cache.
+//
+// Semantics ("量化 llama 的一次前向", section "forward_attn：自己拼 KV";
+// "生成一个 token", section "prefill 和 decode：同一个 forward，不同的路"):
+// scores q.k / sqrt(hd); query head h reads KV head h / (n_head / n_head_kv)
+// (each KV head serves a run of consecutive query heads); softmax over keys;
+// weighted sum of values. A single query (decode) sees every cached key with
+// no mask; T > 1 queries see keys j <= prefix + i (prefix = cached positions
+// before the call) -- the mask whose first `prefix` columns are open and whose
+// last T columns are a causal triangle, applied here as a predicate instead
+// of a mask tensor, and without copying KV heads.
+//
+// Decode: the cache is split into chunks of keys; one workgroup handles one
+// chunk for all query heads of one KV head (K/V are read once per group),
+// keeps scores and softmax in LDS, and writes (max, sum, unnormalised o)
+// partials. The last workgroup of a group to finish (atomic counter) merges
+// the partials in split order, so the result does not depend on timing.
+//
+// Prefill: one workgroup per (32 queries, head); key tiles staged in LDS,
+// online softmax in f32 per query row.
+
+#include "device_common.h"
+
+namespace q8l {
+
+__host__ __device__ int attn_chunk(int hd) { return hd <= 64 ? 64 : 32; }
+
+namespace {
+
+struct DecodeLds {
+    float *q;    // G * hd
+    float *k;    // chunk * (hd + 1)
+    float *v;    // chunk * hd
+    float *sc;   // G * chunk
+    float *m;    // G
+    float *l;    // G
+};
+
+__global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int s = blockIdx.x, g = blockIdx.y;
+    const int hd = a.hd, G = a.nh / a.nkv;
+    const int C = attn_chunk(hd);
+    const int kv_len = a.kv_len_arg >= 0 ? a.kv_len_arg : a.st->slot + 1;
+    const int active = min((kv_len + C - 1) / C, a.n_splits);
+
+    DecodeLds L;
+    float *p = reinterpret_cast<float *>(smem);
+    L.q = p; p += G * hd;
+    L.k = p; p += C * (hd + 1);
+    L.v = p; p += C * hd;
+    L.sc = p; p += G * C;
+    L.m = p; p += G;
+    L.l = p;
+
+    if (s < active) {
+        const int j0 = s * C;
+        const int nk = min(C, kv_len - j0);
+        const float *qg = a.q + size_t(g) * G * hd;
+        for (int e = tid; e < G * hd; e += kThreads) L.q[e] = qg[e];
+        const float *kb = a.kc + (size_t(g) * a.kv_stride + j0) * hd;
+        const float *vb = a.vc + (size_t(g) * a.kv_stride + j0) * hd;
+        for (int e = tid; e < nk * hd; e += kThreads) {
+            const int j = e / hd, d = e - j * hd;
+            L.k[j * (hd + 1) + d] = kb[e];
+            L.v[e] = vb[e];
+        }
+        __syncthreads();
+        for (int e = tid; e < G * nk; e += kThreads) {
+            const int h = e / nk, j = e - h * nk;
+            const float *qh = L.q + h * hd;
+            const float *kj = L.k + j * (hd + 1);
+            float s0 = 0.f, s1 = 0.f;
+            for (int d = 0; d < hd; d += 2) {
+                s0 = fmaf(qh[d], kj[d], s0);
+                s1 = fmaf(qh[d + 1], kj[d + 1], s1);
+            }
+            L.sc[h * C + j] = (s0 + s1) * a.scale;
+        }
+        __syncthreads();
+        for (int h = wid; h < G; h += 4) {
+            float mx = -INFINITY;
+            for (int j = lane; j < nk; j += 64) mx = fmaxf(mx, L.sc[h * C + j]);
+            mx = wave_max(mx);
+            float sum = 0.f;
+            for (int j = lane; j < nk; j += 64) {
+                const float e = expf(L.sc[h * C + j] - mx);
+                L.sc[h * C + j] = e;
+                sum += e;
+            }
+            sum = wave_sum(sum);
+            if (lane == 0) {
+                L.m[h] = mx;
+                L.l[h] = sum;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < G * hd; e += kThreads) {
+            const int h = e / hd, d = e - h * hd;
+            float acc = 0.f;
+            for (int j = 0; j < nk; ++j) acc = fmaf(L.sc[h * C + j], L.v[j * hd + d], acc);
+            const int head = g * G + h;
+            if (active == 1) {
+                a.o[size_t(head) * hd + d] = acc / L.l[h];
+            } else {
+                float *pp = a.part + (size_t(head) * a.n_splits + s) * (hd + 2);
+                pp[2 + d] = acc;
+                if (d == 0) {
+                    pp[0] = L.m[h];
+                    pp[1] = L.l[h];
+                }
+            }
+        }
+    }
+    if (active == 1) return;
+
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(a.counters + g, 1u) == unsigned(a.n_splits) - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    for (int e = tid; e < G * hd; e += kThreads) {
+        const int h = e / hd, d = e - h * hd;
+        const int head = g * G + h;
+        const float *pb = a.part + size_t(head) * a.n_splits * (hd + 2);
+        float M = -INFINITY;
+        for (int t = 0; t < active; ++t) M = fmaxf(M, pb[t * (hd + 2)]);
+        float Lsum = 0.f, O = 0.f;
+        for (int t = 0; t < active; ++t) {
+            const float w = expf(pb[t * (hd + 2)] - M);
+            Lsum = fmaf(w, pb[t * (hd + 2) + 1], Lsum);
+            O = fmaf(w, pb[t * (hd + 2) + 2 + d], O);
+        }
+        a.o[size_t(head) * hd + d] = O / Lsum;
+    }
+    if (tid == 0) a.counters[g] = 0u;
+}
+
+constexpr int kQB = 32;   // queries per prefill workgroup
+constexpr int kKT = 32;   // keys per prefill tile
+
+__global__ __launch_bounds__(kThreads) void k_attn_prefill(AttnPrefillArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int qi = tid >> 3, sub = tid & 7;
+    const int hd = a.hd, G = a.nh / a.nkv;
+    const int h = blockIdx.y, g = h / G;
+    const int q0 = blockIdx.x * kQB;
+    const int nq = min(kQB, a.T - q0);
+    const int prefix = a.kv_len - a.T;
+    const int row_stride = a.nh * hd;
+
+    float *Qs = reinterpret_cast<float *>(smem);       // kQB * (hd + 1)
+    float *Ks = Qs + kQB * (hd + 1);                    // kKT * (hd + 1)
+    float *Vs = Ks + kKT * (hd + 1);                    // kKT * hd
+    float *Ps = Vs + kKT * hd;                          // kQB * kKT
+
+    for (int e = tid; e < kQB * hd; e += kThreads) {
+        const int i = e / hd, d = e - i * hd;
+        Qs[i * (hd + 1) + d] = (i < nq) ? a.q[size_t(q0 + i) * row_stride + h * hd + d] : 0.f;
+    }
+    const int ndim = hd / 8;  // output dims per thread (hd % 8 == 0)
+    float o[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o[k] = 0.f;
+    float m = -INFINITY, lsum = 0.f;
+    const int my_last = prefix + q0 + qi;                  // last visible key of this row
+    const int blk_last = prefix + q0 + nq - 1;             // last key any row sees
+    const float *kb = a.kc + size_t(g) * a.kv_stride * hd;
+    const float *vb = a.vc + size_t(g) * a.kv_stride * hd;
+
+    for (int j0 = 0; j0 <= blk_last; j0 += kKT) {
+        const int nk = min(kKT, blk_last + 1 - j0);
+        __syncthreads();
+        for (int e = tid; e < kKT * hd; e += kThreads) {
+            const int j = e / hd, d = e - j * hd;
+            const bool in = j < nk;
+            Ks[j * (hd + 1) + d] = in ? kb[size_t(j0 + j) * hd + d] : 0.f;
+            Vs[e] = in ? vb[size_t(j0 + j) * hd + d] : 0.f;
+        }
+        __syncthreads();
+        float sv[kKT / 8];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kKT / 8; ++u) {
+            const int jj = sub + 8 * u;
+            const int j = j0 + jj;
+            float sc = -INFINITY;
+            if (qi < nq && jj < nk && j <= my_last) {
+                const float *qr = Qs + qi * (hd + 1);
+                const float *kr = Ks + jj * (hd + 1);
+                float s0 = 0.f, s1 = 0.f;
+                for (int d = 0; d < hd; d += 2) {
+                    s0 = fmaf(qr[d], kr[d], s0);
+                    s1 = fmaf(qr[d + 1], kr[d + 1], s1);
+                }
+                sc = (s0 + s1) * a.scale;
+            }
+            sv[u] = sc;
+            tmax = fmaxf(tmax, sc);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 4, 64));
+        const float m_new = fmaxf(m, tmax);
+        const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int u = 0; u < kKT / 8; ++u) {
+            const float pv = (sv[u] == -INFINITY) ? 0.f : expf(sv[u] - m_new);
+            Ps[qi * kKT + sub + 8 * u] = pv;
+            psum += pv;
+        }
+        psum += __shfl_xor(psum, 1, 64);
+        psum += __shfl_xor(psum, 2, 64);
+        psum += __shfl_xor(psum, 4, 64);
+        lsum = lsum * alpha + psum;
+        m = m_new;
+        __syncthreads();
+        const float *pr = Ps + qi * kKT;
+        for (int k = 0; k < ndim; ++k) {
+            const int d = sub + 8 * k;
+            float acc = 0.f;
+            for (int jj = 0; jj < nk; ++jj) acc = fmaf(pr[jj], Vs[jj * hd + d], acc);
+            o[k] = o[k] * alpha + acc;
+        }
+    }
+    if (qi < nq) {
+        float *dst = a.o + size_t(q0 + qi) * row_stride + h * hd;
+        for (int k = 0; k < ndim; ++k) dst[sub + 8 * k] = o[k] / lsum;
+    }
+}
+
+}  // namespace
+
+int attn_decode_splits(int kv_len, int hd) {
+    const int C = attn_chunk(hd);
+    return (kv_len + C - 1) / C;
+}
+
+size_t attn_decode_lds(int G, int hd) {
+    const int C = attn_chunk(hd);
+    return sizeof(float) * (size_t(G) * hd + size_t(C) * (hd + 1) + size_t(C) * hd + size_t(G) * C + 2 * G);
+}
+
+hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s) {
+    const size_t lds = attn_decode_lds(a.nh / a.nkv, a.hd);
+    hipLaunchKernelGGL(k_attn_decode, dim3(a.n_splits, a.nkv), dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t s) {
+    const size_t lds = sizeof(float) * (size_t(kQB) * (a.hd + 1) + size_t(kKT) * (a.hd + 1) +
+                                        size_t(kKT) * a.hd + size_t(kQB) * kKT);
+    dim3 grid((a.T + kQB - 1) / kQB, a.nh);
+    hipLaunchKernelGGL(k_attn_prefill, grid, dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace q8l

@@ -1,0 +1,121 @@
+// q8l_internal.h -- structures shared by the host runtime and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8l {
+
+constexpr int kThreads = 256;        // every kernel runs 256-thread workgroups (4 wave64)
+constexpr int kQK = 32;              // weights per Q8_0 block
+constexpr int kQBytes = 34;          // bytes per Q8_0 block
+constexpr int kPairBytes = 68;       // two blocks: the unit a lane decodes (4-byte aligned)
+constexpr int kPairWeights = 64;
+constexpr int kMaxTokChunk = 16;     // tokens per workgroup in the multi-token GEMV
+constexpr int kInlineTokens = 256;   // token ids passed in kernel arguments per launch
+constexpr int kAttnChunk = 64;       // keys per split in decode attention
+constexpr int kMaxGroup = 16;        // query heads per KV head supported in-kernel
+
+// Per-call step state, in device memory. Graph-replayed kernels read it
+// instead of kernel arguments, so one captured decode graph serves every step.
+struct StepState {
+    int32_t pos;        // rope position of token 0 (index_pos)
+    int32_t slot;       // KV slot of token 0 (positions cached before the call)
+    int32_t T;          // tokens in the call
+    int32_t step;       // generation step counter
+    uint32_t token;     // single-token input (decode)
+    int32_t advance;    // 1: after the argmax, token := argmax, pos++, slot++, step++
+    float *logits_out;  // lm_head destination
+    uint32_t *argmax_out;  // optional argmax destination
+    uint32_t *ids_out;     // generation: ids_out[step] := argmax
+};
+
+struct SetStateArgs {
+    int32_t pos, slot, T, step;
+    int32_t advance;
+    int32_t tok_offset, tok_count;   // tokens written to tok_buf[tok_offset ..)
+    int32_t set_header;              // 0: only copy tokens
+    float *logits_out;
+    uint32_t *argmax_out;
+    uint32_t *ids_out;
+    uint32_t tokens[kInlineTokens];
+};
+
+// How a GEMV walks one weight matrix: K = P pairs of blocks per row, taken in
+// chunks of PC pairs; a workgroup owns NR rows.
+struct GemvShape {
+    int K;        // weights per row
+    int P;        // 64-weight pairs per row
+    int PC;       // pairs per K-chunk (divides P)
+    int NR;       // rows per workgroup (NR * PC <= 256)
+    int rowbytes; // P * 68
+};
+
+// ---- launchers (k_*.hip) -------------------------------------------------
+
+struct LayerPtrs {
+    const uint8_t *wq, *wk, *wv, *wo, *wg, *wu, *wd;
+    const float *attn_norm, *ffn_norm;
+};
+
+struct Dims {
+    int H, nh, nkv, hd, F, V, max_seq;
+    float eps;
+};
+
+hipError_t launch_set_state(const SetStateArgs &a, StepState *st, uint32_t *tok_buf,
+                            hipStream_t s);
+hipError_t launch_rope_table(float2 *table, int max_seq, int hd, double theta, hipStream_t s);
+hipError_t launch_embed(const uint8_t *E, int H, int V, const StepState *st,
+                        const uint32_t *tok_buf, int T, int from_state_token, float *x,
+                        hipStream_t s);
+
+// q/k/v projections with RMSNorm in front, rope on q and k, k/v written to
+// the cache at slot+t. Tokens [0, T) in chunks of up to kMaxTokChunk.
+hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const StepState *st,
+                      const float2 *rope, float *q, float *kc, float *vc, int T,
+                      hipStream_t s);
+// Y[t] (+)= W U[t] for generic use (o-proj / down with accumulate = 1).
+hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
+                         const float *norm_w, float eps, int accumulate, float *Y,
+                         hipStream_t s);
+// h[t] = silu(Wg u[t]) * (Wu u[t]), u = rmsnorm(x[t]).
+hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, float *h, int T,
+                         hipStream_t s);
+// logits = Wout rmsnorm(x[T-1]); argmax by the last workgroup; state update.
+hipError_t launch_lmhead(const Dims &d, const uint8_t *Wout, const float *out_norm,
+                         const float *x_last, StepState *st, float *partials,
+                         uint32_t *counter, hipStream_t s);
+hipError_t launch_argmax(const float *x, int64_t n, uint32_t *out, float *partials,
+                         uint32_t *counter, hipStream_t s);
+size_t argmax_partials_bytes(int64_t n);
+
+// Decode attention (one query per head over kv_len keys, no mask).
+struct AttnDecodeArgs {
+    const float *q;      // [nh][hd]
+    const float *kc, *vc; // [nkv][kv_stride][hd]
+    float *o;            // [nh][hd]
+    float *part;         // [nh][max_splits][hd + 2]
+    uint32_t *counters;  // [nkv]
+    const StepState *st; // kv_len = st->slot + 1 when kv_len_arg < 0
+    int kv_len_arg;
+    int kv_stride, nh, nkv, hd;
+    int n_splits;        // workgroups per KV group launched
+    float scale;
+};
+hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s);
+int attn_decode_splits(int kv_len, int hd);
+__host__ __device__ int attn_chunk(int hd);
+size_t lmhead_partials_bytes(int V, int K);
+
+// Prefill attention: T queries, causal mask offset by the cached prefix.
+struct AttnPrefillArgs {
+    const float *q;        // [T][nh][hd]
+    const float *kc, *vc;  // [nkv][kv_stride][hd]
+    float *o;              // [T][nh][hd]
+    int T, kv_len, kv_stride, nh, nkv, hd;
+    float scale;
+};
+hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t s);
+
+}  // namespace q8l

@@ -1,0 +1,616 @@
+// runtime.cpp -- host side of the q8l C ABI: model object, tensor binding,
+// argument/state checks, workspace layout, kernel sequencing and the decode
+// graphs.
+//
+// The forward is the sequence the page "量化 llama 的一次前向" walks through
+// (section "forward：mask 什么时候建"): embedding; per layer attention block and
+// MLP block with residuals; final norm on the last position; output layer.
+// Kernels per layer: q/k/v (norm + rope + KV write fused), attention,
+// o-projection (+ residual), gate/up (norm + SiLU*up fused), down (+ residual).
+//
+// Decode (one token) runs as a captured HIP graph: every kernel reads the
+// position, slot and token from a device-side StepState, so one graph serves
+// every step. One graph is captured per power-of-two bucket of attention
+// splits (the host knows the cache length, so it picks the bucket); splits
+// beyond the keys present exit at once.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/q8l.h"
+#include "q8l_internal.h"
+
+namespace q8l {
+size_t lmhead_partials_bytes(int V, int K);
+__host__ __device__ int attn_chunk(int hd);
+size_t attn_decode_lds(int G, int hd);
+}  // namespace q8l
+
+using namespace q8l;
+
+namespace {
+
+const char *kVersion = "q8l 0.1 (gfx950)";
+
+size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Layout {
+    size_t state, counters, rope, tok, kc, vc, x, q, att, h, logits, lm_part, attn_part, total;
+    size_t kv_layer;  // floats per layer in kc (and vc)
+    int max_splits;
+};
+
+bool config_ok(const q8l_config *c, std::string *why) {
+    auto fail = [&](const char *m) {
+        if (why) *why = m;
+        return false;
+    };
+    if (!c) return fail("config is NULL");
+    if (c->n_layer < 1 || c->n_embd < 1 || c->n_head < 1 || c->n_head_kv < 1 || c->head_dim < 1 ||
+        c->n_ff < 1 || c->n_vocab < 1 || c->max_seq_len < 1)
+        return fail("every size in the config must be positive");
+    if (c->n_head % c->n_head_kv) return fail("n_head must be a multiple of n_head_kv");
+    if (c->n_head / c->n_head_kv > kMaxGroup) return fail("n_head / n_head_kv exceeds 16");
+    if (c->head_dim % 8 || c->head_dim > 128) return fail("head_dim must be a multiple of 8 and <= 128");
+    if (c->n_embd % 64 || c->n_ff % 64 || (c->n_head * c->head_dim) % 64)
+        return fail("n_embd, n_ff and n_head*head_dim must be multiples of 64");
+    if (c->n_head_kv > 255) return fail("n_head_kv must be <= 255");
+    if (!(c->rms_eps >= 0.0) || !(c->rope_theta > 0.0)) return fail("rms_eps >= 0 and rope_theta > 0 required");
+    return true;
+}
+
+Layout make_layout(const q8l_config *c) {
+    Layout L{};
+    const size_t S = size_t(c->max_seq_len), H = c->n_embd, QD = size_t(c->n_head) * c->head_dim;
+    const size_t hd = c->head_dim;
+    L.kv_layer = size_t(c->n_head_kv) * S * hd;
+    L.max_splits = (c->max_seq_len + attn_chunk(c->head_dim) - 1) / attn_chunk(c->head_dim);
+    int pow2 = 1;
+    while (pow2 < L.max_splits) pow2 <<= 1;
+    L.max_splits = pow2;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = al256(off + bytes);
+        return o;
+    };
+    L.state = take(sizeof(StepState));
+    L.counters = take(256 * sizeof(uint32_t));
+    L.rope = take(S * (hd / 2) * sizeof(float2));
+    L.tok = take(S * sizeof(uint32_t));
+    L.kc = take(size_t(c->n_layer) * L.kv_layer * 4);
+    L.vc = take(size_t(c->n_layer) * L.kv_layer * 4);
+    L.x = take(S * H * 4);
+    L.q = take(S * QD * 4);
+    L.att = take(S * QD * 4);
+    L.h = take(S * size_t(c->n_ff) * 4);
+    L.logits = take(size_t(c->n_vocab) * 4);
+    L.lm_part = take(std::max(lmhead_partials_bytes(c->n_vocab, c->n_embd), size_t(8)));
+    L.attn_part = take(size_t(c->n_head) * L.max_splits * (hd + 2) * 4);
+    L.total = off;
+    return L;
+}
+
+enum Slot { S_ATTN_NORM, S_WQ, S_WK, S_WV, S_WO, S_FFN_NORM, S_WG, S_WU, S_WD, S_NSLOT };
+const char *kLayerNames[S_NSLOT] = {"attn_norm", "attn_q", "attn_k", "attn_v", "attn_output",
+                                    "ffn_norm", "ffn_gate", "ffn_up", "ffn_down"};
+
+}  // namespace
+
+struct q8l_model {
+    q8l_config cfg;
+    Dims d;
+    Layout lay;
+    const uint8_t *tok_embd = nullptr, *output = nullptr;
+    const float *out_norm = nullptr;
+    std::vector<std::vector<const void *>> layer_ptrs;  // [L][S_NSLOT]
+    uint8_t *ws = nullptr;
+    size_t ws_bytes = 0;
+    bool finalized = false;
+    int32_t len = 0;
+    std::string err;
+    std::map<int, hipGraphExec_t> graphs;  // by split bucket
+    std::map<int, hipGraph_t> graph_defs;
+    hipStream_t cap = nullptr;
+
+    template <typename T>
+    T *at(size_t off) const {
+        return reinterpret_cast<T *>(ws + off);
+    }
+    StepState *state() const { return at<StepState>(lay.state); }
+    LayerPtrs layer(int l) const {
+        const auto &p = layer_ptrs[l];
+        LayerPtrs w;
+        w.attn_norm = static_cast<const float *>(p[S_ATTN_NORM]);
+        w.wq = static_cast<const uint8_t *>(p[S_WQ]);
+        w.wk = static_cast<const uint8_t *>(p[S_WK]);
+        w.wv = static_cast<const uint8_t *>(p[S_WV]);
+        w.wo = static_cast<const uint8_t *>(p[S_WO]);
+        w.ffn_norm = static_cast<const float *>(p[S_FFN_NORM]);
+        w.wg = static_cast<const uint8_t *>(p[S_WG]);
+        w.wu = static_cast<const uint8_t *>(p[S_WU]);
+        w.wd = static_cast<const uint8_t *>(p[S_WD]);
+        return w;
+    }
+    float *kc(int l) const { return at<float>(lay.kc) + size_t(l) * lay.kv_layer; }
+    float *vc(int l) const { return at<float>(lay.vc) + size_t(l) * lay.kv_layer; }
+};
+
+namespace {
+
+q8l_status fail(q8l_model *m, q8l_status st, const std::string &msg) {
+    if (m) m->err = msg;
+    return st;
+}
+
+q8l_status hip_fail(q8l_model *m, hipError_t e, const char *what) {
+    return fail(m, Q8L_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define Q8L_HIP(m, expr, what)                              \
+    do {                                                    \
+        hipError_t e_ = (expr);                             \
+        if (e_ != hipSuccess) return hip_fail((m), e_, what); \
+    } while (0)
+
+// The q/k/v ... down kernels of one layer plus the attention, for T tokens.
+hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_splits,
+                          hipStream_t s) {
+    const Dims &d = m->d;
+    const int QD = d.nh * d.hd;
+    StepState *st = m->state();
+    float *x = m->at<float>(m->lay.x), *q = m->at<float>(m->lay.q);
+    float *att = m->at<float>(m->lay.att), *h = m->at<float>(m->lay.h);
+    const float2 *rope = m->at<float2>(m->lay.rope);
+    hipError_t e;
+    for (int l = 0; l < m->cfg.n_layer; ++l) {
+        const LayerPtrs w = m->layer(l);
+        if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
+        if (T == 1) {
+            AttnDecodeArgs a;
+            a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.o = att;
+            a.part = m->at<float>(m->lay.attn_part);
+            a.counters = m->at<uint32_t>(m->lay.counters);
+            a.st = st; a.kv_len_arg = -1; a.kv_stride = d.max_seq;
+            a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = decode_splits;
+            a.scale = 1.0f / sqrtf(float(d.hd));
+            if ((e = launch_attn_decode(a, s)) != hipSuccess) return e;
+        } else {
+            AttnPrefillArgs a;
+            a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.o = att;
+            a.T = T; a.kv_len = kv_len_prefill; a.kv_stride = d.max_seq;
+            a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.scale = 1.0f / sqrtf(float(d.hd));
+            if ((e = launch_attn_prefill(a, s)) != hipSuccess) return e;
+        }
+        if ((e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s)) != hipSuccess) return e;
+        if ((e = launch_gateup(d, w, x, h, T, s)) != hipSuccess) return e;
+        if ((e = launch_matmul(w.wd, d.H, d.F, h, T, nullptr, d.eps, 1, x, s)) != hipSuccess) return e;
+    }
+    const uint8_t *wout = m->cfg.tied_output ? m->tok_embd : m->output;
+    return launch_lmhead(d, wout, m->out_norm, x + size_t(T - 1) * d.H, st,
+                         m->at<float>(m->lay.lm_part), m->at<uint32_t>(m->lay.counters) + 255, s);
+}
+
+int split_bucket(const q8l_model *m, int kv_len) {
+    const int need = (kv_len + attn_chunk(m->d.hd) - 1) / attn_chunk(m->d.hd);
+    int b = 1;
+    while (b < need) b <<= 1;
+    return std::min(b, m->lay.max_splits);
+}
+
+q8l_status decode_graph(q8l_model *m, int bucket, hipGraphExec_t *out) {
+    auto it = m->graphs.find(bucket);
+    if (it != m->graphs.end()) {
+        *out = it->second;
+        return Q8L_OK;
+    }
+    if (!m->cap) Q8L_HIP(m, hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking), "hipStreamCreate");
+    Q8L_HIP(m, hipStreamBeginCapture(m->cap, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
+    hipError_t e = launch_embed(m->tok_embd, m->d.H, m->d.V, m->state(), m->at<uint32_t>(m->lay.tok), 1, 1,
+                                m->at<float>(m->lay.x), m->cap);
+    if (e == hipSuccess) e = enqueue_layers(m, 1, -1, bucket, m->cap);
+    hipGraph_t g = nullptr;
+    hipError_t e2 = hipStreamEndCapture(m->cap, &g);
+    if (e != hipSuccess) {
+        if (g) hipGraphDestroy(g);
+        return hip_fail(m, e, "capturing the decode step");
+    }
+    if (e2 != hipSuccess) return hip_fail(m, e2, "hipStreamEndCapture");
+    hipGraphExec_t ex = nullptr;
+    e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        hipGraphDestroy(g);
+        return hip_fail(m, e, "hipGraphInstantiate");
+    }
+    m->graphs[bucket] = ex;
+    m->graph_defs[bucket] = g;
+    *out = ex;
+    return Q8L_OK;
+}
+
+bool parse_layer_name(const char *name, int *layer, int *slot) {
+    if (std::strncmp(name, "blk.", 4) != 0) return false;
+    const char *p = name + 4;
+    if (*p < '0' || *p > '9') return false;
+    long v = 0;
+    while (*p >= '0' && *p <= '9') {
+        v = v * 10 + (*p - '0');
+        if (v > 1000000) return false;
+        ++p;
+    }
+    if (*p != '.') return false;
+    ++p;
+    for (int s = 0; s < S_NSLOT; ++s) {
+        const size_t n = std::strlen(kLayerNames[s]);
+        if (std::strncmp(p, kLayerNames[s], n) == 0 && std::strcmp(p + n, ".weight") == 0) {
+            *layer = int(v);
+            *slot = s;
+            return true;
+        }
+    }
+    return false;
+}
+
+// The index_pos / cache-length contract, checked before any change.
+q8l_status check_positions(q8l_model *m, int32_t T, int32_t index_pos, int32_t *eff_len) {
+    const int32_t S = m->cfg.max_seq_len;
+    if (int64_t(index_pos) + T > S)
+        return fail(m, Q8L_E_POS_RANGE,
+                    "index_pos + n_tokens = " + std::to_string(int64_t(index_pos) + T) +
+                        " exceeds the rope table length " + std::to_string(S));
+    const int32_t len = index_pos == 0 ? 0 : m->len;
+    if (T > 1 && index_pos != len)
+        return fail(m, Q8L_E_POS_MISMATCH,
+                    "index_pos " + std::to_string(index_pos) + " != cached positions " +
+                        std::to_string(len) + " with " + std::to_string(T) + " tokens");
+    if (int64_t(len) + T > S)
+        return fail(m, Q8L_E_KV_FULL, "cached positions " + std::to_string(len) + " + " +
+                                          std::to_string(T) + " exceed " + std::to_string(S));
+    *eff_len = len;
+    return Q8L_OK;
+}
+
+q8l_status set_state(q8l_model *m, int pos, int slot, int T, int advance, float *logits,
+                     uint32_t *argmax, uint32_t *ids, const uint32_t *tokens, hipStream_t s) {
+    SetStateArgs a{};
+    a.pos = pos; a.slot = slot; a.T = T; a.step = 0; a.advance = advance;
+    a.logits_out = logits; a.argmax_out = argmax; a.ids_out = ids;
+    a.set_header = 1;
+    const int n = tokens ? T : 0;
+    int off = 0;
+    do {
+        a.tok_offset = off;
+        a.tok_count = std::min(n - off, kInlineTokens);
+        if (a.tok_count > 0) std::memcpy(a.tokens, tokens + off, sizeof(uint32_t) * a.tok_count);
+        Q8L_HIP(m, launch_set_state(a, m->state(), m->at<uint32_t>(m->lay.tok), s), "set_state");
+        a.set_header = 0;
+        off += std::max(a.tok_count, 0);
+    } while (off < n);
+    return Q8L_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *q8l_version(void) { return kVersion; }
+
+size_t q8l_workspace_bytes(const q8l_config *cfg) {
+    if (!config_ok(cfg, nullptr)) return 0;
+    return make_layout(cfg).total;
+}
+
+q8l_status q8l_create(const q8l_config *cfg, q8l_model **out) {
+    if (!out) return Q8L_E_INVALID_ARG;
+    *out = nullptr;
+    std::string why;
+    if (!config_ok(cfg, &why)) return Q8L_E_INVALID_ARG;
+    q8l_model *m = new q8l_model();
+    m->cfg = *cfg;
+    m->d.H = cfg->n_embd; m->d.nh = cfg->n_head; m->d.nkv = cfg->n_head_kv; m->d.hd = cfg->head_dim;
+    m->d.F = cfg->n_ff; m->d.V = cfg->n_vocab; m->d.max_seq = cfg->max_seq_len;
+    m->d.eps = float(cfg->rms_eps);
+    m->lay = make_layout(cfg);
+    m->layer_ptrs.assign(cfg->n_layer, std::vector<const void *>(S_NSLOT, nullptr));
+    *out = m;
+    return Q8L_OK;
+}
+
+q8l_status q8l_bind_tensor(q8l_model *m, const char *name, q8l_dtype dtype, int64_t rows,
+                           int64_t cols, const void *dev_ptr, size_t nbytes) {
+    if (!m) return Q8L_E_INVALID_ARG;
+    if (m->finalized) return fail(m, Q8L_E_NOT_FINALIZED, "weights are fixed after finalize");
+    if (!name || !dev_ptr) return fail(m, Q8L_E_INVALID_ARG, "name and dev_ptr must not be NULL");
+    if (reinterpret_cast<uintptr_t>(dev_ptr) & 15)
+        return fail(m, Q8L_E_INVALID_ARG, std::string(name) + ": pointer not 16-byte aligned");
+    const q8l_config &c = m->cfg;
+    const int64_t H = c.n_embd, QD = int64_t(c.n_head) * c.head_dim, KVD = int64_t(c.n_head_kv) * c.head_dim;
+    int64_t er = 0, ec = 0;
+    q8l_dtype et = Q8L_Q8_0;
+    const void **slot = nullptr;
+    int layer = -1, s = -1;
+    if (std::strcmp(name, "token_embd.weight") == 0) {
+        er = c.n_vocab; ec = H; slot = reinterpret_cast<const void **>(&m->tok_embd);
+    } else if (std::strcmp(name, "output.weight") == 0) {
+        if (c.tied_output) return fail(m, Q8L_E_INVALID_ARG, "output.weight given for a tied model");
+        er = c.n_vocab; ec = H; slot = reinterpret_cast<const void **>(&m->output);
+    } else if (std::strcmp(name, "output_norm.weight") == 0) {
+        er = 1; ec = H; et = Q8L_F32; slot = reinterpret_cast<const void **>(&m->out_norm);
+    } else if (parse_layer_name(name, &layer, &s)) {
+        if (layer >= c.n_layer) return fail(m, Q8L_E_INVALID_ARG, std::string(name) + ": layer out of range");
+        switch (s) {
+            case S_ATTN_NORM: case S_FFN_NORM: er = 1; ec = H; et = Q8L_F32; break;
+            case S_WQ: er = QD; ec = H; break;
+            case S_WK: case S_WV: er = KVD; ec = H; break;
+            case S_WO: er = H; ec = QD; break;
+            case S_WG: case S_WU: er = c.n_ff; ec = H; break;
+            case S_WD: er = H; ec = c.n_ff; break;
+        }
+        slot = &m->layer_ptrs[layer][s];
+    } else {
+        return fail(m, Q8L_E_INVALID_ARG, std::string("unknown tensor name ") + name);
+    }
+    const size_t want = et == Q8L_Q8_0 ? size_t(er * ec / kQK * kQBytes) : size_t(er * ec * 4);
+    if (dtype != et || rows != er || cols != ec || nbytes != want) {
+        char buf[256];
+        std::snprintf(buf, sizeof buf, "%s: expected %s [%lld, %lld] (%zu bytes), got %s [%lld, %lld] (%zu bytes)",
+                      name, et == Q8L_Q8_0 ? "Q8_0" : "F32", (long long)er, (long long)ec, want,
+                      dtype == Q8L_Q8_0 ? "Q8_0" : "F32", (long long)rows, (long long)cols, nbytes);
+        return fail(m, Q8L_E_SHAPE, buf);
+    }
+    *slot = dev_ptr;
+    return Q8L_OK;
+}
+
+q8l_status q8l_bind_workspace(q8l_model *m, void *dev_ptr, size_t nbytes) {
+    if (!m) return Q8L_E_INVALID_ARG;
+    if (m->finalized) return fail(m, Q8L_E_NOT_FINALIZED, "workspace is fixed after finalize");
+    if (!dev_ptr || (reinterpret_cast<uintptr_t>(dev_ptr) & 255))
+        return fail(m, Q8L_E_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+    if (nbytes < m->lay.total)
+        return fail(m, Q8L_E_INVALID_ARG, "workspace too small: need " + std::to_string(m->lay.total) +
+                                              " bytes, got " + std::to_string(nbytes));
+    m->ws = static_cast<uint8_t *>(dev_ptr);
+    m->ws_bytes = nbytes;
+    return Q8L_OK;
+}
+
+q8l_status q8l_finalize(q8l_model *m, void *stream) {
+    if (!m) return Q8L_E_INVALID_ARG;
+    if (m->finalized) return Q8L_OK;
+    if (!m->tok_embd) return fail(m, Q8L_E_MISSING_TENSOR, "cannot find token_embd.weight");
+    for (int l = 0; l < m->cfg.n_layer; ++l)
+        for (int s = 0; s < S_NSLOT; ++s)
+            if (!m->layer_ptrs[l][s])
+                return fail(m, Q8L_E_MISSING_TENSOR, "cannot find blk." + std::to_string(l) + "." +
+                                                         kLayerNames[s] + ".weight");
+    if (!m->out_norm) return fail(m, Q8L_E_MISSING_TENSOR, "cannot find output_norm.weight");
+    if (!m->cfg.tied_output && !m->output) return fail(m, Q8L_E_MISSING_TENSOR, "cannot find output.weight");
+    if (!m->ws) return fail(m, Q8L_E_MISSING_TENSOR, "no workspace bound");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Q8L_HIP(m, hipMemsetAsync(m->ws + m->lay.state, 0, m->lay.rope - m->lay.state, s), "clearing state");
+    Q8L_HIP(m, launch_rope_table(m->at<float2>(m->lay.rope), m->cfg.max_seq_len, m->cfg.head_dim,
+                                 m->cfg.rope_theta, s),
+            "building the rope table");
+    m->len = 0;
+    m->finalized = true;
+    return Q8L_OK;
+}
+
+q8l_status q8l_forward(q8l_model *m, const uint32_t *tokens_host, int32_t n_tokens,
+                       int32_t index_pos, float *logits_dev, uint32_t *argmax_dev, void *stream) {
+    if (!m) return Q8L_E_INVALID_ARG;
+    if (n_tokens < 1 || !tokens_host || index_pos < 0 || !logits_dev)
+        return fail(m, Q8L_E_INVALID_ARG, "need n_tokens >= 1, tokens, index_pos >= 0 and logits_dev");
+    for (int32_t i = 0; i < n_tokens; ++i)
+        if (tokens_host[i] >= uint32_t(m->cfg.n_vocab))
+            return fail(m, Q8L_E_INVALID_ARG, "token id " + std::to_string(tokens_host[i]) +
+                                                  " at " + std::to_string(i) + " >= n_vocab");
+    int32_t len;
+    q8l_status st = check_positions(m, n_tokens, index_pos, &len);
+    if (st != Q8L_OK) return st;
+    if (!m->finalized) return fail(m, Q8L_E_NOT_FINALIZED, "forward before finalize");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int T = n_tokens;
+    if (T == 1) {
+        hipGraphExec_t g;
+        if ((st = decode_graph(m, split_bucket(m, len + 1), &g)) != Q8L_OK) return st;
+        if ((st = set_state(m, index_pos, len, 1, 0, logits_dev, argmax_dev, nullptr, tokens_host, s)) != Q8L_OK)
+            return st;
+        Q8L_HIP(m, hipGraphLaunch(g, s), "hipGraphLaunch");
+    } else {
+        if ((st = set_state(m, index_pos, len, T, 0, logits_dev, argmax_dev, nullptr, tokens_host, s)) != Q8L_OK)
+            return st;
+        Q8L_HIP(m, launch_embed(m->tok_embd, m->d.H, m->d.V, m->state(), m->at<uint32_t>(m->lay.tok), T, 0,
+                                m->at<float>(m->lay.x), s),
+                "embedding");
+        Q8L_HIP(m, enqueue_layers(m, T, len + T, 0, s), "prefill");
+    }
+    m->len = len + T;
+    m->err.clear();
+    return Q8L_OK;
+}
+
+q8l_status q8l_generate(q8l_model *m, const uint32_t *token_dev, int32_t index_pos,
+                        int32_t n_steps, uint32_t *ids_dev, float *logits_dev, void *stream) {
+    if (!m) return Q8L_E_INVALID_ARG;
+    if (!token_dev || !ids_dev || n_steps < 1 || index_pos < 0)
+        return fail(m, Q8L_E_INVALID_ARG, "need token_dev, ids_dev, n_steps >= 1, index_pos >= 0");
+    const int32_t S = m->cfg.max_seq_len;
+    if (int64_t(index_pos) + n_steps > S)
+        return fail(m, Q8L_E_POS_RANGE, "index_pos + n_steps exceeds the rope table length");
+    const int32_t len = index_pos == 0 ? 0 : m->len;
+    if (int64_t(len) + n_steps > S) return fail(m, Q8L_E_KV_FULL, "cache would overflow");
+    if (!m->finalized) return fail(m, Q8L_E_NOT_FINALIZED, "generate before finalize");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<hipGraphExec_t> gs(n_steps);
+    for (int k = 0; k < n_steps; ++k) {
+        q8l_status st = decode_graph(m, split_bucket(m, len + k + 1), &gs[k]);
+        if (st != Q8L_OK) return st;
+    }
+    float *lg = logits_dev ? logits_dev : m->at<float>(m->lay.logits);
+    q8l_status st = set_state(m, index_pos, len, 1, 1, lg, nullptr, ids_dev, nullptr, s);
+    if (st != Q8L_OK) return st;
+    Q8L_HIP(m, hipMemcpyAsync(&m->state()->token, token_dev, sizeof(uint32_t), hipMemcpyDeviceToDevice, s),
+            "token copy");
+    for (int k = 0; k < n_steps; ++k) Q8L_HIP(m, hipGraphLaunch(gs[k], s), "hipGraphLaunch");
+    m->len = len + n_steps;
+    m->err.clear();
+    return Q8L_OK;
+}
+
+q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, void *stream) {
+    if (!m) return Q8L_E_INVALID_ARG;
+    if (!m->finalized) return fail(m, Q8L_E_NOT_FINALIZED, "timing before finalize");
+    if (reps < 1 || !ms_out || m->len + 1 > m->cfg.max_seq_len)
+        return fail(m, Q8L_E_INVALID_ARG, "need reps >= 1, ms_out, and a free cache slot");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Dims &d = m->d;
+    const int QD = d.nh * d.hd;
+    const int kv_len = m->len + 1;
+    q8l_status st = set_state(m, m->len, m->len, 1, 0, m->at<float>(m->lay.logits), nullptr, nullptr,
+                              nullptr, s);
+    if (st != Q8L_OK) return st;
+    StepState *S = m->state();
+    float *x = m->at<float>(m->lay.x), *q = m->at<float>(m->lay.q);
+    float *att = m->at<float>(m->lay.att), *h = m->at<float>(m->lay.h);
+    const LayerPtrs w = m->layer(0);
+    const uint8_t *wout = m->cfg.tied_output ? m->tok_embd : m->output;
+    AttnDecodeArgs a;
+    a.q = q; a.kc = m->kc(0); a.vc = m->vc(0); a.o = att;
+    a.part = m->at<float>(m->lay.attn_part);
+    a.counters = m->at<uint32_t>(m->lay.counters);
+    a.st = S; a.kv_len_arg = -1; a.kv_stride = d.max_seq;
+    a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = split_bucket(m, kv_len);
+    a.scale = 1.0f / sqrtf(float(d.hd));
+    auto launch = [&](int kind) -> hipError_t {
+        switch (kind) {
+            case 0: return launch_embed(m->tok_embd, d.H, d.V, S, m->at<uint32_t>(m->lay.tok), 1, 1, x, s);
+            case 1: return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
+            case 2: return launch_attn_decode(a, s);
+            case 3: return launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, x, s);
+            case 4: return launch_gateup(d, w, x, h, 1, s);
+            case 5: return launch_matmul(w.wd, d.H, d.F, h, 1, nullptr, d.eps, 1, x, s);
+            default:
+                return launch_lmhead(d, wout, m->out_norm, x, S, m->at<float>(m->lay.lm_part),
+                                     m->at<uint32_t>(m->lay.counters) + 255, s);
+        }
+    };
+    constexpr int kKinds = 7;
+    std::vector<hipEvent_t> ev(size_t(2) * reps * kKinds, nullptr);
+    for (auto &e : ev) Q8L_HIP(m, hipEventCreate(&e), "hipEventCreate");
+    hipError_t err = hipSuccess;
+    for (int k = 0; k < kKinds && err == hipSuccess; ++k)
+        for (int r = 0; r < reps && err == hipSuccess; ++r) {
+            hipEvent_t *p = &ev[(size_t(k) * reps + r) * 2];
+            if ((err = hipEventRecord(p[0], s)) != hipSuccess) break;
+            if ((err = launch(k)) != hipSuccess) break;
+            err = hipEventRecord(p[1], s);
+        }
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    for (int k = 0; k < kKinds && err == hipSuccess; ++k) {
+        double sum = 0.0;
+        for (int r = 0; r < reps; ++r) {
+            float ms = 0.f;
+            hipEvent_t *p = &ev[(size_t(k) * reps + r) * 2];
+            if ((err = hipEventElapsedTime(&ms, p[0], p[1])) != hipSuccess) break;
+            sum += ms;
+        }
+        ms_out[k] = float(sum / reps);
+    }
+    for (auto &e : ev)
+        if (e) hipEventDestroy(e);
+    if (err != hipSuccess) return hip_fail(m, err, "timing decode kernels");
+    return Q8L_OK;
+}
+
+q8l_status q8l_clear_kv_cache(q8l_model *m) {
+    if (!m) return Q8L_E_INVALID_ARG;
+    m->len = 0;
+    return Q8L_OK;
+}
+
+int32_t q8l_cache_len(const q8l_model *m) { return m ? m->len : -1; }
+
+const char *q8l_last_error(const q8l_model *m) { return m ? m->err.c_str() : "model is NULL"; }
+
+void q8l_destroy(q8l_model *m) {
+    if (!m) return;
+    for (auto &kv : m->graphs) hipGraphExecDestroy(kv.second);
+    for (auto &kv : m->graph_defs) hipGraphDestroy(kv.second);
+    if (m->cap) hipStreamDestroy(m->cap);
+    delete m;
+}
+
+// ---------------------------------------------------------------- single ops
+
+q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *X, int64_t T,
+                              const float *norm_w, double eps, int32_t accumulate, float *Y,
+                              void *stream) {
+    if (!W || !X || !Y || N < 1 || K < 64 || K % 64 || T < 1 || N > (1 << 30) || K > (1 << 24) ||
+        T > (1 << 20) || (reinterpret_cast<uintptr_t>(W) & 15) || (reinterpret_cast<uintptr_t>(X) & 15) ||
+        (norm_w && (reinterpret_cast<uintptr_t>(norm_w) & 15)))
+        return Q8L_E_INVALID_ARG;
+    hipError_t e = launch_matmul(static_cast<const uint8_t *>(W), int(N), int(K), X, int(T), norm_w,
+                                 float(eps), accumulate, Y, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8L_OK : Q8L_E_HIP;
+}
+
+size_t q8l_op_attention_workspace(int32_t T, int32_t kv_len, int32_t n_head, int32_t n_head_kv,
+                                  int32_t hd) {
+    if (T != 1 || kv_len < 1 || n_head < 1 || hd < 8) return 256;
+    const int splits = (kv_len + attn_chunk(hd) - 1) / attn_chunk(hd);
+    return al256(256 * 4) + al256(size_t(n_head) * splits * (hd + 2) * 4);
+}
+
+q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int32_t T,
+                            int32_t kv_len, int32_t kv_stride, int32_t n_head, int32_t n_head_kv,
+                            int32_t hd, float *O, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    if (!Q || !K || !V || !O || T < 1 || kv_len < T || kv_stride < kv_len || n_head < 1 ||
+        n_head_kv < 1 || n_head % n_head_kv || n_head / n_head_kv > kMaxGroup || hd % 8 || hd > 128 ||
+        n_head_kv > 255)
+        return Q8L_E_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (T == 1) {
+        if (!workspace || workspace_bytes < q8l_op_attention_workspace(T, kv_len, n_head, n_head_kv, hd))
+            return Q8L_E_INVALID_ARG;
+        AttnDecodeArgs a;
+        a.q = Q; a.kc = K; a.vc = V; a.o = O;
+        a.counters = static_cast<uint32_t *>(workspace);
+        a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + al256(256 * 4));
+        a.st = nullptr; a.kv_len_arg = kv_len; a.kv_stride = kv_stride;
+        a.nh = n_head; a.nkv = n_head_kv; a.hd = hd;
+        a.n_splits = (kv_len + attn_chunk(hd) - 1) / attn_chunk(hd);
+        a.scale = 1.0f / sqrtf(float(hd));
+        if ((e = hipMemsetAsync(workspace, 0, 256 * 4, s)) != hipSuccess) return Q8L_E_HIP;
+        e = launch_attn_decode(a, s);
+    } else {
+        AttnPrefillArgs a;
+        a.q = Q; a.kc = K; a.vc = V; a.o = O; a.T = T; a.kv_len = kv_len; a.kv_stride = kv_stride;
+        a.nh = n_head; a.nkv = n_head_kv; a.hd = hd; a.scale = 1.0f / sqrtf(float(hd));
+        e = launch_attn_prefill(a, s);
+    }
+    return e == hipSuccess ? Q8L_OK : Q8L_E_HIP;
+}
+
+q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    if (!x || !out || n < 1 || n > (int64_t(1) << 31) || !workspace ||
+        workspace_bytes < 256 + argmax_partials_bytes(n))
+        return Q8L_E_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t *counter = static_cast<uint32_t *>(workspace);
+    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + 256);
+    if (hipMemsetAsync(counter, 0, 4, s) != hipSuccess) return Q8L_E_HIP;
+    return launch_argmax(x, n, out, part, counter, s) == hipSuccess ? Q8L_OK : Q8L_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+"""Q8Model: place a model's tensors in device memory and drive the library.
+
+Argument marshalling only: the forward pass runs in libq8l.so's kernels.
+"""
+
+from __future__ import annotations
+
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import q8l as C
+
+
+class Q8Model:
+    """A model bound to the library.
+
+    ``config`` is a dict of q8l_config fields; ``tensors`` yields objects with
+    ``name``, ``dtype`` ('q8_0' or 'f32'), ``rows``, ``cols`` and ``data``
+    (a host numpy array of the raw bytes / f32 values).
+    """
+
+    def __init__(self, config: dict, tensors: Iterable, device: str = "cuda:0", stream=None):
+        import torch
+
+        self.torch = torch
+        self.device = torch.device(device)
+        self.cfg = C.q8l_config(**config)
+        self.n_vocab = self.cfg.n_vocab
+        nbytes = C.q8l_workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise C.Q8LError(C.Q8L_E_INVALID_ARG, "invalid config")
+        self.handle = C.q8l_create(self.cfg)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.buffers = {}
+        for t in tensors:
+            arr = np.ascontiguousarray(t.data)
+            dev = torch.from_numpy(arr.view(np.uint8).reshape(-1)).to(self.device)
+            self.buffers[t.name] = dev
+            dt = C.Q8L_Q8_0 if t.dtype == "q8_0" else C.Q8L_F32
+            self._check(C.q8l_bind_tensor(self.handle, t.name, dt, t.rows, t.cols, dev, dev.numel()))
+        self._check(C.q8l_bind_workspace(self.handle, self.workspace, nbytes))
+        self._check(C.q8l_finalize(self.handle, stream))
+        self.logits = torch.empty(self.n_vocab, dtype=torch.float32, device=self.device)
+        self.argmax = torch.zeros(1, dtype=torch.int32, device=self.device)
+
+    def _check(self, st: int) -> None:
+        if st != C.Q8L_OK:
+            raise C.Q8LError(st, C.q8l_last_error(self.handle))
+
+    def forward_async(self, tokens: Sequence[int], index_pos: int, stream=None) -> int:
+        """Enqueue forward(tokens, index_pos); returns the status (no raise)."""
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).astype(np.uint32))
+        return C.q8l_forward(self.handle, toks, int(toks.size), int(index_pos), self.logits,
+                             self.argmax, stream)
+
+    def forward(self, tokens: Sequence[int], index_pos: int, stream=None) -> Tuple[np.ndarray, int]:
+        """Run forward and wait; returns (f32 logits on the host, argmax)."""
+        self._check(self.forward_async(tokens, index_pos, stream))
+        self.torch.cuda.synchronize(self.device)
+        return self.logits.cpu().numpy(), int(self.argmax.item())
+
+    def generate_async(self, token_dev, index_pos: int, n_steps: int, ids_dev, stream=None) -> int:
+        return C.q8l_generate(self.handle, token_dev, int(index_pos), int(n_steps), ids_dev,
+                              self.logits, stream)
+
+    def clear_kv_cache(self) -> None:
+        self._check(C.q8l_clear_kv_cache(self.handle))
+
+    @property
+    def cache_len(self) -> int:
+        return C.q8l_cache_len(self.handle)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            C.q8l_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,169 @@
+"""End-to-end GPU parity of the forward pass against the CPU oracle, and the
+index_pos / KV-cache contract, through the C ABI (Q8Model only marshals)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_logits_close, compare_generation, gpu_model, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    w, m, prompt = synth.workload_inputs("C1")
+    return m, prompt, gpu_model(m)
+
+
+def test_tiny_generation_matches_oracle(tiny):
+    m, prompt, gm = tiny
+    ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 20, "tiny 13+20")
+    log(f"tiny: max abs err {err:.3g}, near ties {ties}, ids {ids[:8]}...")
+    assert ties <= 1
+
+
+def test_135m_generation_matches_oracle():
+    w, m, prompt = synth.workload_inputs("C2")
+    gm = gpu_model(m)
+    ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 20, "135m 13+20")
+    log(f"135m 13+20: max abs err {err:.3g}, near ties {ties}")
+    assert ties <= 1
+
+
+def test_135m_203_prompt_128_steps():
+    w, m, prompt = synth.workload_inputs("C3")
+    gm = gpu_model(m)
+    ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 128, "135m 203+128")
+    log(f"135m 203+128: max abs err {err:.3g}, near ties {ties}")
+    assert ties <= 2
+
+
+def test_chunked_prefill_and_reset(tiny):
+    m, prompt, gm = tiny
+    gm.clear_kv_cache()
+    one, _ = gm.forward(prompt, 0)
+    gm.forward(prompt[:8], 0)
+    two, _ = gm.forward(prompt[8:], 8)
+    assert_logits_close(two, one, "chunked vs single")
+    # index_pos == 0 drops the cache: identical to a fresh prefill (bitwise)
+    gm.forward([5], 13)
+    again, _ = gm.forward(prompt, 0)
+    assert np.array_equal(again, one)
+    assert gm.cache_len == 13
+
+
+def test_position_errors_leave_state_unchanged(tiny):
+    from quantized_q8_gemv_amd import q8l as C
+    m, prompt, gm = tiny
+    gm.forward(prompt[:8], 0)
+    assert gm.forward_async(prompt[8:], 5) == C.Q8L_E_POS_MISMATCH
+    assert gm.cache_len == 8
+    two, _ = gm.forward(prompt[8:], 8)                     # the right counter still works
+    om = oracle.OracleModel(m)
+    om.forward(prompt[:8], 0)
+    _, ref, _ = om.forward(prompt[8:], 8)
+    assert_logits_close(two, ref, "after a rejected call")
+    gm.clear_kv_cache()
+    assert gm.forward_async(prompt, 33) == C.Q8L_E_POS_MISMATCH
+    assert gm.forward_async([1], m.shape.max_seq_len) == C.Q8L_E_POS_RANGE
+    assert gm.cache_len == 0
+
+
+def test_single_token_misuse_matches_oracle(tiny):
+    """T == 1 with a stale counter is not an error; both sides compute the same thing."""
+    m, prompt, gm = tiny
+    om = oracle.OracleModel(m)
+    gm.forward(prompt, 0)
+    om.forward(prompt, 0)
+    for tok, p in ((7, 113), (9, 10), (3, 0), (4, 1)):
+        g, _ = gm.forward([tok], p)
+        st, ref, _ = om.forward([tok], p)
+        assert st == oracle.OK
+        assert_logits_close(g, ref, f"misuse p={p}")
+        assert gm.cache_len == om.cache_len
+
+
+def test_kv_full():
+    from quantized_q8_gemv_amd import q8l as C
+    s = synth.micro_shape(n_layer=1, n_embd=64, n_head=4, n_head_kv=2, head_dim=16, n_ff=128,
+                          n_vocab=64, max_seq_len=16)
+    m = synth.random_model(s, 2)
+    gm = gpu_model(m)
+    om = oracle.OracleModel(m)
+    toks = list(range(16))
+    g, _ = gm.forward(toks, 0)
+    _, ref, _ = om.forward(toks, 0)
+    assert_logits_close(g, ref, "full cache")
+    assert gm.forward_async([1], 3) == C.Q8L_E_KV_FULL
+    assert gm.cache_len == 16
+
+
+def test_decode_is_deterministic(tiny):
+    m, prompt, gm = tiny
+    runs = []
+    for _ in range(2):
+        gm.forward(prompt, 0)
+        outs = [gm.forward([i + 1], 13 + i)[0] for i in range(5)]
+        runs.append(np.stack(outs))
+    assert np.array_equal(runs[0], runs[1])
+
+
+def test_device_generation_equals_host_loop(tiny):
+    m, prompt, gm = tiny
+    lg, first = gm.forward(prompt, 0)
+    host_ids, host_last = [first], None
+    for k in range(12):
+        host_last, nxt = gm.forward([host_ids[-1]], 13 + k)
+        host_ids.append(nxt)
+    gm.forward(prompt, 0)
+    tok = torch.tensor([first], dtype=torch.int32, device="cuda:0")
+    ids = torch.zeros(12, dtype=torch.int32, device="cuda:0")
+    from quantized_q8_gemv_amd import q8l as C
+    assert gm.generate_async(tok, 13, 12, ids) == C.Q8L_OK
+    torch.cuda.synchronize()
+    assert ids.cpu().numpy().tolist() == host_ids[1:]
+    assert np.array_equal(gm.logits.cpu().numpy(), host_last)
+    assert gm.cache_len == 25
+
+
+def test_long_context_prefill_and_decode_to_the_table_end():
+    """4000-token prefill + decode to position 4095 at the 135M widths (2 layers)."""
+    from quantized_q8_gemv_amd import q8l as C
+    s = synth.ModelShape("135m-width-2layer", n_layer=2, n_embd=576, n_head=9, n_head_kv=3,
+                         head_dim=64, n_ff=1536, n_vocab=49152)
+    m = synth.random_model(s, 4)
+    prompt = synth.prompt_ids(s.n_vocab, 4000, 5)
+    gm = gpu_model(m)
+    om = oracle.OracleModel(m)
+    log("long context: prefill 4000")
+    g, gid = gm.forward(prompt, 0)
+    _, ref, _ = om.forward(prompt, 0)
+    assert_logits_close(g, ref, "prefill 4000")
+    tok = oracle.argmax(ref)
+    for p in range(4000, 4096):
+        g, _ = gm.forward([tok], p)
+        _, ref, _ = om.forward([tok], p)
+        assert_logits_close(g, ref, f"decode at {p}")
+        tok = oracle.argmax(ref)
+    assert gm.cache_len == 4096
+    assert gm.forward_async([tok], 4096) == C.Q8L_E_POS_RANGE
+
+
+def test_big_gqa_shape_two_layers():
+    """hidden 4096, 32/8 heads, head_dim 128, FFN 14336, vocab 32000 untied (2 layers)."""
+    s = synth.ModelShape("7b-width-2layer", n_layer=2, n_embd=4096, n_head=32, n_head_kv=8,
+                         head_dim=128, n_ff=14336, n_vocab=32000, tied_output=False)
+    m = synth.random_model(s, 6)
+    prompt = synth.prompt_ids(s.n_vocab, 64, 7)
+    gm = gpu_model(m)
+    ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 4, "7b-width 64+4")
+    log(f"7b-width: max abs err {err:.3g}")

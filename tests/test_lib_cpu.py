@@ -1,0 +1,104 @@
+"""Host-side checks of libq8l.so that need no GPU: it loads, exports every
+function include/q8l.h declares, and rejects bad configs, bindings and
+positions before touching the device."""
+
+import ctypes
+
+import pytest
+
+import synth
+from quantized_q8_gemv_amd import q8l as C
+
+
+def test_library_exports_every_declared_function():
+    lib = C.lib()
+    names = C.header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in C.q8l_version()
+
+
+def cfg_of(shape):
+    return C.config_from(synth.shape_fields(shape))
+
+
+def test_workspace_bytes_cover_the_kv_arena():
+    s = synth.SMOL135M
+    ws = C.q8l_workspace_bytes(cfg_of(s))
+    kv = s.n_layer * 2 * s.n_head_kv * s.max_seq_len * s.head_dim * 4
+    assert kv == 188_743_680
+    assert ws > kv
+    assert C.q8l_workspace_bytes(cfg_of(synth.BIG_GQA)) > 32 * 2 * 8 * 4096 * 128 * 4
+
+
+@pytest.mark.parametrize("field,value", [("n_head_kv", 2), ("head_dim", 6), ("n_embd", 96),
+                                         ("n_layer", 0), ("head_dim", 256), ("rope_theta", 0.0)])
+def test_invalid_configs_rejected(field, value):
+    f = synth.shape_fields(synth.TINY)
+    f[field] = value
+    cfg = C.config_from(f)
+    assert C.q8l_workspace_bytes(cfg) == 0
+    with pytest.raises(C.Q8LError):
+        C.q8l_create(cfg)
+
+
+FAKE = 1 << 20  # a 16-byte aligned address; never dereferenced by these checks
+
+
+@pytest.fixture
+def tiny_handle():
+    h = C.q8l_create(cfg_of(synth.TINY))
+    yield h
+    C.q8l_destroy(h)
+
+
+def test_bind_checks(tiny_handle):
+    h = tiny_handle
+    s = synth.TINY
+    nb = s.n_vocab * s.n_embd // 32 * 34
+    assert C.q8l_bind_tensor(h, "token_embd.weight", C.Q8L_Q8_0, s.n_vocab, s.n_embd, FAKE, nb) == C.Q8L_OK
+    assert C.q8l_bind_tensor(h, "token_embd.weight", C.Q8L_Q8_0, s.n_vocab, s.n_embd, FAKE, nb + 1) == C.Q8L_E_SHAPE
+    assert C.q8l_bind_tensor(h, "token_embd.weight", C.Q8L_F32, s.n_vocab, s.n_embd, FAKE, nb) == C.Q8L_E_SHAPE
+    assert C.q8l_bind_tensor(h, "blk.0.attn_q.weight", C.Q8L_Q8_0, 576, 576, FAKE + 4, 576 * 18 * 34) == C.Q8L_E_INVALID_ARG
+    assert C.q8l_bind_tensor(h, "blk.4.attn_q.weight", C.Q8L_Q8_0, 576, 576, FAKE, 576 * 18 * 34) == C.Q8L_E_INVALID_ARG
+    assert C.q8l_bind_tensor(h, "blk.0.attn_qq.weight", C.Q8L_Q8_0, 576, 576, FAKE, 576 * 18 * 34) == C.Q8L_E_INVALID_ARG
+    assert C.q8l_bind_tensor(h, "output.weight", C.Q8L_Q8_0, s.n_vocab, s.n_embd, FAKE, nb) == C.Q8L_E_INVALID_ARG
+    assert C.q8l_bind_tensor(h, "blk.3.ffn_down.weight", C.Q8L_Q8_0, 576, 1536, FAKE, 576 * 48 * 34) == C.Q8L_OK
+    assert C.q8l_bind_tensor(h, "blk.3.ffn_norm.weight", C.Q8L_F32, 1, 576, FAKE, 576 * 4) == C.Q8L_OK
+
+
+def test_finalize_names_the_first_missing_tensor(tiny_handle):
+    h = tiny_handle
+    s = synth.TINY
+    for name, dt, r, c in s.tensor_specs():
+        if name == "blk.2.ffn_up.weight":
+            continue
+        nbytes = s.tensor_nbytes(dt, r, c)
+        st = C.q8l_bind_tensor(h, name, C.Q8L_Q8_0 if dt == "q8_0" else C.Q8L_F32, r, c, FAKE, nbytes)
+        assert st == C.Q8L_OK, (name, C.q8l_last_error(h))
+    assert C.q8l_finalize(h, 0) == C.Q8L_E_MISSING_TENSOR
+    assert "cannot find blk.2.ffn_up.weight" in C.q8l_last_error(h)
+
+
+def test_tensor_count_required_at_the_135m_shape(golden_printed):
+    assert len(synth.SMOL135M.tensor_specs()) == golden_printed["gguf_tensor_count"]
+
+
+def test_forward_argument_and_position_checks_precede_device_work(tiny_handle):
+    h = tiny_handle
+    s = synth.TINY
+    toks = (ctypes.c_uint32 * 13)(*range(13))
+    bad = (ctypes.c_uint32 * 1)(s.n_vocab)
+    lib = C.lib()
+    fwd = lambda t, n, p: lib.q8l_forward(h, ctypes.cast(t, ctypes.c_void_p), n, p, FAKE, None, None)
+    assert fwd(toks, 0, 0) == C.Q8L_E_INVALID_ARG
+    assert fwd(bad, 1, 0) == C.Q8L_E_INVALID_ARG
+    assert fwd(toks, 1, -1) == C.Q8L_E_INVALID_ARG
+    assert fwd(toks, 1, s.max_seq_len) == C.Q8L_E_POS_RANGE
+    assert fwd(toks, 2, s.max_seq_len - 1) == C.Q8L_E_POS_RANGE
+    assert fwd(toks, 5, 5) == C.Q8L_E_POS_MISMATCH      # nothing cached yet
+    assert C.q8l_cache_len(h) == 0
+    assert fwd(toks, 13, 0) == C.Q8L_E_NOT_FINALIZED
+    assert C.q8l_cache_len(h) == 0
+    assert C.q8l_clear_kv_cache(h) == C.Q8L_OK
