@@ -39,10 +39,11 @@ PEAK_HBM_GBS = 8000.0
 # 20 decode steps after a 13-token prompt, 2.6 ms mean per step incl. the argmax
 # readback, on an Apple M2 Max -- another machine, quoted as context.
 PAGES_DECODE_MS = {"C2": 2.6}
-KIND_NAMES = ["embed", "qkv_rope_kv", "attn_decode", "oproj_residual", "gateup_silu",
-              "down_residual", "lmhead_argmax"]
-KERNEL_SYMBOLS = ["k_embed", "k_qkv<1>", "k_attn_decode", "k_matmul<1>", "k_gateup<1>",
-                  "k_matmul<1>", "k_lmhead"]
+KIND_NAMES = ["embed", "qkv_rope_kv", "attn_decode", "oproj_combine_residual", "gateup_silu",
+              "down_residual", "lmhead", "argmax_finish"]
+KERNEL_SYMBOLS = ["k_embed", "k_qkv", "k_attn_decode", "k_matmul<1, 1, false>", "k_gateup",
+                  "k_matmul<1, 0, *>", "k_lmhead", "k_argmax_finish"]
+NKINDS = len(KIND_NAMES)
 
 
 def eprint(*a):
@@ -71,11 +72,12 @@ def kernel_bytes(s, kv_len):
     return [
         q8_bytes(1, H) + H * 4,
         q8_bytes(QD + 2 * KVD, H) + 2 * H * 4 + (QD + 2 * KVD) * 4,
-        kv_len * s.n_head_kv * s.head_dim * 4 * 2 + 2 * QD * 4,
+        kv_len * s.n_head_kv * s.head_dim * 4 * 2 + QD * 4,
         q8_bytes(H, QD) + QD * 4 + 2 * H * 4,
         2 * q8_bytes(F, H) + 2 * H * 4 + F * 4,
         q8_bytes(H, F) + F * 4 + 2 * H * 4,
         q8_bytes(V, H) + 2 * H * 4 + V * 4,
+        0,
     ]
 
 
@@ -185,18 +187,18 @@ def main():
     # Per-kernel launch times (HIP events on the stream the kernels run on).
     assert gm.forward_async(prompt, 0) == C.Q8L_OK
     torch.cuda.synchronize()
-    ms = (ctypes.c_float * 7)()
+    ms = (ctypes.c_float * NKINDS)()
     st = C.lib().q8l_time_decode_kernels(gm.handle, args.kernel_reps, ms,
                                          torch.cuda.current_stream().cuda_stream)
     assert st == C.Q8L_OK, C.q8l_last_error(gm.handle)
     kv_len = len(prompt) + 1
     kb = kernel_bytes(s, kv_len)
-    launches = [1, s.n_layer, s.n_layer, s.n_layer, s.n_layer, s.n_layer, 1]
-    per_step = [ms[i] * launches[i] for i in range(7)]
-    dom = max(range(7), key=lambda i: per_step[i])
+    launches = [1, s.n_layer, s.n_layer, s.n_layer, s.n_layer, s.n_layer, 1, 1]
+    per_step = [ms[i] * launches[i] for i in range(NKINDS)]
+    dom = max(range(NKINDS), key=lambda i: per_step[i])
     kernels = {KIND_NAMES[i]: {"us": round(ms[i] * 1e3, 2), "bytes": kb[i],
                                "gbs": round(kb[i] / (ms[i] * 1e-3) / 1e9, 1),
-                               "launches_per_token": launches[i]} for i in range(7)}
+                               "launches_per_token": launches[i]} for i in range(NKINDS)}
     achieved = kb[dom] / (ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,

@@ -217,17 +217,19 @@ q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int3
 size_t q8l_op_attention_workspace(int32_t T, int32_t kv_len, int32_t n_head, int32_t n_head_kv,
                                   int32_t hd);
 
-/* Largest element of x (f32[n], device), lowest index on ties, to *out. */
+/* Largest element of x (f32[n], device), lowest index on ties, to *out.
+ * workspace_bytes >= 8 * ceil(n / 4096). */
 q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspace,
                          size_t workspace_bytes, void *stream);
 
 /*
  * Measurement: launch each kernel of one decode step on its own, `reps`
  * times, each launch between two HIP events on `stream`, and write the mean
- * duration in milliseconds to ms_out[kind], kinds
- *   0 embedding, 1 q/k/v (+norm, rope, KV write), 2 attention,
- *   3 o-projection (+residual), 4 gate/up (+norm, SiLU*up),
- *   5 down (+residual), 6 output layer (+norm, argmax).
+ * duration in milliseconds to ms_out[kind] (ms_out holds 8 floats), kinds
+ *   0 embedding, 1 q/k/v (+norm, rope, KV write), 2 attention (split
+ *   partials), 3 o-projection (+partial merge, residual), 4 gate/up (+norm,
+ *   SiLU*up), 5 down (+residual), 6 output layer (+norm, per-workgroup
+ *   argmax), 7 argmax merge.
  * Layer 0's weights are used, at the current cache length (attention over
  * cache_len + 1 keys). The residual stream, the next KV slot and the logits
  * buffer are scratch afterwards: the next forward rewrites them before use.

@@ -48,6 +48,40 @@ __device__ __forceinline__ void decode_pair(const uint32_t *w, PairQ &o) {
     }
 }
 
+// One pair against one activation row, decoding on the fly (no 64-float
+// array: keeps register use low). Same summation order as decode_pair +
+// block_dot: per block four interleaved partial sums, (s0 + s1) + (s2 + s3).
+__device__ __forceinline__ void pair_dot1(const uint32_t *w, const float *x, float &dA, float &sA,
+                                          float &dB, float &sB) {
+    uint32_t prev = w[0];
+    dA = half_bits_to_float(prev);
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t nxt = w[j + 1];
+        const uint32_t q = __builtin_amdgcn_alignbyte(nxt, prev, 2);
+        const float4 xv = *reinterpret_cast<const float4 *>(x + 4 * j);
+        s0 = fmaf(sbyte(q, 0), xv.x, s0);
+        s1 = fmaf(sbyte(q, 1), xv.y, s1);
+        s2 = fmaf(sbyte(q, 2), xv.z, s2);
+        s3 = fmaf(sbyte(q, 3), xv.w, s3);
+        prev = nxt;
+    }
+    sA = (s0 + s1) + (s2 + s3);
+    dB = half_bits_to_float(prev >> 16);
+    s0 = s1 = s2 = s3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t q = w[9 + j];
+        const float4 xv = *reinterpret_cast<const float4 *>(x + 32 + 4 * j);
+        s0 = fmaf(sbyte(q, 0), xv.x, s0);
+        s1 = fmaf(sbyte(q, 1), xv.y, s1);
+        s2 = fmaf(sbyte(q, 2), xv.z, s2);
+        s3 = fmaf(sbyte(q, 3), xv.w, s3);
+    }
+    sB = (s0 + s1) + (s2 + s3);
+}
+
 // d * sum_i q[i] x[i] over one 32-weight block, in a fixed order: four
 // interleaved partial sums, then (s0 + s1) + (s2 + s3).
 __device__ __forceinline__ float block_dot(const float *q, const float *x) {

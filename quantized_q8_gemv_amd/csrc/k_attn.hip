@@ -13,11 +13,14 @@
 // Decode: the cache is split into chunks of keys; one workgroup handles one
 // chunk for all query heads of one KV head (K/V are read once per group),
 // keeps scores and softmax in LDS, and writes (max, sum, unnormalised o)
-// partials. The last workgroup of a group to finish (atomic counter) merges
-// the partials in split order, so the result does not depend on timing.
+// partials. The partials are merged in split order by the consumer (the
+// o-projection's prologue, or k_attn_combine), so the result does not depend
+// on timing and no device-wide atomics are needed.
 //
 // Prefill: one workgroup per (32 queries, head); key tiles staged in LDS,
 // online softmax in f32 per query row.
+
+#include <algorithm>
 
 #include "device_common.h"
 
@@ -38,7 +41,6 @@ struct DecodeLds {
 
 __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int s = blockIdx.x, g = blockIdx.y;
     const int hd = a.hd, G = a.nh / a.nkv;
@@ -101,42 +103,33 @@ __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
             const int h = e / hd, d = e - h * hd;
             float acc = 0.f;
             for (int j = 0; j < nk; ++j) acc = fmaf(L.sc[h * C + j], L.v[j * hd + d], acc);
-            const int head = g * G + h;
-            if (active == 1) {
-                a.o[size_t(head) * hd + d] = acc / L.l[h];
-            } else {
-                float *pp = a.part + (size_t(head) * a.n_splits + s) * (hd + 2);
-                pp[2 + d] = acc;
-                if (d == 0) {
-                    pp[0] = L.m[h];
-                    pp[1] = L.l[h];
-                }
+            float *pp = a.part + (size_t(g * G + h) * a.n_splits + s) * (hd + 2);
+            pp[2 + d] = acc;
+            if (d == 0) {
+                pp[0] = L.m[h];
+                pp[1] = L.l[h];
             }
         }
     }
-    if (active == 1) return;
+}
 
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(a.counters + g, 1u) == unsigned(a.n_splits) - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int e = tid; e < G * hd; e += kThreads) {
-        const int h = e / hd, d = e - h * hd;
-        const int head = g * G + h;
-        const float *pb = a.part + size_t(head) * a.n_splits * (hd + 2);
-        float M = -INFINITY;
-        for (int t = 0; t < active; ++t) M = fmaxf(M, pb[t * (hd + 2)]);
-        float Lsum = 0.f, O = 0.f;
-        for (int t = 0; t < active; ++t) {
-            const float w = expf(pb[t * (hd + 2)] - M);
-            Lsum = fmaf(w, pb[t * (hd + 2) + 1], Lsum);
-            O = fmaf(w, pb[t * (hd + 2) + 2 + d], O);
-        }
-        a.o[size_t(head) * hd + d] = O / Lsum;
+// Merge the split partials into O (single-op path; the forward merges them
+// in the o-projection's prologue instead). Fixed split order.
+__global__ __launch_bounds__(kThreads) void k_attn_combine(const float *part, int n_splits,
+                                                          int active, int nh, int hd, float *o) {
+    const int e = blockIdx.x * kThreads + threadIdx.x;
+    if (e >= nh * hd) return;
+    const int h = e / hd, d = e - h * hd;
+    const float *pb = part + size_t(h) * n_splits * (hd + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < active; ++s) M = fmaxf(M, pb[s * (hd + 2)]);
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < active; ++s) {
+        const float w = expf(pb[s * (hd + 2)] - M);
+        L = fmaf(w, pb[s * (hd + 2) + 1], L);
+        O = fmaf(w, pb[s * (hd + 2) + 2 + d], O);
     }
-    if (tid == 0) a.counters[g] = 0u;
+    o[e] = O / L;
 }
 
 constexpr int kQB = 32;   // queries per prefill workgroup
@@ -249,6 +242,15 @@ size_t attn_decode_lds(int G, int hd) {
 hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s) {
     const size_t lds = attn_decode_lds(a.nh / a.nkv, a.hd);
     hipLaunchKernelGGL(k_attn_decode, dim3(a.n_splits, a.nkv), dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int nh, int hd,
+                               float *o, hipStream_t s) {
+    const int active = std::min((kv_len + attn_chunk(hd) - 1) / attn_chunk(hd), n_splits);
+    const int n = nh * hd;
+    hipLaunchKernelGGL(k_attn_combine, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                       part, n_splits, active, nh, hd, o);
     return hipGetLastError();
 }
 

@@ -84,70 +84,120 @@ __device__ inline Lds carve(uint8_t *smem, const GemvShape &sh, int nmat, int ma
     return l;
 }
 
-// Copy rows [row0, row0+nrows), pairs [c*PC, (c+1)*PC) of one matrix to LDS
-// as a flat [row][pair] array of 17-dword pairs.
-__device__ inline void load_tile(const uint8_t *W, const GemvShape &sh, int row0, int nrows,
-                                 int c, uint32_t *dst) {
-    const int tid = threadIdx.x;
-    const uint8_t *base = W + size_t(row0) * sh.rowbytes + size_t(c) * sh.PC * kPairBytes;
+// Weight tile staging. A workgroup's tile for chunk c is nmat x nrows row
+// slices of PC pairs; in LDS it is one flat [m][r][p] array of 17-dword
+// pairs. Loads are issued into registers first (so they are in flight while
+// the workgroup does other work) and written to LDS later.
+constexpr int kMaxV4 = 5;   // 16-byte loads per thread (tile <= 256 pairs = 17408 bytes)
+
+struct WStage {
+    u32x4 v[kMaxV4];
+};
+
+// Whether chunk tiles can be moved with 16-byte loads (all pieces 16-byte
+// aligned and whole). Otherwise (only ragged edge tiles of some shapes) the
+// tile is copied with 4-byte loads at store time (pairs are 4-byte aligned).
+__device__ inline bool tile_vec(const CoreArgs &a, int nrows) {
+    const GemvShape &sh = a.sh;
+    if (sh.PC == sh.P) return ((size_t(a.row0) * sh.rowbytes) % 16 == 0) && ((nrows * sh.rowbytes) % 16 == 0);
+    return (sh.PC % 4 == 0) && (sh.P % 4 == 0);
+}
+
+__device__ inline const uint8_t *tile_src(const CoreArgs &a, int nrows, int c, int i, int unit) {
+    // i indexes `unit`-byte pieces of the flat tile
+    const GemvShape &sh = a.sh;
     if (sh.PC == sh.P) {
-        const int nbytes = nrows * sh.rowbytes;
-        if (((reinterpret_cast<uintptr_t>(base) | reinterpret_cast<uintptr_t>(dst) | nbytes) & 15) == 0) {
-            const u32x4 *s4 = reinterpret_cast<const u32x4 *>(base);
-            u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
-            for (int i = tid; i < nbytes / 16; i += kThreads) d4[i] = __builtin_nontemporal_load(s4 + i);
-        } else {
-            const uint32_t *s1 = reinterpret_cast<const uint32_t *>(base);
-            for (int i = tid; i < nbytes / 4; i += kThreads) dst[i] = __builtin_nontemporal_load(s1 + i);
-        }
-    } else {
-        const int slice = sh.PC * (kPairBytes / 4);
-        const int total = nrows * slice;
-        for (int i = tid; i < total; i += kThreads) {
-            const int r = i / slice;
-            const int w = i - r * slice;
-            const uint32_t *s1 = reinterpret_cast<const uint32_t *>(base + size_t(r) * sh.rowbytes);
-            dst[i] = __builtin_nontemporal_load(s1 + w);
-        }
+        const int per_mat = nrows * sh.rowbytes / unit;
+        const int m = i >= per_mat ? 1 : 0;
+        return a.W[m] + size_t(a.row0) * sh.rowbytes + size_t(i - m * per_mat) * unit;
+    }
+    const int per_row = sh.PC * kPairBytes / unit;
+    const int per_mat = nrows * per_row;
+    const int m = i >= per_mat ? 1 : 0;
+    const int ii = i - m * per_mat;
+    const int r = ii / per_row, j = ii - r * per_row;
+    return a.W[m] + size_t(a.row0 + r) * sh.rowbytes + size_t(c) * sh.PC * kPairBytes + size_t(j) * unit;
+}
+
+__device__ inline void stage_issue(const CoreArgs &a, int nrows, int c, bool vec, WStage &st) {
+    if (!vec) return;
+    const int tid = threadIdx.x;
+    const int n16 = a.nmat * nrows * a.sh.PC * kPairBytes / 16;
+#pragma unroll
+    for (int k = 0; k < kMaxV4; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < n16)
+            st.v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(tile_src(a, nrows, c, i, 16)));
     }
 }
 
+__device__ inline void stage_store(const CoreArgs &a, int nrows, int c, bool vec, const WStage &st,
+                                   uint32_t *wt) {
+    const int tid = threadIdx.x;
+    const int bytes = a.nmat * nrows * a.sh.PC * kPairBytes;
+    if (vec) {
+        u32x4 *d = reinterpret_cast<u32x4 *>(wt);
+#pragma unroll
+        for (int k = 0; k < kMaxV4; ++k) {
+            const int i = tid + k * kThreads;
+            if (i < bytes / 16) d[i] = st.v[k];
+        }
+    } else {
+#pragma unroll 1
+        for (int i = tid; i < bytes / 4; i += kThreads)
+            wt[i] = *reinterpret_cast<const uint32_t *>(tile_src(a, nrows, c, i, 4));
+    }
+}
+
+// Activation sources for the x staging step.
+enum XMode { X_PLAIN = 0, X_ATTN_COMBINE = 1 };
+
+struct Combine {
+    const float *part;   // [nh][n_splits][hd + 2]: (max, sum, unnormalised o[hd])
+    const StepState *st; // kv_len = st->slot + 1
+    int n_splits, hd, chunk;
+};
+
+// Merge the split-KV partials of attention output element e = h*hd + d in
+// split order (fixed, so the result does not depend on timing).
+__device__ inline float combine_elem(const Combine &cb, int e) {
+    const int kv_len = cb.st->slot + 1;
+    const int active = min((kv_len + cb.chunk - 1) / cb.chunk, cb.n_splits);
+    const int h = e / cb.hd, d = e - h * cb.hd;
+    const float *pb = cb.part + size_t(h) * cb.n_splits * (cb.hd + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < active; ++s) M = fmaxf(M, pb[s * (cb.hd + 2)]);
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < active; ++s) {
+        const float w = expf(pb[s * (cb.hd + 2)] - M);
+        L = fmaf(w, pb[s * (cb.hd + 2) + 1], L);
+        O = fmaf(w, pb[s * (cb.hd + 2) + 2 + d], O);
+    }
+    return O / L;
+}
+
 // Computes outv[(t*nmat + m)*NR + r] = sum_k W_m[row0+r][k] * U[t][k].
-template <int MAXT>
-__device__ void gemv_core(const CoreArgs &a, const Lds &l) {
+//   U = X, or rmsnorm(X) * norm_w when norm_w is set, or (X_ATTN_COMBINE)
+//   the merged attention partials.
+// Timeline: chunk-0 weight loads are issued first; the activation row is
+// read (and its norm computed) while they are in flight; chunk c+1's loads
+// are issued before chunk c is computed.
+template <int MAXT, int XM = X_PLAIN, bool MULTI = true>
+__device__ void gemv_core(const CoreArgs &a, const Lds &l, const Combine *cb = nullptr) {
     const int tid = threadIdx.x;
     const GemvShape &sh = a.sh;
     const int nrows = min(sh.NR, a.N - a.row0);
     const int per_mat = nrows * sh.PC;
     const int units = a.nmat * per_mat;
+    const int nchunks = MULTI ? sh.P / sh.PC : 1;
+    const bool x_full = (nchunks == 1);   // the whole activation row fits in one staging
+    const bool vec = tile_vec(a, nrows);
 
-    if (a.norm_w) {
-        for (int t = 0; t < a.Tc; ++t) {
-            float ss = 0.f;
-            const float *xr = a.X + size_t(t) * a.ldx;
-            for (int k = tid; k < sh.K; k += kThreads) {
-                float v = xr[k];
-                ss = fmaf(v, v, ss);
-            }
-            ss = block_sum(ss, l.red);
-            if (tid == 0) l.rinv[t] = 1.0f / sqrtf(ss / static_cast<float>(sh.K) + a.eps);
-        }
-        __syncthreads();
-    }
+    WStage st;
+    stage_issue(a, nrows, 0, vec, st);
 
-    float acc[MAXT];
-#pragma unroll
-    for (int t = 0; t < MAXT; ++t) acc[t] = 0.f;
-
-    int up = 0;
-    if (tid < units) {
-        const int rem = tid % per_mat;
-        up = rem % sh.PC;
-    }
-    const int nchunks = sh.P / sh.PC;
-    for (int c = 0; c < nchunks; ++c) {
-        for (int m = 0; m < a.nmat; ++m)
-            load_tile(a.W[m], sh, a.row0, nrows, c, l.wt + size_t(m) * per_mat * (kPairBytes / 4));
+    // Stage x for chunk c (all of K when x_full); rinv must be ready if norm.
+    auto stage_x = [&](int c, bool normalize) {
         const int n4 = a.Tc * sh.PC * 16;
         for (int e = tid; e < n4; e += kThreads) {
             const int t = e / (sh.PC * 16);
@@ -155,8 +205,16 @@ __device__ void gemv_core(const CoreArgs &a, const Lds &l) {
             const int p = rem >> 4;
             const int i4 = rem & 15;
             const int k = (c * sh.PC + p) * kPairWeights + i4 * 4;
-            float4 v = *reinterpret_cast<const float4 *>(a.X + size_t(t) * a.ldx + k);
-            if (a.norm_w) {
+            float4 v;
+            if (XM == X_ATTN_COMBINE) {
+                v.x = combine_elem(*cb, k);
+                v.y = combine_elem(*cb, k + 1);
+                v.z = combine_elem(*cb, k + 2);
+                v.w = combine_elem(*cb, k + 3);
+            } else {
+                v = *reinterpret_cast<const float4 *>(a.X + size_t(t) * a.ldx + k);
+            }
+            if (normalize) {
                 const float r = l.rinv[t];
                 const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + k);
                 v.x = v.x * r * w.x;
@@ -166,16 +224,86 @@ __device__ void gemv_core(const CoreArgs &a, const Lds &l) {
             }
             *reinterpret_cast<float4 *>(l.xs + (size_t(t) * sh.PC + p) * kXPad + i4 * 4) = v;
         }
+    };
+
+    if (a.norm_w) {
+        if (x_full) {
+            // raw x to LDS, sum of squares from the same values, then scale in place
+            const int n4 = a.Tc * sh.PC * 16;
+            for (int t = 0; t < a.Tc; ++t) {
+                float ss = 0.f;
+                for (int e = tid; e < sh.PC * 16; e += kThreads) {
+                    const int p = e >> 4, i4 = e & 15;
+                    const float4 v = *reinterpret_cast<const float4 *>(a.X + size_t(t) * a.ldx + p * kPairWeights + i4 * 4);
+                    *reinterpret_cast<float4 *>(l.xs + (size_t(t) * sh.PC + p) * kXPad + i4 * 4) = v;
+                    ss = fmaf(v.x, v.x, ss);
+                    ss = fmaf(v.y, v.y, ss);
+                    ss = fmaf(v.z, v.z, ss);
+                    ss = fmaf(v.w, v.w, ss);
+                }
+                ss = block_sum(ss, l.red);
+                if (tid == 0) l.rinv[t] = 1.0f / sqrtf(ss / static_cast<float>(sh.K) + a.eps);
+            }
+            __syncthreads();
+            for (int e = tid; e < n4; e += kThreads) {
+                const int t = e / (sh.PC * 16);
+                const int rem = e - t * sh.PC * 16;
+                const int p = rem >> 4, i4 = rem & 15;
+                float4 *xp = reinterpret_cast<float4 *>(l.xs + (size_t(t) * sh.PC + p) * kXPad + i4 * 4);
+                const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + p * kPairWeights + i4 * 4);
+                const float r = l.rinv[t];
+                float4 v = *xp;
+                v.x = v.x * r * w.x;
+                v.y = v.y * r * w.y;
+                v.z = v.z * r * w.z;
+                v.w = v.w * r * w.w;
+                *xp = v;
+            }
+        } else {
+            for (int t = 0; t < a.Tc; ++t) {
+                float ss = 0.f;
+                const float *xr = a.X + size_t(t) * a.ldx;
+                for (int k = tid; k < sh.K; k += kThreads) {
+                    const float v = xr[k];
+                    ss = fmaf(v, v, ss);
+                }
+                ss = block_sum(ss, l.red);
+                if (tid == 0) l.rinv[t] = 1.0f / sqrtf(ss / static_cast<float>(sh.K) + a.eps);
+            }
+            __syncthreads();
+        }
+    } else if (x_full) {
+        stage_x(0, false);
+    }
+
+    float acc[MAXT];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) acc[t] = 0.f;
+    int up = 0;
+    if (tid < units) up = (tid % per_mat) % sh.PC;
+
+    for (int c = 0; c < nchunks; ++c) {
+        if (!x_full) stage_x(c, a.norm_w != nullptr);
+        stage_store(a, nrows, c, vec, st, l.wt);
+        if (MULTI && c + 1 < nchunks) stage_issue(a, nrows, c + 1, vec, st);
         __syncthreads();
         if (tid < units) {
-            PairQ pq;
-            decode_pair(l.wt + size_t(tid) * (kPairBytes / 4), pq);
+            const uint32_t *wp = l.wt + size_t(tid) * (kPairBytes / 4);
+            if constexpr (MAXT == 1) {
+                float dA, sA, dB, sB;
+                pair_dot1(wp, l.xs + size_t(up) * kXPad, dA, sA, dB, sB);
+                acc[0] = fmaf(dA, sA, acc[0]);
+                acc[0] = fmaf(dB, sB, acc[0]);
+            } else {
+                PairQ pq;
+                decode_pair(wp, pq);
 #pragma unroll
-            for (int t = 0; t < MAXT; ++t) {
-                if (t < a.Tc) {
-                    const float *x = l.xs + (size_t(t) * sh.PC + up) * kXPad;
-                    acc[t] = fmaf(pq.dA, block_dot(pq.q, x), acc[t]);
-                    acc[t] = fmaf(pq.dB, block_dot(pq.q + 32, x + 32), acc[t]);
+                for (int t = 0; t < MAXT; ++t) {
+                    if (t < a.Tc) {
+                        const float *x = l.xs + (size_t(t) * sh.PC + up) * kXPad;
+                        acc[t] = fmaf(pq.dA, block_dot(pq.q, x), acc[t]);
+                        acc[t] = fmaf(pq.dB, block_dot(pq.q + 32, x + 32), acc[t]);
+                    }
                 }
             }
         }
@@ -222,7 +350,7 @@ struct QkvArgs {
     float eps;
 };
 
-template <int MAXT>
+template <int MAXT, bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds l = carve(smem, a.sh, 1, MAXT);
@@ -241,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
     c.W[0] = W; c.W[1] = nullptr; c.nmat = 1; c.sh = a.sh; c.N = N;
     c.row0 = tile * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<MAXT>(c, l);
+    gemv_core<MAXT, X_PLAIN, MULTI>(c, l);
 
     const int nrows = min(a.sh.NR, N - c.row0);
     const int half = nrows >> 1;
@@ -281,7 +409,7 @@ struct GateUpArgs {
     float eps;
 };
 
-template <int MAXT>
+template <int MAXT, bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_gateup(GateUpArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds l = carve(smem, a.sh, 2, MAXT);
@@ -290,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(GateUpArgs a) {
     c.W[0] = a.wg; c.W[1] = a.wu; c.nmat = 2; c.sh = a.sh; c.N = a.F;
     c.row0 = blockIdx.x * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<MAXT>(c, l);
+    gemv_core<MAXT, X_PLAIN, MULTI>(c, l);
     const int nrows = min(a.sh.NR, a.F - c.row0);
     for (int e = threadIdx.x; e < c.Tc * nrows; e += kThreads) {
         const int t = e / nrows, r = e - t * nrows;
@@ -310,9 +438,10 @@ struct MatmulArgs {
     GemvShape sh;
     int N, T, accumulate;
     float eps;
+    Combine cb;  // used by the attention-combine variant only
 };
 
-template <int MAXT>
+template <int MAXT, int XM, bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_matmul(MatmulArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds l = carve(smem, a.sh, 1, MAXT);
@@ -321,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void k_matmul(MatmulArgs a) {
     c.W[0] = a.W; c.W[1] = nullptr; c.nmat = 1; c.sh = a.sh; c.N = a.N;
     c.row0 = blockIdx.x * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<MAXT>(c, l);
+    gemv_core<MAXT, XM, MULTI>(c, l, &a.cb);
     const int nrows = min(a.sh.NR, a.N - c.row0);
     for (int e = threadIdx.x; e < c.Tc * nrows; e += kThreads) {
         const int t = e / nrows, r = e - t * nrows;
@@ -339,51 +468,30 @@ struct LmHeadArgs {
     const float *x;      // [H], the last position
     StepState *st;
     float *partials;     // [gridDim.x][2] (value, index bits)
-    uint32_t *counter;
     GemvShape sh;
     int V;
     float eps;
 };
 
-// Final reduction of per-workgroup (value, index) partials; called by the
-// last workgroup to finish. Fixed order: thread-strided, then butterflies.
-__device__ void argmax_finish(const float *partials, int n, float *red, uint32_t *redi,
-                              float &bv, uint32_t &bi) {
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    float v = -INFINITY;
-    uint32_t i = 0xffffffffu;
-    for (int b = tid; b < n; b += kThreads) {
-        const float ov = __builtin_nontemporal_load(partials + 2 * b);
-        const uint32_t oi = __float_as_uint(__builtin_nontemporal_load(partials + 2 * b + 1));
-        argmax_merge(v, i, ov, oi);
-    }
-    wave_argmax(v, i);
-    if (lane == 0) {
-        red[wid] = v;
-        redi[wid] = i;
-    }
-    __syncthreads();
-    bv = red[0];
-    bi = redi[0];
-    for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, red[w], redi[w]);
-}
-
+// Logits for this workgroup's rows, plus the workgroup's (max, index) pair.
+// The pairs are merged by k_argmax_finish (a second, one-workgroup launch):
+// a device-wide atomic per workgroup would serialize at the memory side.
+template <bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_lmhead(LmHeadArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds l = carve(smem, a.sh, 1, 1);
     __shared__ float s_red[4];
     __shared__ uint32_t s_redi[4];
-    __shared__ int s_last;
     CoreArgs c;
     c.W[0] = a.W; c.W[1] = nullptr; c.nmat = 1; c.sh = a.sh; c.N = a.V;
     c.row0 = blockIdx.x * a.sh.NR; c.Tc = 1;
     c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<1>(c, l);
+    gemv_core<1, X_PLAIN, MULTI>(c, l);
     const int nrows = min(a.sh.NR, a.V - c.row0);
     float *logits = a.st->logits_out;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     float bv = -INFINITY;
-    uint32_t bi = 0xffffffffu;
+    uint32_t bi = uint32_t(c.row0);
     for (int r = tid; r < nrows; r += kThreads) {
         const float v = l.outv[r];
         logits[c.row0 + r] = v;
@@ -401,18 +509,36 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(LmHeadArgs a) {
         for (int w = 1; w < 4; ++w) argmax_merge(v, i, s_red[w], s_redi[w]);
         a.partials[2 * blockIdx.x] = v;
         a.partials[2 * blockIdx.x + 1] = __uint_as_float(i);
-        __threadfence();
-        const uint32_t prev = atomicAdd(a.counter, 1u);
-        s_last = (prev == gridDim.x - 1);
+    }
+}
+
+// Merge n (value, index) partials in a fixed order; lowest index on ties.
+__device__ void argmax_reduce(const float *partials, int n, float &bv, uint32_t &bi) {
+    __shared__ float red[4];
+    __shared__ uint32_t redi[4];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    float v = -INFINITY;
+    uint32_t i = 0xffffffffu;
+    for (int b = tid; b < n; b += kThreads)
+        argmax_merge(v, i, partials[2 * b], __float_as_uint(partials[2 * b + 1]));
+    wave_argmax(v, i);
+    if (lane == 0) {
+        red[wid] = v;
+        redi[wid] = i;
     }
     __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    bv = red[0];
+    bi = redi[0];
+    for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, red[w], redi[w]);
+}
+
+// One workgroup: final argmax of the output layer, then the step state
+// update used by on-device generation (the picked id becomes the next input).
+__global__ __launch_bounds__(kThreads) void k_argmax_finish(const float *partials, int n, StepState *st) {
     float v;
     uint32_t i;
-    argmax_finish(a.partials, gridDim.x, s_red, s_redi, v, i);
-    if (tid == 0) {
-        StepState *st = a.st;
+    argmax_reduce(partials, n, v, i);
+    if (threadIdx.x == 0) {
         if (st->argmax_out) *st->argmax_out = i;
         if (st->advance) {
             if (st->ids_out) st->ids_out[st->step] = i;
@@ -421,21 +547,19 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(LmHeadArgs a) {
             st->slot += 1;
             st->step += 1;
         }
-        *a.counter = 0u;  // ready for the next launch (no memset node needed)
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_argmax(const float *x, int64_t n, uint32_t *out,
-                                                     float *partials, uint32_t *counter) {
+// Standalone argmax: per-workgroup partials, then a one-workgroup merge.
+__global__ __launch_bounds__(kThreads) void k_argmax_part(const float *x, int64_t n, float *partials) {
     __shared__ float s_red[4];
     __shared__ uint32_t s_redi[4];
-    __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t per = 4096;
     const int64_t b0 = int64_t(blockIdx.x) * per;
     const int64_t e = min(n, b0 + per);
     float bv = -INFINITY;
-    uint32_t bi = 0xffffffffu;
+    uint32_t bi = uint32_t(b0);
     for (int64_t j = b0 + tid; j < e; j += kThreads) argmax_merge(bv, bi, x[j], uint32_t(j));
     wave_argmax(bv, bi);
     if (lane == 0) {
@@ -449,19 +573,14 @@ __global__ __launch_bounds__(kThreads) void k_argmax(const float *x, int64_t n, 
         for (int w = 1; w < 4; ++w) argmax_merge(v, i, s_red[w], s_redi[w]);
         partials[2 * blockIdx.x] = v;
         partials[2 * blockIdx.x + 1] = __uint_as_float(i);
-        __threadfence();
-        s_last = (atomicAdd(counter, 1u) == gridDim.x - 1);
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+}
+
+__global__ __launch_bounds__(kThreads) void k_argmax_out(const float *partials, int n, uint32_t *out) {
     float v;
     uint32_t i;
-    argmax_finish(partials, gridDim.x, s_red, s_redi, v, i);
-    if (tid == 0) {
-        *out = i;
-        *counter = 0u;
-    }
+    argmax_reduce(partials, n, v, i);
+    if (threadIdx.x == 0) *out = i;
 }
 
 // ---------------------------------------------------------------- host side
@@ -514,10 +633,13 @@ hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const S
     a.tk = (a.KVD + a.sh.NR - 1) / a.sh.NR;
     dim3 grid(a.tq + 2 * a.tk, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 1, maxt);
+    const bool multi = a.sh.PC != a.sh.P;
     if (maxt == 1) {
-        hipLaunchKernelGGL(k_qkv<1>, grid, dim3(kThreads), lds, s, a);
+        if (multi) hipLaunchKernelGGL((k_qkv<1, true>), grid, dim3(kThreads), lds, s, a);
+        else hipLaunchKernelGGL((k_qkv<1, false>), grid, dim3(kThreads), lds, s, a);
     } else {
-        hipLaunchKernelGGL(k_qkv<kMaxTokChunk>, grid, dim3(kThreads), lds, s, a);
+        if (multi) hipLaunchKernelGGL((k_qkv<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
+        else hipLaunchKernelGGL((k_qkv<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
     }
     return hipGetLastError();
 }
@@ -531,10 +653,13 @@ hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, floa
     a.sh = choose_shape(d.F, d.H, maxt, 2, 512, 1);
     dim3 grid((d.F + a.sh.NR - 1) / a.sh.NR, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 2, maxt);
+    const bool multi = a.sh.PC != a.sh.P;
     if (maxt == 1) {
-        hipLaunchKernelGGL(k_gateup<1>, grid, dim3(kThreads), lds, s, a);
+        if (multi) hipLaunchKernelGGL((k_gateup<1, true>), grid, dim3(kThreads), lds, s, a);
+        else hipLaunchKernelGGL((k_gateup<1, false>), grid, dim3(kThreads), lds, s, a);
     } else {
-        hipLaunchKernelGGL(k_gateup<kMaxTokChunk>, grid, dim3(kThreads), lds, s, a);
+        if (multi) hipLaunchKernelGGL((k_gateup<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
+        else hipLaunchKernelGGL((k_gateup<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
     }
     return hipGetLastError();
 }
@@ -543,45 +668,74 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
                          const float *norm_w, float eps, int accumulate, float *Y,
                          hipStream_t s) {
     const int maxt = T == 1 ? 1 : kMaxTokChunk;
-    MatmulArgs a;
+    MatmulArgs a{};
     a.W = W; a.norm_w = norm_w; a.x = X; a.y = Y; a.N = N; a.T = T; a.accumulate = accumulate;
     a.eps = eps;
     a.sh = choose_shape(N, K, maxt, 1, 512, 1);
     dim3 grid((N + a.sh.NR - 1) / a.sh.NR, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 1, maxt);
+    const bool multi = a.sh.PC != a.sh.P;
     if (maxt == 1) {
-        hipLaunchKernelGGL(k_matmul<1>, grid, dim3(kThreads), lds, s, a);
+        if (multi) hipLaunchKernelGGL((k_matmul<1, X_PLAIN, true>), grid, dim3(kThreads), lds, s, a);
+        else hipLaunchKernelGGL((k_matmul<1, X_PLAIN, false>), grid, dim3(kThreads), lds, s, a);
     } else {
-        hipLaunchKernelGGL(k_matmul<kMaxTokChunk>, grid, dim3(kThreads), lds, s, a);
+        if (multi) hipLaunchKernelGGL((k_matmul<kMaxTokChunk, X_PLAIN, true>), grid, dim3(kThreads), lds, s, a);
+        else hipLaunchKernelGGL((k_matmul<kMaxTokChunk, X_PLAIN, false>), grid, dim3(kThreads), lds, s, a);
     }
     return hipGetLastError();
 }
 
-static int lmhead_nr(int V, int K) { return choose_shape(V, K, 1, 1, 1024, 1).NR; }
-
-hipError_t launch_lmhead(const Dims &d, const uint8_t *Wout, const float *out_norm,
-                         const float *x_last, StepState *st, float *partials, uint32_t *counter,
-                         hipStream_t s) {
-    LmHeadArgs a;
-    a.W = Wout; a.norm_w = out_norm; a.x = x_last; a.st = st; a.partials = partials;
-    a.counter = counter; a.V = d.V; a.eps = d.eps;
-    a.sh = choose_shape(d.V, d.H, 1, 1, 1024, 1);
-    dim3 grid((d.V + a.sh.NR - 1) / a.sh.NR);
-    hipLaunchKernelGGL(k_lmhead, grid, dim3(kThreads), lds_bytes(a.sh, 1, 1), s, a);
+hipError_t launch_oproj_combine(const uint8_t *Wo, int H, int QD, const float *part,
+                                const StepState *st, int n_splits, int hd, float *x,
+                                hipStream_t s) {
+    MatmulArgs a{};
+    a.W = Wo; a.norm_w = nullptr; a.x = nullptr; a.y = x; a.N = H; a.T = 1; a.accumulate = 1;
+    a.eps = 0.f;
+    a.cb.part = part; a.cb.st = st; a.cb.n_splits = n_splits; a.cb.hd = hd;
+    a.cb.chunk = attn_chunk(hd);
+    a.sh = choose_shape(H, QD, 1, 1, 512, 1);
+    if (a.sh.PC != a.sh.P) return hipErrorInvalidValue;  // the merged row must fit one staging
+    dim3 grid((H + a.sh.NR - 1) / a.sh.NR, 1);
+    hipLaunchKernelGGL((k_matmul<1, X_ATTN_COMBINE, false>), grid, dim3(kThreads), lds_bytes(a.sh, 1, 1), s, a);
     return hipGetLastError();
 }
 
-size_t lmhead_partials_bytes(int V, int K) {
-    const int nr = lmhead_nr(V, K);
-    return size_t((V + nr - 1) / nr) * 8;
+static int lmhead_blocks(int V, int K) {
+    const int nr = choose_shape(V, K, 1, 1, 1024, 1).NR;
+    return (V + nr - 1) / nr;
 }
+
+hipError_t launch_lmhead(const Dims &d, const uint8_t *Wout, const float *out_norm,
+                         const float *x_last, StepState *st, float *partials, hipStream_t s) {
+    LmHeadArgs a;
+    a.W = Wout; a.norm_w = out_norm; a.x = x_last; a.st = st; a.partials = partials;
+    a.V = d.V; a.eps = d.eps;
+    a.sh = choose_shape(d.V, d.H, 1, 1, 1024, 1);
+    const int nb = lmhead_blocks(d.V, d.H);
+    if (a.sh.PC != a.sh.P)
+        hipLaunchKernelGGL(k_lmhead<true>, dim3(nb), dim3(kThreads), lds_bytes(a.sh, 1, 1), s, a);
+    else
+        hipLaunchKernelGGL(k_lmhead<false>, dim3(nb), dim3(kThreads), lds_bytes(a.sh, 1, 1), s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_argmax_finish(const Dims &d, const float *partials, StepState *st,
+                                hipStream_t s) {
+    hipLaunchKernelGGL(k_argmax_finish, dim3(1), dim3(kThreads), 0, s, partials,
+                       lmhead_blocks(d.V, d.H), st);
+    return hipGetLastError();
+}
+
+size_t lmhead_partials_bytes(int V, int K) { return size_t(lmhead_blocks(V, K)) * 8; }
 
 size_t argmax_partials_bytes(int64_t n) { return size_t((n + 4095) / 4096) * 8; }
 
-hipError_t launch_argmax(const float *x, int64_t n, uint32_t *out, float *partials,
-                         uint32_t *counter, hipStream_t s) {
-    const unsigned grid = unsigned((n + 4095) / 4096);
-    hipLaunchKernelGGL(k_argmax, dim3(grid), dim3(kThreads), 0, s, x, n, out, partials, counter);
+hipError_t launch_argmax(const float *x, int64_t n, uint32_t *out, float *partials, hipStream_t s) {
+    const int grid = int((n + 4095) / 4096);
+    hipLaunchKernelGGL(k_argmax_part, dim3(grid), dim3(kThreads), 0, s, x, n, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_argmax_out, dim3(1), dim3(kThreads), 0, s, (const float *)partials, grid, out);
     return hipGetLastError();
 }
 

@@ -83,20 +83,26 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
 hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, float *h, int T,
                          hipStream_t s);
 // logits = Wout rmsnorm(x[T-1]); argmax by the last workgroup; state update.
+// Output layer logits + per-workgroup argmax partials; then the one-workgroup
+// merge (which also advances the step state for on-device generation).
 hipError_t launch_lmhead(const Dims &d, const uint8_t *Wout, const float *out_norm,
-                         const float *x_last, StepState *st, float *partials,
-                         uint32_t *counter, hipStream_t s);
+                         const float *x_last, StepState *st, float *partials, hipStream_t s);
+hipError_t launch_argmax_finish(const Dims &d, const float *partials, StepState *st,
+                                hipStream_t s);
 hipError_t launch_argmax(const float *x, int64_t n, uint32_t *out, float *partials,
-                         uint32_t *counter, hipStream_t s);
+                         hipStream_t s);
+// o-projection + residual for one token whose input is the decode attention's
+// split partials (merged in the kernel's prologue).
+hipError_t launch_oproj_combine(const uint8_t *Wo, int H, int QD, const float *part,
+                                const StepState *st, int n_splits, int hd, float *x,
+                                hipStream_t s);
 size_t argmax_partials_bytes(int64_t n);
 
 // Decode attention (one query per head over kv_len keys, no mask).
 struct AttnDecodeArgs {
     const float *q;      // [nh][hd]
     const float *kc, *vc; // [nkv][kv_stride][hd]
-    float *o;            // [nh][hd]
-    float *part;         // [nh][max_splits][hd + 2]
-    uint32_t *counters;  // [nkv]
+    float *part;         // [nh][n_splits][hd + 2]
     const StepState *st; // kv_len = st->slot + 1 when kv_len_arg < 0
     int kv_len_arg;
     int kv_stride, nh, nkv, hd;
@@ -104,6 +110,8 @@ struct AttnDecodeArgs {
     float scale;
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s);
+hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int nh, int hd,
+                               float *o, hipStream_t s);
 int attn_decode_splits(int kv_len, int hd);
 __host__ __device__ int attn_chunk(int hd);
 size_t lmhead_partials_bytes(int V, int K);

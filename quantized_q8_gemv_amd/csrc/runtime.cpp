@@ -174,27 +174,30 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
         if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
         if (T == 1) {
             AttnDecodeArgs a;
-            a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.o = att;
+            a.q = q; a.kc = m->kc(l); a.vc = m->vc(l);
             a.part = m->at<float>(m->lay.attn_part);
-            a.counters = m->at<uint32_t>(m->lay.counters);
             a.st = st; a.kv_len_arg = -1; a.kv_stride = d.max_seq;
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = decode_splits;
             a.scale = 1.0f / sqrtf(float(d.hd));
             if ((e = launch_attn_decode(a, s)) != hipSuccess) return e;
+            if ((e = launch_oproj_combine(w.wo, d.H, QD, a.part, st, decode_splits, d.hd, x, s)) != hipSuccess)
+                return e;
         } else {
             AttnPrefillArgs a;
             a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.o = att;
             a.T = T; a.kv_len = kv_len_prefill; a.kv_stride = d.max_seq;
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.scale = 1.0f / sqrtf(float(d.hd));
             if ((e = launch_attn_prefill(a, s)) != hipSuccess) return e;
+            if ((e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s)) != hipSuccess) return e;
         }
-        if ((e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s)) != hipSuccess) return e;
         if ((e = launch_gateup(d, w, x, h, T, s)) != hipSuccess) return e;
         if ((e = launch_matmul(w.wd, d.H, d.F, h, T, nullptr, d.eps, 1, x, s)) != hipSuccess) return e;
     }
     const uint8_t *wout = m->cfg.tied_output ? m->tok_embd : m->output;
-    return launch_lmhead(d, wout, m->out_norm, x + size_t(T - 1) * d.H, st,
-                         m->at<float>(m->lay.lm_part), m->at<uint32_t>(m->lay.counters) + 255, s);
+    if ((e = launch_lmhead(d, wout, m->out_norm, x + size_t(T - 1) * d.H, st,
+                           m->at<float>(m->lay.lm_part), s)) != hipSuccess)
+        return e;
+    return launch_argmax_finish(d, m->at<float>(m->lay.lm_part), st, s);
 }
 
 int split_bucket(const q8l_model *m, int kv_len) {
@@ -479,13 +482,12 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     if (st != Q8L_OK) return st;
     StepState *S = m->state();
     float *x = m->at<float>(m->lay.x), *q = m->at<float>(m->lay.q);
-    float *att = m->at<float>(m->lay.att), *h = m->at<float>(m->lay.h);
+    float *h = m->at<float>(m->lay.h);
     const LayerPtrs w = m->layer(0);
     const uint8_t *wout = m->cfg.tied_output ? m->tok_embd : m->output;
     AttnDecodeArgs a;
-    a.q = q; a.kc = m->kc(0); a.vc = m->vc(0); a.o = att;
+    a.q = q; a.kc = m->kc(0); a.vc = m->vc(0);
     a.part = m->at<float>(m->lay.attn_part);
-    a.counters = m->at<uint32_t>(m->lay.counters);
     a.st = S; a.kv_len_arg = -1; a.kv_stride = d.max_seq;
     a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = split_bucket(m, kv_len);
     a.scale = 1.0f / sqrtf(float(d.hd));
@@ -494,15 +496,14 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
             case 0: return launch_embed(m->tok_embd, d.H, d.V, S, m->at<uint32_t>(m->lay.tok), 1, 1, x, s);
             case 1: return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
             case 2: return launch_attn_decode(a, s);
-            case 3: return launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, x, s);
+            case 3: return launch_oproj_combine(w.wo, d.H, QD, a.part, S, a.n_splits, d.hd, x, s);
             case 4: return launch_gateup(d, w, x, h, 1, s);
             case 5: return launch_matmul(w.wd, d.H, d.F, h, 1, nullptr, d.eps, 1, x, s);
-            default:
-                return launch_lmhead(d, wout, m->out_norm, x, S, m->at<float>(m->lay.lm_part),
-                                     m->at<uint32_t>(m->lay.counters) + 255, s);
+            case 6: return launch_lmhead(d, wout, m->out_norm, x, S, m->at<float>(m->lay.lm_part), s);
+            default: return launch_argmax_finish(d, m->at<float>(m->lay.lm_part), S, s);
         }
     };
-    constexpr int kKinds = 7;
+    constexpr int kKinds = 8;
     std::vector<hipEvent_t> ev(size_t(2) * reps * kKinds, nullptr);
     for (auto &e : ev) Q8L_HIP(m, hipEventCreate(&e), "hipEventCreate");
     hipError_t err = hipSuccess;
@@ -564,9 +565,10 @@ q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *
 
 size_t q8l_op_attention_workspace(int32_t T, int32_t kv_len, int32_t n_head, int32_t n_head_kv,
                                   int32_t hd) {
+    (void)n_head_kv;
     if (T != 1 || kv_len < 1 || n_head < 1 || hd < 8) return 256;
     const int splits = (kv_len + attn_chunk(hd) - 1) / attn_chunk(hd);
-    return al256(256 * 4) + al256(size_t(n_head) * splits * (hd + 2) * 4);
+    return al256(size_t(n_head) * splits * (hd + 2) * 4);
 }
 
 q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int32_t T,
@@ -574,8 +576,7 @@ q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int3
                             int32_t hd, float *O, void *workspace, size_t workspace_bytes,
                             void *stream) {
     if (!Q || !K || !V || !O || T < 1 || kv_len < T || kv_stride < kv_len || n_head < 1 ||
-        n_head_kv < 1 || n_head % n_head_kv || n_head / n_head_kv > kMaxGroup || hd % 8 || hd > 128 ||
-        n_head_kv > 255)
+        n_head_kv < 1 || n_head % n_head_kv || n_head / n_head_kv > kMaxGroup || hd % 8 || hd > 128)
         return Q8L_E_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
@@ -583,15 +584,14 @@ q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int3
         if (!workspace || workspace_bytes < q8l_op_attention_workspace(T, kv_len, n_head, n_head_kv, hd))
             return Q8L_E_INVALID_ARG;
         AttnDecodeArgs a;
-        a.q = Q; a.kc = K; a.vc = V; a.o = O;
-        a.counters = static_cast<uint32_t *>(workspace);
-        a.part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + al256(256 * 4));
+        a.q = Q; a.kc = K; a.vc = V;
+        a.part = static_cast<float *>(workspace);
         a.st = nullptr; a.kv_len_arg = kv_len; a.kv_stride = kv_stride;
         a.nh = n_head; a.nkv = n_head_kv; a.hd = hd;
         a.n_splits = (kv_len + attn_chunk(hd) - 1) / attn_chunk(hd);
         a.scale = 1.0f / sqrtf(float(hd));
-        if ((e = hipMemsetAsync(workspace, 0, 256 * 4, s)) != hipSuccess) return Q8L_E_HIP;
         e = launch_attn_decode(a, s);
+        if (e == hipSuccess) e = launch_attn_combine(a.part, a.n_splits, kv_len, n_head, hd, O, s);
     } else {
         AttnPrefillArgs a;
         a.q = Q; a.kc = K; a.vc = V; a.o = O; a.T = T; a.kv_len = kv_len; a.kv_stride = kv_stride;
@@ -604,13 +604,10 @@ q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int3
 q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspace,
                          size_t workspace_bytes, void *stream) {
     if (!x || !out || n < 1 || n > (int64_t(1) << 31) || !workspace ||
-        workspace_bytes < 256 + argmax_partials_bytes(n))
+        workspace_bytes < argmax_partials_bytes(n))
         return Q8L_E_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint32_t *counter = static_cast<uint32_t *>(workspace);
-    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + 256);
-    if (hipMemsetAsync(counter, 0, 4, s) != hipSuccess) return Q8L_E_HIP;
-    return launch_argmax(x, n, out, part, counter, s) == hipSuccess ? Q8L_OK : Q8L_E_HIP;
+    return launch_argmax(x, n, out, static_cast<float *>(workspace), s) == hipSuccess ? Q8L_OK : Q8L_E_HIP;
 }
 
 }  // extern "C"
