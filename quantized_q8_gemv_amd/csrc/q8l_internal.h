@@ -116,6 +116,17 @@ int attn_decode_splits(int kv_len, int hd);
 __host__ __device__ int attn_chunk(int hd);
 size_t lmhead_partials_bytes(int V, int K);
 
+// MFMA matrix-matrix path (prefill with T > kMaxTokChunk tokens).
+hipError_t launch_rms_rows(const float *x, int T, int K, float eps, float *rinv, hipStream_t s);
+hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const float *X, int T,
+                              const float *rinv, const float *norm_w, int accumulate, float *Y,
+                              hipStream_t s);
+hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const float *x, const float *rinv,
+                           const StepState *st, const float2 *rope, float *q, float *kc, float *vc,
+                           int T, hipStream_t s);
+hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const float *x, const float *rinv,
+                              float *h, int T, hipStream_t s);
+
 // Prefill attention: T queries, causal mask offset by the cached prefix.
 struct AttnPrefillArgs {
     const float *q;        // [T][nh][hd]

@@ -36,7 +36,7 @@ SHAPES = [(576, 576), (192, 576), (1536, 576), (576, 1536), (49152, 576),
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
-@pytest.mark.parametrize("T", [1, 13])
+@pytest.mark.parametrize("T", [1, 13, 100])
 def test_matmul_q8_0_matches_oracle(C, N, K, T):
     log(f"matmul N={N} K={K} T={T}")
     rng = np.random.default_rng(N * 7 + K + T)
