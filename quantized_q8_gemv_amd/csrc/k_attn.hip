@@ -227,6 +227,177 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill(AttnPrefillArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- prefill on MFMA
+//
+// One workgroup = 64 queries of one head; each wave owns 16 queries. Per
+// block of 64 keys:
+//   S^T[key][query] = K . Q^T   (contraction over hd, 3 f16 MFMAs per 32:
+//                                 Kh.Qh + Kl.Qh + Kh.Ql, Q pre-scaled)
+//   online softmax per query column in f32 (each lane holds one query)
+//   O^T[d][query] += V^T . P^T  (contraction over keys)
+// In the S^T accumulator a lane holds keys 4*(l/16)+i of one 16-key tile for
+// query l%16. The P^T . V contraction runs over keys in the order
+// slot 8*(l/16)+j -> key (j < 4 ? 4*(l/16)+j : 16 + 4*(l/16)+j-4) of each
+// 32-key step, so the S accumulators are the B operand as they stand and only
+// the V^T operand is gathered in that order from LDS.
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int FQ = 64;    // queries per workgroup
+constexpr int FK = 64;    // keys per block
+
+template <int HD>
+struct FlashLds {
+    _Float16 kh[FK * (HD + 8)];
+    _Float16 kl[FK * (HD + 8)];
+    _Float16 vh[FK * (HD + 8)];
+    _Float16 vl[FK * (HD + 8)];
+};
+
+__device__ __forceinline__ void split16(float v, _Float16 &hi, _Float16 &lo) {
+    hi = static_cast<_Float16>(v);
+    lo = static_cast<_Float16>(v - static_cast<float>(hi));
+}
+
+template <int HD>
+__global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs a) {
+    __shared__ __align__(16) FlashLds<HD> L;
+    constexpr int LD = HD + 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = a.nh / a.nkv;
+    const int h = blockIdx.y, g = h / G;
+    const int q0 = blockIdx.x * FQ;
+    const int prefix = a.kv_len - a.T;
+    const int row_stride = a.nh * HD;
+    const int qi = q0 + wave * 16 + (lane & 15);   // this lane's query
+    const int grp = lane >> 4;
+
+    // Q^T fragments (B operand): lane holds Q[qi][32*s + 8*grp + j], pre-scaled
+    half8 qh[HD / 32], ql[HD / 32];
+#pragma unroll
+    for (int s = 0; s < HD / 32; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float v = (qi < a.T) ? a.q[size_t(qi) * row_stride + h * HD + 32 * s + 8 * grp + j] * a.scale : 0.f;
+            _Float16 hi, lo;
+            split16(v, hi, lo);
+            qh[s][j] = hi;
+            ql[s][j] = lo;
+        }
+
+    f32x4 o[HD / 16];
+#pragma unroll
+    for (int t = 0; t < HD / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+    const int last_q = min(q0 + FQ, a.T) - 1;
+    const int blk_last = prefix + last_q;                // last key any query of the block sees
+    const float *kb = a.kc + size_t(g) * a.kv_stride * HD;
+    const float *vb = a.vc + size_t(g) * a.kv_stride * HD;
+
+    for (int j0 = 0; j0 <= blk_last; j0 += FK) {
+        __syncthreads();
+        for (int e = tid; e < FK * HD / 4; e += kThreads) {
+            const int j = e / (HD / 4), d4 = (e - j * (HD / 4)) * 4;
+            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+            if (j0 + j <= blk_last) {
+                kv = *reinterpret_cast<const float4 *>(kb + size_t(j0 + j) * HD + d4);
+                vv = *reinterpret_cast<const float4 *>(vb + size_t(j0 + j) * HD + d4);
+            }
+            const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, vvv[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                split16(kk[i], L.kh[j * LD + d4 + i], L.kl[j * LD + d4 + i]);
+                split16(vvv[i], L.vh[j * LD + d4 + i], L.vl[j * LD + d4 + i]);
+            }
+        }
+        __syncthreads();
+        // S^T for 4 key tiles of 16
+        f32x4 st[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int key = kt * 16 + (lane & 15);
+#pragma unroll
+            for (int s = 0; s < HD / 32; ++s) {
+                const half8 ah = *reinterpret_cast<const half8 *>(L.kh + key * LD + 32 * s + 8 * grp);
+                const half8 al = *reinterpret_cast<const half8 *>(L.kl + key * LD + 32 * s + 8 * grp);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qh[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qh[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ql[s], acc, 0, 0, 0);
+            }
+            st[kt] = acc;
+        }
+        // mask (keys beyond the causal limit of this query or beyond kv_len)
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = j0 + kt * 16 + 4 * grp + i;
+                const bool vis = key <= prefix + qi && key <= blk_last;
+                st[kt][i] = vis ? st[kt][i] : -INFINITY;
+                bmax = fmaxf(bmax, st[kt][i]);
+            }
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        const float m_new = fmaxf(m, bmax);
+        const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = (st[kt][i] == -INFINITY) ? 0.f : expf(st[kt][i] - m_new);
+                st[kt][i] = p;
+                psum += p;
+            }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        lsum = lsum * alpha + psum;
+        m = m_new;
+        // P^T as the B operand for two 32-key steps: keys {kt=2s, kt=2s+1}
+        half8 ph[2], pl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float p = (j < 4) ? st[2 * s][j] : st[2 * s + 1][j - 4];
+                _Float16 hi, lo;
+                split16(p, hi, lo);
+                ph[s][j] = hi;
+                pl[s][j] = lo;
+            }
+#pragma unroll
+        for (int t = 0; t < HD / 16; ++t) {
+            f32x4 acc = o[t] * alpha;
+            const int d = t * 16 + (lane & 15);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                half8 vh, vl;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int key = 32 * s + ((j < 4) ? (4 * grp + j) : (16 + 4 * grp + j - 4));
+                    vh[j] = L.vh[key * LD + d];
+                    vl[j] = L.vl[key * LD + d];
+                }
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, ph[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, ph[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, pl[s], acc, 0, 0, 0);
+            }
+            o[t] = acc;
+        }
+    }
+    if (qi < a.T) {
+        const float inv = 1.0f / lsum;
+        float *dst = a.o + size_t(qi) * row_stride + h * HD;
+#pragma unroll
+        for (int t = 0; t < HD / 16; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[t * 16 + 4 * grp + i] = o[t][i] * inv;
+    }
+}
+
 }  // namespace
 
 int attn_decode_splits(int kv_len, int hd) {
@@ -255,6 +426,14 @@ hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int 
 }
 
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t s) {
+    if (a.hd == 64 || a.hd == 128) {
+        dim3 grid((a.T + FQ - 1) / FQ, a.nh);
+        if (a.hd == 64)
+            hipLaunchKernelGGL(k_attn_prefill_mfma<64>, grid, dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(k_attn_prefill_mfma<128>, grid, dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+    }
     const size_t lds = sizeof(float) * (size_t(kQB) * (a.hd + 1) + size_t(kKT) * (a.hd + 1) +
                                         size_t(kKT) * a.hd + size_t(kQB) * kKT);
     dim3 grid((a.T + kQB - 1) / kQB, a.nh);

@@ -50,7 +50,7 @@ struct CoreArgs {
 struct Lds {
     uint32_t *wt;   // nmat*NR*PC*17 dwords (reused for partials)
     float *xs;      // MAXT*PC*kXPad
-    float *outv;    // MAXT*nmat*NR
+    float *outv;    // max(MAXT*nmat*NR, 4*MAXT); also the norm prologue's scratch
     float *rinv;    // MAXT
     float *red;     // 4
 };
@@ -62,7 +62,7 @@ __host__ __device__ inline size_t lds_bytes(const GemvShape &sh, int nmat, int m
     size_t part = size_t(maxt) * nmat * sh.NR * sh.PC * 4;
     size_t b = align16(std::max(wt, part));
     b += align16(size_t(maxt) * sh.PC * kXPad * 4);
-    b += align16(size_t(maxt) * nmat * sh.NR * 4);
+    b += align16(std::max(size_t(maxt) * nmat * sh.NR, size_t(4) * maxt) * 4);
     b += align16(size_t(maxt) * 4) + 16;
     return b;
 }
@@ -77,7 +77,8 @@ __device__ inline Lds carve(uint8_t *smem, const GemvShape &sh, int nmat, int ma
     l.xs = reinterpret_cast<float *>(smem + off);
     off += align16(size_t(maxt) * sh.PC * kXPad * 4);
     l.outv = reinterpret_cast<float *>(smem + off);
-    off += align16(size_t(maxt) * nmat * sh.NR * 4);
+    off += align16((size_t(maxt) * nmat * sh.NR > size_t(4) * maxt ? size_t(maxt) * nmat * sh.NR
+                                                                 : size_t(4) * maxt) * 4);
     l.rinv = reinterpret_cast<float *>(smem + off);
     off += align16(size_t(maxt) * 4);
     l.red = reinterpret_cast<float *>(smem + off);
@@ -227,24 +228,43 @@ __device__ void gemv_core(const CoreArgs &a, const Lds &l, const Combine *cb = n
     };
 
     if (a.norm_w) {
-        if (x_full) {
-            // raw x to LDS, sum of squares from the same values, then scale in place
-            const int n4 = a.Tc * sh.PC * 16;
-            for (int t = 0; t < a.Tc; ++t) {
-                float ss = 0.f;
-                for (int e = tid; e < sh.PC * 16; e += kThreads) {
-                    const int p = e >> 4, i4 = e & 15;
-                    const float4 v = *reinterpret_cast<const float4 *>(a.X + size_t(t) * a.ldx + p * kPairWeights + i4 * 4);
-                    *reinterpret_cast<float4 *>(l.xs + (size_t(t) * sh.PC + p) * kXPad + i4 * 4) = v;
-                    ss = fmaf(v.x, v.x, ss);
-                    ss = fmaf(v.y, v.y, ss);
-                    ss = fmaf(v.z, v.z, ss);
-                    ss = fmaf(v.w, v.w, ss);
+        // Sum of squares for every token at once: all activation loads are in
+        // flight together, then one reduction (per-token partials in fixed order).
+        float ss[MAXT];
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) ss[t] = 0.f;
+        const int n4row = x_full ? sh.PC * 16 : sh.K / 4;
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+            if (t < a.Tc) {
+                for (int e = tid; e < n4row; e += kThreads) {
+                    const float4 v = *reinterpret_cast<const float4 *>(a.X + size_t(t) * a.ldx + e * 4);
+                    if (x_full) {
+                        const int p = e >> 4, i4 = e & 15;
+                        *reinterpret_cast<float4 *>(l.xs + (size_t(t) * sh.PC + p) * kXPad + i4 * 4) = v;
+                    }
+                    ss[t] = fmaf(v.x, v.x, ss[t]);
+                    ss[t] = fmaf(v.y, v.y, ss[t]);
+                    ss[t] = fmaf(v.z, v.z, ss[t]);
+                    ss[t] = fmaf(v.w, v.w, ss[t]);
                 }
-                ss = block_sum(ss, l.red);
-                if (tid == 0) l.rinv[t] = 1.0f / sqrtf(ss / static_cast<float>(sh.K) + a.eps);
             }
-            __syncthreads();
+        }
+        float *red = l.outv;  // MAXT * nmat * NR >= 4 * MAXT floats of scratch until the end
+        const int lane0 = tid & 63, wid0 = tid >> 6;
+#pragma unroll
+        for (int t = 0; t < MAXT; ++t) {
+            const float v = wave_sum(ss[t]);
+            if (lane0 == 0) red[wid0 * MAXT + t] = v;
+        }
+        __syncthreads();
+        if (tid < a.Tc) {
+            const float tot = (red[tid] + red[MAXT + tid]) + (red[2 * MAXT + tid] + red[3 * MAXT + tid]);
+            l.rinv[tid] = 1.0f / sqrtf(tot / static_cast<float>(sh.K) + a.eps);
+        }
+        __syncthreads();
+        if (x_full) {
+            const int n4 = a.Tc * sh.PC * 16;
             for (int e = tid; e < n4; e += kThreads) {
                 const int t = e / (sh.PC * 16);
                 const int rem = e - t * sh.PC * 16;
@@ -259,18 +279,6 @@ __device__ void gemv_core(const CoreArgs &a, const Lds &l, const Combine *cb = n
                 v.w = v.w * r * w.w;
                 *xp = v;
             }
-        } else {
-            for (int t = 0; t < a.Tc; ++t) {
-                float ss = 0.f;
-                const float *xr = a.X + size_t(t) * a.ldx;
-                for (int k = tid; k < sh.K; k += kThreads) {
-                    const float v = xr[k];
-                    ss = fmaf(v, v, ss);
-                }
-                ss = block_sum(ss, l.red);
-                if (tid == 0) l.rinv[t] = 1.0f / sqrtf(ss / static_cast<float>(sh.K) + a.eps);
-            }
-            __syncthreads();
         }
     } else if (x_full) {
         stage_x(0, false);

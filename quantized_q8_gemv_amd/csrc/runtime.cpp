@@ -218,6 +218,8 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
     return launch_argmax_finish(d, m->at<float>(m->lay.lm_part), st, s);
 }
 
+// Decode graph variant for a cache length: the power-of-two number of
+// attention splits that covers it.
 int split_bucket(const q8l_model *m, int kv_len) {
     const int need = (kv_len + attn_chunk(m->d.hd) - 1) / attn_chunk(m->d.hd);
     int b = 1;
@@ -525,8 +527,9 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     std::vector<hipEvent_t> ev(size_t(2) * reps * kKinds, nullptr);
     for (auto &e : ev) Q8L_HIP(m, hipEventCreate(&e), "hipEventCreate");
     hipError_t err = hipSuccess;
+    auto used = [&](int) { return true; };  // every kind runs in the decode step
     for (int k = 0; k < kKinds && err == hipSuccess; ++k)
-        for (int r = 0; r < reps && err == hipSuccess; ++r) {
+        for (int r = 0; r < reps && err == hipSuccess && used(k); ++r) {
             hipEvent_t *p = &ev[(size_t(k) * reps + r) * 2];
             if ((err = hipEventRecord(p[0], s)) != hipSuccess) break;
             if ((err = launch(k)) != hipSuccess) break;
@@ -535,7 +538,7 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     if (err == hipSuccess) err = hipStreamSynchronize(s);
     for (int k = 0; k < kKinds && err == hipSuccess; ++k) {
         double sum = 0.0;
-        for (int r = 0; r < reps; ++r) {
+        for (int r = 0; r < reps && used(k); ++r) {
             float ms = 0.f;
             hipEvent_t *p = &ev[(size_t(k) * reps + r) * 2];
             if ((err = hipEventElapsedTime(&ms, p[0], p[1])) != hipSuccess) break;
