@@ -116,9 +116,14 @@ __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
 // Merge the split partials into O (single-op path; the forward merges them
 // in the o-projection's prologue instead). Fixed split order.
 __global__ __launch_bounds__(kThreads) void k_attn_combine(const float *part, int n_splits,
-                                                          int active, int nh, int hd, float *o) {
+                                                          int active, int nh, int hd, float *o,
+                                                          const StepState *st) {
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= nh * hd) return;
+    if (st) {  // graph replay: the cache length comes from the step state
+        const int C = attn_chunk(hd);
+        active = min((st->slot + 1 + C - 1) / C, n_splits);
+    }
     const int h = e / hd, d = e - h * hd;
     const float *pb = part + size_t(h) * n_splits * (hd + 2);
     float M = -INFINITY;
@@ -417,11 +422,11 @@ hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int nh, int hd,
-                               float *o, hipStream_t s) {
+                               float *o, const StepState *st, hipStream_t s) {
     const int active = std::min((kv_len + attn_chunk(hd) - 1) / attn_chunk(hd), n_splits);
     const int n = nh * hd;
     hipLaunchKernelGGL(k_attn_combine, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
-                       part, n_splits, active, nh, hd, o);
+                       part, n_splits, active, nh, hd, o, st);
     return hipGetLastError();
 }
 

@@ -481,45 +481,6 @@ struct LmHeadArgs {
     float eps;
 };
 
-// Logits for this workgroup's rows, plus the workgroup's (max, index) pair.
-// The pairs are merged by k_argmax_finish (a second, one-workgroup launch):
-// a device-wide atomic per workgroup would serialize at the memory side.
-template <bool MULTI>
-__global__ __launch_bounds__(kThreads) void k_lmhead(LmHeadArgs a) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    const Lds l = carve(smem, a.sh, 1, 1);
-    __shared__ float s_red[4];
-    __shared__ uint32_t s_redi[4];
-    CoreArgs c;
-    c.W[0] = a.W; c.W[1] = nullptr; c.nmat = 1; c.sh = a.sh; c.N = a.V;
-    c.row0 = blockIdx.x * a.sh.NR; c.Tc = 1;
-    c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<1, X_PLAIN, MULTI>(c, l);
-    const int nrows = min(a.sh.NR, a.V - c.row0);
-    float *logits = a.st->logits_out;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    float bv = -INFINITY;
-    uint32_t bi = uint32_t(c.row0);
-    for (int r = tid; r < nrows; r += kThreads) {
-        const float v = l.outv[r];
-        logits[c.row0 + r] = v;
-        argmax_merge(bv, bi, v, uint32_t(c.row0 + r));
-    }
-    wave_argmax(bv, bi);
-    if (lane == 0) {
-        s_red[wid] = bv;
-        s_redi[wid] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float v = s_red[0];
-        uint32_t i = s_redi[0];
-        for (int w = 1; w < 4; ++w) argmax_merge(v, i, s_red[w], s_redi[w]);
-        a.partials[2 * blockIdx.x] = v;
-        a.partials[2 * blockIdx.x + 1] = __uint_as_float(i);
-    }
-}
-
 // Merge n (value, index) partials in a fixed order; lowest index on ties.
 __device__ void argmax_reduce(const float *partials, int n, float &bv, uint32_t &bi) {
     __shared__ float red[4];
@@ -591,6 +552,298 @@ __global__ __launch_bounds__(kThreads) void k_argmax_out(const float *partials, 
     if (threadIdx.x == 0) *out = i;
 }
 
+// ---------------------------------------------------------------- decode (T = 1)
+//
+// A decode workgroup stages the whole activation row once (normalised, or
+// merged from attention partials) and then walks row tiles
+// blockIdx.x, blockIdx.x + gridDim.x, ...: the next tile's weights are issued
+// into registers while the current tile is computed, so the weight stream
+// never waits on the activation staging and the row is read once per
+// workgroup instead of once per tile.
+
+struct Lds1 {
+    uint32_t *wt;   // nmat*NR*PC*17 dwords (reused for partials)
+    float *xs;      // P*kXPad: the whole activation row
+    float *outv;    // max(nmat*NR, 4)
+    float *red;     // 4
+};
+
+__host__ __device__ inline size_t lds1_bytes(const GemvShape &sh, int nmat) {
+    size_t b = align16(size_t(nmat) * sh.NR * sh.PC * kPairBytes);
+    b += align16(size_t(sh.P) * kXPad * 4);
+    b += align16((size_t(nmat) * sh.NR > 4 ? size_t(nmat) * sh.NR : 4) * 4);
+    b += 16;
+    return b;
+}
+
+__device__ inline Lds1 carve1(uint8_t *smem, const GemvShape &sh, int nmat) {
+    Lds1 l;
+    size_t off = 0;
+    l.wt = reinterpret_cast<uint32_t *>(smem + off);
+    off += align16(size_t(nmat) * sh.NR * sh.PC * kPairBytes);
+    l.xs = reinterpret_cast<float *>(smem + off);
+    off += align16(size_t(sh.P) * kXPad * 4);
+    l.outv = reinterpret_cast<float *>(smem + off);
+    off += align16((size_t(nmat) * sh.NR > 4 ? size_t(nmat) * sh.NR : 4) * 4);
+    l.red = reinterpret_cast<float *>(smem + off);
+    return l;
+}
+
+// The whole row u (K values) into xs in pair layout; the caller syncs.
+template <int XM>
+__device__ void stage_row1(const CoreArgs &a, const Lds1 &l, const Combine *cb) {
+    const int tid = threadIdx.x;
+    const int n4 = a.sh.P * 16;
+    if (XM == X_ATTN_COMBINE) {
+        for (int e = tid; e < n4; e += kThreads) {
+            const int k = e * 4;
+            float4 v;
+            v.x = combine_elem(*cb, k);
+            v.y = combine_elem(*cb, k + 1);
+            v.z = combine_elem(*cb, k + 2);
+            v.w = combine_elem(*cb, k + 3);
+            *reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4) = v;
+        }
+        return;
+    }
+    float ss = 0.f;
+    for (int e = tid; e < n4; e += kThreads) {
+        const float4 v = *reinterpret_cast<const float4 *>(a.X + size_t(e) * 4);
+        *reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4) = v;
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+    }
+    if (!a.norm_w) return;
+    ss = block_sum(ss, l.red);
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(a.sh.K) + a.eps);
+    for (int e = tid; e < n4; e += kThreads) {
+        float4 *xp = reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4);
+        const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + size_t(e) * 4);
+        float4 v = *xp;
+        v.x = v.x * r * w.x;
+        v.y = v.y * r * w.y;
+        v.z = v.z * r * w.z;
+        v.w = v.w * r * w.w;
+        *xp = v;
+    }
+}
+
+// One row tile: outv[m*NR + r] = sum_k W_m[row0+r][k] * u[k]. Chunk 0 of this
+// tile is already in `st`; the next tile's chunk 0 is issued during the last
+// chunk (when has_next).
+template <bool MULTI>
+__device__ void tile_run1(const CoreArgs &c, const Lds1 &l, int nrows, bool vec, WStage &st,
+                          const CoreArgs &n, int nn, bool nvec, bool has_next) {
+    const int tid = threadIdx.x;
+    const GemvShape &sh = c.sh;
+    const int per_mat = nrows * sh.PC;
+    const int units = c.nmat * per_mat;
+    const int nchunks = MULTI ? sh.P / sh.PC : 1;
+    const int up = tid < units ? (tid % per_mat) % sh.PC : 0;
+    float acc = 0.f;
+    for (int ch = 0; ch < nchunks; ++ch) {
+        stage_store(c, nrows, ch, vec, st, l.wt);
+        if (MULTI && ch + 1 < nchunks)
+            stage_issue(c, nrows, ch + 1, vec, st);
+        else if (has_next)
+            stage_issue(n, nn, 0, nvec, st);
+        __syncthreads();
+        if (tid < units) {
+            float dA, sA, dB, sB;
+            pair_dot1(l.wt + size_t(tid) * (kPairBytes / 4), l.xs + size_t(ch * sh.PC + up) * kXPad,
+                      dA, sA, dB, sB);
+            acc = fmaf(dA, sA, acc);
+            acc = fmaf(dB, sB, acc);
+        }
+        __syncthreads();
+    }
+    float *part = reinterpret_cast<float *>(l.wt);
+    if (tid < units) part[tid] = acc;
+    __syncthreads();
+    const int lane = tid & 63, wid = tid >> 6;
+    const int items = c.nmat * nrows;
+    for (int it = wid; it < items; it += 4) {
+        const float *src = part + size_t(it) * sh.PC;
+        float v = 0.f;
+        for (int p = lane; p < sh.PC; p += 64) v += src[p];
+        v = wave_sum(v);
+        if (lane == 0) {
+            const int m = it / nrows, r = it - m * nrows;
+            l.outv[m * sh.NR + r] = v;
+        }
+    }
+    __syncthreads();
+}
+
+__device__ inline int tile_rows(const CoreArgs &c) { return min(c.sh.NR, c.N - c.row0); }
+
+// q/k/v with rope and the KV write, T = 1.
+template <bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const Lds1 l = carve1(smem, a.sh, 1);
+    const int ntiles = a.tq + 2 * a.tk;
+    auto ref = [&](int tile, int &kind) {
+        CoreArgs c{};
+        c.nmat = 1; c.sh = a.sh; c.Tc = 1; c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
+        if (tile < a.tq) {
+            kind = 0; c.W[0] = a.wq; c.N = a.QD;
+        } else if (tile < a.tq + a.tk) {
+            kind = 1; c.W[0] = a.wk; c.N = a.KVD; tile -= a.tq;
+        } else {
+            kind = 2; c.W[0] = a.wv; c.N = a.KVD; tile -= a.tq + a.tk;
+        }
+        c.row0 = tile * a.sh.NR;
+        return c;
+    };
+    int tile = blockIdx.x, kind;
+    CoreArgs c = ref(tile, kind);
+    int nrows = tile_rows(c);
+    bool vec = tile_vec(c, nrows);
+    WStage st;
+    stage_issue(c, nrows, 0, vec, st);
+    stage_row1<X_PLAIN>(c, l, nullptr);
+    const int pos = a.st->pos, slot = a.st->slot;
+    for (; tile < ntiles; tile += gridDim.x) {
+        const bool has_next = tile + int(gridDim.x) < ntiles;
+        int nkind = 0;
+        CoreArgs n = has_next ? ref(tile + gridDim.x, nkind) : c;
+        const int nn = has_next ? tile_rows(n) : 0;
+        const bool nvec = has_next ? tile_vec(n, nn) : false;
+        tile_run1<MULTI>(c, l, nrows, vec, st, n, nn, nvec, has_next);
+        for (int e = threadIdx.x; e < nrows / 2; e += kThreads) {
+            const int r = 2 * e;
+            const float a0 = l.outv[r], a1 = l.outv[r + 1];
+            const int row = c.row0 + r;
+            const int d = row % a.hd;
+            if (kind == 2) {
+                float *dst = a.vc + (size_t(row / a.hd) * a.max_seq + slot) * a.hd + d;
+                dst[0] = a0;
+                dst[1] = a1;
+            } else {
+                const float2 cs = a.rope[size_t(pos) * (a.hd / 2) + (d >> 1)];
+                const float b0 = a0 * cs.x - a1 * cs.y;
+                const float b1 = a0 * cs.y + a1 * cs.x;
+                float *dst = (kind == 0) ? a.q + row
+                                         : a.kc + (size_t(row / a.hd) * a.max_seq + slot) * a.hd + d;
+                dst[0] = b0;
+                dst[1] = b1;
+            }
+        }
+        c = n; nrows = nn; vec = nvec; kind = nkind;
+    }
+}
+
+template <bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const Lds1 l = carve1(smem, a.sh, 2);
+    const int ntiles = (a.F + a.sh.NR - 1) / a.sh.NR;
+    CoreArgs c{};
+    c.W[0] = a.wg; c.W[1] = a.wu; c.nmat = 2; c.sh = a.sh; c.N = a.F; c.Tc = 1;
+    c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
+    int tile = blockIdx.x;
+    c.row0 = tile * a.sh.NR;
+    int nrows = tile_rows(c);
+    bool vec = tile_vec(c, nrows);
+    WStage st;
+    stage_issue(c, nrows, 0, vec, st);
+    stage_row1<X_PLAIN>(c, l, nullptr);
+    for (; tile < ntiles; tile += gridDim.x) {
+        const bool has_next = tile + int(gridDim.x) < ntiles;
+        CoreArgs n = c;
+        n.row0 = (tile + gridDim.x) * a.sh.NR;
+        const int nn = has_next ? tile_rows(n) : 0;
+        const bool nvec = has_next ? tile_vec(n, nn) : false;
+        tile_run1<MULTI>(c, l, nrows, vec, st, n, nn, nvec, has_next);
+        for (int r = threadIdx.x; r < nrows; r += kThreads)
+            a.h[c.row0 + r] = silu(l.outv[r]) * l.outv[a.sh.NR + r];
+        c = n; nrows = nn; vec = nvec;
+    }
+}
+
+template <int XM, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const Lds1 l = carve1(smem, a.sh, 1);
+    const int ntiles = (a.N + a.sh.NR - 1) / a.sh.NR;
+    CoreArgs c{};
+    c.W[0] = a.W; c.nmat = 1; c.sh = a.sh; c.N = a.N; c.Tc = 1;
+    c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
+    int tile = blockIdx.x;
+    c.row0 = tile * a.sh.NR;
+    int nrows = tile_rows(c);
+    bool vec = tile_vec(c, nrows);
+    WStage st;
+    stage_issue(c, nrows, 0, vec, st);
+    stage_row1<XM>(c, l, &a.cb);
+    for (; tile < ntiles; tile += gridDim.x) {
+        const bool has_next = tile + int(gridDim.x) < ntiles;
+        CoreArgs n = c;
+        n.row0 = (tile + gridDim.x) * a.sh.NR;
+        const int nn = has_next ? tile_rows(n) : 0;
+        const bool nvec = has_next ? tile_vec(n, nn) : false;
+        tile_run1<MULTI>(c, l, nrows, vec, st, n, nn, nvec, has_next);
+        for (int r = threadIdx.x; r < nrows; r += kThreads) {
+            float *dst = a.y + c.row0 + r;
+            *dst = a.accumulate ? *dst + l.outv[r] : l.outv[r];
+        }
+        c = n; nrows = nn; vec = nvec;
+    }
+}
+
+template <bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_lmhead1(LmHeadArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const Lds1 l = carve1(smem, a.sh, 1);
+    __shared__ float s_red[4];
+    __shared__ uint32_t s_redi[4];
+    const int ntiles = (a.V + a.sh.NR - 1) / a.sh.NR;
+    CoreArgs c{};
+    c.W[0] = a.W; c.nmat = 1; c.sh = a.sh; c.N = a.V; c.Tc = 1;
+    c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
+    int tile = blockIdx.x;
+    c.row0 = tile * a.sh.NR;
+    int nrows = tile_rows(c);
+    bool vec = tile_vec(c, nrows);
+    WStage st;
+    stage_issue(c, nrows, 0, vec, st);
+    stage_row1<X_PLAIN>(c, l, nullptr);
+    float *logits = a.st->logits_out;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    float bv = -INFINITY;
+    uint32_t bi = uint32_t(c.row0);
+    for (; tile < ntiles; tile += gridDim.x) {
+        const bool has_next = tile + int(gridDim.x) < ntiles;
+        CoreArgs n = c;
+        n.row0 = (tile + gridDim.x) * a.sh.NR;
+        const int nn = has_next ? tile_rows(n) : 0;
+        const bool nvec = has_next ? tile_vec(n, nn) : false;
+        tile_run1<MULTI>(c, l, nrows, vec, st, n, nn, nvec, has_next);
+        for (int r = tid; r < nrows; r += kThreads) {
+            const float v = l.outv[r];
+            logits[c.row0 + r] = v;
+            argmax_merge(bv, bi, v, uint32_t(c.row0 + r));
+        }
+        c = n; nrows = nn; vec = nvec;
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) {
+        s_red[wid] = bv;
+        s_redi[wid] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float v = s_red[0];
+        uint32_t i = s_redi[0];
+        for (int w = 1; w < 4; ++w) argmax_merge(v, i, s_red[w], s_redi[w]);
+        a.partials[2 * blockIdx.x] = v;
+        a.partials[2 * blockIdx.x + 1] = __uint_as_float(i);
+    }
+}
+
 // ---------------------------------------------------------------- host side
 
 int divisor_at_most(int P, int cap) {
@@ -621,6 +874,13 @@ GemvShape choose_shape(int N, int K, int maxt, int nmat, int target_wgs, int nr_
     return s;
 }
 
+// Decode grid: one workgroup per tile up to what the chip holds at once (by
+// LDS use), beyond that workgroups loop over tiles.
+int grid1(int ntiles, size_t lds) {
+    const size_t per_cu = std::max<size_t>(1, std::min<size_t>(8, (160 * 1024) / std::max<size_t>(lds, 1)));
+    return std::max(1, std::min(ntiles, int(256 * per_cu)));
+}
+
 static hipError_t set_lds(const void *fn, size_t bytes) {
     if (bytes <= 64 * 1024) return hipSuccess;
     return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
@@ -639,16 +899,20 @@ hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const S
     a.sh = choose_shape(a.QD + 2 * a.KVD, d.H, maxt, 1, 512, 2);
     a.tq = (a.QD + a.sh.NR - 1) / a.sh.NR;
     a.tk = (a.KVD + a.sh.NR - 1) / a.sh.NR;
+    if (T == 1) {  // decode: row-looping kernel
+        const size_t lds = lds1_bytes(a.sh, 1);
+        const int g = grid1(a.tq + 2 * a.tk, lds);
+        if (a.sh.PC != a.sh.P)
+            hipLaunchKernelGGL(k_qkv1<true>, dim3(g), dim3(kThreads), lds, s, a);
+        else
+            hipLaunchKernelGGL(k_qkv1<false>, dim3(g), dim3(kThreads), lds, s, a);
+        return hipGetLastError();
+    }
     dim3 grid(a.tq + 2 * a.tk, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 1, maxt);
     const bool multi = a.sh.PC != a.sh.P;
-    if (maxt == 1) {
-        if (multi) hipLaunchKernelGGL((k_qkv<1, true>), grid, dim3(kThreads), lds, s, a);
-        else hipLaunchKernelGGL((k_qkv<1, false>), grid, dim3(kThreads), lds, s, a);
-    } else {
-        if (multi) hipLaunchKernelGGL((k_qkv<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
-        else hipLaunchKernelGGL((k_qkv<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
-    }
+    if (multi) hipLaunchKernelGGL((k_qkv<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
+    else hipLaunchKernelGGL((k_qkv<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -659,16 +923,20 @@ hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, floa
     a.wg = w.wg; a.wu = w.wu; a.norm_w = w.ffn_norm; a.x = x; a.h = h; a.F = d.F; a.T = T;
     a.eps = d.eps;
     a.sh = choose_shape(d.F, d.H, maxt, 2, 512, 1);
+    if (T == 1) {
+        const size_t lds = lds1_bytes(a.sh, 2);
+        const int g = grid1((d.F + a.sh.NR - 1) / a.sh.NR, lds);
+        if (a.sh.PC != a.sh.P)
+            hipLaunchKernelGGL(k_gateup1<true>, dim3(g), dim3(kThreads), lds, s, a);
+        else
+            hipLaunchKernelGGL(k_gateup1<false>, dim3(g), dim3(kThreads), lds, s, a);
+        return hipGetLastError();
+    }
     dim3 grid((d.F + a.sh.NR - 1) / a.sh.NR, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 2, maxt);
     const bool multi = a.sh.PC != a.sh.P;
-    if (maxt == 1) {
-        if (multi) hipLaunchKernelGGL((k_gateup<1, true>), grid, dim3(kThreads), lds, s, a);
-        else hipLaunchKernelGGL((k_gateup<1, false>), grid, dim3(kThreads), lds, s, a);
-    } else {
-        if (multi) hipLaunchKernelGGL((k_gateup<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
-        else hipLaunchKernelGGL((k_gateup<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
-    }
+    if (multi) hipLaunchKernelGGL((k_gateup<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
+    else hipLaunchKernelGGL((k_gateup<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -680,16 +948,20 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
     a.W = W; a.norm_w = norm_w; a.x = X; a.y = Y; a.N = N; a.T = T; a.accumulate = accumulate;
     a.eps = eps;
     a.sh = choose_shape(N, K, maxt, 1, 512, 1);
+    if (T == 1) {
+        const size_t lds = lds1_bytes(a.sh, 1);
+        const int g = grid1((N + a.sh.NR - 1) / a.sh.NR, lds);
+        if (a.sh.PC != a.sh.P)
+            hipLaunchKernelGGL((k_matmul1<X_PLAIN, true>), dim3(g), dim3(kThreads), lds, s, a);
+        else
+            hipLaunchKernelGGL((k_matmul1<X_PLAIN, false>), dim3(g), dim3(kThreads), lds, s, a);
+        return hipGetLastError();
+    }
     dim3 grid((N + a.sh.NR - 1) / a.sh.NR, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 1, maxt);
     const bool multi = a.sh.PC != a.sh.P;
-    if (maxt == 1) {
-        if (multi) hipLaunchKernelGGL((k_matmul<1, X_PLAIN, true>), grid, dim3(kThreads), lds, s, a);
-        else hipLaunchKernelGGL((k_matmul<1, X_PLAIN, false>), grid, dim3(kThreads), lds, s, a);
-    } else {
-        if (multi) hipLaunchKernelGGL((k_matmul<kMaxTokChunk, X_PLAIN, true>), grid, dim3(kThreads), lds, s, a);
-        else hipLaunchKernelGGL((k_matmul<kMaxTokChunk, X_PLAIN, false>), grid, dim3(kThreads), lds, s, a);
-    }
+    if (multi) hipLaunchKernelGGL((k_matmul<kMaxTokChunk, X_PLAIN, true>), grid, dim3(kThreads), lds, s, a);
+    else hipLaunchKernelGGL((k_matmul<kMaxTokChunk, X_PLAIN, false>), grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -702,15 +974,18 @@ hipError_t launch_oproj_combine(const uint8_t *Wo, int H, int QD, const float *p
     a.cb.part = part; a.cb.st = st; a.cb.n_splits = n_splits; a.cb.hd = hd;
     a.cb.chunk = attn_chunk(hd);
     a.sh = choose_shape(H, QD, 1, 1, 512, 1);
-    if (a.sh.PC != a.sh.P) return hipErrorInvalidValue;  // the merged row must fit one staging
-    dim3 grid((H + a.sh.NR - 1) / a.sh.NR, 1);
-    hipLaunchKernelGGL((k_matmul<1, X_ATTN_COMBINE, false>), grid, dim3(kThreads), lds_bytes(a.sh, 1, 1), s, a);
+    const size_t lds = lds1_bytes(a.sh, 1);
+    const int g = grid1((H + a.sh.NR - 1) / a.sh.NR, lds);
+    if (a.sh.PC != a.sh.P)
+        hipLaunchKernelGGL((k_matmul1<X_ATTN_COMBINE, true>), dim3(g), dim3(kThreads), lds, s, a);
+    else
+        hipLaunchKernelGGL((k_matmul1<X_ATTN_COMBINE, false>), dim3(g), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
 static int lmhead_blocks(int V, int K) {
-    const int nr = choose_shape(V, K, 1, 1, 1024, 1).NR;
-    return (V + nr - 1) / nr;
+    const GemvShape sh = choose_shape(V, K, 1, 1, 1024, 1);
+    return grid1((V + sh.NR - 1) / sh.NR, lds1_bytes(sh, 1));
 }
 
 hipError_t launch_lmhead(const Dims &d, const uint8_t *Wout, const float *out_norm,
@@ -720,10 +995,11 @@ hipError_t launch_lmhead(const Dims &d, const uint8_t *Wout, const float *out_no
     a.V = d.V; a.eps = d.eps;
     a.sh = choose_shape(d.V, d.H, 1, 1, 1024, 1);
     const int nb = lmhead_blocks(d.V, d.H);
+    const size_t lds = lds1_bytes(a.sh, 1);
     if (a.sh.PC != a.sh.P)
-        hipLaunchKernelGGL(k_lmhead<true>, dim3(nb), dim3(kThreads), lds_bytes(a.sh, 1, 1), s, a);
+        hipLaunchKernelGGL(k_lmhead1<true>, dim3(nb), dim3(kThreads), lds, s, a);
     else
-        hipLaunchKernelGGL(k_lmhead<false>, dim3(nb), dim3(kThreads), lds_bytes(a.sh, 1, 1), s, a);
+        hipLaunchKernelGGL(k_lmhead1<false>, dim3(nb), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 

@@ -110,8 +110,9 @@ struct AttnDecodeArgs {
     float scale;
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s);
+// Merge split partials into o; with st set, kv_len is read from st->slot + 1.
 hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int nh, int hd,
-                               float *o, hipStream_t s);
+                               float *o, const StepState *st, hipStream_t s);
 int attn_decode_splits(int kv_len, int hd);
 __host__ __device__ int attn_chunk(int hd);
 size_t lmhead_partials_bytes(int V, int K);

@@ -188,8 +188,13 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = decode_splits;
             a.scale = 1.0f / sqrtf(float(d.hd));
             if ((e = launch_attn_decode(a, s)) != hipSuccess) return e;
-            if ((e = launch_oproj_combine(w.wo, d.H, QD, a.part, st, decode_splits, d.hd, x, s)) != hipSuccess)
-                return e;
+            if (decode_splits == 1) {  // one split: its normalisation is merged into the o-projection
+                e = launch_oproj_combine(w.wo, d.H, QD, a.part, st, 1, d.hd, x, s);
+            } else {                   // several: one merge kernel, then the plain o-projection
+                e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s);
+                if (e == hipSuccess) e = launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, x, s);
+            }
+            if (e != hipSuccess) return e;
         } else {
             AttnPrefillArgs a;
             a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.o = att;
@@ -516,7 +521,9 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
             case 0: return launch_embed(m->tok_embd, d.H, d.V, S, m->at<uint32_t>(m->lay.tok), 1, 1, x, s);
             case 1: return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
             case 2: return launch_attn_decode(a, s);
-            case 3: return launch_oproj_combine(w.wo, d.H, QD, a.part, S, a.n_splits, d.hd, x, s);
+            case 3:
+                if (a.n_splits == 1) return launch_oproj_combine(w.wo, d.H, QD, a.part, S, 1, d.hd, x, s);
+                return launch_matmul(w.wo, d.H, QD, m->at<float>(m->lay.att), 1, nullptr, d.eps, 1, x, s);
             case 4: return launch_gateup(d, w, x, h, 1, s);
             case 5: return launch_matmul(w.wd, d.H, d.F, h, 1, nullptr, d.eps, 1, x, s);
             case 6: return launch_lmhead(d, wout, m->out_norm, x, S, m->at<float>(m->lay.lm_part), s);
@@ -617,7 +624,7 @@ q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int3
         a.n_splits = (kv_len + attn_chunk(hd) - 1) / attn_chunk(hd);
         a.scale = 1.0f / sqrtf(float(hd));
         e = launch_attn_decode(a, s);
-        if (e == hipSuccess) e = launch_attn_combine(a.part, a.n_splits, kv_len, n_head, hd, O, s);
+        if (e == hipSuccess) e = launch_attn_combine(a.part, a.n_splits, kv_len, n_head, hd, O, nullptr, s);
     } else {
         AttnPrefillArgs a;
         a.q = Q; a.kc = K; a.vc = V; a.o = O; a.T = T; a.kv_len = kv_len; a.kv_stride = kv_stride;

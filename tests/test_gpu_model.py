@@ -167,3 +167,29 @@ def test_big_gqa_shape_two_layers():
     gm = gpu_model(m)
     ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 4, "7b-width 64+4")
     log(f"7b-width: max abs err {err:.3g}")
+
+
+@pytest.fixture(scope="module")
+def big_full():
+    """The full 7B-class shape (32 layers, 7.7 GB of Q8_0 weights)."""
+    w, m, prompt = synth.workload_inputs("C5")
+    log(f"7b full: {m.total_bytes / 1e9:.2f} GB generated")
+    return m, prompt, gpu_model(m)
+
+
+def test_big_gqa_full_depth_matches_oracle(big_full):
+    """Short prompt at full depth against the oracle (its cost grows with T)."""
+    m, prompt, gm = big_full
+    ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt[:4], 3, "7b full 4+3")
+    log(f"7b full 4+3: max abs err {err:.3g}, near ties {ties}")
+    assert ties <= 1
+
+
+def test_big_gqa_full_depth_prefill_equals_decode_chain(big_full):
+    """Prefill of 64 tokens (MFMA path) = the same tokens fed one at a time (GEMV path)."""
+    m, prompt, gm = big_full
+    toks = prompt[:64]
+    full, _ = gm.forward(toks, 0)
+    for i, t in enumerate(toks):
+        step, _ = gm.forward([t], i)
+    assert_logits_close(step, full, "7b full: prefill 64 vs 64 single-token steps")
