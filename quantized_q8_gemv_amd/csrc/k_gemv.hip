@@ -764,6 +764,99 @@ __global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) {
     }
 }
 
+// Large K (several chunks), no norm: chunk-outer, tile-inner. Only one
+// activation chunk is in LDS at a time (so more workgroups fit per CU); each
+// thread keeps one accumulator per tile of its workgroup (at most kTilesPerWg)
+// across chunks; the tiles are reduced and written at the end.
+constexpr int kTilesPerWg = 8;
+
+__host__ __device__ inline size_t lds1c_bytes(const GemvShape &sh) {
+    return align16(size_t(sh.NR) * sh.PC * kPairBytes) + align16(size_t(sh.PC) * kXPad * 4) +
+           align16(size_t(sh.NR > 4 ? sh.NR : 4) * 4) + 16;
+}
+
+__global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const GemvShape &sh = a.sh;
+    uint32_t *wt = reinterpret_cast<uint32_t *>(smem);
+    float *xs = reinterpret_cast<float *>(smem + align16(size_t(sh.NR) * sh.PC * kPairBytes));
+    float *outv = xs + align16(size_t(sh.PC) * kXPad * 4) / 4;
+    const int tid = threadIdx.x;
+    const int ntiles = (a.N + sh.NR - 1) / sh.NR;
+    const int nchunks = sh.P / sh.PC;
+    CoreArgs base{};
+    base.W[0] = a.W; base.nmat = 1; base.sh = sh; base.N = a.N; base.Tc = 1;
+    int my_tiles = 0;
+    for (int k = 0; k < kTilesPerWg; ++k) my_tiles += (int(blockIdx.x) + k * int(gridDim.x) < ntiles) ? 1 : 0;
+    float acc[kTilesPerWg];
+#pragma unroll
+    for (int k = 0; k < kTilesPerWg; ++k) acc[k] = 0.f;
+
+    CoreArgs cur = base;
+    cur.row0 = int(blockIdx.x) * sh.NR;
+    int nrows = tile_rows(cur);
+    bool vec = tile_vec(cur, nrows);
+    WStage st;
+    stage_issue(cur, nrows, 0, vec, st);
+    for (int ch = 0; ch < nchunks; ++ch) {
+        __syncthreads();  // the previous chunk's activations are no longer read
+        const int n4 = sh.PC * 16;
+        for (int e = tid; e < n4; e += kThreads) {
+            const float4 v = *reinterpret_cast<const float4 *>(a.x + size_t(ch) * sh.PC * kPairWeights + size_t(e) * 4);
+            *reinterpret_cast<float4 *>(xs + (e >> 4) * kXPad + (e & 15) * 4) = v;
+        }
+#pragma unroll
+        for (int k = 0; k < kTilesPerWg; ++k) {
+            if (k < my_tiles) {
+                // the next (tile, chunk) in stream order
+                int nk = k + 1, nch = ch;
+                if (nk >= my_tiles) { nk = 0; ++nch; }
+                const bool has_next = nch < nchunks;
+                CoreArgs n = base;
+                n.row0 = (int(blockIdx.x) + nk * int(gridDim.x)) * sh.NR;
+                const int nn = has_next ? tile_rows(n) : 0;
+                const bool nvec = has_next ? tile_vec(n, nn) : false;
+                stage_store(cur, nrows, ch, vec, st, wt);
+                if (has_next) stage_issue(n, nn, nch, nvec, st);
+                __syncthreads();
+                const int units = nrows * sh.PC;
+                if (tid < units) {
+                    float dA, sA, dB, sB;
+                    pair_dot1(wt + size_t(tid) * (kPairBytes / 4), xs + size_t(tid % sh.PC) * kXPad, dA, sA, dB, sB);
+                    acc[k] = fmaf(dA, sA, acc[k]);
+                    acc[k] = fmaf(dB, sB, acc[k]);
+                }
+                __syncthreads();
+                cur = n; nrows = nn; vec = nvec;
+            }
+        }
+    }
+    // reduce and write each tile
+    float *part = reinterpret_cast<float *>(wt);
+    const int lane = tid & 63, wid = tid >> 6;
+#pragma unroll
+    for (int k = 0; k < kTilesPerWg; ++k) {
+        if (k < my_tiles) {
+            const int row0 = (int(blockIdx.x) + k * int(gridDim.x)) * sh.NR;
+            const int nr = min(sh.NR, a.N - row0);
+            if (tid < nr * sh.PC) part[tid] = acc[k];
+            __syncthreads();
+            for (int r = wid; r < nr; r += 4) {
+                float v = 0.f;
+                for (int p = lane; p < sh.PC; p += 64) v += part[r * sh.PC + p];
+                v = wave_sum(v);
+                if (lane == 0) outv[r] = v;
+            }
+            __syncthreads();
+            for (int r = tid; r < nr; r += kThreads) {
+                float *dst = a.y + row0 + r;
+                *dst = a.accumulate ? *dst + outv[r] : outv[r];
+            }
+            __syncthreads();
+        }
+    }
+}
+
 template <int XM, bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -949,6 +1042,13 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
     a.eps = eps;
     a.sh = choose_shape(N, K, maxt, 1, 512, 1);
     if (T == 1) {
+        if (a.sh.PC != a.sh.P && !norm_w) {  // large K: chunk-outer walk
+            const size_t lds = lds1c_bytes(a.sh);
+            const int ntiles = (N + a.sh.NR - 1) / a.sh.NR;
+            const int g = std::max(grid1(ntiles, lds), (ntiles + kTilesPerWg - 1) / kTilesPerWg);
+            hipLaunchKernelGGL(k_matmul1_chunked, dim3(g), dim3(kThreads), lds, s, a);
+            return hipGetLastError();
+        }
         const size_t lds = lds1_bytes(a.sh, 1);
         const int g = grid1((N + a.sh.NR - 1) / a.sh.NR, lds);
         if (a.sh.PC != a.sh.P)
