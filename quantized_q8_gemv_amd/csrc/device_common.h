@@ -139,4 +139,12 @@ __device__ __forceinline__ void wave_argmax(float &v, uint32_t &i) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// v as an f16 pair: hi = f16(v) at hi[i], lo = f16(v - hi) at hi[plane + i]
+// (the layout the matrix-matrix kernel reads its activations in).
+__device__ __forceinline__ void store_hilo(_Float16 *hi, size_t plane, size_t i, float v) {
+    const _Float16 h = static_cast<_Float16>(v);
+    hi[i] = h;
+    hi[plane + i] = static_cast<_Float16>(v - static_cast<float>(h));
+}
+
 }  // namespace q8l

@@ -227,8 +227,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill(AttnPrefillArgs a) {
         }
     }
     if (qi < nq) {
-        float *dst = a.o + size_t(q0 + qi) * row_stride + h * hd;
-        for (int k = 0; k < ndim; ++k) dst[sub + 8 * k] = o[k] / lsum;
+        const size_t base = size_t(q0 + qi) * row_stride + h * hd;
+        if (a.o_split) {
+            const size_t plane = size_t(a.T) * row_stride;
+            for (int k = 0; k < ndim; ++k) store_hilo(a.o_split, plane, base + sub + 8 * k, o[k] / lsum);
+        } else {
+            for (int k = 0; k < ndim; ++k) a.o[base + sub + 8 * k] = o[k] / lsum;
+        }
     }
 }
 
@@ -395,11 +400,20 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
     }
     if (qi < a.T) {
         const float inv = 1.0f / lsum;
-        float *dst = a.o + size_t(qi) * row_stride + h * HD;
+        const size_t base = size_t(qi) * row_stride + h * HD;
+        if (a.o_split) {
+            const size_t plane = size_t(a.T) * row_stride;
 #pragma unroll
-        for (int t = 0; t < HD / 16; ++t)
+            for (int t = 0; t < HD / 16; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[t * 16 + 4 * grp + i] = o[t][i] * inv;
+                for (int i = 0; i < 4; ++i) store_hilo(a.o_split, plane, base + t * 16 + 4 * grp + i, o[t][i] * inv);
+        } else {
+            float *dst = a.o + base;
+#pragma unroll
+            for (int t = 0; t < HD / 16; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[t * 16 + 4 * grp + i] = o[t][i] * inv;
+        }
     }
 }
 

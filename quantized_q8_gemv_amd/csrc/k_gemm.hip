@@ -7,18 +7,23 @@
 // gfx950 has v_mfma_f32_16x16x32_f16, whose K = 32 is exactly one Q8_0 block.
 // Per 32-wide block and 16x16 output tile:
 //   * B = the block's int8 values as f16 (exact: |q| <= 127);
-//   * A = the activations split as f16 hi + f16 lo (u = hi + lo to ~2^-22
-//     relative), two MFMAs accumulate (hi + lo) . q in f32;
+//   * A = the activations as an f16 pair hi + lo (u = hi + lo to ~2^-22
+//     relative); two MFMAs accumulate (hi + lo) . q in f32;
 //   * the block's f16 scale d (one per output column = one per lane) is then
 //     applied in f32: acc += d * tile.
 // The result is f32-accurate up to summation order; the int8 values are never
 // rounded and the scale is never folded into f16.
 //
-// Workgroup tile: 64 tokens x 128 output rows, K in steps of 64 (one block
-// pair per row, 68 bytes, 4-byte aligned). Per step: activations f32 -> hi/lo
-// f16 in LDS (RMSNorm applied on the way when the projection has one), raw
-// Q8_0 pairs -> LDS -> f16 values + f32 scales in LDS. 4 waves, each owns a
-// 64 x 32 slice (4 x 2 MFMA tiles).
+// Activations arrive already split: the RMSNorm kernel, the attention kernel
+// and the gate/up epilogue write their outputs as an f16 hi plane [T][K]
+// followed by an f16 lo plane, so a K step of A is a plain copy. (The single-op
+// entry point passes f32 activations; that variant splits them on the way into
+// LDS.)
+//
+// Workgroup tile TM tokens x TN output rows, 4 waves in 2 x 2, K in steps of
+// 64 (one block pair per row, 68 bytes, 4-byte aligned). Software pipeline:
+// the global loads of step k+1 are issued into registers before the MFMAs of
+// step k run from LDS; two LDS buffers, one barrier per step.
 
 #include <algorithm>
 
@@ -29,22 +34,19 @@ namespace q8l {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int GM = 64;     // tokens per workgroup tile
-constexpr int GN = 128;    // output rows per workgroup tile
 constexpr int GK = 64;     // weights per K step (two Q8_0 blocks)
 constexpr int LPAD = 72;   // halves per LDS row (64 + 8)
 
 enum GemmEpi { G_STORE = 0, G_ACCUM = 1, G_QKV = 2, G_GATEUP = 3 };
 
 struct GemmArgs {
-    const float *X;        // [T][K] f32 activations
-    const float *rinv;     // [T] RMSNorm factors (with norm_w) or null
-    const float *norm_w;   // [K] or null
+    const void *A;         // A32: f32 [T][K]; else f16 hi plane [T][K] then lo plane [T][K]
     const uint8_t *W[3];   // matrices (q, k, v | gate, up | single)
     int Nm[3];             // rows of each matrix
-    int tiles[3];          // N tiles of each matrix (QKV); GATEUP: tiles of 64 rows
+    int tiles[3];          // row tiles of each matrix (QKV)
     int T, K, rowbytes;
     // G_STORE / G_ACCUM
     float *Y;              // [T][N]
@@ -53,173 +55,270 @@ struct GemmArgs {
     const float2 *rope;
     float *q, *kc, *vc;
     int QD, hd, max_seq;
-    // G_GATEUP
-    float *h;              // [T][F]
+    // G_GATEUP: h = silu(gate) * up as f16 hi plane [T][F] then lo plane
+    _Float16 *h;
 };
 
-struct GemmLds {
-    _Float16 ahi[GM * LPAD];
-    _Float16 alo[GM * LPAD];
-    _Float16 bq[GN * LPAD];
-    float bd[GN * 2];
-    uint32_t braw[GN * 17];
+template <int TM, int TN>
+struct Cfg {
+    static constexpr int WM = TM / 2, WN = TN / 2;       // wave tile
+    static constexpr int MS = WM / 16, NS = WN / 16;     // MFMA tiles per wave
+    static constexpr int AP = TM * 16 / kThreads;        // 16-byte A pieces per thread per step
+    static constexpr int BU = TN * 4 / kThreads;         // B quarter rows per thread per step
+    static constexpr int A_HALVES = TM * LPAD;
+    static constexpr int B_HALVES = TN * LPAD;
+    static constexpr size_t BUF = sizeof(_Float16) * (2 * A_HALVES + B_HALVES) + sizeof(float) * TN * 2;
+    static constexpr size_t LDS = 2 * BUF;
+    static_assert(AP >= 1 && BU >= 1 && MS >= 1 && NS >= 1, "tile too small");
+    static_assert(BUF % 16 == 0, "LDS buffer alignment");
+    static_assert(size_t(TM) * WN * sizeof(float) <= LDS, "gate/up exchange fits");
 };
 
-template <int EPI>
+struct GBuf {
+    _Float16 *ahi, *alo, *bq;
+    float *bd;
+};
+
+template <int TM, int TN>
+__device__ inline GBuf gbuf(uint8_t *smem, int k) {
+    using C = Cfg<TM, TN>;
+    GBuf b;
+    uint8_t *p = smem + size_t(k) * C::BUF;
+    b.ahi = reinterpret_cast<_Float16 *>(p);
+    b.alo = b.ahi + C::A_HALVES;
+    b.bq = b.alo + C::A_HALVES;
+    b.bd = reinterpret_cast<float *>(b.bq + C::B_HALVES);
+    return b;
+}
+
+// Registers holding one K step of global data in flight.
+template <int TM, int TN>
+struct GRegs {
+    u32x4 a[Cfg<TM, TN>::AP];
+    uint32_t b[Cfg<TM, TN>::BU][5];
+};
+
+// Quarter qd of a 68-byte block pair (dwords): 0 -> d0 + q0..15 of block 0
+// (dwords 0..4), 1 -> q16..31 + d1 (4..8), 2 -> q0..15 of block 1 (9..13, the
+// last unused), 3 -> q16..31 of block 1 (12..16, the first unused).
+__device__ inline int quarter_base(int qd) { return qd == 0 ? 0 : qd == 1 ? 4 : qd == 2 ? 9 : 12; }
+
+template <bool A32, int TM, int TN, int EPI>
+__device__ inline void g_load(const GemmArgs &a, int m0, int row0, const int nvalid[2],
+                              const uint8_t *const Wb[2], int ks, GRegs<TM, TN> &r) {
+    using C = Cfg<TM, TN>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::AP; ++i) {
+        const int c = tid + i * kThreads;
+        int m;
+        size_t off;  // bytes
+        if (A32) {
+            m = c >> 4;
+            off = (size_t(m0 + m) * a.K + size_t(ks) * GK + (c & 15) * 4) * sizeof(float);
+        } else {
+            const int plane = c / (TM * 8), rr = c - plane * (TM * 8);
+            m = rr >> 3;
+            off = (size_t(plane) * a.T * a.K + size_t(m0 + m) * a.K + size_t(ks) * GK + (rr & 7) * 8) *
+                  sizeof(_Float16);
+        }
+        if (m0 + m < a.T)
+            r.a[i] = *reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(a.A) + off);
+        else
+            r.a[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < C::BU; ++i) {
+        const int u = tid + i * kThreads;
+        const int b = u >> 2, qd = u & 3;
+        const int part = (EPI == G_GATEUP) ? (b >= TN / 2) : 0;
+        const int rr = (EPI == G_GATEUP) ? (b - part * (TN / 2)) : b;
+        if (rr < nvalid[part]) {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(
+                                      Wb[part] + size_t(row0 + rr) * a.rowbytes + size_t(ks) * kPairBytes) +
+                                  quarter_base(qd);
+#pragma unroll
+            for (int j = 0; j < 5; ++j) r.b[i][j] = src[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 5; ++j) r.b[i][j] = 0u;
+        }
+    }
+}
+
+// int8 x 4 (one dword) -> 4 exact f16 values: bias each byte to an unsigned
+// value u = q + 128, place it in the mantissa of 1024.0 (f16 bits 0x6400 | u)
+// and subtract 1152 = 1024 + 128.
+__device__ inline void q4_to_half(uint32_t w, half2v &lo, half2v &hi) {
+    const uint32_t x = w ^ 0x80808080u;
+    const uint32_t l = __builtin_amdgcn_perm(0x64646464u, x, 0x05010400u);
+    const uint32_t h = __builtin_amdgcn_perm(0x64646464u, x, 0x07030602u);
+    const half2v bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+    lo = __builtin_bit_cast(half2v, l) - bias;
+    hi = __builtin_bit_cast(half2v, h) - bias;
+}
+
+template <bool A32, int TM, int TN>
+__device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf) {
+    using C = Cfg<TM, TN>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < C::AP; ++i) {
+        const int c = tid + i * kThreads;
+        if (A32) {
+            const int m = c >> 4, c4 = c & 15;
+            const float4 v = __builtin_bit_cast(float4, r.a[i]);
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+            _Float16 hi[4], lo[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                hi[k] = static_cast<_Float16>(vv[k]);
+                lo[k] = static_cast<_Float16>(vv[k] - static_cast<float>(hi[k]));
+            }
+            *reinterpret_cast<uint2 *>(bf.ahi + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, hi);
+            *reinterpret_cast<uint2 *>(bf.alo + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, lo);
+        } else {
+            const int plane = c / (TM * 8), rr = c - plane * (TM * 8);
+            const int m = rr >> 3, p = rr & 7;
+            *reinterpret_cast<u32x4 *>((plane ? bf.alo : bf.ahi) + m * LPAD + p * 8) = r.a[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < C::BU; ++i) {
+        const int u = tid + i * kThreads;
+        const int b = u >> 2, qd = u & 3;
+        const uint32_t *w = r.b[i];
+        const uint32_t shift = qd < 2 ? 2u : 0u;
+        half2v v[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t q4 = qd == 3 ? w[k + 1] : __builtin_amdgcn_alignbyte(w[k + 1], w[k], shift);
+            q4_to_half(q4, v[2 * k], v[2 * k + 1]);
+        }
+        const u32x4 s0 = u32x4{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                               __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
+        const u32x4 s1 = u32x4{__builtin_bit_cast(uint32_t, v[4]), __builtin_bit_cast(uint32_t, v[5]),
+                               __builtin_bit_cast(uint32_t, v[6]), __builtin_bit_cast(uint32_t, v[7])};
+        _Float16 *dst = bf.bq + b * LPAD + (qd >> 1) * 32 + (qd & 1) * 16;
+        *reinterpret_cast<u32x4 *>(dst) = s0;
+        *reinterpret_cast<u32x4 *>(dst + 8) = s1;
+        if (qd == 0) bf.bd[b * 2 + 0] = half_bits_to_float(w[0] & 0xffffu);
+        if (qd == 1) bf.bd[b * 2 + 1] = half_bits_to_float(w[4] >> 16);
+    }
+}
+
+template <int EPI, int TM, int TN, bool A32>
 __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
-    __shared__ __align__(16) GemmLds L;
+    using C = Cfg<TM, TN>;
+    extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int m0 = blockIdx.x * GM;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int m0 = blockIdx.x * TM;
 
-    // Which weight row feeds B row b of this tile (b in [0, GN)).
-    int mat = 0, row0 = 0, rows_in_tile = GN;
+    // Which weight rows feed B rows [0, TN) of this tile.
+    int mat = 0, row0 = 0;
     const uint8_t *Wb[2] = {nullptr, nullptr};
     int nvalid[2] = {0, 0};
     if (EPI == G_GATEUP) {
-        row0 = blockIdx.y * (GN / 2);
+        row0 = blockIdx.y * (TN / 2);
         Wb[0] = a.W[0];
         Wb[1] = a.W[1];
-        nvalid[0] = nvalid[1] = min(GN / 2, a.Nm[0] - row0);
+        nvalid[0] = nvalid[1] = min(TN / 2, a.Nm[0] - row0);
     } else {
         int t = blockIdx.y;
         if (EPI == G_QKV) {
             while (mat < 2 && t >= a.tiles[mat]) t -= a.tiles[mat++];
         }
-        row0 = t * GN;
+        row0 = t * TN;
         Wb[0] = a.W[mat];
-        nvalid[0] = min(GN, a.Nm[mat] - row0);
-        rows_in_tile = nvalid[0];
+        nvalid[0] = min(TN, a.Nm[mat] - row0);
     }
-    (void)rows_in_tile;
 
-    f32x4 acc[4][2];
+    f32x4 acc[C::MS][C::NS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::MS; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < C::NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nsteps = a.K / GK;
+    GRegs<TM, TN> regs;
+    g_load<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, 0, regs);
     for (int ks = 0; ks < nsteps; ++ks) {
-        // activations: 64 rows x 64 f32 -> hi/lo f16
-        for (int e = tid; e < GM * 16; e += kThreads) {
-            const int m = e >> 4, c4 = e & 15;
-            const int k = ks * GK + c4 * 4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (m0 + m < a.T) {
-                v = *reinterpret_cast<const float4 *>(a.X + size_t(m0 + m) * a.K + k);
-                if (a.norm_w) {
-                    const float r = a.rinv[m0 + m];
-                    const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + k);
-                    v.x = v.x * r * w.x;
-                    v.y = v.y * r * w.y;
-                    v.z = v.z * r * w.z;
-                    v.w = v.w * r * w.w;
-                }
-            }
-            const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const _Float16 hi = static_cast<_Float16>(vv[i]);
-                const _Float16 lo = static_cast<_Float16>(vv[i] - static_cast<float>(hi));
-                L.ahi[m * LPAD + c4 * 4 + i] = hi;
-                L.alo[m * LPAD + c4 * 4 + i] = lo;
-            }
-        }
-        // raw Q8_0 pairs: GN rows x 17 dwords
-        for (int e = tid; e < GN * 17; e += kThreads) {
-            const int b = e / 17, j = e - b * 17;
-            const int part = (EPI == G_GATEUP) ? (b >= GN / 2) : 0;
-            const int r = (EPI == G_GATEUP) ? (b - part * (GN / 2)) : b;
-            uint32_t v = 0;
-            if (r < nvalid[part])
-                v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(
-                    Wb[part] + size_t(row0 + r) * a.rowbytes + size_t(ks) * kPairBytes) + j);
-            L.braw[e] = v;
-        }
+        const GBuf bf = gbuf<TM, TN>(smem, ks & 1);
+        g_store<A32, TM, TN>(regs, bf);
         __syncthreads();
-        // decode: int8 -> f16 values, f16 scales -> f32
-        for (int e = tid; e < GN * 16; e += kThreads) {
-            const int b = e >> 4, j = e & 15;
-            const uint32_t *raw = L.braw + b * 17;
-            const uint32_t q4 = (j < 8) ? __builtin_amdgcn_alignbyte(raw[j + 1], raw[j], 2) : raw[9 + (j - 8)];
-            _Float16 *dst = L.bq + b * LPAD + 4 * j;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dst[i] = static_cast<_Float16>(static_cast<float>(static_cast<int8_t>((q4 >> (8 * i)) & 0xffu)));
-            if (j == 0) L.bd[b * 2 + 0] = half_bits_to_float(raw[0]);
-            if (j == 8) L.bd[b * 2 + 1] = half_bits_to_float(raw[8] >> 16);
-        }
-        __syncthreads();
-        // MFMA: wave owns columns [wave*32, wave*32 + 32)
+        if (ks + 1 < nsteps) g_load<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, ks + 1, regs);
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-            half8 bf[2];
-            float dsc[2];
+            half8 bfr[C::NS];
+            float dsc[C::NS];
 #pragma unroll
-            for (int ns = 0; ns < 2; ++ns) {
-                const int col = wave * 32 + ns * 16 + (lane & 15);
-                bf[ns] = *reinterpret_cast<const half8 *>(L.bq + col * LPAD + hb * 32 + 8 * (lane >> 4));
-                dsc[ns] = L.bd[col * 2 + hb];
+            for (int ns = 0; ns < C::NS; ++ns) {
+                const int col = wn * C::WN + ns * 16 + (lane & 15);
+                bfr[ns] = *reinterpret_cast<const half8 *>(bf.bq + col * LPAD + hb * 32 + 8 * (lane >> 4));
+                dsc[ns] = bf.bd[col * 2 + hb];
             }
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
-                const int row = ms * 16 + (lane & 15);
-                const half8 ah = *reinterpret_cast<const half8 *>(L.ahi + row * LPAD + hb * 32 + 8 * (lane >> 4));
-                const half8 al = *reinterpret_cast<const half8 *>(L.alo + row * LPAD + hb * 32 + 8 * (lane >> 4));
+            for (int ms = 0; ms < C::MS; ++ms) {
+                const int row = wm * C::WM + ms * 16 + (lane & 15);
+                const half8 ah = *reinterpret_cast<const half8 *>(bf.ahi + row * LPAD + hb * 32 + 8 * (lane >> 4));
+                const half8 al = *reinterpret_cast<const half8 *>(bf.alo + row * LPAD + hb * 32 + 8 * (lane >> 4));
 #pragma unroll
-                for (int ns = 0; ns < 2; ++ns) {
-                    f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bf[ns], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bf[ns], t, 0, 0, 0);
+                for (int ns = 0; ns < C::NS; ++ns) {
+                    f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bfr[ns], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bfr[ns], t, 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[ms][ns][i] = fmaf(dsc[ns], t[i], acc[ms][ns][i]);
                 }
             }
         }
-        __syncthreads();
     }
 
-    // ---- epilogue: acc[ms][ns][i] is (m, c) = (ms*16 + 4*(lane/16) + i, wave*32 + ns*16 + lane%16)
+    // ---- epilogue: acc[ms][ns][i] is (m, c) with
+    //      m = wm*WM + ms*16 + 4*(lane/16) + i, c = wn*WN + ns*16 + lane%16
     if (EPI == G_GATEUP) {
-        // waves 2, 3 hold the up rows: pass them to waves 0, 1 through LDS
-        float *ub = reinterpret_cast<float *>(L.ahi);  // 64 x 64 f32 = 16 KB (ahi+alo)
-        if (wave >= 2) {
+        // waves with wn = 1 hold the up rows: pass them to the wn = 0 waves through LDS
+        __syncthreads();  // every wave is done with the K-step buffers
+        float *ub = reinterpret_cast<float *>(smem);  // TM x WN f32
+        if (wn == 1) {
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
+            for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-                for (int ns = 0; ns < 2; ++ns)
+                for (int ns = 0; ns < C::NS; ++ns)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int m = ms * 16 + 4 * (lane >> 4) + i;
-                        const int c = (wave - 2) * 32 + ns * 16 + (lane & 15);
-                        ub[m * 64 + c] = acc[ms][ns][i];
+                        const int m = wm * C::WM + ms * 16 + 4 * (lane >> 4) + i;
+                        const int c = ns * 16 + (lane & 15);
+                        ub[m * C::WN + c] = acc[ms][ns][i];
                     }
         }
         __syncthreads();
-        if (wave < 2) {
+        if (wn == 0) {
+            const size_t plane = size_t(a.T) * a.Nm[0];
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
+            for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-                for (int ns = 0; ns < 2; ++ns)
+                for (int ns = 0; ns < C::NS; ++ns)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int m = ms * 16 + 4 * (lane >> 4) + i;
-                        const int c = wave * 32 + ns * 16 + (lane & 15);
+                        const int m = wm * C::WM + ms * 16 + 4 * (lane >> 4) + i;
+                        const int c = ns * 16 + (lane & 15);
                         if (m0 + m < a.T && c < nvalid[0]) {
-                            const float g = acc[ms][ns][i], u = ub[m * 64 + c];
-                            a.h[size_t(m0 + m) * a.Nm[0] + row0 + c] = silu(g) * u;
+                            const float g = acc[ms][ns][i], u = ub[m * C::WN + c];
+                            store_hilo(a.h, plane, size_t(m0 + m) * a.Nm[0] + row0 + c, silu(g) * u);
                         }
                     }
         }
         return;
     }
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
+    for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
+        for (int ns = 0; ns < C::NS; ++ns)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = ms * 16 + 4 * (lane >> 4) + i;
-                const int c = wave * 32 + ns * 16 + (lane & 15);
+                const int m = wm * C::WM + ms * 16 + 4 * (lane >> 4) + i;
+                const int c = wn * C::WN + ns * 16 + (lane & 15);
                 const float v = acc[ms][ns][i];
                 if (EPI == G_QKV) {
                     // rope pairs (2j, 2j+1) sit in adjacent lanes
@@ -246,65 +345,112 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
             }
 }
 
-// rinv[t] = 1 / sqrt(mean(x[t]^2) + eps), one workgroup per row.
-__global__ __launch_bounds__(kThreads) void k_rms_rows(const float *x, int K, float eps, float *rinv) {
+// u = x / sqrt(mean(x^2) + eps) * w for each token row, written as the f16
+// hi plane [T][K] followed by the lo plane. One workgroup per row.
+__global__ __launch_bounds__(kThreads) void k_rms_split(const float *x, int T, int K, const float *w,
+                                                        float eps, _Float16 *u) {
     __shared__ float red[4];
-    const float *xr = x + size_t(blockIdx.x) * K;
+    const size_t row = blockIdx.x;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + row * K);
+    const int n4 = K / 4;
     float ss = 0.f;
-    for (int k = threadIdx.x; k < K; k += kThreads) ss = fmaf(xr[k], xr[k], ss);
+    for (int e = threadIdx.x; e < n4; e += kThreads) {
+        const float4 v = xr[e];
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+    }
     ss = block_sum(ss, red);
-    if (threadIdx.x == 0) rinv[blockIdx.x] = 1.0f / sqrtf(ss / static_cast<float>(K) + eps);
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(K) + eps);
+    const size_t plane = size_t(T) * K;
+    for (int e = threadIdx.x; e < n4; e += kThreads) {
+        const float4 v = xr[e];
+        const float4 g = reinterpret_cast<const float4 *>(w)[e];
+        const float vv[4] = {v.x * r * g.x, v.y * r * g.y, v.z * r * g.z, v.w * r * g.w};
+        _Float16 hi[4], lo[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            hi[k] = static_cast<_Float16>(vv[k]);
+            lo[k] = static_cast<_Float16>(vv[k] - static_cast<float>(hi[k]));
+        }
+        *reinterpret_cast<uint2 *>(u + row * K + e * 4) = __builtin_bit_cast(uint2, hi);
+        *reinterpret_cast<uint2 *>(u + plane + row * K + e * 4) = __builtin_bit_cast(uint2, lo);
+    }
 }
 
-}  // namespace
+int row_tiles(int n, int tn) { return (n + tn - 1) / tn; }
 
-hipError_t launch_rms_rows(const float *x, int T, int K, float eps, float *rinv, hipStream_t s) {
-    hipLaunchKernelGGL(k_rms_rows, dim3(T), dim3(kThreads), 0, s, x, K, eps, rinv);
+// Tile choice: the large tile (64 x 128) when it still gives every CU a
+// workgroup, otherwise the small one (32 x 64: short prompts, narrow matrices).
+bool large_tiles(int T, int n_tiles_large) {
+    return long((T + 63) / 64) * n_tiles_large >= 256;
+}
+
+template <int EPI, int TM, int TN, bool A32>
+hipError_t launch_cfg(const GemmArgs &a, int ytiles, hipStream_t s) {
+    using C = Cfg<TM, TN>;
+    if (C::LDS > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_q8<EPI, TM, TN, A32>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid((a.T + TM - 1) / TM, ytiles);
+    hipLaunchKernelGGL((k_gemm_q8<EPI, TM, TN, A32>), grid, dim3(kThreads), C::LDS, s, a);
     return hipGetLastError();
 }
 
-static GemmArgs gemm_base(const float *X, const float *rinv, const float *norm_w, int T, int K) {
+template <int EPI, bool A32>
+hipError_t launch_plain(const GemmArgs &a, int N, hipStream_t s) {
+    if (large_tiles(a.T, row_tiles(N, 128))) return launch_cfg<EPI, 64, 128, A32>(a, row_tiles(N, 128), s);
+    return launch_cfg<EPI, 32, 64, A32>(a, row_tiles(N, 64), s);
+}
+
+GemmArgs gemm_base(const void *A, int T, int K) {
     GemmArgs a{};
-    a.X = X; a.rinv = rinv; a.norm_w = norm_w; a.T = T; a.K = K;
+    a.A = A; a.T = T; a.K = K;
     a.rowbytes = K / kQK * kQBytes;
     return a;
 }
 
-hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const float *X, int T,
-                              const float *rinv, const float *norm_w, int accumulate, float *Y,
-                              hipStream_t s) {
-    GemmArgs a = gemm_base(X, rinv, norm_w, T, K);
-    a.W[0] = W; a.Nm[0] = N; a.Y = Y;
-    dim3 grid((T + GM - 1) / GM, (N + GN - 1) / GN);
-    if (accumulate)
-        hipLaunchKernelGGL(k_gemm_q8<G_ACCUM>, grid, dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_gemm_q8<G_STORE>, grid, dim3(kThreads), 0, s, a);
+}  // namespace
+
+hipError_t launch_rms_split(const float *x, int T, int K, const float *w, float eps, _Float16 *u,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(k_rms_split, dim3(T), dim3(kThreads), 0, s, x, T, K, w, eps, u);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const float *x, const float *rinv,
-                           const StepState *st, const float2 *rope, float *q, float *kc, float *vc,
-                           int T, hipStream_t s) {
-    GemmArgs a = gemm_base(x, rinv, w.attn_norm, T, d.H);
+hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
+                              int accumulate, float *Y, hipStream_t s) {
+    GemmArgs a = gemm_base(A, T, K);
+    a.W[0] = W; a.Nm[0] = N; a.Y = Y;
+    if (a_split)
+        return accumulate ? launch_plain<G_ACCUM, false>(a, N, s) : launch_plain<G_STORE, false>(a, N, s);
+    return accumulate ? launch_plain<G_ACCUM, true>(a, N, s) : launch_plain<G_STORE, true>(a, N, s);
+}
+
+hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u, const StepState *st,
+                           const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s) {
+    GemmArgs a = gemm_base(u, T, d.H);
     const int QD = d.nh * d.hd, KVD = d.nkv * d.hd;
     a.W[0] = w.wq; a.W[1] = w.wk; a.W[2] = w.wv;
     a.Nm[0] = QD; a.Nm[1] = KVD; a.Nm[2] = KVD;
-    for (int i = 0; i < 3; ++i) a.tiles[i] = (a.Nm[i] + GN - 1) / GN;
     a.st = st; a.rope = rope; a.q = q; a.kc = kc; a.vc = vc;
     a.QD = QD; a.hd = d.hd; a.max_seq = d.max_seq;
-    dim3 grid((T + GM - 1) / GM, a.tiles[0] + a.tiles[1] + a.tiles[2]);
-    hipLaunchKernelGGL(k_gemm_q8<G_QKV>, grid, dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    const bool large = large_tiles(T, row_tiles(QD, 128) + 2 * row_tiles(KVD, 128));
+    const int tn = large ? 128 : 64;
+    for (int i = 0; i < 3; ++i) a.tiles[i] = row_tiles(a.Nm[i], tn);
+    const int yt = a.tiles[0] + a.tiles[1] + a.tiles[2];
+    return large ? launch_cfg<G_QKV, 64, 128, false>(a, yt, s) : launch_cfg<G_QKV, 32, 64, false>(a, yt, s);
 }
 
-hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const float *x, const float *rinv,
-                              float *h, int T, hipStream_t s) {
-    GemmArgs a = gemm_base(x, rinv, w.ffn_norm, T, d.H);
+hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const _Float16 *u, _Float16 *h, int T,
+                              hipStream_t s) {
+    GemmArgs a = gemm_base(u, T, d.H);
     a.W[0] = w.wg; a.W[1] = w.wu; a.Nm[0] = d.F; a.Nm[1] = d.F; a.h = h;
-    dim3 grid((T + GM - 1) / GM, (d.F + GN / 2 - 1) / (GN / 2));
-    hipLaunchKernelGGL(k_gemm_q8<G_GATEUP>, grid, dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    if (large_tiles(T, row_tiles(d.F, 64))) return launch_cfg<G_GATEUP, 64, 128, false>(a, row_tiles(d.F, 64), s);
+    return launch_cfg<G_GATEUP, 32, 64, false>(a, row_tiles(d.F, 32), s);
 }
 
 }  // namespace q8l

@@ -117,22 +117,24 @@ int attn_decode_splits(int kv_len, int hd);
 __host__ __device__ int attn_chunk(int hd);
 size_t lmhead_partials_bytes(int V, int K);
 
-// MFMA matrix-matrix path (prefill with T > kMaxTokChunk tokens).
-hipError_t launch_rms_rows(const float *x, int T, int K, float eps, float *rinv, hipStream_t s);
-hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const float *X, int T,
-                              const float *rinv, const float *norm_w, int accumulate, float *Y,
+// MFMA matrix-matrix path (prefill with T > kMaxTokChunk tokens). Activations
+// are passed as an f16 hi plane [T][K] followed by an f16 lo plane (a_split),
+// or as f32 [T][K].
+hipError_t launch_rms_split(const float *x, int T, int K, const float *w, float eps, _Float16 *u,
+                            hipStream_t s);
+hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
+                              int accumulate, float *Y, hipStream_t s);
+hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u, const StepState *st,
+                           const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s);
+hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const _Float16 *u, _Float16 *h, int T,
                               hipStream_t s);
-hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const float *x, const float *rinv,
-                           const StepState *st, const float2 *rope, float *q, float *kc, float *vc,
-                           int T, hipStream_t s);
-hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const float *x, const float *rinv,
-                              float *h, int T, hipStream_t s);
 
 // Prefill attention: T queries, causal mask offset by the cached prefix.
 struct AttnPrefillArgs {
     const float *q;        // [T][nh][hd]
     const float *kc, *vc;  // [nkv][kv_stride][hd]
-    float *o;              // [T][nh][hd]
+    float *o;              // [T][nh][hd] f32, or (o_split set) unused
+    _Float16 *o_split;     // when set: f16 hi plane [T][nh*hd], then the lo plane
     int T, kv_len, kv_stride, nh, nkv, hd;
     float scale;
 };

@@ -41,7 +41,7 @@ const char *kVersion = "q8l 0.1 (gfx950)";
 size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t state, counters, rope, tok, kc, vc, x, q, att, h, rinv, logits, lm_part, attn_part, total;
+    size_t state, counters, rope, tok, kc, vc, x, q, att, h, u, logits, lm_part, attn_part, total;
     size_t kv_layer;  // floats per layer in kc (and vc)
     int max_splits;
 };
@@ -90,7 +90,7 @@ Layout make_layout(const q8l_config *c) {
     L.q = take(S * QD * 4);
     L.att = take(S * QD * 4);
     L.h = take(S * size_t(c->n_ff) * 4);
-    L.rinv = take(S * 4);
+    L.u = take(S * H * 4);  // normalised activations as f16 hi + lo planes (prefill)
     L.logits = take(size_t(c->n_vocab) * 4);
     L.lm_part = take(std::max(lmhead_partials_bytes(c->n_vocab, c->n_embd), size_t(8)));
     L.attn_part = take(size_t(c->n_head) * L.max_splits * (hd + 2) * 4);
@@ -171,12 +171,13 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
     const float2 *rope = m->at<float2>(m->lay.rope);
     hipError_t e;
     const bool gemm = T > kMaxTokChunk;  // MFMA matrix-matrix path for long prompts
-    float *rinv = m->at<float>(m->lay.rinv);
+    _Float16 *u = m->at<_Float16>(m->lay.u);
+    _Float16 *att_s = m->at<_Float16>(m->lay.att), *h_s = m->at<_Float16>(m->lay.h);
     for (int l = 0; l < m->cfg.n_layer; ++l) {
         const LayerPtrs w = m->layer(l);
         if (gemm) {
-            if ((e = launch_rms_rows(x, T, d.H, d.eps, rinv, s)) != hipSuccess) return e;
-            if ((e = launch_gemm_qkv(d, w, x, rinv, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
+            if ((e = launch_rms_split(x, T, d.H, w.attn_norm, d.eps, u, s)) != hipSuccess) return e;
+            if ((e = launch_gemm_qkv(d, w, u, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
         } else {
             if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
         }
@@ -198,19 +199,20 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
         } else {
             AttnPrefillArgs a;
             a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.o = att;
+            a.o_split = gemm ? att_s : nullptr;  // the o-projection GEMM reads f16 hi + lo
             a.T = T; a.kv_len = kv_len_prefill; a.kv_stride = d.max_seq;
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.scale = 1.0f / sqrtf(float(d.hd));
             if ((e = launch_attn_prefill(a, s)) != hipSuccess) return e;
             if (gemm)
-                e = launch_gemm_matmul(w.wo, d.H, QD, att, T, nullptr, nullptr, 1, x, s);
+                e = launch_gemm_matmul(w.wo, d.H, QD, att_s, true, T, 1, x, s);
             else
                 e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s);
             if (e != hipSuccess) return e;
         }
         if (gemm) {
-            if ((e = launch_rms_rows(x, T, d.H, d.eps, rinv, s)) != hipSuccess) return e;
-            if ((e = launch_gemm_gateup(d, w, x, rinv, h, T, s)) != hipSuccess) return e;
-            if ((e = launch_gemm_matmul(w.wd, d.H, d.F, h, T, nullptr, nullptr, 1, x, s)) != hipSuccess) return e;
+            if ((e = launch_rms_split(x, T, d.H, w.ffn_norm, d.eps, u, s)) != hipSuccess) return e;
+            if ((e = launch_gemm_gateup(d, w, u, h_s, T, s)) != hipSuccess) return e;
+            if ((e = launch_gemm_matmul(w.wd, d.H, d.F, h_s, true, T, 1, x, s)) != hipSuccess) return e;
         } else {
             if ((e = launch_gateup(d, w, x, h, T, s)) != hipSuccess) return e;
             if ((e = launch_matmul(w.wd, d.H, d.F, h, T, nullptr, d.eps, 1, x, s)) != hipSuccess) return e;
@@ -588,8 +590,8 @@ q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *
         return Q8L_E_INVALID_ARG;
     hipError_t e;
     if (T > kMaxTokChunk && !norm_w)
-        e = launch_gemm_matmul(static_cast<const uint8_t *>(W), int(N), int(K), X, int(T), nullptr, nullptr,
-                               accumulate, Y, static_cast<hipStream_t>(stream));
+        e = launch_gemm_matmul(static_cast<const uint8_t *>(W), int(N), int(K), X, false, int(T), accumulate, Y,
+                               static_cast<hipStream_t>(stream));
     else
         e = launch_matmul(static_cast<const uint8_t *>(W), int(N), int(K), X, int(T), norm_w, float(eps),
                           accumulate, Y, static_cast<hipStream_t>(stream));
@@ -627,7 +629,7 @@ q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int3
         if (e == hipSuccess) e = launch_attn_combine(a.part, a.n_splits, kv_len, n_head, hd, O, nullptr, s);
     } else {
         AttnPrefillArgs a;
-        a.q = Q; a.kc = K; a.vc = V; a.o = O; a.T = T; a.kv_len = kv_len; a.kv_stride = kv_stride;
+        a.q = Q; a.kc = K; a.vc = V; a.o = O; a.o_split = nullptr; a.T = T; a.kv_len = kv_len; a.kv_stride = kv_stride;
         a.nh = n_head; a.nkv = n_head_kv; a.hd = hd; a.scale = 1.0f / sqrtf(float(hd));
         e = launch_attn_prefill(a, s);
     }
