@@ -28,9 +28,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wno-unused-variable"]
 
 
+# MFMA kernels keep their results in VGPRs (no AGPR round trip before the
+# per-block scale is applied in f32).
+PER_FILE = {"k_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+            "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, obj: str) -> None:
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + PER_FILE.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
 
 

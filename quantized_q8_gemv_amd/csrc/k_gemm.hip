@@ -22,8 +22,9 @@
 //
 // Workgroup tile TM tokens x TN output rows, 4 waves in 2 x 2, K in steps of
 // 64 (one block pair per row, 68 bytes, 4-byte aligned). Software pipeline:
-// the global loads of step k+1 are issued into registers before the MFMAs of
-// step k run from LDS; two LDS buffers, one barrier per step.
+// the global loads of the next few K steps are in flight in registers while
+// the MFMAs of the current step run from LDS (a step's MFMA work is far
+// shorter than a global round trip); two LDS buffers, one barrier per step.
 
 #include <algorithm>
 
@@ -69,6 +70,7 @@ struct Cfg {
     static constexpr int B_HALVES = TN * LPAD;
     static constexpr size_t BUF = sizeof(_Float16) * (2 * A_HALVES + B_HALVES) + sizeof(float) * TN * 2;
     static constexpr size_t LDS = 2 * BUF;
+    static constexpr int STAGES = 1;                     // K steps of global loads in flight
     static_assert(AP >= 1 && BU >= 1 && MS >= 1 && NS >= 1, "tile too small");
     static_assert(BUF % 16 == 0, "LDS buffer alignment");
     static_assert(size_t(TM) * WN * sizeof(float) <= LDS, "gate/up exchange fits");
@@ -103,46 +105,73 @@ struct GRegs {
 // last unused), 3 -> q16..31 of block 1 (12..16, the first unused).
 __device__ inline int quarter_base(int qd) { return qd == 0 ? 0 : qd == 1 ? 4 : qd == 2 ? 9 : 12; }
 
+// Buffer-load sources of a thread: one resource per operand and a fixed byte
+// offset per piece; a K step adds a uniform offset. Rows past the end of A or
+// W get an offset past the resource's size, so the hardware range check
+// returns zeros (no branches; those rows' results are never stored).
+constexpr uint32_t kOutOfRange = 0x80000000u;   // resources are < kOutOfRange bytes
+constexpr int kRsrcWord3 = 0x00020000;           // raw buffer, 32-bit data format
+
+template <int TM, int TN>
+struct GSrc {
+    __amdgpu_buffer_rsrc_t ra;
+    __amdgpu_buffer_rsrc_t rb[Cfg<TM, TN>::BU];
+    uint32_t aoff[Cfg<TM, TN>::AP];
+    uint32_t boff[Cfg<TM, TN>::BU];
+};
+
 template <bool A32, int TM, int TN, int EPI>
-__device__ inline void g_load(const GemmArgs &a, int m0, int row0, const int nvalid[2],
-                              const uint8_t *const Wb[2], int ks, GRegs<TM, TN> &r) {
+__device__ inline void g_setup(const GemmArgs &a, int m0, int row0, const int nvalid[2],
+                               const uint8_t *const Wb[2], GSrc<TM, TN> &g) {
     using C = Cfg<TM, TN>;
     const int tid = threadIdx.x;
+    const uint32_t abytes = uint32_t(size_t(a.T) * a.K * 4);  // f32, or two f16 planes
+    g.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.A), 0, int(abytes), kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < C::AP; ++i) {
         const int c = tid + i * kThreads;
-        int m;
-        size_t off;  // bytes
         if (A32) {
-            m = c >> 4;
-            off = (size_t(m0 + m) * a.K + size_t(ks) * GK + (c & 15) * 4) * sizeof(float);
+            const int m = c >> 4;
+            g.aoff[i] = m0 + m < a.T ? uint32_t((size_t(m0 + m) * a.K + (c & 15) * 4) * 4) : kOutOfRange;
         } else {
             const int plane = c / (TM * 8), rr = c - plane * (TM * 8);
-            m = rr >> 3;
-            off = (size_t(plane) * a.T * a.K + size_t(m0 + m) * a.K + size_t(ks) * GK + (rr & 7) * 8) *
-                  sizeof(_Float16);
+            const int m = rr >> 3;
+            g.aoff[i] = m0 + m < a.T
+                            ? uint32_t((size_t(plane) * a.T * a.K + size_t(m0 + m) * a.K + (rr & 7) * 8) * 2)
+                            : kOutOfRange;
         }
-        if (m0 + m < a.T)
-            r.a[i] = *reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(a.A) + off);
-        else
-            r.a[i] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < C::BU; ++i) {
         const int u = tid + i * kThreads;
         const int b = u >> 2, qd = u & 3;
-        const int part = (EPI == G_GATEUP) ? (b >= TN / 2) : 0;
+        // wave-uniform: a wave's B rows all come from one matrix
+        const int part = (EPI == G_GATEUP) ? __builtin_amdgcn_readfirstlane(b >= TN / 2 ? 1 : 0) : 0;
         const int rr = (EPI == G_GATEUP) ? (b - part * (TN / 2)) : b;
-        if (rr < nvalid[part]) {
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(
-                                      Wb[part] + size_t(row0 + rr) * a.rowbytes + size_t(ks) * kPairBytes) +
-                                  quarter_base(qd);
+        const uint8_t *W = part ? Wb[1] : Wb[0];
+        g.rb[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(W), 0,
+                                                    int(uint32_t(row0 + nvalid[part]) * uint32_t(a.rowbytes)),
+                                                    kRsrcWord3);
+        g.boff[i] = rr < nvalid[part] ? uint32_t(row0 + rr) * uint32_t(a.rowbytes) + quarter_base(qd) * 4
+                                      : kOutOfRange;
+    }
+}
+
+template <bool A32, int TM, int TN>
+__device__ inline void g_load(const GSrc<TM, TN> &g, int ks, GRegs<TM, TN> &r) {
+    using C = Cfg<TM, TN>;
+    const int sa = ks * GK * (A32 ? 4 : 2);
+    const int sb = ks * kPairBytes;
 #pragma unroll
-            for (int j = 0; j < 5; ++j) r.b[i][j] = src[j];
-        } else {
+    for (int i = 0; i < C::AP; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(g.ra, g.aoff[i], sa, 0);
 #pragma unroll
-            for (int j = 0; j < 5; ++j) r.b[i][j] = 0u;
-        }
+    for (int i = 0; i < C::BU; ++i) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(g.rb[i], g.boff[i], sb, 0);
+        r.b[i][0] = v.x;
+        r.b[i][1] = v.y;
+        r.b[i][2] = v.z;
+        r.b[i][3] = v.w;
+        r.b[i][4] = __builtin_amdgcn_raw_buffer_load_b32(g.rb[i], g.boff[i] + 16, sb, 0);
     }
 }
 
@@ -240,35 +269,48 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < C::NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // S register stages: the loads of steps ks+1 .. ks+S-1 are in flight while
+    // step ks is computed (the loop is unrolled by S so each stage is a fixed
+    // set of registers).
+    constexpr int S = C::STAGES;
     const int nsteps = a.K / GK;
-    GRegs<TM, TN> regs;
-    g_load<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, 0, regs);
-    for (int ks = 0; ks < nsteps; ++ks) {
-        const GBuf bf = gbuf<TM, TN>(smem, ks & 1);
-        g_store<A32, TM, TN>(regs, bf);
-        __syncthreads();
-        if (ks + 1 < nsteps) g_load<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, ks + 1, regs);
+    GSrc<TM, TN> src;
+    g_setup<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, src);
+    GRegs<TM, TN> regs[S];
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            half8 bfr[C::NS];
-            float dsc[C::NS];
+    for (int j = 0; j < S; ++j)
+        if (j < nsteps) g_load<A32, TM, TN>(src, j, regs[j]);
+    for (int k0 = 0; k0 < nsteps; k0 += S) {
 #pragma unroll
-            for (int ns = 0; ns < C::NS; ++ns) {
-                const int col = wn * C::WN + ns * 16 + (lane & 15);
-                bfr[ns] = *reinterpret_cast<const half8 *>(bf.bq + col * LPAD + hb * 32 + 8 * (lane >> 4));
-                dsc[ns] = bf.bd[col * 2 + hb];
-            }
+        for (int j = 0; j < S; ++j) {
+            const int ks = k0 + j;
+            if (ks >= nsteps) break;
+            const GBuf bf = gbuf<TM, TN>(smem, ks & 1);
+            g_store<A32, TM, TN>(regs[j], bf);
+            __syncthreads();
+            if (ks + S < nsteps) g_load<A32, TM, TN>(src, ks + S, regs[j]);
 #pragma unroll
-            for (int ms = 0; ms < C::MS; ++ms) {
-                const int row = wm * C::WM + ms * 16 + (lane & 15);
-                const half8 ah = *reinterpret_cast<const half8 *>(bf.ahi + row * LPAD + hb * 32 + 8 * (lane >> 4));
-                const half8 al = *reinterpret_cast<const half8 *>(bf.alo + row * LPAD + hb * 32 + 8 * (lane >> 4));
+            for (int hb = 0; hb < 2; ++hb) {
+                half8 bfr[C::NS];
+                float dsc[C::NS];
 #pragma unroll
                 for (int ns = 0; ns < C::NS; ++ns) {
-                    f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bfr[ns], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bfr[ns], t, 0, 0, 0);
+                    const int col = wn * C::WN + ns * 16 + (lane & 15);
+                    bfr[ns] = *reinterpret_cast<const half8 *>(bf.bq + col * LPAD + hb * 32 + 8 * (lane >> 4));
+                    dsc[ns] = bf.bd[col * 2 + hb];
+                }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[ms][ns][i] = fmaf(dsc[ns], t[i], acc[ms][ns][i]);
+                for (int ms = 0; ms < C::MS; ++ms) {
+                    const int row = wm * C::WM + ms * 16 + (lane & 15);
+                    const half8 ah = *reinterpret_cast<const half8 *>(bf.ahi + row * LPAD + hb * 32 + 8 * (lane >> 4));
+                    const half8 al = *reinterpret_cast<const half8 *>(bf.alo + row * LPAD + hb * 32 + 8 * (lane >> 4));
+#pragma unroll
+                    for (int ns = 0; ns < C::NS; ++ns) {
+                        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bfr[ns], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bfr[ns], t, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[ms][ns][i] = fmaf(dsc[ns], t[i], acc[ms][ns][i]);
+                    }
                 }
             }
         }
@@ -390,6 +432,10 @@ bool large_tiles(int T, int n_tiles_large) {
 template <int EPI, int TM, int TN, bool A32>
 hipError_t launch_cfg(const GemmArgs &a, int ytiles, hipStream_t s) {
     using C = Cfg<TM, TN>;
+    // buffer resources address < 2 GiB (offsets past that read as zeros)
+    if (size_t(a.T) * a.K * 4 >= kOutOfRange) return hipErrorInvalidValue;
+    for (int i = 0; i < 3; ++i)
+        if (a.W[i] && size_t(a.Nm[i]) * a.rowbytes >= kOutOfRange) return hipErrorInvalidValue;
     if (C::LDS > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_q8<EPI, TM, TN, A32>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
