@@ -1,4 +1,4 @@
-// k_gemm.hip -- Q8_0 x f32 matrix-matrix product on MFMA (prefill, T > 16).
+// k_gemm.hip -- Q8_0 x f32 matrix-matrix product on MFMA (prefill).
 //
 // Prefill runs every projection on T token rows at once ("生成一个 token",
 // section "prefill 和 decode：同一个 forward，不同的路": several input rows take

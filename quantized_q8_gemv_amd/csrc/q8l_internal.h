@@ -12,6 +12,7 @@ constexpr int kQBytes = 34;          // bytes per Q8_0 block
 constexpr int kPairBytes = 68;       // two blocks: the unit a lane decodes (4-byte aligned)
 constexpr int kPairWeights = 64;
 constexpr int kMaxTokChunk = 16;     // tokens per workgroup in the multi-token GEMV
+constexpr int kGemmMinTokens = 6;    // forward calls with at least this many tokens use the MFMA GEMM
 constexpr int kInlineTokens = 256;   // token ids passed in kernel arguments per launch
 constexpr int kAttnChunk = 64;       // keys per split in decode attention
 constexpr int kMaxGroup = 16;        // query heads per KV head supported in-kernel
@@ -117,7 +118,7 @@ int attn_decode_splits(int kv_len, int hd);
 __host__ __device__ int attn_chunk(int hd);
 size_t lmhead_partials_bytes(int V, int K);
 
-// MFMA matrix-matrix path (prefill with T > kMaxTokChunk tokens). Activations
+// MFMA matrix-matrix path (prefill with T >= kGemmMinTokens tokens). Activations
 // are passed as an f16 hi plane [T][K] followed by an f16 lo plane (a_split),
 // or as f32 [T][K].
 hipError_t launch_rms_split(const float *x, int T, int K, const float *w, float eps, _Float16 *u,

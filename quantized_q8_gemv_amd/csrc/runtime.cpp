@@ -170,7 +170,7 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
     float *att = m->at<float>(m->lay.att), *h = m->at<float>(m->lay.h);
     const float2 *rope = m->at<float2>(m->lay.rope);
     hipError_t e;
-    const bool gemm = T > kMaxTokChunk;  // MFMA matrix-matrix path for long prompts
+    const bool gemm = T >= kGemmMinTokens;  // MFMA matrix-matrix path for prompts
     _Float16 *u = m->at<_Float16>(m->lay.u);
     _Float16 *att_s = m->at<_Float16>(m->lay.att), *h_s = m->at<_Float16>(m->lay.h);
     for (int l = 0; l < m->cfg.n_layer; ++l) {
