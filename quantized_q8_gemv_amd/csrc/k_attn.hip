@@ -259,10 +259,10 @@ constexpr int FK = 64;    // keys per block
 
 template <int HD>
 struct FlashLds {
-    _Float16 kh[FK * (HD + 8)];
+    _Float16 kh[FK * (HD + 8)];     // K [key][d]
     _Float16 kl[FK * (HD + 8)];
-    _Float16 vh[FK * (HD + 8)];
-    _Float16 vl[FK * (HD + 8)];
+    _Float16 vh[HD * (FK + 8)];     // V^T [d][slot]: keys in P^T slot order
+    _Float16 vl[HD * (FK + 8)];
 };
 
 __device__ __forceinline__ void split16(float v, _Float16 &hi, _Float16 &lo) {
@@ -270,14 +270,86 @@ __device__ __forceinline__ void split16(float v, _Float16 &hi, _Float16 &lo) {
     lo = static_cast<_Float16>(v - static_cast<float>(hi));
 }
 
+__device__ __forceinline__ void split4(const float v[4], uint2 &hi, uint2 &lo) {
+    _Float16 h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split16(v[i], h[i], l[i]);
+    hi = __builtin_bit_cast(uint2, h);
+    lo = __builtin_bit_cast(uint2, l);
+}
+
+// Slot of key k (0..FK-1, a multiple of 4) in the P^T operand order: within a
+// 32-key step, keys 4g..4g+3 sit in slots 8g..8g+3 and keys 16+4g..16+4g+3 in
+// slots 8g+4..8g+7.
+__device__ __forceinline__ int key_slot(int k) {
+    const int kk = k & 31;
+    return (k & ~31) + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4);
+}
+
+// One key block of K and V in registers (loaded a block ahead).
+template <int HD>
+struct KvRegs {
+    float4 k[FK * HD / 4 / kThreads];
+    float v[FK * HD / kThreads];
+};
+
+template <int HD>
+__device__ __forceinline__ void kv_load(const float *kb, const float *vb, int j0, int blk_last, KvRegs<HD> &r) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < FK * HD / 4 / kThreads; ++i) {
+        const int e = tid + i * kThreads;
+        const int j = e / (HD / 4), d4 = (e - j * (HD / 4)) * 4;
+        r.k[i] = (j0 + j <= blk_last) ? *reinterpret_cast<const float4 *>(kb + size_t(j0 + j) * HD + d4)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < FK * HD / 4 / kThreads; ++i) {
+        const int e = tid + i * kThreads;       // (quad of keys, d): consecutive threads, consecutive d
+        const int quad = e / HD, d = e - quad * HD;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int key = j0 + 4 * quad + t;
+            r.v[4 * i + t] = (key <= blk_last) ? vb[size_t(key) * HD + d] : 0.f;
+        }
+    }
+}
+
+template <int HD>
+__device__ __forceinline__ void kv_store(const KvRegs<HD> &r, FlashLds<HD> &L) {
+    constexpr int LD = HD + 8, LV = FK + 8;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < FK * HD / 4 / kThreads; ++i) {
+        const int e = tid + i * kThreads;
+        const int j = e / (HD / 4), d4 = (e - j * (HD / 4)) * 4;
+        const float kk[4] = {r.k[i].x, r.k[i].y, r.k[i].z, r.k[i].w};
+        uint2 hi, lo;
+        split4(kk, hi, lo);
+        *reinterpret_cast<uint2 *>(L.kh + j * LD + d4) = hi;
+        *reinterpret_cast<uint2 *>(L.kl + j * LD + d4) = lo;
+    }
+#pragma unroll
+    for (int i = 0; i < FK * HD / 4 / kThreads; ++i) {
+        const int e = tid + i * kThreads;
+        const int quad = e / HD, d = e - quad * HD;
+        uint2 hi, lo;
+        split4(&r.v[4 * i], hi, lo);
+        const int slot = key_slot(4 * quad);
+        *reinterpret_cast<uint2 *>(L.vh + d * LV + slot) = hi;
+        *reinterpret_cast<uint2 *>(L.vl + d * LV + slot) = lo;
+    }
+}
+
 template <int HD>
 __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs a) {
     __shared__ __align__(16) FlashLds<HD> L;
-    constexpr int LD = HD + 8;
+    constexpr int LD = HD + 8, LV = FK + 8;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = a.nh / a.nkv;
     const int h = blockIdx.y, g = h / G;
-    const int q0 = blockIdx.x * FQ;
+    // causal work grows with the query block: start the longest blocks first
+    const int q0 = (gridDim.x - 1 - blockIdx.x) * FQ;
     const int prefix = a.kv_len - a.T;
     const int row_stride = a.nh * HD;
     const int qi = q0 + wave * 16 + (lane & 15);   // this lane's query
@@ -305,23 +377,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
     const float *kb = a.kc + size_t(g) * a.kv_stride * HD;
     const float *vb = a.vc + size_t(g) * a.kv_stride * HD;
 
+    KvRegs<HD> kv;
+    kv_load<HD>(kb, vb, 0, blk_last, kv);
     for (int j0 = 0; j0 <= blk_last; j0 += FK) {
+        __syncthreads();  // the previous block's LDS tiles are no longer read
+        kv_store<HD>(kv, L);
         __syncthreads();
-        for (int e = tid; e < FK * HD / 4; e += kThreads) {
-            const int j = e / (HD / 4), d4 = (e - j * (HD / 4)) * 4;
-            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-            if (j0 + j <= blk_last) {
-                kv = *reinterpret_cast<const float4 *>(kb + size_t(j0 + j) * HD + d4);
-                vv = *reinterpret_cast<const float4 *>(vb + size_t(j0 + j) * HD + d4);
-            }
-            const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, vvv[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                split16(kk[i], L.kh[j * LD + d4 + i], L.kl[j * LD + d4 + i]);
-                split16(vvv[i], L.vh[j * LD + d4 + i], L.vl[j * LD + d4 + i]);
-            }
-        }
-        __syncthreads();
+        if (j0 + FK <= blk_last) kv_load<HD>(kb, vb, j0 + FK, blk_last, kv);
         // S^T for 4 key tiles of 16
         f32x4 st[4];
 #pragma unroll
@@ -384,13 +446,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
             const int d = t * 16 + (lane & 15);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                half8 vh, vl;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int key = 32 * s + ((j < 4) ? (4 * grp + j) : (16 + 4 * grp + j - 4));
-                    vh[j] = L.vh[key * LD + d];
-                    vl[j] = L.vl[key * LD + d];
-                }
+                const half8 vh = *reinterpret_cast<const half8 *>(L.vh + d * LV + 32 * s + 8 * grp);
+                const half8 vl = *reinterpret_cast<const half8 *>(L.vl + d * LV + 32 * s + 8 * grp);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, ph[s], acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, ph[s], acc, 0, 0, 0);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, pl[s], acc, 0, 0, 0);
