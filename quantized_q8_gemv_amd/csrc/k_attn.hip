@@ -356,12 +356,14 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
     const int grp = lane >> 4;
 
     // Q^T fragments (B operand): lane holds Q[qi][32*s + 8*grp + j], pre-scaled
+    // by 1/sqrt(hd) * log2(e) so that the softmax runs on exp2
+    const float qscale = a.scale * 1.4426950408889634f;
     half8 qh[HD / 32], ql[HD / 32];
 #pragma unroll
     for (int s = 0; s < HD / 32; ++s)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float v = (qi < a.T) ? a.q[size_t(qi) * row_stride + h * HD + 32 * s + 8 * grp + j] * a.scale : 0.f;
+            const float v = (qi < a.T) ? a.q[size_t(qi) * row_stride + h * HD + 32 * s + 8 * grp + j] * qscale : 0.f;
             _Float16 hi, lo;
             split16(v, hi, lo);
             qh[s][j] = hi;
@@ -400,27 +402,36 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
             }
             st[kt] = acc;
         }
-        // mask (keys beyond the causal limit of this query or beyond kv_len)
+        // mask keys beyond the causal limit of this query (or beyond kv_len):
+        // only blocks that reach past the first query's limit need it
+        if (j0 + FK - 1 > prefix + q0) {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = j0 + kt * 16 + 4 * grp + i;
+                    const bool vis = key <= prefix + qi && key <= blk_last;
+                    st[kt][i] = vis ? st[kt][i] : -INFINITY;
+                }
+        }
         float bmax = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = j0 + kt * 16 + 4 * grp + i;
-                const bool vis = key <= prefix + qi && key <= blk_last;
-                st[kt][i] = vis ? st[kt][i] : -INFINITY;
-                bmax = fmaxf(bmax, st[kt][i]);
-            }
+            for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, st[kt][i]);
         bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
         bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+        // Scores are in log2 units (Q carries log2(e)). Key 0 is visible to
+        // every query, so m_new is finite and exp2(-inf) = 0 handles masked
+        // keys and the first block's alpha.
         const float m_new = fmaxf(m, bmax);
-        const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         float psum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = (st[kt][i] == -INFINITY) ? 0.f : expf(st[kt][i] - m_new);
+                const float p = __builtin_amdgcn_exp2f(st[kt][i] - m_new);
                 st[kt][i] = p;
                 psum += p;
             }
