@@ -957,11 +957,17 @@ GemvShape choose_shape(int N, int K, int maxt, int nmat, int target_wgs, int nr_
     s.rowbytes = s.P * kPairBytes;
     const int lds_cap_pairs = std::max(1, (40 * 1024) / (maxt * kXPad * 4));
     s.PC = divisor_at_most(s.P, std::min(lds_cap_pairs, kThreads / nmat));
-    int nr = kThreads / (nmat * s.PC);
+    const int cap = kThreads / (nmat * s.PC);
     const int want = (N + target_wgs - 1) / target_wgs;
-    nr = std::min(nr, std::max(want, 1));
-    // prefer 16-byte aligned whole-row tiles (4 rows of any K are aligned)
+    int nr = std::min(cap, std::max(want, 1));
+    // Whole-row tiles move with 16-byte loads only when the tile is a
+    // multiple of 16 bytes: round the row count up to that multiple (4 rows of
+    // any K are), else down to a multiple of 4.
+    int align = 1;
+    if (s.PC == s.P)
+        while ((align * s.rowbytes) % 16) ++align;
     if (nr >= 4) nr -= nr % 4;
+    if (nr % align && ((nr + align - 1) / align) * align <= cap) nr = ((nr + align - 1) / align) * align;
     nr = std::max(nr_mult, nr - nr % nr_mult);
     s.NR = nr;
     return s;
