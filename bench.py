@@ -41,9 +41,63 @@ PEAK_HBM_GBS = 8000.0
 PAGES_DECODE_MS = {"C2": 2.6}
 KIND_NAMES = ["embed", "qkv_rope_kv", "attn_decode", "oproj_residual", "gateup_silu",
               "down_residual", "lmhead", "argmax_finish"]
-KERNEL_SYMBOLS = ["k_embed", "k_qkv", "k_attn_decode", "k_matmul<1, 1|2, false>", "k_gateup",
-                  "k_matmul<1, 0, *>", "k_lmhead", "k_argmax_finish"]
 NKINDS = len(KIND_NAMES)
+# rocprofv3 PMC summaries of the decode kernels (FETCH_SIZE and WRITE_SIZE per
+# dispatch, scaled by the same counters on a copy of known size); a summary
+# counts only while the kernel source it was taken with is unchanged.
+TRAFFIC_FILES = {"C2": "profiles/decode_kernels_135m_13+20_pmc_traffic.md"}
+
+
+def kernel_symbols(s):
+    """Device symbol of each decode kernel kind at this shape (T = 1)."""
+    multi = (s.n_embd // 64) * 272 > 40 * 1024  # rows longer than one LDS chunk
+    down_multi = (s.n_ff // 64) * 272 > 40 * 1024
+    return ["k_embed", f"k_qkv1<{str(multi).lower()}>", "k_attn_decode",
+            f"k_matmul1<1, {str(multi).lower()}>", f"k_gateup1<{str(multi).lower()}>",
+            "k_matmul1_chunked" if down_multi else "k_matmul1<0, false>",
+            f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
+
+
+def source_digest(path):
+    import hashlib
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(config, kind):
+    """HBM bytes per launch of decode kernel `kind` from the committed PMC
+    summary, or None if there is none or the kernel source changed since."""
+    path = TRAFFIC_FILES.get(config)
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    for line in open(os.path.join(ROOT, path)):
+        if not line.startswith("traffic:"):
+            continue
+        f = dict(kv.split("=", 1) for kv in line.split()[1:])
+        if f.get("kind") != kind:
+            continue
+        if source_digest(f["source"]) != f["sha256"]:
+            return None
+        return int(f["bytes_per_launch"])
+    return None
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
+    """Device-to-device copy of `nbytes` (read + write) in GB/s; also the
+    reference dispatch for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def eprint(*a):
@@ -209,10 +263,13 @@ def main():
                                "gbs": round(kb[i] / (ms[i] * 1e-3) / 1e9, 1) if ms[i] > 0 else 0.0,
                                "launches_per_token": launches[i]} for i in range(NKINDS)}
     achieved = kb[dom] / (ms[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(args.config, KIND_NAMES[dom])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": KIND_NAMES[dom], "symbol": KERNEL_SYMBOLS[dom],
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": KIND_NAMES[dom], "symbol": kernel_symbols(s)[dom],
                 "bytes_per_launch": kb[dom], "us_per_launch": round(ms[dom] * 1e3, 2)}
+    copy_gbs = copy_bandwidth(torch)
+    eprint(f"[bench] device copy: {copy_gbs:.0f} GB/s (1 GiB, read + write)")
     eprint(f"[bench] kernels: " + ", ".join(f"{k} {v['us']}us" for k, v in kernels.items()))
 
     cpu = None
@@ -246,6 +303,7 @@ def main():
                         "hbm_gbs": round(dev_gbs, 1),
                         "hbm_frac": round(dev_gbs / PEAK_HBM_GBS, 4)},
         "roofline": roofline,
+        "copy_gbs": round(copy_gbs, 1),
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
