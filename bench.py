@@ -48,12 +48,16 @@ NKINDS = len(KIND_NAMES)
 TRAFFIC_FILES = {"C2": "profiles/decode_kernels_135m_13+20_pmc_traffic.md"}
 
 
-def kernel_symbols(s):
-    """Device symbol of each decode kernel kind at this shape (T = 1)."""
+def kernel_symbols(s, kv_len):
+    """Device symbol of each decode kernel kind at this shape (T = 1). With
+    one attention split the o-projection merges the split itself (variant 1);
+    with several a separate merge kernel runs first (variant 0)."""
     multi = (s.n_embd // 64) * 272 > 40 * 1024  # rows longer than one LDS chunk
     down_multi = (s.n_ff // 64) * 272 > 40 * 1024
+    chunk = 64 if s.head_dim <= 64 else 32
+    fused = 1 if kv_len <= chunk else 0
     return ["k_embed", f"k_qkv1<{str(multi).lower()}>", "k_attn_decode",
-            f"k_matmul1<1, {str(multi).lower()}>", f"k_gateup1<{str(multi).lower()}>",
+            f"k_matmul1<{fused}, {str(multi).lower()}>", f"k_gateup1<{str(multi).lower()}>",
             "k_matmul1_chunked" if down_multi else "k_matmul1<0, false>",
             f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
 
@@ -266,7 +270,7 @@ def main():
     traffic = measured_traffic(args.config, KIND_NAMES[dom])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": KIND_NAMES[dom], "symbol": kernel_symbols(s)[dom],
+                "kernel": KIND_NAMES[dom], "symbol": kernel_symbols(s, kv_len)[dom],
                 "bytes_per_launch": kb[dom], "us_per_launch": round(ms[dom] * 1e3, 2)}
     copy_gbs = copy_bandwidth(torch)
     eprint(f"[bench] device copy: {copy_gbs:.0f} GB/s (1 GiB, read + write)")

@@ -113,28 +113,41 @@ __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
     }
 }
 
-// Merge the split partials into O (single-op path; the forward merges them
-// in the o-projection's prologue instead). Fixed split order.
+// Merge the split partials of the decode attention into O: one workgroup per
+// query head. The split weights w_s = exp(m_s - M) (M = max over splits) are
+// computed once per split into LDS; then o[d] = sum_s w_s o_s[d] / sum_s w_s l_s,
+// every sum in split order (the result does not depend on timing).
 __global__ __launch_bounds__(kThreads) void k_attn_combine(const float *part, int n_splits,
-                                                          int active, int nh, int hd, float *o,
+                                                          int active, int hd, float *o,
                                                           const StepState *st) {
-    const int e = blockIdx.x * kThreads + threadIdx.x;
-    if (e >= nh * hd) return;
+    extern __shared__ float w[];  // n_splits
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int h = blockIdx.x;
     if (st) {  // graph replay: the cache length comes from the step state
         const int C = attn_chunk(hd);
         active = min((st->slot + 1 + C - 1) / C, n_splits);
     }
-    const int h = e / hd, d = e - h * hd;
     const float *pb = part + size_t(h) * n_splits * (hd + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < active; ++s) M = fmaxf(M, pb[s * (hd + 2)]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < active; ++s) {
-        const float w = expf(pb[s * (hd + 2)] - M);
-        L = fmaf(w, pb[s * (hd + 2) + 1], L);
-        O = fmaf(w, pb[s * (hd + 2) + 2 + d], O);
+    float mx = -INFINITY;
+    for (int t = tid; t < active; t += kThreads) mx = fmaxf(mx, pb[size_t(t) * (hd + 2)]);
+    mx = wave_max(mx);
+    if (lane == 0) red[wid] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float ls = 0.f;
+    for (int t = tid; t < active; t += kThreads) {
+        const float wt = expf(pb[size_t(t) * (hd + 2)] - mx);
+        w[t] = wt;
+        ls = fmaf(wt, pb[size_t(t) * (hd + 2) + 1], ls);
     }
-    o[e] = O / L;
+    ls = block_sum(ls, red);  // its barriers also publish w[]
+    const float inv = 1.0f / ls;
+    for (int d = tid; d < hd; d += kThreads) {
+        float acc = 0.f;
+        for (int t = 0; t < active; ++t) acc = fmaf(w[t], pb[size_t(t) * (hd + 2) + 2 + d], acc);
+        o[size_t(h) * hd + d] = acc * inv;
+    }
 }
 
 constexpr int kQB = 32;   // queries per prefill workgroup
@@ -506,9 +519,9 @@ hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s) {
 hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int nh, int hd,
                                float *o, const StepState *st, hipStream_t s) {
     const int active = std::min((kv_len + attn_chunk(hd) - 1) / attn_chunk(hd), n_splits);
-    const int n = nh * hd;
-    hipLaunchKernelGGL(k_attn_combine, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
-                       part, n_splits, active, nh, hd, o, st);
+    const size_t lds = size_t(n_splits) * sizeof(float);
+    if (lds > 64 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_attn_combine, dim3(nh), dim3(kThreads), lds, s, part, n_splits, active, hd, o, st);
     return hipGetLastError();
 }
 
