@@ -48,7 +48,7 @@ class _Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("n_ff", ctypes.c_int32),
                 ("n_vocab", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double),
-                ("tied_output", ctypes.c_int32)]
+                ("tied_output", ctypes.c_int32), ("rope_neox", ctypes.c_int32)]
 
 
 _lib = None
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.orc_rmsnorm.argtypes = [P, P, I64, D, P]; L.orc_rmsnorm.restype = None
         L.orc_rope_angle.argtypes = [I64, I64, I64, D]; L.orc_rope_angle.restype = D
         L.orc_rope_i.argtypes = [P, I64, I64, D]; L.orc_rope_i.restype = None
+        L.orc_rope_neox.argtypes = [P, I64, I64, D]; L.orc_rope_neox.restype = None
         L.orc_silu.argtypes = [D]; L.orc_silu.restype = D
         L.orc_attend.argtypes = [P, P, P, I64, I64, I64, P]; L.orc_attend.restype = None
         L.orc_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_void_p)]
@@ -129,6 +130,12 @@ def rope_i(v: np.ndarray, p: int, theta: float) -> np.ndarray:
     return out
 
 
+def rope_neox(v: np.ndarray, p: int, theta: float) -> np.ndarray:
+    out = np.ascontiguousarray(v, dtype=np.float64).copy()
+    lib().orc_rope_neox(_ptr(out), out.size, p, theta)
+    return out
+
+
 def silu(z: float) -> float:
     return lib().orc_silu(z)
 
@@ -159,7 +166,7 @@ class OracleModel:
         self.shape = s
         self.cfg = _Config(s.n_layer, s.n_embd, s.n_head, s.n_head_kv, s.head_dim, s.n_ff,
                            s.n_vocab, max_seq_len or s.max_seq_len, s.rms_eps, s.rope_theta,
-                           int(s.tied_output))
+                           int(s.tied_output), int(getattr(s, "rope_neox", False)))
         self._arrays = [np.ascontiguousarray(t.data) for t in model.tensors]
         ptrs = (ctypes.c_void_p * len(self._arrays))(*[a.ctypes.data for a in self._arrays])
         self._ptrs = ptrs

@@ -87,10 +87,14 @@ class NumpyLlama:
         return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + self.s.rms_eps) * w
 
     def _rope(self, x, index_pos):
-        # x [heads, T, hd]; pairs (2j, 2j+1)
+        # x [heads, T, hd]; pairs (2j, 2j+1), or with rope_neox the two halves
+        # rotated against each other (dimension j with j + hd/2)
         T = x.shape[1]
         c = self.cos[index_pos:index_pos + T][None]
         s = self.sin[index_pos:index_pos + T][None]
+        if getattr(self.s, "rope_neox", False):
+            x1, x2 = np.split(x, 2, axis=-1)
+            return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
         a, b = x[..., 0::2], x[..., 1::2]
         out = np.empty_like(x)
         out[..., 0::2] = a * c - b * s

@@ -22,7 +22,8 @@
  *     output layer when output.weight is absent).
  * Formulas the pages name but do not write out are taken in their textbook
  * form: RMSNorm y = x / sqrt(mean(x^2) + eps) * w; interleaved rope (pairs
- * 2j, 2j+1) with inverse frequency theta^(-2j/hd); SiLU z / (1 + e^-z).
+ * 2j, 2j+1) with inverse frequency theta^(-2j/hd), or the NEOX pairing
+ * (j, j + hd/2) with the same angles; SiLU z / (1 + e^-z).
  *
  * Precision: every weight is decoded exactly (w = f16 scale * int8, exact in
  * f64); activations, the KV cache and every sum are f64; logits are rounded
@@ -56,6 +57,7 @@ typedef struct {
     int32_t n_layer, n_embd, n_head, n_head_kv, head_dim, n_ff, n_vocab, max_seq_len;
     double rms_eps, rope_theta;
     int32_t tied_output;
+    int32_t rope_neox;    /* 0: pairs (2j, 2j+1) (llama); 1: pairs (j, j + hd/2) */
 } orc_config;
 
 typedef struct {
@@ -140,6 +142,19 @@ void orc_rope_i(double *v, int64_t hd, int64_t p, double theta) {
         double x0 = v[2 * j], x1 = v[2 * j + 1];
         v[2 * j] = x0 * c - x1 * s;
         v[2 * j + 1] = x0 * s + x1 * c;
+    }
+}
+
+/* The other convention ("量化 llama 的一次前向", section "RoPE：两种约定，按架构名选":
+ * the NEOX one, dimension j paired with dimension j + hd/2), same angles. */
+void orc_rope_neox(double *v, int64_t hd, int64_t p, double theta) {
+    const int64_t half = hd / 2;
+    for (int64_t j = 0; j < half; ++j) {
+        double a = orc_rope_angle(p, j, hd, theta);
+        double c = cos(a), s = sin(a);
+        double x0 = v[j], x1 = v[j + half];
+        v[j] = x0 * c - x1 * s;
+        v[j + half] = x0 * s + x1 * c;
     }
 }
 
@@ -291,8 +306,9 @@ int orc_forward(orc_model *m, const uint32_t *tokens, int32_t T, int32_t index_p
         orc_matmul_q8(L->wv, KVD, H, u, T, v);
         m->n_matmul += 3;
         for (int32_t i = 0; i < T; ++i) {
-            for (int64_t h = 0; h < nh; ++h) orc_rope_i(q + i * QD + h * hd, hd, (int64_t)index_pos + i, c->rope_theta);
-            for (int64_t h = 0; h < nkv; ++h) orc_rope_i(k + i * KVD + h * hd, hd, (int64_t)index_pos + i, c->rope_theta);
+            void (*rope)(double *, int64_t, int64_t, double) = c->rope_neox ? orc_rope_neox : orc_rope_i;
+            for (int64_t h = 0; h < nh; ++h) rope(q + i * QD + h * hd, hd, (int64_t)index_pos + i, c->rope_theta);
+            for (int64_t h = 0; h < nkv; ++h) rope(k + i * KVD + h * hd, hd, (int64_t)index_pos + i, c->rope_theta);
         }
         m->n_rope += 2;
         for (int32_t i = 0; i < T; ++i)

@@ -54,6 +54,7 @@ class ModelShape:
     max_seq_len: int = 4096
     rms_eps: float = 1e-5
     rope_theta: float = 10000.0
+    rope_neox: bool = False   # rope pairs (j, j + hd/2) instead of (2j, 2j + 1)
 
     @property
     def q_dim(self) -> int:
@@ -129,11 +130,12 @@ WORKLOADS: Dict[str, Workload] = {
 
 
 def micro_shape(n_layer=2, n_embd=64, n_head=4, n_head_kv=2, head_dim=16, n_ff=128,
-                n_vocab=50, tied_output=True, max_seq_len=64, name="micro") -> ModelShape:
+                n_vocab=50, tied_output=True, max_seq_len=64, name="micro",
+                rope_neox=False) -> ModelShape:
     """Small shapes for brute-force and edge-case tests."""
     return ModelShape(name, n_layer=n_layer, n_embd=n_embd, n_head=n_head,
                       n_head_kv=n_head_kv, head_dim=head_dim, n_ff=n_ff, n_vocab=n_vocab,
-                      tied_output=tied_output, max_seq_len=max_seq_len)
+                      tied_output=tied_output, max_seq_len=max_seq_len, rope_neox=rope_neox)
 
 
 def draw_q8_0(rng: np.random.Generator, rows: int, cols: int,
@@ -241,7 +243,7 @@ def shape_fields(shape: ModelShape) -> Dict[str, object]:
                 n_head_kv=shape.n_head_kv, head_dim=shape.head_dim, n_ff=shape.n_ff,
                 n_vocab=shape.n_vocab, max_seq_len=shape.max_seq_len,
                 rms_eps=shape.rms_eps, rope_theta=shape.rope_theta,
-                tied_output=int(shape.tied_output))
+                tied_output=int(shape.tied_output), rope_type=int(shape.rope_neox))
 
 
 __all__ = ["QK8_0", "Q8_0_BLOCK_BYTES", "LAYER_TENSORS", "ModelShape", "TINY", "SMOL135M",

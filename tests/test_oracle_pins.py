@@ -154,6 +154,62 @@ def test_rope_scores_depend_on_relative_position_only():
         assert s == pytest.approx(base, rel=1e-5)
 
 
+# NEOX pairing ("量化 llama 的一次前向", section "RoPE：两种约定，按架构名选": dimension
+# j is paired with j + hd/2; the angles are the same table's).
+
+def test_rope_neox_pairs_half_apart():
+    hd, theta = 64, 10000.0
+    for p in (0, 1, 7, 100):
+        for j in (0, 1, 31):
+            e = np.zeros(hd); e[j] = 1.0
+            r = oracle.rope_neox(e, p, theta)
+            ang = float(np.float32(p) * np.float32(theta ** (-2.0 * j / hd)))
+            assert r[j] == pytest.approx(math.cos(ang), abs=1e-15)
+            assert r[j + hd // 2] == pytest.approx(math.sin(ang), abs=1e-15)
+            assert np.count_nonzero(r) <= 2
+
+
+def test_rope_neox_is_interleaved_rope_under_the_half_permutation():
+    # Placing dimension j at 2j and j + hd/2 at 2j + 1 turns the NEOX rotation
+    # into the interleaved one: neox(v) = P^-1 rope_i(P v).
+    hd = 64
+    perm = np.empty(hd, dtype=np.int64)
+    perm[0::2] = np.arange(hd // 2)
+    perm[1::2] = np.arange(hd // 2) + hd // 2
+    v = np.random.default_rng(11).standard_normal(hd)
+    for p in (0, 5, 4095):
+        inter = oracle.rope_i(v[perm], p, 1e4)
+        back = np.empty(hd); back[perm] = inter
+        assert np.allclose(oracle.rope_neox(v, p, 1e4), back, rtol=0, atol=1e-15)
+
+
+def test_rope_neox_identity_norms_and_relative_position():
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal(64)
+    assert np.array_equal(oracle.rope_neox(v, 0, 1e4), v)
+    r = oracle.rope_neox(v, 777, 1e4)
+    assert np.allclose(np.hypot(r[:32], r[32:]), np.hypot(v[:32], v[32:]), rtol=1e-14)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    base = oracle.rope_neox(q, 9, 1e4) @ oracle.rope_neox(k, 4, 1e4)
+    for shift in (1, 3, 20):
+        s = oracle.rope_neox(q, 9 + shift, 1e4) @ oracle.rope_neox(k, 4 + shift, 1e4)
+        assert s == pytest.approx(base, rel=1e-5)
+
+
+def test_rope_convention_changes_the_forward():
+    a = synth.micro_shape(name="i")
+    b = synth.micro_shape(name="neox", rope_neox=True)
+    ma, mb = synth.random_model(a, 5), synth.random_model(b, 5)
+    toks = synth.prompt_ids(a.n_vocab, 6, 2)
+    _, _, la = oracle.OracleModel(ma).forward(toks, 0)
+    _, _, lb = oracle.OracleModel(mb).forward(toks, 0)
+    assert not np.allclose(la, lb)
+    # position 0 only: rope is the identity there, so one token agrees exactly
+    _, _, la1 = oracle.OracleModel(ma).forward(toks[:1], 0)
+    _, _, lb1 = oracle.OracleModel(mb).forward(toks[:1], 0)
+    assert np.array_equal(la1, lb1)
+
+
 def test_silu_identities():
     assert oracle.silu(0.0) == 0.0
     for z in (-3.0, -0.5, 0.25, 2.0):
@@ -217,6 +273,8 @@ MICRO_SHAPES = [
     synth.micro_shape(n_head=4, n_head_kv=4, name="mha"),
     synth.micro_shape(n_layer=1, n_embd=96, n_head=6, n_head_kv=3, head_dim=16, n_ff=96,
                       n_vocab=37, tied_output=False, name="odd-untied"),
+    synth.micro_shape(name="neox", rope_neox=True),
+    synth.micro_shape(n_head=4, n_head_kv=1, name="mqa-neox", rope_neox=True),
 ]
 
 
