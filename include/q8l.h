@@ -79,7 +79,13 @@ typedef struct q8l_config {
     double rms_eps;       /* RMSNorm epsilon (1e-5) */
     double rope_theta;    /* rope base (10000) */
     int32_t tied_output;  /* 1: the output layer is token_embd */
+    int32_t rope_type;    /* Q8L_ROPE_NORM: pairs (2j, 2j+1), llama's rope_i;
+                             Q8L_ROPE_NEOX: pairs (j, j + head_dim/2) ("量化 llama 的一次
+                             前向", section "RoPE：两种约定，按架构名选"); same angles */
 } q8l_config;
+
+#define Q8L_ROPE_NORM 0
+#define Q8L_ROPE_NEOX 1
 
 typedef struct q8l_model q8l_model;
 

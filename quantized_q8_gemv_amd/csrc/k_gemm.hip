@@ -56,6 +56,7 @@ struct GemmArgs {
     const float2 *rope;
     float *q, *kc, *vc;
     int QD, hd, max_seq;
+    int rope_neox;         // 1: q and k are written unrotated
     // G_GATEUP: h = silu(gate) * up as f16 hi plane [T][F] then lo plane
     _Float16 *h;
 };
@@ -369,8 +370,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
                     const int row = row0 + c;
                     const int d = row % a.hd;
                     const int t = m0 + m;
-                    if (mat == 2) {
-                        a.vc[(size_t(row / a.hd) * a.max_seq + a.st->slot + t) * a.hd + d] = v;
+                    if (mat == 2 || a.rope_neox) {
+                        float *dst = mat == 0 ? a.q + size_t(t) * a.QD + row
+                                              : (mat == 1 ? a.kc : a.vc) +
+                                                    (size_t(row / a.hd) * a.max_seq + a.st->slot + t) * a.hd + d;
+                        *dst = v;
                     } else {
                         const float2 cs = a.rope[size_t(a.st->pos + t) * (a.hd / 2) + (d >> 1)];
                         const float r = (d & 1) ? (partner * cs.y + v * cs.x) : (v * cs.x - partner * cs.y);
@@ -483,7 +487,7 @@ hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u,
     a.W[0] = w.wq; a.W[1] = w.wk; a.W[2] = w.wv;
     a.Nm[0] = QD; a.Nm[1] = KVD; a.Nm[2] = KVD;
     a.st = st; a.rope = rope; a.q = q; a.kc = kc; a.vc = vc;
-    a.QD = QD; a.hd = d.hd; a.max_seq = d.max_seq;
+    a.QD = QD; a.hd = d.hd; a.max_seq = d.max_seq; a.rope_neox = d.rope_neox;
     const bool large = large_tiles(T, row_tiles(QD, 128) + 2 * row_tiles(KVD, 128));
     const int tn = large ? 128 : 64;
     for (int i = 0; i < 3; ++i) a.tiles[i] = row_tiles(a.Nm[i], tn);

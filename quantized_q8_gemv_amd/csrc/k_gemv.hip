@@ -356,6 +356,7 @@ struct QkvArgs {
     int tq, tk;          // tiles of q, of k (v has tk too)
     int QD, KVD, hd, max_seq, T;
     float eps;
+    int rope_neox;       // 1: q and k are written unrotated (a separate kernel rotates them)
 };
 
 template <int MAXT, bool MULTI>
@@ -388,8 +389,10 @@ __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
         const float a0 = l.outv[t * a.sh.NR + r], a1 = l.outv[t * a.sh.NR + r + 1];
         const int row = c.row0 + r;
         const int d = row % a.hd;
-        if (kind == 2) {
-            float *dst = a.vc + (size_t(row / a.hd) * a.max_seq + slot0 + t) * a.hd + d;
+        if (kind == 2 || a.rope_neox) {
+            float *dst = kind == 0   ? a.q + size_t(t0 + t) * a.QD + row
+                         : kind == 1 ? a.kc + (size_t(row / a.hd) * a.max_seq + slot0 + t) * a.hd + d
+                                     : a.vc + (size_t(row / a.hd) * a.max_seq + slot0 + t) * a.hd + d;
             dst[0] = a0;
             dst[1] = a1;
         } else {
@@ -718,8 +721,10 @@ __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
             const float a0 = l.outv[r], a1 = l.outv[r + 1];
             const int row = c.row0 + r;
             const int d = row % a.hd;
-            if (kind == 2) {
-                float *dst = a.vc + (size_t(row / a.hd) * a.max_seq + slot) * a.hd + d;
+            if (kind == 2 || a.rope_neox) {
+                float *dst = kind == 0   ? a.q + row
+                             : kind == 1 ? a.kc + (size_t(row / a.hd) * a.max_seq + slot) * a.hd + d
+                                         : a.vc + (size_t(row / a.hd) * a.max_seq + slot) * a.hd + d;
                 dst[0] = a0;
                 dst[1] = a1;
             } else {
@@ -994,7 +999,7 @@ hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const S
     a.wq = w.wq; a.wk = w.wk; a.wv = w.wv; a.norm_w = w.attn_norm; a.x = x; a.st = st;
     a.rope = rope; a.q = q; a.kc = kc; a.vc = vc;
     a.QD = d.nh * d.hd; a.KVD = d.nkv * d.hd; a.hd = d.hd; a.max_seq = d.max_seq; a.T = T;
-    a.eps = d.eps;
+    a.eps = d.eps; a.rope_neox = d.rope_neox;
     a.sh = choose_shape(a.QD + 2 * a.KVD, d.H, maxt, 1, 512, 2);
     a.tq = (a.QD + a.sh.NR - 1) / a.sh.NR;
     a.tk = (a.KVD + a.sh.NR - 1) / a.sh.NR;

@@ -70,6 +70,24 @@ __global__ __launch_bounds__(kThreads) void k_embed(const uint8_t *E, int H, int
     }
 }
 
+// The NEOX rope convention ("量化 llama 的一次前向", section "RoPE：两种约定，按架构名
+// 选"): dimension j of a head is rotated with dimension j + hd/2 by the table's
+// angle for pair j. One workgroup per (token, head); heads [0, nh) are the
+// token's q row, heads [nh, nh + nkv) its new key slot in the cache.
+__global__ __launch_bounds__(kThreads) void k_rope_neox(const StepState *st, const float2 *rope, float *q,
+                                                       float *kc, int nh, int hd, int max_seq) {
+    const int t = blockIdx.x, h = blockIdx.y;
+    const int half = hd / 2;
+    float *v = h < nh ? q + (size_t(t) * nh + h) * hd
+                      : kc + (size_t(h - nh) * max_seq + st->slot + t) * hd;
+    const float2 *cs = rope + size_t(st->pos + t) * half;
+    for (int j = threadIdx.x; j < half; j += kThreads) {
+        const float x0 = v[j], x1 = v[j + half];
+        v[j] = x0 * cs[j].x - x1 * cs[j].y;
+        v[j + half] = x0 * cs[j].y + x1 * cs[j].x;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_set_state(const SetStateArgs &a, StepState *st, uint32_t *tok_buf,
@@ -90,6 +108,13 @@ hipError_t launch_embed(const uint8_t *E, int H, int V, const StepState *st,
                         hipStream_t s) {
     hipLaunchKernelGGL(k_embed, dim3(T), dim3(kThreads), 0, s, E, H, V, st, tok_buf,
                        from_state_token, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_neox(const Dims &d, const StepState *st, const float2 *rope, float *q, float *kc,
+                            int T, hipStream_t s) {
+    hipLaunchKernelGGL(k_rope_neox, dim3(T, d.nh + d.nkv), dim3(64), 0, s, st, rope, q, kc, d.nh, d.hd,
+                       d.max_seq);
     return hipGetLastError();
 }
 

@@ -62,11 +62,16 @@ struct LayerPtrs {
 struct Dims {
     int H, nh, nkv, hd, F, V, max_seq;
     float eps;
+    int rope_neox;  // 1: pairs (j, j + hd/2), applied by launch_rope_neox after q/k/v
 };
 
 hipError_t launch_set_state(const SetStateArgs &a, StepState *st, uint32_t *tok_buf,
                             hipStream_t s);
 hipError_t launch_rope_table(float2 *table, int max_seq, int hd, double theta, hipStream_t s);
+// NEOX rotation of the T new tokens' q (rows of [T][nh*hd]) and k (cache slots
+// st->slot + t) at positions st->pos + t.
+hipError_t launch_rope_neox(const Dims &d, const StepState *st, const float2 *rope, float *q, float *kc,
+                            int T, hipStream_t s);
 hipError_t launch_embed(const uint8_t *E, int H, int V, const StepState *st,
                         const uint32_t *tok_buf, int T, int from_state_token, float *x,
                         hipStream_t s);

@@ -62,6 +62,8 @@ bool config_ok(const q8l_config *c, std::string *why) {
         return fail("n_embd, n_ff and n_head*head_dim must be multiples of 64");
     if (c->n_head_kv > 255) return fail("n_head_kv must be <= 255");
     if (!(c->rms_eps >= 0.0) || !(c->rope_theta > 0.0)) return fail("rms_eps >= 0 and rope_theta > 0 required");
+    if (c->rope_type != Q8L_ROPE_NORM && c->rope_type != Q8L_ROPE_NEOX)
+        return fail("rope_type must be Q8L_ROPE_NORM or Q8L_ROPE_NEOX");
     return true;
 }
 
@@ -181,6 +183,7 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
         } else {
             if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
         }
+        if (d.rope_neox && (e = launch_rope_neox(d, st, rope, q, m->kc(l), T, s)) != hipSuccess) return e;
         if (T == 1) {
             AttnDecodeArgs a;
             a.q = q; a.kc = m->kc(l); a.vc = m->vc(l);
@@ -346,6 +349,7 @@ q8l_status q8l_create(const q8l_config *cfg, q8l_model **out) {
     m->d.H = cfg->n_embd; m->d.nh = cfg->n_head; m->d.nkv = cfg->n_head_kv; m->d.hd = cfg->head_dim;
     m->d.F = cfg->n_ff; m->d.V = cfg->n_vocab; m->d.max_seq = cfg->max_seq_len;
     m->d.eps = float(cfg->rms_eps);
+    m->d.rope_neox = cfg->rope_type == Q8L_ROPE_NEOX ? 1 : 0;
     m->lay = make_layout(cfg);
     m->layer_ptrs.assign(cfg->n_layer, std::vector<const void *>(S_NSLOT, nullptr));
     *out = m;

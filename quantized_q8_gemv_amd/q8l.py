@@ -32,6 +32,9 @@ STATUS_NAMES = {0: "OK", 1: "E_INVALID_ARG", 2: "E_MISSING_TENSOR", 3: "E_SHAPE"
 Q8L_F32 = 0
 Q8L_Q8_0 = 1
 
+Q8L_ROPE_NORM = 0
+Q8L_ROPE_NEOX = 1
+
 
 class q8l_config(ctypes.Structure):
     _fields_ = [("n_layer", ctypes.c_int32), ("n_embd", ctypes.c_int32),
@@ -39,7 +42,7 @@ class q8l_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("n_ff", ctypes.c_int32),
                 ("n_vocab", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double),
-                ("tied_output", ctypes.c_int32)]
+                ("tied_output", ctypes.c_int32), ("rope_type", ctypes.c_int32)]
 
 
 class Q8LError(RuntimeError):

@@ -47,6 +47,28 @@ def test_135m_203_prompt_128_steps():
     assert ties <= 2
 
 
+@pytest.mark.parametrize("plen", [4, 13, 203])
+def test_neox_rope_generation_matches_oracle(plen):
+    """The NEOX pairing (j, j + hd/2): prompts through the multi-token GEMV
+    (4 tokens) and the GEMM path (13, 203), then decode."""
+    s = synth.ModelShape("tiny-neox", n_layer=4, n_embd=576, n_head=9, n_head_kv=3, head_dim=64,
+                         n_ff=1536, n_vocab=4096, rope_neox=True)
+    m = synth.random_model(s, 0)
+    prompt = synth.prompt_ids(s.n_vocab, plen, 1)
+    ids, err, ties = compare_generation(gpu_model(m), oracle.OracleModel(m), prompt, 8, f"neox {plen}+8")
+    log(f"neox {plen}+8: max abs err {err:.3g}, near ties {ties}")
+    assert ties <= 1
+
+
+def test_neox_rope_head_dim_128():
+    s = synth.ModelShape("neox-hd128", n_layer=2, n_embd=1024, n_head=8, n_head_kv=2, head_dim=128,
+                         n_ff=1024, n_vocab=2048, rope_neox=True)
+    m = synth.random_model(s, 4)
+    prompt = synth.prompt_ids(s.n_vocab, 40, 3)
+    ids, err, ties = compare_generation(gpu_model(m), oracle.OracleModel(m), prompt, 6, "neox hd128 40+6")
+    assert ties <= 1
+
+
 def test_chunked_prefill_and_reset(tiny):
     m, prompt, gm = tiny
     gm.clear_kv_cache()

@@ -33,7 +33,8 @@ def test_workspace_bytes_cover_the_kv_arena():
 
 
 @pytest.mark.parametrize("field,value", [("n_head_kv", 2), ("head_dim", 6), ("n_embd", 96),
-                                         ("n_layer", 0), ("head_dim", 256), ("rope_theta", 0.0)])
+                                         ("n_layer", 0), ("head_dim", 256), ("rope_theta", 0.0),
+                                         ("rope_type", 2), ("rope_type", -1)])
 def test_invalid_configs_rejected(field, value):
     f = synth.shape_fields(synth.TINY)
     f[field] = value
@@ -102,3 +103,10 @@ def test_forward_argument_and_position_checks_precede_device_work(tiny_handle):
     assert fwd(toks, 13, 0) == C.Q8L_E_NOT_FINALIZED
     assert C.q8l_cache_len(h) == 0
     assert C.q8l_clear_kv_cache(h) == C.Q8L_OK
+
+
+def test_rope_types_accepted():
+    for rt in (C.Q8L_ROPE_NORM, C.Q8L_ROPE_NEOX):
+        f = synth.shape_fields(synth.TINY)
+        f["rope_type"] = rt
+        assert C.q8l_workspace_bytes(C.config_from(f)) > 0
