@@ -54,7 +54,10 @@ typedef enum {
     Q8L_E_POS_MISMATCH = 5,   /* T > 1 and index_pos != cached positions */
     Q8L_E_KV_FULL = 6,        /* cached positions + T > max_seq_len */
     Q8L_E_NOT_FINALIZED = 7,  /* forward before finalize, or bind after it */
-    Q8L_E_HIP = 8             /* a HIP call failed (message has the HIP error) */
+    Q8L_E_HIP = 8,            /* a HIP call failed (message has the HIP error) */
+    Q8L_E_FORMAT = 9,         /* GGUF: malformed or unsupported file content */
+    Q8L_E_MISSING_KEY = 10,   /* GGUF: a required metadata key is absent */
+    Q8L_E_IO = 11             /* GGUF: the file cannot be opened or read */
 } q8l_status;
 
 typedef enum { Q8L_F32 = 0, Q8L_Q8_0 = 1 } q8l_dtype;
@@ -246,6 +249,64 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
 
 /* Version string of the library build. */
 const char *q8l_version(void);
+
+/* ---------------------------------------------------------------- GGUF model files
+ *
+ * Reading a model file: the step before the forward. "生成一个 token", section
+ * "读 GGUF：130 ms，只读头部": the header, metadata key/values and tensor
+ * directory are read and the start of the tensor data is recorded, no weight
+ * is read; section "建模型：按名字取张量": each tensor is found by name and its
+ * raw bytes are read from the data region (Q8_0 bytes stay as they are, so
+ * binding them is a copy). The byte format is the public GGUF specification
+ * (versions 2 and 3, little-endian, data aligned to general.alignment, 32 by
+ * default). Host-only calls: no device memory is touched. A handle holds the
+ * open file; it is not thread-safe. Errors: Q8L_E_IO (open/read), Q8L_E_FORMAT
+ * (bad magic, unsupported version, truncated or inconsistent directory,
+ * tensor types other than F32 and Q8_0 when read), Q8L_E_MISSING_KEY.
+ */
+typedef struct q8l_gguf q8l_gguf;
+
+/* Parse the header, metadata and tensor directory of `path`. On failure *out
+ * is NULL and q8l_gguf_open_error() describes the problem (per thread). */
+q8l_status q8l_gguf_open(const char *path, q8l_gguf **out);
+const char *q8l_gguf_open_error(void);
+const char *q8l_gguf_last_error(const q8l_gguf *g);
+void q8l_gguf_close(q8l_gguf *g);
+
+/* Directory facts ("读 GGUF" prints: file size, data start, key and tensor counts). */
+uint32_t q8l_gguf_version(const q8l_gguf *g);
+int64_t q8l_gguf_n_kv(const q8l_gguf *g);
+int64_t q8l_gguf_n_tensors(const q8l_gguf *g);
+uint64_t q8l_gguf_data_offset(const q8l_gguf *g);   /* absolute file offset */
+uint64_t q8l_gguf_file_size(const q8l_gguf *g);
+
+/* A numeric metadata value (any integer or float type, as double), or a
+ * string value copied NUL-terminated into buf (Q8L_E_INVALID_ARG if it does not
+ * fit). Q8L_E_MISSING_KEY if the key is absent or of another kind. */
+q8l_status q8l_gguf_get_number(const q8l_gguf *g, const char *key, double *out);
+q8l_status q8l_gguf_get_string(const q8l_gguf *g, const char *key, char *buf, size_t buf_bytes);
+
+/* Model config from the llama.* keys ("量化 llama 的一次前向", section "from_gguf：
+ * 键名写死了 llama."): block_count, embedding_length, attention.head_count,
+ * attention.head_count_kv, feed_forward_length, rope.dimension_count (must
+ * equal embedding_length / head_count), attention.layer_norm_rms_epsilon
+ * (all required: Q8L_E_MISSING_KEY, message "cannot find <key> in metadata"),
+ * rope.freq_base (optional, 10000). n_vocab = rows of token_embd.weight;
+ * tied_output = 1 when output.weight is absent (section "建模型"); rope_type
+ * from general.architecture (section "RoPE：两种约定，按架构名选": qwen, qwen2,
+ * falcon, phi3, stablelm and gptneox pair j with j + hd/2, every other
+ * architecture 2j with 2j+1). max_seq_len is the caller's (4096 in candle). */
+q8l_status q8l_gguf_config(q8l_gguf *g, int32_t max_seq_len, q8l_config *cfg);
+
+/* Index of the tensor called `name`, or -1. */
+int64_t q8l_gguf_find_tensor(const q8l_gguf *g, const char *name);
+/* Tensor `index`: name (valid while the handle is open), dtype (a q8l_dtype, or
+ * -1 with Q8L_E_FORMAT for other types), rows x cols (cols = the innermost
+ * dimension), absolute file offset and byte size. Any output may be NULL. */
+q8l_status q8l_gguf_tensor_info(const q8l_gguf *g, int64_t index, const char **name, int32_t *dtype,
+                                int64_t *rows, int64_t *cols, uint64_t *offset, uint64_t *nbytes);
+/* Read tensor `index`'s bytes into host memory; nbytes must equal its size. */
+q8l_status q8l_gguf_read_tensor(q8l_gguf *g, int64_t index, void *host_dst, size_t nbytes);
 
 #ifdef __cplusplus
 }

@@ -44,6 +44,28 @@ class Q8Model:
         self.logits = torch.empty(self.n_vocab, dtype=torch.float32, device=self.device)
         self.argmax = torch.zeros(1, dtype=torch.int32, device=self.device)
 
+    @classmethod
+    def from_gguf(cls, path: str, device: str = "cuda:0", max_seq_len: int = 4096, stream=None) -> "Q8Model":
+        """Build a model from a GGUF file: config from its llama.* keys, then
+        each required tensor read by name and bound (C ABI q8l_gguf_*)."""
+        g = C.q8l_gguf_open(path)
+        try:
+            st, cfg = C.q8l_gguf_config(g, max_seq_len)
+            if st != C.Q8L_OK:
+                raise C.Q8LError(st, C.q8l_gguf_last_error(g))
+            fields = {name: getattr(cfg, name) for name, _ in C.q8l_config._fields_}
+            names = ["token_embd.weight"]
+            for i in range(cfg.n_layer):
+                names += [f"blk.{i}.{t}.weight" for t in ("attn_norm", "attn_q", "attn_k", "attn_v",
+                                                           "attn_output", "ffn_norm", "ffn_gate", "ffn_up",
+                                                           "ffn_down")]
+            names.append("output_norm.weight")
+            if not cfg.tied_output:
+                names.append("output.weight")
+            return cls(fields, _gguf_tensors(g, names), device=device, stream=stream)
+        finally:
+            C.q8l_gguf_close(g)
+
     def _check(self, st: int) -> None:
         if st != C.Q8L_OK:
             raise C.Q8LError(st, C.q8l_last_error(self.handle))
@@ -81,3 +103,27 @@ class Q8Model:
             self.close()
         except Exception:
             pass
+
+
+class _FileTensor:
+    __slots__ = ("name", "dtype", "rows", "cols", "data")
+
+
+def _gguf_tensors(g: int, names):
+    """Yield the named tensors of an open GGUF file one at a time (absent names
+    are skipped: finalize then reports the first missing one)."""
+    for name in names:
+        idx = C.q8l_gguf_find_tensor(g, name)
+        if idx < 0:
+            continue
+        st, info = C.q8l_gguf_tensor_info(g, idx)
+        if st != C.Q8L_OK:
+            raise C.Q8LError(st, C.q8l_gguf_last_error(g))
+        buf = np.empty(info["nbytes"], dtype=np.uint8)
+        st = C.q8l_gguf_read_tensor(g, idx, buf, info["nbytes"])
+        if st != C.Q8L_OK:
+            raise C.Q8LError(st, C.q8l_gguf_last_error(g))
+        t = _FileTensor()
+        t.name, t.rows, t.cols, t.data = name, info["rows"], info["cols"], buf
+        t.dtype = "q8_0" if info["dtype"] == C.Q8L_Q8_0 else "f32"
+        yield t

@@ -25,9 +25,12 @@ Q8L_E_POS_MISMATCH = 5
 Q8L_E_KV_FULL = 6
 Q8L_E_NOT_FINALIZED = 7
 Q8L_E_HIP = 8
+Q8L_E_FORMAT = 9
+Q8L_E_MISSING_KEY = 10
+Q8L_E_IO = 11
 STATUS_NAMES = {0: "OK", 1: "E_INVALID_ARG", 2: "E_MISSING_TENSOR", 3: "E_SHAPE",
                 4: "E_POS_RANGE", 5: "E_POS_MISMATCH", 6: "E_KV_FULL",
-                7: "E_NOT_FINALIZED", 8: "E_HIP"}
+                7: "E_NOT_FINALIZED", 8: "E_HIP", 9: "E_FORMAT", 10: "E_MISSING_KEY", 11: "E_IO"}
 
 Q8L_F32 = 0
 Q8L_Q8_0 = 1
@@ -76,6 +79,24 @@ _SIGS = {
     "q8l_op_attention_workspace": ([ctypes.c_int32] * 5, ctypes.c_size_t),
     "q8l_op_argmax": ([_P, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "q8l_time_decode_kernels": ([_P, ctypes.c_int32, _P, _P], ctypes.c_int),
+    "q8l_gguf_open": ([ctypes.c_char_p, ctypes.POINTER(_P)], ctypes.c_int),
+    "q8l_gguf_open_error": ([], ctypes.c_char_p),
+    "q8l_gguf_last_error": ([_P], ctypes.c_char_p),
+    "q8l_gguf_close": ([_P], None),
+    "q8l_gguf_version": ([_P], ctypes.c_uint32),
+    "q8l_gguf_n_kv": ([_P], ctypes.c_int64),
+    "q8l_gguf_n_tensors": ([_P], ctypes.c_int64),
+    "q8l_gguf_data_offset": ([_P], ctypes.c_uint64),
+    "q8l_gguf_file_size": ([_P], ctypes.c_uint64),
+    "q8l_gguf_get_number": ([_P, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+    "q8l_gguf_get_string": ([_P, ctypes.c_char_p, ctypes.c_char_p, ctypes.c_size_t], ctypes.c_int),
+    "q8l_gguf_config": ([_P, ctypes.c_int32, ctypes.POINTER(q8l_config)], ctypes.c_int),
+    "q8l_gguf_find_tensor": ([_P, ctypes.c_char_p], ctypes.c_int64),
+    "q8l_gguf_tensor_info": ([_P, ctypes.c_int64, ctypes.POINTER(ctypes.c_char_p),
+                              ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64),
+                              ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64),
+                              ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
+    "q8l_gguf_read_tensor": ([_P, ctypes.c_int64, _P, ctypes.c_size_t], ctypes.c_int),
 }
 
 
@@ -204,6 +225,90 @@ def q8l_op_argmax(x, n: int, out, workspace, workspace_bytes: int, stream=None) 
 
 def q8l_time_decode_kernels(m: int, reps: int, ms_out, stream=None) -> int:
     return lib().q8l_time_decode_kernels(m, reps, _ptr(ms_out), _stream(stream))
+
+
+# ---- GGUF model files (host side) ----
+
+def q8l_gguf_open(path: str) -> int:
+    """Open and parse a GGUF file; raises Q8LError with the reader's message."""
+    h = _P()
+    st = lib().q8l_gguf_open(path.encode(), ctypes.byref(h))
+    if st != Q8L_OK:
+        raise Q8LError(st, lib().q8l_gguf_open_error().decode())
+    return h.value
+
+
+def q8l_gguf_open_error() -> str:
+    return lib().q8l_gguf_open_error().decode()
+
+
+def q8l_gguf_last_error(g: int) -> str:
+    return lib().q8l_gguf_last_error(g).decode()
+
+
+def q8l_gguf_close(g: int) -> None:
+    lib().q8l_gguf_close(g)
+
+
+def q8l_gguf_version(g: int) -> int:
+    return int(lib().q8l_gguf_version(g))
+
+
+def q8l_gguf_n_kv(g: int) -> int:
+    return int(lib().q8l_gguf_n_kv(g))
+
+
+def q8l_gguf_n_tensors(g: int) -> int:
+    return int(lib().q8l_gguf_n_tensors(g))
+
+
+def q8l_gguf_data_offset(g: int) -> int:
+    return int(lib().q8l_gguf_data_offset(g))
+
+
+def q8l_gguf_file_size(g: int) -> int:
+    return int(lib().q8l_gguf_file_size(g))
+
+
+def q8l_gguf_get_number(g: int, key: str):
+    """(status, value)"""
+    v = ctypes.c_double()
+    st = lib().q8l_gguf_get_number(g, key.encode(), ctypes.byref(v))
+    return st, v.value
+
+
+def q8l_gguf_get_string(g: int, key: str, size: int = 4096):
+    """(status, value)"""
+    buf = ctypes.create_string_buffer(size)
+    st = lib().q8l_gguf_get_string(g, key.encode(), buf, size)
+    return st, buf.value.decode(errors="replace")
+
+
+def q8l_gguf_config(g: int, max_seq_len: int = 4096):
+    """(status, q8l_config)"""
+    cfg = q8l_config()
+    st = lib().q8l_gguf_config(g, max_seq_len, ctypes.byref(cfg))
+    return st, cfg
+
+
+def q8l_gguf_find_tensor(g: int, name: str) -> int:
+    return int(lib().q8l_gguf_find_tensor(g, name.encode()))
+
+
+def q8l_gguf_tensor_info(g: int, index: int):
+    """(status, dict(name, dtype, rows, cols, offset, nbytes))"""
+    name = ctypes.c_char_p()
+    dt, rows, cols = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    off, nb = ctypes.c_uint64(), ctypes.c_uint64()
+    st = lib().q8l_gguf_tensor_info(g, index, ctypes.byref(name), ctypes.byref(dt), ctypes.byref(rows),
+                                    ctypes.byref(cols), ctypes.byref(off), ctypes.byref(nb))
+    info = dict(name=(name.value or b"").decode(), dtype=dt.value, rows=rows.value, cols=cols.value,
+                offset=off.value, nbytes=nb.value)
+    return st, info
+
+
+def q8l_gguf_read_tensor(g: int, index: int, host_dst, nbytes: int) -> int:
+    return lib().q8l_gguf_read_tensor(g, index, _ptr(host_dst), nbytes)
 
 
 def config_from(shape_fields: dict) -> q8l_config:

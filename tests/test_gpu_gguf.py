@@ -1,0 +1,66 @@
+"""A model built from a GGUF file (Q8Model.from_gguf over the C ABI reader)
+runs the same forward as the same tensors bound directly, and matches the
+oracle; the architecture key selects the rope pairing end to end."""
+
+import numpy as np
+import pytest
+
+import gguf_writer as W
+import oracle
+import synth
+from helpers import compare_generation, gpu_model, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _write(tmp_path, m, arch="llama", drop=()):
+    path = str(tmp_path / f"{m.shape.name}-{arch}.gguf")
+    tensors = [t for t in W.model_tensors(m) if t[0] not in drop]
+    W.write(path, W.llama_kv(m.shape, arch), tensors)
+    return path
+
+
+def test_gguf_model_equals_direct_binding(tmp_path):
+    from quantized_q8_gemv_amd.model import Q8Model
+    w, m, prompt = synth.workload_inputs("C1")
+    path = _write(tmp_path, m)
+    log(f"gguf tiny: {path}")
+    a, b = Q8Model.from_gguf(path), gpu_model(m)
+    la, ia = a.forward(prompt, 0)
+    lb, ib = b.forward(prompt, 0)
+    assert np.array_equal(la, lb) and ia == ib
+    tok = ia
+    for k in range(5):
+        la, ia = a.forward([tok], len(prompt) + k)
+        lb, ib = b.forward([tok], len(prompt) + k)
+        assert np.array_equal(la, lb) and ia == ib
+        tok = ia
+    ids, err, ties = compare_generation(Q8Model.from_gguf(path), oracle.OracleModel(m), prompt, 8, "gguf tiny 13+8")
+    assert ties <= 1
+
+
+def test_gguf_neox_architecture_runs_the_neox_forward(tmp_path):
+    from quantized_q8_gemv_amd.model import Q8Model
+    s = synth.ModelShape("tiny-neox", n_layer=4, n_embd=576, n_head=9, n_head_kv=3, head_dim=64,
+                         n_ff=1536, n_vocab=4096, rope_neox=True)
+    m = synth.random_model(s, 0)
+    path = _write(tmp_path, m, arch="qwen2")
+    gm = Q8Model.from_gguf(path)
+    assert gm.cfg.rope_type == 1
+    prompt = synth.prompt_ids(s.n_vocab, 13, 1)
+    ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 6, "gguf qwen2-arch neox 13+6")
+    log(f"gguf neox: max abs err {err:.3g}")
+    assert ties <= 1
+
+
+def test_gguf_missing_tensor_is_named(tmp_path):
+    from quantized_q8_gemv_amd import q8l as C
+    from quantized_q8_gemv_amd.model import Q8Model
+    w, m, prompt = synth.workload_inputs("C1")
+    path = _write(tmp_path, m, drop=("blk.2.attn_v.weight",))
+    with pytest.raises(C.Q8LError) as e:
+        Q8Model.from_gguf(path)
+    assert e.value.status == C.Q8L_E_MISSING_TENSOR
+    assert "cannot find blk.2.attn_v.weight" in str(e.value)
