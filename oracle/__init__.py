@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         P, D, I64, I32 = ctypes.c_void_p, ctypes.c_double, ctypes.c_int64, ctypes.c_int32
         L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]; L.orc_f16_to_f64.restype = D
         L.orc_dequant_row.argtypes = [P, I64, P]; L.orc_dequant_row.restype = None
+        L.orc_dequant_q4_0_row.argtypes = [P, I64, P]; L.orc_dequant_q4_0_row.restype = None
+        L.orc_dequant_q5_0_row.argtypes = [P, I64, P]; L.orc_dequant_q5_0_row.restype = None
         L.orc_matmul_q8.argtypes = [P, I64, I64, P, I64, P]; L.orc_matmul_q8.restype = None
         L.orc_rmsnorm.argtypes = [P, P, I64, D, P]; L.orc_rmsnorm.restype = None
         L.orc_rope_angle.argtypes = [I64, I64, I64, D]; L.orc_rope_angle.restype = D
@@ -100,6 +102,24 @@ def dequant_q8_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
     out = np.empty((rows, cols), dtype=np.float64)
     for r in range(rows):
         lib().orc_dequant_row(_ptr(raw[r]), cols, _ptr(out[r]))
+    return out
+
+
+def dequant_q4_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Decode a Q4_0 matrix [rows, cols] (18 bytes per 32 weights)."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8).reshape(rows, cols // 32 * 18)
+    out = np.empty((rows, cols), dtype=np.float64)
+    for r in range(rows):
+        lib().orc_dequant_q4_0_row(_ptr(raw[r]), cols, _ptr(out[r]))
+    return out
+
+
+def dequant_q5_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Decode a Q5_0 matrix [rows, cols] (22 bytes per 32 weights)."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8).reshape(rows, cols // 32 * 22)
+    out = np.empty((rows, cols), dtype=np.float64)
+    for r in range(rows):
+        lib().orc_dequant_q5_0_row(_ptr(raw[r]), cols, _ptr(out[r]))
     return out
 
 

@@ -89,6 +89,37 @@ double orc_f16_to_f64(uint16_t h) {
 }
 
 /* Decode one row of K weights (K/32 blocks of 34 bytes) into f64. */
+/* Two other 32-weight block formats of the same file family (the public GGUF
+ * block definitions; the pages fix only their sizes, "速度", section "CPU GGUF"):
+ * Q4_0 = f16 d + 16 bytes: weight i < 16 is the low nibble of byte i, weight
+ * i + 16 its high nibble, value = d * (nibble - 8). Q5_0 = f16 d + a 32-bit
+ * little-endian word of fifth bits (bit i for weight i) + 16 bytes of nibbles
+ * in the Q4_0 order, value = d * ((nibble | fifth bit << 4) - 16). */
+void orc_dequant_q4_0_row(const uint8_t *row, int64_t K, double *out) {
+    for (int64_t b = 0; b < K / 32; ++b) {
+        const uint8_t *blk = row + b * 18;
+        double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+        for (int i = 0; i < 16; ++i) {
+            out[b * 32 + i] = d * (double)((blk[2 + i] & 0x0f) - 8);
+            out[b * 32 + i + 16] = d * (double)((blk[2 + i] >> 4) - 8);
+        }
+    }
+}
+
+void orc_dequant_q5_0_row(const uint8_t *row, int64_t K, double *out) {
+    for (int64_t b = 0; b < K / 32; ++b) {
+        const uint8_t *blk = row + b * 22;
+        double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+        uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) | ((uint32_t)blk[5] << 24);
+        for (int i = 0; i < 16; ++i) {
+            int lo = (blk[6 + i] & 0x0f) | (int)(((qh >> i) & 1u) << 4);
+            int hi = (blk[6 + i] >> 4) | (int)(((qh >> (i + 16)) & 1u) << 4);
+            out[b * 32 + i] = d * (double)(lo - 16);
+            out[b * 32 + i + 16] = d * (double)(hi - 16);
+        }
+    }
+}
+
 void orc_dequant_row(const uint8_t *row, int64_t K, double *out) {
     for (int64_t b = 0; b < K / ORC_QK; ++b) {
         const uint8_t *blk = row + b * ORC_QBYTES;

@@ -23,7 +23,7 @@ def load_golden(name):
                 continue
             k, v = (s.strip() for s in line.split("=", 1))
             if "," in v:
-                out[k] = tuple(int(x) for x in v.split(","))
+                out[k] = tuple(float(x) if "." in x else int(x) for x in v.split(","))
             elif "." in v:
                 out[k] = float(v)
             else:

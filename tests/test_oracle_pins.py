@@ -448,3 +448,68 @@ def test_zero_gate_or_down_removes_the_mlp(micro):
 def test_argmax_lowest_index_on_ties():
     assert oracle.argmax(np.array([1.0, 3.0, 3.0, 2.0], np.float32)) == 1
     assert oracle.argmax(np.array([5.0], np.float32)) == 0
+
+
+# ---------------------------------------------------------------- other block formats
+
+def test_q4_k_m_table_pins_the_block_sizes(golden_printed):
+    """The pages' Q4_K_M file of the 135M model ("速度", section "CPU GGUF"): 166
+    Q5_0 tensors hold 51.2 MiB, 16 Q4K 7.6, 14 Q6K 9.7, 15 Q8_0 30.3, 61 F32 0.1.
+    With 22 bytes per 32 weights (Q5_0), 144 and 210 per 256 (Q4K, Q6K) and the
+    reading that rows of 576 (not a multiple of 256) fall back to Q5_0 or Q8_0:
+    q, k, o, gate, up and 16 of the v projections in Q5_0; token_embd and the
+    other 14 v in Q8_0; ffn_down (rows of 1536) in Q4K (16) and Q6K (14)."""
+    s = synth.SMOL135M
+    H, F, KV = s.n_embd, s.n_ff, s.kv_dim
+    b = lambda rows, cols, per, size: rows * cols // per * size
+    q5 = 30 * (b(s.q_dim, H, 32, 22) + b(KV, H, 32, 22) + b(H, s.q_dim, 32, 22) + 2 * b(F, H, 32, 22)) \
+        + 16 * b(KV, H, 32, 22)
+    q8 = b(s.n_vocab, H, 32, 34) + 14 * b(KV, H, 32, 34)
+    q4k, q6k = 16 * b(H, F, 256, 144), 14 * b(H, F, 256, 210)
+    f32 = 61 * H * 4
+    mib = lambda x: round(x / 2 ** 20, 1)
+    assert (166, mib(q5)) == golden_printed["q4km_q5_0"]
+    assert (15, mib(q8)) == golden_printed["q4km_q8_0"]
+    assert (16, mib(q4k)) == golden_printed["q4km_q4k"]
+    assert (14, mib(q6k)) == golden_printed["q4km_q6k"]
+    assert (61, mib(f32)) == golden_printed["q4km_f32"]
+    # and 30 x 9 + 2 = 272 tensors in all
+    assert 166 + 15 + 16 + 14 + 61 == golden_printed["gguf_tensor_count"]
+
+
+def test_q4_0_and_q5_0_hand_blocks():
+    d = np.float16(0.5).view(np.uint16)
+    # Q4_0: byte i = (high << 4) | low; weights i and i + 16
+    qs = np.array([(15 << 4) | 0] + [(8 << 4) | 9] * 15, dtype=np.uint8)
+    blk = np.concatenate([np.array([d & 0xff, d >> 8], dtype=np.uint8), qs])
+    w = oracle.dequant_q4_0(blk, 1, 32)[0]
+    assert w[0] == 0.5 * -8 and w[16] == 0.5 * 7
+    assert np.all(w[1:16] == 0.5) and np.all(w[17:] == 0.0)
+    # Q5_0: fifth bits for weights 0 and 17 only
+    qh = (1 << 0) | (1 << 17)
+    qs = np.zeros(16, dtype=np.uint8)
+    qs[1] = (3 << 4) | 2
+    blk = np.concatenate([np.array([d & 0xff, d >> 8], dtype=np.uint8),
+                          np.frombuffer(np.uint32(qh).tobytes(), dtype=np.uint8), qs])
+    w = oracle.dequant_q5_0(blk, 1, 32)[0]
+    assert w[0] == 0.5 * (16 - 16) and w[16] == 0.5 * -16
+    assert w[1] == 0.5 * (2 - 16) and w[17] == 0.5 * (3 + 16 - 16)
+    assert np.all(w[2:16] == 0.5 * -16) and np.all(w[18:] == 0.5 * -16)
+
+
+def test_q4_0_and_q5_0_values_are_q8_0_values():
+    """Both formats hold d * (small integer) per 32-weight block: the same
+    values as a Q8_0 block with the same d and int8 = the integer (the basis
+    of loading them on the Q8_0 path)."""
+    rng = np.random.default_rng(21)
+    rows, cols = 3, 128
+    d = synth.draw_q8_0(rng, rows, cols)[0]           # f16 scales [rows, cols/32]
+    q5 = rng.integers(0, 256, (rows, cols // 32, 20), dtype=np.uint8)
+    raw5 = np.concatenate([d.view(np.uint8).reshape(rows, cols // 32, 2), q5], axis=2).reshape(rows, -1)
+    w5 = oracle.dequant_q5_0(raw5, rows, cols)
+    ints = np.rint(w5 / np.repeat(d.astype(np.float64), 32, axis=1), where=np.repeat(d != 0, 32, axis=1),
+                   out=np.zeros_like(w5))
+    assert ints.min() >= -16 and ints.max() <= 15
+    q8 = synth.pack_q8_0(d, ints.astype(np.int8))
+    nz = np.repeat(d != 0, 32, axis=1)
+    assert np.array_equal(oracle.dequant_q8_0(q8, rows, cols)[nz], w5[nz])
