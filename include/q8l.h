@@ -302,11 +302,18 @@ q8l_status q8l_gguf_config(q8l_gguf *g, int32_t max_seq_len, q8l_config *cfg);
 int64_t q8l_gguf_find_tensor(const q8l_gguf *g, const char *name);
 /* Tensor `index`: name (valid while the handle is open), dtype (a q8l_dtype, or
  * -1 with Q8L_E_FORMAT for other types), rows x cols (cols = the innermost
- * dimension), absolute file offset and byte size. Any output may be NULL. */
+ * dimension), absolute file offset and byte size as read. Any output may be
+ * NULL. Q4_0 and Q5_0 tensors (32-weight blocks of an f16 scale times 4- or
+ * 5-bit integers; sizes pinned by "速度", section "CPU GGUF") are read as Q8_0:
+ * dtype Q8L_Q8_0, size rows*cols/32*34, each block converted exactly (same
+ * scale, int8 = the block's integer). Other block formats (the K-quants) are
+ * listed but not read. */
 q8l_status q8l_gguf_tensor_info(const q8l_gguf *g, int64_t index, const char **name, int32_t *dtype,
                                 int64_t *rows, int64_t *cols, uint64_t *offset, uint64_t *nbytes);
-/* Read tensor `index`'s bytes into host memory; nbytes must equal its size. */
+/* Read tensor `index`'s bytes into host memory; nbytes must equal its size as read. */
 q8l_status q8l_gguf_read_tensor(q8l_gguf *g, int64_t index, void *host_dst, size_t nbytes);
+/* The tensor's type id in the file (the GGUF numbering: 0 F32, 2 Q4_0, 6 Q5_0, 8 Q8_0, ...), or -1. */
+int32_t q8l_gguf_tensor_file_type(const q8l_gguf *g, int64_t index);
 
 #ifdef __cplusplus
 }

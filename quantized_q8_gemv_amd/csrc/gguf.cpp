@@ -22,6 +22,7 @@
 // Q8L_E_FORMAT instead of a large allocation or an out-of-range read.
 
 #include <cstdio>
+#include <sys/types.h>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -37,8 +38,13 @@ enum GgufType : uint32_t {
     G_STRING = 8, G_ARRAY = 9, G_U64 = 10, G_I64 = 11, G_F64 = 12
 };
 
-// Tensor element types of the file format this library can bind.
+// Tensor element types of the file format this library can bind. Q4_0 and
+// Q5_0 blocks hold d * (an integer in [-8, 7] or [-16, 15]) per 32 weights:
+// the same values as a Q8_0 block with the same d, so they are read as Q8_0
+// (converted exactly while reading).
 constexpr uint32_t kTypeF32 = 0;
+constexpr uint32_t kTypeQ4_0 = 2;
+constexpr uint32_t kTypeQ5_0 = 6;
 constexpr uint32_t kTypeQ8_0 = 8;
 
 struct Value {
@@ -58,9 +64,37 @@ struct TensorInfo {
     std::string name;
     std::vector<uint64_t> dims;
     uint32_t type = 0;
-    uint64_t offset = 0;   // within the data region
-    uint64_t nbytes = 0;
+    uint64_t offset = 0;      // within the data region
+    uint64_t file_bytes = 0;  // bytes in the file
+    uint64_t nbytes = 0;      // bytes as read (Q8_0 for the 32-weight integer formats), 0 if unreadable
 };
+
+bool q8_family(uint32_t t) { return t == kTypeQ4_0 || t == kTypeQ5_0 || t == kTypeQ8_0; }
+
+uint64_t block_bytes(uint32_t t) { return t == kTypeQ4_0 ? 18 : t == kTypeQ5_0 ? 22 : 34; }
+
+// One Q4_0 / Q5_0 block (file layout: public GGUF block definitions) as a
+// Q8_0 block: the f16 scale is copied, weight i of the block becomes the int8
+// (nibble - 8), resp. ((nibble | fifth bit << 4) - 16); nibble i < 16 is the
+// low half of byte i, nibble i + 16 its high half.
+void to_q8_0(uint32_t type, const uint8_t *src, uint8_t *dst) {
+    dst[0] = src[0];
+    dst[1] = src[1];
+    int8_t *q = reinterpret_cast<int8_t *>(dst + 2);
+    if (type == kTypeQ4_0) {
+        for (int i = 0; i < 16; ++i) {
+            q[i] = int8_t((src[2 + i] & 0x0f) - 8);
+            q[i + 16] = int8_t((src[2 + i] >> 4) - 8);
+        }
+        return;
+    }
+    uint32_t qh = 0;
+    std::memcpy(&qh, src + 2, 4);  // little-endian host
+    for (int i = 0; i < 16; ++i) {
+        q[i] = int8_t(((src[6 + i] & 0x0f) | (((qh >> i) & 1u) << 4)) - 16);
+        q[i + 16] = int8_t(((src[6 + i] >> 4) | (((qh >> (i + 16)) & 1u) << 4)) - 16);
+    }
+}
 
 class Reader {
   public:
@@ -231,15 +265,17 @@ q8l_status parse(q8l_gguf *g) {
             if (d == 0 || n > (uint64_t(1) << 48) / d) return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " has bad dimensions");
             n *= d;
         }
-        if (t.type == kTypeF32) t.nbytes = n * 4;
-        else if (t.type == kTypeQ8_0) {
-            if (t.dims[0] % 32) return fail(g, Q8L_E_FORMAT, "Q8_0 tensor " + t.name + " rows are not whole blocks");
+        if (t.type == kTypeF32) {
+            t.file_bytes = t.nbytes = n * 4;
+        } else if (q8_family(t.type)) {
+            if (t.dims[0] % 32) return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " rows are not whole blocks");
+            t.file_bytes = n / 32 * block_bytes(t.type);
             t.nbytes = n / 32 * 34;
         } else {
-            t.nbytes = 0;  // unsupported type: listed, but not readable
+            t.file_bytes = t.nbytes = 0;  // other types: listed, not readable (size unknown here)
         }
         if (t.offset % a) return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " is not aligned");
-        if (t.offset > g->file_size - g->data_offset || t.nbytes > g->file_size - g->data_offset - t.offset)
+        if (t.offset > g->file_size - g->data_offset || t.file_bytes > g->file_size - g->data_offset - t.offset)
             return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " extends past the end of the file");
     }
     return Q8L_OK;
@@ -393,25 +429,40 @@ q8l_status q8l_gguf_tensor_info(const q8l_gguf *g, int64_t index, const char **n
     if (nbytes) *nbytes = t.nbytes;
     if (dtype) {
         if (t.type == kTypeF32) *dtype = Q8L_F32;
-        else if (t.type == kTypeQ8_0) *dtype = Q8L_Q8_0;
+        else if (q8_family(t.type)) *dtype = Q8L_Q8_0;
         else {
             *dtype = -1;
             return fail(const_cast<q8l_gguf *>(g), Q8L_E_FORMAT,
-                        "tensor " + t.name + " has type " + std::to_string(t.type) + " (only F32 and Q8_0 are read)");
+                        "tensor " + t.name + " has type " + std::to_string(t.type) +
+                            " (F32, Q8_0, Q4_0 and Q5_0 are read)");
         }
     }
     return Q8L_OK;
 }
 
+int32_t q8l_gguf_tensor_file_type(const q8l_gguf *g, int64_t index) {
+    if (!g || index < 0 || index >= int64_t(g->tensors.size())) return -1;
+    return int32_t(g->tensors[size_t(index)].type);
+}
+
 q8l_status q8l_gguf_read_tensor(q8l_gguf *g, int64_t index, void *host_dst, size_t nbytes) {
     if (!g || !host_dst || index < 0 || index >= int64_t(g->tensors.size())) return Q8L_E_INVALID_ARG;
     const TensorInfo &t = g->tensors[size_t(index)];
-    if (t.type != kTypeF32 && t.type != kTypeQ8_0)
+    if (t.type != kTypeF32 && !q8_family(t.type))
         return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " has an unsupported type");
     if (nbytes != t.nbytes) return fail(g, Q8L_E_SHAPE, "tensor " + t.name + ": buffer size differs");
     const uint64_t off = g->data_offset + t.offset;
-    if (std::fseek(g->f, long(off), SEEK_SET) != 0) return fail(g, Q8L_E_IO, "seek failed for " + t.name);
-    if (std::fread(host_dst, 1, nbytes, g->f) != nbytes) return fail(g, Q8L_E_IO, "short read for " + t.name);
+    if (fseeko(g->f, off_t(off), SEEK_SET) != 0) return fail(g, Q8L_E_IO, "seek failed for " + t.name);
+    if (t.type == kTypeF32 || t.type == kTypeQ8_0) {
+        if (std::fread(host_dst, 1, nbytes, g->f) != nbytes) return fail(g, Q8L_E_IO, "short read for " + t.name);
+        return Q8L_OK;
+    }
+    std::vector<uint8_t> raw(size_t(t.file_bytes));
+    if (std::fread(raw.data(), 1, raw.size(), g->f) != raw.size())
+        return fail(g, Q8L_E_IO, "short read for " + t.name);
+    const uint64_t nblk = t.file_bytes / block_bytes(t.type);
+    uint8_t *dst = static_cast<uint8_t *>(host_dst);
+    for (uint64_t b = 0; b < nblk; ++b) to_q8_0(t.type, raw.data() + b * block_bytes(t.type), dst + b * 34);
     return Q8L_OK;
 }
 

@@ -97,6 +97,7 @@ _SIGS = {
                               ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_uint64),
                               ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
     "q8l_gguf_read_tensor": ([_P, ctypes.c_int64, _P, ctypes.c_size_t], ctypes.c_int),
+    "q8l_gguf_tensor_file_type": ([_P, ctypes.c_int64], ctypes.c_int32),
 }
 
 
@@ -309,6 +310,10 @@ def q8l_gguf_tensor_info(g: int, index: int):
 
 def q8l_gguf_read_tensor(g: int, index: int, host_dst, nbytes: int) -> int:
     return lib().q8l_gguf_read_tensor(g, index, _ptr(host_dst), nbytes)
+
+
+def q8l_gguf_tensor_file_type(g: int, index: int) -> int:
+    return int(lib().q8l_gguf_tensor_file_type(g, index))
 
 
 def config_from(shape_fields: dict) -> q8l_config:

@@ -106,3 +106,36 @@ def model_tensors(model) -> List[TensorEntry]:
         else:
             out.append((t.name, TYPE_F32, [t.cols] if t.rows == 1 else [t.cols, t.rows], data))
     return out
+
+
+# ---- 32-weight integer block formats (public GGUF block definitions) ----
+# Q4_0: f16 d, 16 bytes; weight i < 16 = low nibble of byte i, i + 16 = high
+# nibble; value d * (nibble - 8). Q5_0: f16 d, u32 fifth bits (bit i for weight
+# i), 16 bytes of nibbles as in Q4_0; value d * ((nibble | bit << 4) - 16).
+TYPE_Q4_0, TYPE_Q5_0 = 2, 6
+
+
+def random_blocks(rng: np.random.Generator, rows: int, cols: int, fmt: str) -> np.ndarray:
+    """Random Q4_0 / Q5_0 bytes [rows, cols/32 * block] with synth-style f16 scales."""
+    nb = cols // 32
+    d = (np.abs(rng.standard_normal((rows, nb))) * 0.02 / 15).astype(np.float16)
+    body = 16 if fmt == "q4_0" else 20
+    rest = rng.integers(0, 256, (rows, nb, body), dtype=np.uint8)
+    return np.concatenate([d.view(np.uint8).reshape(rows, nb, 2), rest], axis=2).reshape(rows, -1)
+
+
+def to_q8_0(raw: np.ndarray, rows: int, cols: int, fmt: str) -> np.ndarray:
+    """The same values as Q8_0 blocks (same scale, int8 = the block's integer)."""
+    nb = cols // 32
+    size = 18 if fmt == "q4_0" else 22
+    b = raw.reshape(rows, nb, size)
+    qs = b[:, :, size - 16:]
+    lo, hi = (qs & 0x0F).astype(np.int16), (qs >> 4).astype(np.int16)
+    if fmt == "q4_0":
+        vals = np.concatenate([lo - 8, hi - 8], axis=2)
+    else:
+        qh = b[:, :, 2:6].copy().view("<u4")[..., 0]
+        bits = (qh[..., None] >> np.arange(32, dtype=np.uint32)) & 1
+        vals = np.concatenate([lo, hi], axis=2) + (bits.astype(np.int16) << 4) - 16
+    out = np.concatenate([b[:, :, :2], vals.astype(np.int8).view(np.uint8)], axis=2)
+    return out.reshape(rows, nb * 34)

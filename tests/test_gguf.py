@@ -235,3 +235,28 @@ def test_unsupported_tensor_type_is_reported_by_name(lib, tmp_path):
         assert C.q8l_gguf_read_tensor(g, idx, np.empty(8, np.uint8), 8) == C.Q8L_E_FORMAT
     finally:
         C.q8l_gguf_close(g)
+
+
+@pytest.mark.parametrize("fmt,ftype", [("q5_0", W.TYPE_Q5_0), ("q4_0", W.TYPE_Q4_0)])
+def test_q4_0_and_q5_0_tensors_read_as_exact_q8_0(lib, tmp_path, fmt, ftype):
+    import oracle
+    rng = np.random.default_rng(9)
+    rows, cols = 40, 1536
+    raw = W.random_blocks(rng, rows, cols, fmt)
+    path = str(tmp_path / f"{fmt}.gguf")
+    W.write(path, W.llama_kv(synth.TINY), [("blk.0.ffn_down.weight", ftype, [cols, rows], raw.tobytes())])
+    g = C.q8l_gguf_open(path)
+    try:
+        assert C.q8l_gguf_tensor_file_type(g, 0) == ftype
+        st, info = C.q8l_gguf_tensor_info(g, 0)
+        assert st == C.Q8L_OK and info["dtype"] == C.Q8L_Q8_0
+        assert info["nbytes"] == rows * cols // 32 * 34
+        buf = np.empty(info["nbytes"], np.uint8)
+        assert C.q8l_gguf_read_tensor(g, 0, buf, buf.size) == C.Q8L_OK
+    finally:
+        C.q8l_gguf_close(g)
+    # the reader's blocks equal the test's own conversion byte for byte ...
+    assert np.array_equal(buf.reshape(rows, -1), W.to_q8_0(raw, rows, cols, fmt))
+    # ... and decode to the oracle's values of the original format exactly
+    ref = oracle.dequant_q5_0(raw, rows, cols) if fmt == "q5_0" else oracle.dequant_q4_0(raw, rows, cols)
+    assert np.array_equal(oracle.dequant_q8_0(buf, rows, cols), ref)

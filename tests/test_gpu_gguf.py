@@ -64,3 +64,35 @@ def test_gguf_missing_tensor_is_named(tmp_path):
         Q8Model.from_gguf(path)
     assert e.value.status == C.Q8L_E_MISSING_TENSOR
     assert "cannot find blk.2.attn_v.weight" in str(e.value)
+
+
+def test_gguf_mixed_block_formats_match_the_oracle(tmp_path):
+    """A file in the mix the pages' Q4_K_M file shows for rows of 576 (Q5_0
+    projections, some v in Q8_0) plus Q4_0 down projections: read as exact
+    Q8_0 and compared with the oracle on the test's own conversion."""
+    from quantized_q8_gemv_amd.model import Q8Model
+    w, m, prompt = synth.workload_inputs("C1")
+    s = m.shape
+    rng = np.random.default_rng(17)
+    file_tensors, oracle_model = [], m
+    for name, ftype, dims, data in W.model_tensors(m):
+        kind = name.split(".")[-2] if name.startswith("blk.") else ""
+        layer = int(name.split(".")[1]) if name.startswith("blk.") else -1
+        fmt = None
+        if kind in ("attn_q", "attn_k", "attn_output", "ffn_gate", "ffn_up") or (kind == "attn_v" and layer % 2):
+            fmt = "q5_0"
+        elif kind == "ffn_down":
+            fmt = "q4_0"
+        if fmt is None:
+            file_tensors.append((name, ftype, dims, data))
+            continue
+        cols, rows = dims
+        raw = W.random_blocks(rng, rows, cols, fmt)
+        file_tensors.append((name, W.TYPE_Q5_0 if fmt == "q5_0" else W.TYPE_Q4_0, dims, raw.tobytes()))
+        oracle_model = oracle_model.replace(name, W.to_q8_0(raw, rows, cols, fmt))
+    path = str(tmp_path / "mixed.gguf")
+    W.write(path, W.llama_kv(s), file_tensors)
+    ids, err, ties = compare_generation(Q8Model.from_gguf(path), oracle.OracleModel(oracle_model), prompt, 8,
+                                        "gguf mixed q5_0/q4_0/q8_0 13+8")
+    log(f"gguf mixed formats: max abs err {err:.3g}")
+    assert ties <= 1
