@@ -251,27 +251,31 @@ def main():
     # Per-kernel launch times (HIP events on the stream the kernels run on).
     assert gm.forward_async(prompt, 0) == C.Q8L_OK
     torch.cuda.synchronize()
-    ms = (ctypes.c_float * NKINDS)()
+    ms = (ctypes.c_float * (NKINDS + 1))()
     st = C.lib().q8l_time_decode_kernels(gm.handle, args.kernel_reps, ms,
                                          torch.cuda.current_stream().cuda_stream)
     assert st == C.Q8L_OK, C.q8l_last_error(gm.handle)
+    # mean time per launch of back-to-back launches (the last entry: an empty
+    # kernel, the dispatch gap alone)
+    overhead = ms[NKINDS]
+    raw = [ms[i] for i in range(NKINDS)]
+    ms = raw
     kv_len = len(prompt) + 1
     kb = kernel_bytes(s, kv_len)
-    if ms[2] == 0:  # attention folded into the o-projection: it reads the KV cache too
-        kb[3] += kb[2] - s.q_dim * 4
     launches = [1, s.n_layer, s.n_layer, s.n_layer, s.n_layer, s.n_layer, 1, 1]
-    launches = [n if ms[i] > 0 else 0 for i, n in enumerate(launches)]
+    launches = [n if raw[i] > 0 else 0 for i, n in enumerate(launches)]
     per_step = [ms[i] * launches[i] for i in range(NKINDS)]
     dom = max(range(NKINDS), key=lambda i: per_step[i])
     kernels = {KIND_NAMES[i]: {"us": round(ms[i] * 1e3, 2), "bytes": kb[i],
-                               "gbs": round(kb[i] / (ms[i] * 1e-3) / 1e9, 1) if ms[i] > 0 else 0.0,
+                               "gbs": round(kb[i] / (ms[i] * 1e-3) / 1e9, 1) if raw[i] > 0 else 0.0,
                                "launches_per_token": launches[i]} for i in range(NKINDS)}
     achieved = kb[dom] / (ms[dom] * 1e-3) / 1e9
     traffic = measured_traffic(args.config, KIND_NAMES[dom])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": KIND_NAMES[dom], "symbol": kernel_symbols(s, kv_len)[dom],
-                "bytes_per_launch": kb[dom], "us_per_launch": round(ms[dom] * 1e3, 2)}
+                "bytes_per_launch": kb[dom], "us_per_launch": round(ms[dom] * 1e3, 2),
+                "empty_kernel_us": round(overhead * 1e3, 2)}
     copy_gbs = copy_bandwidth(torch)
     eprint(f"[bench] device copy: {copy_gbs:.0f} GB/s (1 GiB, read + write)")
     eprint(f"[bench] kernels: " + ", ".join(f"{k} {v['us']}us" for k, v in kernels.items()))

@@ -232,13 +232,15 @@ q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspa
                          size_t workspace_bytes, void *stream);
 
 /*
- * Measurement: launch each kernel of one decode step on its own, `reps`
- * times, each launch between two HIP events on `stream`, and write the mean
- * duration in milliseconds to ms_out[kind] (ms_out holds 8 floats), kinds
+ * Measurement: launch each kernel of one decode step on its own, once
+ * untimed and then `reps` times back to back between two HIP events on
+ * `stream`, and write the mean time per launch in milliseconds to
+ * ms_out[kind] (ms_out holds 9 floats), kinds
  *   0 embedding, 1 q/k/v (+norm, rope, KV write), 2 attention (split
  *   partials), 3 o-projection (+partial merge, residual), 4 gate/up (+norm,
  *   SiLU*up), 5 down (+residual), 6 output layer (+norm, per-workgroup
- *   argmax), 7 argmax merge.
+ *   argmax), 7 argmax merge, 8 an empty kernel (the dispatch gap between
+ *   back-to-back launches, included in every other entry).
  * Layer 0's weights are used, at the current cache length (attention over
  * cache_len + 1 keys). The residual stream, the next KV slot and the logits
  * buffer are scratch afterwards: the next forward rewrites them before use.

@@ -70,6 +70,9 @@ __global__ __launch_bounds__(kThreads) void k_embed(const uint8_t *E, int H, int
     }
 }
 
+// An empty kernel: the launch-and-event overhead that timings subtract.
+__global__ void k_noop() {}
+
 // The NEOX rope convention ("量化 llama 的一次前向", section "RoPE：两种约定，按架构名
 // 选"): dimension j of a head is rotated with dimension j + hd/2 by the table's
 // angle for pair j. One workgroup per (token, head); heads [0, nh) are the
@@ -108,6 +111,11 @@ hipError_t launch_embed(const uint8_t *E, int H, int V, const StepState *st,
                         hipStream_t s) {
     hipLaunchKernelGGL(k_embed, dim3(T), dim3(kThreads), 0, s, E, H, V, st, tok_buf,
                        from_state_token, x);
+    return hipGetLastError();
+}
+
+hipError_t launch_noop(hipStream_t s) {
+    hipLaunchKernelGGL(k_noop, dim3(1), dim3(64), 0, s);
     return hipGetLastError();
 }
 

@@ -68,6 +68,7 @@ struct Dims {
 hipError_t launch_set_state(const SetStateArgs &a, StepState *st, uint32_t *tok_buf,
                             hipStream_t s);
 hipError_t launch_rope_table(float2 *table, int max_seq, int hd, double theta, hipStream_t s);
+hipError_t launch_noop(hipStream_t s);
 // NEOX rotation of the T new tokens' q (rows of [T][nh*hd]) and k (cache slots
 // st->slot + t) at positions st->pos + t.
 hipError_t launch_rope_neox(const Dims &d, const StepState *st, const float2 *rope, float *q, float *kc,

@@ -533,31 +533,28 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
             case 4: return launch_gateup(d, w, x, h, 1, s);
             case 5: return launch_matmul(w.wd, d.H, d.F, h, 1, nullptr, d.eps, 1, x, s);
             case 6: return launch_lmhead(d, wout, m->out_norm, x, S, m->at<float>(m->lay.lm_part), s);
-            default: return launch_argmax_finish(d, m->at<float>(m->lay.lm_part), S, s);
+            case 7: return launch_argmax_finish(d, m->at<float>(m->lay.lm_part), S, s);
+            default: return launch_noop(s);
         }
     };
-    constexpr int kKinds = 8;
-    std::vector<hipEvent_t> ev(size_t(2) * reps * kKinds, nullptr);
+    constexpr int kKinds = 9;
+    // One pair of events around `reps` back-to-back launches of a kind: the
+    // mean is the kernel's own time plus the dispatch gap between launches
+    // (kind 8, an empty kernel, shows that gap alone).
+    std::vector<hipEvent_t> ev(size_t(2) * kKinds, nullptr);
     for (auto &e : ev) Q8L_HIP(m, hipEventCreate(&e), "hipEventCreate");
     hipError_t err = hipSuccess;
-    auto used = [&](int) { return true; };  // every kind runs in the decode step
-    for (int k = 0; k < kKinds && err == hipSuccess; ++k)
-        for (int r = 0; r < reps && err == hipSuccess && used(k); ++r) {
-            hipEvent_t *p = &ev[(size_t(k) * reps + r) * 2];
-            if ((err = hipEventRecord(p[0], s)) != hipSuccess) break;
-            if ((err = launch(k)) != hipSuccess) break;
-            err = hipEventRecord(p[1], s);
-        }
+    for (int k = 0; k < kKinds && err == hipSuccess; ++k) {
+        if ((err = launch(k)) != hipSuccess) break;  // warm-up launch, not timed
+        if ((err = hipEventRecord(ev[2 * k], s)) != hipSuccess) break;
+        for (int r = 0; r < reps && err == hipSuccess; ++r) err = launch(k);
+        if (err == hipSuccess) err = hipEventRecord(ev[2 * k + 1], s);
+    }
     if (err == hipSuccess) err = hipStreamSynchronize(s);
     for (int k = 0; k < kKinds && err == hipSuccess; ++k) {
-        double sum = 0.0;
-        for (int r = 0; r < reps && used(k); ++r) {
-            float ms = 0.f;
-            hipEvent_t *p = &ev[(size_t(k) * reps + r) * 2];
-            if ((err = hipEventElapsedTime(&ms, p[0], p[1])) != hipSuccess) break;
-            sum += ms;
-        }
-        ms_out[k] = float(sum / reps);
+        float ms = 0.f;
+        if ((err = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1])) != hipSuccess) break;
+        ms_out[k] = ms / float(reps);
     }
     for (auto &e : ev)
         if (e) hipEventDestroy(e);
