@@ -65,7 +65,11 @@ def lib() -> ctypes.CDLL:
         L.orc_dequant_row.argtypes = [P, I64, P]; L.orc_dequant_row.restype = None
         L.orc_dequant_q4_0_row.argtypes = [P, I64, P]; L.orc_dequant_q4_0_row.restype = None
         L.orc_dequant_q5_0_row.argtypes = [P, I64, P]; L.orc_dequant_q5_0_row.restype = None
+        L.orc_dequant_q4_k_row.argtypes = [P, I64, P]; L.orc_dequant_q4_k_row.restype = None
+        L.orc_dequant_q6_k_row.argtypes = [P, I64, P]; L.orc_dequant_q6_k_row.restype = None
         L.orc_matmul_q8.argtypes = [P, I64, I64, P, I64, P]; L.orc_matmul_q8.restype = None
+        L.orc_matmul_fmt.argtypes = [P, ctypes.c_int32, I64, I64, P, I64, P]
+        L.orc_matmul_fmt.restype = None
         L.orc_rmsnorm.argtypes = [P, P, I64, D, P]; L.orc_rmsnorm.restype = None
         L.orc_rope_angle.argtypes = [I64, I64, I64, D]; L.orc_rope_angle.restype = D
         L.orc_rope_i.argtypes = [P, I64, I64, D]; L.orc_rope_i.restype = None
@@ -74,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.orc_attend.argtypes = [P, P, P, I64, I64, I64, P]; L.orc_attend.restype = None
         L.orc_create.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_void_p)]
         L.orc_create.restype = P
+        L.orc_create_fmt.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_void_p), P, P]
+        L.orc_create_fmt.restype = P
         L.orc_destroy.argtypes = [P]; L.orc_destroy.restype = None
         L.orc_clear_kv_cache.argtypes = [P]; L.orc_clear_kv_cache.restype = None
         L.orc_cache_len.argtypes = [P]; L.orc_cache_len.restype = I32
@@ -121,6 +127,39 @@ def dequant_q5_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
     for r in range(rows):
         lib().orc_dequant_q5_0_row(_ptr(raw[r]), cols, _ptr(out[r]))
     return out
+
+
+# Block formats of the 256-weight "K" family (bytes per 256 weights) and the
+# oracle's format codes for matrices that may hold them.
+K_BLOCK_BYTES = {"q4_k": 144, "q6_k": 210}
+FMT_CODES = {"q8_0": 0, "q4_k": 1, "q6_k": 2}
+
+
+def dequant_q4_k(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Decode a Q4_K matrix [rows, cols] (144 bytes per 256 weights)."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8).reshape(rows, cols // 256 * 144)
+    out = np.empty((rows, cols), dtype=np.float64)
+    for r in range(rows):
+        lib().orc_dequant_q4_k_row(_ptr(raw[r]), cols, _ptr(out[r]))
+    return out
+
+
+def dequant_q6_k(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Decode a Q6_K matrix [rows, cols] (210 bytes per 256 weights)."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8).reshape(rows, cols // 256 * 210)
+    out = np.empty((rows, cols), dtype=np.float64)
+    for r in range(rows):
+        lib().orc_dequant_q6_k_row(_ptr(raw[r]), cols, _ptr(out[r]))
+    return out
+
+
+def matmul_fmt(raw: np.ndarray, fmt: str, rows: int, cols: int, x: np.ndarray) -> np.ndarray:
+    """Y[t] = W @ X[t] for W [rows, cols] in block format ``fmt`` ('q8_0', 'q4_k', 'q6_k')."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint8)
+    X = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float64)
+    Y = np.empty((X.shape[0], rows), dtype=np.float64)
+    lib().orc_matmul_fmt(_ptr(raw), FMT_CODES[fmt], rows, cols, _ptr(X), X.shape[0], _ptr(Y))
+    return Y
 
 
 def matmul_q8(raw: np.ndarray, rows: int, cols: int, x: np.ndarray) -> np.ndarray:
@@ -190,7 +229,12 @@ class OracleModel:
         self._arrays = [np.ascontiguousarray(t.data) for t in model.tensors]
         ptrs = (ctypes.c_void_p * len(self._arrays))(*[a.ctypes.data for a in self._arrays])
         self._ptrs = ptrs
-        h = lib().orc_create(ctypes.byref(self.cfg), ptrs)
+        fo = np.array([FMT_CODES[model[f"blk.{l}.attn_output.weight"].dtype] for l in range(s.n_layer)],
+                      dtype=np.int32)
+        fd = np.array([FMT_CODES[model[f"blk.{l}.ffn_down.weight"].dtype] for l in range(s.n_layer)],
+                      dtype=np.int32)
+        self._fmts = (fo, fd)
+        h = lib().orc_create_fmt(ctypes.byref(self.cfg), ptrs, _ptr(fo), _ptr(fd))
         if not h:
             raise ValueError("oracle rejected the model configuration")
         self._h = h

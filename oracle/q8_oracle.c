@@ -60,9 +60,15 @@ typedef struct {
     int32_t rope_neox;    /* 0: pairs (2j, 2j+1) (llama); 1: pairs (j, j + hd/2) */
 } orc_config;
 
+/* Block formats of the o and down projections (the others are Q8_0). */
+#define ORC_FMT_Q8_0 0
+#define ORC_FMT_Q4_K 1
+#define ORC_FMT_Q6_K 2
+
 typedef struct {
     const float *attn_norm, *ffn_norm;
     const uint8_t *wq, *wk, *wv, *wo, *wg, *wu, *wd;
+    int32_t fo, fd;   /* formats of wo and wd */
 } orc_layer;
 
 typedef struct {
@@ -120,6 +126,66 @@ void orc_dequant_q5_0_row(const uint8_t *row, int64_t K, double *out) {
     }
 }
 
+/* Two 256-weight "K" formats (public GGUF block definitions; the pages fix
+ * their sizes through the Q4_K_M table of "速度", section "CPU GGUF").
+ * Q4_K, 144 bytes: f16 d, f16 dmin, 12 bytes holding eight 6-bit scales and
+ * eight 6-bit mins, 128 bytes of nibbles. Sub-block j (32 weights) has scale s_j
+ * and min m_j; for j < 4 they are the low 6 bits of bytes j and j + 4; for
+ * j >= 4 the scale is the low nibble of byte j + 4 with the top two bits of
+ * byte j - 4 above it, the min the high nibble of byte j + 4 with the top two
+ * bits of byte j above it. Weight l of sub-block j = d*s_j*q - dmin*m_j, q the
+ * low (j even) or high (j odd) nibble of byte 32*(j/2) + l. */
+static void q4k_scale_min(int j, const uint8_t *sc, int *s, int *m) {
+    if (j < 4) {
+        *s = sc[j] & 63;
+        *m = sc[j + 4] & 63;
+    } else {
+        *s = (sc[j + 4] & 0x0f) | ((sc[j - 4] >> 6) << 4);
+        *m = (sc[j + 4] >> 4) | ((sc[j] >> 6) << 4);
+    }
+}
+
+void orc_dequant_q4_k_row(const uint8_t *row, int64_t K, double *out) {
+    for (int64_t b = 0; b < K / 256; ++b) {
+        const uint8_t *blk = row + b * 144;
+        const double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+        const double dmin = orc_f16_to_f64((uint16_t)(blk[2] | (blk[3] << 8)));
+        const uint8_t *sc = blk + 4, *qs = blk + 16;
+        for (int j = 0; j < 8; ++j) {
+            int s, m;
+            q4k_scale_min(j, sc, &s, &m);
+            for (int l = 0; l < 32; ++l) {
+                const uint8_t byte = qs[32 * (j / 2) + l];
+                const int q = (j & 1) ? (byte >> 4) : (byte & 0x0f);
+                out[b * 256 + 32 * j + l] = d * (double)s * (double)q - dmin * (double)m;
+            }
+        }
+    }
+}
+
+/* Q6_K, 210 bytes: 128 bytes of low nibbles, 64 bytes of 2-bit high parts,
+ * 16 int8 scales (one per 16 weights), f16 d. In each half (128 weights: low
+ * nibbles 64h.., high parts 32h.., scales 8h..), weight 32*k + l (k = 0..3,
+ * l = 0..31) takes the low (k < 2) or high (k >= 2) nibble of low byte
+ * l + 32*(k odd), the 2-bit field k of high byte l, minus 32, times d and
+ * scale 2*k + l/16. */
+void orc_dequant_q6_k_row(const uint8_t *row, int64_t K, double *out) {
+    for (int64_t b = 0; b < K / 256; ++b) {
+        const uint8_t *blk = row + b * 210;
+        const uint8_t *ql = blk, *qh = blk + 128;
+        const int8_t *sc = (const int8_t *)(blk + 192);
+        const double d = orc_f16_to_f64((uint16_t)(blk[208] | (blk[209] << 8)));
+        for (int h = 0; h < 2; ++h)
+            for (int k = 0; k < 4; ++k)
+                for (int l = 0; l < 32; ++l) {
+                    const uint8_t lo = ql[64 * h + l + 32 * (k & 1)];
+                    const int nib = (k < 2) ? (lo & 0x0f) : (lo >> 4);
+                    const int q = (nib | (((qh[32 * h + l] >> (2 * k)) & 3) << 4)) - 32;
+                    out[b * 256 + 128 * h + 32 * k + l] = d * (double)sc[8 * h + 2 * k + l / 16] * (double)q;
+                }
+    }
+}
+
 void orc_dequant_row(const uint8_t *row, int64_t K, double *out) {
     for (int64_t b = 0; b < K / ORC_QK; ++b) {
         const uint8_t *blk = row + b * ORC_QBYTES;
@@ -130,7 +196,37 @@ void orc_dequant_row(const uint8_t *row, int64_t K, double *out) {
 
 static int64_t row_bytes(int64_t K) { return K / ORC_QK * ORC_QBYTES; }
 
+static int64_t fmt_row_bytes(int32_t fmt, int64_t K) {
+    return fmt == ORC_FMT_Q4_K ? K / 256 * 144 : fmt == ORC_FMT_Q6_K ? K / 256 * 210 : row_bytes(K);
+}
+
+static void dequant_fmt(int32_t fmt, const uint8_t *row, int64_t K, double *out) {
+    if (fmt == ORC_FMT_Q4_K) orc_dequant_q4_k_row(row, K, out);
+    else if (fmt == ORC_FMT_Q6_K) orc_dequant_q6_k_row(row, K, out);
+    else orc_dequant_row(row, K, out);
+}
+
 /* Y[t][n] = sum_k W[n][k] * X[t][k] for T input rows; W is Q8_0 [N][K]. */
+/* Y[t] = W X[t] for a matrix in block format fmt. */
+void orc_matmul_fmt(const uint8_t *W, int32_t fmt, int64_t N, int64_t K, const double *X, int64_t T,
+                    double *Y) {
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * K);
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            dequant_fmt(fmt, W + n * fmt_row_bytes(fmt, K), K, w);
+            for (int64_t t = 0; t < T; ++t) {
+                const double *x = X + t * K;
+                double acc = 0.0;
+                for (int64_t k = 0; k < K; ++k) acc += w[k] * x[k];
+                Y[t * N + n] = acc;
+            }
+        }
+        free(w);
+    }
+}
+
 void orc_matmul_q8(const uint8_t *W, int64_t N, int64_t K, const double *X, int64_t T,
                    double *Y) {
 #pragma omp parallel
@@ -236,8 +332,24 @@ static int cfg_ok(const orc_config *c) {
  * attn_q, attn_k, attn_v, attn_output, ffn_norm, ffn_gate, ffn_up, ffn_down;
  * output_norm; output (only when not tied). The model borrows them.
  */
+orc_model *orc_create_fmt(const orc_config *c, const void *const *tensors, const int32_t *wo_fmt,
+                          const int32_t *wd_fmt);
+
 orc_model *orc_create(const orc_config *c, const void *const *tensors) {
+    return orc_create_fmt(c, tensors, NULL, NULL);
+}
+
+/* As orc_create, with per-layer block formats of attn_output and ffn_down
+ * (ORC_FMT_*; NULL = Q8_0 everywhere). */
+orc_model *orc_create_fmt(const orc_config *c, const void *const *tensors, const int32_t *wo_fmt,
+                          const int32_t *wd_fmt) {
     if (!c || !tensors || !cfg_ok(c)) return NULL;
+    for (int l = 0; l < c->n_layer; ++l) {  /* 256-weight blocks need whole blocks per row */
+        const int32_t fo = wo_fmt ? wo_fmt[l] : ORC_FMT_Q8_0, fd = wd_fmt ? wd_fmt[l] : ORC_FMT_Q8_0;
+        if (fo < 0 || fo > 2 || fd < 0 || fd > 2) return NULL;
+        if (fo != ORC_FMT_Q8_0 && ((int64_t)c->n_head * c->head_dim) % 256) return NULL;
+        if (fd != ORC_FMT_Q8_0 && c->n_ff % 256) return NULL;
+    }
     orc_model *m = (orc_model *)calloc(1, sizeof(orc_model));
     m->c = *c;
     int64_t i = 0;
@@ -254,6 +366,8 @@ orc_model *orc_create(const orc_config *c, const void *const *tensors) {
         L->wg = (const uint8_t *)tensors[i++];
         L->wu = (const uint8_t *)tensors[i++];
         L->wd = (const uint8_t *)tensors[i++];
+        L->fo = wo_fmt ? wo_fmt[l] : ORC_FMT_Q8_0;
+        L->fd = wd_fmt ? wd_fmt[l] : ORC_FMT_Q8_0;
     }
     m->out_norm = (const float *)tensors[i++];
     m->out = c->tied_output ? m->tok_embd : (const uint8_t *)tensors[i++];
@@ -356,7 +470,7 @@ int orc_forward(orc_model *m, const uint32_t *tokens, int32_t T, int32_t index_p
                 orc_attend(q + i * QD + h * hd, kslot(m, m->kc, l, (int)gh, 0),
                            kslot(m, m->vc, l, (int)gh, 0), kv_len, hd, last, att + i * QD + h * hd);
             }
-        orc_matmul_q8(L->wo, H, QD, att, T, y);
+        orc_matmul_fmt(L->wo, L->fo, H, QD, att, T, y);
         m->n_matmul += 1;
         for (int64_t e = 0; e < T * H; ++e) x[e] += y[e];
 
@@ -366,7 +480,7 @@ int orc_forward(orc_model *m, const uint32_t *tokens, int32_t T, int32_t index_p
         orc_matmul_q8(L->wg, F, H, u, T, g);
         orc_matmul_q8(L->wu, F, H, u, T, up);
         for (int64_t e = 0; e < T * F; ++e) g[e] = orc_silu(g[e]) * up[e];
-        orc_matmul_q8(L->wd, H, F, g, T, y);
+        orc_matmul_fmt(L->wd, L->fd, H, F, g, T, y);
         m->n_matmul += 3;
         for (int64_t e = 0; e < T * H; ++e) x[e] += y[e];
     }

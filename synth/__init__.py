@@ -167,10 +167,10 @@ def pack_q8_0(scales: np.ndarray, q: np.ndarray) -> np.ndarray:
 @dataclasses.dataclass
 class Tensor:
     name: str
-    dtype: str          # 'q8_0' or 'f32'
+    dtype: str          # 'q8_0', 'q4_k', 'q6_k' or 'f32'
     rows: int
     cols: int
-    data: np.ndarray    # q8_0: uint8 [rows, cols/32*34]; f32: float32 [cols]
+    data: np.ndarray    # block formats: uint8 [rows, row bytes]; f32: float32 [cols]
 
     @property
     def nbytes(self) -> int:
@@ -226,6 +226,54 @@ def random_model(shape: ModelShape, seed: int = 0, keep_parts: bool = False) -> 
     return Model(shape, tensors)
 
 
+# ---- 256-weight "K" block formats (public GGUF block definitions) ----------
+# Q4_K, 144 bytes: f16 d, f16 dmin, 12 bytes of packed 6-bit scales and mins,
+# 128 bytes of 4-bit values. Q6_K, 210 bytes: 128 bytes of low 4 bits, 64 of
+# high 2 bits, 16 int8 scales, f16 d. Only their byte layout is drawn here.
+K_BLOCK_BYTES = {"q4_k": 144, "q6_k": 210}
+
+
+def draw_k_quant(rng: np.random.Generator, rows: int, cols: int, fmt: str,
+                 scale_std: float = 0.02) -> np.ndarray:
+    """Random Q4_K / Q6_K bytes [rows, cols/256 * block]: uniform random
+    value, scale and min bytes; f16 super-block scales |z| * scale_std / (63*15)
+    (Q4_K d), / (63*4) (Q4_K dmin), / (127*32) (Q6_K d), so weights stay near
+    the Q8_0 draw's magnitude."""
+    if cols % 256:
+        raise ValueError(f"{fmt} rows must hold whole 256-weight blocks, got cols={cols}")
+    nb = cols // 256
+    size = K_BLOCK_BYTES[fmt]
+    body = rng.integers(0, 256, size=(rows, nb, size), dtype=np.uint8)
+    f16 = lambda div: (np.abs(rng.standard_normal((rows, nb))) * (scale_std / div)).astype("<f2").view(np.uint8)
+    if fmt == "q4_k":
+        body[:, :, 0:2] = f16(63 * 15).reshape(rows, nb, 2)
+        body[:, :, 2:4] = f16(63 * 4).reshape(rows, nb, 2)
+    elif fmt == "q6_k":
+        body[:, :, 208:210] = f16(127 * 32).reshape(rows, nb, 2)
+    else:
+        raise ValueError(fmt)
+    return body.reshape(rows, nb * size)
+
+
+def with_k_quants(model: Model, o_fmts, d_fmts, seed: int = 7) -> Model:
+    """A copy of ``model`` whose per-layer attn_output / ffn_down matrices are
+    redrawn in the given formats ('q8_0' keeps the original tensor)."""
+    rng = np.random.default_rng(seed)
+    L = model.shape.n_layer
+    want = {}
+    for l in range(L):
+        want[f"blk.{l}.attn_output.weight"] = o_fmts[l]
+        want[f"blk.{l}.ffn_down.weight"] = d_fmts[l]
+    ts = []
+    for t in model.tensors:
+        f = want.get(t.name, "q8_0")
+        if t.dtype == "q8_0" and f != "q8_0":
+            ts.append(Tensor(t.name, f, t.rows, t.cols, draw_k_quant(rng, t.rows, t.cols, f)))
+        else:
+            ts.append(t)
+    return Model(model.shape, ts)
+
+
 def prompt_ids(n_vocab: int, length: int, seed: int = 1) -> np.ndarray:
     """Uniform-random prompt token ids in [0, V) as uint32."""
     return np.random.default_rng(seed).integers(0, n_vocab, size=length).astype(np.uint32)
@@ -248,5 +296,5 @@ def shape_fields(shape: ModelShape) -> Dict[str, object]:
 
 __all__ = ["QK8_0", "Q8_0_BLOCK_BYTES", "LAYER_TENSORS", "ModelShape", "TINY", "SMOL135M",
            "BIG_GQA", "Workload", "WORKLOADS", "micro_shape", "draw_q8_0", "pack_q8_0",
-           "Tensor", "Model", "random_model", "prompt_ids", "workload_inputs", "shape_fields"]
+           "Tensor", "Model", "random_model", "K_BLOCK_BYTES", "draw_k_quant", "with_k_quants", "prompt_ids", "workload_inputs", "shape_fields"]
 

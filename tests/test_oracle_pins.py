@@ -513,3 +513,158 @@ def test_q4_0_and_q5_0_values_are_q8_0_values():
     q8 = synth.pack_q8_0(d, ints.astype(np.int8))
     nz = np.repeat(d != 0, 32, axis=1)
     assert np.array_equal(oracle.dequant_q8_0(q8, rows, cols)[nz], w5[nz])
+
+
+# ---- 256-weight "K" formats. The pages fix only their block sizes (the
+# Q4_K_M table above); the bit layouts follow the public GGUF block
+# definitions. Blocks are built here by packing chosen integers (the inverse
+# of decoding, written separately), and the K formats are tied to the Q8_0
+# decoding (pinned by the pages' printed values) where their values coincide.
+
+def _f16_bytes(v: float) -> list:
+    b = int(np.float16(v).view(np.uint16))
+    return [b & 0xFF, b >> 8]
+
+
+def _pack_q4_k(d: float, dmin: float, s, m, q) -> np.ndarray:
+    """One Q4_K block from 8 scales, 8 mins (0..63) and 256 values (0..15):
+    scale/min j < 4 in the low 6 bits of bytes j / j + 4; j >= 4 split into
+    low nibbles in byte j + 4 (scale low, min high) and top two bits in the
+    top of bytes j - 4 (scale) and j (min). Values of sub-blocks 2c and 2c+1
+    share bytes 32c..32c+31 (low / high nibble)."""
+    sc = [0] * 12
+    for j in range(4):
+        sc[j] = (s[j] & 63) | ((s[j + 4] >> 4) << 6)
+        sc[j + 4] = (m[j] & 63) | ((m[j + 4] >> 4) << 6)
+        sc[j + 8] = (s[j + 4] & 15) | ((m[j + 4] & 15) << 4)
+    qs = [0] * 128
+    for c in range(4):
+        for l in range(32):
+            qs[32 * c + l] = q[64 * c + l] | (q[64 * c + 32 + l] << 4)
+    return np.array(_f16_bytes(d) + _f16_bytes(dmin) + sc + qs, dtype=np.uint8)
+
+
+def _pack_q6_k(d: float, sc, q) -> np.ndarray:
+    """One Q6_K block from 16 int8 scales and 256 values (0..63, stored +32):
+    in half h, value 32k + l keeps its low 4 bits in byte 64h + l + 32(k odd)
+    (low nibble for k < 2, high for k >= 2) and its top 2 bits at bit 2k of
+    byte 128 + 32h + l."""
+    ql = [0] * 128
+    qh = [0] * 64
+    for h in range(2):
+        for k in range(4):
+            for l in range(32):
+                v = q[128 * h + 32 * k + l]
+                i = 64 * h + l + 32 * (k & 1)
+                ql[i] |= (v & 15) << (4 * (k >= 2))
+                qh[32 * h + l] |= (v >> 4) << (2 * k)
+    scb = [int(np.int8(x).view(np.uint8)) for x in sc]
+    return np.array(ql + qh + scb + _f16_bytes(d), dtype=np.uint8)
+
+
+def test_q4_k_hand_block():
+    s = [1, 2, 3, 4, 17, 33, 49, 63]          # >= 16 uses the split top bits
+    m = [0, 1, 2, 63, 20, 40, 60, 5]
+    q = [(7 * i + 3) % 16 for i in range(256)]
+    d, dmin = 0.25, 0.125
+    blk = _pack_q4_k(d, dmin, s, m, q)
+    assert blk.size == 144
+    w = oracle.dequant_q4_k(blk, 1, 256)[0]
+    want = np.array([d * s[i // 32] * q[i] - dmin * m[i // 32] for i in range(256)])
+    assert np.array_equal(w, want)
+
+
+def test_q6_k_hand_block():
+    sc = [1, -2, 3, -4, 5, 127, -128, 8, 9, -10, 11, 12, -13, 14, 15, 100]
+    q = [(11 * i + 5) % 64 for i in range(256)]
+    d = 0.5
+    blk = _pack_q6_k(d, sc, q)
+    assert blk.size == 210
+    w = oracle.dequant_q6_k(blk, 1, 256)[0]
+    want = np.array([d * sc[i // 16] * (q[i] - 32) for i in range(256)])
+    assert np.array_equal(w, want)
+
+
+def test_k_formats_equal_q8_0_where_values_coincide():
+    """Q4_K with dmin = 0 holds (d * s_j) * q per 32 weights, Q6_K with equal
+    scales in each 32 holds (d * sc) * (q - 32): Q8_0 blocks with those f16
+    scales and int8 values hold the same numbers (d = 2^-10, so d * s is an
+    exact f16)."""
+    rng = np.random.default_rng(31)
+    rows, cols = 3, 512
+    nb = cols // 256
+    q4 = [[], [], []]
+    q8_scales = np.zeros((rows, cols // 32), np.float16)
+    q8_vals = np.zeros((rows, cols), np.int8)
+    q6 = [[], [], []]
+    q8b_scales = np.zeros((rows, cols // 32), np.float16)
+    q8b_vals = np.zeros((rows, cols), np.int8)
+    d = 2.0 ** -10
+    for r in range(rows):
+        for b in range(nb):
+            s = rng.integers(0, 64, 8)
+            q = rng.integers(0, 16, 256)
+            q4[r].append(_pack_q4_k(d, 0.0, s.tolist(), [int(x) for x in rng.integers(0, 64, 8)], q.tolist()))
+            q8_scales[r, 8 * b:8 * b + 8] = (d * s).astype(np.float16)
+            q8_vals[r, 256 * b:256 * b + 256] = q
+            s6 = np.repeat(rng.integers(-128, 128, 8), 2)
+            v6 = rng.integers(0, 64, 256)
+            q6[r].append(_pack_q6_k(d, s6.tolist(), v6.tolist()))
+            q8b_scales[r, 8 * b:8 * b + 8] = (d * s6[::2]).astype(np.float16)
+            q8b_vals[r, 256 * b:256 * b + 256] = v6 - 32
+    raw4 = np.stack([np.concatenate(x) for x in q4])
+    raw6 = np.stack([np.concatenate(x) for x in q6])
+    ref4 = oracle.dequant_q8_0(synth.pack_q8_0(q8_scales, q8_vals), rows, cols)
+    ref6 = oracle.dequant_q8_0(synth.pack_q8_0(q8b_scales, q8b_vals), rows, cols)
+    assert np.array_equal(oracle.dequant_q4_k(raw4, rows, cols), ref4)
+    assert np.array_equal(oracle.dequant_q6_k(raw6, rows, cols), ref6)
+    # and the matrix products through the per-format entry
+    x = rng.standard_normal((2, cols))
+    assert np.array_equal(oracle.matmul_fmt(raw4, "q4_k", rows, cols, x),
+                          oracle.matmul_fmt(synth.pack_q8_0(q8_scales, q8_vals), "q8_0", rows, cols, x))
+    np.testing.assert_allclose(oracle.matmul_fmt(raw6, "q6_k", rows, cols, x), (ref6 @ x.T).T,
+                               rtol=1e-13, atol=1e-15)
+
+
+def test_k_quant_model_matches_its_q8_0_twin():
+    """A model whose o and down projections are K-quant matrices with
+    Q8_0-representable values gives bitwise the logits of the same model with
+    those matrices stored as Q8_0 (the per-layer format plumbing)."""
+    shape = synth.micro_shape(n_layer=2, n_embd=64, n_head=4, n_head_kv=2, head_dim=64, n_ff=256)
+    base = synth.random_model(shape, 3)
+    rng = np.random.default_rng(5)
+    d = 2.0 ** -12
+    k_ts, q8_ts = {}, {}
+    for l in range(shape.n_layer):
+        for name, rows, cols, fmt in ((f"blk.{l}.attn_output.weight", shape.n_embd, shape.q_dim, "q6_k"),
+                                      (f"blk.{l}.ffn_down.weight", shape.n_embd, shape.n_ff, "q4_k")):
+            blocks, scales, vals = [], np.zeros((rows, cols // 32), np.float16), np.zeros((rows, cols), np.int8)
+            for r in range(rows):
+                row = []
+                for b in range(cols // 256):
+                    if fmt == "q4_k":
+                        s, q = rng.integers(0, 64, 8), rng.integers(0, 16, 256)
+                        row.append(_pack_q4_k(d, 0.0, s.tolist(), [0] * 8, q.tolist()))
+                        scales[r, 8 * b:8 * b + 8], vals[r, 256 * b:256 * b + 256] = d * s, q
+                    else:
+                        s, v = np.repeat(rng.integers(-128, 128, 8), 2), rng.integers(0, 64, 256)
+                        row.append(_pack_q6_k(d, s.tolist(), v.tolist()))
+                        scales[r, 8 * b:8 * b + 8], vals[r, 256 * b:256 * b + 256] = d * s[::2], v - 32
+                blocks.append(np.concatenate(row))
+            k_ts[name] = synth.Tensor(name, fmt, rows, cols, np.stack(blocks))
+            q8_ts[name] = synth.Tensor(name, "q8_0", rows, cols, synth.pack_q8_0(scales, vals))
+    mk = synth.Model(shape, [k_ts.get(t.name, t) for t in base.tensors])
+    mq = synth.Model(shape, [q8_ts.get(t.name, t) for t in base.tensors])
+    toks = synth.prompt_ids(shape.n_vocab, 7, seed=2)
+    a = oracle.OracleModel(mk).forward(toks, 0)[2]
+    b = oracle.OracleModel(mq).forward(toks, 0)[2]
+    assert np.array_equal(a, b)
+
+
+def test_k_quant_oracle_rejects_rows_without_whole_blocks():
+    shape = synth.micro_shape(n_ff=128)          # 128 is not a multiple of 256
+    m = synth.random_model(shape, 0)
+    ts = [synth.Tensor(t.name, "q4_k", t.rows, t.cols, np.zeros((t.rows, 72), np.uint8))
+          if t.name == "blk.0.ffn_down.weight" else t for t in m.tensors]
+    with pytest.raises(ValueError):
+        oracle.OracleModel(synth.Model(shape, ts))
