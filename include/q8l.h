@@ -60,7 +60,15 @@ typedef enum {
     Q8L_E_IO = 11             /* GGUF: the file cannot be opened or read */
 } q8l_status;
 
-typedef enum { Q8L_F32 = 0, Q8L_Q8_0 = 1 } q8l_dtype;
+/* Q4_K and Q6_K: the 256-weight block formats of the 4-bit "K" file mix
+ * ("速度", section "CPU GGUF": 144 and 210 bytes per 256 weights by its
+ * Q4_K_M tensor table; bit layouts as in the public GGUF block definitions).
+ * Q4_K block: f16 d, f16 dmin, 12 bytes packing eight 6-bit scales s_j and
+ * mins m_j, 128 bytes of 4-bit values q; weight = d*s_j*q - dmin*m_j per
+ * 32-weight sub-block j. Q6_K block: 128 bytes of low 4 bits, 64 bytes of
+ * high 2 bits, 16 int8 scales (one per 16 weights), f16 d;
+ * weight = d*scale*(q - 32). */
+typedef enum { Q8L_F32 = 0, Q8L_Q8_0 = 1, Q8L_Q4_K = 2, Q8L_Q6_K = 3 } q8l_dtype;
 
 /*
  * Model hyper-parameters: the llama.* metadata keys the page "生成一个 token"
@@ -116,9 +124,13 @@ q8l_status q8l_create(const q8l_config *cfg, q8l_model **out);
  *   blk.{i}.ffn_down.weight        Q8_0 [n_embd, n_ff]
  *   output_norm.weight             F32  [1, n_embd]
  *   output.weight                  Q8_0 [n_vocab, n_embd]  (untied models only)
- * `dev_ptr` holds the raw bytes (Q8_0 blocks exactly as in the file; F32
- * little-endian), 16-byte aligned, borrowed. Q8L_E_SHAPE when rows, cols or
- * nbytes (rows*cols/32*34 for Q8_0, rows*cols*4 for F32) do not match;
+ * attn_output and ffn_down may instead be Q4_K or Q6_K when their cols are a
+ * multiple of 256 (as files of the 4-bit mix store the down projection);
+ * each layer's format is taken from its binding.
+ * `dev_ptr` holds the raw bytes (blocks exactly as in the file, rows back to
+ * back; F32 little-endian), 16-byte aligned, borrowed. Q8L_E_SHAPE when the
+ * dtype, rows, cols or nbytes (rows*cols/32*34 for Q8_0, rows*cols/256*144
+ * for Q4_K, rows*cols/256*210 for Q6_K, rows*cols*4 for F32) do not match;
  * Q8L_E_INVALID_ARG for an unknown name, NULL or misaligned pointer;
  * Q8L_E_NOT_FINALIZED after finalize (weights are fixed once finalized).
  * Binding a name twice replaces the earlier pointer.
@@ -208,6 +220,21 @@ void q8l_destroy(q8l_model *m);
 q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *X, int64_t T,
                               const float *norm_w, double eps, int32_t accumulate, float *Y,
                               void *stream);
+
+/*
+ * The same product for a Q4_K or Q6_K matrix (dtype Q8L_Q4_K / Q8L_Q6_K; the
+ * pages time it on the down projection's shape, [203, 1536] x [1536, 576] and
+ * [1, 1536] x [1536, 576], "速度", section "CPU GGUF"):
+ *   Y[t][n] (+)= sum_k W[n][k] * X[t][k].
+ * W: N rows of K/256 blocks back to back (16-byte aligned), X f32 [T][K]
+ * (16-byte aligned), Y f32 [T][N]; accumulate 1 adds to Y. K must be a
+ * multiple of 256. T = 1 runs the matrix-vector kernel, T > 1 the MFMA
+ * matrix-matrix kernel. Q8L_E_INVALID_ARG for a NULL or misaligned pointer,
+ * another dtype, sizes out of range, or a matrix or activation block of 2 GiB
+ * or more.
+ */
+q8l_status q8l_op_matmul_kq(const void *W, int32_t dtype, int64_t N, int64_t K, const float *X, int64_t T,
+                            int32_t accumulate, float *Y, void *stream);
 
 /*
  * Attention of T queries over kv_len cached keys with grouped heads:
@@ -308,13 +335,15 @@ int64_t q8l_gguf_find_tensor(const q8l_gguf *g, const char *name);
  * NULL. Q4_0 and Q5_0 tensors (32-weight blocks of an f16 scale times 4- or
  * 5-bit integers; sizes pinned by "速度", section "CPU GGUF") are read as Q8_0:
  * dtype Q8L_Q8_0, size rows*cols/32*34, each block converted exactly (same
- * scale, int8 = the block's integer). Other block formats (the K-quants) are
- * listed but not read. */
+ * scale, int8 = the block's integer). Q4_K and Q6_K tensors are read as they
+ * are (dtype Q8L_Q4_K / Q8L_Q6_K). Other block formats are listed but not
+ * read (dtype -1). */
 q8l_status q8l_gguf_tensor_info(const q8l_gguf *g, int64_t index, const char **name, int32_t *dtype,
                                 int64_t *rows, int64_t *cols, uint64_t *offset, uint64_t *nbytes);
 /* Read tensor `index`'s bytes into host memory; nbytes must equal its size as read. */
 q8l_status q8l_gguf_read_tensor(q8l_gguf *g, int64_t index, void *host_dst, size_t nbytes);
-/* The tensor's type id in the file (the GGUF numbering: 0 F32, 2 Q4_0, 6 Q5_0, 8 Q8_0, ...), or -1. */
+/* The tensor's type id in the file (the GGUF numbering: 0 F32, 2 Q4_0, 6 Q5_0, 8 Q8_0, 12 Q4_K,
+ * 14 Q6_K, ...), or -1. */
 int32_t q8l_gguf_tensor_file_type(const q8l_gguf *g, int64_t index);
 
 #ifdef __cplusplus

@@ -137,6 +137,22 @@ __device__ __forceinline__ void wave_argmax(float &v, uint32_t &i) {
     }
 }
 
+// Scale s and min m (6 bits each) of Q4_K sub-block j (0..7) from the block's
+// 12 packed bytes (dwords s03 = bytes 0..3, s47 = 4..7, s811 = 8..11): for
+// j < 4 the low 6 bits of bytes j and j + 4; for j >= 4 the low / high nibble
+// of byte j + 4 with the top two bits of byte j - 4 / j above it.
+__device__ __forceinline__ void q4k_scale_min(int j, uint32_t s03, uint32_t s47, uint32_t s811, uint32_t &sc,
+                                              uint32_t &mn) {
+    const int sh = 8 * (j & 3);
+    if (j < 4) {
+        sc = (s03 >> sh) & 63u;
+        mn = (s47 >> sh) & 63u;
+    } else {
+        sc = ((s811 >> sh) & 15u) | (((s03 >> (sh + 6)) & 3u) << 4);
+        mn = ((s811 >> (sh + 4)) & 15u) | (((s47 >> (sh + 6)) & 3u) << 4);
+    }
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // v as an f16 pair: hi = f16(v) at hi[i], lo = f16(v - hi) at hi[plane + i]

@@ -41,11 +41,14 @@ enum GgufType : uint32_t {
 // Tensor element types of the file format this library can bind. Q4_0 and
 // Q5_0 blocks hold d * (an integer in [-8, 7] or [-16, 15]) per 32 weights:
 // the same values as a Q8_0 block with the same d, so they are read as Q8_0
-// (converted exactly while reading).
+// (converted exactly while reading). Q4_K and Q6_K (256-weight blocks of 144
+// and 210 bytes) are read as they are.
 constexpr uint32_t kTypeF32 = 0;
 constexpr uint32_t kTypeQ4_0 = 2;
 constexpr uint32_t kTypeQ5_0 = 6;
 constexpr uint32_t kTypeQ8_0 = 8;
+constexpr uint32_t kTypeQ4_K = 12;
+constexpr uint32_t kTypeQ6_K = 14;
 
 struct Value {
     uint32_t type = 0;
@@ -70,6 +73,7 @@ struct TensorInfo {
 };
 
 bool q8_family(uint32_t t) { return t == kTypeQ4_0 || t == kTypeQ5_0 || t == kTypeQ8_0; }
+bool k_family(uint32_t t) { return t == kTypeQ4_K || t == kTypeQ6_K; }
 
 uint64_t block_bytes(uint32_t t) { return t == kTypeQ4_0 ? 18 : t == kTypeQ5_0 ? 22 : 34; }
 
@@ -271,6 +275,9 @@ q8l_status parse(q8l_gguf *g) {
             if (t.dims[0] % 32) return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " rows are not whole blocks");
             t.file_bytes = n / 32 * block_bytes(t.type);
             t.nbytes = n / 32 * 34;
+        } else if (k_family(t.type)) {
+            if (t.dims[0] % 256) return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " rows are not whole blocks");
+            t.file_bytes = t.nbytes = n / 256 * (t.type == kTypeQ4_K ? 144 : 210);
         } else {
             t.file_bytes = t.nbytes = 0;  // other types: listed, not readable (size unknown here)
         }
@@ -430,11 +437,13 @@ q8l_status q8l_gguf_tensor_info(const q8l_gguf *g, int64_t index, const char **n
     if (dtype) {
         if (t.type == kTypeF32) *dtype = Q8L_F32;
         else if (q8_family(t.type)) *dtype = Q8L_Q8_0;
+        else if (t.type == kTypeQ4_K) *dtype = Q8L_Q4_K;
+        else if (t.type == kTypeQ6_K) *dtype = Q8L_Q6_K;
         else {
             *dtype = -1;
             return fail(const_cast<q8l_gguf *>(g), Q8L_E_FORMAT,
                         "tensor " + t.name + " has type " + std::to_string(t.type) +
-                            " (F32, Q8_0, Q4_0 and Q5_0 are read)");
+                            " (F32, Q8_0, Q4_0, Q5_0, Q4_K and Q6_K are read)");
         }
     }
     return Q8L_OK;
@@ -448,12 +457,12 @@ int32_t q8l_gguf_tensor_file_type(const q8l_gguf *g, int64_t index) {
 q8l_status q8l_gguf_read_tensor(q8l_gguf *g, int64_t index, void *host_dst, size_t nbytes) {
     if (!g || !host_dst || index < 0 || index >= int64_t(g->tensors.size())) return Q8L_E_INVALID_ARG;
     const TensorInfo &t = g->tensors[size_t(index)];
-    if (t.type != kTypeF32 && !q8_family(t.type))
+    if (t.type != kTypeF32 && !q8_family(t.type) && !k_family(t.type))
         return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " has an unsupported type");
     if (nbytes != t.nbytes) return fail(g, Q8L_E_SHAPE, "tensor " + t.name + ": buffer size differs");
     const uint64_t off = g->data_offset + t.offset;
     if (fseeko(g->f, off_t(off), SEEK_SET) != 0) return fail(g, Q8L_E_IO, "seek failed for " + t.name);
-    if (t.type == kTypeF32 || t.type == kTypeQ8_0) {
+    if (t.type == kTypeF32 || t.type == kTypeQ8_0 || k_family(t.type)) {
         if (std::fread(host_dst, 1, nbytes, g->f) != nbytes) return fail(g, Q8L_E_IO, "short read for " + t.name);
         return Q8L_OK;
     }

@@ -121,27 +121,35 @@ struct GSrc {
     uint32_t boff[Cfg<TM, TN>::BU];
 };
 
-template <bool A32, int TM, int TN, int EPI>
-__device__ inline void g_setup(const GemmArgs &a, int m0, int row0, const int nvalid[2],
-                               const uint8_t *const Wb[2], GSrc<TM, TN> &g) {
+// A-side (activation) sources: shared by the Q8_0 and the K-format kernels.
+template <bool A32, int TM, int TN>
+__device__ inline void a_setup(const GemmArgs &a, int m0, __amdgpu_buffer_rsrc_t &ra, uint32_t *aoff) {
     using C = Cfg<TM, TN>;
     const int tid = threadIdx.x;
     const uint32_t abytes = uint32_t(size_t(a.T) * a.K * 4);  // f32, or two f16 planes
-    g.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.A), 0, int(abytes), kRsrcWord3);
+    ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.A), 0, int(abytes), kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < C::AP; ++i) {
         const int c = tid + i * kThreads;
         if (A32) {
             const int m = c >> 4;
-            g.aoff[i] = m0 + m < a.T ? uint32_t((size_t(m0 + m) * a.K + (c & 15) * 4) * 4) : kOutOfRange;
+            aoff[i] = m0 + m < a.T ? uint32_t((size_t(m0 + m) * a.K + (c & 15) * 4) * 4) : kOutOfRange;
         } else {
             const int plane = c / (TM * 8), rr = c - plane * (TM * 8);
             const int m = rr >> 3;
-            g.aoff[i] = m0 + m < a.T
-                            ? uint32_t((size_t(plane) * a.T * a.K + size_t(m0 + m) * a.K + (rr & 7) * 8) * 2)
-                            : kOutOfRange;
+            aoff[i] = m0 + m < a.T
+                          ? uint32_t((size_t(plane) * a.T * a.K + size_t(m0 + m) * a.K + (rr & 7) * 8) * 2)
+                          : kOutOfRange;
         }
     }
+}
+
+template <bool A32, int TM, int TN, int EPI>
+__device__ inline void g_setup(const GemmArgs &a, int m0, int row0, const int nvalid[2],
+                               const uint8_t *const Wb[2], GSrc<TM, TN> &g) {
+    using C = Cfg<TM, TN>;
+    const int tid = threadIdx.x;
+    a_setup<A32, TM, TN>(a, m0, g.ra, g.aoff);
 #pragma unroll
     for (int i = 0; i < C::BU; ++i) {
         const int u = tid + i * kThreads;
@@ -159,12 +167,18 @@ __device__ inline void g_setup(const GemmArgs &a, int m0, int row0, const int nv
 }
 
 template <bool A32, int TM, int TN>
-__device__ inline void g_load(const GSrc<TM, TN> &g, int ks, GRegs<TM, TN> &r) {
+__device__ inline void a_load(__amdgpu_buffer_rsrc_t ra, const uint32_t *aoff, int ks, u32x4 *ra_out) {
     using C = Cfg<TM, TN>;
     const int sa = ks * GK * (A32 ? 4 : 2);
-    const int sb = ks * kPairBytes;
 #pragma unroll
-    for (int i = 0; i < C::AP; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(g.ra, g.aoff[i], sa, 0);
+    for (int i = 0; i < C::AP; ++i) ra_out[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i], sa, 0);
+}
+
+template <bool A32, int TM, int TN>
+__device__ inline void g_load(const GSrc<TM, TN> &g, int ks, GRegs<TM, TN> &r) {
+    using C = Cfg<TM, TN>;
+    a_load<A32, TM, TN>(g.ra, g.aoff, ks, r.a);
+    const int sb = ks * kPairBytes;
 #pragma unroll
     for (int i = 0; i < C::BU; ++i) {
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(g.rb[i], g.boff[i], sb, 0);
@@ -189,7 +203,7 @@ __device__ inline void q4_to_half(uint32_t w, half2v &lo, half2v &hi) {
 }
 
 template <bool A32, int TM, int TN>
-__device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf) {
+__device__ inline void a_store(const u32x4 *ra, _Float16 *ahi, _Float16 *alo) {
     using C = Cfg<TM, TN>;
     const int tid = threadIdx.x;
 #pragma unroll
@@ -197,7 +211,7 @@ __device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf) {
         const int c = tid + i * kThreads;
         if (A32) {
             const int m = c >> 4, c4 = c & 15;
-            const float4 v = __builtin_bit_cast(float4, r.a[i]);
+            const float4 v = __builtin_bit_cast(float4, ra[i]);
             const float vv[4] = {v.x, v.y, v.z, v.w};
             _Float16 hi[4], lo[4];
 #pragma unroll
@@ -205,14 +219,21 @@ __device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf) {
                 hi[k] = static_cast<_Float16>(vv[k]);
                 lo[k] = static_cast<_Float16>(vv[k] - static_cast<float>(hi[k]));
             }
-            *reinterpret_cast<uint2 *>(bf.ahi + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, hi);
-            *reinterpret_cast<uint2 *>(bf.alo + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, lo);
+            *reinterpret_cast<uint2 *>(ahi + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, hi);
+            *reinterpret_cast<uint2 *>(alo + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, lo);
         } else {
             const int plane = c / (TM * 8), rr = c - plane * (TM * 8);
             const int m = rr >> 3, p = rr & 7;
-            *reinterpret_cast<u32x4 *>((plane ? bf.alo : bf.ahi) + m * LPAD + p * 8) = r.a[i];
+            *reinterpret_cast<u32x4 *>((plane ? alo : ahi) + m * LPAD + p * 8) = ra[i];
         }
     }
+}
+
+template <bool A32, int TM, int TN>
+__device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf) {
+    using C = Cfg<TM, TN>;
+    const int tid = threadIdx.x;
+    a_store<A32, TM, TN>(r.a, bf.ahi, bf.alo);
 #pragma unroll
     for (int i = 0; i < C::BU; ++i) {
         const int u = tid + i * kThreads;
@@ -391,6 +412,283 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
             }
 }
 
+// ---- 256-weight block formats (Q4_K, Q6_K), 64 weights per K step.
+//
+// Q4_K, step ks of a row: block ks/4, chunk c = ks%4 = sub-block 2c (low
+// nibbles of bytes 32c..32c+31) and sub-block 2c+1 (their high nibbles). A
+// sub-block holds (d*s)*q - dmin*m with q in 0..15: the MFMAs take q as f16
+// (exact), the product d*s is applied in f32 per sub-block as the Q8_0 scale
+// is, and the min term needs each token's activation sum over the sub-block,
+// which one more MFMA pair against a B of ones gives (shared by all rows).
+// Q6_K, step ks: block ks/4, half h = (ks%4)/2, k-pair kk = ks%2: values
+// 32k + l of half h for k = 2kk, 2kk+1, each 16 with its own int8 scale. The
+// MFMA's 32 k-rows span two scales (B lanes 0..31 hold k-rows 0..15, lanes
+// 32..63 rows 16..31), so each step's B is used twice with the other half's
+// lanes zeroed. Q6_K blocks are 210 bytes and start 2-byte aligned: pieces are
+// loaded from the dword-aligned floor and re-aligned with alignbyte.
+
+template <int FMT, int TN>
+struct KB {
+    static constexpr int TPR = FMT == F_Q4_K ? 2 : 4;    // threads per row and step
+    static constexpr int BU = (TN * TPR + kThreads - 1) / kThreads;
+    static constexpr int NW = FMT == F_Q4_K ? 8 : 12;     // dwords a thread loads per row and step
+};
+
+template <int TM, int TN>
+struct KCfg {
+    using C = Cfg<TM, TN>;
+    static constexpr size_t BUF = sizeof(_Float16) * (2 * C::A_HALVES + C::B_HALVES) + sizeof(float) * TN * 4;
+    static constexpr size_t LDS = 2 * BUF;
+    static_assert(BUF % 16 == 0, "LDS buffer alignment");
+};
+
+template <int FMT, int TM, int TN>
+struct KSrc {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t aoff[Cfg<TM, TN>::AP];
+    uint32_t rowoff[KB<FMT, TN>::BU];   // byte offset of the thread's row in W, or kOutOfRange
+};
+
+template <int FMT, int TM, int TN>
+struct KRegs {
+    u32x4 a[Cfg<TM, TN>::AP];
+    uint32_t b[KB<FMT, TN>::BU][KB<FMT, TN>::NW];
+};
+
+// Byte offsets of a Q6_K thread piece (row offset ro, step ks, 16-column group
+// qd). d is read with a 16-bit load: the dword holding it may reach past the
+// end of the matrix (a dword-aligned last block), where the range check would
+// return zero.
+struct Q6Piece {
+    uint32_t ql, qh, sc, d;
+};
+__device__ inline Q6Piece q6_piece(uint32_t ro, int ks, int qd) {
+    const uint32_t blk = ro + uint32_t(ks >> 2) * kQ6KBytes;
+    const int h = (ks >> 1) & 1, kk = ks & 1;
+    Q6Piece p;
+    p.ql = blk + 64 * h + 16 * qd;
+    p.qh = blk + 128 + 32 * h + 16 * (qd & 1);
+    p.sc = blk + 192 + 8 * h + 4 * kk + qd;
+    p.d = blk + 208;
+    return p;
+}
+
+template <int FMT, int TM, int TN>
+__device__ inline void kb_load(const KSrc<FMT, TM, TN> &g, int ks, KRegs<FMT, TM, TN> &r) {
+    using B = KB<FMT, TN>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < B::BU; ++i) {
+        const int part = (tid + i * kThreads) % B::TPR;
+        const uint32_t ro = g.rowoff[i];
+        uint32_t *w = r.b[i];
+        if (FMT == F_Q4_K) {
+            const uint32_t blk = ro + uint32_t(ks >> 2) * kQ4KBytes;
+            const u32x4 hd = __builtin_amdgcn_raw_buffer_load_b128(g.rb, blk, 0, 0);
+            const u32x4 qs = __builtin_amdgcn_raw_buffer_load_b128(g.rb, blk + 16 + 32 * (ks & 3) + 16 * part, 0, 0);
+            w[0] = hd.x; w[1] = hd.y; w[2] = hd.z; w[3] = hd.w;
+            w[4] = qs.x; w[5] = qs.y; w[6] = qs.z; w[7] = qs.w;
+        } else {
+            const Q6Piece p = q6_piece(ro, ks, part);
+            const u32x4 l = __builtin_amdgcn_raw_buffer_load_b128(g.rb, p.ql & ~3u, 0, 0);
+            const u32x4 h = __builtin_amdgcn_raw_buffer_load_b128(g.rb, p.qh & ~3u, 0, 0);
+            w[0] = l.x; w[1] = l.y; w[2] = l.z; w[3] = l.w;
+            w[4] = __builtin_amdgcn_raw_buffer_load_b32(g.rb, (p.ql & ~3u) + 16, 0, 0);
+            w[5] = h.x; w[6] = h.y; w[7] = h.z; w[8] = h.w;
+            w[9] = __builtin_amdgcn_raw_buffer_load_b32(g.rb, (p.qh & ~3u) + 16, 0, 0);
+            w[10] = __builtin_amdgcn_raw_buffer_load_b32(g.rb, p.sc & ~3u, 0, 0);
+            w[11] = __builtin_amdgcn_raw_buffer_load_b16(g.rb, p.d, 0, 0);   // 2-byte aligned; see q6_piece
+        }
+    }
+}
+
+// Four bytes (each 0..255) -> four f16 values 1024 + byte (two half2).
+__device__ inline void bytes_to_half_biased(uint32_t w, half2v &lo, half2v &hi) {
+    lo = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w, 0x05010400u));
+    hi = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w, 0x07030602u));
+}
+
+// 16 small unsigned values (4 dwords of bytes) minus `bias` + 1024, as f16, to LDS.
+__device__ inline void store16(const uint32_t *v, float bias, _Float16 *dst) {
+    const half2v b = {static_cast<_Float16>(1024.0f + bias), static_cast<_Float16>(1024.0f + bias)};
+    half2v o[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        bytes_to_half_biased(v[k], o[2 * k], o[2 * k + 1]);
+        o[2 * k] = o[2 * k] - b;
+        o[2 * k + 1] = o[2 * k + 1] - b;
+    }
+    *reinterpret_cast<u32x4 *>(dst) = u32x4{__builtin_bit_cast(uint32_t, o[0]), __builtin_bit_cast(uint32_t, o[1]),
+                                            __builtin_bit_cast(uint32_t, o[2]), __builtin_bit_cast(uint32_t, o[3])};
+    *reinterpret_cast<u32x4 *>(dst + 8) = u32x4{__builtin_bit_cast(uint32_t, o[4]), __builtin_bit_cast(uint32_t, o[5]),
+                                                __builtin_bit_cast(uint32_t, o[6]), __builtin_bit_cast(uint32_t, o[7])};
+}
+
+template <int FMT, int TM, int TN>
+__device__ inline void kb_store(const KSrc<FMT, TM, TN> &g, int ks, const KRegs<FMT, TM, TN> &r, _Float16 *bq,
+                                float *bd) {
+    using B = KB<FMT, TN>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < B::BU; ++i) {
+        const int u = tid + i * kThreads;
+        if (B::BU * kThreads > TN * B::TPR && u >= TN * B::TPR) break;
+        const int b = u / B::TPR, part = u % B::TPR;
+        const uint32_t *w = r.b[i];
+        if (FMT == F_Q4_K) {
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lo[e] = w[4 + e] & 0x0f0f0f0fu;
+                hi[e] = (w[4 + e] >> 4) & 0x0f0f0f0fu;
+            }
+            store16(lo, 0.f, bq + b * LPAD + 16 * part);
+            store16(hi, 0.f, bq + b * LPAD + 32 + 16 * part);
+            if (part == 0) {
+                const int c = ks & 3;
+                const float d = half_bits_to_float(w[0]), dmin = half_bits_to_float(w[0] >> 16);
+                uint32_t s0, m0, s1, m1;
+                q4k_scale_min(2 * c, w[1], w[2], w[3], s0, m0);
+                q4k_scale_min(2 * c + 1, w[1], w[2], w[3], s1, m1);
+                *reinterpret_cast<float4 *>(bd + b * 4) =
+                    make_float4(d * float(s0), d * float(s1), dmin * float(m0), dmin * float(m1));
+            }
+        } else {
+            const Q6Piece p = q6_piece(g.rowoff[i], ks, part);
+            const uint32_t sh = p.ql & 3u;   // the block's misalignment (0 or 2), same for every piece
+            const int kk = ks & 1;
+            const uint32_t hshift = 2u * (2 * kk + (part >> 1));
+            uint32_t q6[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t l = __builtin_amdgcn_alignbyte(w[e + 1], w[e], sh);
+                const uint32_t h = __builtin_amdgcn_alignbyte(w[e + 6], w[e + 5], sh);
+                const uint32_t nib = (kk ? (l >> 4) : l) & 0x0f0f0f0fu;
+                q6[e] = nib | (((h >> hshift) & 0x03030303u) << 4);
+            }
+            store16(q6, 32.f, bq + b * LPAD + 16 * part);
+            const int scv = static_cast<int8_t>((w[10] >> (8 * (p.sc & 3u))) & 0xffu);
+            const float d = half_bits_to_float(w[11]);
+            bd[b * 4 + part] = d * float(scv);
+        }
+    }
+}
+
+template <int FMT, int EPI, int TM, int TN, bool A32>
+__global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
+    using C = Cfg<TM, TN>;
+    using KC = KCfg<TM, TN>;
+    using B = KB<FMT, TN>;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int m0 = blockIdx.x * TM;
+    const int row0 = blockIdx.y * TN;
+    const int nvalid = min(TN, a.Nm[0] - row0);
+
+    KSrc<FMT, TM, TN> src;
+    a_setup<A32, TM, TN>(a, m0, src.ra, src.aoff);
+    src.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.W[0]), 0,
+                                               int(uint32_t(a.Nm[0]) * uint32_t(a.rowbytes)), kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < B::BU; ++i) {
+        const int u = tid + i * kThreads;
+        const int b = u / B::TPR;
+        src.rowoff[i] = (u < TN * B::TPR && b < nvalid) ? uint32_t(row0 + b) * uint32_t(a.rowbytes) : kOutOfRange;
+    }
+
+    f32x4 acc[C::MS][C::NS];
+#pragma unroll
+    for (int i = 0; i < C::MS; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = a.K / GK;
+    KRegs<FMT, TM, TN> regs;
+    a_load<A32, TM, TN>(src.ra, src.aoff, 0, regs.a);
+    kb_load<FMT, TM, TN>(src, 0, regs);
+    const _Float16 one = static_cast<_Float16>(1.0f);
+    const half8 ones = {one, one, one, one, one, one, one, one};
+    const half8 zeros = {};
+    for (int ks = 0; ks < nsteps; ++ks) {
+        uint8_t *p = smem + size_t(ks & 1) * KC::BUF;
+        _Float16 *ahi = reinterpret_cast<_Float16 *>(p), *alo = ahi + C::A_HALVES, *bq = alo + C::A_HALVES;
+        float *bd = reinterpret_cast<float *>(bq + C::B_HALVES);
+        a_store<A32, TM, TN>(regs.a, ahi, alo);
+        kb_store<FMT, TM, TN>(src, ks, regs, bq, bd);
+        __syncthreads();
+        if (ks + 1 < nsteps) {
+            a_load<A32, TM, TN>(src.ra, src.aoff, ks + 1, regs.a);
+            kb_load<FMT, TM, TN>(src, ks + 1, regs);
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            half8 bfr[C::NS], bfr1[C::NS];
+            float s0[C::NS], s1[C::NS];
+#pragma unroll
+            for (int ns = 0; ns < C::NS; ++ns) {
+                const int col = wn * C::WN + ns * 16 + (lane & 15);
+                const half8 v = *reinterpret_cast<const half8 *>(bq + col * LPAD + hb * 32 + 8 * (lane >> 4));
+                if (FMT == F_Q4_K) {
+                    bfr[ns] = v;
+                    s0[ns] = bd[col * 4 + hb];          // d * s
+                    s1[ns] = -bd[col * 4 + 2 + hb];     // -dmin * m
+                } else {
+                    bfr[ns] = lane < 32 ? v : zeros;    // k-rows 0..15: scale 2hb
+                    bfr1[ns] = lane < 32 ? zeros : v;   // k-rows 16..31: scale 2hb + 1
+                    s0[ns] = bd[col * 4 + 2 * hb];
+                    s1[ns] = bd[col * 4 + 2 * hb + 1];
+                }
+            }
+#pragma unroll
+            for (int ms = 0; ms < C::MS; ++ms) {
+                const int row = wm * C::WM + ms * 16 + (lane & 15);
+                const half8 ah = *reinterpret_cast<const half8 *>(ahi + row * LPAD + hb * 32 + 8 * (lane >> 4));
+                const half8 al = *reinterpret_cast<const half8 *>(alo + row * LPAD + hb * 32 + 8 * (lane >> 4));
+                if (FMT == F_Q4_K) {
+                    f32x4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ones, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, ones, sx, 0, 0, 0);
+#pragma unroll
+                    for (int ns = 0; ns < C::NS; ++ns) {
+                        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bfr[ns], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bfr[ns], t, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[ms][ns][i] = fmaf(s0[ns], t[i], acc[ms][ns][i]);
+                            acc[ms][ns][i] = fmaf(s1[ns], sx[i], acc[ms][ns][i]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int ns = 0; ns < C::NS; ++ns) {
+                        f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bfr[ns], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        t0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bfr[ns], t0, 0, 0, 0);
+                        f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bfr1[ns], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bfr1[ns], t1, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[ms][ns][i] = fmaf(s0[ns], t0[i], acc[ms][ns][i]);
+                            acc[ms][ns][i] = fmaf(s1[ns], t1[i], acc[ms][ns][i]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < C::NS; ++ns)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = wm * C::WM + ms * 16 + 4 * (lane >> 4) + i;
+                const int c = wn * C::WN + ns * 16 + (lane & 15);
+                if (m0 + m >= a.T || c >= nvalid) continue;
+                float *dst = a.Y + size_t(m0 + m) * a.Nm[0] + row0 + c;
+                *dst = (EPI == G_ACCUM) ? *dst + acc[ms][ns][i] : acc[ms][ns][i];
+            }
+}
+
 // u = x / sqrt(mean(x^2) + eps) * w for each token row, written as the f16
 // hi plane [T][K] followed by the lo plane. One workgroup per row.
 __global__ __launch_bounds__(kThreads) void k_rms_split(const float *x, int T, int K, const float *w,
@@ -456,6 +754,34 @@ hipError_t launch_plain(const GemmArgs &a, int N, hipStream_t s) {
     return launch_cfg<EPI, 32, 64, A32>(a, row_tiles(N, 64), s);
 }
 
+template <int FMT, int EPI, int TM, int TN, bool A32>
+hipError_t launch_kq_cfg(const GemmArgs &a, hipStream_t s) {
+    using KC = KCfg<TM, TN>;
+    if (size_t(a.T) * a.K * 4 >= kOutOfRange || size_t(a.Nm[0]) * a.rowbytes + 64 >= kOutOfRange)
+        return hipErrorInvalidValue;
+    if (KC::LDS > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_kq<FMT, EPI, TM, TN, A32>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(KC::LDS));
+        if (e != hipSuccess) return e;
+    }
+    dim3 grid((a.T + TM - 1) / TM, row_tiles(a.Nm[0], TN));
+    hipLaunchKernelGGL((k_gemm_kq<FMT, EPI, TM, TN, A32>), grid, dim3(kThreads), KC::LDS, s, a);
+    return hipGetLastError();
+}
+
+template <int FMT, int EPI, bool A32>
+hipError_t launch_kq_plain(const GemmArgs &a, hipStream_t s) {
+    if (large_tiles(a.T, row_tiles(a.Nm[0], 128))) return launch_kq_cfg<FMT, EPI, 64, 128, A32>(a, s);
+    return launch_kq_cfg<FMT, EPI, 32, 64, A32>(a, s);
+}
+
+template <int FMT>
+hipError_t launch_kq_fmt(const GemmArgs &a, bool a_split, int accumulate, hipStream_t s) {
+    if (a_split)
+        return accumulate ? launch_kq_plain<FMT, G_ACCUM, false>(a, s) : launch_kq_plain<FMT, G_STORE, false>(a, s);
+    return accumulate ? launch_kq_plain<FMT, G_ACCUM, true>(a, s) : launch_kq_plain<FMT, G_STORE, true>(a, s);
+}
+
 GemmArgs gemm_base(const void *A, int T, int K) {
     GemmArgs a{};
     a.A = A; a.T = T; a.K = K;
@@ -478,6 +804,17 @@ hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, boo
     if (a_split)
         return accumulate ? launch_plain<G_ACCUM, false>(a, N, s) : launch_plain<G_STORE, false>(a, N, s);
     return accumulate ? launch_plain<G_ACCUM, true>(a, N, s) : launch_plain<G_STORE, true>(a, N, s);
+}
+
+hipError_t launch_gemm_kq(int fmt, const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
+                          int accumulate, float *Y, hipStream_t s) {
+    if (K % kQKK || (fmt != F_Q4_K && fmt != F_Q6_K)) return hipErrorInvalidValue;
+    GemmArgs a{};
+    a.A = A; a.T = T; a.K = K;
+    a.rowbytes = int(fmt_row_bytes(fmt, K));
+    a.W[0] = W; a.Nm[0] = N; a.Y = Y;
+    return fmt == F_Q4_K ? launch_kq_fmt<F_Q4_K>(a, a_split, accumulate, s)
+                         : launch_kq_fmt<F_Q6_K>(a, a_split, accumulate, s);
 }
 
 hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u, const StepState *st,

@@ -54,9 +54,21 @@ struct GemvShape {
 
 // ---- launchers (k_*.hip) -------------------------------------------------
 
+// Block formats a matrix may be stored in. Q4_K and Q6_K (256-weight blocks)
+// are accepted for the plain-matmul roles (o and down projections).
+enum WFmt { F_Q8_0 = 0, F_Q4_K = 1, F_Q6_K = 2 };
+constexpr int kQKK = 256;            // weights per Q4_K / Q6_K block
+constexpr int kQ4KBytes = 144;       // f16 d, f16 dmin, 12 scale/min bytes, 128 nibble bytes
+constexpr int kQ6KBytes = 210;       // 128 low-nibble bytes, 64 high-bit bytes, 16 int8 scales, f16 d
+
+__host__ __device__ inline int64_t fmt_row_bytes(int fmt, int64_t K) {
+    return fmt == F_Q4_K ? K / kQKK * kQ4KBytes : fmt == F_Q6_K ? K / kQKK * kQ6KBytes : K / kQK * kQBytes;
+}
+
 struct LayerPtrs {
     const uint8_t *wq, *wk, *wv, *wo, *wg, *wu, *wd;
     const float *attn_norm, *ffn_norm;
+    int fo, fd;  // WFmt of wo and wd
 };
 
 struct Dims {
@@ -135,6 +147,14 @@ hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u,
                            const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s);
 hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const _Float16 *u, _Float16 *h, int T,
                               hipStream_t s);
+
+// Q4_K / Q6_K matrices (N rows of K weights, K % 256 == 0). One token: the
+// VALU GEMV; several: the MFMA GEMM (activations f32, or split planes).
+// Y[t] (+)= W X[t].
+hipError_t launch_kq_gemv(int fmt, const uint8_t *W, int N, int K, const float *X, int accumulate, float *Y,
+                          hipStream_t s);
+hipError_t launch_gemm_kq(int fmt, const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
+                          int accumulate, float *Y, hipStream_t s);
 
 // Prefill attention: T queries, causal mask offset by the cached prefix.
 struct AttnPrefillArgs {

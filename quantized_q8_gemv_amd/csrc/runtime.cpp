@@ -113,6 +113,7 @@ struct q8l_model {
     const uint8_t *tok_embd = nullptr, *output = nullptr;
     const float *out_norm = nullptr;
     std::vector<std::vector<const void *>> layer_ptrs;  // [L][S_NSLOT]
+    std::vector<int> fmt_o, fmt_d;                      // [L] WFmt of attn_output / ffn_down
     uint8_t *ws = nullptr;
     size_t ws_bytes = 0;
     bool finalized = false;
@@ -139,6 +140,8 @@ struct q8l_model {
         w.wg = static_cast<const uint8_t *>(p[S_WG]);
         w.wu = static_cast<const uint8_t *>(p[S_WU]);
         w.wd = static_cast<const uint8_t *>(p[S_WD]);
+        w.fo = fmt_o[l];
+        w.fd = fmt_d[l];
         return w;
     }
     float *kc(int l) const { return at<float>(lay.kc) + size_t(l) * lay.kv_layer; }
@@ -192,7 +195,10 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = decode_splits;
             a.scale = 1.0f / sqrtf(float(d.hd));
             if ((e = launch_attn_decode(a, s)) != hipSuccess) return e;
-            if (decode_splits == 1) {  // one split: its normalisation is merged into the o-projection
+            if (w.fo != F_Q8_0) {      // 256-weight blocks: merge, then the K-format GEMV
+                e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s);
+                if (e == hipSuccess) e = launch_kq_gemv(w.fo, w.wo, d.H, QD, att, 1, x, s);
+            } else if (decode_splits == 1) {  // one split: its normalisation is merged into the o-projection
                 e = launch_oproj_combine(w.wo, d.H, QD, a.part, st, 1, d.hd, x, s);
             } else {                   // several: one merge kernel, then the plain o-projection
                 e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s);
@@ -206,7 +212,10 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.T = T; a.kv_len = kv_len_prefill; a.kv_stride = d.max_seq;
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.scale = 1.0f / sqrtf(float(d.hd));
             if ((e = launch_attn_prefill(a, s)) != hipSuccess) return e;
-            if (gemm)
+            if (w.fo != F_Q8_0)
+                e = gemm ? launch_gemm_kq(w.fo, w.wo, d.H, QD, att_s, true, T, 1, x, s)
+                         : launch_gemm_kq(w.fo, w.wo, d.H, QD, att, false, T, 1, x, s);
+            else if (gemm)
                 e = launch_gemm_matmul(w.wo, d.H, QD, att_s, true, T, 1, x, s);
             else
                 e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s);
@@ -215,11 +224,18 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
         if (gemm) {
             if ((e = launch_rms_split(x, T, d.H, w.ffn_norm, d.eps, u, s)) != hipSuccess) return e;
             if ((e = launch_gemm_gateup(d, w, u, h_s, T, s)) != hipSuccess) return e;
-            if ((e = launch_gemm_matmul(w.wd, d.H, d.F, h_s, true, T, 1, x, s)) != hipSuccess) return e;
+            e = w.fd != F_Q8_0 ? launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s)
+                               : launch_gemm_matmul(w.wd, d.H, d.F, h_s, true, T, 1, x, s);
         } else {
             if ((e = launch_gateup(d, w, x, h, T, s)) != hipSuccess) return e;
-            if ((e = launch_matmul(w.wd, d.H, d.F, h, T, nullptr, d.eps, 1, x, s)) != hipSuccess) return e;
+            if (w.fd == F_Q8_0)
+                e = launch_matmul(w.wd, d.H, d.F, h, T, nullptr, d.eps, 1, x, s);
+            else if (T == 1)
+                e = launch_kq_gemv(w.fd, w.wd, d.H, d.F, h, 1, x, s);
+            else
+                e = launch_gemm_kq(w.fd, w.wd, d.H, d.F, h, false, T, 1, x, s);
         }
+        if (e != hipSuccess) return e;
     }
     const uint8_t *wout = m->cfg.tied_output ? m->tok_embd : m->output;
     if ((e = launch_lmhead(d, wout, m->out_norm, x + size_t(T - 1) * d.H, st,
@@ -265,6 +281,10 @@ q8l_status decode_graph(q8l_model *m, int bucket, hipGraphExec_t *out) {
     m->graph_defs[bucket] = g;
     *out = ex;
     return Q8L_OK;
+}
+
+const char *dtype_name(int t) {
+    return t == Q8L_F32 ? "F32" : t == Q8L_Q8_0 ? "Q8_0" : t == Q8L_Q4_K ? "Q4_K" : t == Q8L_Q6_K ? "Q6_K" : "unknown";
 }
 
 bool parse_layer_name(const char *name, int *layer, int *slot) {
@@ -352,6 +372,8 @@ q8l_status q8l_create(const q8l_config *cfg, q8l_model **out) {
     m->d.rope_neox = cfg->rope_type == Q8L_ROPE_NEOX ? 1 : 0;
     m->lay = make_layout(cfg);
     m->layer_ptrs.assign(cfg->n_layer, std::vector<const void *>(S_NSLOT, nullptr));
+    m->fmt_o.assign(cfg->n_layer, F_Q8_0);
+    m->fmt_d.assign(cfg->n_layer, F_Q8_0);
     *out = m;
     return Q8L_OK;
 }
@@ -390,15 +412,25 @@ q8l_status q8l_bind_tensor(q8l_model *m, const char *name, q8l_dtype dtype, int6
     } else {
         return fail(m, Q8L_E_INVALID_ARG, std::string("unknown tensor name ") + name);
     }
-    const size_t want = et == Q8L_Q8_0 ? size_t(er * ec / kQK * kQBytes) : size_t(er * ec * 4);
+    // attn_output and ffn_down may also be Q4_K / Q6_K (rows of whole 256-weight blocks)
+    const bool kquant_ok = layer >= 0 && (s == S_WO || s == S_WD) && ec % kQKK == 0;
+    if (kquant_ok && (dtype == Q8L_Q4_K || dtype == Q8L_Q6_K)) et = dtype;
+    const size_t want = et == Q8L_F32 ? size_t(er * ec * 4)
+                                      : size_t(er * fmt_row_bytes(et == Q8L_Q4_K ? F_Q4_K : et == Q8L_Q6_K ? F_Q6_K
+                                                                                                            : F_Q8_0,
+                                                                  ec));
     if (dtype != et || rows != er || cols != ec || nbytes != want) {
-        char buf[256];
+        char buf[320];
         std::snprintf(buf, sizeof buf, "%s: expected %s [%lld, %lld] (%zu bytes), got %s [%lld, %lld] (%zu bytes)",
-                      name, et == Q8L_Q8_0 ? "Q8_0" : "F32", (long long)er, (long long)ec, want,
-                      dtype == Q8L_Q8_0 ? "Q8_0" : "F32", (long long)rows, (long long)cols, nbytes);
+                      name, kquant_ok && et == Q8L_Q8_0 ? "Q8_0, Q4_K or Q6_K" : dtype_name(et), (long long)er,
+                      (long long)ec, want, dtype_name(dtype), (long long)rows, (long long)cols, nbytes);
         return fail(m, Q8L_E_SHAPE, buf);
     }
     *slot = dev_ptr;
+    if (layer >= 0 && (s == S_WO || s == S_WD)) {
+        const int f = et == Q8L_Q4_K ? F_Q4_K : et == Q8L_Q6_K ? F_Q6_K : F_Q8_0;
+        (s == S_WO ? m->fmt_o : m->fmt_d)[layer] = f;
+    }
     return Q8L_OK;
 }
 
@@ -528,10 +560,13 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
             case 1: return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
             case 2: return launch_attn_decode(a, s);
             case 3:
+                if (w.fo != F_Q8_0) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
                 if (a.n_splits == 1) return launch_oproj_combine(w.wo, d.H, QD, a.part, S, 1, d.hd, x, s);
                 return launch_matmul(w.wo, d.H, QD, m->at<float>(m->lay.att), 1, nullptr, d.eps, 1, x, s);
             case 4: return launch_gateup(d, w, x, h, 1, s);
-            case 5: return launch_matmul(w.wd, d.H, d.F, h, 1, nullptr, d.eps, 1, x, s);
+            case 5:
+                if (w.fd != F_Q8_0) return launch_kq_gemv(w.fd, w.wd, d.H, d.F, h, 1, x, s);
+                return launch_matmul(w.wd, d.H, d.F, h, 1, nullptr, d.eps, 1, x, s);
             case 6: return launch_lmhead(d, wout, m->out_norm, x, S, m->at<float>(m->lay.lm_part), s);
             case 7: return launch_argmax_finish(d, m->at<float>(m->lay.lm_part), S, s);
             default: return launch_noop(s);
@@ -596,6 +631,21 @@ q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *
     else
         e = launch_matmul(static_cast<const uint8_t *>(W), int(N), int(K), X, int(T), norm_w, float(eps),
                           accumulate, Y, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8L_OK : Q8L_E_HIP;
+}
+
+q8l_status q8l_op_matmul_kq(const void *W, int32_t dtype, int64_t N, int64_t K, const float *X, int64_t T,
+                            int32_t accumulate, float *Y, void *stream) {
+    if (!W || !X || !Y || (dtype != Q8L_Q4_K && dtype != Q8L_Q6_K) || N < 1 || K < kQKK || K % kQKK || T < 1 ||
+        N > (1 << 30) || K > (1 << 24) || T > (1 << 20) || (reinterpret_cast<uintptr_t>(W) & 15) ||
+        (reinterpret_cast<uintptr_t>(X) & 15))
+        return Q8L_E_INVALID_ARG;
+    const int fmt = dtype == Q8L_Q4_K ? F_Q4_K : F_Q6_K;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = T == 1 ? launch_kq_gemv(fmt, static_cast<const uint8_t *>(W), int(N), int(K), X, accumulate, Y, s)
+                                : launch_gemm_kq(fmt, static_cast<const uint8_t *>(W), int(N), int(K), X, false, int(T),
+                                                 accumulate, Y, s);
+    if (e == hipErrorInvalidValue) return Q8L_E_INVALID_ARG;   // beyond the kernels' 2 GiB addressing
     return e == hipSuccess ? Q8L_OK : Q8L_E_HIP;
 }
 

@@ -16,8 +16,8 @@ class Q8Model:
     """A model bound to the library.
 
     ``config`` is a dict of q8l_config fields; ``tensors`` yields objects with
-    ``name``, ``dtype`` ('q8_0' or 'f32'), ``rows``, ``cols`` and ``data``
-    (a host numpy array of the raw bytes / f32 values).
+    ``name``, ``dtype`` ('q8_0', 'q4_k', 'q6_k' or 'f32'), ``rows``, ``cols``
+    and ``data`` (a host numpy array of the raw bytes / f32 values).
     """
 
     def __init__(self, config: dict, tensors: Iterable, device: str = "cuda:0", stream=None):
@@ -37,7 +37,7 @@ class Q8Model:
             arr = np.ascontiguousarray(t.data)
             dev = torch.from_numpy(arr.view(np.uint8).reshape(-1)).to(self.device)
             self.buffers[t.name] = dev
-            dt = C.Q8L_Q8_0 if t.dtype == "q8_0" else C.Q8L_F32
+            dt = _DTYPES[t.dtype]
             self._check(C.q8l_bind_tensor(self.handle, t.name, dt, t.rows, t.cols, dev, dev.numel()))
         self._check(C.q8l_bind_workspace(self.handle, self.workspace, nbytes))
         self._check(C.q8l_finalize(self.handle, stream))
@@ -105,6 +105,10 @@ class Q8Model:
             pass
 
 
+_DTYPES = {"f32": C.Q8L_F32, "q8_0": C.Q8L_Q8_0, "q4_k": C.Q8L_Q4_K, "q6_k": C.Q8L_Q6_K}
+_DTYPE_NAMES = {v: k for k, v in _DTYPES.items()}
+
+
 class _FileTensor:
     __slots__ = ("name", "dtype", "rows", "cols", "data")
 
@@ -125,5 +129,5 @@ def _gguf_tensors(g: int, names):
             raise C.Q8LError(st, C.q8l_gguf_last_error(g))
         t = _FileTensor()
         t.name, t.rows, t.cols, t.data = name, info["rows"], info["cols"], buf
-        t.dtype = "q8_0" if info["dtype"] == C.Q8L_Q8_0 else "f32"
+        t.dtype = _DTYPE_NAMES[info["dtype"]]
         yield t

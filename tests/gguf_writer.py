@@ -101,8 +101,9 @@ def model_tensors(model) -> List[TensorEntry]:
     out = []
     for t in model.tensors:
         data = np.ascontiguousarray(t.data).tobytes()
-        if t.dtype == "q8_0":
-            out.append((t.name, TYPE_Q8_0, [t.cols, t.rows], data))
+        if t.dtype in ("q8_0", "q4_k", "q6_k"):
+            ty = {"q8_0": TYPE_Q8_0, "q4_k": TYPE_Q4_K, "q6_k": TYPE_Q6_K}[t.dtype]
+            out.append((t.name, ty, [t.cols, t.rows], data))
         else:
             out.append((t.name, TYPE_F32, [t.cols] if t.rows == 1 else [t.cols, t.rows], data))
     return out
@@ -113,6 +114,7 @@ def model_tensors(model) -> List[TensorEntry]:
 # nibble; value d * (nibble - 8). Q5_0: f16 d, u32 fifth bits (bit i for weight
 # i), 16 bytes of nibbles as in Q4_0; value d * ((nibble | bit << 4) - 16).
 TYPE_Q4_0, TYPE_Q5_0 = 2, 6
+TYPE_Q4_K, TYPE_Q6_K = 12, 14
 
 
 def random_blocks(rng: np.random.Generator, rows: int, cols: int, fmt: str) -> np.ndarray:

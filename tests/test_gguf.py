@@ -260,3 +260,35 @@ def test_q4_0_and_q5_0_tensors_read_as_exact_q8_0(lib, tmp_path, fmt, ftype):
     # ... and decode to the oracle's values of the original format exactly
     ref = oracle.dequant_q5_0(raw, rows, cols) if fmt == "q5_0" else oracle.dequant_q4_0(raw, rows, cols)
     assert np.array_equal(oracle.dequant_q8_0(buf, rows, cols), ref)
+
+
+@pytest.mark.parametrize("fmt,ftype,size", [("q4_k", W.TYPE_Q4_K, 144), ("q6_k", W.TYPE_Q6_K, 210)])
+def test_k_format_tensors_read_as_they_are(lib, tmp_path, fmt, ftype, size):
+    rng = np.random.default_rng(12)
+    rows, cols = 24, 1536                                 # an odd row count of 210-byte blocks too
+    raw = synth.draw_k_quant(rng, rows, cols, fmt)
+    other = synth.draw_k_quant(rng, 3, 512, fmt)
+    path = str(tmp_path / f"{fmt}.gguf")
+    W.write(path, W.llama_kv(synth.TINY), [("blk.0.ffn_down.weight", ftype, [cols, rows], raw.tobytes()),
+                                           ("blk.1.ffn_down.weight", ftype, [512, 3], other.tobytes())])
+    g = C.q8l_gguf_open(path)
+    try:
+        for idx, (arr, r, c) in enumerate(((raw, rows, cols), (other, 3, 512))):
+            assert C.q8l_gguf_tensor_file_type(g, idx) == ftype
+            st, info = C.q8l_gguf_tensor_info(g, idx)
+            want = C.Q8L_Q4_K if fmt == "q4_k" else C.Q8L_Q6_K
+            assert st == C.Q8L_OK and info["dtype"] == want
+            assert (info["rows"], info["cols"], info["nbytes"]) == (r, c, r * c // 256 * size)
+            buf = np.empty(info["nbytes"], np.uint8)
+            assert C.q8l_gguf_read_tensor(g, idx, buf, buf.size) == C.Q8L_OK
+            assert np.array_equal(buf, arr.reshape(-1))
+    finally:
+        C.q8l_gguf_close(g)
+
+
+def test_k_format_rows_must_hold_whole_blocks(lib, tmp_path):
+    path = str(tmp_path / "ragged.gguf")
+    W.write(path, W.llama_kv(synth.TINY), [("blk.0.ffn_down.weight", W.TYPE_Q4_K, [576, 2], bytes(576 * 2 // 256 * 144))])
+    with pytest.raises(C.Q8LError) as e:
+        C.q8l_gguf_open(path)
+    assert e.value.status == C.Q8L_E_FORMAT

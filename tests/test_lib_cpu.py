@@ -69,6 +69,36 @@ def test_bind_checks(tiny_handle):
     assert C.q8l_bind_tensor(h, "blk.3.ffn_norm.weight", C.Q8L_F32, 1, 576, FAKE, 576 * 4) == C.Q8L_OK
 
 
+def test_bind_accepts_k_formats_only_for_o_and_down(tiny_handle):
+    """Q4_K / Q6_K bind for ffn_down (1536 = 6 blocks of 256 per row) with the
+    block sizes 144 / 210; not for other roles, nor for attn_output at the
+    135M shape (576 is not a multiple of 256)."""
+    h = tiny_handle
+    q4, q6 = 576 * 6 * 144, 576 * 6 * 210
+    assert C.q8l_bind_tensor(h, "blk.1.ffn_down.weight", C.Q8L_Q4_K, 576, 1536, FAKE, q4) == C.Q8L_OK
+    assert C.q8l_bind_tensor(h, "blk.2.ffn_down.weight", C.Q8L_Q6_K, 576, 1536, FAKE, q6) == C.Q8L_OK
+    assert C.q8l_bind_tensor(h, "blk.2.ffn_down.weight", C.Q8L_Q6_K, 576, 1536, FAKE, q4) == C.Q8L_E_SHAPE
+    assert C.q8l_bind_tensor(h, "blk.2.ffn_down.weight", C.Q8L_Q4_K, 576, 1536, FAKE, q6) == C.Q8L_E_SHAPE
+    assert "497664 bytes" in C.q8l_last_error(h)
+    assert C.q8l_bind_tensor(h, "blk.2.ffn_down.weight", C.Q8L_F32, 576, 1536, FAKE, q6) == C.Q8L_E_SHAPE
+    assert "Q8_0, Q4_K or Q6_K" in C.q8l_last_error(h)
+    assert C.q8l_bind_tensor(h, "blk.0.ffn_gate.weight", C.Q8L_Q4_K, 1536, 576, FAKE, 1536 * 576 // 256 * 144) \
+        == C.Q8L_E_SHAPE
+    assert C.q8l_bind_tensor(h, "blk.0.attn_output.weight", C.Q8L_Q4_K, 576, 576, FAKE, 576 * 576 // 256 * 144) \
+        == C.Q8L_E_SHAPE
+    assert C.q8l_bind_tensor(h, "blk.0.attn_norm.weight", C.Q8L_Q6_K, 1, 576, FAKE, 576 * 4) == C.Q8L_E_SHAPE
+
+
+def test_k_format_op_rejects_bad_arguments_before_device_work():
+    X, Y = FAKE, FAKE
+    ok = dict(W=FAKE, dtype=C.Q8L_Q4_K, N=576, K=1536, X=X, T=1, accumulate=0, Y=Y)
+    for bad in (dict(dtype=C.Q8L_Q8_0), dict(dtype=7), dict(K=1535), dict(K=128), dict(N=0), dict(T=0),
+                dict(W=FAKE + 4), dict(X=FAKE + 8), dict(W=None), dict(Y=None)):
+        a = {**ok, **bad}
+        assert C.q8l_op_matmul_kq(a["W"], a["dtype"], a["N"], a["K"], a["X"], a["T"], a["accumulate"],
+                                  a["Y"], stream=0) == C.Q8L_E_INVALID_ARG, bad
+
+
 def test_finalize_names_the_first_missing_tensor(tiny_handle):
     h = tiny_handle
     s = synth.TINY
