@@ -35,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+FORMAT_BYTES = {"q8_0": (32, 34), "q4_k": (256, 144), "q6_k": (256, 210)}   # (weights, bytes) per block
 # The pages' Metal figure for this workload ("生成一个 token", section "Metal：热缓存"):
 # 20 decode steps after a 13-token prompt, 2.6 ms mean per step incl. the argmax
 # readback, on an Apple M2 Max -- another machine, quoted as context.
@@ -48,18 +49,22 @@ NKINDS = len(KIND_NAMES)
 TRAFFIC_FILES = {"C2": "profiles/decode_kernels_135m_13+20_pmc_traffic.md"}
 
 
-def kernel_symbols(s, kv_len):
+def kernel_symbols(s, kv_len, down_fmt="q8_0"):
     """Device symbol of each decode kernel kind at this shape (T = 1). With
     one attention split the o-projection merges the split itself (variant 1);
-    with several a separate merge kernel runs first (variant 0)."""
+    with several a separate merge kernel runs first (variant 0). A Q4_K / Q6_K
+    down projection runs k_kq_gemv<format, rows per wave>."""
     multi = (s.n_embd // 64) * 272 > 40 * 1024  # rows longer than one LDS chunk
     down_multi = (s.n_ff // 64) * 272 > 40 * 1024
     chunk = 64 if s.head_dim <= 64 else 32
     fused = 1 if kv_len <= chunk else 0
+    if down_fmt == "q8_0":
+        down = "k_matmul1_chunked" if down_multi else "k_matmul1<0, false>"
+    else:
+        down = f"k_kq_gemv<{1 if down_fmt == 'q4_k' else 2}, {2 if s.n_embd >= 4096 else 1}>"
     return ["k_embed", f"k_qkv1<{str(multi).lower()}>", "k_attn_decode",
             f"k_matmul1<{fused}, {str(multi).lower()}>", f"k_gateup1<{str(multi).lower()}>",
-            "k_matmul1_chunked" if down_multi else "k_matmul1<0, false>",
-            f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
+            down, f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
 
 
 def source_digest(path):
@@ -112,19 +117,27 @@ def q8_bytes(rows, cols):
     return rows * cols // 32 * 34
 
 
-def per_token_weight_bytes(s):
-    """Q8_0 projections + output layer + f32 norm weights + one embedding row."""
-    H, QD, KVD, F, V = s.n_embd, s.q_dim, s.kv_dim, s.n_ff, s.n_vocab
-    layer = (q8_bytes(QD, H) + 2 * q8_bytes(KVD, H) + q8_bytes(H, QD) + 2 * q8_bytes(F, H)
-             + q8_bytes(H, F) + 2 * H * 4)
-    return s.n_layer * layer + q8_bytes(V, H) + H * 4 + q8_bytes(1, H)
+def fmt_bytes(fmt, rows, cols):
+    per, size = FORMAT_BYTES[fmt]
+    return rows * cols // per * size
+
+
+def per_token_weight_bytes(model):
+    """Every tensor's bytes once (projections in their block formats, norms,
+    the output layer -- the embedding when tied) plus one embedding row."""
+    s = model.shape
+    embd = model["token_embd.weight"].nbytes
+    total = sum(t.nbytes for t in model.tensors)
+    if not s.tied_output:
+        total -= embd
+    return total + q8_bytes(1, s.n_embd)
 
 
 def kv_bytes_per_position(s):
     return s.n_layer * 2 * s.n_head_kv * s.head_dim * 4
 
 
-def kernel_bytes(s, kv_len):
+def kernel_bytes(s, kv_len, down_fmt="q8_0"):
     """Algorithmic bytes of one launch of each decode kernel kind (layer 0)."""
     H, QD, KVD, F, V = s.n_embd, s.q_dim, s.kv_dim, s.n_ff, s.n_vocab
     return [
@@ -133,7 +146,7 @@ def kernel_bytes(s, kv_len):
         kv_len * s.n_head_kv * s.head_dim * 4 * 2 + QD * 4,
         q8_bytes(H, QD) + QD * 4 + 2 * H * 4,
         2 * q8_bytes(F, H) + 2 * H * 4 + F * 4,
-        q8_bytes(H, F) + F * 4 + 2 * H * 4,
+        fmt_bytes(down_fmt, H, F) + F * 4 + 2 * H * 4,
         q8_bytes(V, H) + 2 * H * 4 + V * 4,
         0,
     ]
@@ -171,6 +184,91 @@ def cpu_baseline(model, prompt, steps, seconds):
                       f"decode tokens/s over {t_dec:.1f} s of decode"}
 
 
+# The pages' CPU timings of one QMatMul on the down projection's shape, by
+# block format ("速度", section "CPU GGUF"; minimum of 35 runs, Apple M2 Max,
+# ms) -- another machine, quoted as context.
+PAGES_MATMUL_MS = {("q8_0", 203): 0.8959, ("q4_k", 203): 0.6777, ("q6_k", 203): 1.1029, ("q8_0", 1): 0.0050}
+PEAK_MFMA_F16_TFLOPS = 2500.0
+
+
+def format_matmuls(reps):
+    """Time Y = X W^T per block format through the single-op entries: the
+    pages' down-projection shape [T, 1536] x [1536, 576] (T = 1 and 203) and a
+    7B-sized one [T, 11008] x [11008, 4096]. One JSON line per case. T = 1 is
+    HBM-bound (algorithmic bytes = the matrix + X + Y); T > 1 is compared with
+    the dense f16 MFMA peak on its 2*N*K*T flops (the kernels issue twice that
+    on the matrix cores: activations are an f16 pair hi + lo)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_q8_gemv_amd import q8l as C
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    rng = np.random.default_rng(0)
+    lines = []
+    for (N, K, Ts, name) in ((576, 1536, (1, 203), "down 135M"), (4096, 11008, (1, 203, 512), "down 7B")):
+        for fmt in ("q8_0", "q4_k", "q6_k"):
+            if fmt == "q8_0":
+                sc, q = synth.draw_q8_0(rng, N, K)
+                raw = synth.pack_q8_0(sc, q)
+            else:
+                raw = synth.draw_k_quant(rng, N, K, fmt)
+            Wd = torch.from_numpy(raw.reshape(-1)).to(dev)
+            for T in Ts:
+                X = torch.randn(T, K, device=dev)
+                Y = torch.empty(T, N, device=dev)
+
+                def call_on(st):
+                    if fmt == "q8_0":
+                        return C.q8l_op_matmul_q8_0(Wd, N, K, X, T, None, 0.0, 0, Y, st)
+                    dt = C.Q8L_Q4_K if fmt == "q4_k" else C.Q8L_Q6_K
+                    return C.q8l_op_matmul_kq(Wd, dt, N, K, X, T, 0, Y, st)
+
+                def call():
+                    return call_on(stream)
+
+                for _ in range(3):
+                    assert call() == C.Q8L_OK
+                torch.cuda.synchronize()
+                # the timed launches replay from a captured graph, so the events
+                # see GPU time rather than the host's call rate
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    cs = torch.cuda.current_stream()
+                    for _ in range(reps):
+                        assert call_on(cs) == C.Q8L_OK
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / reps * 1e3
+                del g
+                wbytes = raw.nbytes
+                nbytes = wbytes + T * K * 4 + T * N * 4
+                if T == 1:
+                    ach = nbytes / (us * 1e-6) / 1e9
+                    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(ach / PEAK_HBM_GBS, 4)}
+                else:
+                    ach = 2.0 * N * K * T / (us * 1e-6) / 1e12
+                    roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4)}
+                pages = PAGES_MATMUL_MS.get((fmt, T)) if N == 576 else None
+                line = {"metric": "single matmul time by block format", "format": fmt, "shape": name,
+                        "N": N, "K": K, "T": T, "us": round(us, 2), "weight_bytes": int(wbytes),
+                        "bytes_per_call": int(nbytes), "roofline": roof,
+                        "pages_cpu_ms": pages, "reps": reps}
+                print(json.dumps(line), flush=True)
+                lines.append(line)
+            del Wd
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,10 +278,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--down-format", default="q8_0", choices=["q8_0", "q4_k", "q6_k", "q4_k_m"],
+                    help="block format of the down projections (q4_k_m: Q4_K and Q6_K in alternate "
+                         "layers, as the pages' 4-bit file holds them)")
+    ap.add_argument("--formats", action="store_true",
+                    help="time the single matmul per block format (Q8_0, Q4_K, Q6_K) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         eprint(f"bench.py runs on one GPU: this build has no multi-GPU path (--gpus {args.gpus}).")
         sys.exit(2)
+    if args.formats:
+        format_matmuls(args.kernel_reps)
+        return
 
     import torch
 
@@ -193,6 +299,12 @@ def main():
 
     w, model, prompt = synth.workload_inputs(args.config)
     s = model.shape
+    down_fmts = None
+    if args.down_format != "q8_0":
+        down_fmts = ([("q4_k", "q6_k")[l % 2] for l in range(s.n_layer)] if args.down_format == "q4_k_m"
+                     else [args.down_format] * s.n_layer)
+        model = synth.with_k_quants(model, ["q8_0"] * s.n_layer, down_fmts)
+    down0 = down_fmts[0] if down_fmts else "q8_0"
     steps = w.decode_steps
     eprint(f"[bench] {w.name}: generating done, uploading {model.total_bytes / 1e6:.1f} MB")
     gm = Q8Model(synth.shape_fields(s), model.tensors, device="cuda:0")
@@ -241,7 +353,7 @@ def main():
         if r >= 2:
             dl.append(ev0.elapsed_time(ev1) / steps)
     dev_ms = statistics.median(dl)
-    W = per_token_weight_bytes(s)
+    W = per_token_weight_bytes(model)
     kvb = kv_bytes_per_position(s)
     mean_kv = len(prompt) + (steps + 1) / 2.0
     b_tok = W + kvb * mean_kv
@@ -261,7 +373,7 @@ def main():
     raw = [ms[i] for i in range(NKINDS)]
     ms = raw
     kv_len = len(prompt) + 1
-    kb = kernel_bytes(s, kv_len)
+    kb = kernel_bytes(s, kv_len, down0)
     launches = [1, s.n_layer, s.n_layer, s.n_layer, s.n_layer, s.n_layer, 1, 1]
     launches = [n if raw[i] > 0 else 0 for i, n in enumerate(launches)]
     per_step = [ms[i] * launches[i] for i in range(NKINDS)]
@@ -270,10 +382,10 @@ def main():
                                "gbs": round(kb[i] / (ms[i] * 1e-3) / 1e9, 1) if raw[i] > 0 else 0.0,
                                "launches_per_token": launches[i]} for i in range(NKINDS)}
     achieved = kb[dom] / (ms[dom] * 1e-3) / 1e9
-    traffic = measured_traffic(args.config, KIND_NAMES[dom])
+    traffic = measured_traffic(args.config, KIND_NAMES[dom]) if down_fmts is None else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": KIND_NAMES[dom], "symbol": kernel_symbols(s, kv_len)[dom],
+                "kernel": KIND_NAMES[dom], "symbol": kernel_symbols(s, kv_len, down0)[dom],
                 "bytes_per_launch": kb[dom], "us_per_launch": round(ms[dom] * 1e3, 2),
                 "empty_kernel_us": round(overhead * 1e3, 2)}
     copy_gbs = copy_bandwidth(torch)
@@ -296,10 +408,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(value / (1e3 / PAGES_DECODE_MS[args.config]), 2)
-                        if args.config in PAGES_DECODE_MS else None),
+                        if args.config in PAGES_DECODE_MS and down_fmts is None else None),
         "dtype": "f32 (Q8_0 int8 x f16-scale weights, f32 activations and accumulation)",
         "data": "synthetic: random-init Q8_0 weights, uniform random prompt ids",
-        "config": {"workload": w.name, "model": s.name, "layers": s.n_layer, "hidden": s.n_embd,
+        "config": {"workload": w.name + ("" if down_fmts is None else f" down={args.down_format}"),
+                   "model": s.name, "layers": s.n_layer, "hidden": s.n_embd,
                    "heads": s.n_head, "kv_heads": s.n_head_kv, "vocab": s.n_vocab,
                    "prompt_len": len(prompt), "decode_steps": steps, "batch": 1,
                    "parallelism": "single GPU"},
