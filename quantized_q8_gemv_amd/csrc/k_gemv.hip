@@ -773,7 +773,58 @@ __global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) {
 // activation chunk is in LDS at a time (so more workgroups fit per CU); each
 // thread keeps one accumulator per tile of its workgroup (at most kTilesPerWg)
 // across chunks; the tiles are reduced and written at the end.
+// The last chunk may be shorter than PC pairs (PC need not divide P: a
+// multiple of 4 pairs keeps every piece 16-byte aligned). Thread u always
+// takes pair u % PC of row u / PC, so its accumulator stays on one row; in
+// LDS a tile keeps a row stride of PC pairs.
 constexpr int kTilesPerWg = 8;
+
+__device__ inline int chunk_pairs(const GemvShape &sh, int c) { return min(sh.PC, sh.P - c * sh.PC); }
+
+// Piece i (of `unit` bytes) of chunk c's tile: source address and LDS byte offset.
+__device__ inline const uint8_t *ctile_src(const uint8_t *W, const GemvShape &sh, int row0, int pcc, int c, int i,
+                                           int unit) {
+    const int per_row = pcc * kPairBytes / unit;
+    const int r = i / per_row, j = i - r * per_row;
+    return W + size_t(row0 + r) * sh.rowbytes + size_t(c) * sh.PC * kPairBytes + size_t(j) * unit;
+}
+__device__ inline int ctile_dst(const GemvShape &sh, int pcc, int i, int unit) {
+    const int per_row = pcc * kPairBytes / unit;
+    const int r = i / per_row, j = i - r * per_row;
+    return r * sh.PC * kPairBytes + j * unit;
+}
+__device__ inline bool ctile_vec(const GemvShape &sh, int pcc) {
+    return (pcc % 4 == 0) && (sh.PC % 4 == 0) && (sh.P % 4 == 0);
+}
+__device__ inline void ctile_issue(const uint8_t *W, const GemvShape &sh, int row0, int nrows, int c, WStage &st) {
+    const int pcc = chunk_pairs(sh, c);
+    if (!ctile_vec(sh, pcc)) return;
+    const int n16 = nrows * pcc * kPairBytes / 16;
+#pragma unroll
+    for (int k = 0; k < kMaxV4; ++k) {
+        const int i = threadIdx.x + k * kThreads;
+        if (i < n16)
+            st.v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ctile_src(W, sh, row0, pcc, c, i, 16)));
+    }
+}
+__device__ inline void ctile_store(const uint8_t *W, const GemvShape &sh, int row0, int nrows, int c,
+                                   const WStage &st, uint32_t *wt) {
+    const int pcc = chunk_pairs(sh, c);
+    uint8_t *base = reinterpret_cast<uint8_t *>(wt);
+    if (ctile_vec(sh, pcc)) {
+        const int n16 = nrows * pcc * kPairBytes / 16;
+#pragma unroll
+        for (int k = 0; k < kMaxV4; ++k) {
+            const int i = threadIdx.x + k * kThreads;
+            if (i < n16) *reinterpret_cast<u32x4 *>(base + ctile_dst(sh, pcc, i, 16)) = st.v[k];
+        }
+    } else {
+#pragma unroll 1
+        for (int i = threadIdx.x; i < nrows * pcc * kPairBytes / 4; i += kThreads)
+            *reinterpret_cast<uint32_t *>(base + ctile_dst(sh, pcc, i, 4)) =
+                *reinterpret_cast<const uint32_t *>(ctile_src(W, sh, row0, pcc, c, i, 4));
+    }
+}
 
 __host__ __device__ inline size_t lds1c_bytes(const GemvShape &sh) {
     return align16(size_t(sh.NR) * sh.PC * kPairBytes) + align16(size_t(sh.PC) * kXPad * 4) +
@@ -788,24 +839,21 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
     float *outv = xs + align16(size_t(sh.PC) * kXPad * 4) / 4;
     const int tid = threadIdx.x;
     const int ntiles = (a.N + sh.NR - 1) / sh.NR;
-    const int nchunks = sh.P / sh.PC;
-    CoreArgs base{};
-    base.W[0] = a.W; base.nmat = 1; base.sh = sh; base.N = a.N; base.Tc = 1;
+    const int nchunks = (sh.P + sh.PC - 1) / sh.PC;
     int my_tiles = 0;
     for (int k = 0; k < kTilesPerWg; ++k) my_tiles += (int(blockIdx.x) + k * int(gridDim.x) < ntiles) ? 1 : 0;
     float acc[kTilesPerWg];
 #pragma unroll
     for (int k = 0; k < kTilesPerWg; ++k) acc[k] = 0.f;
 
-    CoreArgs cur = base;
-    cur.row0 = int(blockIdx.x) * sh.NR;
-    int nrows = tile_rows(cur);
-    bool vec = tile_vec(cur, nrows);
+    int row0 = int(blockIdx.x) * sh.NR;
+    int nrows = min(sh.NR, a.N - row0);
     WStage st;
-    stage_issue(cur, nrows, 0, vec, st);
+    ctile_issue(a.W, sh, row0, nrows, 0, st);
     for (int ch = 0; ch < nchunks; ++ch) {
+        const int pcc = chunk_pairs(sh, ch);
         __syncthreads();  // the previous chunk's activations are no longer read
-        const int n4 = sh.PC * 16;
+        const int n4 = pcc * 16;
         for (int e = tid; e < n4; e += kThreads) {
             const float4 v = *reinterpret_cast<const float4 *>(a.x + size_t(ch) * sh.PC * kPairWeights + size_t(e) * 4);
             *reinterpret_cast<float4 *>(xs + (e >> 4) * kXPad + (e & 15) * 4) = v;
@@ -817,22 +865,20 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
                 int nk = k + 1, nch = ch;
                 if (nk >= my_tiles) { nk = 0; ++nch; }
                 const bool has_next = nch < nchunks;
-                CoreArgs n = base;
-                n.row0 = (int(blockIdx.x) + nk * int(gridDim.x)) * sh.NR;
-                const int nn = has_next ? tile_rows(n) : 0;
-                const bool nvec = has_next ? tile_vec(n, nn) : false;
-                stage_store(cur, nrows, ch, vec, st, wt);
-                if (has_next) stage_issue(n, nn, nch, nvec, st);
+                const int nrow0 = (int(blockIdx.x) + nk * int(gridDim.x)) * sh.NR;
+                const int nn = has_next ? min(sh.NR, a.N - nrow0) : 0;
+                ctile_store(a.W, sh, row0, nrows, ch, st, wt);
+                if (has_next) ctile_issue(a.W, sh, nrow0, nn, nch, st);
                 __syncthreads();
-                const int units = nrows * sh.PC;
-                if (tid < units) {
+                const int r = tid / sh.PC, p = tid - r * sh.PC;
+                if (r < nrows && p < pcc) {
                     float dA, sA, dB, sB;
-                    pair_dot1(wt + size_t(tid) * (kPairBytes / 4), xs + size_t(tid % sh.PC) * kXPad, dA, sA, dB, sB);
+                    pair_dot1(wt + size_t(tid) * (kPairBytes / 4), xs + size_t(p) * kXPad, dA, sA, dB, sB);
                     acc[k] = fmaf(dA, sA, acc[k]);
                     acc[k] = fmaf(dB, sB, acc[k]);
                 }
                 __syncthreads();
-                cur = n; nrows = nn; vec = nvec;
+                row0 = nrow0; nrows = nn;
             }
         }
     }
@@ -978,6 +1024,30 @@ GemvShape choose_shape(int N, int K, int maxt, int nmat, int target_wgs, int nr_
     return s;
 }
 
+// Shape for the chunk-outer kernel. When the dividing chunk size is not a
+// multiple of 4 pairs (its tiles would move with 4-byte loads; e.g. K = 11008,
+// 172 pairs = 4 * 43) but the row is, take a multiple of 4 that need not
+// divide P: the best use of the 256 threads over the chunks, less a small cost
+// per chunk, at least 32 pairs per chunk.
+GemvShape chunked_shape(GemvShape s) {
+    if (s.PC % 4 == 0 || s.P % 4) return s;
+    const int cap = std::max(1, (40 * 1024) / (kXPad * 4));
+    double best = -1.0;
+    int best_pc = s.PC;
+    for (int pc = 32; pc <= std::min(cap, kThreads); pc += 4) {
+        const int nr = kThreads / pc;
+        const int nch = (s.P + pc - 1) / pc;
+        const double score = double(s.P) * nr / (double(nch) * kThreads) - 0.03 * nch;
+        if (score >= best) {
+            best = score;
+            best_pc = pc;
+        }
+    }
+    s.PC = best_pc;
+    s.NR = kThreads / best_pc;
+    return s;
+}
+
 // Decode grid: one workgroup per tile up to what the chip holds at once (by
 // LDS use), beyond that workgroups loop over tiles.
 int grid1(int ntiles, size_t lds) {
@@ -1054,6 +1124,7 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
     a.sh = choose_shape(N, K, maxt, 1, 512, 1);
     if (T == 1) {
         if (a.sh.PC != a.sh.P && !norm_w) {  // large K: chunk-outer walk
+            a.sh = chunked_shape(a.sh);
             const size_t lds = lds1c_bytes(a.sh);
             const int ntiles = (N + a.sh.NR - 1) / a.sh.NR;
             const int g = std::max(grid1(ntiles, lds), (ntiles + kTilesPerWg - 1) / kTilesPerWg);

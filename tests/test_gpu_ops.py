@@ -32,7 +32,9 @@ def gemv_bound(W, X):
 
 SHAPES = [(576, 576), (192, 576), (1536, 576), (576, 1536), (49152, 576),
           (4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (32000, 4096),
-          (37, 64), (1001, 192), (3, 128), (130, 320)]
+          (37, 64), (1001, 192), (3, 128), (130, 320),
+          # 172 block pairs per row: chunks of 64, 64 and a ragged 44
+          (301, 11008), (4096, 11008)]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)
