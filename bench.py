@@ -288,7 +288,10 @@ def main():
         eprint(f"bench.py runs on one GPU: this build has no multi-GPU path (--gpus {args.gpus}).")
         sys.exit(2)
     if args.formats:
+        import torch
         format_matmuls(args.kernel_reps)
+        # a copy of known size: the reference dispatch for scaling HBM counters
+        eprint(f"[bench] device copy: {copy_bandwidth(torch):.0f} GB/s (1 GiB, read + write)")
         return
 
     import torch

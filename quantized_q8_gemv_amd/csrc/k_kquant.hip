@@ -42,7 +42,6 @@ namespace {
 constexpr int kKqMaxChunk = 15360;             // activation floats staged per K chunk (60 KB + sums)
 constexpr uint32_t kKqOut = 0x80000000u;       // offset past any resource: loads return 0
 constexpr int kKqWord3 = 0x00020000;           // raw buffer, 32-bit data format
-constexpr int kKqUnroll = 2;                   // pieces per lane in flight
 
 struct KqArgs {
     const uint8_t *W;
@@ -58,6 +57,7 @@ struct KqFmt {
     static constexpr int PER = FMT == F_Q4_K ? 8 : 4;        // pieces per block
     static constexpr int NW = FMT == F_Q4_K ? 8 : 19;        // dwords a piece loads
     static constexpr int BYTES = FMT == F_Q4_K ? kQ4KBytes : kQ6KBytes;
+    static constexpr int U = FMT == F_Q4_K ? 2 : 1;          // pieces per lane per register stage
 };
 
 template <int FMT>
@@ -89,19 +89,38 @@ __device__ inline void kq_piece_load(__amdgpu_buffer_rsrc_t rs, uint32_t blk, in
 
 __device__ __forceinline__ float ubyte(uint32_t v, int b) { return static_cast<float>((v >> (8 * b)) & 0xffu); }
 
+// A word of small values whose known-zero bits the compiler should not see:
+// otherwise it turns each byte conversion into a bit-field extract plus a
+// conversion of byte 0, instead of one conversion of byte b. An empty asm
+// statement, no instruction; not volatile, so it does not fence the
+// scheduler (a volatile one cost a third of the kernel's speed).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
 // Q4_K piece p of block j (of the staged chunk) against the staged activations.
 __device__ inline float q4k_piece_dot(const uint32_t *w, int p, const float *xs, const float *x16, int j) {
     const int c = p >> 1, l0 = 16 * (p & 1);
     const float d = half_bits_to_float(w[0]), dmin = half_bits_to_float(w[0] >> 16);
-    uint32_t s0, m0, s1, m1;
-    q4k_scale_min(2 * c, w[1], w[2], w[3], s0, m0);
-    q4k_scale_min(2 * c + 1, w[1], w[2], w[3], s1, m1);
+    // scales and mins of sub-blocks 2c and 2c+1, branch-free (c differs across
+    // the wave's lanes): for c < 2 the low 6 bits of bytes 2c(+1) and 2c(+1)+4;
+    // for c >= 2 a nibble of byte 2c(+1)+4 below the top two bits of byte
+    // 2c(+1)-4 (scale) or 2c(+1) (min)
+    const bool hi = c >= 2;
+    const int sh = 16 * (c & 1);
+    const uint32_t s03 = w[1] >> sh, s47 = w[2] >> sh, s811 = w[3] >> sh;
+    const uint32_t lo_s = hi ? s811 : s03, lo_m = hi ? (s811 >> 4) : s47;
+    const uint32_t mask = hi ? 0x0f0fu : 0x3f3fu;
+    const uint32_t top_s = hi ? ((s03 >> 2) & 0x3030u) : 0u, top_m = hi ? ((s47 >> 2) & 0x3030u) : 0u;
+    const uint32_t sc = (lo_s & mask) | top_s, mn = (lo_m & mask) | top_m;   // byte 0: sub-block 2c, byte 1: 2c+1
+    const uint32_t s0 = sc & 0xffu, s1 = (sc >> 8) & 0xffu, m0 = mn & 0xffu, m1 = (mn >> 8) & 0xffu;
     const int xl = j * kQKK + 64 * c + l0;
     const float *xa = xs + xl, *xb = xs + xl + 32;
     float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = w[4 + e] & 0x0f0f0f0fu, hi = (w[4 + e] >> 4) & 0x0f0f0f0fu;
+        const uint32_t lo = opaque(w[4 + e] & 0x0f0f0f0fu), hi = opaque((w[4 + e] >> 4) & 0x0f0f0f0fu);
         const float4 va = *reinterpret_cast<const float4 *>(xa + 4 * e);
         const float4 vb = *reinterpret_cast<const float4 *>(xb + 4 * e);
         a0 = fmaf(ubyte(lo, 0), va.x, a0);
@@ -144,7 +163,7 @@ __device__ inline float q6k_piece_dot(const uint32_t *w, uint32_t blk, int p, co
         for (int e = 0; e < 4; ++e) {
             const uint32_t lowsrc = (k & 1) ? B[e] : A[e];
             const uint32_t nib = (k >= 2 ? (lowsrc >> 4) : lowsrc) & 0x0f0f0f0fu;
-            const uint32_t q = nib | (((Hb[e] >> (2 * k)) & 0x03030303u) << 4);
+            const uint32_t q = opaque(nib | (((Hb[e] >> (2 * k)) & 0x03030303u) << 4));
             const float4 v = *reinterpret_cast<const float4 *>(xk + 4 * e);
             s0 = fmaf(ubyte(q, 0), v.x, s0);
             s1 = fmaf(ubyte(q, 1), v.y, s1);
@@ -159,9 +178,45 @@ __device__ inline float q6k_piece_dot(const uint32_t *w, uint32_t blk, int p, co
     return d * acc;
 }
 
+// One stage: kU pieces per lane (each for the wave's R rows) starting at item i0.
+template <int FMT, int R>
+__device__ inline void kq_issue(__amdgpu_buffer_rsrc_t rs, const uint32_t *roff, uint32_t blk0, int items, int i0,
+                                int lane, int p, uint32_t (&w)[KqFmt<FMT>::U][R][KqFmt<FMT>::NW]) {
+    using F = KqFmt<FMT>;
+#pragma unroll
+    for (int u = 0; u < F::U; ++u) {
+        const int it = i0 + 64 * u + lane;
+        const uint32_t bo = blk0 + uint32_t(it / F::PER) * F::BYTES;
+#pragma unroll
+        for (int r = 0; r < R; ++r) kq_piece_load<FMT>(rs, it < items ? roff[r] + bo : kKqOut, p, w[u][r]);
+    }
+}
+
+template <int FMT, int R>
+__device__ inline void kq_compute(const uint32_t *roff, uint32_t blk0, int items, int i0, int lane, int p,
+                                  const float *xs, const float *x16, const uint32_t (&w)[KqFmt<FMT>::U][R][KqFmt<FMT>::NW],
+                                  float *acc) {
+    using F = KqFmt<FMT>;
+#pragma unroll
+    for (int u = 0; u < F::U; ++u) {
+        const int it = i0 + 64 * u + lane;
+        if (it < items) {
+            const int j = it / F::PER;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (FMT == F_Q4_K)
+                    acc[r] += q4k_piece_dot(w[u][r], p, xs, x16, j);
+                else
+                    acc[r] += q6k_piece_dot(w[u][r], roff[r] + blk0 + uint32_t(j) * F::BYTES, p, xs, x16, j);
+            }
+        }
+    }
+}
+
 template <int FMT, int R>
 __global__ __launch_bounds__(kThreads) void k_kq_gemv(KqArgs a) {
     using F = KqFmt<FMT>;
+    constexpr int STEP = 64 * F::U;   // items per stage
     extern __shared__ __align__(16) float xs[];   // a.kc activations, then a.kc / 16 sums
     float *x16 = xs + a.kc;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -176,8 +231,13 @@ __global__ __launch_bounds__(kThreads) void k_kq_gemv(KqArgs a) {
         acc[r] = 0.f;
     }
     const int p = lane % F::PER;   // the same piece of every block for this lane
+    uint32_t w0[F::U][R][F::NW], w1[F::U][R][F::NW];
     for (int k0 = 0; k0 < a.K; k0 += a.kc) {
         const int kn = min(a.kc, a.K - k0);
+        const uint32_t blk0 = uint32_t(k0 / kQKK) * F::BYTES;
+        const int items = kn / kQKK * F::PER;
+        // the first stage's weights do not depend on the activations: in flight during the staging
+        kq_issue<FMT, R>(rs, roff, blk0, items, 0, lane, p, w0);
         __syncthreads();   // the previous chunk is consumed
         for (int i = tid; i < kn / 16; i += kThreads) {
             const float4 *src = reinterpret_cast<const float4 *>(a.X + k0 + 16 * i);
@@ -188,33 +248,13 @@ __global__ __launch_bounds__(kThreads) void k_kq_gemv(KqArgs a) {
                      (((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w)));
         }
         __syncthreads();
-        const uint32_t blk0 = uint32_t(k0 / kQKK) * F::BYTES;
-        const int items = kn / kQKK * F::PER;
-        for (int i0 = 0; i0 < items; i0 += 64 * kKqUnroll) {
-            uint32_t w[kKqUnroll][R][F::NW];
-#pragma unroll
-            for (int u = 0; u < kKqUnroll; ++u) {
-                const int it = i0 + 64 * u + lane;
-                const uint32_t bo = blk0 + uint32_t(it / F::PER) * F::BYTES;
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    kq_piece_load<FMT>(rs, it < items ? roff[r] + bo : kKqOut, p, w[u][r]);
-            }
-#pragma unroll
-            for (int u = 0; u < kKqUnroll; ++u) {
-                if (i0 + 64 * u >= items) break;   // wave-uniform
-                const int it = i0 + 64 * u + lane;
-                if (it < items) {
-                    const int j = it / F::PER;
-#pragma unroll
-                    for (int r = 0; r < R; ++r) {
-                        if (FMT == F_Q4_K)
-                            acc[r] += q4k_piece_dot(w[u][r], p, xs, x16, j);
-                        else
-                            acc[r] += q6k_piece_dot(w[u][r], roff[r] + blk0 + uint32_t(j) * F::BYTES, p, xs, x16, j);
-                    }
-                }
-            }
+        // two register stages: the next stage's loads are issued before this one is computed
+        for (int i0 = 0; i0 < items; i0 += 2 * STEP) {
+            if (i0 + STEP < items) kq_issue<FMT, R>(rs, roff, blk0, items, i0 + STEP, lane, p, w1);
+            kq_compute<FMT, R>(roff, blk0, items, i0, lane, p, xs, x16, w0, acc);
+            if (i0 + STEP >= items) break;
+            if (i0 + 2 * STEP < items) kq_issue<FMT, R>(rs, roff, blk0, items, i0 + 2 * STEP, lane, p, w0);
+            kq_compute<FMT, R>(roff, blk0, items, i0 + STEP, lane, p, xs, x16, w1, acc);
         }
     }
 #pragma unroll
