@@ -49,21 +49,18 @@ NKINDS = len(KIND_NAMES)
 TRAFFIC_FILES = {"C2": "profiles/decode_kernels_135m_13+20_pmc_traffic.md"}
 
 
-def kernel_symbols(s, kv_len, down_fmt="q8_0"):
-    """Device symbol of each decode kernel kind at this shape (T = 1). With
-    one attention split the o-projection merges the split itself (variant 1);
-    with several a separate merge kernel runs first (variant 0). A Q4_K / Q6_K
-    down projection runs k_kq_gemv<format, rows per wave>."""
+def kernel_symbols(s, down_fmt="q8_0"):
+    """Device symbol of each decode kernel kind at this shape (T = 1). A
+    Q4_K / Q6_K down projection runs k_kq_gemv<format, rows per wave>."""
     multi = (s.n_embd // 64) * 272 > 40 * 1024  # rows longer than one LDS chunk
+    o_multi = (s.q_dim // 64) * 272 > 40 * 1024
     down_multi = (s.n_ff // 64) * 272 > 40 * 1024
-    chunk = 64 if s.head_dim <= 64 else 32
-    fused = 1 if kv_len <= chunk else 0
     if down_fmt == "q8_0":
-        down = "k_matmul1_chunked" if down_multi else "k_matmul1<0, false>"
+        down = "k_matmul1_chunked" if down_multi else "k_matmul1<false>"
     else:
         down = f"k_kq_gemv<{1 if down_fmt == 'q4_k' else 2}, {2 if s.n_embd >= 4096 else 1}>"
     return ["k_embed", f"k_qkv1<{str(multi).lower()}>", "k_attn_decode",
-            f"k_matmul1<{fused}, {str(multi).lower()}>", f"k_gateup1<{str(multi).lower()}>",
+            "k_matmul1_chunked" if o_multi else "k_matmul1<false>", f"k_gateup1<{str(multi).lower()}>",
             down, f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
 
 
@@ -388,7 +385,7 @@ def main():
     traffic = measured_traffic(args.config, KIND_NAMES[dom]) if down_fmts is None else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": KIND_NAMES[dom], "symbol": kernel_symbols(s, kv_len, down0)[dom],
+                "kernel": KIND_NAMES[dom], "symbol": kernel_symbols(s, down0)[dom],
                 "bytes_per_launch": kb[dom], "us_per_launch": round(ms[dom] * 1e3, 2),
                 "empty_kernel_us": round(overhead * 1e3, 2)}
     copy_gbs = copy_bandwidth(torch)

@@ -13,9 +13,10 @@
 // Decode: the cache is split into chunks of keys; one workgroup handles one
 // chunk for all query heads of one KV head (K/V are read once per group),
 // keeps scores and softmax in LDS, and writes (max, sum, unnormalised o)
-// partials. The partials are merged in split order by the consumer (the
-// o-projection's prologue, or k_attn_combine), so the result does not depend
-// on timing and no device-wide atomics are needed.
+// partials. The partials are merged in split order by k_attn_combine, so the
+// result does not depend on timing and no device-wide atomics are needed;
+// when the cache fits one split, the workgroup writes the normalised output
+// itself (the merge of one split is that division).
 //
 // Prefill: one workgroup per (32 queries, head); key tiles staged in LDS,
 // online softmax in f32 per query row.
@@ -103,6 +104,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
             const int h = e / hd, d = e - h * hd;
             float acc = 0.f;
             for (int j = 0; j < nk; ++j) acc = fmaf(L.sc[h * C + j], L.v[j * hd + d], acc);
+            if (a.o) {  // the only split: its normalised output (what the merge of one split computes)
+                a.o[size_t(g * G + h) * hd + d] = acc / L.l[h];
+                continue;
+            }
             float *pp = a.part + (size_t(g * G + h) * a.n_splits + s) * (hd + 2);
             pp[2 + d] = acc;
             if (d == 0) {

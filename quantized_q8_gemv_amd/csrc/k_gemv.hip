@@ -150,41 +150,13 @@ __device__ inline void stage_store(const CoreArgs &a, int nrows, int c, bool vec
     }
 }
 
-// Activation sources for the x staging step.
-enum XMode { X_PLAIN = 0, X_ATTN_COMBINE = 1 };
-
-struct Combine {
-    const float *part;   // [nh][n_splits][hd + 2]: (max, sum, unnormalised o[hd])
-    const StepState *st; // kv_len = st->slot + 1
-    int n_splits, hd, chunk;
-};
-
-// Merge the split-KV partials of attention output element e = h*hd + d in
-// split order (fixed, so the result does not depend on timing).
-__device__ inline float combine_elem(const Combine &cb, int e) {
-    const int kv_len = cb.st->slot + 1;
-    const int active = min((kv_len + cb.chunk - 1) / cb.chunk, cb.n_splits);
-    const int h = e / cb.hd, d = e - h * cb.hd;
-    const float *pb = cb.part + size_t(h) * cb.n_splits * (cb.hd + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < active; ++s) M = fmaxf(M, pb[s * (cb.hd + 2)]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < active; ++s) {
-        const float w = expf(pb[s * (cb.hd + 2)] - M);
-        L = fmaf(w, pb[s * (cb.hd + 2) + 1], L);
-        O = fmaf(w, pb[s * (cb.hd + 2) + 2 + d], O);
-    }
-    return O / L;
-}
-
 // Computes outv[(t*nmat + m)*NR + r] = sum_k W_m[row0+r][k] * U[t][k].
-//   U = X, or rmsnorm(X) * norm_w when norm_w is set, or (X_ATTN_COMBINE)
-//   the merged attention partials.
+//   U = X, or rmsnorm(X) * norm_w when norm_w is set.
 // Timeline: chunk-0 weight loads are issued first; the activation row is
 // read (and its norm computed) while they are in flight; chunk c+1's loads
 // are issued before chunk c is computed.
-template <int MAXT, int XM = X_PLAIN, bool MULTI = true>
-__device__ void gemv_core(const CoreArgs &a, const Lds &l, const Combine *cb = nullptr) {
+template <int MAXT, bool MULTI = true>
+__device__ void gemv_core(const CoreArgs &a, const Lds &l) {
     const int tid = threadIdx.x;
     const GemvShape &sh = a.sh;
     const int nrows = min(sh.NR, a.N - a.row0);
@@ -206,15 +178,7 @@ __device__ void gemv_core(const CoreArgs &a, const Lds &l, const Combine *cb = n
             const int p = rem >> 4;
             const int i4 = rem & 15;
             const int k = (c * sh.PC + p) * kPairWeights + i4 * 4;
-            float4 v;
-            if (XM == X_ATTN_COMBINE) {
-                v.x = combine_elem(*cb, k);
-                v.y = combine_elem(*cb, k + 1);
-                v.z = combine_elem(*cb, k + 2);
-                v.w = combine_elem(*cb, k + 3);
-            } else {
-                v = *reinterpret_cast<const float4 *>(a.X + size_t(t) * a.ldx + k);
-            }
+            float4 v = *reinterpret_cast<const float4 *>(a.X + size_t(t) * a.ldx + k);
             if (normalize) {
                 const float r = l.rinv[t];
                 const float4 w = *reinterpret_cast<const float4 *>(a.norm_w + k);
@@ -378,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
     c.W[0] = W; c.W[1] = nullptr; c.nmat = 1; c.sh = a.sh; c.N = N;
     c.row0 = tile * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<MAXT, X_PLAIN, MULTI>(c, l);
+    gemv_core<MAXT, MULTI>(c, l);
 
     const int nrows = min(a.sh.NR, N - c.row0);
     const int half = nrows >> 1;
@@ -429,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(GateUpArgs a) {
     c.W[0] = a.wg; c.W[1] = a.wu; c.nmat = 2; c.sh = a.sh; c.N = a.F;
     c.row0 = blockIdx.x * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<MAXT, X_PLAIN, MULTI>(c, l);
+    gemv_core<MAXT, MULTI>(c, l);
     const int nrows = min(a.sh.NR, a.F - c.row0);
     for (int e = threadIdx.x; e < c.Tc * nrows; e += kThreads) {
         const int t = e / nrows, r = e - t * nrows;
@@ -449,10 +413,9 @@ struct MatmulArgs {
     GemvShape sh;
     int N, T, accumulate;
     float eps;
-    Combine cb;  // used by the attention-combine variant only
 };
 
-template <int MAXT, int XM, bool MULTI>
+template <int MAXT, bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_matmul(MatmulArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds l = carve(smem, a.sh, 1, MAXT);
@@ -461,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void k_matmul(MatmulArgs a) {
     c.W[0] = a.W; c.W[1] = nullptr; c.nmat = 1; c.sh = a.sh; c.N = a.N;
     c.row0 = blockIdx.x * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<MAXT, XM, MULTI>(c, l, &a.cb);
+    gemv_core<MAXT, MULTI>(c, l);
     const int nrows = min(a.sh.NR, a.N - c.row0);
     for (int e = threadIdx.x; e < c.Tc * nrows; e += kThreads) {
         const int t = e / nrows, r = e - t * nrows;
@@ -557,8 +520,8 @@ __global__ __launch_bounds__(kThreads) void k_argmax_out(const float *partials, 
 
 // ---------------------------------------------------------------- decode (T = 1)
 //
-// A decode workgroup stages the whole activation row once (normalised, or
-// merged from attention partials) and then walks row tiles
+// A decode workgroup stages the whole activation row once (normalised when
+// a norm comes first) and then walks row tiles
 // blockIdx.x, blockIdx.x + gridDim.x, ...: the next tile's weights are issued
 // into registers while the current tile is computed, so the weight stream
 // never waits on the activation staging and the row is read once per
@@ -593,22 +556,9 @@ __device__ inline Lds1 carve1(uint8_t *smem, const GemvShape &sh, int nmat) {
 }
 
 // The whole row u (K values) into xs in pair layout; the caller syncs.
-template <int XM>
-__device__ void stage_row1(const CoreArgs &a, const Lds1 &l, const Combine *cb) {
+__device__ void stage_row1(const CoreArgs &a, const Lds1 &l) {
     const int tid = threadIdx.x;
     const int n4 = a.sh.P * 16;
-    if (XM == X_ATTN_COMBINE) {
-        for (int e = tid; e < n4; e += kThreads) {
-            const int k = e * 4;
-            float4 v;
-            v.x = combine_elem(*cb, k);
-            v.y = combine_elem(*cb, k + 1);
-            v.z = combine_elem(*cb, k + 2);
-            v.w = combine_elem(*cb, k + 3);
-            *reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4) = v;
-        }
-        return;
-    }
     float ss = 0.f;
     for (int e = tid; e < n4; e += kThreads) {
         const float4 v = *reinterpret_cast<const float4 *>(a.X + size_t(e) * 4);
@@ -707,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
     bool vec = tile_vec(c, nrows);
     WStage st;
     stage_issue(c, nrows, 0, vec, st);
-    stage_row1<X_PLAIN>(c, l, nullptr);
+    stage_row1(c, l);
     const int pos = a.st->pos, slot = a.st->slot;
     for (; tile < ntiles; tile += gridDim.x) {
         const bool has_next = tile + int(gridDim.x) < ntiles;
@@ -755,7 +705,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) {
     bool vec = tile_vec(c, nrows);
     WStage st;
     stage_issue(c, nrows, 0, vec, st);
-    stage_row1<X_PLAIN>(c, l, nullptr);
+    stage_row1(c, l);
     for (; tile < ntiles; tile += gridDim.x) {
         const bool has_next = tile + int(gridDim.x) < ntiles;
         CoreArgs n = c;
@@ -908,7 +858,7 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
     }
 }
 
-template <int XM, bool MULTI>
+template <bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds1 l = carve1(smem, a.sh, 1);
@@ -922,7 +872,7 @@ __global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
     bool vec = tile_vec(c, nrows);
     WStage st;
     stage_issue(c, nrows, 0, vec, st);
-    stage_row1<XM>(c, l, &a.cb);
+    stage_row1(c, l);
     for (; tile < ntiles; tile += gridDim.x) {
         const bool has_next = tile + int(gridDim.x) < ntiles;
         CoreArgs n = c;
@@ -954,7 +904,7 @@ __global__ __launch_bounds__(kThreads) void k_lmhead1(LmHeadArgs a) {
     bool vec = tile_vec(c, nrows);
     WStage st;
     stage_issue(c, nrows, 0, vec, st);
-    stage_row1<X_PLAIN>(c, l, nullptr);
+    stage_row1(c, l);
     float *logits = a.st->logits_out;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     float bv = -INFINITY;
@@ -1134,34 +1084,16 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
         const size_t lds = lds1_bytes(a.sh, 1);
         const int g = grid1((N + a.sh.NR - 1) / a.sh.NR, lds);
         if (a.sh.PC != a.sh.P)
-            hipLaunchKernelGGL((k_matmul1<X_PLAIN, true>), dim3(g), dim3(kThreads), lds, s, a);
+            hipLaunchKernelGGL((k_matmul1<true>), dim3(g), dim3(kThreads), lds, s, a);
         else
-            hipLaunchKernelGGL((k_matmul1<X_PLAIN, false>), dim3(g), dim3(kThreads), lds, s, a);
+            hipLaunchKernelGGL((k_matmul1<false>), dim3(g), dim3(kThreads), lds, s, a);
         return hipGetLastError();
     }
     dim3 grid((N + a.sh.NR - 1) / a.sh.NR, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 1, maxt);
     const bool multi = a.sh.PC != a.sh.P;
-    if (multi) hipLaunchKernelGGL((k_matmul<kMaxTokChunk, X_PLAIN, true>), grid, dim3(kThreads), lds, s, a);
-    else hipLaunchKernelGGL((k_matmul<kMaxTokChunk, X_PLAIN, false>), grid, dim3(kThreads), lds, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_oproj_combine(const uint8_t *Wo, int H, int QD, const float *part,
-                                const StepState *st, int n_splits, int hd, float *x,
-                                hipStream_t s) {
-    MatmulArgs a{};
-    a.W = Wo; a.norm_w = nullptr; a.x = nullptr; a.y = x; a.N = H; a.T = 1; a.accumulate = 1;
-    a.eps = 0.f;
-    a.cb.part = part; a.cb.st = st; a.cb.n_splits = n_splits; a.cb.hd = hd;
-    a.cb.chunk = attn_chunk(hd);
-    a.sh = choose_shape(H, QD, 1, 1, 512, 1);
-    const size_t lds = lds1_bytes(a.sh, 1);
-    const int g = grid1((H + a.sh.NR - 1) / a.sh.NR, lds);
-    if (a.sh.PC != a.sh.P)
-        hipLaunchKernelGGL((k_matmul1<X_ATTN_COMBINE, true>), dim3(g), dim3(kThreads), lds, s, a);
-    else
-        hipLaunchKernelGGL((k_matmul1<X_ATTN_COMBINE, false>), dim3(g), dim3(kThreads), lds, s, a);
+    if (multi) hipLaunchKernelGGL((k_matmul<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
+    else hipLaunchKernelGGL((k_matmul<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 

@@ -110,11 +110,6 @@ hipError_t launch_argmax_finish(const Dims &d, const float *partials, StepState 
                                 hipStream_t s);
 hipError_t launch_argmax(const float *x, int64_t n, uint32_t *out, float *partials,
                          hipStream_t s);
-// o-projection + residual for one token whose input is the decode attention's
-// split partials (merged in the kernel's prologue).
-hipError_t launch_oproj_combine(const uint8_t *Wo, int H, int QD, const float *part,
-                                const StepState *st, int n_splits, int hd, float *x,
-                                hipStream_t s);
 size_t argmax_partials_bytes(int64_t n);
 
 // Decode attention (one query per head over kv_len keys, no mask).
@@ -127,6 +122,7 @@ struct AttnDecodeArgs {
     int kv_stride, nh, nkv, hd;
     int n_splits;        // workgroups per KV group launched
     float scale;
+    float *o;            // n_splits == 1 only: the normalised output [nh][hd] instead of partials (or NULL)
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s);
 // Merge split partials into o; with st set, kv_len is read from st->slot + 1.

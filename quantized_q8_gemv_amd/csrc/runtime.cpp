@@ -194,16 +194,12 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.st = st; a.kv_len_arg = -1; a.kv_stride = d.max_seq;
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = decode_splits;
             a.scale = 1.0f / sqrtf(float(d.hd));
+            a.o = decode_splits == 1 ? att : nullptr;  // one split: the attention kernel normalises
             if ((e = launch_attn_decode(a, s)) != hipSuccess) return e;
-            if (w.fo != F_Q8_0) {      // 256-weight blocks: merge, then the K-format GEMV
-                e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s);
-                if (e == hipSuccess) e = launch_kq_gemv(w.fo, w.wo, d.H, QD, att, 1, x, s);
-            } else if (decode_splits == 1) {  // one split: its normalisation is merged into the o-projection
-                e = launch_oproj_combine(w.wo, d.H, QD, a.part, st, 1, d.hd, x, s);
-            } else {                   // several: one merge kernel, then the plain o-projection
-                e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s);
-                if (e == hipSuccess) e = launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, x, s);
-            }
+            if (decode_splits > 1 && (e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s)) != hipSuccess)
+                return e;
+            e = w.fo != F_Q8_0 ? launch_kq_gemv(w.fo, w.wo, d.H, QD, att, 1, x, s)
+                               : launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, x, s);
             if (e != hipSuccess) return e;
         } else {
             AttnPrefillArgs a;
@@ -554,6 +550,7 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     a.st = S; a.kv_len_arg = -1; a.kv_stride = d.max_seq;
     a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = split_bucket(m, kv_len);
     a.scale = 1.0f / sqrtf(float(d.hd));
+    a.o = a.n_splits == 1 ? m->at<float>(m->lay.att) : nullptr;
     auto launch = [&](int kind) -> hipError_t {
         switch (kind) {
             case 0: return launch_embed(m->tok_embd, d.H, d.V, S, m->at<uint32_t>(m->lay.tok), 1, 1, x, s);
@@ -561,7 +558,6 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
             case 2: return launch_attn_decode(a, s);
             case 3:
                 if (w.fo != F_Q8_0) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
-                if (a.n_splits == 1) return launch_oproj_combine(w.wo, d.H, QD, a.part, S, 1, d.hd, x, s);
                 return launch_matmul(w.wo, d.H, QD, m->at<float>(m->lay.att), 1, nullptr, d.eps, 1, x, s);
             case 4: return launch_gateup(d, w, x, h, 1, s);
             case 5:
@@ -676,6 +672,7 @@ q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int3
         a.nh = n_head; a.nkv = n_head_kv; a.hd = hd;
         a.n_splits = (kv_len + attn_chunk(hd) - 1) / attn_chunk(hd);
         a.scale = 1.0f / sqrtf(float(hd));
+        a.o = nullptr;
         e = launch_attn_decode(a, s);
         if (e == hipSuccess) e = launch_attn_combine(a.part, a.n_splits, kv_len, n_head, hd, O, nullptr, s);
     } else {
