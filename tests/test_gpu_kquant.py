@@ -59,9 +59,6 @@ def _run_op(fmt, N, K, T, accumulate, seed, sample_rows=None):
     assert np.isfinite(Y).all()
     bad = err > bound
     assert not bad.any(), f"{fmt} N={N} K={K} T={T}: {int(bad.sum())} outputs off, worst {float((err / scale).max()):.3g}"
-    if sample_rows is None and not accumulate:
-        # rows the op was not asked about are not touched: none here, all N written
-        assert np.isfinite(Y).all()
     return float((err / scale).max())
 
 
@@ -164,4 +161,16 @@ def test_gguf_in_the_pages_q4_k_m_mix_matches_the_oracle(tmp_path):
     om = oracle.OracleModel(synth.Model(s, om_tensors))
     ids, err, ties = compare_generation(Q8Model.from_gguf(path), om, prompt, 8, "gguf Q4_K_M mix 13+8")
     log(f"gguf Q4_K_M mix: max abs err {err:.3g}")
+    assert ties <= 1
+
+
+def test_k_format_o_projection_after_a_multi_split_merge():
+    """A 70-token prompt puts the cache past one 64-key split, so decode runs
+    the split merge before the K-format o-projection GEMV."""
+    s = _kquant_shape()
+    m = synth.with_k_quants(synth.random_model(s, 2), ["q4_k", "q6_k", "q4_k"], ["q8_0", "q4_k", "q6_k"])
+    prompt = synth.prompt_ids(s.n_vocab, 70, 9)
+    ids, err, ties = compare_generation(gpu_model(m), oracle.OracleModel(m), prompt, 6,
+                                        "k-format model 70+6")
+    log(f"k-format model 70+6: max abs err {err:.3g}")
     assert ties <= 1
