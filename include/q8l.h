@@ -243,6 +243,7 @@ q8l_status q8l_op_matmul_kq(const void *W, int32_t dtype, int64_t N, int64_t K, 
  * Query head h reads KV group h / (n_head/n_head_kv). Scores are
  * q.k / sqrt(hd); when T > 1, query t sees keys j <= kv_len - T + t (the
  * causal mask offset by the cached prefix); when T == 1 it sees all kv_len.
+ * Q, K and V must be 16-byte aligned (Q8L_E_INVALID_ARG otherwise).
  */
 q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int32_t T,
                             int32_t kv_len, int32_t kv_stride, int32_t n_head,

@@ -61,14 +61,21 @@ __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
     if (s < active) {
         const int j0 = s * C;
         const int nk = min(C, kv_len - j0);
-        const float *qg = a.q + size_t(g) * G * hd;
-        for (int e = tid; e < G * hd; e += kThreads) L.q[e] = qg[e];
-        const float *kb = a.kc + (size_t(g) * a.kv_stride + j0) * hd;
-        const float *vb = a.vc + (size_t(g) * a.kv_stride + j0) * hd;
-        for (int e = tid; e < nk * hd; e += kThreads) {
-            const int j = e / hd, d = e - j * hd;
-            L.k[j * (hd + 1) + d] = kb[e];
-            L.v[e] = vb[e];
+        const float4 *qg = reinterpret_cast<const float4 *>(a.q + size_t(g) * G * hd);
+        for (int e4 = tid; e4 < G * hd / 4; e4 += kThreads) reinterpret_cast<float4 *>(L.q)[e4] = qg[e4];
+        // 16-byte loads (hd % 8 == 0; the cache and the V tile are 16-byte aligned);
+        // K rows keep a one-float pad in LDS (conflict-free score reads)
+        const float4 *kb = reinterpret_cast<const float4 *>(a.kc + (size_t(g) * a.kv_stride + j0) * hd);
+        const float4 *vb = reinterpret_cast<const float4 *>(a.vc + (size_t(g) * a.kv_stride + j0) * hd);
+        for (int e4 = tid; e4 < nk * hd / 4; e4 += kThreads) {
+            const float4 kv = kb[e4], vv = vb[e4];
+            const int e = 4 * e4, j = e / hd, d = e - j * hd;
+            float *kd = L.k + j * (hd + 1) + d;
+            kd[0] = kv.x;
+            kd[1] = kv.y;
+            kd[2] = kv.z;
+            kd[3] = kv.w;
+            *reinterpret_cast<float4 *>(L.v + e) = vv;
         }
         __syncthreads();
         for (int e = tid; e < G * nk; e += kThreads) {

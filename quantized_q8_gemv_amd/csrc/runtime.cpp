@@ -658,7 +658,9 @@ q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int3
                             int32_t hd, float *O, void *workspace, size_t workspace_bytes,
                             void *stream) {
     if (!Q || !K || !V || !O || T < 1 || kv_len < T || kv_stride < kv_len || n_head < 1 ||
-        n_head_kv < 1 || n_head % n_head_kv || n_head / n_head_kv > kMaxGroup || hd % 8 || hd > 128)
+        n_head_kv < 1 || n_head % n_head_kv || n_head / n_head_kv > kMaxGroup || hd % 8 || hd > 128 ||
+        (reinterpret_cast<uintptr_t>(Q) & 15) || (reinterpret_cast<uintptr_t>(K) & 15) ||
+        (reinterpret_cast<uintptr_t>(V) & 15))
         return Q8L_E_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;

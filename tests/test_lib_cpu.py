@@ -140,3 +140,12 @@ def test_rope_types_accepted():
         f = synth.shape_fields(synth.TINY)
         f["rope_type"] = rt
         assert C.q8l_workspace_bytes(C.config_from(f)) > 0
+
+
+def test_attention_op_rejects_misaligned_operands():
+    ok = [FAKE, FAKE, FAKE]
+    for i in range(3):
+        ptrs = list(ok)
+        ptrs[i] = FAKE + 4
+        assert C.q8l_op_attention(ptrs[0], ptrs[1], ptrs[2], 1, 16, 16, 4, 2, 64, FAKE, FAKE, 1 << 20,
+                                  stream=0) == C.Q8L_E_INVALID_ARG
