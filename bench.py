@@ -18,6 +18,11 @@ Printed JSON line:
   roofline         the decode kernel with the most time per step, its algorithmic
                    bytes per launch over its mean launch time (HIP events)
   cpu_baseline     the CPU oracle timed on a bounded sample of the same workload
+  host_loop_reps   min and median over the timed steps (per-token decode, prefill)
+
+Other modes: --formats times one matmul per block format; --kv-sweep prints
+one line per cache length (16 ... 4000 prompt tokens on the 135M-shaped
+model): device-loop us/token and the attention kernel's time at that length.
 """
 
 from __future__ import annotations
@@ -266,6 +271,60 @@ def format_matmuls(reps):
     return lines
 
 
+KV_SWEEP = [16, 64, 256, 1024, 2048, 4000]
+
+
+def kv_sweep(kernel_reps, steps=16):
+    """Decode cost against cache length on the 135M-shaped model: for each
+    prompt length, prefill it, then `steps` greedy steps through q8l_generate
+    (device loop, HIP events), and the attention kernel alone at that length
+    (q8l_time_decode_kernels; with several splits, the merge kernel that
+    follows it is not included)."""
+    import torch
+
+    import synth
+    from quantized_q8_gemv_amd import q8l as C
+    from quantized_q8_gemv_amd.model import Q8Model
+
+    w, model, _ = synth.workload_inputs("C4")
+    s = model.shape
+    gm = Q8Model(synth.shape_fields(s), model.tensors, device="cuda:0")
+    ids = torch.zeros(steps, dtype=torch.int32, device="cuda:0")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    W = per_token_weight_bytes(model)
+    kvb = kv_bytes_per_position(s)
+    chunk = 64 if s.head_dim <= 64 else 32
+    for kv in KV_SWEEP:
+        prompt = synth.prompt_ids(s.n_vocab, kv, 11)
+        dl = []
+        for r in range(5):
+            assert gm.forward_async(prompt, 0) == C.Q8L_OK
+            ev0.record()
+            assert gm.generate_async(gm.argmax, kv, steps, ids) == C.Q8L_OK
+            ev1.record()
+            torch.cuda.synchronize()
+            if r >= 1:
+                dl.append(ev0.elapsed_time(ev1) / steps)
+        assert gm.forward_async(prompt, 0) == C.Q8L_OK
+        torch.cuda.synchronize()
+        ms = (ctypes.c_float * (NKINDS + 1))()
+        assert C.lib().q8l_time_decode_kernels(gm.handle, kernel_reps, ms,
+                                               torch.cuda.current_stream().cuda_stream) == C.Q8L_OK
+        dev_ms = statistics.median(dl)
+        b_tok = W + kvb * (kv + (steps + 1) / 2.0)
+        splits = -(-(kv + 1) // chunk)
+        attn_bytes = (kv + 1) * s.n_head_kv * s.head_dim * 4 * 2 + s.q_dim * 4
+        line = {"mode": "kv_sweep", "model": s.name, "kv_len": kv + 1, "decode_steps": steps,
+                "us_per_token": round(dev_ms * 1e3, 2), "us_per_token_min": round(min(dl) * 1e3, 2),
+                "hbm_gbs": round(b_tok / (dev_ms * 1e-3) / 1e9, 1),
+                "attention_us": round(ms[2] * 1e3, 2), "attention_splits": splits,
+                "attention_gbs": round(attn_bytes / (ms[2] * 1e-3) / 1e9, 1),
+                "attention_us_per_token": round(ms[2] * 1e3 * s.n_layer, 1)}
+        eprint(f"[bench] kv {kv + 1}: {line['us_per_token']} us/token, attention {line['attention_us']} us "
+               f"({splits} splits)")
+        print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,10 +339,16 @@ def main():
                          "layers, as the pages' 4-bit file holds them)")
     ap.add_argument("--formats", action="store_true",
                     help="time the single matmul per block format (Q8_0, Q4_K, Q6_K) instead")
+    ap.add_argument("--kv-sweep", action="store_true",
+                    help="decode cost against cache length on the 135M-shaped model instead "
+                         "(one JSON line per length)")
     args = ap.parse_args()
     if args.gpus != 1:
         eprint(f"bench.py runs on one GPU: this build has no multi-GPU path (--gpus {args.gpus}).")
         sys.exit(2)
+    if args.kv_sweep:
+        kv_sweep(args.kernel_reps)
+        return
     if args.formats:
         import torch
         format_matmuls(args.kernel_reps)
@@ -418,7 +483,13 @@ def main():
                    "parallelism": "single GPU"},
         "prefill_tok_s": round(prefill_tok_s, 1),
         "decode_ms_per_token_host_loop": round(sum(dec) / (args.steps * steps) * 1e3, 4),
+        # per timed step (one generation each): min and median over the steps
+        "host_loop_reps": {"decode_ms_per_token_min": round(min(dec) / steps * 1e3, 4),
+                           "decode_ms_per_token_median": round(statistics.median(dec) / steps * 1e3, 4),
+                           "prefill_ms_min": round(min(pre) * 1e3, 3),
+                           "prefill_ms_median": round(statistics.median(pre) * 1e3, 3)},
         "device_loop": {"us_per_token": round(dev_ms * 1e3, 2),
+                        "us_per_token_min": round(min(dl) * 1e3, 2),
                         "tok_s": round(1e3 / dev_ms, 1),
                         "bytes_per_token": int(b_tok),
                         "hbm_gbs": round(dev_gbs, 1),

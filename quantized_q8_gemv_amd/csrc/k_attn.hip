@@ -40,6 +40,8 @@ struct DecodeLds {
     float *l;    // G
 };
 
+constexpr int kKvPer = 4;   // float4 per thread of a K (or V) tile: 64 x 64 or 32 x 128 floats
+
 __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -67,15 +69,30 @@ __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
         // K rows keep a one-float pad in LDS (conflict-free score reads)
         const float4 *kb = reinterpret_cast<const float4 *>(a.kc + (size_t(g) * a.kv_stride + j0) * hd);
         const float4 *vb = reinterpret_cast<const float4 *>(a.vc + (size_t(g) * a.kv_stride + j0) * hd);
-        for (int e4 = tid; e4 < nk * hd / 4; e4 += kThreads) {
-            const float4 kv = kb[e4], vv = vb[e4];
-            const int e = 4 * e4, j = e / hd, d = e - j * hd;
-            float *kd = L.k + j * (hd + 1) + d;
-            kd[0] = kv.x;
-            kd[1] = kv.y;
-            kd[2] = kv.z;
-            kd[3] = kv.w;
-            *reinterpret_cast<float4 *>(L.v + e) = vv;
+        // Every load of the tile is issued before the first LDS store, so the
+        // tile costs one memory round trip (chunk * hd <= 4096 floats: at most
+        // kKvPer float4 of K and of V per thread). Indexes past the tile re-read
+        // its last float4 (in bounds); those registers are not stored.
+        const int last = nk * hd / 4 - 1;
+        float4 r[2 * kKvPer];  // K then V, one array (kept in registers)
+#pragma unroll
+        for (int i = 0; i < kKvPer; ++i) {
+            const int e4 = min(tid + i * kThreads, last);
+            r[i] = kb[e4];
+            r[kKvPer + i] = vb[e4];
+        }
+#pragma unroll
+        for (int i = 0; i < kKvPer; ++i) {
+            const int e4 = tid + i * kThreads;
+            if (e4 <= last) {
+                const int e = 4 * e4, j = e / hd, d = e - j * hd;
+                float *kd = L.k + j * (hd + 1) + d;
+                kd[0] = r[i].x;
+                kd[1] = r[i].y;
+                kd[2] = r[i].z;
+                kd[3] = r[i].w;
+                *reinterpret_cast<float4 *>(L.v + e) = r[kKvPer + i];
+            }
         }
         __syncthreads();
         for (int e = tid; e < G * nk; e += kThreads) {
