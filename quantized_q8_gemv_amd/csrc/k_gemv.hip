@@ -728,6 +728,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) {
 // takes pair u % PC of row u / PC, so its accumulator stays on one row; in
 // LDS a tile keeps a row stride of PC pairs.
 constexpr int kTilesPerWg = 8;
+constexpr int kMaxX4 = 10;   // float4 of one activation chunk per thread (chunks of <= 160 pairs)
 
 __device__ inline int chunk_pairs(const GemvShape &sh, int c) { return min(sh.PC, sh.P - c * sh.PC); }
 
@@ -799,14 +800,32 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
     int row0 = int(blockIdx.x) * sh.NR;
     int nrows = min(sh.NR, a.N - row0);
     WStage st;
+    // The next chunk's activations are loaded into registers while the
+    // current chunk's tiles are computed (indexes past a short last chunk
+    // re-read its last float4; those registers are not stored).
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 xr[kMaxX4];
+    {
+        const int last = chunk_pairs(sh, 0) * 16 - 1;
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.x);
+#pragma unroll
+        for (int i = 0; i < kMaxX4; ++i) xr[i] = src[min(tid + i * kThreads, last)];
+    }
     ctile_issue(a.W, sh, row0, nrows, 0, st);
     for (int ch = 0; ch < nchunks; ++ch) {
         const int pcc = chunk_pairs(sh, ch);
         __syncthreads();  // the previous chunk's activations are no longer read
         const int n4 = pcc * 16;
-        for (int e = tid; e < n4; e += kThreads) {
-            const float4 v = *reinterpret_cast<const float4 *>(a.x + size_t(ch) * sh.PC * kPairWeights + size_t(e) * 4);
-            *reinterpret_cast<float4 *>(xs + (e >> 4) * kXPad + (e & 15) * 4) = v;
+#pragma unroll
+        for (int i = 0; i < kMaxX4; ++i) {
+            const int e = tid + i * kThreads;
+            if (e < n4) *reinterpret_cast<f32x4 *>(xs + (e >> 4) * kXPad + (e & 15) * 4) = xr[i];
+        }
+        if (ch + 1 < nchunks) {
+            const int last = chunk_pairs(sh, ch + 1) * 16 - 1;
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(a.x + size_t(ch + 1) * sh.PC * kPairWeights);
+#pragma unroll
+            for (int i = 0; i < kMaxX4; ++i) xr[i] = src[min(tid + i * kThreads, last)];
         }
 #pragma unroll
         for (int k = 0; k < kTilesPerWg; ++k) {
@@ -1075,6 +1094,7 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
     if (T == 1) {
         if (a.sh.PC != a.sh.P && !norm_w) {  // large K: chunk-outer walk
             a.sh = chunked_shape(a.sh);
+            if (a.sh.PC * 16 > kMaxX4 * kThreads) return hipErrorInvalidValue;  // activation chunk > registers
             const size_t lds = lds1c_bytes(a.sh);
             const int ntiles = (N + a.sh.NR - 1) / a.sh.NR;
             const int g = std::max(grid1(ntiles, lds), (ntiles + kTilesPerWg - 1) / kTilesPerWg);
