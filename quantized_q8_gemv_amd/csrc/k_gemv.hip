@@ -632,7 +632,45 @@ __device__ void tile_run1(const CoreArgs &c, const Lds1 &l, int nrows, bool vec,
 
 __device__ inline int tile_rows(const CoreArgs &c) { return min(c.sh.NR, c.N - c.row0); }
 
-// q/k/v with rope and the KV write, T = 1.
+// The workgroup's tiles blockIdx.x, +G, +2G, ... (G = gridDim.x) with two
+// tiles' weights in flight: tile t + 2G is issued as soon as tile t's
+// weights are in LDS, into the registers tile t used (two register stages,
+// alternating). The activation row is staged while the first two tiles load.
+// epi(tile, rows) consumes outv after each tile.
+template <bool MULTI, class Epi>
+__device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, int ntiles, Epi &&epi) {
+    const int G = int(gridDim.x);
+    auto at = [&](int t, CoreArgs &x, int &nr, bool &v) {
+        x = c;
+        x.row0 = t * c.sh.NR;
+        nr = t < ntiles ? tile_rows(x) : 0;
+        v = nr > 0 ? tile_vec(x, nr) : false;
+    };
+    int t = blockIdx.x;
+    CoreArgs ca, cb, n;
+    int na, nb, nn;
+    bool va, vb, nv;
+    at(t, ca, na, va);
+    at(t + G, cb, nb, vb);
+    WStage sa, sb;
+    if (na > 0) stage_issue(ca, na, 0, va, sa);
+    if (nb > 0) stage_issue(cb, nb, 0, vb, sb);
+    stage_row1(c, l);
+    while (t < ntiles) {
+        at(t + 2 * G, n, nn, nv);
+        tile_run1<MULTI>(ca, l, na, va, sa, n, nn, nv, nn > 0);
+        epi(ca, na);
+        ca = n; na = nn; va = nv;
+        t += G;
+        if (t >= ntiles) break;
+        at(t + 2 * G, n, nn, nv);
+        tile_run1<MULTI>(cb, l, nb, vb, sb, n, nn, nv, nn > 0);
+        epi(cb, nb);
+        cb = n; nb = nn; vb = nv;
+        t += G;
+    }
+}
+
 template <bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -699,24 +737,10 @@ __global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) {
     CoreArgs c{};
     c.W[0] = a.wg; c.W[1] = a.wu; c.nmat = 2; c.sh = a.sh; c.N = a.F; c.Tc = 1;
     c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    int tile = blockIdx.x;
-    c.row0 = tile * a.sh.NR;
-    int nrows = tile_rows(c);
-    bool vec = tile_vec(c, nrows);
-    WStage st;
-    stage_issue(c, nrows, 0, vec, st);
-    stage_row1(c, l);
-    for (; tile < ntiles; tile += gridDim.x) {
-        const bool has_next = tile + int(gridDim.x) < ntiles;
-        CoreArgs n = c;
-        n.row0 = (tile + gridDim.x) * a.sh.NR;
-        const int nn = has_next ? tile_rows(n) : 0;
-        const bool nvec = has_next ? tile_vec(n, nn) : false;
-        tile_run1<MULTI>(c, l, nrows, vec, st, n, nn, nvec, has_next);
+    walk_tiles2<MULTI>(c, l, ntiles, [&](const CoreArgs &t, int nrows) {
         for (int r = threadIdx.x; r < nrows; r += kThreads)
-            a.h[c.row0 + r] = silu(l.outv[r]) * l.outv[a.sh.NR + r];
-        c = n; nrows = nn; vec = nvec;
-    }
+            a.h[t.row0 + r] = silu(l.outv[r]) * l.outv[a.sh.NR + r];
+    });
 }
 
 // Large K (several chunks), no norm: chunk-outer, tile-inner. Only one
@@ -885,26 +909,12 @@ __global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
     CoreArgs c{};
     c.W[0] = a.W; c.nmat = 1; c.sh = a.sh; c.N = a.N; c.Tc = 1;
     c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    int tile = blockIdx.x;
-    c.row0 = tile * a.sh.NR;
-    int nrows = tile_rows(c);
-    bool vec = tile_vec(c, nrows);
-    WStage st;
-    stage_issue(c, nrows, 0, vec, st);
-    stage_row1(c, l);
-    for (; tile < ntiles; tile += gridDim.x) {
-        const bool has_next = tile + int(gridDim.x) < ntiles;
-        CoreArgs n = c;
-        n.row0 = (tile + gridDim.x) * a.sh.NR;
-        const int nn = has_next ? tile_rows(n) : 0;
-        const bool nvec = has_next ? tile_vec(n, nn) : false;
-        tile_run1<MULTI>(c, l, nrows, vec, st, n, nn, nvec, has_next);
+    walk_tiles2<MULTI>(c, l, ntiles, [&](const CoreArgs &t, int nrows) {
         for (int r = threadIdx.x; r < nrows; r += kThreads) {
-            float *dst = a.y + c.row0 + r;
+            float *dst = a.y + t.row0 + r;
             *dst = a.accumulate ? *dst + l.outv[r] : l.outv[r];
         }
-        c = n; nrows = nn; vec = nvec;
-    }
+    });
 }
 
 template <bool MULTI>
