@@ -71,7 +71,6 @@ struct Cfg {
     static constexpr int B_HALVES = TN * LPAD;
     static constexpr size_t BUF = sizeof(_Float16) * (2 * A_HALVES + B_HALVES) + sizeof(float) * TN * 2;
     static constexpr size_t LDS = 2 * BUF;
-    static constexpr int STAGES = 1;                     // K steps of global loads in flight
     static_assert(AP >= 1 && BU >= 1 && MS >= 1 && NS >= 1, "tile too small");
     static_assert(BUF % 16 == 0, "LDS buffer alignment");
     static_assert(size_t(TM) * WN * sizeof(float) <= LDS, "gate/up exchange fits");
@@ -258,7 +257,7 @@ __device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf) {
     }
 }
 
-template <int EPI, int TM, int TN, bool A32>
+template <int EPI, int TM, int TN, bool A32, int ST>
 __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
     using C = Cfg<TM, TN>;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -291,17 +290,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < C::NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // S register stages: the loads of steps ks+1 .. ks+S-1 are in flight while
+    // S register stages: the loads of steps ks+1 .. ks+S are in flight while
     // step ks is computed (the loop is unrolled by S so each stage is a fixed
     // set of registers).
-    constexpr int S = C::STAGES;
+    constexpr int S = ST;
     const int nsteps = a.K / GK;
     GSrc<TM, TN> src;
     g_setup<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, src);
+    // Every stage issues its loads unconditionally (steps past the end
+    // re-read the last step, whose registers are never stored): with no
+    // branch around them the compiler can wait for the oldest stage alone
+    // instead of draining every load in flight.
     GRegs<TM, TN> regs[S];
 #pragma unroll
-    for (int j = 0; j < S; ++j)
-        if (j < nsteps) g_load<A32, TM, TN>(src, j, regs[j]);
+    for (int j = 0; j < S; ++j) g_load<A32, TM, TN>(src, min(j, nsteps - 1), regs[j]);
     for (int k0 = 0; k0 < nsteps; k0 += S) {
 #pragma unroll
         for (int j = 0; j < S; ++j) {
@@ -310,7 +312,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
             const GBuf bf = gbuf<TM, TN>(smem, ks & 1);
             g_store<A32, TM, TN>(regs[j], bf);
             __syncthreads();
-            if (ks + S < nsteps) g_load<A32, TM, TN>(src, ks + S, regs[j]);
+            if (S == 1) {
+                if (ks + 1 < nsteps) g_load<A32, TM, TN>(src, ks + 1, regs[j]);
+            } else {
+                g_load<A32, TM, TN>(src, min(ks + S, nsteps - 1), regs[j]);
+            }
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
                 half8 bfr[C::NS];
@@ -731,21 +737,34 @@ bool large_tiles(int T, int n_tiles_large) {
     return long((T + 63) / 64) * n_tiles_large >= 256;
 }
 
+// K steps of global loads in flight per workgroup: one when the grid fills
+// the chip (more registers would cost occupancy), several when it is small
+// (short prompts of small models: a few workgroups each walking all of K,
+// where every step would otherwise wait a full memory round trip).
+constexpr int kSmallGridStages = 4;
+
+template <int EPI, int TM, int TN, bool A32, int ST>
+hipError_t launch_st(const GemmArgs &a, dim3 grid, hipStream_t s) {
+    using C = Cfg<TM, TN>;
+    if (C::LDS > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_q8<EPI, TM, TN, A32, ST>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_gemm_q8<EPI, TM, TN, A32, ST>), grid, dim3(kThreads), C::LDS, s, a);
+    return hipGetLastError();
+}
+
 template <int EPI, int TM, int TN, bool A32>
 hipError_t launch_cfg(const GemmArgs &a, int ytiles, hipStream_t s) {
-    using C = Cfg<TM, TN>;
     // buffer resources address < 2 GiB (offsets past that read as zeros)
     if (size_t(a.T) * a.K * 4 >= kOutOfRange) return hipErrorInvalidValue;
     for (int i = 0; i < 3; ++i)
         if (a.W[i] && size_t(a.Nm[i]) * a.rowbytes >= kOutOfRange) return hipErrorInvalidValue;
-    if (C::LDS > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_q8<EPI, TM, TN, A32>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
-        if (e != hipSuccess) return e;
-    }
-    dim3 grid((a.T + TM - 1) / TM, ytiles);
-    hipLaunchKernelGGL((k_gemm_q8<EPI, TM, TN, A32>), grid, dim3(kThreads), C::LDS, s, a);
-    return hipGetLastError();
+    const dim3 grid((a.T + TM - 1) / TM, ytiles);
+    if constexpr (TM == 32)
+        if (long(grid.x) * grid.y < 256) return launch_st<EPI, TM, TN, A32, kSmallGridStages>(a, grid, s);
+    return launch_st<EPI, TM, TN, A32, 1>(a, grid, s);
 }
 
 template <int EPI, bool A32>
