@@ -356,11 +356,12 @@ def main():
         eprint(f"[bench] device copy: {copy_bandwidth(torch):.0f} GB/s (1 GiB, read + write)")
         return
 
+    import numpy as np
     import torch
 
     import synth
     from quantized_q8_gemv_amd import q8l as C
-    from quantized_q8_gemv_amd.model import Q8Model
+    from quantized_q8_gemv_amd.model import Q8Model, host_mapped_u32
 
     w, model, prompt = synth.workload_inputs(args.config)
     s = model.shape
@@ -375,16 +376,26 @@ def main():
     gm = Q8Model(synth.shape_fields(s), model.tensors, device="cuda:0")
     torch.cuda.synchronize()
 
+    # The greedy id goes to pinned host memory that the last kernel writes
+    # directly: each step's 4-byte readback is a stream synchronisation.
+    am_host, am_dev = host_mapped_u32()
+    stream = torch.cuda.current_stream()
+    tok = np.zeros(1, dtype=np.uint32)
+    prompt_u32 = np.ascontiguousarray(np.asarray(prompt, dtype=np.uint32))
+
     def generation():
         t0 = time.perf_counter()
-        st = gm.forward_async(prompt, 0)
+        st = gm.forward_async(prompt_u32, 0, argmax_out=am_dev)
         assert st == C.Q8L_OK, st
-        nxt = int(gm.argmax.item())
+        stream.synchronize()
+        nxt = int(am_host[0])
         t1 = time.perf_counter()
         for k in range(steps):
-            st = gm.forward_async([nxt], len(prompt) + k)
+            tok[0] = nxt
+            st = gm.forward_async(tok, len(prompt) + k, argmax_out=am_dev)
             assert st == C.Q8L_OK, st
-            nxt = int(gm.argmax.item())
+            stream.synchronize()
+            nxt = int(am_host[0])
         t2 = time.perf_counter()
         return t1 - t0, t2 - t1
 

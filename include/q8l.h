@@ -155,7 +155,10 @@ q8l_status q8l_finalize(q8l_model *m, void *stream);
  * forward(tokens, index_pos): run T = n_tokens tokens starting at position
  * index_pos and write the logits of the LAST position to logits_dev
  * (f32[n_vocab], device) and, if argmax_dev is not NULL, the index of the
- * largest logit (lowest index on ties) to *argmax_dev (device uint32).
+ * largest logit (lowest index on ties) to *argmax_dev (a uint32 the device
+ * can address: device memory, or pinned host memory by its device address,
+ * which the last kernel writes directly, so a per-token readback needs no
+ * copy).
  * `tokens_host` is host memory (read before the call returns).
  * Checks, in this order, before anything is enqueued or changed:
  *   1. n_tokens >= 1, tokens < n_vocab, index_pos >= 0, logits_dev != NULL

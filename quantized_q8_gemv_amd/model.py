@@ -5,6 +5,7 @@ Argument marshalling only: the forward pass runs in libq8l.so's kernels.
 
 from __future__ import annotations
 
+import ctypes
 from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
@@ -70,11 +71,18 @@ class Q8Model:
         if st != C.Q8L_OK:
             raise C.Q8LError(st, C.q8l_last_error(self.handle))
 
-    def forward_async(self, tokens: Sequence[int], index_pos: int, stream=None) -> int:
-        """Enqueue forward(tokens, index_pos); returns the status (no raise)."""
-        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).astype(np.uint32))
+    def forward_async(self, tokens: Sequence[int], index_pos: int, stream=None, argmax_out=None) -> int:
+        """Enqueue forward(tokens, index_pos); returns the status (no raise).
+
+        ``argmax_out`` (default: the device tensor ``self.argmax``) may be the
+        device address of pinned host memory (``host_mapped_u32``): the last
+        kernel then writes the greedy id straight to the host."""
+        if isinstance(tokens, np.ndarray) and tokens.dtype == np.uint32 and tokens.flags.c_contiguous:
+            toks = tokens
+        else:
+            toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64).astype(np.uint32))
         return C.q8l_forward(self.handle, toks, int(toks.size), int(index_pos), self.logits,
-                             self.argmax, stream)
+                             self.argmax if argmax_out is None else argmax_out, stream)
 
     def forward(self, tokens: Sequence[int], index_pos: int, stream=None) -> Tuple[np.ndarray, int]:
         """Run forward and wait; returns (f32 logits on the host, argmax)."""
@@ -103,6 +111,23 @@ class Q8Model:
             self.close()
         except Exception:
             pass
+
+
+def host_mapped_u32():
+    """A pinned host int32 tensor of one element and its device address.
+
+    The device writes it directly (pinned host memory is mapped into the
+    device's address space), so reading a per-token result needs only a stream
+    synchronisation, no copy."""
+    import torch
+
+    t = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded (same soname)
+    dptr = ctypes.c_void_p()
+    err = hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
+    if err != 0 or not dptr.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({err})")
+    return t, int(dptr.value)
 
 
 _DTYPES = {"f32": C.Q8L_F32, "q8_0": C.Q8L_Q8_0, "q4_k": C.Q8L_Q4_K, "q6_k": C.Q8L_Q6_K}

@@ -215,3 +215,25 @@ def test_big_gqa_full_depth_prefill_equals_decode_chain(big_full):
     for i, t in enumerate(toks):
         step, _ = gm.forward([t], i)
     assert_logits_close(step, full, "7b full: prefill 64 vs 64 single-token steps")
+
+
+def test_argmax_to_host_mapped_memory(tiny):
+    """forward's argmax written by the last kernel into pinned host memory (by
+    its device address) equals the argmax written to device memory, for the
+    prefill and for decode steps through the captured graph."""
+    from quantized_q8_gemv_amd.model import host_mapped_u32
+
+    m, prompt, gm = tiny
+    am_host, am_dev = host_mapped_u32()
+    stream = torch.cuda.current_stream()
+    nxt = None
+    for k in range(6):
+        toks, pos = (prompt, 0) if k == 0 else ([nxt], len(prompt) + k - 1)
+        am_host[0] = -1
+        assert gm.forward_async(toks, pos, argmax_out=am_dev) == 0
+        stream.synchronize()
+        host_id = int(am_host[0])
+        ref = int(np.argmax(gm.logits.cpu().numpy()))
+        log(f"host-mapped argmax step {k}: {host_id} (logits argmax {ref})")
+        assert host_id == ref
+        nxt = host_id
