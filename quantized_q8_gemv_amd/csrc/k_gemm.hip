@@ -41,7 +41,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int GK = 64;     // weights per K step (two Q8_0 blocks)
 constexpr int LPAD = 72;   // halves per LDS row (64 + 8)
 
-enum GemmEpi { G_STORE = 0, G_ACCUM = 1, G_QKV = 2, G_GATEUP = 3 };
+enum GemmEpi { G_STORE = 0, G_ACCUM = 1, G_QKV = 2, G_GATEUP = 3, G_PART = 4 };
 
 struct GemmArgs {
     const void *A;         // A32: f32 [T][K]; else f16 hi plane [T][K] then lo plane [T][K]
@@ -59,6 +59,9 @@ struct GemmArgs {
     int rope_neox;         // 1: q and k are written unrotated
     // G_GATEUP: h = silu(gate) * up as f16 hi plane [T][F] then lo plane
     _Float16 *h;
+    // G_PART: K split over gridDim.z slices; slice z writes its sum to part[z][T][N]
+    float *part;
+    int splits;
 };
 
 template <int TM, int TN>
@@ -294,7 +297,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
     // step ks is computed (the loop is unrolled by S so each stage is a fixed
     // set of registers).
     constexpr int S = ST;
-    const int nsteps = a.K / GK;
+    int kfirst = 0, nsteps = a.K / GK;
+    if (EPI == G_PART) {  // this workgroup's slice of the K steps
+        const int all = nsteps;
+        kfirst = int(blockIdx.z) * all / a.splits;
+        nsteps = (int(blockIdx.z) + 1) * all / a.splits - kfirst;
+    }
     GSrc<TM, TN> src;
     g_setup<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, src);
     // Every stage issues its loads unconditionally (steps past the end
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
     // instead of draining every load in flight.
     GRegs<TM, TN> regs[S];
 #pragma unroll
-    for (int j = 0; j < S; ++j) g_load<A32, TM, TN>(src, min(j, nsteps - 1), regs[j]);
+    for (int j = 0; j < S; ++j) g_load<A32, TM, TN>(src, kfirst + min(j, nsteps - 1), regs[j]);
     for (int k0 = 0; k0 < nsteps; k0 += S) {
 #pragma unroll
         for (int j = 0; j < S; ++j) {
@@ -313,9 +321,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
             g_store<A32, TM, TN>(regs[j], bf);
             __syncthreads();
             if (S == 1) {
-                if (ks + 1 < nsteps) g_load<A32, TM, TN>(src, ks + 1, regs[j]);
+                if (ks + 1 < nsteps) g_load<A32, TM, TN>(src, kfirst + ks + 1, regs[j]);
             } else {
-                g_load<A32, TM, TN>(src, min(ks + S, nsteps - 1), regs[j]);
+                g_load<A32, TM, TN>(src, kfirst + min(ks + S, nsteps - 1), regs[j]);
             }
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
@@ -410,6 +418,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
                         else
                             a.kc[(size_t(row / a.hd) * a.max_seq + a.st->slot + t) * a.hd + d] = r;
                     }
+                } else if (EPI == G_PART) {
+                    if (m0 + m >= a.T || c >= nvalid[0]) continue;
+                    a.part[(size_t(blockIdx.z) * a.T + m0 + m) * a.Nm[0] + row0 + c] = v;
                 } else {
                     if (m0 + m >= a.T || c >= nvalid[0]) continue;
                     float *dst = a.Y + size_t(m0 + m) * a.Nm[0] + row0 + c;
@@ -697,20 +708,35 @@ __global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
 
 // u = x / sqrt(mean(x^2) + eps) * w for each token row, written as the f16
 // hi plane [T][K] followed by the lo plane. One workgroup per row.
-__global__ __launch_bounds__(kThreads) void k_rms_split(const float *x, int T, int K, const float *w,
-                                                        float eps, _Float16 *u) {
+// With splits > 0 the residual add of a split-K product happens here first:
+// x += part[0] + part[1] + ... (that order), written back to x. With u NULL
+// only that add is done.
+__global__ __launch_bounds__(kThreads) void k_rms_split(float *x, int T, int K, const float *w,
+                                                        float eps, _Float16 *u, const float *part,
+                                                        int splits) {
     __shared__ float red[4];
     const size_t row = blockIdx.x;
-    const float4 *xr = reinterpret_cast<const float4 *>(x + row * K);
+    float4 *xr = reinterpret_cast<float4 *>(x + row * K);
     const int n4 = K / 4;
     float ss = 0.f;
     for (int e = threadIdx.x; e < n4; e += kThreads) {
-        const float4 v = xr[e];
+        float4 v = xr[e];
+        if (splits > 0) {
+            const float4 *pr = reinterpret_cast<const float4 *>(part) + row * n4 + e;
+            float4 p = pr[0];
+            for (int z = 1; z < splits; ++z) {
+                const float4 q = pr[size_t(z) * T * n4];
+                p.x += q.x; p.y += q.y; p.z += q.z; p.w += q.w;
+            }
+            v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+            xr[e] = v;
+        }
         ss = fmaf(v.x, v.x, ss);
         ss = fmaf(v.y, v.y, ss);
         ss = fmaf(v.z, v.z, ss);
         ss = fmaf(v.w, v.w, ss);
     }
+    if (!u) return;
     ss = block_sum(ss, red);
     const float r = 1.0f / sqrtf(ss / static_cast<float>(K) + eps);
     const size_t plane = size_t(T) * K;
@@ -761,9 +787,9 @@ hipError_t launch_cfg(const GemmArgs &a, int ytiles, hipStream_t s) {
     if (size_t(a.T) * a.K * 4 >= kOutOfRange) return hipErrorInvalidValue;
     for (int i = 0; i < 3; ++i)
         if (a.W[i] && size_t(a.Nm[i]) * a.rowbytes >= kOutOfRange) return hipErrorInvalidValue;
-    const dim3 grid((a.T + TM - 1) / TM, ytiles);
+    const dim3 grid((a.T + TM - 1) / TM, ytiles, EPI == G_PART ? a.splits : 1);
     if constexpr (TM == 32)
-        if (long(grid.x) * grid.y < 256) return launch_st<EPI, TM, TN, A32, kSmallGridStages>(a, grid, s);
+        if (long(grid.x) * grid.y * grid.z < 256) return launch_st<EPI, TM, TN, A32, kSmallGridStages>(a, grid, s);
     return launch_st<EPI, TM, TN, A32, 1>(a, grid, s);
 }
 
@@ -810,10 +836,26 @@ GemmArgs gemm_base(const void *A, int T, int K) {
 
 }  // namespace
 
-hipError_t launch_rms_split(const float *x, int T, int K, const float *w, float eps, _Float16 *u,
-                            hipStream_t s) {
-    hipLaunchKernelGGL(k_rms_split, dim3(T), dim3(kThreads), 0, s, x, T, K, w, eps, u);
+hipError_t launch_rms_split(float *x, int T, int K, const float *w, float eps, _Float16 *u,
+                            const float *part, int splits, hipStream_t s) {
+    hipLaunchKernelGGL(k_rms_split, dim3(T), dim3(kThreads), 0, s, x, T, K, w, eps, u, part, splits);
     return hipGetLastError();
+}
+
+int gemm_splitk(int N, int K, int T) {
+    if (T > kSplitKMaxTokens) return 1;
+    const long wgs = long(row_tiles(T, 32)) * row_tiles(N, 64);
+    if (wgs >= 256 || large_tiles(T, row_tiles(N, 128))) return 1;
+    const long want = (256 + wgs - 1) / wgs;
+    return int(std::max(1L, std::min<long>({want, long(kSplitKMax), long(K / GK)})));
+}
+
+hipError_t launch_gemm_part(const uint8_t *W, int N, int K, const _Float16 *A, int T, int splits, float *part,
+                            hipStream_t s) {
+    if (splits < 1 || splits > kSplitKMax || splits > K / GK || T > kSplitKMaxTokens) return hipErrorInvalidValue;
+    GemmArgs a = gemm_base(A, T, K);
+    a.W[0] = W; a.Nm[0] = N; a.part = part; a.splits = splits;
+    return launch_cfg<G_PART, 32, 64, false>(a, row_tiles(N, 64), s);
 }
 
 hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, bool a_split, int T,

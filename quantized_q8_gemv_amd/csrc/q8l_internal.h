@@ -135,7 +135,16 @@ size_t lmhead_partials_bytes(int V, int K);
 // MFMA matrix-matrix path (prefill with T >= kGemmMinTokens tokens). Activations
 // are passed as an f16 hi plane [T][K] followed by an f16 lo plane (a_split),
 // or as f32 [T][K].
-hipError_t launch_rms_split(const float *x, int T, int K, const float *w, float eps, _Float16 *u,
+hipError_t launch_rms_split(float *x, int T, int K, const float *w, float eps, _Float16 *u,
+                            const float *part, int splits, hipStream_t s);
+// Split-K for short prompts: when the plain GEMM would launch only a few
+// workgroups (each walking all of K), the K steps are split over
+// gemm_splitk(N, K, T) > 1 slices that write partial sums part[z][T][N];
+// launch_rms_split (or its add-only form, u = NULL) then adds them to x.
+constexpr int kSplitKMax = 8;
+constexpr int kSplitKMaxTokens = 1024;
+int gemm_splitk(int N, int K, int T);
+hipError_t launch_gemm_part(const uint8_t *W, int N, int K, const _Float16 *A, int T, int splits, float *part,
                             hipStream_t s);
 hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
                               int accumulate, float *Y, hipStream_t s);

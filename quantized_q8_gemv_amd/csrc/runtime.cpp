@@ -41,7 +41,7 @@ const char *kVersion = "q8l 0.1 (gfx950)";
 size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t state, counters, rope, tok, kc, vc, x, q, att, h, u, logits, lm_part, attn_part, total;
+    size_t state, counters, rope, tok, kc, vc, x, q, att, h, u, logits, lm_part, attn_part, kpart, total;
     size_t kv_layer;  // floats per layer in kc (and vc)
     int max_splits;
 };
@@ -96,6 +96,7 @@ Layout make_layout(const q8l_config *c) {
     L.logits = take(size_t(c->n_vocab) * 4);
     L.lm_part = take(std::max(lmhead_partials_bytes(c->n_vocab, c->n_embd), size_t(8)));
     L.attn_part = take(size_t(c->n_head) * L.max_splits * (hd + 2) * 4);
+    L.kpart = take(size_t(kSplitKMax) * kSplitKMaxTokens * H * 4);  // split-K partial sums (short prompts)
     L.total = off;
     return L;
 }
@@ -178,10 +179,13 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
     const bool gemm = T >= kGemmMinTokens;  // MFMA matrix-matrix path for prompts
     _Float16 *u = m->at<_Float16>(m->lay.u);
     _Float16 *att_s = m->at<_Float16>(m->lay.att), *h_s = m->at<_Float16>(m->lay.h);
+    float *kpart = m->at<float>(m->lay.kpart);
+    int pend = 0;  // split-K partial sums not yet added to x (the next norm kernel adds them)
     for (int l = 0; l < m->cfg.n_layer; ++l) {
         const LayerPtrs w = m->layer(l);
         if (gemm) {
-            if ((e = launch_rms_split(x, T, d.H, w.attn_norm, d.eps, u, s)) != hipSuccess) return e;
+            if ((e = launch_rms_split(x, T, d.H, w.attn_norm, d.eps, u, kpart, pend, s)) != hipSuccess) return e;
+            pend = 0;
             if ((e = launch_gemm_qkv(d, w, u, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
         } else {
             if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
@@ -211,17 +215,24 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             if (w.fo != F_Q8_0)
                 e = gemm ? launch_gemm_kq(w.fo, w.wo, d.H, QD, att_s, true, T, 1, x, s)
                          : launch_gemm_kq(w.fo, w.wo, d.H, QD, att, false, T, 1, x, s);
+            else if (gemm && (pend = gemm_splitk(d.H, QD, T)) > 1)
+                e = launch_gemm_part(w.wo, d.H, QD, att_s, T, pend, kpart, s);
             else if (gemm)
-                e = launch_gemm_matmul(w.wo, d.H, QD, att_s, true, T, 1, x, s);
+                pend = 0, e = launch_gemm_matmul(w.wo, d.H, QD, att_s, true, T, 1, x, s);
             else
                 e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s);
             if (e != hipSuccess) return e;
         }
         if (gemm) {
-            if ((e = launch_rms_split(x, T, d.H, w.ffn_norm, d.eps, u, s)) != hipSuccess) return e;
+            if ((e = launch_rms_split(x, T, d.H, w.ffn_norm, d.eps, u, kpart, pend, s)) != hipSuccess) return e;
+            pend = 0;
             if ((e = launch_gemm_gateup(d, w, u, h_s, T, s)) != hipSuccess) return e;
-            e = w.fd != F_Q8_0 ? launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s)
-                               : launch_gemm_matmul(w.wd, d.H, d.F, h_s, true, T, 1, x, s);
+            if (w.fd != F_Q8_0)
+                e = launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s);
+            else if ((pend = gemm_splitk(d.H, d.F, T)) > 1)
+                e = launch_gemm_part(w.wd, d.H, d.F, h_s, T, pend, kpart, s);
+            else
+                pend = 0, e = launch_gemm_matmul(w.wd, d.H, d.F, h_s, true, T, 1, x, s);
         } else {
             if ((e = launch_gateup(d, w, x, h, T, s)) != hipSuccess) return e;
             if (w.fd == F_Q8_0)
@@ -233,6 +244,8 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
         }
         if (e != hipSuccess) return e;
     }
+    if (pend > 0 && (e = launch_rms_split(x, T, d.H, nullptr, d.eps, nullptr, kpart, pend, s)) != hipSuccess)
+        return e;
     const uint8_t *wout = m->cfg.tied_output ? m->tok_embd : m->output;
     if ((e = launch_lmhead(d, wout, m->out_norm, x + size_t(T - 1) * d.H, st,
                            m->at<float>(m->lay.lm_part), s)) != hipSuccess)
