@@ -48,6 +48,9 @@ PAGES_DECODE_MS = {"C2": 2.6}
 KIND_NAMES = ["embed", "qkv_rope_kv", "attn_decode", "oproj_residual", "gateup_silu",
               "down_residual", "lmhead", "argmax_finish"]
 NKINDS = len(KIND_NAMES)
+KIND_SOURCES = {"embed": "quantized_q8_gemv_amd/csrc/k_misc.hip", "attn_decode": "quantized_q8_gemv_amd/csrc/k_attn.hip"}
+for _k in KIND_NAMES:
+    KIND_SOURCES.setdefault(_k, "quantized_q8_gemv_amd/csrc/k_gemv.hip")
 # rocprofv3 PMC summaries of the decode kernels (FETCH_SIZE and WRITE_SIZE per
 # dispatch, scaled by the same counters on a copy of known size); a summary
 # counts only while the kernel source it was taken with is unchanged.
@@ -91,6 +94,84 @@ def measured_traffic(config, kind):
             return None
         return int(f["bytes_per_launch"])
     return None
+
+
+def pmc_summary(fetch_dir, write_dir, config="C2"):
+    """Per-launch HBM traffic of each decode kernel kind from two rocprofv3
+    counter runs of this script (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; CSV
+    output). Each counter is scaled by what it reads for the 1 GiB device copy
+    of copy_bandwidth() (the largest __amd_rocclr_copyBuffer dispatches).
+    Dispatches are assigned to kinds by symbol; the o-projection and the down
+    projection share a symbol at some shapes and are told apart by what ran
+    just before them (the attention kernels, or gate/up). Prints a markdown
+    table and the `traffic:` lines read by measured_traffic()."""
+    import csv
+    import glob
+
+    import synth
+    _, model, prompt = synth.workload_inputs(config)
+    s = model.shape
+    syms = kernel_symbols(s)
+    alg_bytes = kernel_bytes(s, len(prompt) + 1)  # attention at the first decode step
+
+    def load(d, counter):
+        rows = []
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if r.get("Counter_Name") == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        per = {}
+        for did, name, v in rows:  # a counter may come in several rows per dispatch
+            n0, v0 = per.get(did, (name, 0.0))
+            per[did] = (n0, v0 + v)
+        return [(did, n, v) for did, (n, v) in sorted(per.items())]
+
+    def kinds(disp):
+        out, prev = [], ""
+        for did, name, v in disp:
+            short = name.replace("void ", "").replace("q8l::(anonymous namespace)::", "").replace("q8l::", "")
+            short = short.split("(")[0].strip()
+            kind = None
+            for k, sym in enumerate(syms):
+                if short == sym:
+                    kind = KIND_NAMES[k]
+            if short == syms[3] and short == syms[5]:
+                kind = "oproj_residual" if prev.startswith("k_attn") else "down_residual"
+            out.append((kind, short, v))
+            prev = short
+        return out
+
+    res = {}
+    scale = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        disp = load(d, counter)
+        copies = sorted(v for _, n, v in disp if "copyBuffer" in n)
+        big = [v for v in copies if v >= 0.4 * copies[-1]] if copies else []
+        scale[counter] = (1 << 30) / (statistics.mean(big) * 1024) if big else float("nan")
+        acc = {}
+        for kind, short, v in kinds(disp):
+            if kind:
+                acc.setdefault(kind, (short, []))[1].append(v)
+        for kind, (short, vals) in acc.items():
+            res.setdefault(kind, {"symbol": short})[counter] = (len(vals), statistics.mean(vals))
+    print(f"scale FETCH_SIZE {scale['FETCH_SIZE']:.4f}, WRITE_SIZE {scale['WRITE_SIZE']:.4f}")
+    print("| kind | symbol | dispatches | FETCH KiB | WRITE KiB | scaled bytes | algorithmic bytes | ratio |")
+    print("|---|---|---:|---:|---:|---:|---:|---:|")
+    lines = []
+    for kind in KIND_NAMES:
+        if kind not in res or "FETCH_SIZE" not in res[kind] or "WRITE_SIZE" not in res[kind]:
+            continue
+        r = res[kind]
+        n, f = r["FETCH_SIZE"]
+        _, w = r["WRITE_SIZE"]
+        b = int(round((f * scale["FETCH_SIZE"] + w * scale["WRITE_SIZE"]) * 1024))
+        alg = alg_bytes[KIND_NAMES.index(kind)]
+        print(f"| {kind} | `{r['symbol']}` | {n} | {f:.1f} | {w:.1f} | {b:,} | {alg:,} | "
+              f"{b / alg if alg else float('nan'):.2f} |")
+        src = KIND_SOURCES[kind]
+        lines.append(f"traffic: kind={kind} bytes_per_launch={b} source={src} sha256={source_digest(src)}")
+    print()
+    print("\n".join(lines))
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
@@ -339,6 +420,8 @@ def main():
                          "layers, as the pages' 4-bit file holds them)")
     ap.add_argument("--formats", action="store_true",
                     help="time the single matmul per block format (Q8_0, Q4_K, Q6_K) instead")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script; no GPU use")
     ap.add_argument("--kv-sweep", action="store_true",
                     help="decode cost against cache length on the 135M-shaped model instead "
                          "(one JSON line per length)")
@@ -346,6 +429,9 @@ def main():
     if args.gpus != 1:
         eprint(f"bench.py runs on one GPU: this build has no multi-GPU path (--gpus {args.gpus}).")
         sys.exit(2)
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, config=args.config)
+        return
     if args.kv_sweep:
         kv_sweep(args.kernel_reps)
         return

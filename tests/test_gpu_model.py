@@ -237,3 +237,17 @@ def test_argmax_to_host_mapped_memory(tiny):
         log(f"host-mapped argmax step {k}: {host_id} (logits argmax {ref})")
         assert host_id == ref
         nxt = host_id
+
+
+@pytest.mark.parametrize("plen", [6, 31, 64, 65, 300, 1024, 1025])
+def test_prompt_lengths_around_split_k(tiny, plen):
+    """Prompts on both sides of the split-K limits: short prompts split the
+    o and down products' K steps over several workgroups whose partial sums
+    the next norm kernel adds to the residual (the last layer's through the
+    add-only form); 1025 tokens take the plain accumulating GEMM. Logits of
+    the prefill and of 3 decode steps against the oracle."""
+    m, _, gm = tiny
+    prompt = synth.prompt_ids(m.shape.n_vocab, plen, 5)
+    ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 3, f"tiny {plen}+3")
+    log(f"tiny {plen}+3: max abs err {err:.3g}, near ties {ties}")
+    assert ties <= 1
