@@ -842,17 +842,30 @@ hipError_t launch_rms_split(float *x, int T, int K, const float *w, float eps, _
     return hipGetLastError();
 }
 
+// Split-K applies while the plain 32 x 64 grid has fewer than kSplitKWgs
+// workgroups. The slices bring it to about 256 workgroups (512 for rows of
+// 4096 weights or more, whose K walk is long), at least 2 slices, at most 8.
+// Measured at the 135M shape (K = 576 / 1536) and the 7B-class one
+// (K = 4096 / 14336) for prompts of 13 to 1024 tokens.
+constexpr int kSplitKWgs = 512;
+
+int gemm_splitk_max_tokens(int N) {
+    return std::min(kSplitKMaxTokens, 32 * ((kSplitKWgs - 1) / row_tiles(N, 64)));
+}
+
 int gemm_splitk(int N, int K, int T) {
-    if (T > kSplitKMaxTokens) return 1;
+    if (T > gemm_splitk_max_tokens(N)) return 1;
     const long wgs = long(row_tiles(T, 32)) * row_tiles(N, 64);
-    if (wgs >= 256 || large_tiles(T, row_tiles(N, 128))) return 1;
-    const long want = (256 + wgs - 1) / wgs;
+    if (wgs >= kSplitKWgs || large_tiles(T, row_tiles(N, 128))) return 1;
+    const long target = K >= 4096 ? 512 : 256;
+    const long want = std::max(2L, (target + wgs - 1) / wgs);
     return int(std::max(1L, std::min<long>({want, long(kSplitKMax), long(K / GK)})));
 }
 
 hipError_t launch_gemm_part(const uint8_t *W, int N, int K, const _Float16 *A, int T, int splits, float *part,
                             hipStream_t s) {
-    if (splits < 1 || splits > kSplitKMax || splits > K / GK || T > kSplitKMaxTokens) return hipErrorInvalidValue;
+    if (splits < 1 || splits > kSplitKMax || splits > K / GK || T > gemm_splitk_max_tokens(N))
+        return hipErrorInvalidValue;
     GemmArgs a = gemm_base(A, T, K);
     a.W[0] = W; a.Nm[0] = N; a.part = part; a.splits = splits;
     return launch_cfg<G_PART, 32, 64, false>(a, row_tiles(N, 64), s);

@@ -144,6 +144,9 @@ hipError_t launch_rms_split(float *x, int T, int K, const float *w, float eps, _
 constexpr int kSplitKMax = 8;
 constexpr int kSplitKMaxTokens = 1024;
 int gemm_splitk(int N, int K, int T);
+// Longest prompt for which an N-row product may be split: the partial-sum
+// scratch holds kSplitKMax * gemm_splitk_max_tokens(N) * N floats.
+int gemm_splitk_max_tokens(int N);
 hipError_t launch_gemm_part(const uint8_t *W, int N, int K, const _Float16 *A, int T, int splits, float *part,
                             hipStream_t s);
 hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, bool a_split, int T,

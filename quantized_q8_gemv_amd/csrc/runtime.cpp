@@ -96,7 +96,7 @@ Layout make_layout(const q8l_config *c) {
     L.logits = take(size_t(c->n_vocab) * 4);
     L.lm_part = take(std::max(lmhead_partials_bytes(c->n_vocab, c->n_embd), size_t(8)));
     L.attn_part = take(size_t(c->n_head) * L.max_splits * (hd + 2) * 4);
-    L.kpart = take(size_t(kSplitKMax) * kSplitKMaxTokens * H * 4);  // split-K partial sums (short prompts)
+    L.kpart = take(size_t(kSplitKMax) * std::max(1, gemm_splitk_max_tokens(int(H))) * H * 4);  // split-K partials
     L.total = off;
     return L;
 }

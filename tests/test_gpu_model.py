@@ -244,8 +244,9 @@ def test_prompt_lengths_around_split_k(tiny, plen):
     """Prompts on both sides of the split-K limits: short prompts split the
     o and down products' K steps over several workgroups whose partial sums
     the next norm kernel adds to the residual (the last layer's through the
-    add-only form); 1025 tokens take the plain accumulating GEMM. Logits of
-    the prefill and of 3 decode steps against the oracle."""
+    add-only form); at hidden size 576 prompts of up to 1024 tokens split,
+    1025 take the plain accumulating GEMM. Logits of the prefill and of 3
+    decode steps against the oracle."""
     m, _, gm = tiny
     prompt = synth.prompt_ids(m.shape.n_vocab, plen, 5)
     ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 3, f"tiny {plen}+3")
