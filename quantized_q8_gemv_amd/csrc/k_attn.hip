@@ -27,8 +27,6 @@
 
 namespace q8l {
 
-__host__ __device__ int attn_chunk(int hd) { return hd <= 64 ? 64 : 32; }
-
 namespace {
 
 struct DecodeLds {

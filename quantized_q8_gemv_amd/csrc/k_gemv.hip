@@ -45,6 +45,11 @@ struct CoreArgs {
     int ldx;
     const float *norm_w;
     float eps;
+    // Decode o-projection after a multi-split attention: the activation row is
+    // merged from the attention's split partials instead of read from X.
+    const float *mpart;      // [nh][msplits][mhd + 2]: (max, sum, unnormalised o)
+    int msplits, mhd;
+    const StepState *mst;    // active splits from the cache length
 };
 
 struct Lds {
@@ -413,6 +418,9 @@ struct MatmulArgs {
     GemvShape sh;
     int N, T, accumulate;
     float eps;
+    const float *mpart;      // decode only: merge x from attention partials (see CoreArgs)
+    int msplits, mhd;
+    const StepState *mst;
 };
 
 template <int MAXT, bool MULTI>
@@ -555,6 +563,49 @@ __device__ inline Lds1 carve1(uint8_t *smem, const GemvShape &sh, int nmat) {
     return l;
 }
 
+// The attention output, merged from the split partials of the decode
+// attention, into xs in pair layout: for head h and split s with (m_s, l_s,
+// o_s), o[d] = sum_s w_s o_s[d] / sum_s w_s l_s with w_s = exp(m_s - M), M the
+// largest m_s, sums in split order (what k_attn_combine computes). Every
+// split's values are loaded before any is used (splits past the active ones
+// re-read the last active split and are not summed).
+__device__ void stage_merged1(const CoreArgs &a, const Lds1 &l) {
+    const int hd = a.mhd, S = a.msplits;
+    const int C = attn_chunk(hd);
+    const int active = min((a.mst->slot + 1 + C - 1) / C, S);
+    const int n4 = a.sh.P * 16;
+    for (int e = threadIdx.x; e < n4; e += kThreads) {
+        const int k = 4 * e, h = k / hd, d = k - h * hd;
+        const float *pb = a.mpart + size_t(h) * S * (hd + 2);
+        float m[kMergeMaxSplits], ls[kMergeMaxSplits], o[kMergeMaxSplits][4];
+#pragma unroll
+        for (int s = 0; s < kMergeMaxSplits; ++s) {
+            const float *ps = pb + size_t(min(s, active - 1)) * (hd + 2);
+            m[s] = ps[0];
+            ls[s] = ps[1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[s][i] = ps[2 + d + i];
+        }
+        float M = m[0];
+#pragma unroll
+        for (int s = 1; s < kMergeMaxSplits; ++s)
+            if (s < active) M = fmaxf(M, m[s]);
+        float sum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kMergeMaxSplits; ++s) {
+            if (s < active) {
+                const float w = expf(m[s] - M);
+                sum = fmaf(w, ls[s], sum);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, o[s][i], acc[i]);
+            }
+        }
+        const float inv = 1.0f / sum;
+        *reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4) =
+            float4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    }
+}
+
 // The whole row u (K values) into xs in pair layout; the caller syncs.
 __device__ void stage_row1(const CoreArgs &a, const Lds1 &l) {
     const int tid = threadIdx.x;
@@ -637,7 +688,7 @@ __device__ inline int tile_rows(const CoreArgs &c) { return min(c.sh.NR, c.N - c
 // weights are in LDS, into the registers tile t used (two register stages,
 // alternating). The activation row is staged while the first two tiles load.
 // epi(tile, rows) consumes outv after each tile.
-template <bool MULTI, class Epi>
+template <bool MULTI, bool MERGE = false, class Epi>
 __device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, int ntiles, Epi &&epi) {
     const int G = int(gridDim.x);
     auto at = [&](int t, CoreArgs &x, int &nr, bool &v) {
@@ -655,7 +706,10 @@ __device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, in
     WStage sa, sb;
     if (na > 0) stage_issue(ca, na, 0, va, sa);
     if (nb > 0) stage_issue(cb, nb, 0, vb, sb);
-    stage_row1(c, l);
+    if constexpr (MERGE)
+        stage_merged1(c, l);
+    else
+        stage_row1(c, l);
     while (t < ntiles) {
         at(t + 2 * G, n, nn, nv);
         tile_run1<MULTI>(ca, l, na, va, sa, n, nn, nv, nn > 0);
@@ -901,7 +955,7 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
     }
 }
 
-template <bool MULTI>
+template <bool MULTI, bool MERGE = false>
 __global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds1 l = carve1(smem, a.sh, 1);
@@ -909,7 +963,8 @@ __global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
     CoreArgs c{};
     c.W[0] = a.W; c.nmat = 1; c.sh = a.sh; c.N = a.N; c.Tc = 1;
     c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    walk_tiles2<MULTI>(c, l, ntiles, [&](const CoreArgs &t, int nrows) {
+    c.mpart = a.mpart; c.msplits = a.msplits; c.mhd = a.mhd; c.mst = a.mst;
+    walk_tiles2<MULTI, MERGE>(c, l, ntiles, [&](const CoreArgs &t, int nrows) {
         for (int r = threadIdx.x; r < nrows; r += kThreads) {
             float *dst = a.y + t.row0 + r;
             *dst = a.accumulate ? *dst + l.outv[r] : l.outv[r];
@@ -1124,6 +1179,22 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
     const bool multi = a.sh.PC != a.sh.P;
     if (multi) hipLaunchKernelGGL((k_matmul<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
     else hipLaunchKernelGGL((k_matmul<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_oproj_merged(const uint8_t *W, int N, int K, const float *part, int n_splits, int hd,
+                               const StepState *st, float *Y, hipStream_t s) {
+    if (n_splits < 1 || n_splits > kMergeMaxSplits || K % hd || hd % 4) return hipErrorInvalidValue;
+    MatmulArgs a{};
+    a.W = W; a.x = nullptr; a.y = Y; a.N = N; a.T = 1; a.accumulate = 1;
+    a.mpart = part; a.msplits = n_splits; a.mhd = hd; a.mst = st;
+    a.sh = choose_shape(N, K, 1, 1, 512, 1);
+    if (a.sh.PC != a.sh.P) return hipErrorInvalidValue;  // the merged row is staged whole
+    const size_t lds = lds1_bytes(a.sh, 1);
+    const hipError_t e = set_lds(reinterpret_cast<const void *>(&k_matmul1<false, true>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_matmul1<false, true>), dim3(grid1((N + a.sh.NR - 1) / a.sh.NR, lds)), dim3(kThreads), lds,
+                       s, a);
     return hipGetLastError();
 }
 

@@ -98,6 +98,21 @@ hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const S
 hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
                          const float *norm_w, float eps, int accumulate, float *Y,
                          hipStream_t s);
+// Decode o-projection after an attention of 2..kMergeMaxSplits splits: the
+// merge of the split partials (part, [nh][n_splits][hd + 2]) is the GEMV's
+// prologue (no merge kernel); Y += W o. Every workgroup of the GEMV reads all
+// partials, so this pays only while they are few: oproj_merges says when
+// (at most kMergeMaxBytes of partials; measured: the 135M shape, 9 heads of
+// 64, merges up to 8 splits 6-9 % faster per token; the 7B-class shape, 32
+// heads of 128, was 2-5 % slower with 4 or 8 splits).
+constexpr int kMergeMaxSplits = 8;
+constexpr int kMergeMaxBytes = 24 * 1024;
+inline bool oproj_merges(const Dims &d, int n_splits) {
+    return n_splits > 1 && n_splits <= kMergeMaxSplits &&
+           int64_t(d.nh) * n_splits * (d.hd + 2) * 4 <= kMergeMaxBytes;
+}
+hipError_t launch_oproj_merged(const uint8_t *W, int N, int K, const float *part, int n_splits, int hd,
+                               const StepState *st, float *Y, hipStream_t s);
 // h[t] = silu(Wg u[t]) * (Wu u[t]), u = rmsnorm(x[t]).
 hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, float *h, int T,
                          hipStream_t s);
@@ -129,7 +144,8 @@ hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s);
 hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int nh, int hd,
                                float *o, const StepState *st, hipStream_t s);
 int attn_decode_splits(int kv_len, int hd);
-__host__ __device__ int attn_chunk(int hd);
+// Keys per decode attention split.
+__host__ __device__ inline int attn_chunk(int hd) { return hd <= 64 ? 64 : 32; }
 size_t lmhead_partials_bytes(int V, int K);
 
 // MFMA matrix-matrix path (prefill with T >= kGemmMinTokens tokens). Activations

@@ -113,6 +113,7 @@ struct q8l_model {
     Layout lay;
     const uint8_t *tok_embd = nullptr, *output = nullptr;
     const float *out_norm = nullptr;
+    bool merge_in_o = false;  // decode o-projection merges 2..8 attention splits in its prologue
     std::vector<std::vector<const void *>> layer_ptrs;  // [L][S_NSLOT]
     std::vector<int> fmt_o, fmt_d;                      // [L] WFmt of attn_output / ffn_down
     uint8_t *ws = nullptr;
@@ -199,10 +200,14 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = decode_splits;
             a.scale = 1.0f / sqrtf(float(d.hd));
             a.o = decode_splits == 1 ? att : nullptr;  // one split: the attention kernel normalises
+            // a few splits of a small model: the o-projection merges them in its prologue (no merge node)
+            const bool merge_o = w.fo == F_Q8_0 && m->merge_in_o && oproj_merges(d, decode_splits);
             if ((e = launch_attn_decode(a, s)) != hipSuccess) return e;
-            if (decode_splits > 1 && (e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s)) != hipSuccess)
+            if (decode_splits > 1 && !merge_o &&
+                (e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s)) != hipSuccess)
                 return e;
             e = w.fo != F_Q8_0 ? launch_kq_gemv(w.fo, w.wo, d.H, QD, att, 1, x, s)
+                : merge_o      ? launch_oproj_merged(w.wo, d.H, QD, a.part, decode_splits, d.hd, st, x, s)
                                : launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, x, s);
             if (e != hipSuccess) return e;
         } else {
@@ -380,6 +385,8 @@ q8l_status q8l_create(const q8l_config *cfg, q8l_model **out) {
     m->d.eps = float(cfg->rms_eps);
     m->d.rope_neox = cfg->rope_type == Q8L_ROPE_NEOX ? 1 : 0;
     m->lay = make_layout(cfg);
+    // the merged attention row is staged whole in LDS (as the o-projection GEMV stages rows of <= 150 pairs)
+    m->merge_in_o = (cfg->n_head * cfg->head_dim / kPairWeights) * 68 * 4 <= 40 * 1024;
     m->layer_ptrs.assign(cfg->n_layer, std::vector<const void *>(S_NSLOT, nullptr));
     m->fmt_o.assign(cfg->n_layer, F_Q8_0);
     m->fmt_d.assign(cfg->n_layer, F_Q8_0);
@@ -571,6 +578,8 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
             case 2: return launch_attn_decode(a, s);
             case 3:
                 if (w.fo != F_Q8_0) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
+                if (m->merge_in_o && oproj_merges(d, a.n_splits))  // as in the step
+                    return launch_oproj_merged(w.wo, d.H, QD, a.part, a.n_splits, d.hd, S, x, s);
                 return launch_matmul(w.wo, d.H, QD, m->at<float>(m->lay.att), 1, nullptr, d.eps, 1, x, s);
             case 4: return launch_gateup(d, w, x, h, 1, s);
             case 5:
