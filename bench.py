@@ -64,11 +64,13 @@ def kernel_symbols(s, down_fmt="q8_0"):
     o_multi = (s.q_dim // 64) * 272 > 40 * 1024
     down_multi = (s.n_ff // 64) * 272 > 40 * 1024
     if down_fmt == "q8_0":
-        down = "k_matmul1_chunked" if down_multi else "k_matmul1<false>"
+        down = "k_matmul1_chunked" if down_multi else "k_matmul1<false, false>"
     else:
         down = f"k_kq_gemv<{1 if down_fmt == 'q4_k' else 2}, {2 if s.n_embd >= 4096 else 1}>"
+    # the o-projection at one attention split (k_matmul1<false, true> merges
+    # several splits in its prologue at the 135M shape)
     return ["k_embed", f"k_qkv1<{str(multi).lower()}>", "k_attn_decode",
-            "k_matmul1_chunked" if o_multi else "k_matmul1<false>", f"k_gateup1<{str(multi).lower()}>",
+            "k_matmul1_chunked" if o_multi else "k_matmul1<false, false>", f"k_gateup1<{str(multi).lower()}>",
             down, f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
 
 

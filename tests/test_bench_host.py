@@ -1,0 +1,78 @@
+"""Host-side logic of bench.py that needs no GPU: the counter summary that
+turns two rocprofv3 --pmc runs into per-launch traffic of the decode kernels."""
+
+import csv
+import io
+import os
+import sys
+from contextlib import redirect_stdout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth  # noqa: E402
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _write(dirname, counter, rows):
+    os.makedirs(dirname, exist_ok=True)
+    with open(os.path.join(dirname, "x_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Correlation_Id": i + 1, "Dispatch_Id": i + 1, "Kernel_Name": name,
+                        "Counter_Name": counter, "Counter_Value": value})
+
+
+def _dispatches(values):
+    """One decode layer's dispatch sequence with the given counter values,
+    between two 1 GiB copies (the reference dispatches)."""
+    ns = "void q8l::(anonymous namespace)::"
+    seq = [("__amd_rocclr_copyBuffer", values["copy"]),
+           (ns + "k_embed(unsigned char const*, int)", values["embed"]),
+           (ns + "k_qkv1<false>(q8l::(anonymous namespace)::QkvArgs)", values["qkv"]),
+           ("q8l::(anonymous namespace)::k_attn_decode(q8l::AttnDecodeArgs)", values["attn"]),
+           (ns + "k_matmul1<false, false>(q8l::(anonymous namespace)::MatmulArgs)", values["o"]),
+           (ns + "k_gateup1<false>(q8l::(anonymous namespace)::GateUpArgs)", values["gateup"]),
+           (ns + "k_matmul1<false, false>(q8l::(anonymous namespace)::MatmulArgs)", values["down"]),
+           (ns + "k_lmhead1<false>(q8l::(anonymous namespace)::LmHeadArgs)", values["lm"]),
+           ("__amd_rocclr_copyBuffer", values["copy"]),
+           ("__amd_rocclr_copyBuffer", 3.0)]  # a small upload copy: not a reference dispatch
+    return seq
+
+
+def test_pmc_summary_scales_by_the_copy_and_tells_o_from_down(tmp_path):
+    fetch = {"copy": 524288.0, "embed": 2.0, "qkv": 400.0, "attn": 30.0, "o": 280.0, "gateup": 1000.0,
+             "down": 570.0, "lm": 15000.0}
+    write = {"copy": 1048576.0, "embed": 1.0, "qkv": 8.0, "attn": 2.0, "o": 4.0, "gateup": 12.0,
+             "down": 9.0, "lm": 270.0}
+    _write(str(tmp_path / "f"), "FETCH_SIZE", _dispatches(fetch))
+    _write(str(tmp_path / "w"), "WRITE_SIZE", _dispatches(write))
+    buf = io.StringIO()
+    with redirect_stdout(buf):
+        bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), config="C2")
+    out = buf.getvalue()
+    assert "scale FETCH_SIZE 2.0000, WRITE_SIZE 1.0000" in out
+    lines = {l.split()[1].split("=")[1]: l for l in out.splitlines() if l.startswith("traffic:")}
+    # bytes = (FETCH KiB * 2 + WRITE KiB * 1) * 1024
+    for kind, key in [("qkv_rope_kv", "qkv"), ("oproj_residual", "o"), ("gateup_silu", "gateup"),
+                      ("down_residual", "down"), ("lmhead", "lm")]:
+        want = int(round((fetch[key] * 2 + write[key]) * 1024))
+        assert f"bytes_per_launch={want} " in lines[kind], (kind, lines[kind])
+        src = bench.KIND_SOURCES[kind]
+        assert f"sha256={bench.source_digest(src)}" in lines[kind]
+
+
+def test_measured_traffic_follows_the_source_digest(tmp_path, monkeypatch):
+    path = tmp_path / "t.md"
+    src = bench.KIND_SOURCES["gateup_silu"]
+    path.write_text(f"traffic: kind=gateup_silu bytes_per_launch=123 source={src} "
+                    f"sha256={bench.source_digest(src)}\n"
+                    f"traffic: kind=lmhead bytes_per_launch=456 source={src} sha256=0000000000000000\n")
+    monkeypatch.setitem(bench.TRAFFIC_FILES, "C2", str(path))
+    assert bench.measured_traffic("C2", "gateup_silu") == 123
+    assert bench.measured_traffic("C2", "lmhead") is None     # digest of another source: stale
+    assert bench.measured_traffic("C2", "embed") is None       # not measured
+    assert synth.WORKLOADS["C2"].prompt_len == 13
