@@ -45,11 +45,15 @@ struct CoreArgs {
     int ldx;
     const float *norm_w;
     float eps;
-    // Decode o-projection after a multi-split attention: the activation row is
-    // merged from the attention's split partials instead of read from X.
-    const float *mpart;      // [nh][msplits][mhd + 2]: (max, sum, unnormalised o)
-    int msplits, mhd;
-    const StepState *mst;    // active splits from the cache length
+};
+
+// Decode o-projection after a multi-split attention: the activation row is
+// merged from the attention's split partials instead of read from X. (Kept out
+// of CoreArgs: a larger CoreArgs is copied through scratch memory.)
+struct MergeSrc {
+    const float *part;       // [nh][splits][hd + 2]: (max, sum, unnormalised o)
+    int splits, hd;
+    const StepState *st;     // active splits from the cache length
 };
 
 struct Lds {
@@ -569,14 +573,14 @@ __device__ inline Lds1 carve1(uint8_t *smem, const GemvShape &sh, int nmat) {
 // largest m_s, sums in split order (what k_attn_combine computes). Every
 // split's values are loaded before any is used (splits past the active ones
 // re-read the last active split and are not summed).
-__device__ void stage_merged1(const CoreArgs &a, const Lds1 &l) {
-    const int hd = a.mhd, S = a.msplits;
+__device__ void stage_merged1(const CoreArgs &a, const MergeSrc &ms, const Lds1 &l) {
+    const int hd = ms.hd, S = ms.splits;
     const int C = attn_chunk(hd);
-    const int active = min((a.mst->slot + 1 + C - 1) / C, S);
+    const int active = min((ms.st->slot + 1 + C - 1) / C, S);
     const int n4 = a.sh.P * 16;
     for (int e = threadIdx.x; e < n4; e += kThreads) {
         const int k = 4 * e, h = k / hd, d = k - h * hd;
-        const float *pb = a.mpart + size_t(h) * S * (hd + 2);
+        const float *pb = ms.part + size_t(h) * S * (hd + 2);
         float m[kMergeMaxSplits], ls[kMergeMaxSplits], o[kMergeMaxSplits][4];
 #pragma unroll
         for (int s = 0; s < kMergeMaxSplits; ++s) {
@@ -689,7 +693,8 @@ __device__ inline int tile_rows(const CoreArgs &c) { return min(c.sh.NR, c.N - c
 // alternating). The activation row is staged while the first two tiles load.
 // epi(tile, rows) consumes outv after each tile.
 template <bool MULTI, bool MERGE = false, class Epi>
-__device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, int ntiles, Epi &&epi) {
+__device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, int ntiles, Epi &&epi,
+                                            const MergeSrc *ms = nullptr) {
     const int G = int(gridDim.x);
     auto at = [&](int t, CoreArgs &x, int &nr, bool &v) {
         x = c;
@@ -707,7 +712,7 @@ __device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, in
     if (na > 0) stage_issue(ca, na, 0, va, sa);
     if (nb > 0) stage_issue(cb, nb, 0, vb, sb);
     if constexpr (MERGE)
-        stage_merged1(c, l);
+        stage_merged1(c, *ms, l);
     else
         stage_row1(c, l);
     while (t < ntiles) {
@@ -963,13 +968,16 @@ __global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
     CoreArgs c{};
     c.W[0] = a.W; c.nmat = 1; c.sh = a.sh; c.N = a.N; c.Tc = 1;
     c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    c.mpart = a.mpart; c.msplits = a.msplits; c.mhd = a.mhd; c.mst = a.mst;
-    walk_tiles2<MULTI, MERGE>(c, l, ntiles, [&](const CoreArgs &t, int nrows) {
-        for (int r = threadIdx.x; r < nrows; r += kThreads) {
-            float *dst = a.y + t.row0 + r;
-            *dst = a.accumulate ? *dst + l.outv[r] : l.outv[r];
-        }
-    });
+    const MergeSrc ms{a.mpart, a.msplits, a.mhd, a.mst};
+    walk_tiles2<MULTI, MERGE>(
+        c, l, ntiles,
+        [&](const CoreArgs &t, int nrows) {
+            for (int r = threadIdx.x; r < nrows; r += kThreads) {
+                float *dst = a.y + t.row0 + r;
+                *dst = a.accumulate ? *dst + l.outv[r] : l.outv[r];
+            }
+        },
+        &ms);
 }
 
 template <bool MULTI>
