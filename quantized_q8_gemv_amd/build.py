@@ -40,6 +40,38 @@ def _compile(src: str, obj: str) -> None:
     subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
 
 
+LLVM = os.environ.get("ROCM_LLVM", "/opt/rocm/llvm/bin")
+
+
+def scratch_kernels(obj: str) -> list:
+    """Kernels of a compiled .hip object (its gfx950 code object's metadata)
+    that use scratch memory: a private segment or spilled VGPRs. A kernel of
+    this library that does is a performance bug (its stack traffic goes to
+    HBM), e.g. an argument struct grown past what stays in registers.
+    Returns [] when the LLVM tools are not there."""
+    objcopy, bundler, readelf = (os.path.join(LLVM, t) for t in
+                                 ("llvm-objcopy", "clang-offload-bundler", "llvm-readelf"))
+    if not all(os.path.exists(t) for t in (objcopy, bundler, readelf)):
+        return []
+    fat, co = obj + ".fatbin", obj + ".co"
+    subprocess.run([objcopy, f"--dump-section=.hip_fatbin={fat}", obj], check=True,
+                   stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    subprocess.run([bundler, "--unbundle", "--type=o", f"--targets=hipv4-amdgcn-amd-amdhsa--{ARCH}",
+                    f"--input={fat}", f"--output={co}"], check=True, stdout=subprocess.PIPE,
+                   stderr=subprocess.STDOUT)
+    notes = subprocess.run([readelf, "--notes", co], check=True, stdout=subprocess.PIPE,
+                           stderr=subprocess.STDOUT).stdout.decode(errors="replace")
+    bad, name = [], None
+    for line in notes.splitlines():
+        line = line.strip()
+        if line.startswith(".name:"):
+            name = line.split(":", 1)[1].strip()
+        elif line.startswith((".private_segment_fixed_size:", ".vgpr_spill_count:")):
+            if int(line.split(":", 1)[1]) > 0 and name and name not in bad:
+                bad.append(name)
+    return bad
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libq8l.so; returns its path."""
     with tempfile.TemporaryDirectory(prefix="q8l_build_") as tmp:
@@ -52,6 +84,9 @@ def build(verbose: bool = False) -> str:
                 except subprocess.CalledProcessError as e:
                     sys.stderr.write(e.stdout.decode(errors="replace"))
                     raise RuntimeError(f"hipcc failed on {s}") from None
+        bad = [k for s, o in zip(SOURCES, objs) if s.endswith(".hip") for k in scratch_kernels(o)]
+        if bad:
+            raise RuntimeError("kernels using scratch memory (private segment or VGPR spills): " + ", ".join(bad))
         tmp_lib = LIB + ".tmp"
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib] + objs
         subprocess.run(cmd, check=True)
