@@ -15,12 +15,17 @@ Printed JSON line:
                    without host round trips), per-token time and HBM fraction
                    = algorithmic bytes per token (Q8_0 weights + norms + one
                    embedding row + KV cache read/written) / time / 8 TB/s
+  device_loop_cache_flushed
+                   the same per-token time with the 256 MB memory-side cache
+                   flushed before each step (a 512 MiB copy outside the timed
+                   region): the weights stream from HBM
   roofline         the decode kernel with the most time per step, its algorithmic
                    bytes per launch over its mean launch time (HIP events)
   cpu_baseline     the CPU oracle timed on a bounded sample of the same workload
   host_loop_reps   min and median over the timed steps (per-token decode, prefill)
 
-Other modes: --formats times one matmul per block format; --kv-sweep prints
+Other modes: --pmc-summary FETCH_DIR WRITE_DIR summarises two rocprofv3
+counter runs (no GPU); --formats times one matmul per block format; --kv-sweep prints
 one line per cache length (16 ... 4000 prompt tokens on the 135M-shaped
 model): device-loop us/token and the attention kernel's time at that length.
 """
@@ -522,6 +527,30 @@ def main():
     mean_kv = len(prompt) + (steps + 1) / 2.0
     b_tok = W + kvb * mean_kv
     dev_gbs = b_tok / (dev_ms * 1e-3) / 1e9
+
+    # The same decode with the memory-side cache (256 MB) flushed before every
+    # step: a 512 MiB device copy (1 GiB of traffic) runs between steps and
+    # only the step itself (its state-setting kernel + the decode graph) is
+    # timed, so the weights come from HBM as they would for a model that does
+    # not fit that cache.
+    flush_src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    flush_dst = torch.empty_like(flush_src)
+    cold = []
+    for r in range(3):
+        assert gm.forward_async(prompt, 0) == C.Q8L_OK
+        for k in range(steps):
+            flush_dst.copy_(flush_src)
+            ev0.record()
+            assert gm.generate_async(gm.argmax, len(prompt) + k, 1, ids) == C.Q8L_OK
+            ev1.record()
+            torch.cuda.synchronize()
+            if r >= 1:
+                cold.append(ev0.elapsed_time(ev1))
+    del flush_src, flush_dst
+    cold_ms = statistics.median(cold)
+    cold_gbs = b_tok / (cold_ms * 1e-3) / 1e9
+    eprint(f"[bench] device loop, cache flushed before each step: {cold_ms * 1e3:.1f} us/token, "
+           f"{cold_gbs:.0f} GB/s algorithmic")
     eprint(f"[bench] device loop: {dev_ms * 1e3:.1f} us/token, {dev_gbs:.0f} GB/s algorithmic")
 
     # Per-kernel launch times (HIP events on the stream the kernels run on).
@@ -593,6 +622,10 @@ def main():
                         "bytes_per_token": int(b_tok),
                         "hbm_gbs": round(dev_gbs, 1),
                         "hbm_frac": round(dev_gbs / PEAK_HBM_GBS, 4)},
+        "device_loop_cache_flushed": {"us_per_token": round(cold_ms * 1e3, 2),
+                                      "hbm_gbs": round(cold_gbs, 1),
+                                      "hbm_frac": round(cold_gbs / PEAK_HBM_GBS, 4),
+                                      "flush": "512 MiB device copy before each step, outside the timed region"},
         "roofline": roofline,
         "copy_gbs": round(copy_gbs, 1),
         "kernels": kernels,
