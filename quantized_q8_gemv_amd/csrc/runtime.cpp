@@ -7,6 +7,10 @@
 // MLP block with residuals; final norm on the last position; output layer.
 // Kernels per layer: q/k/v (norm + rope + KV write fused), attention,
 // o-projection (+ residual), gate/up (norm + SiLU*up fused), down (+ residual).
+// Decode with 2..8 attention splits of a small model merges them in the
+// o-projection's prologue; more splits take a merge kernel. Short prompts
+// split the o and down products over K, and the next norm kernel adds the
+// partial sums to the residual.
 //
 // Decode (one token) runs as a captured HIP graph: every kernel reads the
 // position, slot and token from a device-side StepState, so one graph serves
@@ -182,6 +186,14 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
     _Float16 *att_s = m->at<_Float16>(m->lay.att), *h_s = m->at<_Float16>(m->lay.h);
     float *kpart = m->at<float>(m->lay.kpart);
     int pend = 0;  // split-K partial sums not yet added to x (the next norm kernel adds them)
+    // Prefill x += A W^T for a Q8_0 matrix of H rows: split over K when the
+    // plain grid would be small (the partial sums wait in kpart).
+    auto gemm_accumulate = [&](const uint8_t *W, int K, const _Float16 *A) -> hipError_t {
+        const int sk = gemm_splitk(d.H, K, T);
+        pend = sk > 1 ? sk : 0;
+        return sk > 1 ? launch_gemm_part(W, d.H, K, A, T, sk, kpart, s)
+                      : launch_gemm_matmul(W, d.H, K, A, true, T, 1, x, s);
+    };
     for (int l = 0; l < m->cfg.n_layer; ++l) {
         const LayerPtrs w = m->layer(l);
         if (gemm) {
@@ -220,10 +232,8 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             if (w.fo != F_Q8_0)
                 e = gemm ? launch_gemm_kq(w.fo, w.wo, d.H, QD, att_s, true, T, 1, x, s)
                          : launch_gemm_kq(w.fo, w.wo, d.H, QD, att, false, T, 1, x, s);
-            else if (gemm && (pend = gemm_splitk(d.H, QD, T)) > 1)
-                e = launch_gemm_part(w.wo, d.H, QD, att_s, T, pend, kpart, s);
             else if (gemm)
-                pend = 0, e = launch_gemm_matmul(w.wo, d.H, QD, att_s, true, T, 1, x, s);
+                e = gemm_accumulate(w.wo, QD, att_s);
             else
                 e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s);
             if (e != hipSuccess) return e;
@@ -232,12 +242,8 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             if ((e = launch_rms_split(x, T, d.H, w.ffn_norm, d.eps, u, kpart, pend, s)) != hipSuccess) return e;
             pend = 0;
             if ((e = launch_gemm_gateup(d, w, u, h_s, T, s)) != hipSuccess) return e;
-            if (w.fd != F_Q8_0)
-                e = launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s);
-            else if ((pend = gemm_splitk(d.H, d.F, T)) > 1)
-                e = launch_gemm_part(w.wd, d.H, d.F, h_s, T, pend, kpart, s);
-            else
-                pend = 0, e = launch_gemm_matmul(w.wd, d.H, d.F, h_s, true, T, 1, x, s);
+            e = w.fd != F_Q8_0 ? launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s)
+                               : gemm_accumulate(w.wd, d.F, h_s);
         } else {
             if ((e = launch_gateup(d, w, x, h, T, s)) != hipSuccess) return e;
             if (w.fd == F_Q8_0)
