@@ -270,8 +270,9 @@ q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspa
  * ms_out[kind] (ms_out holds 9 floats), kinds
  *   0 embedding, 1 q/k/v (+norm, rope, KV write), 2 attention (split
  *   partials, or the normalised output when the cache fits one split),
- *   3 o-projection (+residual; the merge of several splits is a kernel of
- *   its own, not timed here), 4 gate/up (+norm,
+ *   3 o-projection (+residual; as in the step at this length: with 2..8
+ *   splits and few partial bytes it merges them in its prologue, with more
+ *   the merge is a kernel of its own, not timed here), 4 gate/up (+norm,
  *   SiLU*up), 5 down (+residual), 6 output layer (+norm, per-workgroup
  *   argmax), 7 argmax merge, 8 an empty kernel (the dispatch gap between
  *   back-to-back launches, included in every other entry).
