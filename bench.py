@@ -46,10 +46,14 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 FORMAT_BYTES = {"q8_0": (32, 34), "q4_k": (256, 144), "q6_k": (256, 210)}   # (weights, bytes) per block
-# The pages' Metal figure for this workload ("生成一个 token", section "Metal：热缓存"):
-# 20 decode steps after a 13-token prompt, 2.6 ms mean per step incl. the argmax
-# readback, on an Apple M2 Max -- another machine, quoted as context.
-PAGES_DECODE_MS = {"C2": 2.6}
+# The pages' Metal figures for these workloads, on an Apple M2 Max -- another
+# machine, quoted as context:
+#   C2: 20 decode steps after a 13-token prompt, 2.6 ms mean per step incl. the
+#       argmax readback ("生成一个 token", section "Metal：热缓存");
+#   C3: 203-token prompt + 128 greedy steps, fresh cache per rep, best of 10
+#       reps, Q8_0 on Metal 2.72 ms per token ("速度", sections
+#       "两边量的是同一件事" and "小结").
+PAGES_DECODE_MS = {"C2": 2.6, "C3": 2.72}
 KIND_NAMES = ["embed", "qkv_rope_kv", "attn_decode", "oproj_residual", "gateup_silu",
               "down_residual", "lmhead", "argmax_finish"]
 NKINDS = len(KIND_NAMES)
