@@ -156,8 +156,10 @@ def pmc_summary(fetch_dir, write_dir, config="C2"):
     scale = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         disp = load(d, counter)
+        # the 1 GiB copies of copy_bandwidth() are the largest copy dispatches
+        # (the 512 MiB cache-flush copies and the uploads are smaller)
         copies = sorted(v for _, n, v in disp if "copyBuffer" in n)
-        big = [v for v in copies if v >= 0.4 * copies[-1]] if copies else []
+        big = [v for v in copies if v >= 0.9 * copies[-1]] if copies else []
         scale[counter] = (1 << 30) / (statistics.mean(big) * 1024) if big else float("nan")
         acc = {}
         for kind, short, v in kinds(disp):

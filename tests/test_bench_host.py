@@ -39,6 +39,7 @@ def _dispatches(values):
            (ns + "k_matmul1<false, false>(q8l::(anonymous namespace)::MatmulArgs)", values["down"]),
            (ns + "k_lmhead1<false>(q8l::(anonymous namespace)::LmHeadArgs)", values["lm"]),
            ("__amd_rocclr_copyBuffer", values["copy"]),
+           ("__amd_rocclr_copyBuffer", values["copy"] / 2),  # a 512 MiB cache-flush copy: not a reference
            ("__amd_rocclr_copyBuffer", 3.0)]  # a small upload copy: not a reference dispatch
     return seq
 
