@@ -476,26 +476,40 @@ def main():
     torch.cuda.synchronize()
 
     # The greedy id goes to pinned host memory that the last kernel writes
-    # directly: each step's 4-byte readback is a stream synchronisation.
+    # directly; the host polls that word (reset to -1, never a token id,
+    # before each forward) and reads the id as soon as it lands -- the 4-byte
+    # readback of each step, without a copy or a blocking stream sync (the
+    # next forward is ordered after the rest of the step by the stream).
     am_host, am_dev = host_mapped_u32()
+    am_np = am_host.numpy()
     stream = torch.cuda.current_stream()
     tok = np.zeros(1, dtype=np.uint32)
     prompt_u32 = np.ascontiguousarray(np.asarray(prompt, dtype=np.uint32))
 
+    def read_id():
+        deadline = time.perf_counter() + 10.0
+        while am_np[0] == -1:
+            if time.perf_counter() > deadline:
+                stream.synchronize()
+                if am_np[0] == -1:
+                    raise RuntimeError("the forward did not write its argmax")
+        return int(am_np[0])
+
     def generation():
         t0 = time.perf_counter()
+        am_np[0] = -1
         st = gm.forward_async(prompt_u32, 0, argmax_out=am_dev)
         assert st == C.Q8L_OK, st
-        stream.synchronize()
-        nxt = int(am_host[0])
+        nxt = read_id()
         t1 = time.perf_counter()
         for k in range(steps):
             tok[0] = nxt
+            am_np[0] = -1
             st = gm.forward_async(tok, len(prompt) + k, argmax_out=am_dev)
             assert st == C.Q8L_OK, st
-            stream.synchronize()
-            nxt = int(am_host[0])
+            nxt = read_id()
         t2 = time.perf_counter()
+        stream.synchronize()
         return t1 - t0, t2 - t1
 
     for _ in range(args.warmup):
