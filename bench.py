@@ -591,7 +591,7 @@ def main():
     launches = [n if raw[i] > 0 else 0 for i, n in enumerate(launches)]
     per_step = [ms[i] * launches[i] for i in range(NKINDS)]
     dom = max(range(NKINDS), key=lambda i: per_step[i])
-    kernels = {KIND_NAMES[i]: {"us": round(ms[i] * 1e3, 2), "bytes": kb[i],
+    kernels = {KIND_NAMES[i]: {"us": round(ms[i] * 1e3, 2) if raw[i] > 0 else None, "bytes": kb[i],
                                "gbs": round(kb[i] / (ms[i] * 1e-3) / 1e9, 1) if raw[i] > 0 else 0.0,
                                "launches_per_token": launches[i]} for i in range(NKINDS)}
     achieved = kb[dom] / (ms[dom] * 1e-3) / 1e9
@@ -603,7 +603,7 @@ def main():
                 "empty_kernel_us": round(overhead * 1e3, 2)}
     copy_gbs = copy_bandwidth(torch)
     eprint(f"[bench] device copy: {copy_gbs:.0f} GB/s (1 GiB, read + write)")
-    eprint(f"[bench] kernels: " + ", ".join(f"{k} {v['us']}us" for k, v in kernels.items()))
+    eprint(f"[bench] kernels: " + ", ".join(f"{k} {v['us']}us" for k, v in kernels.items() if v["us"] is not None))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -330,6 +330,11 @@ struct QkvArgs {
     int QD, KVD, hd, max_seq, T;
     float eps;
     int rope_neox;       // 1: q and k are written unrotated (a separate kernel rotates them)
+    // Decode of layer 0: the input row is the token's embedding (Q8_0 row of
+    // embed, token from st), dequantized here; workgroup 0 also writes it to
+    // x as the residual. NULL: the row is read from x.
+    const uint8_t *embed;
+    int V;
 };
 
 template <int MAXT, bool MULTI>
@@ -774,6 +779,50 @@ __device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, in
     }
 }
 
+// Layer 0 of a decode step: the embedding of the step's token (x = d * q per
+// 32-weight block, as the embedding kernel computes it) staged and
+// normalised as stage_row1's general path does (same values, same order);
+// workgroup 0 writes the row to x, the residual the o-projection adds to. A
+// token id past the vocabulary (only reachable through a device-side token)
+// gives a zero row, as the embedding kernel does.
+__device__ void stage_embed1(const QkvArgs &a, const CoreArgs &c, const Lds1 &l) {
+    const int tid = threadIdx.x;
+    const int n4 = c.sh.P * 16, H = c.sh.K;
+    const uint32_t tok = a.st->token;
+    const bool valid = tok < uint32_t(a.V);
+    const uint8_t *row = a.embed + (valid ? size_t(tok) : 0) * (size_t(H) / kQK * kQBytes);
+    float *xres = const_cast<float *>(a.x);
+    float ss = 0.f;
+    for (int e = tid; e < n4; e += kThreads) {
+        const uint8_t *blk = row + size_t(e >> 3) * kQBytes;   // 8 float4 per 32-weight block
+        const int i0 = (e & 7) * 4;
+        const float d = half_bits_to_float(uint32_t(blk[0]) | (uint32_t(blk[1]) << 8));
+        float4 v;
+        v.x = valid ? d * static_cast<float>(static_cast<int8_t>(blk[2 + i0])) : 0.f;
+        v.y = valid ? d * static_cast<float>(static_cast<int8_t>(blk[3 + i0])) : 0.f;
+        v.z = valid ? d * static_cast<float>(static_cast<int8_t>(blk[4 + i0])) : 0.f;
+        v.w = valid ? d * static_cast<float>(static_cast<int8_t>(blk[5 + i0])) : 0.f;
+        *reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4) = v;
+        if (blockIdx.x == 0) *reinterpret_cast<float4 *>(xres + size_t(e) * 4) = v;
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+    }
+    ss = block_sum(ss, l.red);
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(c.sh.K) + c.eps);
+    for (int e = tid; e < n4; e += kThreads) {
+        float4 *xp = reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4);
+        const float4 w = *reinterpret_cast<const float4 *>(c.norm_w + size_t(e) * 4);
+        float4 v = *xp;
+        v.x = v.x * r * w.x;
+        v.y = v.y * r * w.y;
+        v.z = v.z * r * w.z;
+        v.w = v.w * r * w.w;
+        *xp = v;
+    }
+}
+
 template <bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -798,7 +847,10 @@ __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
     bool vec = tile_vec(c, nrows);
     WStage st;
     stage_issue(c, nrows, 0, vec, st);
-    stage_row1(c, l);
+    if (a.embed)
+        stage_embed1(a, c, l);
+    else
+        stage_row1(c, l);
     const int pos = a.st->pos, slot = a.st->slot;
     for (; tile < ntiles; tile += gridDim.x) {
         const bool has_next = tile + int(gridDim.x) < ntiles;
@@ -1149,9 +1201,12 @@ static hipError_t set_lds(const void *fn, size_t bytes) {
 }  // namespace
 
 hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const StepState *st,
-                      const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s) {
+                      const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s,
+                      const uint8_t *embed) {
     const int maxt = T == 1 ? 1 : kMaxTokChunk;
+    if (embed && T != 1) return hipErrorInvalidValue;
     QkvArgs a;
+    a.embed = embed; a.V = d.V;
     a.wq = w.wq; a.wk = w.wk; a.wv = w.wv; a.norm_w = w.attn_norm; a.x = x; a.st = st;
     a.rope = rope; a.q = q; a.kc = kc; a.vc = vc;
     a.QD = d.nh * d.hd; a.KVD = d.nkv * d.hd; a.hd = d.hd; a.max_seq = d.max_seq; a.T = T;

@@ -201,7 +201,9 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             pend = 0;
             if ((e = launch_gemm_qkv(d, w, u, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
         } else {
-            if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
+            // a decode step's first layer dequantizes the token's embedding itself
+            const uint8_t *emb = (T == 1 && l == 0) ? m->tok_embd : nullptr;
+            if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s, emb)) != hipSuccess) return e;
         }
         if (d.rope_neox && (e = launch_rope_neox(d, st, rope, q, m->kc(l), T, s)) != hipSuccess) return e;
         if (T == 1) {
@@ -281,9 +283,8 @@ q8l_status decode_graph(q8l_model *m, int bucket, hipGraphExec_t *out) {
     }
     if (!m->cap) Q8L_HIP(m, hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking), "hipStreamCreate");
     Q8L_HIP(m, hipStreamBeginCapture(m->cap, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
-    hipError_t e = launch_embed(m->tok_embd, m->d.H, m->d.V, m->state(), m->at<uint32_t>(m->lay.tok), 1, 1,
-                                m->at<float>(m->lay.x), m->cap);
-    if (e == hipSuccess) e = enqueue_layers(m, 1, -1, bucket, m->cap);
+    // (no embedding kernel: the first layer's q/k/v kernel reads the embedding)
+    hipError_t e = enqueue_layers(m, 1, -1, bucket, m->cap);
     hipGraph_t g = nullptr;
     hipError_t e2 = hipStreamEndCapture(m->cap, &g);
     if (e != hipSuccess) {
@@ -579,8 +580,9 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     a.o = a.n_splits == 1 ? m->at<float>(m->lay.att) : nullptr;
     auto launch = [&](int kind) -> hipError_t {
         switch (kind) {
-            case 0: return launch_embed(m->tok_embd, d.H, d.V, S, m->at<uint32_t>(m->lay.tok), 1, 1, x, s);
-            case 1: return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
+            case 0: return hipSuccess;  // the decode step has no embedding kernel
+            case 1:  // layer 0's q/k/v, which reads the token's embedding in the step
+                return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s, m->tok_embd);
             case 2: return launch_attn_decode(a, s);
             case 3:
                 if (w.fo != F_Q8_0) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
@@ -613,7 +615,7 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     for (int k = 0; k < kKinds && err == hipSuccess; ++k) {
         float ms = 0.f;
         if ((err = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1])) != hipSuccess) break;
-        ms_out[k] = ms / float(reps);
+        ms_out[k] = k == 0 ? -1.0f : ms / float(reps);  // kind 0: not a kernel of the step
     }
     for (auto &e : ev)
         if (e) hipEventDestroy(e);
