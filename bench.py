@@ -172,6 +172,8 @@ def pmc_summary(fetch_dir, write_dir, config="C2"):
     print("|---|---|---:|---:|---:|---:|---:|---:|")
     lines = []
     for kind in KIND_NAMES:
+        if kind == "embed":  # not a kernel of the decode step (its dispatches are the prefill's)
+            continue
         if kind not in res or "FETCH_SIZE" not in res[kind] or "WRITE_SIZE" not in res[kind]:
             continue
         r = res[kind]

@@ -581,8 +581,8 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     auto launch = [&](int kind) -> hipError_t {
         switch (kind) {
             case 0: return hipSuccess;  // the decode step has no embedding kernel
-            case 1:  // layer 0's q/k/v, which reads the token's embedding in the step
-                return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s, m->tok_embd);
+            case 1:  // q/k/v as every layer but the first runs it (that one also reads the embedding)
+                return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
             case 2: return launch_attn_decode(a, s);
             case 3:
                 if (w.fo != F_Q8_0) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
