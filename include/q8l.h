@@ -269,7 +269,8 @@ q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspa
  * `stream`, and write the mean time per launch in milliseconds to
  * ms_out[kind] (ms_out holds 9 floats), kinds
  *   0 embedding (-1: the step has no embedding kernel, the first q/k/v
- *   kernel dequantizes the token's row), 1 q/k/v (+norm, rope, KV write;
+ *   kernel dequantizes the token's row; the slot's launches warm the GPU up
+ *   for the kinds after it), 1 q/k/v (+norm, rope, KV write;
  *   as layers after the first run it), 2 attention (split
  *   partials, or the normalised output when the cache fits one split),
  *   3 o-projection (+residual; as in the step at this length: with 2..8

@@ -580,7 +580,9 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     a.o = a.n_splits == 1 ? m->at<float>(m->lay.att) : nullptr;
     auto launch = [&](int kind) -> hipError_t {
         switch (kind) {
-            case 0: return hipSuccess;  // the decode step has no embedding kernel
+            case 0:  // the step has no embedding kernel: these launches only warm the
+                     // GPU up for the timed kinds (reported as -1)
+                return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
             case 1:  // q/k/v as every layer but the first runs it (that one also reads the embedding)
                 return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
             case 2: return launch_attn_decode(a, s);
