@@ -332,8 +332,9 @@ struct QkvArgs {
     int rope_neox;       // 1: q and k are written unrotated (a separate kernel rotates them)
     // Decode of layer 0: the input row is the token's embedding (Q8_0 row of
     // embed, token from st), dequantized here; workgroup 0 also writes it to
-    // x as the residual. NULL: the row is read from x.
+    // xres (the residual). NULL: the row is read from x.
     const uint8_t *embed;
+    float *xres;
     int V;
 };
 
@@ -791,7 +792,6 @@ __device__ void stage_embed1(const QkvArgs &a, const CoreArgs &c, const Lds1 &l)
     const uint32_t tok = a.st->token;
     const bool valid = tok < uint32_t(a.V);
     const uint8_t *row = a.embed + (valid ? size_t(tok) : 0) * (size_t(H) / kQK * kQBytes);
-    float *xres = const_cast<float *>(a.x);
     float ss = 0.f;
     for (int e = tid; e < n4; e += kThreads) {
         const uint8_t *blk = row + size_t(e >> 3) * kQBytes;   // 8 float4 per 32-weight block
@@ -803,7 +803,7 @@ __device__ void stage_embed1(const QkvArgs &a, const CoreArgs &c, const Lds1 &l)
         v.z = valid ? d * static_cast<float>(static_cast<int8_t>(blk[4 + i0])) : 0.f;
         v.w = valid ? d * static_cast<float>(static_cast<int8_t>(blk[5 + i0])) : 0.f;
         *reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4) = v;
-        if (blockIdx.x == 0) *reinterpret_cast<float4 *>(xres + size_t(e) * 4) = v;
+        if (blockIdx.x == 0) *reinterpret_cast<float4 *>(a.xres + size_t(e) * 4) = v;
         ss = fmaf(v.x, v.x, ss);
         ss = fmaf(v.y, v.y, ss);
         ss = fmaf(v.z, v.z, ss);
@@ -1202,11 +1202,11 @@ static hipError_t set_lds(const void *fn, size_t bytes) {
 
 hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const StepState *st,
                       const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s,
-                      const uint8_t *embed) {
+                      const uint8_t *embed, float *xres) {
     const int maxt = T == 1 ? 1 : kMaxTokChunk;
-    if (embed && T != 1) return hipErrorInvalidValue;
+    if (embed && (T != 1 || !xres)) return hipErrorInvalidValue;
     QkvArgs a;
-    a.embed = embed; a.V = d.V;
+    a.embed = embed; a.xres = xres; a.V = d.V;
     a.wq = w.wq; a.wk = w.wk; a.wv = w.wv; a.norm_w = w.attn_norm; a.x = x; a.st = st;
     a.rope = rope; a.q = q; a.kc = kc; a.vc = vc;
     a.QD = d.nh * d.hd; a.KVD = d.nkv * d.hd; a.hd = d.hd; a.max_seq = d.max_seq; a.T = T;

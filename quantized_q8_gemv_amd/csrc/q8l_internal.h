@@ -92,10 +92,10 @@ hipError_t launch_embed(const uint8_t *E, int H, int V, const StepState *st,
 // q/k/v projections with RMSNorm in front, rope on q and k, k/v written to
 // the cache at slot+t. Tokens [0, T) in chunks of up to kMaxTokChunk.
 // With embed (decode only, T = 1): the input row is the embedding of the
-// step's token (Q8_0 rows of embed), and x receives it as the residual.
+// step's token (Q8_0 rows of embed), and xres receives it as the residual.
 hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const StepState *st,
                       const float2 *rope, float *q, float *kc, float *vc, int T,
-                      hipStream_t s, const uint8_t *embed = nullptr);
+                      hipStream_t s, const uint8_t *embed = nullptr, float *xres = nullptr);
 // Y[t] (+)= W U[t] for generic use (o-proj / down with accumulate = 1).
 hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
                          const float *norm_w, float eps, int accumulate, float *Y,

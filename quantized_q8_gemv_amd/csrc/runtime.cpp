@@ -203,7 +203,8 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
         } else {
             // a decode step's first layer dequantizes the token's embedding itself
             const uint8_t *emb = (T == 1 && l == 0) ? m->tok_embd : nullptr;
-            if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s, emb)) != hipSuccess) return e;
+            if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s, emb, emb ? x : nullptr)) != hipSuccess)
+                return e;
         }
         if (d.rope_neox && (e = launch_rope_neox(d, st, rope, q, m->kc(l), T, s)) != hipSuccess) return e;
         if (T == 1) {
