@@ -757,10 +757,13 @@ __global__ __launch_bounds__(kThreads) void k_rms_split(float *x, int T, int K, 
 
 int row_tiles(int n, int tn) { return (n + tn - 1) / tn; }
 
-// Tile choice: the large tile (64 x 128) when it still gives every CU a
-// workgroup, otherwise the small one (32 x 64: short prompts, narrow matrices).
+// Tile choice: the large tile (64 x 128) when it still gives every CU two
+// workgroups, otherwise the small one (32 x 64: short prompts, narrow
+// matrices). Measured on the 7B-class shape: a threshold of 256 gave 28.6 ms
+// for a 512-token prefill, 512 gave 28.4; 1024 gave 28.3 but moved gate/up
+// at 203 tokens to small tiles (15.5 -> 17.3 ms for that prefill).
 bool large_tiles(int T, int n_tiles_large) {
-    return long((T + 63) / 64) * n_tiles_large >= 256;
+    return long((T + 63) / 64) * n_tiles_large >= 512;
 }
 
 // K steps of global loads in flight per workgroup: one when the grid fills
