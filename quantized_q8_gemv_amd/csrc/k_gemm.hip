@@ -757,13 +757,14 @@ __global__ __launch_bounds__(kThreads) void k_rms_split(float *x, int T, int K, 
 
 int row_tiles(int n, int tn) { return (n + tn - 1) / tn; }
 
-// Tile choice: the large tile (64 x 128) when it still gives every CU two
-// workgroups, otherwise the small one (32 x 64: short prompts, narrow
-// matrices). Measured on the 7B-class shape: a threshold of 256 gave 28.6 ms
-// for a 512-token prefill, 512 gave 28.4; 1024 gave 28.3 but moved gate/up
-// at 203 tokens to small tiles (15.5 -> 17.3 ms for that prefill).
+// Tile choice: the large tile (64 x 128) when it gives at least 1.5
+// workgroups per CU, otherwise the small one (32 x 64: short prompts, narrow
+// matrices). Measured on the 7B-class 512-token prefill: a threshold of 256
+// (o and down on large tiles, one workgroup per CU) gave 28.6 ms, 512 (qkv on
+// small tiles too) 28.4 ms, 384 27.5 ms; 1024 also moved gate/up at 203
+// tokens to small tiles (15.5 -> 17.3 ms for that prefill).
 bool large_tiles(int T, int n_tiles_large) {
-    return long((T + 63) / 64) * n_tiles_large >= 512;
+    return long((T + 63) / 64) * n_tiles_large >= 384;
 }
 
 // K steps of global loads in flight per workgroup: one when the grid fills
