@@ -258,6 +258,33 @@ q8l_status q8l_op_attention(const float *Q, const float *K, const float *V, int3
 size_t q8l_op_attention_workspace(int32_t T, int32_t kv_len, int32_t n_head, int32_t n_head_kv,
                                   int32_t hd);
 
+/* Size of the device array q8l_op_attention_noalloc keeps its partial results
+ * in (per device): 4 MiB holds the single-query split partials
+ * [n_head][ceil(kv_len / C)][head_dim + 2] f32 (C = 64 keys for head_dim <= 64,
+ * else 32), e.g. 32 heads of 128 over 4096 keys = 2.1 MB. */
+#define Q8L_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/*
+ * q8l_op_attention without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments (minus the workspace),
+ * layouts and results -- bitwise, the same kernels -- as q8l_op_attention.
+ * The single-query case (T == 1) keeps its split partials in a static device
+ * array of Q8L_NOALLOC_SCRATCH_BYTES that each device holds until the process
+ * ends; the call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine). T > 1 uses no scratch memory.
+ * Errors: Q8L_E_INVALID_ARG as for q8l_op_attention, and when T == 1 and the
+ * partials would exceed Q8L_NOALLOC_SCRATCH_BYTES; Q8L_E_HIP if the array's
+ * device address cannot be looked up or a launch fails.
+ * Every call on one device shares that device's array and leaves its
+ * contents behind (each call writes every partial it reads): calls that
+ * overlap in time on one device (two streams, or two host threads) race on
+ * it, so the caller must serialise them.
+ */
+q8l_status q8l_op_attention_noalloc(const float *Q, const float *K, const float *V, int32_t T,
+                                    int32_t kv_len, int32_t kv_stride, int32_t n_head,
+                                    int32_t n_head_kv, int32_t hd, float *O, void *stream);
+
 /* Largest element of x (f32[n], device), lowest index on ties, to *out.
  * workspace_bytes >= 8 * ceil(n / 4096). */
 q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspace,

@@ -81,6 +81,8 @@ _SIGS = {
                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t,
                           _P], ctypes.c_int),
     "q8l_op_attention_workspace": ([ctypes.c_int32] * 5, ctypes.c_size_t),
+    "q8l_op_attention_noalloc": ([_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P], ctypes.c_int),
     "q8l_op_argmax": ([_P, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "q8l_time_decode_kernels": ([_P, ctypes.c_int32, _P, _P], ctypes.c_int),
     "q8l_gguf_open": ([ctypes.c_char_p, ctypes.POINTER(_P)], ctypes.c_int),
@@ -225,6 +227,12 @@ def q8l_op_attention(Q, K, V, T: int, kv_len: int, kv_stride: int, n_head: int, 
 
 def q8l_op_attention_workspace(T: int, kv_len: int, n_head: int, n_head_kv: int, hd: int) -> int:
     return int(lib().q8l_op_attention_workspace(T, kv_len, n_head, n_head_kv, hd))
+
+
+def q8l_op_attention_noalloc(Q, K, V, T: int, kv_len: int, kv_stride: int, n_head: int, n_head_kv: int,
+                             hd: int, O, stream=None) -> int:
+    return lib().q8l_op_attention_noalloc(_ptr(Q), _ptr(K), _ptr(V), T, kv_len, kv_stride, n_head, n_head_kv,
+                                          hd, _ptr(O), _stream(stream))
 
 
 def q8l_op_argmax(x, n: int, out, workspace, workspace_bytes: int, stream=None) -> int:
