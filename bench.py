@@ -19,15 +19,28 @@ Printed JSON line:
                    the same per-token time with the 256 MB memory-side cache
                    flushed before each step (a 512 MiB copy outside the timed
                    region): the weights stream from HBM
+  step_frac        the decode step's HBM-roofline fraction: algorithmic bytes per
+                   token / device-loop time per token / 8 TB/s
   roofline         the decode kernel with the most time per step, its algorithmic
-                   bytes per launch over its mean launch time (HIP events)
+                   bytes per launch over its mean launch time (HIP events around
+                   back-to-back launches, each on the next layer's weights), and
+                   the same kernel's mean duration in the committed rocprofv3
+                   summary of this workload (profile_us, profile_frac)
   cpu_baseline     the CPU oracle timed on a bounded sample of the same workload
+                   (all threads, and one thread), with the host's CPU model
   host_loop_reps   min and median over the timed steps (per-token decode, prefill)
+  configs          the other workloads, each measured the same way outside the
+                   timed region: tiny (13 + 20), 203 + 128 (1 warm-up rep + 10
+                   reps with a fresh cache, min and median), 4000 + 96 (decode
+                   cost against cache length) and the 7B-class 512 + 128, each
+                   with its own CPU-oracle sample
 
 Other modes: --pmc-summary FETCH_DIR WRITE_DIR summarises two rocprofv3
-counter runs (no GPU); --formats times one matmul per block format; --kv-sweep prints
-one line per cache length (16 ... 4000 prompt tokens on the 135M-shaped
-model): device-loop us/token and the attention kernel's time at that length.
+counter runs (no GPU); --stats-summary CSV turns a rocprofv3 kernel_stats.csv
+into the table kept in profiles/ (no GPU); --formats times one matmul per
+block format; --kv-sweep prints one line per cache length (16 ... 4000 prompt
+tokens on the 135M-shaped model): device-loop us/token and the attention
+kernel's time at that length.
 """
 
 from __future__ import annotations
@@ -105,6 +118,50 @@ def measured_traffic(config, kind):
             return None
         return int(f["bytes_per_launch"])
     return None
+
+
+# rocprofv3 --kernel-trace --stats summaries of the bench command per workload;
+# a summary's figures count only while the sources it lists are unchanged.
+STATS_FILES = {"C2": "profiles/decode_prefill_135m_13+20_kernel_stats.md"}
+STATS_SOURCES = ["quantized_q8_gemv_amd/csrc/k_gemv.hip", "quantized_q8_gemv_amd/csrc/k_attn.hip",
+                 "quantized_q8_gemv_amd/csrc/runtime.cpp"]
+
+
+def short_symbol(name):
+    import re
+    m = re.match(r"(?:void )?(?:q8l::\(anonymous namespace\)::|q8l::)?([^(]*)", name)
+    return m.group(1).strip() if m and not name.startswith("_Z") else name
+
+
+def stats_summary(csv_path):
+    """The markdown table of a rocprofv3 kernel_stats.csv (one row per kernel
+    symbol: calls, mean / min / max duration, share of GPU time) and the
+    digests of the sources the profiled kernels were built from."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    print("| kernel | calls | avg us | min us | max us | share % |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for r in rows:
+        print(f"| `{short_symbol(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    print()
+    print("sources: " + " ".join(f"{p}={source_digest(p)}" for p in STATS_SOURCES))
+
+
+def profiled_us(config, symbol):
+    """Mean duration (us) of `symbol` in the committed kernel statistics of
+    this workload, or None if there are none or a listed source changed."""
+    path = STATS_FILES.get(config)
+    if not path or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    us, fresh = None, False
+    for line in open(os.path.join(ROOT, path)):
+        if line.startswith("sources:"):
+            pairs = dict(kv.split("=", 1) for kv in line.split()[1:])
+            fresh = all(p in pairs and source_digest(p) == pairs[p] for p in STATS_SOURCES)
+        elif line.startswith(f"| `{symbol}` |"):
+            us = float(line.split("|")[3])
+    return us if fresh else None
 
 
 def pmc_summary(fetch_dir, write_dir, config="C2"):
@@ -250,20 +307,47 @@ def kernel_bytes(s, kv_len, down_fmt="q8_0"):
     ]
 
 
-def cpu_baseline(model, prompt, steps, seconds):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def omp_threads(n=None):
+    """Set (when n is given) and read the OpenMP thread count of the runtime
+    the oracle's library uses (libgomp), or None without it."""
+    try:
+        g = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    if n is not None:
+        g.omp_set_num_threads(int(n))
+    g.omp_get_max_threads.restype = ctypes.c_int
+    return int(g.omp_get_max_threads())
+
+
+def cpu_baseline(model, prompt, steps, seconds, threads=None):
     """The oracle, as it stands, on the same workload: repeat the generation
     until `seconds` of CPU work; report decode tokens/s. For models whose
     oracle prefill alone would exceed the budget, the sample keeps the first
-    few prompt tokens and as many decode steps as fit."""
+    four prompt tokens and as many decode steps as fit (at most 8): the
+    decode rate is then an extrapolation from those steps."""
     import oracle
 
     oracle.build(force=False)
+    prev = omp_threads()
+    used = omp_threads(threads) if threads else prev
     om = oracle.OracleModel(model)
     params = sum(t.rows * t.cols for t in model.tensors)
+    note = ""
     if params * len(prompt) > 2e10:          # oracle prefill alone would take long
         prompt = prompt[:4]
-        steps = max(1, min(steps, int(seconds * 2e9 / params)))
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+        steps = max(1, min(steps, 8, int(seconds * 2e9 / params)))
+        note = "; prompt cut to its first 4 tokens and the decode to the first steps (per-token extrapolation)"
     t_dec, n_dec, reps, t_all0 = 0.0, 0, 0, time.perf_counter()
     while True:
         st, lg, _ = om.forward(prompt, 0)
@@ -277,9 +361,13 @@ def cpu_baseline(model, prompt, steps, seconds):
         reps += 1
         if time.perf_counter() - t_all0 >= seconds:
             break
+    if threads and prev:
+        omp_threads(prev)
+    cores = used or int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
     return {"value": n_dec / t_dec, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{reps} x (prefill {len(prompt)} + {steps} decode steps) of the same model; "
-                      f"decode tokens/s over {t_dec:.1f} s of decode"}
+                      f"decode tokens/s over {t_dec:.1f} s of decode{note}"}
 
 
 # The pages' CPU timings of one QMatMul on the down projection's shape, by
@@ -367,6 +455,148 @@ def format_matmuls(reps):
     return lines
 
 
+class HostLoop:
+    """The pages' generation loop on one model: prefill at position 0, then
+    `steps` single-token forwards, each followed by the greedy id's readback.
+
+    The greedy id goes to pinned host memory that the last kernel writes
+    directly; the host polls that word (reset to -1, never a token id, before
+    each forward) and reads the id as soon as it lands -- the 4-byte readback
+    of each step, without a copy or a blocking stream sync (the next forward
+    is ordered after the rest of the step by the stream)."""
+
+    def __init__(self, gm, prompt, steps):
+        import numpy as np
+        import torch
+        from quantized_q8_gemv_amd.model import host_mapped_u32
+
+        self.gm, self.steps = gm, steps
+        self.am_host, self.am_dev = host_mapped_u32()
+        self.am_np = self.am_host.numpy()
+        self.stream = torch.cuda.current_stream()
+        self.tok = np.zeros(1, dtype=np.uint32)
+        self.prompt = np.ascontiguousarray(np.asarray(prompt, dtype=np.uint32))
+
+    def _read_id(self):
+        deadline = time.perf_counter() + 10.0
+        while self.am_np[0] == -1:
+            if time.perf_counter() > deadline:
+                self.stream.synchronize()
+                if self.am_np[0] == -1:
+                    raise RuntimeError("the forward did not write its argmax")
+        return int(self.am_np[0])
+
+    def generation(self):
+        """One generation; returns (prefill seconds, decode seconds)."""
+        from quantized_q8_gemv_amd import q8l as C
+
+        t0 = time.perf_counter()
+        self.am_np[0] = -1
+        st = self.gm.forward_async(self.prompt, 0, argmax_out=self.am_dev)
+        assert st == C.Q8L_OK, C.q8l_last_error(self.gm.handle)
+        nxt = self._read_id()
+        t1 = time.perf_counter()
+        for k in range(self.steps):
+            self.tok[0] = nxt
+            self.am_np[0] = -1
+            st = self.gm.forward_async(self.tok, len(self.prompt) + k, argmax_out=self.am_dev)
+            assert st == C.Q8L_OK, C.q8l_last_error(self.gm.handle)
+            nxt = self._read_id()
+        t2 = time.perf_counter()
+        self.stream.synchronize()
+        return t1 - t0, t2 - t1
+
+
+def device_loop(gm, prompt, steps, reps, segments=1):
+    """Per-token time (ms) of q8l_generate after a prefill, HIP events around
+    each of `segments` equal parts of the decode; returns a list per rep of
+    the per-segment ms/token."""
+    import torch
+    from quantized_q8_gemv_amd import q8l as C
+
+    per = steps // segments
+    ids = torch.zeros(per, dtype=torch.int32, device="cuda:0")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(segments + 1)]
+    out = []
+    for r in range(reps):
+        assert gm.forward_async(prompt, 0) == C.Q8L_OK
+        tok = gm.argmax
+        ev[0].record()
+        for k in range(segments):
+            assert gm.generate_async(tok, len(prompt) + k * per, per, ids) == C.Q8L_OK, C.q8l_last_error(gm.handle)
+            tok = ids[per - 1:per]
+            ev[k + 1].record()
+        torch.cuda.synchronize()
+        out.append([ev[k].elapsed_time(ev[k + 1]) / per for k in range(segments)])
+    return out
+
+
+def measure_config(key, cpu_seconds, with_cpu):
+    """One workload measured the way the headline is, outside the timed
+    region: host loop (decode ms/token and prefill ms, min and median over
+    reps, each rep with a fresh cache: prefill at position 0 drops it), the
+    device loop with its HBM-roofline fraction, and the oracle's rate. The
+    long-context workload also reports the device loop per segment of 16
+    steps against the cache length."""
+    import torch
+
+    import synth
+    from quantized_q8_gemv_amd.model import Q8Model
+
+    t0 = time.perf_counter()
+    w, model, prompt = synth.workload_inputs(key)
+    s = model.shape
+    gm = Q8Model(synth.shape_fields(s), model.tensors, device="cuda:0")
+    torch.cuda.synchronize()
+    eprint(f"[bench] {key} {w.name}: model ready in {time.perf_counter() - t0:.1f} s")
+    steps = w.decode_steps
+    reps = w.reps if w.reps > 1 else 3
+    loop = HostLoop(gm, prompt, steps)
+    warm_pre, warm_dec = loop.generation()
+    pre, dec = [], []
+    for _ in range(reps):
+        a, b = loop.generation()
+        pre.append(a)
+        dec.append(b)
+    segments = 6 if key == "C4" else 1
+    dl = device_loop(gm, prompt, steps, reps, segments)
+    per_tok = [sum(r) / len(r) for r in dl]
+    dev_ms = statistics.median(per_tok)
+    W = per_token_weight_bytes(model)
+    kvb = kv_bytes_per_position(s)
+    b_tok = W + kvb * (len(prompt) + (steps + 1) / 2.0)
+    out = {"workload": w.name, "model": s.name, "prompt_len": len(prompt), "decode_steps": steps, "reps": reps,
+           "warmup_rep": {"prefill_ms": round(warm_pre * 1e3, 3),
+                          "decode_ms_per_token": round(warm_dec / steps * 1e3, 4)},
+           "decode_ms_per_token_host_loop": {"min": round(min(dec) / steps * 1e3, 4),
+                                             "median": round(statistics.median(dec) / steps * 1e3, 4)},
+           "decode_tok_s_host_loop": round(steps / statistics.median(dec), 1),
+           "prefill_ms": {"min": round(min(pre) * 1e3, 3), "median": round(statistics.median(pre) * 1e3, 3)},
+           "prefill_tok_s": round(len(prompt) / statistics.median(pre), 1),
+           "device_loop_us_per_token": {"min": round(min(per_tok) * 1e3, 2), "median": round(dev_ms * 1e3, 2)},
+           "bytes_per_token": int(b_tok),
+           "step_frac": round(b_tok / (dev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if segments > 1:
+        per = steps // segments
+        seg = [statistics.median(r[k] for r in dl) for k in range(segments)]
+        out["device_loop_by_kv_len"] = [
+            {"kv_len": [len(prompt) + k * per + 1, len(prompt) + (k + 1) * per],
+             "us_per_token": round(seg[k] * 1e3, 2),
+             "step_frac": round((W + kvb * (len(prompt) + (k + 0.5) * per)) / (seg[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            for k in range(segments)]
+    if key in PAGES_DECODE_MS:
+        out["pages_metal_ms_per_token"] = PAGES_DECODE_MS[key]
+    del gm
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline(model, prompt, steps, cpu_seconds)
+    eprint(f"[bench] {key}: host loop {out['decode_ms_per_token_host_loop']['median']} ms/token, device loop "
+           f"{out['device_loop_us_per_token']['median']} us/token (step_frac {out['step_frac']}), prefill "
+           f"{out['prefill_tok_s']} tok/s")
+    return out
+
+
 KV_SWEEP = [16, 64, 256, 1024, 2048, 4000]
 
 
@@ -437,6 +667,10 @@ def main():
                     help="time the single matmul per block format (Q8_0, Q4_K, Q6_K) instead")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this script; no GPU use")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the --config workload (no per-workload block for the others)")
+    ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                    help="print the profiles/ table of a rocprofv3 kernel_stats.csv; no GPU use")
     ap.add_argument("--kv-sweep", action="store_true",
                     help="decode cost against cache length on the 135M-shaped model instead "
                          "(one JSON line per length)")
@@ -446,6 +680,9 @@ def main():
         sys.exit(2)
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, config=args.config)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary)
         return
     if args.kv_sweep:
         kv_sweep(args.kernel_reps)
@@ -477,42 +714,8 @@ def main():
     gm = Q8Model(synth.shape_fields(s), model.tensors, device="cuda:0")
     torch.cuda.synchronize()
 
-    # The greedy id goes to pinned host memory that the last kernel writes
-    # directly; the host polls that word (reset to -1, never a token id,
-    # before each forward) and reads the id as soon as it lands -- the 4-byte
-    # readback of each step, without a copy or a blocking stream sync (the
-    # next forward is ordered after the rest of the step by the stream).
-    am_host, am_dev = host_mapped_u32()
-    am_np = am_host.numpy()
-    stream = torch.cuda.current_stream()
-    tok = np.zeros(1, dtype=np.uint32)
-    prompt_u32 = np.ascontiguousarray(np.asarray(prompt, dtype=np.uint32))
-
-    def read_id():
-        deadline = time.perf_counter() + 10.0
-        while am_np[0] == -1:
-            if time.perf_counter() > deadline:
-                stream.synchronize()
-                if am_np[0] == -1:
-                    raise RuntimeError("the forward did not write its argmax")
-        return int(am_np[0])
-
-    def generation():
-        t0 = time.perf_counter()
-        am_np[0] = -1
-        st = gm.forward_async(prompt_u32, 0, argmax_out=am_dev)
-        assert st == C.Q8L_OK, st
-        nxt = read_id()
-        t1 = time.perf_counter()
-        for k in range(steps):
-            tok[0] = nxt
-            am_np[0] = -1
-            st = gm.forward_async(tok, len(prompt) + k, argmax_out=am_dev)
-            assert st == C.Q8L_OK, st
-            nxt = read_id()
-        t2 = time.perf_counter()
-        stream.synchronize()
-        return t1 - t0, t2 - t1
+    loop = HostLoop(gm, prompt, steps)
+    generation = loop.generation
 
     for _ in range(args.warmup):
         generation()
@@ -598,11 +801,19 @@ def main():
                                "launches_per_token": launches[i]} for i in range(NKINDS)}
     achieved = kb[dom] / (ms[dom] * 1e-3) / 1e9
     traffic = measured_traffic(args.config, KIND_NAMES[dom]) if down_fmts is None else None
+    symbol = kernel_symbols(s, down0)[dom]
+    prof_us = profiled_us(args.config, symbol) if down_fmts is None else None
+    step_frac = round(dev_gbs / PEAK_HBM_GBS, 4)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": KIND_NAMES[dom], "symbol": kernel_symbols(s, down0)[dom],
+                "kernel": KIND_NAMES[dom], "symbol": symbol,
                 "bytes_per_launch": kb[dom], "us_per_launch": round(ms[dom] * 1e3, 2),
-                "empty_kernel_us": round(overhead * 1e3, 2)}
+                "timing": "HIP events around back-to-back launches, launch r on layer r mod n_layer",
+                "profile_us": prof_us,
+                "profile_frac": (round(kb[dom] / (prof_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4) if prof_us else None),
+                "profile": STATS_FILES.get(args.config) if prof_us else None,
+                "empty_kernel_us": round(overhead * 1e3, 2),
+                "step_frac": step_frac}
     copy_gbs = copy_bandwidth(torch)
     eprint(f"[bench] device copy: {copy_gbs:.0f} GB/s (1 GiB, read + write)")
     eprint(f"[bench] kernels: " + ", ".join(f"{k} {v['us']}us" for k, v in kernels.items() if v["us"] is not None))
@@ -611,6 +822,17 @@ def main():
     if not args.no_cpu_baseline:
         eprint(f"[bench] cpu baseline (oracle) ~{args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(model, prompt, steps, args.cpu_seconds)
+        one = cpu_baseline(model, prompt, steps, max(2.0, args.cpu_seconds / 3), threads=1)
+        cpu["value_1_thread"] = one["value"]
+        cpu["sample_1_thread"] = one["sample"]
+
+    configs = {}
+    if not args.no_configs and args.config == "C2" and down_fmts is None:
+        del gm
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        for key in ("C1", "C3", "C4", "C5"):
+            configs[key] = measure_config(key, args.cpu_seconds / 2, not args.no_cpu_baseline)
 
     out = {
         "metric": "decode tokens/s (batch 1) + achieved HBM GB/s vs peak; prefill tokens/s",
@@ -638,6 +860,7 @@ def main():
                            "decode_ms_per_token_median": round(statistics.median(dec) / steps * 1e3, 4),
                            "prefill_ms_min": round(min(pre) * 1e3, 3),
                            "prefill_ms_median": round(statistics.median(pre) * 1e3, 3)},
+        "step_frac": step_frac,
         "device_loop": {"us_per_token": round(dev_ms * 1e3, 2),
                         "us_per_token_min": round(min(dl) * 1e3, 2),
                         "tok_s": round(1e3 / dev_ms, 1),
@@ -652,6 +875,7 @@ def main():
         "copy_gbs": round(copy_gbs, 1),
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "configs": configs,
     }
     print(json.dumps(out), flush=True)
 

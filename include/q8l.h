@@ -306,9 +306,12 @@ q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspa
  *   SiLU*up), 5 down (+residual), 6 output layer (+norm, per-workgroup
  *   argmax), 7 argmax merge, 8 an empty kernel (the dispatch gap between
  *   back-to-back launches, included in every other entry).
- * Layer 0's weights are used, at the current cache length (attention over
- * cache_len + 1 keys). The residual stream, the next KV slot and the logits
- * buffer are scratch afterwards: the next forward rewrites them before use.
+ * The r-th launch of a per-layer kind (1 to 5) uses layer r mod n_layer's
+ * weights and cache, so the weights come from beyond the L2 as they do in a
+ * step, where each layer's weights are read once; attention runs over
+ * cache_len + 1 keys. The residual stream, the next KV slot of every layer
+ * and the logits buffer are scratch afterwards: the next forward rewrites
+ * them before use.
  * The cache length is unchanged. Blocks until the timings are read back.
  * Q8L_E_INVALID_ARG if reps < 1 or the cache is full.
  */

@@ -570,22 +570,25 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     StepState *S = m->state();
     float *x = m->at<float>(m->lay.x), *q = m->at<float>(m->lay.q);
     float *h = m->at<float>(m->lay.h);
-    const LayerPtrs w = m->layer(0);
     const uint8_t *wout = m->cfg.tied_output ? m->tok_embd : m->output;
-    AttnDecodeArgs a;
-    a.q = q; a.kc = m->kc(0); a.vc = m->vc(0);
-    a.part = m->at<float>(m->lay.attn_part);
-    a.st = S; a.kv_len_arg = -1; a.kv_stride = d.max_seq;
-    a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = split_bucket(m, kv_len);
-    a.scale = 1.0f / sqrtf(float(d.hd));
-    a.o = a.n_splits == 1 ? m->at<float>(m->lay.att) : nullptr;
+    const int n_splits = split_bucket(m, kv_len);
+    int rep = 0;  // launches of the current kind so far: layer rep mod n_layer
     auto launch = [&](int kind) -> hipError_t {
+        const int l = rep++ % m->cfg.n_layer;
+        const LayerPtrs w = m->layer(l);
+        AttnDecodeArgs a;
+        a.q = q; a.kc = m->kc(l); a.vc = m->vc(l);
+        a.part = m->at<float>(m->lay.attn_part);
+        a.st = S; a.kv_len_arg = -1; a.kv_stride = d.max_seq;
+        a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = n_splits;
+        a.scale = 1.0f / sqrtf(float(d.hd));
+        a.o = a.n_splits == 1 ? m->at<float>(m->lay.att) : nullptr;
         switch (kind) {
             case 0:  // the step has no embedding kernel: these launches only warm the
                      // GPU up for the timed kinds (reported as -1)
-                return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
+                return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(l), m->vc(l), 1, s);
             case 1:  // q/k/v as every layer but the first runs it (that one also reads the embedding)
-                return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(0), m->vc(0), 1, s);
+                return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(l), m->vc(l), 1, s);
             case 2: return launch_attn_decode(a, s);
             case 3:
                 if (w.fo != F_Q8_0) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
@@ -609,6 +612,7 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     for (auto &e : ev) Q8L_HIP(m, hipEventCreate(&e), "hipEventCreate");
     hipError_t err = hipSuccess;
     for (int k = 0; k < kKinds && err == hipSuccess; ++k) {
+        rep = 0;
         if ((err = launch(k)) != hipSuccess) break;  // warm-up launch, not timed
         if ((err = hipEventRecord(ev[2 * k], s)) != hipSuccess) break;
         for (int r = 0; r < reps && err == hipSuccess; ++r) err = launch(k);

@@ -77,3 +77,34 @@ def test_measured_traffic_follows_the_source_digest(tmp_path, monkeypatch):
     assert bench.measured_traffic("C2", "lmhead") is None     # digest of another source: stale
     assert bench.measured_traffic("C2", "embed") is None       # not measured
     assert synth.WORKLOADS["C2"].prompt_len == 13
+
+
+def test_stats_summary_and_profiled_duration(tmp_path, monkeypatch):
+    """--stats-summary turns a kernel_stats.csv into the profiles/ table with
+    the sources' digests; profiled_us reads a symbol's mean back only while
+    those digests match the sources."""
+    stats = tmp_path / "k_kernel_stats.csv"
+    with open(stats, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage",
+                                          "MinNs", "MaxNs", "StdDev"])
+        w.writeheader()
+        w.writerow({"Name": "void q8l::(anonymous namespace)::k_gateup1<false>(q8l::(anonymous namespace)::GateUpArgs)",
+                    "Calls": 30, "TotalDurationNs": 180000, "AverageNs": 6000.0, "Percentage": 55.0,
+                    "MinNs": 5000, "MaxNs": 7000, "StdDev": 1.0})
+        w.writerow({"Name": "k_attn_decode(q8l::AttnDecodeArgs)", "Calls": 30, "TotalDurationNs": 120000,
+                    "AverageNs": 4000.0, "Percentage": 45.0, "MinNs": 3000, "MaxNs": 5000, "StdDev": 1.0})
+    buf = io.StringIO()
+    with redirect_stdout(buf):
+        bench.stats_summary(str(stats))
+    text = buf.getvalue()
+    assert "| `k_gateup1<false>` | 30 | 6.00 | 5.00 | 7.00 | 55.00 |" in text
+    assert "| `k_attn_decode` | 30 | 4.00 |" in text
+    prof = tmp_path / "prof.md"
+    prof.write_text(text)
+    monkeypatch.setitem(bench.STATS_FILES, "CX", str(prof))
+    assert bench.profiled_us("CX", "k_gateup1<false>") == 6.0
+    assert bench.profiled_us("CX", "k_missing") is None
+    # a changed source makes the table stale
+    stale = text.replace(bench.source_digest(bench.STATS_SOURCES[0]), "0" * 16)
+    prof.write_text(stale)
+    assert bench.profiled_us("CX", "k_gateup1<false>") is None
