@@ -846,7 +846,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": (round(value / (1e3 / PAGES_DECODE_MS[args.config]), 2)
                         if args.config in PAGES_DECODE_MS and down_fmts is None else None),
-        "dtype": "f32 (Q8_0 int8 x f16-scale weights, f32 activations and accumulation)",
+        "dtype": "f32 (Q8_0 int8 x f16-scale weights; decode f32 throughout; prefill MFMA on f16 hi+lo activation pairs, f32 accumulation)",
         "data": "synthetic: random-init Q8_0 weights, uniform random prompt ids",
         "config": {"workload": w.name + ("" if down_fmts is None else f" down={args.down_format}"),
                    "model": s.name, "layers": s.n_layer, "hidden": s.n_embd,

@@ -57,7 +57,8 @@ typedef enum {
     Q8L_E_HIP = 8,            /* a HIP call failed (message has the HIP error) */
     Q8L_E_FORMAT = 9,         /* GGUF: malformed or unsupported file content */
     Q8L_E_MISSING_KEY = 10,   /* GGUF: a required metadata key is absent */
-    Q8L_E_IO = 11             /* GGUF: the file cannot be opened or read */
+    Q8L_E_IO = 11,            /* GGUF: the file cannot be opened or read */
+    Q8L_E_RANGE = 12          /* an earlier prefill met a value outside its f16 pairs' range (see q8l_forward) */
 } q8l_status;
 
 /* Q4_K and Q6_K: the 256-weight block formats of the 4-bit "K" file mix
@@ -173,6 +174,16 @@ q8l_status q8l_finalize(q8l_model *m, void *stream);
  *      single query attends to every cached position without a mask.
  *   5. cached positions + T <= max_seq_len               else Q8L_E_KV_FULL
  * Then enqueue the forward; cached positions += T.
+ *
+ * Prefill arithmetic (T >= 2 runs on the matrix cores): int8 weights exact in
+ * f16, activations as f16 pairs hi + lo (22 bits), f32 accumulation. The
+ * normalised rows are scaled per token by a power of two and the gate/up
+ * output per token and 32-wide block (only when a value would reach 2^15),
+ * both taken out exactly in f32, so those pairs keep 22 bits at any
+ * magnitude. q, k, v, the attention output and the few f32 inputs that are
+ * split on the way must stay below 2^15 in magnitude: when one does not, the
+ * model's NEXT forward or generate call returns Q8L_E_RANGE once (that
+ * prefill's logits are not exact) and does nothing else.
  */
 q8l_status q8l_forward(q8l_model *m, const uint32_t *tokens_host, int32_t n_tokens,
                        int32_t index_pos, float *logits_dev, uint32_t *argmax_dev,
@@ -218,8 +229,12 @@ void q8l_destroy(q8l_model *m);
  * with U = X (norm_w NULL) or U[t] = X[t] / sqrt(mean(X[t]^2) + eps) * norm_w
  * (RMSNorm fused in front). W is Q8_0 [N][K] (16-byte aligned), X f32 [T][K],
  * Y f32 [T][N]. When `accumulate` is 1, Y += the product (residual add).
- * K must be a multiple of 64; 1 <= T <= max(T) for which the multi-token
- * path is used (any T >= 1 is accepted; large T uses the matrix-matrix path).
+ * K must be a multiple of 64; 1 <= T <= 2^20. With norm_w set, or T <= 16
+ * (the multi-token matrix-vector kernel), the arithmetic is f32. Larger
+ * T without norm_w runs the MFMA matrix-matrix kernel on X split into f16
+ * pairs: the product is then within about 2^-22 relative per element only
+ * while every |X| < 2^15 (this entry point does not scale X and reports no
+ * range error; the model's forward scales its activations itself).
  */
 q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *X, int64_t T,
                               const float *norm_w, double eps, int32_t accumulate, float *Y,
@@ -233,7 +248,8 @@ q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *
  * W: N rows of K/256 blocks back to back (16-byte aligned), X f32 [T][K]
  * (16-byte aligned), Y f32 [T][N]; accumulate 1 adds to Y. K must be a
  * multiple of 256. T = 1 runs the matrix-vector kernel, T > 1 the MFMA
- * matrix-matrix kernel. Q8L_E_INVALID_ARG for a NULL or misaligned pointer,
+ * matrix-matrix kernel on X split into f16 pairs (as for q8l_op_matmul_q8_0,
+ * exact to about 2^-22 relative while every |X| < 2^15). Q8L_E_INVALID_ARG for a NULL or misaligned pointer,
  * another dtype, sizes out of range, or a matrix or activation block of 2 GiB
  * or more.
  */

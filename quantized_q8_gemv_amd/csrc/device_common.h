@@ -155,6 +155,11 @@ __device__ __forceinline__ void q4k_scale_min(int j, uint32_t s03, uint32_t s47,
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Magnitudes an f16 pair (hi + lo) holds with its 22 bits: hi = f16(v)
+// overflows at 65520, and keeping below 2^15 leaves lo a normal f16 for
+// every |v| >= 2^-3.
+constexpr float kPairRange = 32768.0f;
+
 // v as an f16 pair: hi = f16(v) at hi[i], lo = f16(v - hi) at hi[plane + i]
 // (the layout the matrix-matrix kernel reads its activations in).
 __device__ __forceinline__ void store_hilo(_Float16 *hi, size_t plane, size_t i, float v) {

@@ -62,6 +62,7 @@ struct GemmArgs {
     // G_PART: K split over gridDim.z slices; slice z writes its sum to part[z][T][N]
     float *part;
     int splits;
+    ActScale sc;           // activation scaling (see ActScale)
 };
 
 template <int TM, int TN>
@@ -204,8 +205,16 @@ __device__ inline void q4_to_half(uint32_t w, half2v &lo, half2v &hi) {
     hi = __builtin_bit_cast(half2v, h) - bias;
 }
 
+// Step ks of the A tile, registers -> LDS. f32 input (A32) is split into an
+// f16 pair here; a value outside the pair's range (|v| >= 2^15, or not
+// finite) sets sc.range_flag. Split planes are copied, and when `resc` (some
+// row of the tile has a nonzero row exponent sc.eg) block b of row t is
+// first multiplied by 2^(eg[t] - el[t][b]): every block of a row then carries
+// the row's common exponent, which the epilogue takes out (exact powers of
+// two; a block far below the row's largest may lose bits to f16 subnormals).
 template <bool A32, int TM, int TN>
-__device__ inline void a_store(const u32x4 *ra, _Float16 *ahi, _Float16 *alo) {
+__device__ inline void a_store(const u32x4 *ra, _Float16 *ahi, _Float16 *alo, const GemmArgs &a, int m0, int ks,
+                               bool resc) {
     using C = Cfg<TM, TN>;
     const int tid = threadIdx.x;
 #pragma unroll
@@ -216,26 +225,57 @@ __device__ inline void a_store(const u32x4 *ra, _Float16 *ahi, _Float16 *alo) {
             const float4 v = __builtin_bit_cast(float4, ra[i]);
             const float vv[4] = {v.x, v.y, v.z, v.w};
             _Float16 hi[4], lo[4];
+            bool bad = false;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
+                bad |= !(fabsf(vv[k]) < kPairRange);
                 hi[k] = static_cast<_Float16>(vv[k]);
                 lo[k] = static_cast<_Float16>(vv[k] - static_cast<float>(hi[k]));
             }
+            if (bad && a.sc.range_flag) *a.sc.range_flag = 1u;
             *reinterpret_cast<uint2 *>(ahi + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, hi);
             *reinterpret_cast<uint2 *>(alo + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, lo);
         } else {
             const int plane = c / (TM * 8), rr = c - plane * (TM * 8);
             const int m = rr >> 3, p = rr & 7;
-            *reinterpret_cast<u32x4 *>((plane ? alo : ahi) + m * LPAD + p * 8) = ra[i];
+            u32x4 v = ra[i];
+            if (resc && m0 + m < a.T) {
+                const int t = m0 + m;
+                const int dexp = a.sc.eg[t] - int(a.sc.el[size_t(t) * a.sc.el_stride + 2 * ks + (p >> 2)]);
+                if (dexp != 0) {
+                    half8 h = __builtin_bit_cast(half8, v);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) h[k] = static_cast<_Float16>(ldexpf(static_cast<float>(h[k]), dexp));
+                    v = __builtin_bit_cast(u32x4, h);
+                }
+            }
+            *reinterpret_cast<u32x4 *>((plane ? alo : ahi) + m * LPAD + p * 8) = v;
         }
     }
 }
 
+// Whether some row of the tile starting at m0 carries a nonzero row exponent
+// (then its A blocks are brought to the row's exponent on their way to LDS).
+template <int TM>
+__device__ inline bool tile_rescales(const GemmArgs &a, int m0) {
+    int any = 0;
+    if (a.sc.eg && threadIdx.x < TM && m0 + int(threadIdx.x) < a.T) any = a.sc.eg[m0 + threadIdx.x] != 0;
+    return __syncthreads_or(any) != 0;
+}
+
+// The factor that takes row t's scaling out of a product: sc.rs[t] (the
+// normalised input's per-row factor) and 2^-eg[t] (the row exponent).
+__device__ inline float row_factor(const GemmArgs &a, int t, bool resc) {
+    float f = a.sc.rs ? a.sc.rs[t] : 1.0f;
+    if (resc) f = ldexpf(f, -a.sc.eg[t]);
+    return f;
+}
+
 template <bool A32, int TM, int TN>
-__device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf) {
+__device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf, const GemmArgs &a, int m0, int ks, bool resc) {
     using C = Cfg<TM, TN>;
     const int tid = threadIdx.x;
-    a_store<A32, TM, TN>(r.a, bf.ahi, bf.alo);
+    a_store<A32, TM, TN>(r.a, bf.ahi, bf.alo, a, m0, ks, resc);
 #pragma unroll
     for (int i = 0; i < C::BU; ++i) {
         const int u = tid + i * kThreads;
@@ -305,6 +345,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
     }
     GSrc<TM, TN> src;
     g_setup<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, src);
+    const bool resc = A32 ? false : tile_rescales<TM>(a, m0);
     // Every stage issues its loads unconditionally (steps past the end
     // re-read the last step, whose registers are never stored): with no
     // branch around them the compiler can wait for the oldest stage alone
@@ -318,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
             const int ks = k0 + j;
             if (ks >= nsteps) break;
             const GBuf bf = gbuf<TM, TN>(smem, ks & 1);
-            g_store<A32, TM, TN>(regs[j], bf);
+            g_store<A32, TM, TN>(regs[j], bf, a, m0, kfirst + ks, resc);
             __syncthreads();
             if (S == 1) {
                 if (ks + 1 < nsteps) g_load<A32, TM, TN>(src, kfirst + ks + 1, regs[j]);
@@ -372,20 +413,46 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
         }
         __syncthreads();
         if (wn == 0) {
+            // h = silu(g) * up in f32, then per (row, 32-column block) the
+            // exponent that keeps the block's largest |h| below 2^15 (0 when it
+            // already is): the block's 32 columns are ns = 2bb, 2bb + 1 of the
+            // 16 lanes sharing lane >> 4.
             const size_t plane = size_t(a.T) * a.Nm[0];
 #pragma unroll
             for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
-                for (int ns = 0; ns < C::NS; ++ns)
+                for (int i = 0; i < 4; ++i) {
+                    const int m = wm * C::WM + ms * 16 + 4 * (lane >> 4) + i;
+                    const int t = m0 + m;
+                    const float f = t < a.T ? row_factor(a, t, false) : 1.0f;
+                    float hv[C::NS];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int m = wm * C::WM + ms * 16 + 4 * (lane >> 4) + i;
+                    for (int ns = 0; ns < C::NS; ++ns) {
                         const int c = ns * 16 + (lane & 15);
-                        if (m0 + m < a.T && c < nvalid[0]) {
-                            const float g = acc[ms][ns][i], u = ub[m * C::WN + c];
-                            store_hilo(a.h, plane, size_t(m0 + m) * a.Nm[0] + row0 + c, silu(g) * u);
+                        const float h = silu(acc[ms][ns][i] * f) * (ub[m * C::WN + c] * f);
+                        hv[ns] = (t < a.T && c < nvalid[0]) ? h : 0.f;
+                    }
+#pragma unroll
+                    for (int bb = 0; bb < (C::NS + 1) / 2; ++bb) {
+                        float mx = fabsf(hv[2 * bb]);
+                        if (2 * bb + 1 < C::NS) mx = fmaxf(mx, fabsf(hv[2 * bb + 1]));
+#pragma unroll
+                        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                        int e = 0;
+                        if (!(mx < kPairRange)) e = isfinite(mx) ? max(14 - ilogbf(mx), -126) : -126;
+                        if (t < a.T && a.sc.el_out && (lane & 15) == 0 && 32 * bb < nvalid[0]) {
+                            a.sc.el_out[size_t(t) * a.sc.el_stride + (row0 >> 5) + bb] = int8_t(e);
+                            if (e < 0) atomicMin(a.sc.eg_out + t, e);
+                        }
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int ns = 2 * bb + q;
+                            const int c = ns * 16 + (lane & 15);
+                            if (ns < C::NS && t < a.T && c < nvalid[0])
+                                store_hilo(a.h, plane, size_t(t) * a.Nm[0] + row0 + c, ldexpf(hv[ns], e));
                         }
                     }
+                }
         }
         return;
     }
@@ -397,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int m = wm * C::WM + ms * 16 + 4 * (lane >> 4) + i;
                 const int c = wn * C::WN + ns * 16 + (lane & 15);
-                const float v = acc[ms][ns][i];
+                const float v = acc[ms][ns][i] * (m0 + m < a.T ? row_factor(a, m0 + m, resc) : 1.0f);
                 if (EPI == G_QKV) {
                     // rope pairs (2j, 2j+1) sit in adjacent lanes
                     const float partner = __shfl_xor(v, 1, 64);
@@ -621,6 +688,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
         for (int j = 0; j < C::NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nsteps = a.K / GK;
+    const bool resc = A32 ? false : tile_rescales<TM>(a, m0);
     KRegs<FMT, TM, TN> regs;
     a_load<A32, TM, TN>(src.ra, src.aoff, 0, regs.a);
     kb_load<FMT, TM, TN>(src, 0, regs);
@@ -631,7 +699,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
         uint8_t *p = smem + size_t(ks & 1) * KC::BUF;
         _Float16 *ahi = reinterpret_cast<_Float16 *>(p), *alo = ahi + C::A_HALVES, *bq = alo + C::A_HALVES;
         float *bd = reinterpret_cast<float *>(bq + C::B_HALVES);
-        a_store<A32, TM, TN>(regs.a, ahi, alo);
+        a_store<A32, TM, TN>(regs.a, ahi, alo, a, m0, ks, resc);
         kb_store<FMT, TM, TN>(src, ks, regs, bq, bd);
         __syncthreads();
         if (ks + 1 < nsteps) {
@@ -702,18 +770,23 @@ __global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
                 const int c = wn * C::WN + ns * 16 + (lane & 15);
                 if (m0 + m >= a.T || c >= nvalid) continue;
                 float *dst = a.Y + size_t(m0 + m) * a.Nm[0] + row0 + c;
-                *dst = (EPI == G_ACCUM) ? *dst + acc[ms][ns][i] : acc[ms][ns][i];
+                const float v = acc[ms][ns][i] * row_factor(a, m0 + m, resc);
+                *dst = (EPI == G_ACCUM) ? *dst + v : v;
             }
 }
 
 // u = x / sqrt(mean(x^2) + eps) * w for each token row, written as the f16
-// hi plane [T][K] followed by the lo plane. One workgroup per row.
-// With splits > 0 the residual add of a split-K product happens here first:
-// x += part[0] + part[1] + ... (that order), written back to x. With u NULL
-// only that add is done.
+// hi plane [T][K] followed by the lo plane, each row multiplied first by the
+// power of two 2^e that puts its largest |u| in [2^14, 2^15) (exact; the
+// pair then holds every value with its 22 bits, however large or small the
+// row); rs[row] = 2^-e for the products' epilogues (1 for a zero row). One
+// workgroup per row. With splits > 0 the residual add of a split-K product
+// happens here first: x += part[0] + part[1] + ... (that order), written back
+// to x. With u NULL only that add is done. eg_zero (if set) is cleared for the
+// row: the row exponent of planes a later kernel of the layer writes.
 __global__ __launch_bounds__(kThreads) void k_rms_split(float *x, int T, int K, const float *w,
                                                         float eps, _Float16 *u, const float *part,
-                                                        int splits) {
+                                                        int splits, float *rs, int *eg_zero) {
     __shared__ float red[4];
     const size_t row = blockIdx.x;
     float4 *xr = reinterpret_cast<float4 *>(x + row * K);
@@ -736,14 +809,30 @@ __global__ __launch_bounds__(kThreads) void k_rms_split(float *x, int T, int K, 
         ss = fmaf(v.z, v.z, ss);
         ss = fmaf(v.w, v.w, ss);
     }
+    if (eg_zero && threadIdx.x == 0) eg_zero[row] = 0;
     if (!u) return;
     ss = block_sum(ss, red);
     const float r = 1.0f / sqrtf(ss / static_cast<float>(K) + eps);
+    float mx = 0.f;
+    for (int e = threadIdx.x; e < n4; e += kThreads) {
+        const float4 v = xr[e];
+        const float4 g = reinterpret_cast<const float4 *>(w)[e];
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x * r * g.x), fabsf(v.y * r * g.y)),
+                             fmaxf(fabsf(v.z * r * g.z), fabsf(v.w * r * g.w))));
+    }
+    mx = wave_max(mx);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int ex = (mx > 0.f && isfinite(mx)) ? min(max(14 - ilogbf(mx), -126), 126) : 0;
+    if (rs && threadIdx.x == 0) rs[row] = ldexpf(1.0f, -ex);
     const size_t plane = size_t(T) * K;
     for (int e = threadIdx.x; e < n4; e += kThreads) {
         const float4 v = xr[e];
         const float4 g = reinterpret_cast<const float4 *>(w)[e];
-        const float vv[4] = {v.x * r * g.x, v.y * r * g.y, v.z * r * g.z, v.w * r * g.w};
+        const float vv[4] = {ldexpf(v.x * r * g.x, ex), ldexpf(v.y * r * g.y, ex), ldexpf(v.z * r * g.z, ex),
+                             ldexpf(v.w * r * g.w, ex)};
         _Float16 hi[4], lo[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -841,8 +930,8 @@ GemmArgs gemm_base(const void *A, int T, int K) {
 }  // namespace
 
 hipError_t launch_rms_split(float *x, int T, int K, const float *w, float eps, _Float16 *u,
-                            const float *part, int splits, hipStream_t s) {
-    hipLaunchKernelGGL(k_rms_split, dim3(T), dim3(kThreads), 0, s, x, T, K, w, eps, u, part, splits);
+                            const float *part, int splits, hipStream_t s, float *rs, int *eg_zero) {
+    hipLaunchKernelGGL(k_rms_split, dim3(T), dim3(kThreads), 0, s, x, T, K, w, eps, u, part, splits, rs, eg_zero);
     return hipGetLastError();
 }
 
@@ -867,28 +956,28 @@ int gemm_splitk(int N, int K, int T) {
 }
 
 hipError_t launch_gemm_part(const uint8_t *W, int N, int K, const _Float16 *A, int T, int splits, float *part,
-                            hipStream_t s) {
+                            hipStream_t s, const ActScale &sc) {
     if (splits < 1 || splits > kSplitKMax || splits > K / GK || T > gemm_splitk_max_tokens(N))
         return hipErrorInvalidValue;
     GemmArgs a = gemm_base(A, T, K);
-    a.W[0] = W; a.Nm[0] = N; a.part = part; a.splits = splits;
+    a.W[0] = W; a.Nm[0] = N; a.part = part; a.splits = splits; a.sc = sc;
     return launch_cfg<G_PART, 32, 64, false>(a, row_tiles(N, 64), s);
 }
 
 hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
-                              int accumulate, float *Y, hipStream_t s) {
+                              int accumulate, float *Y, hipStream_t s, const ActScale &sc) {
     GemmArgs a = gemm_base(A, T, K);
-    a.W[0] = W; a.Nm[0] = N; a.Y = Y;
+    a.W[0] = W; a.Nm[0] = N; a.Y = Y; a.sc = sc;
     if (a_split)
         return accumulate ? launch_plain<G_ACCUM, false>(a, N, s) : launch_plain<G_STORE, false>(a, N, s);
     return accumulate ? launch_plain<G_ACCUM, true>(a, N, s) : launch_plain<G_STORE, true>(a, N, s);
 }
 
 hipError_t launch_gemm_kq(int fmt, const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
-                          int accumulate, float *Y, hipStream_t s) {
+                          int accumulate, float *Y, hipStream_t s, const ActScale &sc) {
     if (K % kQKK || (fmt != F_Q4_K && fmt != F_Q6_K)) return hipErrorInvalidValue;
     GemmArgs a{};
-    a.A = A; a.T = T; a.K = K;
+    a.A = A; a.T = T; a.K = K; a.sc = sc;
     a.rowbytes = int(fmt_row_bytes(fmt, K));
     a.W[0] = W; a.Nm[0] = N; a.Y = Y;
     return fmt == F_Q4_K ? launch_kq_fmt<F_Q4_K>(a, a_split, accumulate, s)
@@ -896,8 +985,10 @@ hipError_t launch_gemm_kq(int fmt, const uint8_t *W, int N, int K, const void *A
 }
 
 hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u, const StepState *st,
-                           const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s) {
+                           const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s,
+                           const ActScale &sc) {
     GemmArgs a = gemm_base(u, T, d.H);
+    a.sc = sc;
     const int QD = d.nh * d.hd, KVD = d.nkv * d.hd;
     a.W[0] = w.wq; a.W[1] = w.wk; a.W[2] = w.wv;
     a.Nm[0] = QD; a.Nm[1] = KVD; a.Nm[2] = KVD;
@@ -911,8 +1002,9 @@ hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u,
 }
 
 hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const _Float16 *u, _Float16 *h, int T,
-                              hipStream_t s) {
+                              hipStream_t s, const ActScale &sc) {
     GemmArgs a = gemm_base(u, T, d.H);
+    a.sc = sc;
     a.W[0] = w.wg; a.W[1] = w.wu; a.Nm[0] = d.F; a.Nm[1] = d.F; a.h = h;
     if (large_tiles(T, row_tiles(d.F, 64))) return launch_cfg<G_GATEUP, 64, 128, false>(a, row_tiles(d.F, 64), s);
     return launch_cfg<G_GATEUP, 32, 64, false>(a, row_tiles(d.F, 32), s);

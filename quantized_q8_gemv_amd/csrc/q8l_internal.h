@@ -150,11 +150,37 @@ int attn_decode_splits(int kv_len, int hd);
 __host__ __device__ inline int attn_chunk(int hd) { return hd <= 64 ? 64 : 32; }
 size_t lmhead_partials_bytes(int V, int K);
 
+// Scaling of the activations the MFMA kernels take as f16 pairs (hi + lo):
+//   rs        per-token factor of a normalised input: the rows of u were
+//             multiplied by 1/rs[t] (a power of two putting the row's largest
+//             |u| in [2^14, 2^15)); the epilogue multiplies by rs[t]
+//   eg, el    per-token and per-(token, 32-wide block) exponents of split
+//             planes written by another kernel (el[t][b]: block b was
+//             multiplied by 2^el[t][b], 0 unless a value would reach 2^15;
+//             eg[t] = the smallest el of row t); the kernel brings every
+//             block to 2^eg[t] and its epilogue multiplies by 2^-eg[t]
+//   eg_out, el_out  the same exponents for planes this kernel writes
+//             (gate/up: h); eg_out must be 0 before the kernel
+//   range_flag set to 1 when a value split here is outside the pair's range
+//             (|v| >= 2^15 or not finite): its products are then not exact
+struct ActScale {
+    const float *rs = nullptr;
+    const int *eg = nullptr;
+    const int8_t *el = nullptr;
+    int el_stride = 0;          // blocks per row of el / el_out
+    int *eg_out = nullptr;
+    int8_t *el_out = nullptr;
+    uint32_t *range_flag = nullptr;
+};
+
 // MFMA matrix-matrix path (prefill with T >= kGemmMinTokens tokens). Activations
 // are passed as an f16 hi plane [T][K] followed by an f16 lo plane (a_split),
 // or as f32 [T][K].
+// rs (if set) receives each row's factor 2^-e of the scaled planes (see
+// ActScale); eg_zero (if set) is cleared for each row.
 hipError_t launch_rms_split(float *x, int T, int K, const float *w, float eps, _Float16 *u,
-                            const float *part, int splits, hipStream_t s);
+                            const float *part, int splits, hipStream_t s, float *rs = nullptr,
+                            int *eg_zero = nullptr);
 // Split-K for short prompts: when the plain GEMM would launch only a few
 // workgroups (each walking all of K), the K steps are split over
 // gemm_splitk(N, K, T) > 1 slices that write partial sums part[z][T][N];
@@ -166,13 +192,14 @@ int gemm_splitk(int N, int K, int T);
 // scratch holds kSplitKMax * gemm_splitk_max_tokens(N) * N floats.
 int gemm_splitk_max_tokens(int N);
 hipError_t launch_gemm_part(const uint8_t *W, int N, int K, const _Float16 *A, int T, int splits, float *part,
-                            hipStream_t s);
+                            hipStream_t s, const ActScale &sc = ActScale{});
 hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
-                              int accumulate, float *Y, hipStream_t s);
+                              int accumulate, float *Y, hipStream_t s, const ActScale &sc = ActScale{});
 hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u, const StepState *st,
-                           const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s);
+                           const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s,
+                           const ActScale &sc = ActScale{});
 hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const _Float16 *u, _Float16 *h, int T,
-                              hipStream_t s);
+                              hipStream_t s, const ActScale &sc = ActScale{});
 
 // Q4_K / Q6_K matrices (N rows of K weights, K % 256 == 0). One token: the
 // VALU GEMV; several: the MFMA GEMM (activations f32, or split planes).
@@ -180,7 +207,7 @@ hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const _Float16 
 hipError_t launch_kq_gemv(int fmt, const uint8_t *W, int N, int K, const float *X, int accumulate, float *Y,
                           hipStream_t s);
 hipError_t launch_gemm_kq(int fmt, const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
-                          int accumulate, float *Y, hipStream_t s);
+                          int accumulate, float *Y, hipStream_t s, const ActScale &sc = ActScale{});
 
 // Prefill attention: T queries, causal mask offset by the cached prefix.
 struct AttnPrefillArgs {
@@ -190,6 +217,7 @@ struct AttnPrefillArgs {
     _Float16 *o_split;     // when set: f16 hi plane [T][nh*hd], then the lo plane
     int T, kv_len, kv_stride, nh, nkv, hd;
     float scale;
+    uint32_t *range_flag = nullptr;  // set to 1 when a value split into an f16 pair is out of its range
 };
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t s);
 

@@ -46,6 +46,8 @@ size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
     size_t state, counters, rope, tok, kc, vc, x, q, att, h, u, logits, lm_part, attn_part, kpart, total;
+    size_t rs, eg_h, el_h;  // prefill activation scaling: row factors, h row / block exponents
+    int el_stride;          // 32-wide blocks per h row
     size_t kv_layer;  // floats per layer in kc (and vc)
     int max_splits;
 };
@@ -101,6 +103,10 @@ Layout make_layout(const q8l_config *c) {
     L.lm_part = take(std::max(lmhead_partials_bytes(c->n_vocab, c->n_embd), size_t(8)));
     L.attn_part = take(size_t(c->n_head) * L.max_splits * (hd + 2) * 4);
     L.kpart = take(size_t(kSplitKMax) * std::max(1, gemm_splitk_max_tokens(int(H))) * H * 4);  // split-K partials
+    L.el_stride = c->n_ff / kQK;
+    L.rs = take(S * 4);
+    L.eg_h = take(S * 4);
+    L.el_h = take(S * size_t(L.el_stride));
     L.total = off;
     return L;
 }
@@ -128,6 +134,8 @@ struct q8l_model {
     std::map<int, hipGraphExec_t> graphs;  // by split bucket
     std::map<int, hipGraph_t> graph_defs;
     hipStream_t cap = nullptr;
+    uint32_t *range_host = nullptr;  // pinned: set by a kernel whose f16-pair split saw a value out of range
+    uint32_t *range_dev = nullptr;   // its device address
 
     template <typename T>
     T *at(size_t off) const {
@@ -186,20 +194,37 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
     _Float16 *att_s = m->at<_Float16>(m->lay.att), *h_s = m->at<_Float16>(m->lay.h);
     float *kpart = m->at<float>(m->lay.kpart);
     int pend = 0;  // split-K partial sums not yet added to x (the next norm kernel adds them)
+    // Activation scaling of the f16-pair planes (ActScale): the normalised
+    // rows carry per-row factors, h per-(row, block) exponents from the
+    // gate/up epilogue; q/k/v, the attention output and f32 inputs split
+    // on the way are range-checked.
+    float *rs = m->at<float>(m->lay.rs);
+    int *eg_h = m->at<int>(m->lay.eg_h);
+    int8_t *el_h = m->at<int8_t>(m->lay.el_h);
+    ActScale sc_u, sc_o, sc_h_out, sc_h_in;
+    sc_u.rs = rs;
+    sc_u.range_flag = sc_o.range_flag = sc_h_out.range_flag = sc_h_in.range_flag = m->range_dev;
+    sc_h_out.rs = rs;
+    sc_h_out.eg_out = eg_h;
+    sc_h_out.el_out = el_h;
+    sc_h_out.el_stride = m->lay.el_stride;
+    sc_h_in.eg = eg_h;
+    sc_h_in.el = el_h;
+    sc_h_in.el_stride = m->lay.el_stride;
     // Prefill x += A W^T for a Q8_0 matrix of H rows: split over K when the
     // plain grid would be small (the partial sums wait in kpart).
-    auto gemm_accumulate = [&](const uint8_t *W, int K, const _Float16 *A) -> hipError_t {
+    auto gemm_accumulate = [&](const uint8_t *W, int K, const _Float16 *A, const ActScale &sc) -> hipError_t {
         const int sk = gemm_splitk(d.H, K, T);
         pend = sk > 1 ? sk : 0;
-        return sk > 1 ? launch_gemm_part(W, d.H, K, A, T, sk, kpart, s)
-                      : launch_gemm_matmul(W, d.H, K, A, true, T, 1, x, s);
+        return sk > 1 ? launch_gemm_part(W, d.H, K, A, T, sk, kpart, s, sc)
+                      : launch_gemm_matmul(W, d.H, K, A, true, T, 1, x, s, sc);
     };
     for (int l = 0; l < m->cfg.n_layer; ++l) {
         const LayerPtrs w = m->layer(l);
         if (gemm) {
-            if ((e = launch_rms_split(x, T, d.H, w.attn_norm, d.eps, u, kpart, pend, s)) != hipSuccess) return e;
+            if ((e = launch_rms_split(x, T, d.H, w.attn_norm, d.eps, u, kpart, pend, s, rs)) != hipSuccess) return e;
             pend = 0;
-            if ((e = launch_gemm_qkv(d, w, u, st, rope, q, m->kc(l), m->vc(l), T, s)) != hipSuccess) return e;
+            if ((e = launch_gemm_qkv(d, w, u, st, rope, q, m->kc(l), m->vc(l), T, s, sc_u)) != hipSuccess) return e;
         } else {
             // a decode step's first layer dequantizes the token's embedding itself
             const uint8_t *emb = (T == 1 && l == 0) ? m->tok_embd : nullptr;
@@ -231,22 +256,24 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.o_split = gemm ? att_s : nullptr;  // the o-projection GEMM reads f16 hi + lo
             a.T = T; a.kv_len = kv_len_prefill; a.kv_stride = d.max_seq;
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.scale = 1.0f / sqrtf(float(d.hd));
+            a.range_flag = m->range_dev;
             if ((e = launch_attn_prefill(a, s)) != hipSuccess) return e;
             if (w.fo != F_Q8_0)
-                e = gemm ? launch_gemm_kq(w.fo, w.wo, d.H, QD, att_s, true, T, 1, x, s)
-                         : launch_gemm_kq(w.fo, w.wo, d.H, QD, att, false, T, 1, x, s);
+                e = gemm ? launch_gemm_kq(w.fo, w.wo, d.H, QD, att_s, true, T, 1, x, s, sc_o)
+                         : launch_gemm_kq(w.fo, w.wo, d.H, QD, att, false, T, 1, x, s, sc_o);
             else if (gemm)
-                e = gemm_accumulate(w.wo, QD, att_s);
+                e = gemm_accumulate(w.wo, QD, att_s, sc_o);
             else
                 e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s);
             if (e != hipSuccess) return e;
         }
         if (gemm) {
-            if ((e = launch_rms_split(x, T, d.H, w.ffn_norm, d.eps, u, kpart, pend, s)) != hipSuccess) return e;
+            if ((e = launch_rms_split(x, T, d.H, w.ffn_norm, d.eps, u, kpart, pend, s, rs, eg_h)) != hipSuccess)
+                return e;
             pend = 0;
-            if ((e = launch_gemm_gateup(d, w, u, h_s, T, s)) != hipSuccess) return e;
-            e = w.fd != F_Q8_0 ? launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s)
-                               : gemm_accumulate(w.wd, d.F, h_s);
+            if ((e = launch_gemm_gateup(d, w, u, h_s, T, s, sc_h_out)) != hipSuccess) return e;
+            e = w.fd != F_Q8_0 ? launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s, sc_h_in)
+                               : gemm_accumulate(w.wd, d.F, h_s, sc_h_in);
         } else {
             if ((e = launch_gateup(d, w, x, h, T, s)) != hipSuccess) return e;
             if (w.fd == F_Q8_0)
@@ -254,7 +281,7 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             else if (T == 1)
                 e = launch_kq_gemv(w.fd, w.wd, d.H, d.F, h, 1, x, s);
             else
-                e = launch_gemm_kq(w.fd, w.wd, d.H, d.F, h, false, T, 1, x, s);
+                e = launch_gemm_kq(w.fd, w.wd, d.H, d.F, h, false, T, 1, x, s, sc_o);
         }
         if (e != hipSuccess) return e;
     }
@@ -368,6 +395,16 @@ q8l_status set_state(q8l_model *m, int pos, int slot, int T, int advance, float 
         off += std::max(a.tok_count, 0);
     } while (off < n);
     return Q8L_OK;
+}
+
+// A prefill kernel of an earlier call split a value outside the f16 pairs'
+// range into a pair (see ActScale): reported once, by the next call.
+q8l_status range_check(q8l_model *m) {
+    if (!m->range_host || __atomic_load_n(m->range_host, __ATOMIC_ACQUIRE) == 0) return Q8L_OK;
+    __atomic_store_n(m->range_host, 0u, __ATOMIC_RELEASE);
+    return fail(m, Q8L_E_RANGE,
+                "an earlier prefill split a q/k/v or input value of magnitude >= 32768 (or not finite) into an "
+                "f16 pair: its logits are not exact");
 }
 
 }  // namespace
@@ -488,6 +525,15 @@ q8l_status q8l_finalize(q8l_model *m, void *stream) {
     Q8L_HIP(m, launch_rope_table(m->at<float2>(m->lay.rope), m->cfg.max_seq_len, m->cfg.head_dim,
                                  m->cfg.rope_theta, s),
             "building the rope table");
+    if (!m->range_host) {
+        void *p = nullptr;
+        Q8L_HIP(m, hipHostMalloc(&p, 64, hipHostMallocMapped), "hipHostMalloc");
+        m->range_host = static_cast<uint32_t *>(p);
+        *m->range_host = 0;
+        void *dp = nullptr;
+        Q8L_HIP(m, hipHostGetDevicePointer(&dp, p, 0), "hipHostGetDevicePointer");
+        m->range_dev = static_cast<uint32_t *>(dp);
+    }
     m->len = 0;
     m->finalized = true;
     return Q8L_OK;
@@ -506,6 +552,7 @@ q8l_status q8l_forward(q8l_model *m, const uint32_t *tokens_host, int32_t n_toke
     q8l_status st = check_positions(m, n_tokens, index_pos, &len);
     if (st != Q8L_OK) return st;
     if (!m->finalized) return fail(m, Q8L_E_NOT_FINALIZED, "forward before finalize");
+    if ((st = range_check(m)) != Q8L_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int T = n_tokens;
     if (T == 1) {
@@ -538,6 +585,7 @@ q8l_status q8l_generate(q8l_model *m, const uint32_t *token_dev, int32_t index_p
     const int32_t len = index_pos == 0 ? 0 : m->len;
     if (int64_t(len) + n_steps > S) return fail(m, Q8L_E_KV_FULL, "cache would overflow");
     if (!m->finalized) return fail(m, Q8L_E_NOT_FINALIZED, "generate before finalize");
+    if (q8l_status rc = range_check(m); rc != Q8L_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::vector<hipGraphExec_t> gs(n_steps);
     for (int k = 0; k < n_steps; ++k) {
@@ -645,6 +693,7 @@ void q8l_destroy(q8l_model *m) {
     for (auto &kv : m->graphs) hipGraphExecDestroy(kv.second);
     for (auto &kv : m->graph_defs) hipGraphDestroy(kv.second);
     if (m->cap) hipStreamDestroy(m->cap);
+    if (m->range_host) hipHostFree(m->range_host);
     delete m;
 }
 

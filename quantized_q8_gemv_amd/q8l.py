@@ -28,9 +28,11 @@ Q8L_E_HIP = 8
 Q8L_E_FORMAT = 9
 Q8L_E_MISSING_KEY = 10
 Q8L_E_IO = 11
+Q8L_E_RANGE = 12
 STATUS_NAMES = {0: "OK", 1: "E_INVALID_ARG", 2: "E_MISSING_TENSOR", 3: "E_SHAPE",
                 4: "E_POS_RANGE", 5: "E_POS_MISMATCH", 6: "E_KV_FULL",
-                7: "E_NOT_FINALIZED", 8: "E_HIP", 9: "E_FORMAT", 10: "E_MISSING_KEY", 11: "E_IO"}
+                7: "E_NOT_FINALIZED", 8: "E_HIP", 9: "E_FORMAT", 10: "E_MISSING_KEY", 11: "E_IO",
+                12: "E_RANGE"}
 
 Q8L_F32 = 0
 Q8L_Q8_0 = 1
