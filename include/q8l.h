@@ -315,11 +315,14 @@ q8l_status q8l_op_argmax(const float *x, int64_t n, uint32_t *out, void *workspa
  *   kernel dequantizes the token's row; the slot's launches warm the GPU up
  *   for the kinds after it), 1 q/k/v (+norm, rope, KV write;
  *   as layers after the first run it), 2 attention (split
- *   partials, or the normalised output when the cache fits one split),
- *   3 o-projection (+residual; as in the step at this length: with 2..8
- *   splits and few partial bytes it merges them in its prologue, with more
- *   the merge is a kernel of its own, not timed here), 4 gate/up (+norm,
- *   SiLU*up), 5 down (+residual), 6 output layer (+norm, per-workgroup
+ *   partials, or the normalised output when the cache fits one split; when
+ *   the step fuses the one-split attention with the o-projection, that
+ *   fused kernel), 3 o-projection (+residual; as in the step at this length:
+ *   with 2..8 splits and few partial bytes it merges them in its prologue,
+ *   with more the merge is a kernel of its own, not timed here; -1 when it
+ *   is part of kind 2), 4 gate/up (+norm, SiLU*up; after the fused kernel
+ *   it first adds that kernel's per-group partial sums to the residual),
+ *   5 down (+residual), 6 output layer (+norm, per-workgroup
  *   argmax), 7 argmax merge, 8 an empty kernel (the dispatch gap between
  *   back-to-back launches, included in every other entry).
  * The r-th launch of a per-layer kind (1 to 5) uses layer r mod n_layer's

@@ -103,6 +103,47 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// v of a lane combined with the lane `ctrl` selects (a DPP move; row_mask,
+// bank_mask all lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes of a wave, in a fixed order, without LDS: within
+// each 16-lane row by DPP (neighbours, pairs of neighbours, mirrored halves
+// of 8, mirrored halves of 16: every lane of a row ends with the row's sum,
+// the same bits in each since a + b == b + a), then the four row sums read
+// from lanes 0, 16, 32, 48 and added as (r0 + r1) + (r2 + r3). Every lane
+// gets the result.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_f<0x141>(v);   // row_half_mirror
+    v += dpp_f<0x140>(v);   // row_mirror
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Largest of v over the 64 lanes, by the same DPP pattern as wave_sum_dpp
+// (max is exact, so the order does not matter); every lane gets it.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -113,7 +154,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // the result. `red` is 4 floats of LDS.
 __device__ __forceinline__ float block_sum(float v, float *red) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    v = wave_sum(v);
+    v = wave_sum_dpp(v);
     __syncthreads();
     if (lane == 0) red[wid] = v;
     __syncthreads();

@@ -31,112 +31,192 @@ namespace {
 
 struct DecodeLds {
     float *q;    // G * hd
-    float *k;    // chunk * (hd + 1)
+    float *k;    // chunk * (hd + 4): rows padded to keep 16-byte reads conflict-free
     float *v;    // chunk * hd
-    float *sc;   // G * chunk
-    float *m;    // G
-    float *l;    // G
+    float *p;    // (kThreads / 64) * chunk: each wave's softmax numerators
 };
 
 constexpr int kKvPer = 4;   // float4 per thread of a K (or V) tile: 64 x 64 or 32 x 128 floats
+constexpr int kQPer = 2;    // float4 per thread of a group's queries (G * hd <= 2048 floats)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline DecodeLds carve_decode(uint8_t *smem, int G, int hd) {
+    const int C = attn_chunk(hd);
+    DecodeLds L;
+    float *p = reinterpret_cast<float *>(smem);
+    L.q = p; p += G * hd;
+    L.k = p; p += C * (hd + kKPad);
+    L.v = p; p += C * hd;
+    L.p = p;
+    return L;
+}
+
+// The G query heads of KV group g against keys [j0, j0 + nk) of the cache
+// (nk <= the split size, <= 64): q and the key/value tile are staged in LDS
+// by the whole workgroup, then wave w takes heads w, w + 4, ...:
+//   scores  lane j: q_h . k_j (four partial sums over d, then
+//           (s0 + s1) + (s2 + s3)), times the scale;
+//   softmax max over the lanes, e_j = exp(s_j - max), l = sum of e_j
+//           (DPP reductions, no barrier);
+//   output  lane d (and d + 64): sum over j in key order of e_j * v_j[d],
+//           e_j read back (four at a time) from the wave's row of L.p.
+// out(h, d, acc, max, l) receives each unnormalised output.
+template <class Out>
+__device__ __forceinline__ void attn_group_split(const AttnDecodeArgs &a, const DecodeLds &L, int g, int j0,
+                                                 int nk, Out &&out) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int hd = a.hd, G = a.nh / a.nkv;
+    const int C = attn_chunk(hd);
+    // 16-byte loads (hd % 8 == 0; the cache and the V tile are 16-byte aligned)
+    const f32x4 *qg = reinterpret_cast<const f32x4 *>(a.q + size_t(g) * G * hd);
+    const f32x4 *kb = reinterpret_cast<const f32x4 *>(a.kc + (size_t(g) * a.kv_stride + j0) * hd);
+    const f32x4 *vb = reinterpret_cast<const f32x4 *>(a.vc + (size_t(g) * a.kv_stride + j0) * hd);
+    // Every load of q and of the tile is issued before the first LDS store,
+    // so they cost one memory round trip together (G * hd <= kQPer * kThreads
+    // float4 of q; chunk * hd <= kKvPer * kThreads float4 of K and of V). The
+    // tile's loads cover the whole chunk that the cache holds from j0 on (not
+    // only the nk keys in use, which are known only from the step state), so
+    // the issue does not wait for that state. Indexes past q or past the
+    // cache re-read the last float4 (in bounds), and every loaded register is
+    // stored without a condition (q's extra copies onto its last float4,
+    // the tile's onto rows past nk that are never read): a load used under a
+    // condition would be sunk into it, one round trip per load.
+    const int nq4 = G * hd / 4;
+    const int last = min(C, a.kv_stride - j0) * hd / 4 - 1;
+    f32x4 qr[kQPer], kr[kKvPer], vr[kKvPer];
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) qr[i] = qg[min(tid + i * kThreads, nq4 - 1)];
+#pragma unroll
+    for (int i = 0; i < kKvPer; ++i) {
+        const int e4 = min(tid + i * kThreads, last);
+        kr[i] = kb[e4];
+        vr[i] = vb[e4];
+    }
+#pragma unroll
+    for (int i = 0; i < kQPer; ++i) reinterpret_cast<f32x4 *>(L.q)[min(tid + i * kThreads, nq4 - 1)] = qr[i];
+    // Destinations past the chunk (head sizes whose chunk is under 4096
+    // floats) go to its last float4: every such store carries the value
+    // loaded from index `last`, which is also what that slot's own thread
+    // loaded (min(C * hd / 4 - 1, last) == last whenever the cache is short).
+    const int tile4 = C * hd / 4 - 1;
+#pragma unroll
+    for (int i = 0; i < kKvPer; ++i) {
+        const int e = 4 * min(tid + i * kThreads, tile4), j = e / hd, d = e - j * hd;
+        *reinterpret_cast<f32x4 *>(L.k + j * (hd + kKPad) + d) = kr[i];
+        *reinterpret_cast<f32x4 *>(L.v + e) = vr[i];
+    }
+    __syncthreads();
+    for (int h = wid; h < G; h += kThreads / 64) {
+        const float *qh = L.q + h * hd;
+        float sc = -INFINITY;
+        if (lane < nk) {
+            const float *kj = L.k + lane * (hd + kKPad);
+            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll 4
+            for (int d = 0; d < hd; d += 4) {
+                const float4 qv = *reinterpret_cast<const float4 *>(qh + d);
+                const float4 kv = *reinterpret_cast<const float4 *>(kj + d);
+                s0 = fmaf(qv.x, kv.x, s0);
+                s1 = fmaf(qv.y, kv.y, s1);
+                s2 = fmaf(qv.z, kv.z, s2);
+                s3 = fmaf(qv.w, kv.w, s3);
+            }
+            sc = ((s0 + s1) + (s2 + s3)) * a.scale;
+        }
+        const float mx = wave_max_dpp(sc);
+        const float e = lane < nk ? expf(sc - mx) : 0.f;
+        const float l = wave_sum_dpp(e);
+        float *pw = L.p + wid * C;   // this wave's row: written and read by the wave alone
+        if (lane < C) pw[lane] = e;
+        __builtin_amdgcn_wave_barrier();
+        for (int d = lane; d < hd; d += 64) {
+            float acc = 0.f;
+            int j = 0;
+#pragma unroll 2
+            for (; j + 4 <= nk; j += 4) {
+                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(pw + j);
+                acc = fmaf(e4.x, L.v[j * hd + d], acc);
+                acc = fmaf(e4.y, L.v[(j + 1) * hd + d], acc);
+                acc = fmaf(e4.z, L.v[(j + 2) * hd + d], acc);
+                acc = fmaf(e4.w, L.v[(j + 3) * hd + d], acc);
+            }
+            for (; j < nk; ++j) acc = fmaf(pw[j], L.v[j * hd + d], acc);
+            out(h, d, acc, mx, l);
+        }
+        __builtin_amdgcn_wave_barrier();   // the row is rewritten for the wave's next head
+    }
+}
 
 __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int s = blockIdx.x, g = blockIdx.y;
     const int hd = a.hd, G = a.nh / a.nkv;
     const int C = attn_chunk(hd);
     const int kv_len = a.kv_len_arg >= 0 ? a.kv_len_arg : a.st->slot + 1;
     const int active = min((kv_len + C - 1) / C, a.n_splits);
+    if (s >= active) return;
+    const DecodeLds L = carve_decode(smem, G, hd);
+    const int j0 = s * C;
+    attn_group_split(a, L, g, j0, min(C, kv_len - j0), [&](int h, int d, float acc, float mx, float l) {
+        if (a.o) {  // the only split: its normalised output (what the merge of one split computes)
+            a.o[size_t(g * G + h) * hd + d] = acc / l;
+            return;
+        }
+        float *pp = a.part + (size_t(g * G + h) * a.n_splits + s) * (hd + 2);
+        pp[2 + d] = acc;
+        if (d == 0) {
+            pp[0] = mx;
+            pp[1] = l;
+        }
+    });
+}
 
-    DecodeLds L;
-    float *p = reinterpret_cast<float *>(smem);
-    L.q = p; p += G * hd;
-    L.k = p; p += C * (hd + 1);
-    L.v = p; p += C * hd;
-    L.sc = p; p += G * C;
-    L.m = p; p += G;
-    L.l = p;
-
-    if (s < active) {
-        const int j0 = s * C;
-        const int nk = min(C, kv_len - j0);
-        const float4 *qg = reinterpret_cast<const float4 *>(a.q + size_t(g) * G * hd);
-        for (int e4 = tid; e4 < G * hd / 4; e4 += kThreads) reinterpret_cast<float4 *>(L.q)[e4] = qg[e4];
-        // 16-byte loads (hd % 8 == 0; the cache and the V tile are 16-byte aligned);
-        // K rows keep a one-float pad in LDS (conflict-free score reads)
-        const float4 *kb = reinterpret_cast<const float4 *>(a.kc + (size_t(g) * a.kv_stride + j0) * hd);
-        const float4 *vb = reinterpret_cast<const float4 *>(a.vc + (size_t(g) * a.kv_stride + j0) * hd);
-        // Every load of the tile is issued before the first LDS store, so the
-        // tile costs one memory round trip (chunk * hd <= 4096 floats: at most
-        // kKvPer float4 of K and of V per thread). Indexes past the tile re-read
-        // its last float4 (in bounds); those registers are not stored.
-        const int last = nk * hd / 4 - 1;
-        float4 r[2 * kKvPer];  // K then V, one array (kept in registers)
+// Decode attention of a cache that fits one split, fused with the
+// o-projection as a sum over KV groups: workgroup (g, row chunk) computes the
+// normalised output of group g's heads and multiplies it by the matching
+// columns of W_o (this group's G*hd columns, whole 64-weight pairs) for its
+// rows, writing part[g][row] = sum over those columns. The residual add of
+// sum_g part[g] is the prologue of the next kernel with a norm in front. Every
+// workgroup of a group recomputes the same attention (at most one split of
+// keys: a few KB of K/V from L2); the workgroup's W_o pairs are loaded into
+// registers first and are in flight during the attention.
+__global__ __launch_bounds__(kThreads) void k_attn_o1(AttnODecodeArgs b) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const AttnDecodeArgs &a = b.at;
+    const int tid = threadIdx.x;
+    const int g = blockIdx.x % a.nkv, r0 = (blockIdx.x / a.nkv) * b.rows;
+    const int hd = a.hd, G = a.nh / a.nkv, C = attn_chunk(hd);
+    const int Pg = G * hd / kPairWeights;   // pairs of this group's columns in one row of W_o
+    const int P = a.nh * hd / kPairWeights; // pairs per row
+    const int nr = min(b.rows, b.N - r0);
+    const int units = nr * Pg;              // <= kThreads (host-checked)
+    uint32_t w[kPairBytes / 4];
+    if (tid < units) {
+        const int r = tid / Pg, p = tid - r * Pg;
+        const uint32_t *src =
+            reinterpret_cast<const uint32_t *>(b.wo + (size_t(r0 + r) * P + size_t(g) * Pg + p) * kPairBytes);
 #pragma unroll
-        for (int i = 0; i < kKvPer; ++i) {
-            const int e4 = min(tid + i * kThreads, last);
-            r[i] = kb[e4];
-            r[kKvPer + i] = vb[e4];
-        }
-#pragma unroll
-        for (int i = 0; i < kKvPer; ++i) {
-            const int e4 = tid + i * kThreads;
-            if (e4 <= last) {
-                const int e = 4 * e4, j = e / hd, d = e - j * hd;
-                float *kd = L.k + j * (hd + 1) + d;
-                kd[0] = r[i].x;
-                kd[1] = r[i].y;
-                kd[2] = r[i].z;
-                kd[3] = r[i].w;
-                *reinterpret_cast<float4 *>(L.v + e) = r[kKvPer + i];
-            }
-        }
-        __syncthreads();
-        for (int e = tid; e < G * nk; e += kThreads) {
-            const int h = e / nk, j = e - h * nk;
-            const float *qh = L.q + h * hd;
-            const float *kj = L.k + j * (hd + 1);
-            float s0 = 0.f, s1 = 0.f;
-            for (int d = 0; d < hd; d += 2) {
-                s0 = fmaf(qh[d], kj[d], s0);
-                s1 = fmaf(qh[d + 1], kj[d + 1], s1);
-            }
-            L.sc[h * C + j] = (s0 + s1) * a.scale;
-        }
-        __syncthreads();
-        for (int h = wid; h < G; h += 4) {
-            float mx = -INFINITY;
-            for (int j = lane; j < nk; j += 64) mx = fmaxf(mx, L.sc[h * C + j]);
-            mx = wave_max(mx);
-            float sum = 0.f;
-            for (int j = lane; j < nk; j += 64) {
-                const float e = expf(L.sc[h * C + j] - mx);
-                L.sc[h * C + j] = e;
-                sum += e;
-            }
-            sum = wave_sum(sum);
-            if (lane == 0) {
-                L.m[h] = mx;
-                L.l[h] = sum;
-            }
-        }
-        __syncthreads();
-        for (int e = tid; e < G * hd; e += kThreads) {
-            const int h = e / hd, d = e - h * hd;
-            float acc = 0.f;
-            for (int j = 0; j < nk; ++j) acc = fmaf(L.sc[h * C + j], L.v[j * hd + d], acc);
-            if (a.o) {  // the only split: its normalised output (what the merge of one split computes)
-                a.o[size_t(g * G + h) * hd + d] = acc / L.l[h];
-                continue;
-            }
-            float *pp = a.part + (size_t(g * G + h) * a.n_splits + s) * (hd + 2);
-            pp[2 + d] = acc;
-            if (d == 0) {
-                pp[0] = L.m[h];
-                pp[1] = L.l[h];
-            }
-        }
+        for (int i = 0; i < kPairBytes / 4; ++i) w[i] = src[i];
+    }
+    const DecodeLds L = carve_decode(smem, G, hd);
+    float *xs = reinterpret_cast<float *>(smem + attn_o_xs_offset(G, hd));  // Pg * kOPad: the group's output
+    float *red = xs + Pg * kOPad;                                           // units
+    const int kv_len = min(a.st->slot + 1, C);
+    attn_group_split(a, L, g, 0, kv_len, [&](int h, int d, float acc, float, float l) {
+        const int k = h * hd + d;
+        xs[(k / kPairWeights) * kOPad + (k % kPairWeights)] = acc / l;
+    });
+    __syncthreads();
+    if (tid < units) {
+        float dA, sA, dB, sB;
+        pair_dot1(w, xs + (tid % Pg) * kOPad, dA, sA, dB, sB);
+        red[tid] = fmaf(dB, sB, dA * sA);
+    }
+    __syncthreads();
+    for (int r = tid; r < nr; r += kThreads) {
+        float v = red[r * Pg];
+        for (int p = 1; p < Pg; ++p) v += red[r * Pg + p];
+        b.part[size_t(g) * b.N + r0 + r] = v;
     }
 }
 
@@ -569,14 +649,39 @@ int attn_decode_splits(int kv_len, int hd) {
     return (kv_len + C - 1) / C;
 }
 
-size_t attn_decode_lds(int G, int hd) {
-    const int C = attn_chunk(hd);
-    return sizeof(float) * (size_t(G) * hd + size_t(C) * (hd + 1) + size_t(C) * hd + size_t(G) * C + 2 * G);
-}
-
 hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s) {
     const size_t lds = attn_decode_lds(a.nh / a.nkv, a.hd);
     hipLaunchKernelGGL(k_attn_decode, dim3(a.n_splits, a.nkv), dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+size_t attn_o_lds(int G, int hd, int rows) {
+    const int Pg = G * hd / kPairWeights;
+    return attn_o_xs_offset(G, hd) + sizeof(float) * (size_t(Pg) * kOPad + size_t(rows) * Pg);
+}
+
+bool attn_o_fits(const Dims &d) {
+    const int G = d.nh / d.nkv;
+    return (G * d.hd) % kPairWeights == 0 && G * d.hd / kPairWeights <= kThreads;
+}
+
+int attn_o_rows(const Dims &d) {
+    const int Pg = d.nh / d.nkv * d.hd / kPairWeights;
+    const int want = (kAttnOWgs + d.nkv - 1) / d.nkv;          // row chunks per group
+    const int rows = (d.H + want - 1) / want;
+    return std::max(1, std::min(rows, kThreads / Pg));
+}
+
+hipError_t launch_attn_o(const AttnDecodeArgs &a, const uint8_t *wo, int N, float *part, hipStream_t s) {
+    Dims d{};
+    d.H = N; d.nh = a.nh; d.nkv = a.nkv; d.hd = a.hd;
+    if (!attn_o_fits(d)) return hipErrorInvalidValue;
+    AttnODecodeArgs b;
+    b.at = a;
+    b.wo = wo; b.N = N; b.part = part;
+    b.rows = attn_o_rows(d);
+    const int chunks = (N + b.rows - 1) / b.rows;
+    hipLaunchKernelGGL(k_attn_o1, dim3(chunks * a.nkv), dim3(kThreads), attn_o_lds(a.nh / a.nkv, a.hd, b.rows), s, b);
     return hipGetLastError();
 }
 

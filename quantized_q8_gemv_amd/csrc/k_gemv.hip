@@ -336,6 +336,7 @@ struct QkvArgs {
     const uint8_t *embed;
     float *xres;
     int V;
+    PartSrc ps;          // decode: split-K partials added to x first (n = 0: none)
 };
 
 template <int MAXT, bool MULTI>
@@ -397,6 +398,7 @@ struct GateUpArgs {
     GemvShape sh;
     int F, T;
     float eps;
+    PartSrc ps;  // decode: split-K partials added to x first (n = 0: none)
 };
 
 template <int MAXT, bool MULTI>
@@ -463,6 +465,7 @@ struct LmHeadArgs {
     GemvShape sh;
     int V;
     float eps;
+    PartSrc ps;          // split-K partials added to x first (n = 0: none)
 };
 
 // Merge n (value, index) partials in a fixed order; lowest index on ties.
@@ -625,10 +628,38 @@ constexpr int kStage4 = 4;   // float4 of the row per thread held in registers (
 // the same, in the same order, as the general path below. Measured: 7B-class
 // decode (rows of 4096) 2601 -> 2554 us/token; with the 135M shape's rows of
 // 576 it was slower (694 -> 700), so short rows keep the general path.
-__device__ void stage_row1(const CoreArgs &a, const Lds1 &l) {
+constexpr int kPartBatch = 4;   // split-K partial rows loaded together (all in flight before the sum)
+
+// v + (p_0 + p_1 + ... + p_{n-1}) for the float4 at e (partials summed in
+// index order, then added to v); kPartBatch loads are issued before any is
+// used (indexes past n re-read the last partial and are not summed).
+__device__ __forceinline__ float4 add_partials(float4 v, const PartSrc &ps, int e) {
+    const float *pp = ps.part + size_t(e) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i0 = 0; i0 < ps.n; i0 += kPartBatch) {
+        float4 t[kPartBatch];
+#pragma unroll
+        for (int i = 0; i < kPartBatch; ++i)
+            t[i] = *reinterpret_cast<const float4 *>(pp + size_t(min(i0 + i, ps.n - 1)) * ps.stride);
+#pragma unroll
+        for (int i = 0; i < kPartBatch; ++i) {
+            if (i0 + i == 0) {
+                acc = t[0];
+            } else if (i0 + i < ps.n) {
+                acc.x += t[i].x;
+                acc.y += t[i].y;
+                acc.z += t[i].z;
+                acc.w += t[i].w;
+            }
+        }
+    }
+    return make_float4(v.x + acc.x, v.y + acc.y, v.z + acc.z, v.w + acc.w);
+}
+
+__device__ void stage_row1(const CoreArgs &a, const Lds1 &l, PartSrc ps = PartSrc{}) {
     const int tid = threadIdx.x;
     const int n4 = a.sh.P * 16;
-    if (a.norm_w && n4 > kThreads && n4 <= kStage4 * kThreads) {
+    if (a.norm_w && ps.n == 0 && n4 > kThreads && n4 <= kStage4 * kThreads) {
         float4 xv[kStage4], wv[kStage4];
 #pragma unroll
         for (int i = 0; i < kStage4; ++i) {   // indexes past the row re-read its last float4 (unused)
@@ -664,9 +695,48 @@ __device__ void stage_row1(const CoreArgs &a, const Lds1 &l) {
         }
         return;
     }
+    if (n4 <= kThreads) {
+        // Rows of at most kThreads float4: one per thread, its norm weights
+        // (and any partial sums) loaded with it, so the row costs one memory
+        // round trip; the values and their order are the general path's.
+        const int e = tid;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f), w = v;
+        if (e < n4) {
+            v = *reinterpret_cast<const float4 *>(a.X + size_t(e) * 4);
+            if (a.norm_w) w = *reinterpret_cast<const float4 *>(a.norm_w + size_t(e) * 4);
+            if (ps.n > 0) {
+                v = add_partials(v, ps, e);
+                if (ps.xout && blockIdx.x == 0) *reinterpret_cast<float4 *>(ps.xout + size_t(e) * 4) = v;
+            }
+        }
+        float4 *xp = reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4);
+        if (!a.norm_w) {
+            if (e < n4) *xp = v;
+            return;
+        }
+        float ss = 0.f;
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+        ss = block_sum(ss, l.red);
+        const float r = 1.0f / sqrtf(ss / static_cast<float>(a.sh.K) + a.eps);
+        if (e < n4) {
+            v.x = v.x * r * w.x;
+            v.y = v.y * r * w.y;
+            v.z = v.z * r * w.z;
+            v.w = v.w * r * w.w;
+            *xp = v;
+        }
+        return;
+    }
     float ss = 0.f;
     for (int e = tid; e < n4; e += kThreads) {
-        const float4 v = *reinterpret_cast<const float4 *>(a.X + size_t(e) * 4);
+        float4 v = *reinterpret_cast<const float4 *>(a.X + size_t(e) * 4);
+        if (ps.n > 0) {
+            v = add_partials(v, ps, e);
+            if (ps.xout && blockIdx.x == 0) *reinterpret_cast<float4 *>(ps.xout + size_t(e) * 4) = v;
+        }
         *reinterpret_cast<float4 *>(l.xs + (e >> 4) * kXPad + (e & 15) * 4) = v;
         ss = fmaf(v.x, v.x, ss);
         ss = fmaf(v.y, v.y, ss);
@@ -688,6 +758,57 @@ __device__ void stage_row1(const CoreArgs &a, const Lds1 &l) {
     }
 }
 
+// Products of a small single-chunk tile (the whole row staged): wave w takes
+// rows w, w + 4, ... of the tile; lane l takes the row's weights l, l + 64,
+// ... (byte l % 32 of block 2i + l / 32 for pair i) and accumulates
+// (d * q) * u (d * q is exact in f32) in pair order; the lanes are summed
+// by wave_sum_dpp. Fewer barriers and a short chain per lane, for tiles that
+// would leave most threads idle one pair per thread.
+__device__ __forceinline__ void rows_dot1(const CoreArgs &c, const Lds1 &l, int nrows) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const GemvShape &sh = c.sh;
+    const int items = c.nmat * nrows;
+    const uint8_t *wt = reinterpret_cast<const uint8_t *>(l.wt) + (lane >> 5) * kQBytes;
+    const int o = lane & 31;
+    constexpr int W = kThreads / 64;
+    auto put = [&](int it, float v) {
+        if (lane == 0) {
+            const int m = it / nrows, r = it - m * nrows;
+            l.outv[m * sh.NR + r] = v;
+        }
+    };
+    int it = wid;
+    // rows it and it + W together while both exist (one read of u for two rows)
+    for (; it + W < items; it += 2 * W) {
+        const uint8_t *ra = wt + size_t(it) * sh.PC * kPairBytes;
+        const uint8_t *rb = wt + size_t(it + W) * sh.PC * kPairBytes;
+        float acc = 0.f, acc2 = 0.f;
+#pragma unroll 8
+        for (int i = 0; i < sh.P; ++i) {
+            const uint8_t *ba = ra + i * kPairBytes, *bb = rb + i * kPairBytes;
+            const float u = l.xs[i * kXPad + lane];
+            const float da = half_bits_to_float(*reinterpret_cast<const uint16_t *>(ba));
+            const float db = half_bits_to_float(*reinterpret_cast<const uint16_t *>(bb));
+            acc = fmaf(da * static_cast<float>(static_cast<int8_t>(ba[2 + o])), u, acc);
+            acc2 = fmaf(db * static_cast<float>(static_cast<int8_t>(bb[2 + o])), u, acc2);
+        }
+        put(it, wave_sum_dpp(acc));
+        put(it + W, wave_sum_dpp(acc2));
+    }
+    for (; it < items; it += W) {
+        const uint8_t *row = wt + size_t(it) * sh.PC * kPairBytes;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int i = 0; i < sh.P; ++i) {
+            const uint8_t *blk = row + i * kPairBytes;
+            const float d = half_bits_to_float(*reinterpret_cast<const uint16_t *>(blk));
+            const float q = static_cast<float>(static_cast<int8_t>(blk[2 + o]));
+            acc = fmaf(d * q, l.xs[i * kXPad + lane], acc);
+        }
+        put(it, wave_sum_dpp(acc));
+    }
+}
+
 // One row tile: outv[m*NR + r] = sum_k W_m[row0+r][k] * u[k]. Chunk 0 of this
 // tile is already in `st`; the next tile's chunk 0 is issued during the last
 // chunk (when has_next).
@@ -698,6 +819,16 @@ __device__ void tile_run1(const CoreArgs &c, const Lds1 &l, int nrows, bool vec,
     const GemvShape &sh = c.sh;
     const int per_mat = nrows * sh.PC;
     const int units = c.nmat * per_mat;
+    if constexpr (!MULTI) {
+        if (2 * units <= kThreads) {
+            stage_store(c, nrows, 0, vec, st, l.wt);
+            if (has_next) stage_issue(n, nn, 0, nvec, st);
+            __syncthreads();
+            rows_dot1(c, l, nrows);
+            __syncthreads();
+            return;
+        }
+    }
     const int nchunks = MULTI ? sh.P / sh.PC : 1;
     const int up = tid < units ? (tid % per_mat) % sh.PC : 0;
     float acc = 0.f;
@@ -744,7 +875,7 @@ __device__ inline int tile_rows(const CoreArgs &c) { return min(c.sh.NR, c.N - c
 // epi(tile, rows) consumes outv after each tile.
 template <bool MULTI, bool MERGE = false, class Epi>
 __device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, int ntiles, Epi &&epi,
-                                            const MergeSrc *ms = nullptr) {
+                                            const MergeSrc *ms = nullptr, PartSrc ps = PartSrc{}) {
     const int G = int(gridDim.x);
     auto at = [&](int t, CoreArgs &x, int &nr, bool &v) {
         x = c;
@@ -764,7 +895,7 @@ __device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, in
     if constexpr (MERGE)
         stage_merged1(c, *ms, l);
     else
-        stage_row1(c, l);
+        stage_row1(c, l, ps);
     while (t < ntiles) {
         at(t + 2 * G, n, nn, nv);
         tile_run1<MULTI>(ca, l, na, va, sa, n, nn, nv, nn > 0);
@@ -847,31 +978,37 @@ __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
     bool vec = tile_vec(c, nrows);
     WStage st;
     stage_issue(c, nrows, 0, vec, st);
+    const int pos = a.st->pos, slot = a.st->slot;   // in flight with the weights and the row
     if (a.embed)
         stage_embed1(a, c, l);
     else
-        stage_row1(c, l);
-    const int pos = a.st->pos, slot = a.st->slot;
+        stage_row1(c, l, a.ps);
     for (; tile < ntiles; tile += gridDim.x) {
         const bool has_next = tile + int(gridDim.x) < ntiles;
         int nkind = 0;
         CoreArgs n = has_next ? ref(tile + gridDim.x, nkind) : c;
         const int nn = has_next ? tile_rows(n) : 0;
         const bool nvec = has_next ? tile_vec(n, nn) : false;
+        // Thread e writes rows 2e, 2e + 1 of the tile (nrows <= NR <= kThreads,
+        // so one pair per thread); its rope factors are loaded before the
+        // products, not after them.
+        const int e = threadIdx.x;
+        const bool rot = kind != 2 && !a.rope_neox;
+        float2 cs = make_float2(1.f, 0.f);
+        if (rot && e < nrows / 2) cs = a.rope[size_t(pos) * (a.hd / 2) + (((c.row0 + 2 * e) % a.hd) >> 1)];
         tile_run1<MULTI>(c, l, nrows, vec, st, n, nn, nvec, has_next);
-        for (int e = threadIdx.x; e < nrows / 2; e += kThreads) {
+        if (e < nrows / 2) {
             const int r = 2 * e;
             const float a0 = l.outv[r], a1 = l.outv[r + 1];
             const int row = c.row0 + r;
             const int d = row % a.hd;
-            if (kind == 2 || a.rope_neox) {
+            if (!rot) {
                 float *dst = kind == 0   ? a.q + row
                              : kind == 1 ? a.kc + (size_t(row / a.hd) * a.max_seq + slot) * a.hd + d
                                          : a.vc + (size_t(row / a.hd) * a.max_seq + slot) * a.hd + d;
                 dst[0] = a0;
                 dst[1] = a1;
             } else {
-                const float2 cs = a.rope[size_t(pos) * (a.hd / 2) + (d >> 1)];
                 const float b0 = a0 * cs.x - a1 * cs.y;
                 const float b1 = a0 * cs.y + a1 * cs.x;
                 float *dst = (kind == 0) ? a.q + row
@@ -892,10 +1029,13 @@ __global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) {
     CoreArgs c{};
     c.W[0] = a.wg; c.W[1] = a.wu; c.nmat = 2; c.sh = a.sh; c.N = a.F; c.Tc = 1;
     c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    walk_tiles2<MULTI>(c, l, ntiles, [&](const CoreArgs &t, int nrows) {
-        for (int r = threadIdx.x; r < nrows; r += kThreads)
-            a.h[t.row0 + r] = silu(l.outv[r]) * l.outv[a.sh.NR + r];
-    });
+    walk_tiles2<MULTI>(
+        c, l, ntiles,
+        [&](const CoreArgs &t, int nrows) {
+            for (int r = threadIdx.x; r < nrows; r += kThreads)
+                a.h[t.row0 + r] = silu(l.outv[r]) * l.outv[a.sh.NR + r];
+        },
+        nullptr, a.ps);
 }
 
 // Large K (several chunks), no norm: chunk-outer, tile-inner. Only one
@@ -1092,7 +1232,7 @@ __global__ __launch_bounds__(kThreads) void k_lmhead1(LmHeadArgs a) {
     bool vec = tile_vec(c, nrows);
     WStage st;
     stage_issue(c, nrows, 0, vec, st);
-    stage_row1(c, l);
+    stage_row1(c, l, a.ps);
     float *logits = a.st->logits_out;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     float bv = -INFINITY;
@@ -1202,10 +1342,13 @@ static hipError_t set_lds(const void *fn, size_t bytes) {
 
 hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const StepState *st,
                       const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s,
-                      const uint8_t *embed, float *xres) {
+                      const uint8_t *embed, float *xres, const PartSrc &ps) {
     const int maxt = T == 1 ? 1 : kMaxTokChunk;
     if (embed && (T != 1 || !xres)) return hipErrorInvalidValue;
+    if (ps.n > 0 && (T != 1 || embed)) return hipErrorInvalidValue;
+    if (T == 1 && wgemv_fits(d.H)) return launch_wqkv(d, w, x, st, rope, q, kc, vc, s, embed, xres, ps);
     QkvArgs a;
+    a.ps = ps;
     a.embed = embed; a.xres = xres; a.V = d.V;
     a.wq = w.wq; a.wk = w.wk; a.wv = w.wv; a.norm_w = w.attn_norm; a.x = x; a.st = st;
     a.rope = rope; a.q = q; a.kc = kc; a.vc = vc;
@@ -1232,9 +1375,12 @@ hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const S
 }
 
 hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, float *h, int T,
-                         hipStream_t s) {
+                         hipStream_t s, const PartSrc &ps) {
     const int maxt = T == 1 ? 1 : kMaxTokChunk;
+    if (ps.n > 0 && T != 1) return hipErrorInvalidValue;
+    if (T == 1 && wgemv_fits(d.H)) return launch_wgateup(d, w, x, h, s, ps);
     GateUpArgs a;
+    a.ps = ps;
     a.wg = w.wg; a.wu = w.wu; a.norm_w = w.ffn_norm; a.x = x; a.h = h; a.F = d.F; a.T = T;
     a.eps = d.eps;
     a.sh = choose_shape(d.F, d.H, maxt, 2, 512, 1);
@@ -1263,6 +1409,7 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
     a.W = W; a.norm_w = norm_w; a.x = X; a.y = Y; a.N = N; a.T = T; a.accumulate = accumulate;
     a.eps = eps;
     a.sh = choose_shape(N, K, maxt, 1, 512, 1);
+    if (T == 1 && !norm_w && wgemv_fits(K)) return launch_wmatmul(W, N, K, X, accumulate, Y, s);
     if (T == 1) {
         if (a.sh.PC != a.sh.P && !norm_w) {  // large K: chunk-outer walk
             a.sh = chunked_shape(a.sh);
@@ -1311,8 +1458,9 @@ static int lmhead_blocks(int V, int K) {
 }
 
 hipError_t launch_lmhead(const Dims &d, const uint8_t *Wout, const float *out_norm,
-                         const float *x_last, StepState *st, float *partials, hipStream_t s) {
+                         const float *x_last, StepState *st, float *partials, hipStream_t s, const PartSrc &ps) {
     LmHeadArgs a;
+    a.ps = ps;
     a.W = Wout; a.norm_w = out_norm; a.x = x_last; a.st = st; a.partials = partials;
     a.V = d.V; a.eps = d.eps;
     a.sh = choose_shape(d.V, d.H, 1, 1, 1024, 1);

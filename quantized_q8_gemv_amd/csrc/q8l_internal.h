@@ -52,6 +52,17 @@ struct GemvShape {
     int rowbytes; // P * 68
 };
 
+// Split-K partial sums waiting to be added to the residual row: the kernels
+// with a norm in front read x + (p_0 + p_1 + ... + p_{n-1}) (each p_i a row of
+// `stride` floats at part + i * stride, summed in index order) and workgroup
+// 0 writes that row to xout, the residual for what follows.
+struct PartSrc {
+    const float *part = nullptr;
+    int n = 0;
+    int stride = 0;
+    float *xout = nullptr;
+};
+
 // ---- launchers (k_*.hip) -------------------------------------------------
 
 // Block formats a matrix may be stored in. Q4_K and Q6_K (256-weight blocks)
@@ -95,7 +106,19 @@ hipError_t launch_embed(const uint8_t *E, int H, int V, const StepState *st,
 // step's token (Q8_0 rows of embed), and xres receives it as the residual.
 hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const StepState *st,
                       const float2 *rope, float *q, float *kc, float *vc, int T,
-                      hipStream_t s, const uint8_t *embed = nullptr, float *xres = nullptr);
+                      hipStream_t s, const uint8_t *embed = nullptr, float *xres = nullptr,
+                      const PartSrc &ps = PartSrc{});
+// Single-token products for short rows (K = 64 P, P in a fixed set of small
+// values: wgemv_fits): one wave per row pair, no LDS or barriers
+// (k_wgemv.hip). launch_qkv, launch_gateup and launch_matmul (without a norm)
+// take this path by themselves when T == 1 and the rows fit.
+bool wgemv_fits(int K);
+hipError_t launch_wqkv(const Dims &d, const LayerPtrs &w, const float *x, const StepState *st, const float2 *rope,
+                       float *q, float *kc, float *vc, hipStream_t s, const uint8_t *embed, float *xres,
+                       const PartSrc &ps);
+hipError_t launch_wgateup(const Dims &d, const LayerPtrs &w, const float *x, float *h, hipStream_t s,
+                          const PartSrc &ps);
+hipError_t launch_wmatmul(const uint8_t *W, int N, int K, const float *x, int accumulate, float *y, hipStream_t s);
 // Y[t] (+)= W U[t] for generic use (o-proj / down with accumulate = 1).
 hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
                          const float *norm_w, float eps, int accumulate, float *Y,
@@ -117,12 +140,13 @@ hipError_t launch_oproj_merged(const uint8_t *W, int N, int K, const float *part
                                const StepState *st, float *Y, hipStream_t s);
 // h[t] = silu(Wg u[t]) * (Wu u[t]), u = rmsnorm(x[t]).
 hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, float *h, int T,
-                         hipStream_t s);
+                         hipStream_t s, const PartSrc &ps = PartSrc{});
 // logits = Wout rmsnorm(x[T-1]); argmax by the last workgroup; state update.
 // Output layer logits + per-workgroup argmax partials; then the one-workgroup
 // merge (which also advances the step state for on-device generation).
 hipError_t launch_lmhead(const Dims &d, const uint8_t *Wout, const float *out_norm,
-                         const float *x_last, StepState *st, float *partials, hipStream_t s);
+                         const float *x_last, StepState *st, float *partials, hipStream_t s,
+                         const PartSrc &ps = PartSrc{});
 hipError_t launch_argmax_finish(const Dims &d, const float *partials, StepState *st,
                                 hipStream_t s);
 hipError_t launch_argmax(const float *x, int64_t n, uint32_t *out, float *partials,
@@ -142,12 +166,41 @@ struct AttnDecodeArgs {
     float *o;            // n_splits == 1 only: the normalised output [nh][hd] instead of partials (or NULL)
 };
 hipError_t launch_attn_decode(const AttnDecodeArgs &a, hipStream_t s);
+// Decode attention of a cache that fits one split (kv_len <= attn_chunk(hd))
+// fused with the o-projection, split over KV groups: part[g][n] = the sum over
+// group g's columns of W_o[n][.] times its heads' normalised output; the
+// residual add of sum_g part[g] is left to the next kernel with a norm in
+// front (PartSrc). W_o Q8_0 [N][nh*hd]; part [nkv][N].
+struct AttnODecodeArgs {
+    AttnDecodeArgs at;
+    const uint8_t *wo;
+    int N;          // rows of W_o (the model width)
+    int rows;       // rows of W_o per workgroup
+    float *part;
+};
+constexpr int kOPad = 68;      // floats per staged 64-value output pair (bank padding)
+constexpr int kAttnOWgs = 64;  // workgroups the fused attention + o-projection aims for
+constexpr size_t kFuseAttnOMaxBytes = 16 * 1024;  // largest n_head_kv * width * 4 fused
+bool attn_o_fits(const Dims &d);  // whole 64-column pairs per group, at most kThreads per row
+int attn_o_rows(const Dims &d);
+hipError_t launch_attn_o(const AttnDecodeArgs &a, const uint8_t *wo, int N, float *part, hipStream_t s);
+
 // Merge split partials into o; with st set, kv_len is read from st->slot + 1.
 hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int nh, int hd,
                                float *o, const StepState *st, hipStream_t s);
 int attn_decode_splits(int kv_len, int hd);
 // Keys per decode attention split.
 __host__ __device__ inline int attn_chunk(int hd) { return hd <= 64 ? 64 : 32; }
+// LDS of one decode attention split: q (G*hd), K tile (chunk*(hd+kKPad)),
+// V tile (chunk*hd), one row of chunk softmax numerators per wave, in floats.
+constexpr int kKPad = 4;
+__host__ __device__ inline size_t attn_decode_lds(int G, int hd) {
+    const int C = attn_chunk(hd);
+    return sizeof(float) * (size_t(G) * hd + size_t(C) * (hd + kKPad) + size_t(C) * hd + size_t(kThreads / 64) * C);
+}
+// The fused attention + o-projection stages the group's output after that,
+// at a 16-byte boundary (it is read as float4).
+__host__ __device__ inline size_t attn_o_xs_offset(int G, int hd) { return (attn_decode_lds(G, hd) + 15) & ~size_t(15); }
 size_t lmhead_partials_bytes(int V, int K);
 
 // Scaling of the activations the MFMA kernels take as f16 pairs (hi + lo):

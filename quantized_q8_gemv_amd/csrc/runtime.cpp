@@ -33,7 +33,6 @@
 namespace q8l {
 size_t lmhead_partials_bytes(int V, int K);
 __host__ __device__ int attn_chunk(int hd);
-size_t attn_decode_lds(int G, int hd);
 }  // namespace q8l
 
 using namespace q8l;
@@ -47,6 +46,7 @@ size_t al256(size_t v) { return (v + 255) & ~size_t(255); }
 struct Layout {
     size_t state, counters, rope, tok, kc, vc, x, q, att, h, u, logits, lm_part, attn_part, kpart, total;
     size_t rs, eg_h, el_h;  // prefill activation scaling: row factors, h row / block exponents
+    size_t x_alt, part_o;   // decode: second residual row, split-K partials of the fused attention + o
     int el_stride;          // 32-wide blocks per h row
     size_t kv_layer;  // floats per layer in kc (and vc)
     int max_splits;
@@ -107,6 +107,8 @@ Layout make_layout(const q8l_config *c) {
     L.rs = take(S * 4);
     L.eg_h = take(S * 4);
     L.el_h = take(S * size_t(L.el_stride));
+    L.x_alt = take(H * 4);
+    L.part_o = take(size_t(c->n_head_kv) * H * 4);
     L.total = off;
     return L;
 }
@@ -124,6 +126,7 @@ struct q8l_model {
     const uint8_t *tok_embd = nullptr, *output = nullptr;
     const float *out_norm = nullptr;
     bool merge_in_o = false;  // decode o-projection merges 2..8 attention splits in its prologue
+    bool fuse_attn_o = false; // one-split decode: attention and o-projection in one kernel (split-K by group)
     std::vector<std::vector<const void *>> layer_ptrs;  // [L][S_NSLOT]
     std::vector<int> fmt_o, fmt_d;                      // [L] WFmt of attn_output / ffn_down
     uint8_t *ws = nullptr;
@@ -194,6 +197,22 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
     _Float16 *att_s = m->at<_Float16>(m->lay.att), *h_s = m->at<_Float16>(m->lay.h);
     float *kpart = m->at<float>(m->lay.kpart);
     int pend = 0;  // split-K partial sums not yet added to x (the next norm kernel adds them)
+    // Decode residual: two rows. A kernel that adds split-K partials (of the
+    // fused attention + o-projection) to the residual reads xr[cur] and its
+    // workgroup 0 writes the sum to xr[cur ^ 1] (the others still read
+    // xr[cur]); cur then flips. Prefill keeps x.
+    float *xr[2] = {x, m->at<float>(m->lay.x_alt)};
+    int cur = 0;
+    PartSrc dpend;  // decode partials not yet added to xr[cur]
+    auto take_pending = [&]() {
+        PartSrc p = dpend;
+        if (p.n > 0) {
+            p.xout = xr[cur ^ 1];
+            cur ^= 1;
+        }
+        dpend = PartSrc{};
+        return p;
+    };
     // Activation scaling of the f16-pair planes (ActScale): the normalised
     // rows carry per-row factors, h per-(row, block) exponents from the
     // gate/up epilogue; q/k/v, the attention output and f32 inputs split
@@ -228,11 +247,15 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
         } else {
             // a decode step's first layer dequantizes the token's embedding itself
             const uint8_t *emb = (T == 1 && l == 0) ? m->tok_embd : nullptr;
-            if ((e = launch_qkv(d, w, x, st, rope, q, m->kc(l), m->vc(l), T, s, emb, emb ? x : nullptr)) != hipSuccess)
+            float *xin = xr[cur];
+            const PartSrc ps = take_pending();
+            if ((e = launch_qkv(d, w, xin, st, rope, q, m->kc(l), m->vc(l), T, s, emb, emb ? xin : nullptr, ps)) !=
+                hipSuccess)
                 return e;
         }
         if (d.rope_neox && (e = launch_rope_neox(d, st, rope, q, m->kc(l), T, s)) != hipSuccess) return e;
         if (T == 1) {
+            bool continue_ffn = false;
             AttnDecodeArgs a;
             a.q = q; a.kc = m->kc(l); a.vc = m->vc(l);
             a.part = m->at<float>(m->lay.attn_part);
@@ -240,16 +263,28 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = decode_splits;
             a.scale = 1.0f / sqrtf(float(d.hd));
             a.o = decode_splits == 1 ? att : nullptr;  // one split: the attention kernel normalises
-            // a few splits of a small model: the o-projection merges them in its prologue (no merge node)
-            const bool merge_o = w.fo == F_Q8_0 && m->merge_in_o && oproj_merges(d, decode_splits);
-            if ((e = launch_attn_decode(a, s)) != hipSuccess) return e;
-            if (decode_splits > 1 && !merge_o &&
-                (e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s)) != hipSuccess)
-                return e;
-            e = w.fo != F_Q8_0 ? launch_kq_gemv(w.fo, w.wo, d.H, QD, att, 1, x, s)
-                : merge_o      ? launch_oproj_merged(w.wo, d.H, QD, a.part, decode_splits, d.hd, st, x, s)
-                               : launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, x, s);
-            if (e != hipSuccess) return e;
+            if (decode_splits == 1 && w.fo == F_Q8_0 && m->fuse_attn_o) {
+                // one kernel; its partial sums wait for the gate/up kernel's prologue
+                float *part_o = m->at<float>(m->lay.part_o);
+                if ((e = launch_attn_o(a, w.wo, d.H, part_o, s)) != hipSuccess) return e;
+                dpend.part = part_o;
+                dpend.n = d.nkv;
+                dpend.stride = d.H;
+                continue_ffn = true;
+            }
+            if (!continue_ffn) {
+                float *xo = xr[cur];
+                // a few splits of a small model: the o-projection merges them in its prologue (no merge node)
+                const bool merge_o = w.fo == F_Q8_0 && m->merge_in_o && oproj_merges(d, decode_splits);
+                if ((e = launch_attn_decode(a, s)) != hipSuccess) return e;
+                if (decode_splits > 1 && !merge_o &&
+                    (e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s)) != hipSuccess)
+                    return e;
+                e = w.fo != F_Q8_0 ? launch_kq_gemv(w.fo, w.wo, d.H, QD, att, 1, xo, s)
+                    : merge_o      ? launch_oproj_merged(w.wo, d.H, QD, a.part, decode_splits, d.hd, st, xo, s)
+                                   : launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, xo, s);
+                if (e != hipSuccess) return e;
+            }
         } else {
             AttnPrefillArgs a;
             a.q = q; a.kc = m->kc(l); a.vc = m->vc(l); a.o = att;
@@ -275,21 +310,25 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             e = w.fd != F_Q8_0 ? launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s, sc_h_in)
                                : gemm_accumulate(w.wd, d.F, h_s, sc_h_in);
         } else {
-            if ((e = launch_gateup(d, w, x, h, T, s)) != hipSuccess) return e;
+            const float *xin = xr[cur];
+            const PartSrc ps = take_pending();
+            if ((e = launch_gateup(d, w, xin, h, T, s, ps)) != hipSuccess) return e;
+            float *xd = xr[cur];
             if (w.fd == F_Q8_0)
-                e = launch_matmul(w.wd, d.H, d.F, h, T, nullptr, d.eps, 1, x, s);
+                e = launch_matmul(w.wd, d.H, d.F, h, T, nullptr, d.eps, 1, xd, s);
             else if (T == 1)
-                e = launch_kq_gemv(w.fd, w.wd, d.H, d.F, h, 1, x, s);
+                e = launch_kq_gemv(w.fd, w.wd, d.H, d.F, h, 1, xd, s);
             else
-                e = launch_gemm_kq(w.fd, w.wd, d.H, d.F, h, false, T, 1, x, s, sc_o);
+                e = launch_gemm_kq(w.fd, w.wd, d.H, d.F, h, false, T, 1, xd, s, sc_o);
         }
         if (e != hipSuccess) return e;
     }
     if (pend > 0 && (e = launch_rms_split(x, T, d.H, nullptr, d.eps, nullptr, kpart, pend, s)) != hipSuccess)
         return e;
     const uint8_t *wout = m->cfg.tied_output ? m->tok_embd : m->output;
-    if ((e = launch_lmhead(d, wout, m->out_norm, x + size_t(T - 1) * d.H, st,
-                           m->at<float>(m->lay.lm_part), s)) != hipSuccess)
+    PartSrc ps = dpend;  // (none: every layer ends with a plain down projection)
+    if ((e = launch_lmhead(d, wout, m->out_norm, xr[cur] + size_t(T - 1) * d.H, st,
+                           m->at<float>(m->lay.lm_part), s, ps)) != hipSuccess)
         return e;
     return launch_argmax_finish(d, m->at<float>(m->lay.lm_part), st, s);
 }
@@ -432,6 +471,9 @@ q8l_status q8l_create(const q8l_config *cfg, q8l_model **out) {
     m->lay = make_layout(cfg);
     // the merged attention row is staged whole in LDS (as the o-projection GEMV stages rows of <= 150 pairs)
     m->merge_in_o = (cfg->n_head * cfg->head_dim / kPairWeights) * 68 * 4 <= 40 * 1024;
+    // every workgroup of the kernel after the fused attention + o-projection
+    // reads the n_head_kv partial rows: only while they are a few KB
+    m->fuse_attn_o = attn_o_fits(m->d) && size_t(cfg->n_head_kv) * cfg->n_embd * 4 <= kFuseAttnOMaxBytes;
     m->layer_ptrs.assign(cfg->n_layer, std::vector<const void *>(S_NSLOT, nullptr));
     m->fmt_o.assign(cfg->n_layer, F_Q8_0);
     m->fmt_d.assign(cfg->n_layer, F_Q8_0);
@@ -620,6 +662,16 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     float *h = m->at<float>(m->lay.h);
     const uint8_t *wout = m->cfg.tied_output ? m->tok_embd : m->output;
     const int n_splits = split_bucket(m, kv_len);
+    // as in the step: with one split the attention and the o-projection are
+    // one kernel, and gate/up adds its partial sums to the residual first
+    const bool fused = n_splits == 1 && m->fuse_attn_o && m->layer(0).fo == F_Q8_0;
+    PartSrc ps_gu;
+    if (fused) {
+        ps_gu.part = m->at<float>(m->lay.part_o);
+        ps_gu.n = d.nkv;
+        ps_gu.stride = d.H;
+        ps_gu.xout = m->at<float>(m->lay.x_alt);
+    }
     int rep = 0;  // launches of the current kind so far: layer rep mod n_layer
     auto launch = [&](int kind) -> hipError_t {
         const int l = rep++ % m->cfg.n_layer;
@@ -637,13 +689,15 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
                 return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(l), m->vc(l), 1, s);
             case 1:  // q/k/v as every layer but the first runs it (that one also reads the embedding)
                 return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(l), m->vc(l), 1, s);
-            case 2: return launch_attn_decode(a, s);
+            case 2:
+                if (fused && w.fo == F_Q8_0) return launch_attn_o(a, w.wo, d.H, m->at<float>(m->lay.part_o), s);
+                return launch_attn_decode(a, s);
             case 3:
                 if (w.fo != F_Q8_0) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
                 if (m->merge_in_o && oproj_merges(d, a.n_splits))  // as in the step
                     return launch_oproj_merged(w.wo, d.H, QD, a.part, a.n_splits, d.hd, S, x, s);
                 return launch_matmul(w.wo, d.H, QD, m->at<float>(m->lay.att), 1, nullptr, d.eps, 1, x, s);
-            case 4: return launch_gateup(d, w, x, h, 1, s);
+            case 4: return launch_gateup(d, w, x, h, 1, s, ps_gu);
             case 5:
                 if (w.fd != F_Q8_0) return launch_kq_gemv(w.fd, w.wd, d.H, d.F, h, 1, x, s);
                 return launch_matmul(w.wd, d.H, d.F, h, 1, nullptr, d.eps, 1, x, s);
@@ -670,7 +724,8 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     for (int k = 0; k < kKinds && err == hipSuccess; ++k) {
         float ms = 0.f;
         if ((err = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1])) != hipSuccess) break;
-        ms_out[k] = k == 0 ? -1.0f : ms / float(reps);  // kind 0: not a kernel of the step
+        // kind 0: not a kernel of the step; kind 3 is part of kind 2 when fused
+        ms_out[k] = (k == 0 || (k == 3 && fused)) ? -1.0f : ms / float(reps);
     }
     for (auto &e : ev)
         if (e) hipEventDestroy(e);
