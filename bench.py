@@ -70,29 +70,57 @@ PAGES_DECODE_MS = {"C2": 2.6, "C3": 2.72}
 KIND_NAMES = ["embed", "qkv_rope_kv", "attn_decode", "oproj_residual", "gateup_silu",
               "down_residual", "lmhead", "argmax_finish"]
 NKINDS = len(KIND_NAMES)
-KIND_SOURCES = {"embed": "quantized_q8_gemv_amd/csrc/k_misc.hip", "attn_decode": "quantized_q8_gemv_amd/csrc/k_attn.hip"}
+# source of each kind's kernel on the 135M shape, whose PMC summary is committed
+KIND_SOURCES = {"embed": "quantized_q8_gemv_amd/csrc/k_misc.hip", "attn_decode": "quantized_q8_gemv_amd/csrc/k_attn.hip",
+                "lmhead": "quantized_q8_gemv_amd/csrc/k_gemv.hip", "argmax_finish": "quantized_q8_gemv_amd/csrc/k_gemv.hip"}
 for _k in KIND_NAMES:
-    KIND_SOURCES.setdefault(_k, "quantized_q8_gemv_amd/csrc/k_gemv.hip")
+    KIND_SOURCES.setdefault(_k, "quantized_q8_gemv_amd/csrc/k_wgemv.hip")
 # rocprofv3 PMC summaries of the decode kernels (FETCH_SIZE and WRITE_SIZE per
 # dispatch, scaled by the same counters on a copy of known size); a summary
 # counts only while the kernel source it was taken with is unchanged.
 TRAFFIC_FILES = {"C2": "profiles/decode_kernels_135m_13+20_pmc_traffic.md"}
 
 
-def kernel_symbols(s, down_fmt="q8_0"):
-    """Device symbol of each decode kernel kind at this shape (T = 1). A
-    Q4_K / Q6_K down projection runs k_kq_gemv<format, rows per wave>."""
+WAVE_GEMV_PAIRS = (1, 2, 4, 8, 9, 12, 16, 24)   # row lengths (64-weight pairs) of the wave-per-row GEMVs
+
+
+def attn_chunk(hd):
+    return 64 if hd <= 64 else 32
+
+
+def decode_fused(s, kv_len, o_fmt="q8_0"):
+    """Whether a decode step at this cache length runs the attention and the
+    o-projection as one kernel (the runtime's rule: one attention split, the
+    group's columns in whole 64-weight pairs, at most 16 KB of per-group
+    partial rows, a Q8_0 o-projection)."""
+    G = s.n_head // s.n_head_kv
+    return (kv_len <= attn_chunk(s.head_dim) and (G * s.head_dim) % 64 == 0 and G * s.head_dim // 64 <= 256
+            and s.n_head_kv * s.n_embd * 4 <= 16 * 1024 and o_fmt == "q8_0")
+
+
+def kernel_symbols(s, down_fmt="q8_0", kv_len=1):
+    """Device symbol of each decode kernel kind at this shape (T = 1) and
+    cache length. Rows of a few pairs run the wave-per-row kernels
+    (k_w*<pairs>); longer rows the LDS-staged ones. A Q4_K / Q6_K down
+    projection runs k_kq_gemv<format, rows per wave>. With the attention
+    fused into the o-projection, the o-projection has no kernel of its own
+    (None)."""
     multi = (s.n_embd // 64) * 272 > 40 * 1024  # rows longer than one LDS chunk
     o_multi = (s.q_dim // 64) * 272 > 40 * 1024
     down_multi = (s.n_ff // 64) * 272 > 40 * 1024
+    ph, pq, pf = s.n_embd // 64, s.q_dim // 64, s.n_ff // 64
+    wave_h = ph in WAVE_GEMV_PAIRS
     if down_fmt == "q8_0":
-        down = "k_matmul1_chunked" if down_multi else "k_matmul1<false, false>"
+        down = (f"k_wmatmul1<{pf}>" if pf in WAVE_GEMV_PAIRS
+                else "k_matmul1_chunked" if down_multi else "k_matmul1<false, false>")
     else:
         down = f"k_kq_gemv<{1 if down_fmt == 'q4_k' else 2}, {2 if s.n_embd >= 4096 else 1}>"
-    # the o-projection at one attention split (k_matmul1<false, true> merges
-    # several splits in its prologue at the 135M shape)
-    return ["k_embed", f"k_qkv1<{str(multi).lower()}>", "k_attn_decode",
-            "k_matmul1_chunked" if o_multi else "k_matmul1<false, false>", f"k_gateup1<{str(multi).lower()}>",
+    fused = decode_fused(s, kv_len)
+    oproj = (None if fused else f"k_wmatmul1<{pq}>" if pq in WAVE_GEMV_PAIRS
+             else "k_matmul1_chunked" if o_multi else "k_matmul1<false, false>")
+    return ["k_embed", f"k_wqkv1<{ph}>" if wave_h else f"k_qkv1<{str(multi).lower()}>",
+            "k_attn_o1" if fused else "k_attn_decode", oproj,
+            f"k_wgateup1<{ph}>" if wave_h else f"k_gateup1<{str(multi).lower()}>",
             down, f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
 
 
@@ -123,8 +151,8 @@ def measured_traffic(config, kind):
 # rocprofv3 --kernel-trace --stats summaries of the bench command per workload;
 # a summary's figures count only while the sources it lists are unchanged.
 STATS_FILES = {"C2": "profiles/decode_prefill_135m_13+20_kernel_stats.md"}
-STATS_SOURCES = ["quantized_q8_gemv_amd/csrc/k_gemv.hip", "quantized_q8_gemv_amd/csrc/k_attn.hip",
-                 "quantized_q8_gemv_amd/csrc/runtime.cpp"]
+STATS_SOURCES = ["quantized_q8_gemv_amd/csrc/k_gemv.hip", "quantized_q8_gemv_amd/csrc/k_wgemv.hip",
+                 "quantized_q8_gemv_amd/csrc/k_attn.hip", "quantized_q8_gemv_amd/csrc/runtime.cpp"]
 
 
 def short_symbol(name):
@@ -179,7 +207,7 @@ def pmc_summary(fetch_dir, write_dir, config="C2"):
     import synth
     _, model, prompt = synth.workload_inputs(config)
     s = model.shape
-    syms = kernel_symbols(s)
+    syms = kernel_symbols(s, kv_len=len(prompt) + 1)
     alg_bytes = kernel_bytes(s, len(prompt) + 1)  # attention at the first decode step
 
     def load(d, counter):
@@ -293,13 +321,18 @@ def kv_bytes_per_position(s):
 
 
 def kernel_bytes(s, kv_len, down_fmt="q8_0"):
-    """Algorithmic bytes of one launch of each decode kernel kind (layer 0)."""
+    """Algorithmic bytes of one launch of each decode kernel kind (layer 0).
+    Fused attention + o-projection (kind 2): the cache and q, the o weights
+    and the per-group partial rows it writes; kind 3 is then 0."""
     H, QD, KVD, F, V = s.n_embd, s.q_dim, s.kv_dim, s.n_ff, s.n_vocab
+    attn = kv_len * s.n_head_kv * s.head_dim * 4 * 2 + QD * 4
+    oproj = q8_bytes(H, QD) + QD * 4 + 2 * H * 4
+    fused = decode_fused(s, kv_len)
     return [
         q8_bytes(1, H) + H * 4,
         q8_bytes(QD + 2 * KVD, H) + 2 * H * 4 + (QD + 2 * KVD) * 4,
-        kv_len * s.n_head_kv * s.head_dim * 4 * 2 + QD * 4,
-        q8_bytes(H, QD) + QD * 4 + 2 * H * 4,
+        attn + q8_bytes(H, QD) + s.n_head_kv * H * 4 if fused else attn,
+        0 if fused else oproj,
         2 * q8_bytes(F, H) + 2 * H * 4 + F * 4,
         fmt_bytes(down_fmt, H, F) + F * 4 + 2 * H * 4,
         q8_bytes(V, H) + 2 * H * 4 + V * 4,
@@ -801,7 +834,7 @@ def main():
                                "launches_per_token": launches[i]} for i in range(NKINDS)}
     achieved = kb[dom] / (ms[dom] * 1e-3) / 1e9
     traffic = measured_traffic(args.config, KIND_NAMES[dom]) if down_fmts is None else None
-    symbol = kernel_symbols(s, down0)[dom]
+    symbol = kernel_symbols(s, down0, kv_len)[dom]
     prof_us = profiled_us(args.config, symbol) if down_fmts is None else None
     step_frac = round(dev_gbs / PEAK_HBM_GBS, 4)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -183,7 +183,10 @@ q8l_status q8l_finalize(q8l_model *m, void *stream);
  * magnitude. q, k, v, the attention output and the few f32 inputs that are
  * split on the way must stay below 2^15 in magnitude: when one does not, the
  * model's NEXT forward or generate call returns Q8L_E_RANGE once (that
- * prefill's logits are not exact) and does nothing else.
+ * prefill's logits are not exact) and does nothing else. q, k and v are
+ * checked where a prefill writes them; cached keys and values that decode
+ * steps wrote (single-token steps compute in f32 and check nothing) are
+ * checked when a prefill that appends to the cache first reads them.
  */
 q8l_status q8l_forward(q8l_model *m, const uint32_t *tokens_host, int32_t n_tokens,
                        int32_t index_pos, float *logits_dev, uint32_t *argmax_dev,

@@ -414,19 +414,15 @@ __device__ __forceinline__ void split16(float v, _Float16 &hi, _Float16 &lo) {
     lo = static_cast<_Float16>(v - static_cast<float>(hi));
 }
 
-// Four values as f16 pairs; true when one of them is outside the pairs'
-// range (|v| >= 2^15 or not finite).
-__device__ __forceinline__ bool split4(const float v[4], uint2 &hi, uint2 &lo) {
+// Four values as f16 pairs. (Q, K and V are range-checked where they are
+// written: the q/k/v kernels of a prefill, and a check of the cached
+// positions a decode step wrote before a prefill reads them.)
+__device__ __forceinline__ void split4(const float v[4], uint2 &hi, uint2 &lo) {
     _Float16 h[4], l[4];
-    bool bad = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        split16(v[i], h[i], l[i]);
-        bad |= !(fabsf(v[i]) < kPairRange);
-    }
+    for (int i = 0; i < 4; ++i) split16(v[i], h[i], l[i]);
     hi = __builtin_bit_cast(uint2, h);
     lo = __builtin_bit_cast(uint2, l);
-    return bad;
 }
 
 // Slot of key k (0..FK-1, a multiple of 4) in the P^T operand order: within a
@@ -466,19 +462,17 @@ __device__ __forceinline__ void kv_load(const float *kb, const float *vb, int j0
     }
 }
 
-// Returns whether a K or V value was outside the f16 pairs' range.
 template <int HD>
-__device__ __forceinline__ bool kv_store(const KvRegs<HD> &r, FlashLds<HD> &L) {
+__device__ __forceinline__ void kv_store(const KvRegs<HD> &r, FlashLds<HD> &L) {
     constexpr int LD = HD + 8, LV = FK + 8;
     const int tid = threadIdx.x;
-    bool bad = false;
 #pragma unroll
     for (int i = 0; i < FK * HD / 4 / kThreads; ++i) {
         const int e = tid + i * kThreads;
         const int j = e / (HD / 4), d4 = (e - j * (HD / 4)) * 4;
         const float kk[4] = {r.k[i].x, r.k[i].y, r.k[i].z, r.k[i].w};
         uint2 hi, lo;
-        bad |= split4(kk, hi, lo);
+        split4(kk, hi, lo);
         *reinterpret_cast<uint2 *>(L.kh + j * LD + d4) = hi;
         *reinterpret_cast<uint2 *>(L.kl + j * LD + d4) = lo;
     }
@@ -487,12 +481,11 @@ __device__ __forceinline__ bool kv_store(const KvRegs<HD> &r, FlashLds<HD> &L) {
         const int e = tid + i * kThreads;
         const int quad = e / HD, d = e - quad * HD;
         uint2 hi, lo;
-        bad |= split4(&r.v[4 * i], hi, lo);
+        split4(&r.v[4 * i], hi, lo);
         const int slot = key_slot(4 * quad);
         *reinterpret_cast<uint2 *>(L.vh + d * LV + slot) = hi;
         *reinterpret_cast<uint2 *>(L.vl + d * LV + slot) = lo;
     }
-    return bad;
 }
 
 template <int HD>
@@ -513,14 +506,12 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
     // by 1/sqrt(hd) * log2(e) so that the softmax runs on exp2
     const float qscale = a.scale * 1.4426950408889634f;
     half8 qh[HD / 32], ql[HD / 32];
-    bool bad = false;   // a Q, K or V value outside the f16 pairs' range
 #pragma unroll
     for (int s = 0; s < HD / 32; ++s)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float v = (qi < a.T) ? a.q[size_t(qi) * row_stride + h * HD + 32 * s + 8 * grp + j] * qscale : 0.f;
             _Float16 hi, lo;
-            bad |= !(fabsf(v) < kPairRange);
             split16(v, hi, lo);
             qh[s][j] = hi;
             ql[s][j] = lo;
@@ -539,7 +530,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
     kv_load<HD>(kb, vb, 0, blk_last, kv);
     for (int j0 = 0; j0 <= blk_last; j0 += FK) {
         __syncthreads();  // the previous block's LDS tiles are no longer read
-        bad |= kv_store<HD>(kv, L);
+        kv_store<HD>(kv, L);
         __syncthreads();
         if (j0 + FK <= blk_last) kv_load<HD>(kb, vb, j0 + FK, blk_last, kv);
         // S^T for 4 key tiles of 16
@@ -622,16 +613,21 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
             o[t] = acc;
         }
     }
-    if (bad && a.range_flag) *a.range_flag = 1u;
     if (qi < a.T) {
         const float inv = 1.0f / lsum;
         const size_t base = size_t(qi) * row_stride + h * HD;
         if (a.o_split) {
             const size_t plane = size_t(a.T) * row_stride;
+            bool bad = false;   // an output outside the f16 pairs' range
 #pragma unroll
             for (int t = 0; t < HD / 16; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) store_hilo(a.o_split, plane, base + t * 16 + 4 * grp + i, o[t][i] * inv);
+                for (int i = 0; i < 4; ++i) {
+                    const float ov = o[t][i] * inv;
+                    bad |= !(fabsf(ov) < kPairRange);
+                    store_hilo(a.o_split, plane, base + t * 16 + 4 * grp + i, ov);
+                }
+            if (bad && a.range_flag) *a.range_flag = 1u;
         } else {
             float *dst = a.o + base;
 #pragma unroll

@@ -263,13 +263,26 @@ __device__ inline bool tile_rescales(const GemmArgs &a, int m0) {
     return __syncthreads_or(any) != 0;
 }
 
-// The factor that takes row t's scaling out of a product: sc.rs[t] (the
-// normalised input's per-row factor) and 2^-eg[t] (the row exponent).
-__device__ inline float row_factor(const GemmArgs &a, int t, bool resc) {
-    float f = a.sc.rs ? a.sc.rs[t] : 1.0f;
-    if (resc) f = ldexpf(f, -a.sc.eg[t]);
-    return f;
-}
+// The factors that take the rows' scaling out of a product: sc.rs[t] (the
+// normalised input's per-row factor) times 2^-eg[t] (the row exponent, 0
+// where rows are not rescaled), for the rows t = m0 + wm*WM + ms*16 +
+// 4*(lane/16) + i this lane's accumulators hold (1 past T). Loaded at the
+// start of the kernel, so the epilogue does not wait for them.
+template <int TM, int TN>
+struct RowFactors {
+    float f[Cfg<TM, TN>::MS][4];
+    __device__ __forceinline__ void load(const GemmArgs &a, int m0, int wm, int lane) {
+        using C = Cfg<TM, TN>;
+#pragma unroll
+        for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = min(m0 + wm * C::WM + ms * 16 + 4 * (lane >> 4) + i, a.T - 1);
+                const float r = a.sc.rs ? a.sc.rs[t] : 1.0f;
+                f[ms][i] = a.sc.eg ? ldexpf(r, -a.sc.eg[t]) : r;
+            }
+    }
+};
 
 template <bool A32, int TM, int TN>
 __device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf, const GemmArgs &a, int m0, int ks, bool resc) {
@@ -345,7 +358,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
     }
     GSrc<TM, TN> src;
     g_setup<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, src);
-    const bool resc = A32 ? false : tile_rescales<TM>(a, m0);
+    // only products of the gate/up output (o-type epilogues) see per-block
+    // exponents; q/k/v and gate/up read the normalised rows (row factors only)
+    constexpr bool kResc = !A32 && EPI != G_QKV && EPI != G_GATEUP;
+    const bool resc = kResc ? tile_rescales<TM>(a, m0) : false;
+    RowFactors<TM, TN> rf;
+    rf.load(a, m0, wm, lane);
     // Every stage issues its loads unconditionally (steps past the end
     // re-read the last step, whose registers are never stored): with no
     // branch around them the compiler can wait for the oldest stage alone
@@ -424,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     const int m = wm * C::WM + ms * 16 + 4 * (lane >> 4) + i;
                     const int t = m0 + m;
-                    const float f = t < a.T ? row_factor(a, t, false) : 1.0f;
+                    const float f = rf.f[ms][i];
                     float hv[C::NS];
 #pragma unroll
                     for (int ns = 0; ns < C::NS; ++ns) {
@@ -436,13 +454,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
                     for (int bb = 0; bb < (C::NS + 1) / 2; ++bb) {
                         float mx = fabsf(hv[2 * bb]);
                         if (2 * bb + 1 < C::NS) mx = fmaxf(mx, fabsf(hv[2 * bb + 1]));
-#pragma unroll
-                        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+                        mx = row16_max_dpp(mx);
                         int e = 0;
                         if (!(mx < kPairRange)) e = isfinite(mx) ? max(14 - ilogbf(mx), -126) : -126;
-                        if (t < a.T && a.sc.el_out && (lane & 15) == 0 && 32 * bb < nvalid[0]) {
+                        // el[t][.] was cleared with eg[t] by the norm kernel: only
+                        // nonzero exponents are written
+                        if (e != 0 && t < a.T && a.sc.el_out && (lane & 15) == 0 && 32 * bb < nvalid[0]) {
                             a.sc.el_out[size_t(t) * a.sc.el_stride + (row0 >> 5) + bb] = int8_t(e);
-                            if (e < 0) atomicMin(a.sc.eg_out + t, e);
+                            atomicMin(a.sc.eg_out + t, e);
                         }
 #pragma unroll
                         for (int q = 0; q < 2; ++q) {
@@ -456,6 +475,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
         }
         return;
     }
+    // q/k/v: each value is range-checked here, where it is written (the
+    // prefill attention splits Q, K and V into f16 pairs)
+    bool bad = false;
 #pragma unroll
     for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
@@ -464,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int m = wm * C::WM + ms * 16 + 4 * (lane >> 4) + i;
                 const int c = wn * C::WN + ns * 16 + (lane & 15);
-                const float v = acc[ms][ns][i] * (m0 + m < a.T ? row_factor(a, m0 + m, resc) : 1.0f);
+                const float v = acc[ms][ns][i] * rf.f[ms][i];
                 if (EPI == G_QKV) {
                     // rope pairs (2j, 2j+1) sit in adjacent lanes
                     const float partner = __shfl_xor(v, 1, 64);
@@ -476,10 +498,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
                         float *dst = mat == 0 ? a.q + size_t(t) * a.QD + row
                                               : (mat == 1 ? a.kc : a.vc) +
                                                     (size_t(row / a.hd) * a.max_seq + a.st->slot + t) * a.hd + d;
+                        if (mat == 2) bad |= !(fabsf(v) < kPairRange);   // (NEOX q, k: checked once rotated)
                         *dst = v;
                     } else {
                         const float2 cs = a.rope[size_t(a.st->pos + t) * (a.hd / 2) + (d >> 1)];
                         const float r = (d & 1) ? (partner * cs.y + v * cs.x) : (v * cs.x - partner * cs.y);
+                        bad |= !(fabsf(r) < kPairRange);
                         if (mat == 0)
                             a.q[size_t(t) * a.QD + row] = r;
                         else
@@ -494,6 +518,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
                     *dst = (EPI == G_ACCUM) ? *dst + v : v;
                 }
             }
+    if (EPI == G_QKV && bad && a.sc.range_flag) *a.sc.range_flag = 1u;
 }
 
 // ---- 256-weight block formats (Q4_K, Q6_K), 64 weights per K step.
@@ -689,6 +714,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
 
     const int nsteps = a.K / GK;
     const bool resc = A32 ? false : tile_rescales<TM>(a, m0);
+    RowFactors<TM, TN> rf;
+    rf.load(a, m0, wm, lane);
     KRegs<FMT, TM, TN> regs;
     a_load<A32, TM, TN>(src.ra, src.aoff, 0, regs.a);
     kb_load<FMT, TM, TN>(src, 0, regs);
@@ -770,7 +797,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
                 const int c = wn * C::WN + ns * 16 + (lane & 15);
                 if (m0 + m >= a.T || c >= nvalid) continue;
                 float *dst = a.Y + size_t(m0 + m) * a.Nm[0] + row0 + c;
-                const float v = acc[ms][ns][i] * row_factor(a, m0 + m, resc);
+                const float v = acc[ms][ns][i] * rf.f[ms][i];
                 *dst = (EPI == G_ACCUM) ? *dst + v : v;
             }
 }
@@ -786,7 +813,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
 // row: the row exponent of planes a later kernel of the layer writes.
 __global__ __launch_bounds__(kThreads) void k_rms_split(float *x, int T, int K, const float *w,
                                                         float eps, _Float16 *u, const float *part,
-                                                        int splits, float *rs, int *eg_zero) {
+                                                        int splits, float *rs, int *eg_zero, int8_t *el_zero,
+                                                        int el_n) {
     __shared__ float red[4];
     const size_t row = blockIdx.x;
     float4 *xr = reinterpret_cast<float4 *>(x + row * K);
@@ -810,6 +838,8 @@ __global__ __launch_bounds__(kThreads) void k_rms_split(float *x, int T, int K, 
         ss = fmaf(v.w, v.w, ss);
     }
     if (eg_zero && threadIdx.x == 0) eg_zero[row] = 0;
+    if (el_zero)
+        for (int b = threadIdx.x; b < el_n; b += kThreads) el_zero[row * el_n + b] = 0;
     if (!u) return;
     ss = block_sum(ss, red);
     const float r = 1.0f / sqrtf(ss / static_cast<float>(K) + eps);
@@ -930,8 +960,10 @@ GemmArgs gemm_base(const void *A, int T, int K) {
 }  // namespace
 
 hipError_t launch_rms_split(float *x, int T, int K, const float *w, float eps, _Float16 *u,
-                            const float *part, int splits, hipStream_t s, float *rs, int *eg_zero) {
-    hipLaunchKernelGGL(k_rms_split, dim3(T), dim3(kThreads), 0, s, x, T, K, w, eps, u, part, splits, rs, eg_zero);
+                            const float *part, int splits, hipStream_t s, float *rs, int *eg_zero, int8_t *el_zero,
+                            int el_n) {
+    hipLaunchKernelGGL(k_rms_split, dim3(T), dim3(kThreads), 0, s, x, T, K, w, eps, u, part, splits, rs, eg_zero,
+                       el_zero, el_n);
     return hipGetLastError();
 }
 

@@ -337,6 +337,10 @@ struct QkvArgs {
     float *xres;
     int V;
     PartSrc ps;          // decode: split-K partials added to x first (n = 0: none)
+    // several tokens (a prefill): set to 1 when a written q, k or v value is
+    // outside the f16 pairs' range of the prefill attention (NEOX q and k are
+    // checked by the kernel that rotates them)
+    uint32_t *range_flag;
 };
 
 template <int MAXT, bool MULTI>
@@ -363,6 +367,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
     const int nrows = min(a.sh.NR, N - c.row0);
     const int half = nrows >> 1;
     const int pos0 = a.st->pos + t0, slot0 = a.st->slot + t0;
+    bool bad = false;
     for (int e = threadIdx.x; e < c.Tc * half; e += kThreads) {
         const int t = e / half;
         const int r = 2 * (e - t * half);
@@ -373,6 +378,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
             float *dst = kind == 0   ? a.q + size_t(t0 + t) * a.QD + row
                          : kind == 1 ? a.kc + (size_t(row / a.hd) * a.max_seq + slot0 + t) * a.hd + d
                                      : a.vc + (size_t(row / a.hd) * a.max_seq + slot0 + t) * a.hd + d;
+            if (kind == 2) bad |= !(fabsf(a0) < kPairRange) || !(fabsf(a1) < kPairRange);
             dst[0] = a0;
             dst[1] = a1;
         } else {
@@ -382,10 +388,12 @@ __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
             float *dst = (kind == 0)
                              ? a.q + size_t(t0 + t) * a.QD + row
                              : a.kc + (size_t(row / a.hd) * a.max_seq + slot0 + t) * a.hd + d;
+            bad |= !(fabsf(b0) < kPairRange) || !(fabsf(b1) < kPairRange);
             dst[0] = b0;
             dst[1] = b1;
         }
     }
+    if (bad && a.range_flag) *a.range_flag = 1u;
 }
 
 // ---------------------------------------------------------------- gate/up
@@ -1342,13 +1350,14 @@ static hipError_t set_lds(const void *fn, size_t bytes) {
 
 hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const StepState *st,
                       const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s,
-                      const uint8_t *embed, float *xres, const PartSrc &ps) {
+                      const uint8_t *embed, float *xres, const PartSrc &ps, uint32_t *range_flag) {
     const int maxt = T == 1 ? 1 : kMaxTokChunk;
     if (embed && (T != 1 || !xres)) return hipErrorInvalidValue;
     if (ps.n > 0 && (T != 1 || embed)) return hipErrorInvalidValue;
     if (T == 1 && wgemv_fits(d.H)) return launch_wqkv(d, w, x, st, rope, q, kc, vc, s, embed, xres, ps);
     QkvArgs a;
     a.ps = ps;
+    a.range_flag = T > 1 ? range_flag : nullptr;
     a.embed = embed; a.xres = xres; a.V = d.V;
     a.wq = w.wq; a.wk = w.wk; a.wv = w.wv; a.norm_w = w.attn_norm; a.x = x; a.st = st;
     a.rope = rope; a.q = q; a.kc = kc; a.vc = vc;

@@ -77,18 +77,46 @@ __global__ void k_noop() {}
 // 选"): dimension j of a head is rotated with dimension j + hd/2 by the table's
 // angle for pair j. One workgroup per (token, head); heads [0, nh) are the
 // token's q row, heads [nh, nh + nkv) its new key slot in the cache.
+// (range_flag, when set: 1 if a rotated value is outside the f16 pairs'
+// range of the prefill attention)
 __global__ __launch_bounds__(kThreads) void k_rope_neox(const StepState *st, const float2 *rope, float *q,
-                                                       float *kc, int nh, int hd, int max_seq) {
+                                                       float *kc, int nh, int hd, int max_seq, uint32_t *range_flag) {
     const int t = blockIdx.x, h = blockIdx.y;
     const int half = hd / 2;
     float *v = h < nh ? q + (size_t(t) * nh + h) * hd
                       : kc + (size_t(h - nh) * max_seq + st->slot + t) * hd;
     const float2 *cs = rope + size_t(st->pos + t) * half;
+    bool bad = false;
     for (int j = threadIdx.x; j < half; j += kThreads) {
         const float x0 = v[j], x1 = v[j + half];
-        v[j] = x0 * cs[j].x - x1 * cs[j].y;
-        v[j + half] = x0 * cs[j].y + x1 * cs[j].x;
+        const float y0 = x0 * cs[j].x - x1 * cs[j].y, y1 = x0 * cs[j].y + x1 * cs[j].x;
+        bad |= !(fabsf(y0) < kPairRange) || !(fabsf(y1) < kPairRange);
+        v[j] = y0;
+        v[j + half] = y1;
     }
+    if (bad && range_flag) *range_flag = 1u;
+}
+
+// Range check of cached K and V before a prefill reads them: positions
+// [lo, hi) of every layer's cache (written by decode steps, whose f32
+// arithmetic does not check them). Sets *range_flag to 1 when a value is
+// outside the f16 pairs' range. Grid: (float4 chunks of one position range,
+// 2 * n_layer * nkv cache rows).
+__global__ __launch_bounds__(kThreads) void k_kv_range(const float *kc, const float *vc, size_t layer_stride,
+                                                      int nkv, int max_seq, int hd, int lo, int hi,
+                                                      uint32_t *range_flag) {
+    const int r = blockIdx.y;                  // (cache, layer, kv head)
+    const int which = r & 1, lh = r >> 1;
+    const int l = lh / nkv, g = lh - l * nkv;
+    const float *base = (which ? vc : kc) + size_t(l) * layer_stride + (size_t(g) * max_seq + lo) * hd;
+    const size_t n4 = size_t(hi - lo) * hd / 4;
+    bool bad = false;
+    for (size_t e = size_t(blockIdx.x) * kThreads + threadIdx.x; e < n4; e += size_t(gridDim.x) * kThreads) {
+        const float4 v = reinterpret_cast<const float4 *>(base)[e];
+        bad |= !(fabsf(v.x) < kPairRange) || !(fabsf(v.y) < kPairRange) || !(fabsf(v.z) < kPairRange) ||
+               !(fabsf(v.w) < kPairRange);
+    }
+    if (bad) *range_flag = 1u;
 }
 
 }  // namespace
@@ -120,9 +148,19 @@ hipError_t launch_noop(hipStream_t s) {
 }
 
 hipError_t launch_rope_neox(const Dims &d, const StepState *st, const float2 *rope, float *q, float *kc,
-                            int T, hipStream_t s) {
+                            int T, hipStream_t s, uint32_t *range_flag) {
     hipLaunchKernelGGL(k_rope_neox, dim3(T, d.nh + d.nkv), dim3(64), 0, s, st, rope, q, kc, d.nh, d.hd,
-                       d.max_seq);
+                       d.max_seq, T > 1 ? range_flag : nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_range(const float *kc, const float *vc, size_t layer_stride, int n_layer, int nkv, int max_seq,
+                           int hd, int lo, int hi, uint32_t *range_flag, hipStream_t s) {
+    if (hi <= lo || !range_flag) return hipSuccess;
+    const size_t n4 = size_t(hi - lo) * hd / 4;
+    const int gx = int(std::min<size_t>((n4 + kThreads - 1) / kThreads, 64));
+    hipLaunchKernelGGL(k_kv_range, dim3(gx, 2 * n_layer * nkv), dim3(kThreads), 0, s, kc, vc, layer_stride, nkv,
+                       max_seq, hd, lo, hi, range_flag);
     return hipGetLastError();
 }
 

@@ -95,7 +95,12 @@ hipError_t launch_noop(hipStream_t s);
 // NEOX rotation of the T new tokens' q (rows of [T][nh*hd]) and k (cache slots
 // st->slot + t) at positions st->pos + t.
 hipError_t launch_rope_neox(const Dims &d, const StepState *st, const float2 *rope, float *q, float *kc,
-                            int T, hipStream_t s);
+                            int T, hipStream_t s, uint32_t *range_flag = nullptr);
+// Sets *range_flag when a value of positions [lo, hi) of any layer's K or V
+// cache is outside the f16 pairs' range (before a prefill reads positions a
+// decode step wrote).
+hipError_t launch_kv_range(const float *kc, const float *vc, size_t layer_stride, int n_layer, int nkv, int max_seq,
+                           int hd, int lo, int hi, uint32_t *range_flag, hipStream_t s);
 hipError_t launch_embed(const uint8_t *E, int H, int V, const StepState *st,
                         const uint32_t *tok_buf, int T, int from_state_token, float *x,
                         hipStream_t s);
@@ -107,7 +112,7 @@ hipError_t launch_embed(const uint8_t *E, int H, int V, const StepState *st,
 hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const StepState *st,
                       const float2 *rope, float *q, float *kc, float *vc, int T,
                       hipStream_t s, const uint8_t *embed = nullptr, float *xres = nullptr,
-                      const PartSrc &ps = PartSrc{});
+                      const PartSrc &ps = PartSrc{}, uint32_t *range_flag = nullptr);
 // Single-token products for short rows (K = 64 P, P in a fixed set of small
 // values: wgemv_fits): one wave per row pair, no LDS or barriers
 // (k_wgemv.hip). launch_qkv, launch_gateup and launch_matmul (without a norm)
@@ -213,7 +218,8 @@ size_t lmhead_partials_bytes(int V, int K);
 //             eg[t] = the smallest el of row t); the kernel brings every
 //             block to 2^eg[t] and its epilogue multiplies by 2^-eg[t]
 //   eg_out, el_out  the same exponents for planes this kernel writes
-//             (gate/up: h); eg_out must be 0 before the kernel
+//             (gate/up: h); eg_out and the el_out rows must be 0 before
+//             the kernel (only nonzero block exponents are written)
 //   range_flag set to 1 when a value split here is outside the pair's range
 //             (|v| >= 2^15 or not finite): its products are then not exact
 struct ActScale {
@@ -230,10 +236,11 @@ struct ActScale {
 // are passed as an f16 hi plane [T][K] followed by an f16 lo plane (a_split),
 // or as f32 [T][K].
 // rs (if set) receives each row's factor 2^-e of the scaled planes (see
-// ActScale); eg_zero (if set) is cleared for each row.
+// ActScale); eg_zero (if set) is cleared for each row, and el_zero's el_n
+// bytes of each row with it.
 hipError_t launch_rms_split(float *x, int T, int K, const float *w, float eps, _Float16 *u,
                             const float *part, int splits, hipStream_t s, float *rs = nullptr,
-                            int *eg_zero = nullptr);
+                            int *eg_zero = nullptr, int8_t *el_zero = nullptr, int el_n = 0);
 // Split-K for short prompts: when the plain GEMM would launch only a few
 // workgroups (each walking all of K), the K steps are split over
 // gemm_splitk(N, K, T) > 1 slices that write partial sums part[z][T][N];

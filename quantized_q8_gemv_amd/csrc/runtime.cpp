@@ -139,6 +139,11 @@ struct q8l_model {
     hipStream_t cap = nullptr;
     uint32_t *range_host = nullptr;  // pinned: set by a kernel whose f16-pair split saw a value out of range
     uint32_t *range_dev = nullptr;   // its device address
+    // Cache positions [0, kv_checked) hold K and V known to be inside the f16
+    // pairs' range (written by a prefill, whose q/k/v kernels check what they
+    // write, or checked since); decode steps write unchecked positions, which
+    // are checked before a prefill reads them.
+    int32_t kv_checked = 0;
 
     template <typename T>
     T *at(size_t off) const {
@@ -249,11 +254,12 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             const uint8_t *emb = (T == 1 && l == 0) ? m->tok_embd : nullptr;
             float *xin = xr[cur];
             const PartSrc ps = take_pending();
-            if ((e = launch_qkv(d, w, xin, st, rope, q, m->kc(l), m->vc(l), T, s, emb, emb ? xin : nullptr, ps)) !=
-                hipSuccess)
+            if ((e = launch_qkv(d, w, xin, st, rope, q, m->kc(l), m->vc(l), T, s, emb, emb ? xin : nullptr, ps,
+                                m->range_dev)) != hipSuccess)
                 return e;
         }
-        if (d.rope_neox && (e = launch_rope_neox(d, st, rope, q, m->kc(l), T, s)) != hipSuccess) return e;
+        if (d.rope_neox && (e = launch_rope_neox(d, st, rope, q, m->kc(l), T, s, m->range_dev)) != hipSuccess)
+            return e;
         if (T == 1) {
             bool continue_ffn = false;
             AttnDecodeArgs a;
@@ -303,7 +309,8 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             if (e != hipSuccess) return e;
         }
         if (gemm) {
-            if ((e = launch_rms_split(x, T, d.H, w.ffn_norm, d.eps, u, kpart, pend, s, rs, eg_h)) != hipSuccess)
+            if ((e = launch_rms_split(x, T, d.H, w.ffn_norm, d.eps, u, kpart, pend, s, rs, eg_h, el_h,
+                                      m->lay.el_stride)) != hipSuccess)
                 return e;
             pend = 0;
             if ((e = launch_gemm_gateup(d, w, u, h_s, T, s, sc_h_out)) != hipSuccess) return e;
@@ -597,6 +604,7 @@ q8l_status q8l_forward(q8l_model *m, const uint32_t *tokens_host, int32_t n_toke
     if ((st = range_check(m)) != Q8L_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int T = n_tokens;
+    m->kv_checked = std::min(m->kv_checked, len);   // positions past len are dropped
     if (T == 1) {
         hipGraphExec_t g;
         if ((st = decode_graph(m, split_bucket(m, len + 1), &g)) != Q8L_OK) return st;
@@ -609,7 +617,13 @@ q8l_status q8l_forward(q8l_model *m, const uint32_t *tokens_host, int32_t n_toke
         Q8L_HIP(m, launch_embed(m->tok_embd, m->d.H, m->d.V, m->state(), m->at<uint32_t>(m->lay.tok), T, 0,
                                 m->at<float>(m->lay.x), s),
                 "embedding");
+        // the prefill's attention reads the cached positions as f16 pairs:
+        // check those a decode step wrote (its own q/k/v are checked as written)
+        Q8L_HIP(m, launch_kv_range(m->kc(0), m->vc(0), m->lay.kv_layer, m->cfg.n_layer, m->d.nkv, m->d.max_seq,
+                                   m->d.hd, m->kv_checked, len, m->range_dev, s),
+                "cache range check");
         Q8L_HIP(m, enqueue_layers(m, T, len + T, 0, s), "prefill");
+        m->kv_checked = len + T;
     }
     m->len = len + T;
     m->err.clear();
@@ -628,6 +642,7 @@ q8l_status q8l_generate(q8l_model *m, const uint32_t *token_dev, int32_t index_p
     if (int64_t(len) + n_steps > S) return fail(m, Q8L_E_KV_FULL, "cache would overflow");
     if (!m->finalized) return fail(m, Q8L_E_NOT_FINALIZED, "generate before finalize");
     if (q8l_status rc = range_check(m); rc != Q8L_OK) return rc;
+    m->kv_checked = std::min(m->kv_checked, len);
     hipStream_t s = static_cast<hipStream_t>(stream);
     std::vector<hipGraphExec_t> gs(n_steps);
     for (int k = 0; k < n_steps; ++k) {
@@ -736,6 +751,7 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
 q8l_status q8l_clear_kv_cache(q8l_model *m) {
     if (!m) return Q8L_E_INVALID_ARG;
     m->len = 0;
+    m->kv_checked = 0;
     return Q8L_OK;
 }
 

@@ -26,44 +26,71 @@ def _write(dirname, counter, rows):
                         "Counter_Name": counter, "Counter_Value": value})
 
 
-def _dispatches(values):
+def _dispatches(values, names):
     """One decode layer's dispatch sequence with the given counter values,
     between two 1 GiB copies (the reference dispatches)."""
-    ns = "void q8l::(anonymous namespace)::"
-    seq = [("__amd_rocclr_copyBuffer", values["copy"]),
-           (ns + "k_embed(unsigned char const*, int)", values["embed"]),
-           (ns + "k_qkv1<false>(q8l::(anonymous namespace)::QkvArgs)", values["qkv"]),
-           ("q8l::(anonymous namespace)::k_attn_decode(q8l::AttnDecodeArgs)", values["attn"]),
-           (ns + "k_matmul1<false, false>(q8l::(anonymous namespace)::MatmulArgs)", values["o"]),
-           (ns + "k_gateup1<false>(q8l::(anonymous namespace)::GateUpArgs)", values["gateup"]),
-           (ns + "k_matmul1<false, false>(q8l::(anonymous namespace)::MatmulArgs)", values["down"]),
-           (ns + "k_lmhead1<false>(q8l::(anonymous namespace)::LmHeadArgs)", values["lm"]),
-           ("__amd_rocclr_copyBuffer", values["copy"]),
-           ("__amd_rocclr_copyBuffer", values["copy"] / 2),  # a 512 MiB cache-flush copy: not a reference
-           ("__amd_rocclr_copyBuffer", 3.0)]  # a small upload copy: not a reference dispatch
+    seq = [("__amd_rocclr_copyBuffer", values["copy"])]
+    seq += [(names[k], values[k]) for k in ("embed", "qkv", "attn", "o", "gateup", "down", "lm") if k in names]
+    seq += [("__amd_rocclr_copyBuffer", values["copy"]),
+            ("__amd_rocclr_copyBuffer", values["copy"] / 2),  # a 512 MiB cache-flush copy: not a reference
+            ("__amd_rocclr_copyBuffer", 3.0)]  # a small upload copy: not a reference dispatch
     return seq
 
 
-def test_pmc_summary_scales_by_the_copy_and_tells_o_from_down(tmp_path):
-    fetch = {"copy": 524288.0, "embed": 2.0, "qkv": 400.0, "attn": 30.0, "o": 280.0, "gateup": 1000.0,
-             "down": 570.0, "lm": 15000.0}
-    write = {"copy": 1048576.0, "embed": 1.0, "qkv": 8.0, "attn": 2.0, "o": 4.0, "gateup": 12.0,
-             "down": 9.0, "lm": 270.0}
-    _write(str(tmp_path / "f"), "FETCH_SIZE", _dispatches(fetch))
-    _write(str(tmp_path / "w"), "WRITE_SIZE", _dispatches(write))
+NS = "void q8l::(anonymous namespace)::"
+FETCH = {"copy": 524288.0, "embed": 2.0, "qkv": 400.0, "attn": 30.0, "o": 280.0, "gateup": 1000.0,
+         "down": 570.0, "lm": 15000.0}
+WRITE = {"copy": 1048576.0, "embed": 1.0, "qkv": 8.0, "attn": 2.0, "o": 4.0, "gateup": 12.0,
+         "down": 9.0, "lm": 270.0}
+
+
+def _summary(tmp_path, names):
+    _write(str(tmp_path / "f"), "FETCH_SIZE", _dispatches(FETCH, names))
+    _write(str(tmp_path / "w"), "WRITE_SIZE", _dispatches(WRITE, names))
     buf = io.StringIO()
     with redirect_stdout(buf):
         bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), config="C2")
     out = buf.getvalue()
     assert "scale FETCH_SIZE 2.0000, WRITE_SIZE 1.0000" in out
-    lines = {l.split()[1].split("=")[1]: l for l in out.splitlines() if l.startswith("traffic:")}
+    return {l.split()[1].split("=")[1]: l for l in out.splitlines() if l.startswith("traffic:")}
+
+
+def test_pmc_summary_scales_by_the_copy(tmp_path):
+    """The 135M decode layer as it runs: wave-per-row q/k/v, gate/up and down,
+    the attention fused with the o-projection."""
+    names = {"embed": NS + "k_embed(unsigned char const*, int)",
+             "qkv": NS + "k_wqkv1<9>(q8l::(anonymous namespace)::WQkvArgs)",
+             "attn": "q8l::(anonymous namespace)::k_attn_o1(q8l::AttnODecodeArgs)",
+             "gateup": NS + "k_wgateup1<9>(q8l::(anonymous namespace)::WGateUpArgs)",
+             "down": NS + "k_wmatmul1<24>(q8l::(anonymous namespace)::WMatmulArgs)",
+             "lm": NS + "k_lmhead1<false>(q8l::(anonymous namespace)::LmHeadArgs)"}
+    lines = _summary(tmp_path, names)
     # bytes = (FETCH KiB * 2 + WRITE KiB * 1) * 1024
-    for kind, key in [("qkv_rope_kv", "qkv"), ("oproj_residual", "o"), ("gateup_silu", "gateup"),
+    for kind, key in [("qkv_rope_kv", "qkv"), ("attn_decode", "attn"), ("gateup_silu", "gateup"),
                       ("down_residual", "down"), ("lmhead", "lm")]:
-        want = int(round((fetch[key] * 2 + write[key]) * 1024))
+        want = int(round((FETCH[key] * 2 + WRITE[key]) * 1024))
         assert f"bytes_per_launch={want} " in lines[kind], (kind, lines[kind])
         src = bench.KIND_SOURCES[kind]
         assert f"sha256={bench.source_digest(src)}" in lines[kind]
+    assert "oproj_residual" not in lines
+
+
+def test_pmc_summary_tells_o_from_down(tmp_path, monkeypatch):
+    """Where the o and down projections run the same kernel, a dispatch
+    right after the attention is the o-projection."""
+    mm = "k_matmul1<false, false>"
+    monkeypatch.setattr(bench, "kernel_symbols", lambda s, down_fmt="q8_0", kv_len=1: [
+        "k_embed", "k_qkv1<false>", "k_attn_decode", mm, "k_gateup1<false>", mm, "k_lmhead1<false>",
+        "k_argmax_finish"])
+    names = {"qkv": NS + "k_qkv1<false>(q8l::(anonymous namespace)::QkvArgs)",
+             "attn": "q8l::(anonymous namespace)::k_attn_decode(q8l::AttnDecodeArgs)",
+             "o": NS + mm + "(q8l::(anonymous namespace)::MatmulArgs)",
+             "gateup": NS + "k_gateup1<false>(q8l::(anonymous namespace)::GateUpArgs)",
+             "down": NS + mm + "(q8l::(anonymous namespace)::MatmulArgs)"}
+    lines = _summary(tmp_path, names)
+    for kind, key in [("oproj_residual", "o"), ("down_residual", "down")]:
+        want = int(round((FETCH[key] * 2 + WRITE[key]) * 1024))
+        assert f"bytes_per_launch={want} " in lines[kind], (kind, lines[kind])
 
 
 def test_measured_traffic_follows_the_source_digest(tmp_path, monkeypatch):
