@@ -69,7 +69,7 @@ typedef enum {
  * 32-weight sub-block j. Q6_K block: 128 bytes of low 4 bits, 64 bytes of
  * high 2 bits, 16 int8 scales (one per 16 weights), f16 d;
  * weight = d*scale*(q - 32). */
-typedef enum { Q8L_F32 = 0, Q8L_Q8_0 = 1, Q8L_Q4_K = 2, Q8L_Q6_K = 3 } q8l_dtype;
+typedef enum { Q8L_F32 = 0, Q8L_Q8_0 = 1, Q8L_Q4_K = 2, Q8L_Q6_K = 3, Q8L_Q5_0 = 4 } q8l_dtype;
 
 /*
  * Model hyper-parameters: the llama.* metadata keys the page "生成一个 token"
@@ -127,12 +127,20 @@ q8l_status q8l_create(const q8l_config *cfg, q8l_model **out);
  *   output_norm.weight             F32  [1, n_embd]
  *   output.weight                  Q8_0 [n_vocab, n_embd]  (untied models only)
  * attn_output and ffn_down may instead be Q4_K or Q6_K when their cols are a
- * multiple of 256 (as files of the 4-bit mix store the down projection);
- * each layer's format is taken from its binding.
+ * multiple of 256 (as files of the 4-bit mix store the down projection), and
+ * every blk.{i} projection (attn_q, attn_k, attn_v, attn_output, ffn_gate,
+ * ffn_up, ffn_down) may be Q5_0
+ * (22-byte blocks: f16 d, a 32-bit little-endian word whose bit i is weight
+ * i's fifth bit, 16 bytes whose low nibbles are weights 0..15 and high
+ * nibbles 16..31; weight = d * ((nibble | bit << 4) - 16)) -- the 4-bit mix
+ * stores most of the 135M model's projections so ("速度", section "CPU
+ * GGUF"). Each matrix's format is taken from its binding; ffn_gate and
+ * ffn_up of a layer must share one (Q8L_E_SHAPE from q8l_finalize otherwise).
  * `dev_ptr` holds the raw bytes (blocks exactly as in the file, rows back to
  * back; F32 little-endian), 16-byte aligned, borrowed. Q8L_E_SHAPE when the
- * dtype, rows, cols or nbytes (rows*cols/32*34 for Q8_0, rows*cols/256*144
- * for Q4_K, rows*cols/256*210 for Q6_K, rows*cols*4 for F32) do not match;
+ * dtype, rows, cols or nbytes (rows*cols/32*34 for Q8_0, rows*cols/32*22 for
+ * Q5_0, rows*cols/256*144 for Q4_K, rows*cols/256*210 for Q6_K, rows*cols*4
+ * for F32) do not match;
  * Q8L_E_INVALID_ARG for an unknown name, NULL or misaligned pointer;
  * Q8L_E_NOT_FINALIZED after finalize (weights are fixed once finalized).
  * Binding a name twice replaces the earlier pointer.
@@ -242,6 +250,22 @@ void q8l_destroy(q8l_model *m);
 q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *X, int64_t T,
                               const float *norm_w, double eps, int32_t accumulate, float *Y,
                               void *stream);
+
+/*
+ * The same product for a Q5_0 matrix (22-byte blocks as described at
+ * q8l_bind; the 4-bit mix of the 135M model stores its 576-wide projections
+ * so, "速度", section "CPU GGUF"):
+ *   Y[t][n] (+)= sum_k W[n][k] * X[t][k].
+ * W: N rows of K/32 blocks back to back (16-byte aligned), X f32 [T][K]
+ * (16-byte aligned), Y f32 [T][N]; accumulate 1 adds to Y. K must be a
+ * multiple of 64; 1 <= T <= 2^20. T <= 16 runs the matrix-vector kernels in
+ * f32; larger T the MFMA matrix-matrix kernel on X split into f16 pairs
+ * (exact to about 2^-22 relative while every |X| < 2^15, as for
+ * q8l_op_matmul_q8_0). Q8L_E_INVALID_ARG for a NULL or misaligned pointer,
+ * sizes out of range, or a matrix or activation block of 2 GiB or more.
+ */
+q8l_status q8l_op_matmul_q5_0(const void *W, int64_t N, int64_t K, const float *X, int64_t T,
+                              int32_t accumulate, float *Y, void *stream);
 
 /*
  * The same product for a Q4_K or Q6_K matrix (dtype Q8L_Q4_K / Q8L_Q6_K; the
@@ -395,12 +419,14 @@ int64_t q8l_gguf_find_tensor(const q8l_gguf *g, const char *name);
 /* Tensor `index`: name (valid while the handle is open), dtype (a q8l_dtype, or
  * -1 with Q8L_E_FORMAT for other types), rows x cols (cols = the innermost
  * dimension), absolute file offset and byte size as read. Any output may be
- * NULL. Q4_0 and Q5_0 tensors (32-weight blocks of an f16 scale times 4- or
- * 5-bit integers; sizes pinned by "速度", section "CPU GGUF") are read as Q8_0:
- * dtype Q8L_Q8_0, size rows*cols/32*34, each block converted exactly (same
- * scale, int8 = the block's integer). Q4_K and Q6_K tensors are read as they
- * are (dtype Q8L_Q4_K / Q8L_Q6_K). Other block formats are listed but not
- * read (dtype -1). */
+ * NULL. Q5_0 tensors of the seven blk.{i} projections are read as they are
+ * (dtype Q8L_Q5_0, 22 bytes per 32 weights). Q4_0 tensors, and Q5_0 tensors
+ * of the other roles (token_embd, output), are read as Q8_0
+ * (32-weight blocks of an f16 scale times 4- or 5-bit integers; sizes pinned
+ * by "速度", section "CPU GGUF"): dtype Q8L_Q8_0, size rows*cols/32*34, each
+ * block converted exactly (same scale, int8 = the block's integer). Q4_K and
+ * Q6_K tensors are read as they are (dtype Q8L_Q4_K / Q8L_Q6_K). Other block
+ * formats are listed but not read (dtype -1). */
 q8l_status q8l_gguf_tensor_info(const q8l_gguf *g, int64_t index, const char **name, int32_t *dtype,
                                 int64_t *rows, int64_t *cols, uint64_t *offset, uint64_t *nbytes);
 /* Read tensor `index`'s bytes into host memory; nbytes must equal its size as read. */

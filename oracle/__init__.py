@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.orc_create.restype = P
         L.orc_create_fmt.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_void_p), P, P]
         L.orc_create_fmt.restype = P
+        L.orc_create_fmt7.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_void_p), P]
+        L.orc_create_fmt7.restype = P
         L.orc_destroy.argtypes = [P]; L.orc_destroy.restype = None
         L.orc_clear_kv_cache.argtypes = [P]; L.orc_clear_kv_cache.restype = None
         L.orc_cache_len.argtypes = [P]; L.orc_cache_len.restype = I32
@@ -130,9 +132,10 @@ def dequant_q5_0(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
 
 
 # Block formats of the 256-weight "K" family (bytes per 256 weights) and the
-# oracle's format codes for matrices that may hold them.
+# oracle's format codes for the matrices' block formats.
 K_BLOCK_BYTES = {"q4_k": 144, "q6_k": 210}
-FMT_CODES = {"q8_0": 0, "q4_k": 1, "q6_k": 2}
+FMT_CODES = {"q8_0": 0, "q4_k": 1, "q6_k": 2, "q5_0": 3}
+LAYER_MATRICES = ("attn_q", "attn_k", "attn_v", "attn_output", "ffn_gate", "ffn_up", "ffn_down")
 
 
 def dequant_q4_k(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
@@ -154,7 +157,7 @@ def dequant_q6_k(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
 
 
 def matmul_fmt(raw: np.ndarray, fmt: str, rows: int, cols: int, x: np.ndarray) -> np.ndarray:
-    """Y[t] = W @ X[t] for W [rows, cols] in block format ``fmt`` ('q8_0', 'q4_k', 'q6_k')."""
+    """Y[t] = W @ X[t] for W [rows, cols] in block format ``fmt`` ('q8_0', 'q5_0', 'q4_k', 'q6_k')."""
     raw = np.ascontiguousarray(raw, dtype=np.uint8)
     X = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float64)
     Y = np.empty((X.shape[0], rows), dtype=np.float64)
@@ -229,12 +232,10 @@ class OracleModel:
         self._arrays = [np.ascontiguousarray(t.data) for t in model.tensors]
         ptrs = (ctypes.c_void_p * len(self._arrays))(*[a.ctypes.data for a in self._arrays])
         self._ptrs = ptrs
-        fo = np.array([FMT_CODES[model[f"blk.{l}.attn_output.weight"].dtype] for l in range(s.n_layer)],
-                      dtype=np.int32)
-        fd = np.array([FMT_CODES[model[f"blk.{l}.ffn_down.weight"].dtype] for l in range(s.n_layer)],
-                      dtype=np.int32)
-        self._fmts = (fo, fd)
-        h = lib().orc_create_fmt(ctypes.byref(self.cfg), ptrs, _ptr(fo), _ptr(fd))
+        fmts = np.array([[FMT_CODES[model[f"blk.{l}.{r}.weight"].dtype] for r in LAYER_MATRICES]
+                         for l in range(s.n_layer)], dtype=np.int32)
+        self._fmts = fmts
+        h = lib().orc_create_fmt7(ctypes.byref(self.cfg), ptrs, _ptr(fmts))
         if not h:
             raise ValueError("oracle rejected the model configuration")
         self._h = h

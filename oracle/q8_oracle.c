@@ -60,15 +60,17 @@ typedef struct {
     int32_t rope_neox;    /* 0: pairs (2j, 2j+1) (llama); 1: pairs (j, j + hd/2) */
 } orc_config;
 
-/* Block formats of the o and down projections (the others are Q8_0). */
+/* Block formats of a layer's projections: Q8_0 or Q5_0 for any of them,
+ * Q4_K and Q6_K for the o and down projections. */
 #define ORC_FMT_Q8_0 0
 #define ORC_FMT_Q4_K 1
 #define ORC_FMT_Q6_K 2
+#define ORC_FMT_Q5_0 3
 
 typedef struct {
     const float *attn_norm, *ffn_norm;
     const uint8_t *wq, *wk, *wv, *wo, *wg, *wu, *wd;
-    int32_t fo, fd;   /* formats of wo and wd */
+    int32_t fq, fk, fv, fo, fg, fu, fd;   /* formats of the seven matrices */
 } orc_layer;
 
 typedef struct {
@@ -197,12 +199,14 @@ void orc_dequant_row(const uint8_t *row, int64_t K, double *out) {
 static int64_t row_bytes(int64_t K) { return K / ORC_QK * ORC_QBYTES; }
 
 static int64_t fmt_row_bytes(int32_t fmt, int64_t K) {
-    return fmt == ORC_FMT_Q4_K ? K / 256 * 144 : fmt == ORC_FMT_Q6_K ? K / 256 * 210 : row_bytes(K);
+    return fmt == ORC_FMT_Q4_K ? K / 256 * 144 : fmt == ORC_FMT_Q6_K ? K / 256 * 210
+         : fmt == ORC_FMT_Q5_0 ? K / 32 * 22 : row_bytes(K);
 }
 
 static void dequant_fmt(int32_t fmt, const uint8_t *row, int64_t K, double *out) {
     if (fmt == ORC_FMT_Q4_K) orc_dequant_q4_k_row(row, K, out);
     else if (fmt == ORC_FMT_Q6_K) orc_dequant_q6_k_row(row, K, out);
+    else if (fmt == ORC_FMT_Q5_0) orc_dequant_q5_0_row(row, K, out);
     else orc_dequant_row(row, K, out);
 }
 
@@ -332,24 +336,40 @@ static int cfg_ok(const orc_config *c) {
  * attn_q, attn_k, attn_v, attn_output, ffn_norm, ffn_gate, ffn_up, ffn_down;
  * output_norm; output (only when not tied). The model borrows them.
  */
-orc_model *orc_create_fmt(const orc_config *c, const void *const *tensors, const int32_t *wo_fmt,
-                          const int32_t *wd_fmt);
+orc_model *orc_create_fmt7(const orc_config *c, const void *const *tensors, const int32_t *fmts);
 
 orc_model *orc_create(const orc_config *c, const void *const *tensors) {
-    return orc_create_fmt(c, tensors, NULL, NULL);
+    return orc_create_fmt7(c, tensors, NULL);
 }
 
 /* As orc_create, with per-layer block formats of attn_output and ffn_down
- * (ORC_FMT_*; NULL = Q8_0 everywhere). */
+ * (ORC_FMT_*; NULL = Q8_0 everywhere; the other matrices Q8_0). */
 orc_model *orc_create_fmt(const orc_config *c, const void *const *tensors, const int32_t *wo_fmt,
                           const int32_t *wd_fmt) {
-    if (!c || !tensors || !cfg_ok(c)) return NULL;
-    for (int l = 0; l < c->n_layer; ++l) {  /* 256-weight blocks need whole blocks per row */
-        const int32_t fo = wo_fmt ? wo_fmt[l] : ORC_FMT_Q8_0, fd = wd_fmt ? wd_fmt[l] : ORC_FMT_Q8_0;
-        if (fo < 0 || fo > 2 || fd < 0 || fd > 2) return NULL;
-        if (fo != ORC_FMT_Q8_0 && ((int64_t)c->n_head * c->head_dim) % 256) return NULL;
-        if (fd != ORC_FMT_Q8_0 && c->n_ff % 256) return NULL;
+    if (!c || c->n_layer < 1) return NULL;
+    int32_t *f = (int32_t *)calloc((size_t)c->n_layer * 7, sizeof(int32_t));
+    for (int l = 0; l < c->n_layer; ++l) {
+        f[7 * l + 3] = wo_fmt ? wo_fmt[l] : ORC_FMT_Q8_0;
+        f[7 * l + 6] = wd_fmt ? wd_fmt[l] : ORC_FMT_Q8_0;
     }
+    orc_model *m = orc_create_fmt7(c, tensors, f);
+    free(f);
+    return m;
+}
+
+/* As orc_create, with the block format of every matrix: fmts[7*l + i] for
+ * layer l and i = q, k, v, o, gate, up, down (ORC_FMT_*; NULL = Q8_0
+ * everywhere). Q4_K / Q6_K only for o and down, with whole 256-weight blocks
+ * per row. */
+orc_model *orc_create_fmt7(const orc_config *c, const void *const *tensors, const int32_t *fmts) {
+    if (!c || !tensors || !cfg_ok(c)) return NULL;
+    for (int l = 0; l < c->n_layer && fmts; ++l)
+        for (int i = 0; i < 7; ++i) {
+            const int32_t f = fmts[7 * l + i];
+            const int64_t K = i == 3 ? (int64_t)c->n_head * c->head_dim : i == 6 ? c->n_ff : c->n_embd;
+            if (f < 0 || f > 3) return NULL;
+            if ((f == ORC_FMT_Q4_K || f == ORC_FMT_Q6_K) && ((i != 3 && i != 6) || K % 256)) return NULL;
+        }
     orc_model *m = (orc_model *)calloc(1, sizeof(orc_model));
     m->c = *c;
     int64_t i = 0;
@@ -366,8 +386,14 @@ orc_model *orc_create_fmt(const orc_config *c, const void *const *tensors, const
         L->wg = (const uint8_t *)tensors[i++];
         L->wu = (const uint8_t *)tensors[i++];
         L->wd = (const uint8_t *)tensors[i++];
-        L->fo = wo_fmt ? wo_fmt[l] : ORC_FMT_Q8_0;
-        L->fd = wd_fmt ? wd_fmt[l] : ORC_FMT_Q8_0;
+        const int32_t *f = fmts ? fmts + 7 * l : NULL;
+        L->fq = f ? f[0] : ORC_FMT_Q8_0;
+        L->fk = f ? f[1] : ORC_FMT_Q8_0;
+        L->fv = f ? f[2] : ORC_FMT_Q8_0;
+        L->fo = f ? f[3] : ORC_FMT_Q8_0;
+        L->fg = f ? f[4] : ORC_FMT_Q8_0;
+        L->fu = f ? f[5] : ORC_FMT_Q8_0;
+        L->fd = f ? f[6] : ORC_FMT_Q8_0;
     }
     m->out_norm = (const float *)tensors[i++];
     m->out = c->tied_output ? m->tok_embd : (const uint8_t *)tensors[i++];
@@ -446,9 +472,9 @@ int orc_forward(orc_model *m, const uint32_t *tokens, int32_t T, int32_t index_p
         /* attention block */
         for (int32_t i = 0; i < T; ++i) orc_rmsnorm(x + i * H, L->attn_norm, H, c->rms_eps, u + i * H);
         m->n_rmsnorm++;
-        orc_matmul_q8(L->wq, QD, H, u, T, q);
-        orc_matmul_q8(L->wk, KVD, H, u, T, k);
-        orc_matmul_q8(L->wv, KVD, H, u, T, v);
+        orc_matmul_fmt(L->wq, L->fq, QD, H, u, T, q);
+        orc_matmul_fmt(L->wk, L->fk, KVD, H, u, T, k);
+        orc_matmul_fmt(L->wv, L->fv, KVD, H, u, T, v);
         m->n_matmul += 3;
         for (int32_t i = 0; i < T; ++i) {
             void (*rope)(double *, int64_t, int64_t, double) = c->rope_neox ? orc_rope_neox : orc_rope_i;
@@ -477,8 +503,8 @@ int orc_forward(orc_model *m, const uint32_t *tokens, int32_t T, int32_t index_p
         /* MLP block */
         for (int32_t i = 0; i < T; ++i) orc_rmsnorm(x + i * H, L->ffn_norm, H, c->rms_eps, u + i * H);
         m->n_rmsnorm++;
-        orc_matmul_q8(L->wg, F, H, u, T, g);
-        orc_matmul_q8(L->wu, F, H, u, T, up);
+        orc_matmul_fmt(L->wg, L->fg, F, H, u, T, g);
+        orc_matmul_fmt(L->wu, L->fu, F, H, u, T, up);
         for (int64_t e = 0; e < T * F; ++e) g[e] = orc_silu(g[e]) * up[e];
         orc_matmul_fmt(L->wd, L->fd, H, F, g, T, y);
         m->n_matmul += 3;

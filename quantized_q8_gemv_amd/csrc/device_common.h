@@ -82,6 +82,49 @@ __device__ __forceinline__ void pair_dot1(const uint32_t *w, const float *x, flo
     sB = (s0 + s1) + (s2 + s3);
 }
 
+// Q5_0 (22-byte blocks: f16 d, a 32-bit word of fifth bits, 16 bytes of
+// nibbles; weight i < 16 is the low nibble of byte i, weight i + 16 its high
+// nibble, bit i of the word is weight i's fifth bit, q = 5-bit value - 16).
+// The 5-bit values of weights 4j .. 4j + 3 (hi = false) or 16 + 4j .. 16 +
+// 4j + 3 (hi = true) as four bytes: the nibbles of dword j of the block's 16
+// value bytes with their fifth bits placed at bit 4 of each byte (the four
+// bits times 0x204081 land at bits 0, 8, 16 and 24).
+__device__ __forceinline__ uint32_t q5_bytes(uint32_t qs, uint32_t qh, int j, bool hi) {
+    const uint32_t nib = (hi ? qs >> 4 : qs) & 0x0f0f0f0fu;
+    const uint32_t b = (qh >> (4 * j + (hi ? 16 : 0))) & 0xfu;
+    return nib | (((b * 0x204081u) & 0x01010101u) << 4);
+}
+
+__device__ __forceinline__ float ubyte_f(uint32_t v, int b) { return static_cast<float>((v >> (8 * b)) & 0xffu); }
+
+// One pair of Q5_0 blocks (44 bytes = 11 dwords at a 4-byte aligned
+// address): block A = bytes [0, 22) (its fifth-bit word and values start 2
+// bytes into a dword and are re-aligned with alignbyte), block B = bytes
+// [22, 44) (d in the high half of dword 5, the word and values dword-aligned).
+// Decoded into the Q8_0 pair form (d and the 64 integers as floats).
+__device__ __forceinline__ void decode_pair_q5(const uint32_t *w, PairQ &o) {
+    uint32_t r[11];
+#pragma unroll
+    for (int i = 0; i < 11; ++i) r[i] = w[i];
+    o.dA = half_bits_to_float(r[0]);
+    o.dB = half_bits_to_float(r[5] >> 16);
+    const uint32_t qhA = __builtin_amdgcn_alignbyte(r[1], r[0], 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t qa = __builtin_amdgcn_alignbyte(r[j + 2], r[j + 1], 2);
+        const uint32_t qb = r[7 + j];
+        const uint32_t la = q5_bytes(qa, qhA, j, false), ha = q5_bytes(qa, qhA, j, true);
+        const uint32_t lb = q5_bytes(qb, r[6], j, false), hb = q5_bytes(qb, r[6], j, true);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o.q[4 * j + e] = ubyte_f(la, e) - 16.0f;
+            o.q[16 + 4 * j + e] = ubyte_f(ha, e) - 16.0f;
+            o.q[32 + 4 * j + e] = ubyte_f(lb, e) - 16.0f;
+            o.q[48 + 4 * j + e] = ubyte_f(hb, e) - 16.0f;
+        }
+    }
+}
+
 // d * sum_i q[i] x[i] over one 32-weight block, in a fixed order: four
 // interleaved partial sums, then (s0 + s1) + (s2 + s3).
 __device__ __forceinline__ float block_dot(const float *q, const float *x) {
@@ -95,6 +138,17 @@ __device__ __forceinline__ float block_dot(const float *q, const float *x) {
         s3 = fmaf(q[i + 3], xv.w, s3);
     }
     return (s0 + s1) + (s2 + s3);
+}
+
+// pair_dot1 for a Q5_0 pair: decode the pair, then block_dot per block.
+__device__ __forceinline__ void pair_dot1_q5(const uint32_t *w, const float *x, float &dA, float &sA, float &dB,
+                                             float &sB) {
+    PairQ pq;
+    decode_pair_q5(w, pq);
+    dA = pq.dA;
+    dB = pq.dB;
+    sA = block_dot(pq.q, x);
+    sB = block_dot(pq.q + 32, x + 32);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -70,12 +70,28 @@ struct TensorInfo {
     uint64_t offset = 0;      // within the data region
     uint64_t file_bytes = 0;  // bytes in the file
     uint64_t nbytes = 0;      // bytes as read (Q8_0 for the 32-weight integer formats), 0 if unreadable
+    bool native = false;      // Q5_0 read as it is (see q5_native_role)
 };
 
 bool q8_family(uint32_t t) { return t == kTypeQ4_0 || t == kTypeQ5_0 || t == kTypeQ8_0; }
 bool k_family(uint32_t t) { return t == kTypeQ4_K || t == kTypeQ6_K; }
 
 uint64_t block_bytes(uint32_t t) { return t == kTypeQ4_0 ? 18 : t == kTypeQ5_0 ? 22 : 34; }
+
+// Q5_0 tensors that the model binds in their own format: the seven
+// projections of a layer ("blk.<n>.<role>.weight"). Others (the embedding,
+// the output matrix) are read as Q8_0.
+bool q5_native_role(const std::string &name) {
+    if (name.compare(0, 4, "blk.") != 0) return false;
+    size_t p = 4;
+    while (p < name.size() && name[p] >= '0' && name[p] <= '9') ++p;
+    if (p == 4 || p >= name.size() || name[p] != '.') return false;
+    const std::string role = name.substr(p + 1);
+    for (const char *r : {"attn_q.weight", "attn_k.weight", "attn_v.weight", "attn_output.weight",
+                          "ffn_gate.weight", "ffn_up.weight", "ffn_down.weight"})
+        if (role == r) return true;
+    return false;
+}
 
 // One Q4_0 / Q5_0 block (file layout: public GGUF block definitions) as a
 // Q8_0 block: the f16 scale is copied, weight i of the block becomes the int8
@@ -274,7 +290,8 @@ q8l_status parse(q8l_gguf *g) {
         } else if (q8_family(t.type)) {
             if (t.dims[0] % 32) return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " rows are not whole blocks");
             t.file_bytes = n / 32 * block_bytes(t.type);
-            t.nbytes = n / 32 * 34;
+            t.native = t.type == kTypeQ5_0 && q5_native_role(t.name);
+            t.nbytes = t.native ? t.file_bytes : n / 32 * 34;
         } else if (k_family(t.type)) {
             if (t.dims[0] % 256) return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " rows are not whole blocks");
             t.file_bytes = t.nbytes = n / 256 * (t.type == kTypeQ4_K ? 144 : 210);
@@ -436,6 +453,7 @@ q8l_status q8l_gguf_tensor_info(const q8l_gguf *g, int64_t index, const char **n
     if (nbytes) *nbytes = t.nbytes;
     if (dtype) {
         if (t.type == kTypeF32) *dtype = Q8L_F32;
+        else if (t.native) *dtype = Q8L_Q5_0;
         else if (q8_family(t.type)) *dtype = Q8L_Q8_0;
         else if (t.type == kTypeQ4_K) *dtype = Q8L_Q4_K;
         else if (t.type == kTypeQ6_K) *dtype = Q8L_Q6_K;
@@ -462,7 +480,7 @@ q8l_status q8l_gguf_read_tensor(q8l_gguf *g, int64_t index, void *host_dst, size
     if (nbytes != t.nbytes) return fail(g, Q8L_E_SHAPE, "tensor " + t.name + ": buffer size differs");
     const uint64_t off = g->data_offset + t.offset;
     if (fseeko(g->f, off_t(off), SEEK_SET) != 0) return fail(g, Q8L_E_IO, "seek failed for " + t.name);
-    if (t.type == kTypeF32 || t.type == kTypeQ8_0 || k_family(t.type)) {
+    if (t.type == kTypeF32 || t.type == kTypeQ8_0 || k_family(t.type) || t.native) {
         if (std::fread(host_dst, 1, nbytes, g->f) != nbytes) return fail(g, Q8L_E_IO, "short read for " + t.name);
         return Q8L_OK;
     }

@@ -675,6 +675,7 @@ hipError_t launch_attn_o(const AttnDecodeArgs &a, const uint8_t *wo, int N, floa
     AttnODecodeArgs b;
     b.at = a;
     b.wo = wo; b.N = N; b.part = part;
+
     b.rows = attn_o_rows(d);
     const int chunks = (N + b.rows - 1) / b.rows;
     hipLaunchKernelGGL(k_attn_o1, dim3(chunks * a.nkv), dim3(kThreads), attn_o_lds(a.nh / a.nkv, a.hd, b.rows), s, b);

@@ -97,17 +97,34 @@ __device__ inline GBuf gbuf(uint8_t *smem, int k) {
     return b;
 }
 
+// Dwords a thread loads per B quarter row and step: a Q8_0 quarter is 16
+// values and a scale or a dword of slack (5), a Q5_0 quarter reads its whole
+// 22-byte block from the dword-aligned floor (6).
+template <int FMT>
+constexpr int quarter_dwords() { return FMT == F_Q5_0 ? 6 : 5; }
+
+template <int FMT>
+constexpr int pair_bytes() { return FMT == F_Q5_0 ? kQ5PairBytes : kPairBytes; }
+
 // Registers holding one K step of global data in flight.
-template <int TM, int TN>
+template <int TM, int TN, int FMT>
 struct GRegs {
     u32x4 a[Cfg<TM, TN>::AP];
-    uint32_t b[Cfg<TM, TN>::BU][5];
+    uint32_t b[Cfg<TM, TN>::BU][quarter_dwords<FMT>()];
 };
 
-// Quarter qd of a 68-byte block pair (dwords): 0 -> d0 + q0..15 of block 0
-// (dwords 0..4), 1 -> q16..31 + d1 (4..8), 2 -> q0..15 of block 1 (9..13, the
-// last unused), 3 -> q16..31 of block 1 (12..16, the first unused).
-__device__ inline int quarter_base(int qd) { return qd == 0 ? 0 : qd == 1 ? 4 : qd == 2 ? 9 : 12; }
+// First dword of quarter qd (block qd / 2, values 16 (qd % 2) .. +15) of a
+// block pair. Q8_0, 68 bytes: 0 -> d0 + q0..15 of block 0 (dwords 0..4), 1 ->
+// q16..31 + d1 (4..8), 2 -> q0..15 of block 1 (9..13, the last unused), 3 ->
+// q16..31 of block 1 (12..16, the first unused). Q5_0, 44 bytes: block 0 is
+// bytes 0..21 (dwords 0..5), block 1 bytes 22..43 (dwords 5..10); both
+// quarters of a block read the whole block (the fifth bits and the nibbles
+// of values j and j + 16 share bytes).
+template <int FMT>
+__device__ inline int quarter_base(int qd) {
+    if (FMT == F_Q5_0) return qd < 2 ? 0 : 5;
+    return qd == 0 ? 0 : qd == 1 ? 4 : qd == 2 ? 9 : 12;
+}
 
 // Buffer-load sources of a thread: one resource per operand and a fixed byte
 // offset per piece; a K step adds a uniform offset. Rows past the end of A or
@@ -147,7 +164,7 @@ __device__ inline void a_setup(const GemmArgs &a, int m0, __amdgpu_buffer_rsrc_t
     }
 }
 
-template <bool A32, int TM, int TN, int EPI>
+template <bool A32, int TM, int TN, int EPI, int FMT>
 __device__ inline void g_setup(const GemmArgs &a, int m0, int row0, const int nvalid[2],
                                const uint8_t *const Wb[2], GSrc<TM, TN> &g) {
     using C = Cfg<TM, TN>;
@@ -164,7 +181,7 @@ __device__ inline void g_setup(const GemmArgs &a, int m0, int row0, const int nv
         g.rb[i] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(W), 0,
                                                     int(uint32_t(row0 + nvalid[part]) * uint32_t(a.rowbytes)),
                                                     kRsrcWord3);
-        g.boff[i] = rr < nvalid[part] ? uint32_t(row0 + rr) * uint32_t(a.rowbytes) + quarter_base(qd) * 4
+        g.boff[i] = rr < nvalid[part] ? uint32_t(row0 + rr) * uint32_t(a.rowbytes) + quarter_base<FMT>(qd) * 4
                                       : kOutOfRange;
     }
 }
@@ -177,11 +194,11 @@ __device__ inline void a_load(__amdgpu_buffer_rsrc_t ra, const uint32_t *aoff, i
     for (int i = 0; i < C::AP; ++i) ra_out[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i], sa, 0);
 }
 
-template <bool A32, int TM, int TN>
-__device__ inline void g_load(const GSrc<TM, TN> &g, int ks, GRegs<TM, TN> &r) {
+template <bool A32, int TM, int TN, int FMT>
+__device__ inline void g_load(const GSrc<TM, TN> &g, int ks, GRegs<TM, TN, FMT> &r) {
     using C = Cfg<TM, TN>;
     a_load<A32, TM, TN>(g.ra, g.aoff, ks, r.a);
-    const int sb = ks * kPairBytes;
+    const int sb = ks * pair_bytes<FMT>();
 #pragma unroll
     for (int i = 0; i < C::BU; ++i) {
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(g.rb[i], g.boff[i], sb, 0);
@@ -189,18 +206,25 @@ __device__ inline void g_load(const GSrc<TM, TN> &g, int ks, GRegs<TM, TN> &r) {
         r.b[i][1] = v.y;
         r.b[i][2] = v.z;
         r.b[i][3] = v.w;
-        r.b[i][4] = __builtin_amdgcn_raw_buffer_load_b32(g.rb[i], g.boff[i] + 16, sb, 0);
+        if constexpr (FMT == F_Q5_0) {
+            const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(g.rb[i], g.boff[i] + 16, sb, 0));
+            r.b[i][4] = t.x;
+            r.b[i][5] = t.y;
+        } else {
+            r.b[i][4] = __builtin_amdgcn_raw_buffer_load_b32(g.rb[i], g.boff[i] + 16, sb, 0);
+        }
     }
 }
 
-// int8 x 4 (one dword) -> 4 exact f16 values: bias each byte to an unsigned
-// value u = q + 128, place it in the mantissa of 1024.0 (f16 bits 0x6400 | u)
-// and subtract 1152 = 1024 + 128.
-__device__ inline void q4_to_half(uint32_t w, half2v &lo, half2v &hi) {
-    const uint32_t x = w ^ 0x80808080u;
+// Four unsigned bytes u (one dword) -> 4 exact f16 values u - zero: place
+// each byte in the mantissa of 1024.0 (f16 bits 0x6400 | u) and subtract
+// 1024 + zero. Q8_0 passes its int8 values biased to q + 128 (zero 128), Q5_0
+// its 5-bit codes (zero 16).
+template <int ZERO>
+__device__ inline void u4_to_half(uint32_t x, half2v &lo, half2v &hi) {
     const uint32_t l = __builtin_amdgcn_perm(0x64646464u, x, 0x05010400u);
     const uint32_t h = __builtin_amdgcn_perm(0x64646464u, x, 0x07030602u);
-    const half2v bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+    const half2v bias = {static_cast<_Float16>(1024.0f + ZERO), static_cast<_Float16>(1024.0f + ZERO)};
     lo = __builtin_bit_cast(half2v, l) - bias;
     hi = __builtin_bit_cast(half2v, h) - bias;
 }
@@ -284,8 +308,9 @@ struct RowFactors {
     }
 };
 
-template <bool A32, int TM, int TN>
-__device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf, const GemmArgs &a, int m0, int ks, bool resc) {
+template <bool A32, int TM, int TN, int FMT>
+__device__ inline void g_store(const GRegs<TM, TN, FMT> &r, const GBuf &bf, const GemmArgs &a, int m0, int ks,
+                               bool resc) {
     using C = Cfg<TM, TN>;
     const int tid = threadIdx.x;
     a_store<A32, TM, TN>(r.a, bf.ahi, bf.alo, a, m0, ks, resc);
@@ -294,12 +319,26 @@ __device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf, const Gem
         const int u = tid + i * kThreads;
         const int b = u >> 2, qd = u & 3;
         const uint32_t *w = r.b[i];
-        const uint32_t shift = qd < 2 ? 2u : 0u;
         half2v v[8];
+        if constexpr (FMT == F_Q5_0) {
+            // block 0 (qd 0, 1): d in bytes 0..1, the fifth-bit word and the
+            // nibbles 2 bytes into a dword; block 1 (qd 2, 3): d in bytes 2..3,
+            // word and nibbles dword-aligned. Quarter qd & 1 takes the high
+            // nibbles and bits 16..31 of the word.
+            const bool blk1 = qd >= 2, hi = qd & 1;
+            const uint32_t qh = blk1 ? w[1] : __builtin_amdgcn_alignbyte(w[1], w[0], 2);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t q4 = qd == 3 ? w[k + 1] : __builtin_amdgcn_alignbyte(w[k + 1], w[k], shift);
-            q4_to_half(q4, v[2 * k], v[2 * k + 1]);
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t qs = blk1 ? w[k + 2] : __builtin_amdgcn_alignbyte(w[k + 2], w[k + 1], 2);
+                u4_to_half<16>(q5_bytes(qs, qh, k, hi), v[2 * k], v[2 * k + 1]);
+            }
+        } else {
+            const uint32_t shift = qd < 2 ? 2u : 0u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t q4 = qd == 3 ? w[k + 1] : __builtin_amdgcn_alignbyte(w[k + 1], w[k], shift);
+                u4_to_half<128>(q4 ^ 0x80808080u, v[2 * k], v[2 * k + 1]);
+            }
         }
         const u32x4 s0 = u32x4{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
                                __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
@@ -308,12 +347,19 @@ __device__ inline void g_store(const GRegs<TM, TN> &r, const GBuf &bf, const Gem
         _Float16 *dst = bf.bq + b * LPAD + (qd >> 1) * 32 + (qd & 1) * 16;
         *reinterpret_cast<u32x4 *>(dst) = s0;
         *reinterpret_cast<u32x4 *>(dst + 8) = s1;
-        if (qd == 0) bf.bd[b * 2 + 0] = half_bits_to_float(w[0] & 0xffffu);
-        if (qd == 1) bf.bd[b * 2 + 1] = half_bits_to_float(w[4] >> 16);
+        if (FMT == F_Q5_0) {
+            if (qd == 0) bf.bd[b * 2 + 0] = half_bits_to_float(w[0] & 0xffffu);
+            if (qd == 2) bf.bd[b * 2 + 1] = half_bits_to_float(w[0] >> 16);
+        } else {
+            if (qd == 0) bf.bd[b * 2 + 0] = half_bits_to_float(w[0] & 0xffffu);
+            if (qd == 1) bf.bd[b * 2 + 1] = half_bits_to_float(w[4] >> 16);
+        }
     }
 }
 
-template <int EPI, int TM, int TN, bool A32, int ST>
+// FMT: the weights' block format, Q8_0 or Q5_0 (a pair of 64 weights per K
+// step either way; only the B tile's load and decode differ).
+template <int FMT, int EPI, int TM, int TN, bool A32, int ST>
 __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
     using C = Cfg<TM, TN>;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -357,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
         nsteps = (int(blockIdx.z) + 1) * all / a.splits - kfirst;
     }
     GSrc<TM, TN> src;
-    g_setup<A32, TM, TN, EPI>(a, m0, row0, nvalid, Wb, src);
+    g_setup<A32, TM, TN, EPI, FMT>(a, m0, row0, nvalid, Wb, src);
     // only products of the gate/up output (o-type epilogues) see per-block
     // exponents; q/k/v and gate/up read the normalised rows (row factors only)
     constexpr bool kResc = !A32 && EPI != G_QKV && EPI != G_GATEUP;
@@ -368,21 +414,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
     // re-read the last step, whose registers are never stored): with no
     // branch around them the compiler can wait for the oldest stage alone
     // instead of draining every load in flight.
-    GRegs<TM, TN> regs[S];
+    GRegs<TM, TN, FMT> regs[S];
 #pragma unroll
-    for (int j = 0; j < S; ++j) g_load<A32, TM, TN>(src, kfirst + min(j, nsteps - 1), regs[j]);
+    for (int j = 0; j < S; ++j) g_load<A32, TM, TN, FMT>(src, kfirst + min(j, nsteps - 1), regs[j]);
     for (int k0 = 0; k0 < nsteps; k0 += S) {
 #pragma unroll
         for (int j = 0; j < S; ++j) {
             const int ks = k0 + j;
             if (ks >= nsteps) break;
             const GBuf bf = gbuf<TM, TN>(smem, ks & 1);
-            g_store<A32, TM, TN>(regs[j], bf, a, m0, kfirst + ks, resc);
+            g_store<A32, TM, TN, FMT>(regs[j], bf, a, m0, kfirst + ks, resc);
             __syncthreads();
             if (S == 1) {
-                if (ks + 1 < nsteps) g_load<A32, TM, TN>(src, kfirst + ks + 1, regs[j]);
+                if (ks + 1 < nsteps) g_load<A32, TM, TN, FMT>(src, kfirst + ks + 1, regs[j]);
             } else {
-                g_load<A32, TM, TN>(src, kfirst + min(ks + S, nsteps - 1), regs[j]);
+                g_load<A32, TM, TN, FMT>(src, kfirst + min(ks + S, nsteps - 1), regs[j]);
             }
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
@@ -892,19 +938,19 @@ bool large_tiles(int T, int n_tiles_large) {
 // where every step would otherwise wait a full memory round trip).
 constexpr int kSmallGridStages = 4;
 
-template <int EPI, int TM, int TN, bool A32, int ST>
+template <int FMT, int EPI, int TM, int TN, bool A32, int ST>
 hipError_t launch_st(const GemmArgs &a, dim3 grid, hipStream_t s) {
     using C = Cfg<TM, TN>;
     if (C::LDS > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_q8<EPI, TM, TN, A32, ST>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_q8<FMT, EPI, TM, TN, A32, ST>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_gemm_q8<EPI, TM, TN, A32, ST>), grid, dim3(kThreads), C::LDS, s, a);
+    hipLaunchKernelGGL((k_gemm_q8<FMT, EPI, TM, TN, A32, ST>), grid, dim3(kThreads), C::LDS, s, a);
     return hipGetLastError();
 }
 
-template <int EPI, int TM, int TN, bool A32>
+template <int EPI, int TM, int TN, bool A32, int FMT = F_Q8_0>
 hipError_t launch_cfg(const GemmArgs &a, int ytiles, hipStream_t s) {
     // buffer resources address < 2 GiB (offsets past that read as zeros)
     if (size_t(a.T) * a.K * 4 >= kOutOfRange) return hipErrorInvalidValue;
@@ -912,14 +958,15 @@ hipError_t launch_cfg(const GemmArgs &a, int ytiles, hipStream_t s) {
         if (a.W[i] && size_t(a.Nm[i]) * a.rowbytes >= kOutOfRange) return hipErrorInvalidValue;
     const dim3 grid((a.T + TM - 1) / TM, ytiles, EPI == G_PART ? a.splits : 1);
     if constexpr (TM == 32)
-        if (long(grid.x) * grid.y * grid.z < 256) return launch_st<EPI, TM, TN, A32, kSmallGridStages>(a, grid, s);
-    return launch_st<EPI, TM, TN, A32, 1>(a, grid, s);
+        if (long(grid.x) * grid.y * grid.z < 256)
+            return launch_st<FMT, EPI, TM, TN, A32, kSmallGridStages>(a, grid, s);
+    return launch_st<FMT, EPI, TM, TN, A32, 1>(a, grid, s);
 }
 
-template <int EPI, bool A32>
+template <int EPI, bool A32, int FMT = F_Q8_0>
 hipError_t launch_plain(const GemmArgs &a, int N, hipStream_t s) {
-    if (large_tiles(a.T, row_tiles(N, 128))) return launch_cfg<EPI, 64, 128, A32>(a, row_tiles(N, 128), s);
-    return launch_cfg<EPI, 32, 64, A32>(a, row_tiles(N, 64), s);
+    if (large_tiles(a.T, row_tiles(N, 128))) return launch_cfg<EPI, 64, 128, A32, FMT>(a, row_tiles(N, 128), s);
+    return launch_cfg<EPI, 32, 64, A32, FMT>(a, row_tiles(N, 64), s);
 }
 
 template <int FMT, int EPI, int TM, int TN, bool A32>
@@ -950,12 +997,14 @@ hipError_t launch_kq_fmt(const GemmArgs &a, bool a_split, int accumulate, hipStr
     return accumulate ? launch_kq_plain<FMT, G_ACCUM, true>(a, s) : launch_kq_plain<FMT, G_STORE, true>(a, s);
 }
 
-GemmArgs gemm_base(const void *A, int T, int K) {
+GemmArgs gemm_base(const void *A, int T, int K, int fmt = F_Q8_0) {
     GemmArgs a{};
     a.A = A; a.T = T; a.K = K;
-    a.rowbytes = K / kQK * kQBytes;
+    a.rowbytes = int(fmt_row_bytes(fmt, K));
     return a;
 }
+
+bool pair_format(int fmt) { return fmt == F_Q8_0 || fmt == F_Q5_0; }
 
 }  // namespace
 
@@ -988,18 +1037,26 @@ int gemm_splitk(int N, int K, int T) {
 }
 
 hipError_t launch_gemm_part(const uint8_t *W, int N, int K, const _Float16 *A, int T, int splits, float *part,
-                            hipStream_t s, const ActScale &sc) {
-    if (splits < 1 || splits > kSplitKMax || splits > K / GK || T > gemm_splitk_max_tokens(N))
+                            hipStream_t s, const ActScale &sc, int fmt) {
+    if (splits < 1 || splits > kSplitKMax || splits > K / GK || T > gemm_splitk_max_tokens(N) || !pair_format(fmt))
         return hipErrorInvalidValue;
-    GemmArgs a = gemm_base(A, T, K);
+    GemmArgs a = gemm_base(A, T, K, fmt);
     a.W[0] = W; a.Nm[0] = N; a.part = part; a.splits = splits; a.sc = sc;
-    return launch_cfg<G_PART, 32, 64, false>(a, row_tiles(N, 64), s);
+    return fmt == F_Q5_0 ? launch_cfg<G_PART, 32, 64, false, F_Q5_0>(a, row_tiles(N, 64), s)
+                         : launch_cfg<G_PART, 32, 64, false>(a, row_tiles(N, 64), s);
 }
 
 hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
-                              int accumulate, float *Y, hipStream_t s, const ActScale &sc) {
-    GemmArgs a = gemm_base(A, T, K);
+                              int accumulate, float *Y, hipStream_t s, const ActScale &sc, int fmt) {
+    if (!pair_format(fmt)) return hipErrorInvalidValue;
+    GemmArgs a = gemm_base(A, T, K, fmt);
     a.W[0] = W; a.Nm[0] = N; a.Y = Y; a.sc = sc;
+    if (fmt == F_Q5_0) {
+        if (a_split)
+            return accumulate ? launch_plain<G_ACCUM, false, F_Q5_0>(a, N, s)
+                              : launch_plain<G_STORE, false, F_Q5_0>(a, N, s);
+        return accumulate ? launch_plain<G_ACCUM, true, F_Q5_0>(a, N, s) : launch_plain<G_STORE, true, F_Q5_0>(a, N, s);
+    }
     if (a_split)
         return accumulate ? launch_plain<G_ACCUM, false>(a, N, s) : launch_plain<G_STORE, false>(a, N, s);
     return accumulate ? launch_plain<G_ACCUM, true>(a, N, s) : launch_plain<G_STORE, true>(a, N, s);
@@ -1016,30 +1073,60 @@ hipError_t launch_gemm_kq(int fmt, const uint8_t *W, int N, int K, const void *A
                          : launch_kq_fmt<F_Q6_K>(a, a_split, accumulate, s);
 }
 
+template <int FMT>
+hipError_t launch_qkv_fmt(const GemmArgs &a, bool large, int yt, hipStream_t s) {
+    return large ? launch_cfg<G_QKV, 64, 128, false, FMT>(a, yt, s) : launch_cfg<G_QKV, 32, 64, false, FMT>(a, yt, s);
+}
+
+// q, k and v in one launch when they share a block format; otherwise one
+// launch per run of matrices of one format (the other matrices get no row
+// tiles, so the kernel's tile -> matrix walk skips them).
 hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u, const StepState *st,
                            const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s,
                            const ActScale &sc) {
-    GemmArgs a = gemm_base(u, T, d.H);
-    a.sc = sc;
     const int QD = d.nh * d.hd, KVD = d.nkv * d.hd;
-    a.W[0] = w.wq; a.W[1] = w.wk; a.W[2] = w.wv;
-    a.Nm[0] = QD; a.Nm[1] = KVD; a.Nm[2] = KVD;
-    a.st = st; a.rope = rope; a.q = q; a.kc = kc; a.vc = vc;
-    a.QD = QD; a.hd = d.hd; a.max_seq = d.max_seq; a.rope_neox = d.rope_neox;
+    const int fm[3] = {w.fq, w.fk, w.fv};
+    for (int i = 0; i < 3; ++i)
+        if (!pair_format(fm[i])) return hipErrorInvalidValue;
     const bool large = large_tiles(T, row_tiles(QD, 128) + 2 * row_tiles(KVD, 128));
     const int tn = large ? 128 : 64;
-    for (int i = 0; i < 3; ++i) a.tiles[i] = row_tiles(a.Nm[i], tn);
-    const int yt = a.tiles[0] + a.tiles[1] + a.tiles[2];
-    return large ? launch_cfg<G_QKV, 64, 128, false>(a, yt, s) : launch_cfg<G_QKV, 32, 64, false>(a, yt, s);
+    for (int first = 0; first < 3;) {
+        int last = first;
+        while (last + 1 < 3 && fm[last + 1] == fm[first]) ++last;
+        GemmArgs a = gemm_base(u, T, d.H, fm[first]);
+        a.sc = sc;
+        a.W[0] = w.wq; a.W[1] = w.wk; a.W[2] = w.wv;
+        a.Nm[0] = QD; a.Nm[1] = KVD; a.Nm[2] = KVD;
+        a.st = st; a.rope = rope; a.q = q; a.kc = kc; a.vc = vc;
+        a.QD = QD; a.hd = d.hd; a.max_seq = d.max_seq; a.rope_neox = d.rope_neox;
+        int yt = 0;
+        for (int i = 0; i < 3; ++i) {
+            a.tiles[i] = (i >= first && i <= last) ? row_tiles(a.Nm[i], tn) : 0;
+            if (!a.tiles[i]) a.W[i] = nullptr;
+            yt += a.tiles[i];
+        }
+        const hipError_t e = fm[first] == F_Q5_0 ? launch_qkv_fmt<F_Q5_0>(a, large, yt, s)
+                                                 : launch_qkv_fmt<F_Q8_0>(a, large, yt, s);
+        if (e != hipSuccess) return e;
+        first = last + 1;
+    }
+    return hipSuccess;
+}
+
+template <int FMT>
+hipError_t launch_gateup_fmt(const GemmArgs &a, hipStream_t s) {
+    const int F = a.Nm[0];
+    if (large_tiles(a.T, row_tiles(F, 64))) return launch_cfg<G_GATEUP, 64, 128, false, FMT>(a, row_tiles(F, 64), s);
+    return launch_cfg<G_GATEUP, 32, 64, false, FMT>(a, row_tiles(F, 32), s);
 }
 
 hipError_t launch_gemm_gateup(const Dims &d, const LayerPtrs &w, const _Float16 *u, _Float16 *h, int T,
                               hipStream_t s, const ActScale &sc) {
-    GemmArgs a = gemm_base(u, T, d.H);
+    if (!pair_format(w.fg) || w.fu != w.fg) return hipErrorInvalidValue;
+    GemmArgs a = gemm_base(u, T, d.H, w.fg);
     a.sc = sc;
     a.W[0] = w.wg; a.W[1] = w.wu; a.Nm[0] = d.F; a.Nm[1] = d.F; a.h = h;
-    if (large_tiles(T, row_tiles(d.F, 64))) return launch_cfg<G_GATEUP, 64, 128, false>(a, row_tiles(d.F, 64), s);
-    return launch_cfg<G_GATEUP, 32, 64, false>(a, row_tiles(d.F, 32), s);
+    return w.fg == F_Q5_0 ? launch_gateup_fmt<F_Q5_0>(a, s) : launch_gateup_fmt<F_Q8_0>(a, s);
 }
 
 }  // namespace q8l

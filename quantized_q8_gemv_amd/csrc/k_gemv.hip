@@ -121,18 +121,18 @@ __device__ inline const uint8_t *tile_src(const CoreArgs &a, int nrows, int c, i
         const int m = i >= per_mat ? 1 : 0;
         return a.W[m] + size_t(a.row0) * sh.rowbytes + size_t(i - m * per_mat) * unit;
     }
-    const int per_row = sh.PC * kPairBytes / unit;
+    const int per_row = sh.PC * sh.pb / unit;
     const int per_mat = nrows * per_row;
     const int m = i >= per_mat ? 1 : 0;
     const int ii = i - m * per_mat;
     const int r = ii / per_row, j = ii - r * per_row;
-    return a.W[m] + size_t(a.row0 + r) * sh.rowbytes + size_t(c) * sh.PC * kPairBytes + size_t(j) * unit;
+    return a.W[m] + size_t(a.row0 + r) * sh.rowbytes + size_t(c) * sh.PC * sh.pb + size_t(j) * unit;
 }
 
 __device__ inline void stage_issue(const CoreArgs &a, int nrows, int c, bool vec, WStage &st) {
     if (!vec) return;
     const int tid = threadIdx.x;
-    const int n16 = a.nmat * nrows * a.sh.PC * kPairBytes / 16;
+    const int n16 = a.nmat * nrows * a.sh.PC * a.sh.pb / 16;
 #pragma unroll
     for (int k = 0; k < kMaxV4; ++k) {
         const int i = tid + k * kThreads;
@@ -144,7 +144,7 @@ __device__ inline void stage_issue(const CoreArgs &a, int nrows, int c, bool vec
 __device__ inline void stage_store(const CoreArgs &a, int nrows, int c, bool vec, const WStage &st,
                                    uint32_t *wt) {
     const int tid = threadIdx.x;
-    const int bytes = a.nmat * nrows * a.sh.PC * kPairBytes;
+    const int bytes = a.nmat * nrows * a.sh.PC * a.sh.pb;
     if (vec) {
         u32x4 *d = reinterpret_cast<u32x4 *>(wt);
 #pragma unroll
@@ -269,15 +269,22 @@ __device__ void gemv_core(const CoreArgs &a, const Lds &l) {
         if (MULTI && c + 1 < nchunks) stage_issue(a, nrows, c + 1, vec, st);
         __syncthreads();
         if (tid < units) {
-            const uint32_t *wp = l.wt + size_t(tid) * (kPairBytes / 4);
+            const uint32_t *wp = l.wt + size_t(tid) * (sh.pb / 4);
+            const bool q5 = sh.pb == kQ5PairBytes;
             if constexpr (MAXT == 1) {
                 float dA, sA, dB, sB;
-                pair_dot1(wp, l.xs + size_t(up) * kXPad, dA, sA, dB, sB);
+                if (q5)
+                    pair_dot1_q5(wp, l.xs + size_t(up) * kXPad, dA, sA, dB, sB);
+                else
+                    pair_dot1(wp, l.xs + size_t(up) * kXPad, dA, sA, dB, sB);
                 acc[0] = fmaf(dA, sA, acc[0]);
                 acc[0] = fmaf(dB, sB, acc[0]);
             } else {
                 PairQ pq;
-                decode_pair(wp, pq);
+                if (q5)
+                    decode_pair_q5(wp, pq);
+                else
+                    decode_pair(wp, pq);
 #pragma unroll
                 for (int t = 0; t < MAXT; ++t) {
                     if (t < a.Tc) {
@@ -337,6 +344,7 @@ struct QkvArgs {
     float *xres;
     int V;
     PartSrc ps;          // decode: split-K partials added to x first (n = 0: none)
+    int pb[3];           // pair bytes of q, k, v (68 Q8_0, 44 Q5_0)
     // several tokens (a prefill): set to 1 when a written q, k or v value is
     // outside the f16 pairs' range of the prefill attention (NEOX q and k are
     // checked by the kernel that rotates them)
@@ -360,6 +368,8 @@ __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
     const int t0 = blockIdx.y * MAXT;
     CoreArgs c;
     c.W[0] = W; c.W[1] = nullptr; c.nmat = 1; c.sh = a.sh; c.N = N;
+    c.sh.pb = (kind == 0 ? a.pb[0] : kind == 1 ? a.pb[1] : a.pb[2]);
+    c.sh.rowbytes = a.sh.P * (kind == 0 ? a.pb[0] : kind == 1 ? a.pb[1] : a.pb[2]);
     c.row0 = tile * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
     gemv_core<MAXT, MULTI>(c, l);
@@ -776,8 +786,6 @@ __device__ __forceinline__ void rows_dot1(const CoreArgs &c, const Lds1 &l, int 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const GemvShape &sh = c.sh;
     const int items = c.nmat * nrows;
-    const uint8_t *wt = reinterpret_cast<const uint8_t *>(l.wt) + (lane >> 5) * kQBytes;
-    const int o = lane & 31;
     constexpr int W = kThreads / 64;
     auto put = [&](int it, float v) {
         if (lane == 0) {
@@ -785,6 +793,29 @@ __device__ __forceinline__ void rows_dot1(const CoreArgs &c, const Lds1 &l, int 
             l.outv[m * sh.NR + r] = v;
         }
     };
+    if (sh.pb == kQ5PairBytes) {
+        // Q5_0: weight j = lane % 32 of block 2i + lane / 32 (nibble j / 16 of
+        // byte 6 + j % 16, fifth bit j of the word at byte 2)
+        const uint8_t *wt = reinterpret_cast<const uint8_t *>(l.wt) + (lane >> 5) * kQ5Bytes;
+        const int j = lane & 31;
+        for (int it = wid; it < items; it += W) {
+            const uint8_t *row = wt + size_t(it) * sh.PC * kQ5PairBytes;
+            float acc = 0.f;
+#pragma unroll 4
+            for (int i = 0; i < sh.P; ++i) {
+                const uint8_t *blk = row + i * kQ5PairBytes;
+                const float d = half_bits_to_float(*reinterpret_cast<const uint16_t *>(blk));
+                const uint32_t qh = uint32_t(*reinterpret_cast<const uint16_t *>(blk + 2)) |
+                                    (uint32_t(*reinterpret_cast<const uint16_t *>(blk + 4)) << 16);
+                const int q5 = ((blk[6 + (j & 15)] >> (4 * (j >> 4))) & 15) | int(((qh >> j) & 1u) << 4);
+                acc = fmaf(d * static_cast<float>(q5 - 16), l.xs[i * kXPad + lane], acc);
+            }
+            put(it, wave_sum_dpp(acc));
+        }
+        return;
+    }
+    const uint8_t *wt = reinterpret_cast<const uint8_t *>(l.wt) + (lane >> 5) * kQBytes;
+    const int o = lane & 31;
     int it = wid;
     // rows it and it + W together while both exist (one read of u for two rows)
     for (; it + W < items; it += 2 * W) {
@@ -849,8 +880,12 @@ __device__ void tile_run1(const CoreArgs &c, const Lds1 &l, int nrows, bool vec,
         __syncthreads();
         if (tid < units) {
             float dA, sA, dB, sB;
-            pair_dot1(l.wt + size_t(tid) * (kPairBytes / 4), l.xs + size_t(ch * sh.PC + up) * kXPad,
-                      dA, sA, dB, sB);
+            const uint32_t *wp = l.wt + size_t(tid) * (sh.pb / 4);
+            const float *xp = l.xs + size_t(ch * sh.PC + up) * kXPad;
+            if (sh.pb == kQ5PairBytes)
+                pair_dot1_q5(wp, xp, dA, sA, dB, sB);
+            else
+                pair_dot1(wp, xp, dA, sA, dB, sB);
             acc = fmaf(dA, sA, acc);
             acc = fmaf(dB, sB, acc);
         }
@@ -978,6 +1013,8 @@ __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
             kind = 2; c.W[0] = a.wv; c.N = a.KVD; tile -= a.tq + a.tk;
         }
         c.row0 = tile * a.sh.NR;
+        c.sh.pb = (kind == 0 ? a.pb[0] : kind == 1 ? a.pb[1] : a.pb[2]);
+        c.sh.rowbytes = a.sh.P * (kind == 0 ? a.pb[0] : kind == 1 ? a.pb[1] : a.pb[2]);
         return c;
     };
     int tile = blockIdx.x, kind;
@@ -1062,14 +1099,14 @@ __device__ inline int chunk_pairs(const GemvShape &sh, int c) { return min(sh.PC
 // Piece i (of `unit` bytes) of chunk c's tile: source address and LDS byte offset.
 __device__ inline const uint8_t *ctile_src(const uint8_t *W, const GemvShape &sh, int row0, int pcc, int c, int i,
                                            int unit) {
-    const int per_row = pcc * kPairBytes / unit;
+    const int per_row = pcc * sh.pb / unit;
     const int r = i / per_row, j = i - r * per_row;
-    return W + size_t(row0 + r) * sh.rowbytes + size_t(c) * sh.PC * kPairBytes + size_t(j) * unit;
+    return W + size_t(row0 + r) * sh.rowbytes + size_t(c) * sh.PC * sh.pb + size_t(j) * unit;
 }
 __device__ inline int ctile_dst(const GemvShape &sh, int pcc, int i, int unit) {
-    const int per_row = pcc * kPairBytes / unit;
+    const int per_row = pcc * sh.pb / unit;
     const int r = i / per_row, j = i - r * per_row;
-    return r * sh.PC * kPairBytes + j * unit;
+    return r * sh.PC * sh.pb + j * unit;
 }
 __device__ inline bool ctile_vec(const GemvShape &sh, int pcc) {
     return (pcc % 4 == 0) && (sh.PC % 4 == 0) && (sh.P % 4 == 0);
@@ -1077,7 +1114,7 @@ __device__ inline bool ctile_vec(const GemvShape &sh, int pcc) {
 __device__ inline void ctile_issue(const uint8_t *W, const GemvShape &sh, int row0, int nrows, int c, WStage &st) {
     const int pcc = chunk_pairs(sh, c);
     if (!ctile_vec(sh, pcc)) return;
-    const int n16 = nrows * pcc * kPairBytes / 16;
+    const int n16 = nrows * pcc * sh.pb / 16;
 #pragma unroll
     for (int k = 0; k < kMaxV4; ++k) {
         const int i = threadIdx.x + k * kThreads;
@@ -1090,7 +1127,7 @@ __device__ inline void ctile_store(const uint8_t *W, const GemvShape &sh, int ro
     const int pcc = chunk_pairs(sh, c);
     uint8_t *base = reinterpret_cast<uint8_t *>(wt);
     if (ctile_vec(sh, pcc)) {
-        const int n16 = nrows * pcc * kPairBytes / 16;
+        const int n16 = nrows * pcc * sh.pb / 16;
 #pragma unroll
         for (int k = 0; k < kMaxV4; ++k) {
             const int i = threadIdx.x + k * kThreads;
@@ -1098,14 +1135,14 @@ __device__ inline void ctile_store(const uint8_t *W, const GemvShape &sh, int ro
         }
     } else {
 #pragma unroll 1
-        for (int i = threadIdx.x; i < nrows * pcc * kPairBytes / 4; i += kThreads)
+        for (int i = threadIdx.x; i < nrows * pcc * sh.pb / 4; i += kThreads)
             *reinterpret_cast<uint32_t *>(base + ctile_dst(sh, pcc, i, 4)) =
                 *reinterpret_cast<const uint32_t *>(ctile_src(W, sh, row0, pcc, c, i, 4));
     }
 }
 
 __host__ __device__ inline size_t lds1c_bytes(const GemvShape &sh) {
-    return align16(size_t(sh.NR) * sh.PC * kPairBytes) + align16(size_t(sh.PC) * kXPad * 4) +
+    return align16(size_t(sh.NR) * sh.PC * sh.pb) + align16(size_t(sh.PC) * kXPad * 4) +
            align16(size_t(sh.NR > 4 ? sh.NR : 4) * 4) + 16;
 }
 
@@ -1113,11 +1150,12 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const GemvShape &sh = a.sh;
     uint32_t *wt = reinterpret_cast<uint32_t *>(smem);
-    float *xs = reinterpret_cast<float *>(smem + align16(size_t(sh.NR) * sh.PC * kPairBytes));
+    float *xs = reinterpret_cast<float *>(smem + align16(size_t(sh.NR) * sh.PC * sh.pb));
     float *outv = xs + align16(size_t(sh.PC) * kXPad * 4) / 4;
     const int tid = threadIdx.x;
     const int ntiles = (a.N + sh.NR - 1) / sh.NR;
     const int nchunks = (sh.P + sh.PC - 1) / sh.PC;
+    const bool q5 = sh.pb == kQ5PairBytes;
     int my_tiles = 0;
     for (int k = 0; k < kTilesPerWg; ++k) my_tiles += (int(blockIdx.x) + k * int(gridDim.x) < ntiles) ? 1 : 0;
     float acc[kTilesPerWg];
@@ -1169,7 +1207,10 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
                 const int r = tid / sh.PC, p = tid - r * sh.PC;
                 if (r < nrows && p < pcc) {
                     float dA, sA, dB, sB;
-                    pair_dot1(wt + size_t(tid) * (kPairBytes / 4), xs + size_t(p) * kXPad, dA, sA, dB, sB);
+                    if (q5)
+                        pair_dot1_q5(wt + size_t(tid) * (kQ5PairBytes / 4), xs + size_t(p) * kXPad, dA, sA, dB, sB);
+                    else
+                        pair_dot1(wt + size_t(tid) * (kPairBytes / 4), xs + size_t(p) * kXPad, dA, sA, dB, sB);
                     acc[k] = fmaf(dA, sA, acc[k]);
                     acc[k] = fmaf(dB, sB, acc[k]);
                 }
@@ -1287,11 +1328,14 @@ int divisor_at_most(int P, int cap) {
 //   nmat:        matrices processed together
 //   target_wgs:  aim for at least this many workgroups
 //   nr_mult:     rows per workgroup must be a multiple of this (2 for rope pairs)
-GemvShape choose_shape(int N, int K, int maxt, int nmat, int target_wgs, int nr_mult) {
+//   fmt:         the matrix's block format (Q8_0 or Q5_0: 68- or 44-byte pairs;
+//                both need the same row alignment, P * align a multiple of 4)
+GemvShape choose_shape(int N, int K, int maxt, int nmat, int target_wgs, int nr_mult, int fmt = F_Q8_0) {
     GemvShape s;
     s.K = K;
     s.P = K / kPairWeights;
-    s.rowbytes = s.P * kPairBytes;
+    s.pb = fmt == F_Q5_0 ? kQ5PairBytes : kPairBytes;
+    s.rowbytes = s.P * s.pb;
     const int lds_cap_pairs = std::max(1, (40 * 1024) / (maxt * kXPad * 4));
     s.PC = divisor_at_most(s.P, std::min(lds_cap_pairs, kThreads / nmat));
     const int cap = kThreads / (nmat * s.PC);
@@ -1364,6 +1408,9 @@ hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const S
     a.QD = d.nh * d.hd; a.KVD = d.nkv * d.hd; a.hd = d.hd; a.max_seq = d.max_seq; a.T = T;
     a.eps = d.eps; a.rope_neox = d.rope_neox;
     a.sh = choose_shape(a.QD + 2 * a.KVD, d.H, maxt, 1, 512, 2);
+    a.pb[0] = w.fq == F_Q5_0 ? kQ5PairBytes : kPairBytes;
+    a.pb[1] = w.fk == F_Q5_0 ? kQ5PairBytes : kPairBytes;
+    a.pb[2] = w.fv == F_Q5_0 ? kQ5PairBytes : kPairBytes;
     a.tq = (a.QD + a.sh.NR - 1) / a.sh.NR;
     a.tk = (a.KVD + a.sh.NR - 1) / a.sh.NR;
     if (T == 1) {  // decode: row-looping kernel
@@ -1392,7 +1439,7 @@ hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, floa
     a.ps = ps;
     a.wg = w.wg; a.wu = w.wu; a.norm_w = w.ffn_norm; a.x = x; a.h = h; a.F = d.F; a.T = T;
     a.eps = d.eps;
-    a.sh = choose_shape(d.F, d.H, maxt, 2, 512, 1);
+    a.sh = choose_shape(d.F, d.H, maxt, 2, 512, 1, w.fg);
     if (T == 1) {
         const size_t lds = lds1_bytes(a.sh, 2);
         const int g = grid1((d.F + a.sh.NR - 1) / a.sh.NR, lds);
@@ -1412,13 +1459,14 @@ hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, floa
 
 hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
                          const float *norm_w, float eps, int accumulate, float *Y,
-                         hipStream_t s) {
+                         hipStream_t s, int fmt) {
+    if (fmt != F_Q8_0 && fmt != F_Q5_0) return hipErrorInvalidValue;
     const int maxt = T == 1 ? 1 : kMaxTokChunk;
     MatmulArgs a{};
     a.W = W; a.norm_w = norm_w; a.x = X; a.y = Y; a.N = N; a.T = T; a.accumulate = accumulate;
     a.eps = eps;
-    a.sh = choose_shape(N, K, maxt, 1, 512, 1);
-    if (T == 1 && !norm_w && wgemv_fits(K)) return launch_wmatmul(W, N, K, X, accumulate, Y, s);
+    a.sh = choose_shape(N, K, maxt, 1, 512, 1, fmt);
+    if (T == 1 && !norm_w && wgemv_fits(K)) return launch_wmatmul(W, N, K, X, accumulate, Y, s, fmt);
     if (T == 1) {
         if (a.sh.PC != a.sh.P && !norm_w) {  // large K: chunk-outer walk
             a.sh = chunked_shape(a.sh);

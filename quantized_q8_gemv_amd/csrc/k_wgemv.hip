@@ -15,7 +15,11 @@
 // round trip plus a short arithmetic chain.
 //
 // Arithmetic per row: acc = sum over i (in order) of (d * q) * u in each lane
-// (d * q is exact in f32), then the 64 lanes summed by wave_sum_dpp. The
+// (d * q is exact in f32), then the 64 lanes summed by wave_sum_dpp. Q5_0
+// rows (22-byte blocks) are read the same way: the lane's weight j = l % 32
+// of its block is nibble j / 16 of byte 6 + j % 16 with fifth bit j of the
+// word at byte 2, q = (nibble | bit << 4) - 16; each wave picks its matrix's
+// format once, before any load (a template of the whole wave's work). The
 // epilogues are those of the LDS-staged kernels: rope and the KV-cache write
 // (q/k/v), SiLU(gate) * up (gate/up), the residual add (o, down).
 
@@ -102,31 +106,61 @@ __device__ __forceinline__ void rms_norm(float (&v)[P], const float (&w)[P], flo
     for (int i = 0; i < P; ++i) v[i] = v[i] * r * w[i];
 }
 
-// This lane's weights and scales of one row (row bytes at `row`).
-template <int P>
+// This lane's weights and scales of one row (row bytes at `row`), as loaded:
+// Q8_0 the int8, Q5_0 the nibble byte and the fifth-bit word.
+template <int P, int FMT>
 struct RowRegs {
     int q[P];
     uint32_t d[P];
+    uint32_t h[FMT == F_Q5_0 ? P : 1];
 };
 
-template <int P>
-__device__ __forceinline__ void load_weights(const uint8_t *row, RowRegs<P> &r) {
+template <int P, int FMT>
+__device__ __forceinline__ void load_weights(const uint8_t *row, RowRegs<P, FMT> &r) {
     const int lane = threadIdx.x & 63;
-    const uint8_t *b = row + (lane >> 5) * kQBytes;
-    const int o = 2 + (lane & 31);
+    if (FMT == F_Q5_0) {
+        const uint8_t *b = row + (lane >> 5) * kQ5Bytes;
+        const int j = lane & 31;
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-        r.d[i] = *reinterpret_cast<const uint16_t *>(b + i * kPairBytes);
-        r.q[i] = static_cast<int8_t>(b[i * kPairBytes + o]);
+        for (int i = 0; i < P; ++i) {
+            const uint8_t *blk = b + i * kQ5PairBytes;
+            r.d[i] = *reinterpret_cast<const uint16_t *>(blk);
+            r.h[i] = uint32_t(*reinterpret_cast<const uint16_t *>(blk + 2)) |
+                     (uint32_t(*reinterpret_cast<const uint16_t *>(blk + 4)) << 16);
+            r.q[i] = blk[6 + (j & 15)];
+        }
+    } else {
+        const uint8_t *b = row + (lane >> 5) * kQBytes;
+        const int o = 2 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            r.d[i] = *reinterpret_cast<const uint16_t *>(b + i * kPairBytes);
+            r.q[i] = static_cast<int8_t>(b[i * kPairBytes + o]);
+        }
     }
 }
 
-template <int P>
-__device__ __forceinline__ float row_dot(const RowRegs<P> &r, const float (&u)[P]) {
+template <int P, int FMT>
+__device__ __forceinline__ float weight(const RowRegs<P, FMT> &r, int i) {
+    if (FMT == F_Q5_0) {
+        const int j = threadIdx.x & 31;
+        const int q5 = ((r.q[i] >> (4 * (j >> 4))) & 15) | int(((r.h[i] >> j) & 1u) << 4);
+        return half_bits_to_float(r.d[i]) * static_cast<float>(q5 - 16);
+    }
+    return half_bits_to_float(r.d[i]) * static_cast<float>(r.q[i]);
+}
+
+template <int P, int FMT>
+__device__ __forceinline__ float row_dot(const RowRegs<P, FMT> &r, const float (&u)[P]) {
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < P; ++i) acc = fmaf(half_bits_to_float(r.d[i]) * static_cast<float>(r.q[i]), u[i], acc);
+    for (int i = 0; i < P; ++i) acc = fmaf(weight<P, FMT>(r, i), u[i], acc);
     return wave_sum_dpp(acc);
+}
+
+template <int P>
+__device__ __forceinline__ size_t row_bytes_of(int fmt) {
+    return size_t(P) * (fmt == F_Q5_0 ? kQ5PairBytes : kPairBytes);
 }
 
 // ---------------------------------------------------------------- q/k/v
@@ -150,22 +184,17 @@ struct WQkvArgs {
     float *xres;
     int V;
     PartSrc ps;
+    int fmt[3];   // WFmt of q, k, v (Q8_0 or Q5_0)
 };
 
-template <int P>
-__global__ __launch_bounds__(kThreads) void k_wqkv1(WQkvArgs a) {
+template <int P, int FMT>
+__device__ __forceinline__ void wqkv_body(const WQkvArgs &a, int kind, int lrow) {
     const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int N = a.QD + 2 * a.KVD;
-    if (2 * e >= N) return;   // (no barriers in this kernel)
-    const int row = 2 * e;
-    const int kind = row < a.QD ? 0 : row < a.QD + a.KVD ? 1 : 2;
-    const int lrow = kind == 0 ? row : kind == 1 ? row - a.QD : row - a.QD - a.KVD;
     const uint8_t *W = kind == 0 ? a.wq : kind == 1 ? a.wk : a.wv;
-    const size_t rowbytes = size_t(P) * kPairBytes;
-    RowRegs<P> r0, r1;
-    load_weights<P>(W + size_t(lrow) * rowbytes, r0);
-    load_weights<P>(W + size_t(lrow + 1) * rowbytes, r1);
+    const size_t rowbytes = row_bytes_of<P>(FMT);
+    RowRegs<P, FMT> r0, r1;
+    load_weights<P, FMT>(W + size_t(lrow) * rowbytes, r0);
+    load_weights<P, FMT>(W + size_t(lrow + 1) * rowbytes, r1);
     float w[P];
 #pragma unroll
     for (int i = 0; i < P; ++i) w[i] = a.norm_w[i * 64 + lane];
@@ -181,8 +210,8 @@ __global__ __launch_bounds__(kThreads) void k_wqkv1(WQkvArgs a) {
     if (a.embed) {
         const uint32_t tok = a.st->token;
         const bool valid = tok < uint32_t(a.V);
-        RowRegs<P> er;
-        load_weights<P>(a.embed + (valid ? size_t(tok) : 0) * rowbytes, er);
+        RowRegs<P, F_Q8_0> er;
+        load_weights<P, F_Q8_0>(a.embed + (valid ? size_t(tok) : 0) * row_bytes_of<P>(F_Q8_0), er);
 #pragma unroll
         for (int i = 0; i < P; ++i) v[i] = valid ? half_bits_to_float(er.d[i]) * static_cast<float>(er.q[i]) : 0.f;
         if (blockIdx.x == 0 && threadIdx.x < 64) {
@@ -193,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void k_wqkv1(WQkvArgs a) {
         in.finish(a.ps);
     }
     rms_norm<P>(v, w, a.eps);
-    const float a0 = row_dot<P>(r0, v), a1 = row_dot<P>(r1, v);
+    const float a0 = row_dot<P, FMT>(r0, v), a1 = row_dot<P, FMT>(r1, v);
     // (an empty use here keeps the rope load where it was issued, at the
     // start: a load used only inside the branch below would be moved into it)
     asm volatile("" : : "v"(cs.x), "v"(cs.y));
@@ -208,6 +237,20 @@ __global__ __launch_bounds__(kThreads) void k_wqkv1(WQkvArgs a) {
     }
 }
 
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wqkv1(WQkvArgs a) {
+    const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int N = a.QD + 2 * a.KVD;
+    if (2 * e >= N) return;   // (no barriers in this kernel)
+    const int row = 2 * e;
+    const int kind = row < a.QD ? 0 : row < a.QD + a.KVD ? 1 : 2;
+    const int lrow = kind == 0 ? row : kind == 1 ? row - a.QD : row - a.QD - a.KVD;
+    if ((kind == 0 ? a.fmt[0] : kind == 1 ? a.fmt[1] : a.fmt[2]) == F_Q5_0)
+        wqkv_body<P, F_Q5_0>(a, kind, lrow);
+    else
+        wqkv_body<P, F_Q8_0>(a, kind, lrow);
+}
+
 // ---------------------------------------------------------------- gate/up
 
 struct WGateUpArgs {
@@ -218,18 +261,17 @@ struct WGateUpArgs {
     int F;
     float eps;
     PartSrc ps;
+    int fmt;   // WFmt of gate and up (one format)
 };
 
 // Wave w of workgroup b: row f = 4 b + w of gate and of up; h[f] = SiLU(g) * u.
-template <int P>
-__global__ __launch_bounds__(kThreads) void k_wgateup1(WGateUpArgs a) {
+template <int P, int FMT>
+__device__ __forceinline__ void wgateup_body(const WGateUpArgs &a, int f) {
     const int lane = threadIdx.x & 63;
-    const int f = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (f >= a.F) return;
-    const size_t rowbytes = size_t(P) * kPairBytes;
-    RowRegs<P> rg, ru;
-    load_weights<P>(a.wg + size_t(f) * rowbytes, rg);
-    load_weights<P>(a.wu + size_t(f) * rowbytes, ru);
+    const size_t rowbytes = row_bytes_of<P>(FMT);
+    RowRegs<P, FMT> rg, ru;
+    load_weights<P, FMT>(a.wg + size_t(f) * rowbytes, rg);
+    load_weights<P, FMT>(a.wu + size_t(f) * rowbytes, ru);
     float w[P];
 #pragma unroll
     for (int i = 0; i < P; ++i) w[i] = a.norm_w[i * 64 + lane];
@@ -237,8 +279,18 @@ __global__ __launch_bounds__(kThreads) void k_wgateup1(WGateUpArgs a) {
     in.issue(a.x, a.ps);
     in.finish(a.ps);
     rms_norm<P>(in.v, w, a.eps);
-    const float g = row_dot<P>(rg, in.v), u = row_dot<P>(ru, in.v);
+    const float g = row_dot<P, FMT>(rg, in.v), u = row_dot<P, FMT>(ru, in.v);
     if (lane == 0) a.h[f] = silu(g) * u;
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wgateup1(WGateUpArgs a) {
+    const int f = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (f >= a.F) return;
+    if (a.fmt == F_Q5_0)
+        wgateup_body<P, F_Q5_0>(a, f);
+    else
+        wgateup_body<P, F_Q8_0>(a, f);
 }
 
 // ---------------------------------------------------------------- o, down
@@ -248,31 +300,40 @@ struct WMatmulArgs {
     const float *x;
     float *y;
     int N, accumulate;
+    int fmt;   // WFmt of W (Q8_0 or Q5_0)
 };
 
 // Wave w of workgroup b: rows 2e, 2e + 1 (e = 4 b + w); y[row] (+)= W[row] . x.
-template <int P>
-__global__ __launch_bounds__(kThreads) void k_wmatmul1(WMatmulArgs a) {
+template <int P, int FMT>
+__device__ __forceinline__ void wmatmul_body(const WMatmulArgs &a, int row) {
     const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int row = 2 * e;
-    if (row >= a.N) return;
     const bool two = row + 1 < a.N;
-    const size_t rowbytes = size_t(P) * kPairBytes;
-    RowRegs<P> r0, r1;
-    load_weights<P>(a.W + size_t(row) * rowbytes, r0);
-    load_weights<P>(a.W + size_t(two ? row + 1 : row) * rowbytes, r1);
+    const size_t rowbytes = row_bytes_of<P>(FMT);
+    RowRegs<P, FMT> r0, r1;
+    load_weights<P, FMT>(a.W + size_t(row) * rowbytes, r0);
+    load_weights<P, FMT>(a.W + size_t(two ? row + 1 : row) * rowbytes, r1);
     const float y0 = a.accumulate ? a.y[row] : 0.f;
     const float y1 = a.accumulate ? a.y[two ? row + 1 : row] : 0.f;
     RowIn<P> in;
     in.issue(a.x, PartSrc{});
-    const float s0 = row_dot<P>(r0, in.v), s1 = row_dot<P>(r1, in.v);
+    const float s0 = row_dot<P, FMT>(r0, in.v), s1 = row_dot<P, FMT>(r1, in.v);
     asm volatile("" : : "v"(y0), "v"(y1));   // keeps the residual loads at the start (see k_wqkv1)
     const float o0 = a.accumulate ? y0 + s0 : s0, o1 = a.accumulate ? y1 + s1 : s1;
     if (lane == 0) {
         a.y[row] = o0;
         if (two) a.y[row + 1] = o1;
     }
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wmatmul1(WMatmulArgs a) {
+    const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int row = 2 * e;
+    if (row >= a.N) return;
+    if (a.fmt == F_Q5_0)
+        wmatmul_body<P, F_Q5_0>(a, row);
+    else
+        wmatmul_body<P, F_Q8_0>(a, row);
 }
 
 template <class F>
@@ -306,6 +367,7 @@ hipError_t launch_wqkv(const Dims &dm, const LayerPtrs &w, const float *x, const
     a.QD = dm.nh * dm.hd; a.KVD = dm.nkv * dm.hd; a.hd = dm.hd; a.max_seq = dm.max_seq;
     a.eps = dm.eps; a.rope_neox = dm.rope_neox;
     a.embed = embed; a.xres = xres; a.V = dm.V; a.ps = ps;
+    a.fmt[0] = w.fq; a.fmt[1] = w.fk; a.fmt[2] = w.fv;
     const int pairs = (a.QD + 2 * a.KVD) / 2;
     const int grid = (pairs + kWaves - 1) / kWaves;
     if (!dispatch_p(dm.H / kPairWeights, [&](auto p) {
@@ -319,6 +381,7 @@ hipError_t launch_wgateup(const Dims &dm, const LayerPtrs &w, const float *x, fl
                           const PartSrc &ps) {
     WGateUpArgs a;
     a.wg = w.wg; a.wu = w.wu; a.norm_w = w.ffn_norm; a.x = x; a.h = h; a.F = dm.F; a.eps = dm.eps; a.ps = ps;
+    a.fmt = w.fg;
     const int grid = (dm.F + kWaves - 1) / kWaves;
     if (!dispatch_p(dm.H / kPairWeights, [&](auto p) {
             hipLaunchKernelGGL(k_wgateup1<decltype(p)::value>, dim3(grid), dim3(kThreads), 0, s, a);
@@ -327,9 +390,10 @@ hipError_t launch_wgateup(const Dims &dm, const LayerPtrs &w, const float *x, fl
     return hipGetLastError();
 }
 
-hipError_t launch_wmatmul(const uint8_t *W, int N, int K, const float *x, int accumulate, float *y, hipStream_t s) {
+hipError_t launch_wmatmul(const uint8_t *W, int N, int K, const float *x, int accumulate, float *y, hipStream_t s,
+                          int fmt) {
     WMatmulArgs a;
-    a.W = W; a.x = x; a.y = y; a.N = N; a.accumulate = accumulate;
+    a.W = W; a.x = x; a.y = y; a.N = N; a.accumulate = accumulate; a.fmt = fmt;
     const int grid = ((N + 1) / 2 + kWaves - 1) / kWaves;
     if (!dispatch_p(K / kPairWeights, [&](auto p) {
             hipLaunchKernelGGL(k_wmatmul1<decltype(p)::value>, dim3(grid), dim3(kThreads), 0, s, a);

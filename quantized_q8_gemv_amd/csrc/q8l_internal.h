@@ -49,7 +49,8 @@ struct GemvShape {
     int P;        // 64-weight pairs per row
     int PC;       // pairs per K-chunk (divides P)
     int NR;       // rows per workgroup (NR * PC <= 256)
-    int rowbytes; // P * 68
+    int rowbytes; // P * pb
+    int pb;       // bytes per 64-weight pair: 68 (Q8_0) or 44 (Q5_0)
 };
 
 // Split-K partial sums waiting to be added to the residual row: the kernels
@@ -67,19 +68,30 @@ struct PartSrc {
 
 // Block formats a matrix may be stored in. Q4_K and Q6_K (256-weight blocks)
 // are accepted for the plain-matmul roles (o and down projections).
-enum WFmt { F_Q8_0 = 0, F_Q4_K = 1, F_Q6_K = 2 };
+// Q5_0 (32-weight blocks: f16 d, a 32-bit word of fifth bits, 16 bytes of
+// nibbles; weight = d * ((nibble | bit << 4) - 16)) is accepted for the q, k,
+// v, o, gate and up projections.
+enum WFmt { F_Q8_0 = 0, F_Q4_K = 1, F_Q6_K = 2, F_Q5_0 = 3 };
+constexpr int kQ5Bytes = 22;         // bytes per Q5_0 block
+constexpr int kQ5PairBytes = 44;     // two Q5_0 blocks: 64 weights
 constexpr int kQKK = 256;            // weights per Q4_K / Q6_K block
 constexpr int kQ4KBytes = 144;       // f16 d, f16 dmin, 12 scale/min bytes, 128 nibble bytes
 constexpr int kQ6KBytes = 210;       // 128 low-nibble bytes, 64 high-bit bytes, 16 int8 scales, f16 d
 
+// 256-weight block formats: the K-format GEMV and GEMM kernels.
+__host__ __device__ inline bool kq_format(int fmt) { return fmt == F_Q4_K || fmt == F_Q6_K; }
+
 __host__ __device__ inline int64_t fmt_row_bytes(int fmt, int64_t K) {
-    return fmt == F_Q4_K ? K / kQKK * kQ4KBytes : fmt == F_Q6_K ? K / kQKK * kQ6KBytes : K / kQK * kQBytes;
+    return fmt == F_Q4_K ? K / kQKK * kQ4KBytes
+         : fmt == F_Q6_K ? K / kQKK * kQ6KBytes
+         : fmt == F_Q5_0 ? K / kQK * kQ5Bytes
+                         : K / kQK * kQBytes;
 }
 
 struct LayerPtrs {
     const uint8_t *wq, *wk, *wv, *wo, *wg, *wu, *wd;
     const float *attn_norm, *ffn_norm;
-    int fo, fd;  // WFmt of wo and wd
+    int fq, fk, fv, fo, fg, fu, fd;  // WFmt of each matrix
 };
 
 struct Dims {
@@ -123,11 +135,13 @@ hipError_t launch_wqkv(const Dims &d, const LayerPtrs &w, const float *x, const 
                        const PartSrc &ps);
 hipError_t launch_wgateup(const Dims &d, const LayerPtrs &w, const float *x, float *h, hipStream_t s,
                           const PartSrc &ps);
-hipError_t launch_wmatmul(const uint8_t *W, int N, int K, const float *x, int accumulate, float *y, hipStream_t s);
+hipError_t launch_wmatmul(const uint8_t *W, int N, int K, const float *x, int accumulate, float *y, hipStream_t s,
+                          int fmt = F_Q8_0);
 // Y[t] (+)= W U[t] for generic use (o-proj / down with accumulate = 1).
+// fmt: Q8_0 or Q5_0.
 hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
                          const float *norm_w, float eps, int accumulate, float *Y,
-                         hipStream_t s);
+                         hipStream_t s, int fmt = F_Q8_0);
 // Decode o-projection after an attention of 2..kMergeMaxSplits splits: the
 // merge of the split partials (part, [nh][n_splits][hd + 2]) is the GEMV's
 // prologue (no merge kernel); Y += W o. Every workgroup of the GEMV reads all
@@ -251,10 +265,12 @@ int gemm_splitk(int N, int K, int T);
 // Longest prompt for which an N-row product may be split: the partial-sum
 // scratch holds kSplitKMax * gemm_splitk_max_tokens(N) * N floats.
 int gemm_splitk_max_tokens(int N);
+// W in Q8_0 or Q5_0 (fmt).
 hipError_t launch_gemm_part(const uint8_t *W, int N, int K, const _Float16 *A, int T, int splits, float *part,
-                            hipStream_t s, const ActScale &sc = ActScale{});
+                            hipStream_t s, const ActScale &sc = ActScale{}, int fmt = F_Q8_0);
 hipError_t launch_gemm_matmul(const uint8_t *W, int N, int K, const void *A, bool a_split, int T,
-                              int accumulate, float *Y, hipStream_t s, const ActScale &sc = ActScale{});
+                              int accumulate, float *Y, hipStream_t s, const ActScale &sc = ActScale{},
+                              int fmt = F_Q8_0);
 hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u, const StepState *st,
                            const float2 *rope, float *q, float *kc, float *vc, int T, hipStream_t s,
                            const ActScale &sc = ActScale{});

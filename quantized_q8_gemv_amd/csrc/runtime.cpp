@@ -128,7 +128,7 @@ struct q8l_model {
     bool merge_in_o = false;  // decode o-projection merges 2..8 attention splits in its prologue
     bool fuse_attn_o = false; // one-split decode: attention and o-projection in one kernel (split-K by group)
     std::vector<std::vector<const void *>> layer_ptrs;  // [L][S_NSLOT]
-    std::vector<int> fmt_o, fmt_d;                      // [L] WFmt of attn_output / ffn_down
+    std::vector<std::vector<int>> fmt;                  // [L][S_NSLOT] WFmt of each matrix
     uint8_t *ws = nullptr;
     size_t ws_bytes = 0;
     bool finalized = false;
@@ -162,8 +162,9 @@ struct q8l_model {
         w.wg = static_cast<const uint8_t *>(p[S_WG]);
         w.wu = static_cast<const uint8_t *>(p[S_WU]);
         w.wd = static_cast<const uint8_t *>(p[S_WD]);
-        w.fo = fmt_o[l];
-        w.fd = fmt_d[l];
+        const auto &f = fmt[l];
+        w.fq = f[S_WQ]; w.fk = f[S_WK]; w.fv = f[S_WV]; w.fo = f[S_WO];
+        w.fg = f[S_WG]; w.fu = f[S_WU]; w.fd = f[S_WD];
         return w;
     }
     float *kc(int l) const { return at<float>(lay.kc) + size_t(l) * lay.kv_layer; }
@@ -237,11 +238,12 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
     sc_h_in.el_stride = m->lay.el_stride;
     // Prefill x += A W^T for a Q8_0 matrix of H rows: split over K when the
     // plain grid would be small (the partial sums wait in kpart).
-    auto gemm_accumulate = [&](const uint8_t *W, int K, const _Float16 *A, const ActScale &sc) -> hipError_t {
+    auto gemm_accumulate = [&](const uint8_t *W, int K, const _Float16 *A, const ActScale &sc,
+                               int fmt) -> hipError_t {
         const int sk = gemm_splitk(d.H, K, T);
         pend = sk > 1 ? sk : 0;
-        return sk > 1 ? launch_gemm_part(W, d.H, K, A, T, sk, kpart, s, sc)
-                      : launch_gemm_matmul(W, d.H, K, A, true, T, 1, x, s, sc);
+        return sk > 1 ? launch_gemm_part(W, d.H, K, A, T, sk, kpart, s, sc, fmt)
+                      : launch_gemm_matmul(W, d.H, K, A, true, T, 1, x, s, sc, fmt);
     };
     for (int l = 0; l < m->cfg.n_layer; ++l) {
         const LayerPtrs w = m->layer(l);
@@ -286,9 +288,9 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
                 if (decode_splits > 1 && !merge_o &&
                     (e = launch_attn_combine(a.part, decode_splits, 0, d.nh, d.hd, att, st, s)) != hipSuccess)
                     return e;
-                e = w.fo != F_Q8_0 ? launch_kq_gemv(w.fo, w.wo, d.H, QD, att, 1, xo, s)
-                    : merge_o      ? launch_oproj_merged(w.wo, d.H, QD, a.part, decode_splits, d.hd, st, xo, s)
-                                   : launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, xo, s);
+                e = kq_format(w.fo) ? launch_kq_gemv(w.fo, w.wo, d.H, QD, att, 1, xo, s)
+                    : merge_o       ? launch_oproj_merged(w.wo, d.H, QD, a.part, decode_splits, d.hd, st, xo, s)
+                                    : launch_matmul(w.wo, d.H, QD, att, 1, nullptr, d.eps, 1, xo, s, w.fo);
                 if (e != hipSuccess) return e;
             }
         } else {
@@ -299,13 +301,13 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.scale = 1.0f / sqrtf(float(d.hd));
             a.range_flag = m->range_dev;
             if ((e = launch_attn_prefill(a, s)) != hipSuccess) return e;
-            if (w.fo != F_Q8_0)
+            if (kq_format(w.fo))
                 e = gemm ? launch_gemm_kq(w.fo, w.wo, d.H, QD, att_s, true, T, 1, x, s, sc_o)
                          : launch_gemm_kq(w.fo, w.wo, d.H, QD, att, false, T, 1, x, s, sc_o);
             else if (gemm)
-                e = gemm_accumulate(w.wo, QD, att_s, sc_o);
+                e = gemm_accumulate(w.wo, QD, att_s, sc_o, w.fo);
             else
-                e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s);
+                e = launch_matmul(w.wo, d.H, QD, att, T, nullptr, d.eps, 1, x, s, w.fo);
             if (e != hipSuccess) return e;
         }
         if (gemm) {
@@ -314,15 +316,15 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
                 return e;
             pend = 0;
             if ((e = launch_gemm_gateup(d, w, u, h_s, T, s, sc_h_out)) != hipSuccess) return e;
-            e = w.fd != F_Q8_0 ? launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s, sc_h_in)
-                               : gemm_accumulate(w.wd, d.F, h_s, sc_h_in);
+            e = kq_format(w.fd) ? launch_gemm_kq(w.fd, w.wd, d.H, d.F, h_s, true, T, 1, x, s, sc_h_in)
+                                : gemm_accumulate(w.wd, d.F, h_s, sc_h_in, w.fd);
         } else {
             const float *xin = xr[cur];
             const PartSrc ps = take_pending();
             if ((e = launch_gateup(d, w, xin, h, T, s, ps)) != hipSuccess) return e;
             float *xd = xr[cur];
-            if (w.fd == F_Q8_0)
-                e = launch_matmul(w.wd, d.H, d.F, h, T, nullptr, d.eps, 1, xd, s);
+            if (!kq_format(w.fd))
+                e = launch_matmul(w.wd, d.H, d.F, h, T, nullptr, d.eps, 1, xd, s, w.fd);
             else if (T == 1)
                 e = launch_kq_gemv(w.fd, w.wd, d.H, d.F, h, 1, xd, s);
             else
@@ -379,7 +381,8 @@ q8l_status decode_graph(q8l_model *m, int bucket, hipGraphExec_t *out) {
 }
 
 const char *dtype_name(int t) {
-    return t == Q8L_F32 ? "F32" : t == Q8L_Q8_0 ? "Q8_0" : t == Q8L_Q4_K ? "Q4_K" : t == Q8L_Q6_K ? "Q6_K" : "unknown";
+    return t == Q8L_F32 ? "F32" : t == Q8L_Q8_0 ? "Q8_0" : t == Q8L_Q4_K ? "Q4_K" : t == Q8L_Q6_K ? "Q6_K"
+         : t == Q8L_Q5_0 ? "Q5_0" : "unknown";
 }
 
 bool parse_layer_name(const char *name, int *layer, int *slot) {
@@ -482,8 +485,7 @@ q8l_status q8l_create(const q8l_config *cfg, q8l_model **out) {
     // reads the n_head_kv partial rows: only while they are a few KB
     m->fuse_attn_o = attn_o_fits(m->d) && size_t(cfg->n_head_kv) * cfg->n_embd * 4 <= kFuseAttnOMaxBytes;
     m->layer_ptrs.assign(cfg->n_layer, std::vector<const void *>(S_NSLOT, nullptr));
-    m->fmt_o.assign(cfg->n_layer, F_Q8_0);
-    m->fmt_d.assign(cfg->n_layer, F_Q8_0);
+    m->fmt.assign(cfg->n_layer, std::vector<int>(S_NSLOT, F_Q8_0));
     *out = m;
     return Q8L_OK;
 }
@@ -522,25 +524,29 @@ q8l_status q8l_bind_tensor(q8l_model *m, const char *name, q8l_dtype dtype, int6
     } else {
         return fail(m, Q8L_E_INVALID_ARG, std::string("unknown tensor name ") + name);
     }
-    // attn_output and ffn_down may also be Q4_K / Q6_K (rows of whole 256-weight blocks)
+    // attn_output and ffn_down may also be Q4_K / Q6_K (rows of whole 256-weight
+    // blocks); every projection of a layer may be Q5_0
     const bool kquant_ok = layer >= 0 && (s == S_WO || s == S_WD) && ec % kQKK == 0;
+    const bool q5_ok = layer >= 0 && (s == S_WQ || s == S_WK || s == S_WV || s == S_WO || s == S_WG || s == S_WU ||
+                                      s == S_WD);
     if (kquant_ok && (dtype == Q8L_Q4_K || dtype == Q8L_Q6_K)) et = dtype;
-    const size_t want = et == Q8L_F32 ? size_t(er * ec * 4)
-                                      : size_t(er * fmt_row_bytes(et == Q8L_Q4_K ? F_Q4_K : et == Q8L_Q6_K ? F_Q6_K
-                                                                                                            : F_Q8_0,
-                                                                  ec));
+    if (q5_ok && dtype == Q8L_Q5_0) et = dtype;
+    const int ef = et == Q8L_Q4_K ? F_Q4_K : et == Q8L_Q6_K ? F_Q6_K : et == Q8L_Q5_0 ? F_Q5_0 : F_Q8_0;
+    const size_t want = et == Q8L_F32 ? size_t(er * ec * 4) : size_t(er * fmt_row_bytes(ef, ec));
     if (dtype != et || rows != er || cols != ec || nbytes != want) {
         char buf[320];
+        const char *allowed = et != Q8L_Q8_0 ? dtype_name(et)
+                              : kquant_ok && q5_ok ? "Q8_0, Q5_0, Q4_K or Q6_K"
+                              : kquant_ok          ? "Q8_0, Q4_K or Q6_K"
+                              : q5_ok              ? "Q8_0 or Q5_0"
+                                                   : "Q8_0";
         std::snprintf(buf, sizeof buf, "%s: expected %s [%lld, %lld] (%zu bytes), got %s [%lld, %lld] (%zu bytes)",
-                      name, kquant_ok && et == Q8L_Q8_0 ? "Q8_0, Q4_K or Q6_K" : dtype_name(et), (long long)er,
-                      (long long)ec, want, dtype_name(dtype), (long long)rows, (long long)cols, nbytes);
+                      name, allowed, (long long)er, (long long)ec, want, dtype_name(dtype), (long long)rows,
+                      (long long)cols, nbytes);
         return fail(m, Q8L_E_SHAPE, buf);
     }
     *slot = dev_ptr;
-    if (layer >= 0 && (s == S_WO || s == S_WD)) {
-        const int f = et == Q8L_Q4_K ? F_Q4_K : et == Q8L_Q6_K ? F_Q6_K : F_Q8_0;
-        (s == S_WO ? m->fmt_o : m->fmt_d)[layer] = f;
-    }
+    if (layer >= 0 && et != Q8L_F32) m->fmt[layer][s] = ef;
     return Q8L_OK;
 }
 
@@ -569,6 +575,9 @@ q8l_status q8l_finalize(q8l_model *m, void *stream) {
     if (!m->out_norm) return fail(m, Q8L_E_MISSING_TENSOR, "cannot find output_norm.weight");
     if (!m->cfg.tied_output && !m->output) return fail(m, Q8L_E_MISSING_TENSOR, "cannot find output.weight");
     if (!m->ws) return fail(m, Q8L_E_MISSING_TENSOR, "no workspace bound");
+    for (int l = 0; l < m->cfg.n_layer; ++l)   // gate and up run as one product
+        if (m->fmt[l][S_WG] != m->fmt[l][S_WU])
+            return fail(m, Q8L_E_SHAPE, "blk." + std::to_string(l) + ": ffn_gate and ffn_up must share a format");
     hipStream_t s = static_cast<hipStream_t>(stream);
     Q8L_HIP(m, hipMemsetAsync(m->ws + m->lay.state, 0, m->lay.rope - m->lay.state, s), "clearing state");
     Q8L_HIP(m, launch_rope_table(m->at<float2>(m->lay.rope), m->cfg.max_seq_len, m->cfg.head_dim,
@@ -708,14 +717,14 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
                 if (fused && w.fo == F_Q8_0) return launch_attn_o(a, w.wo, d.H, m->at<float>(m->lay.part_o), s);
                 return launch_attn_decode(a, s);
             case 3:
-                if (w.fo != F_Q8_0) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
-                if (m->merge_in_o && oproj_merges(d, a.n_splits))  // as in the step
+                if (kq_format(w.fo)) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
+                if (w.fo == F_Q8_0 && m->merge_in_o && oproj_merges(d, a.n_splits))  // as in the step
                     return launch_oproj_merged(w.wo, d.H, QD, a.part, a.n_splits, d.hd, S, x, s);
-                return launch_matmul(w.wo, d.H, QD, m->at<float>(m->lay.att), 1, nullptr, d.eps, 1, x, s);
+                return launch_matmul(w.wo, d.H, QD, m->at<float>(m->lay.att), 1, nullptr, d.eps, 1, x, s, w.fo);
             case 4: return launch_gateup(d, w, x, h, 1, s, ps_gu);
             case 5:
-                if (w.fd != F_Q8_0) return launch_kq_gemv(w.fd, w.wd, d.H, d.F, h, 1, x, s);
-                return launch_matmul(w.wd, d.H, d.F, h, 1, nullptr, d.eps, 1, x, s);
+                if (kq_format(w.fd)) return launch_kq_gemv(w.fd, w.wd, d.H, d.F, h, 1, x, s);
+                return launch_matmul(w.wd, d.H, d.F, h, 1, nullptr, d.eps, 1, x, s, w.fd);
             case 6: return launch_lmhead(d, wout, m->out_norm, x, S, m->at<float>(m->lay.lm_part), s);
             case 7: return launch_argmax_finish(d, m->at<float>(m->lay.lm_part), S, s);
             default: return launch_noop(s);
@@ -784,6 +793,21 @@ q8l_status q8l_op_matmul_q8_0(const void *W, int64_t N, int64_t K, const float *
     else
         e = launch_matmul(static_cast<const uint8_t *>(W), int(N), int(K), X, int(T), norm_w, float(eps),
                           accumulate, Y, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? Q8L_OK : Q8L_E_HIP;
+}
+
+q8l_status q8l_op_matmul_q5_0(const void *W, int64_t N, int64_t K, const float *X, int64_t T,
+                              int32_t accumulate, float *Y, void *stream) {
+    if (!W || !X || !Y || N < 1 || K < 64 || K % 64 || T < 1 || N > (1 << 30) || K > (1 << 24) ||
+        T > (1 << 20) || (reinterpret_cast<uintptr_t>(W) & 15) || (reinterpret_cast<uintptr_t>(X) & 15))
+        return Q8L_E_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t *w = static_cast<const uint8_t *>(W);
+    const hipError_t e = T > kMaxTokChunk
+                             ? launch_gemm_matmul(w, int(N), int(K), X, false, int(T), accumulate, Y, s, ActScale{},
+                                                  F_Q5_0)
+                             : launch_matmul(w, int(N), int(K), X, int(T), nullptr, 0.f, accumulate, Y, s, F_Q5_0);
+    if (e == hipErrorInvalidValue) return Q8L_E_INVALID_ARG;   // beyond the kernels' 2 GiB addressing
     return e == hipSuccess ? Q8L_OK : Q8L_E_HIP;
 }
 

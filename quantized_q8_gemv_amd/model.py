@@ -17,7 +17,7 @@ class Q8Model:
     """A model bound to the library.
 
     ``config`` is a dict of q8l_config fields; ``tensors`` yields objects with
-    ``name``, ``dtype`` ('q8_0', 'q4_k', 'q6_k' or 'f32'), ``rows``, ``cols``
+    ``name``, ``dtype`` ('q8_0', 'q5_0', 'q4_k', 'q6_k' or 'f32'), ``rows``, ``cols``
     and ``data`` (a host numpy array of the raw bytes / f32 values).
     """
 
@@ -130,7 +130,7 @@ def host_mapped_u32():
     return t, int(dptr.value)
 
 
-_DTYPES = {"f32": C.Q8L_F32, "q8_0": C.Q8L_Q8_0, "q4_k": C.Q8L_Q4_K, "q6_k": C.Q8L_Q6_K}
+_DTYPES = {"f32": C.Q8L_F32, "q8_0": C.Q8L_Q8_0, "q4_k": C.Q8L_Q4_K, "q6_k": C.Q8L_Q6_K, "q5_0": C.Q8L_Q5_0}
 _DTYPE_NAMES = {v: k for k, v in _DTYPES.items()}
 
 

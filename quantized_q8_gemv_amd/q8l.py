@@ -38,6 +38,7 @@ Q8L_F32 = 0
 Q8L_Q8_0 = 1
 Q8L_Q4_K = 2
 Q8L_Q6_K = 3
+Q8L_Q5_0 = 4
 
 Q8L_ROPE_NORM = 0
 Q8L_ROPE_NEOX = 1
@@ -77,6 +78,8 @@ _SIGS = {
     "q8l_destroy": ([_P], None),
     "q8l_op_matmul_q8_0": ([_P, ctypes.c_int64, ctypes.c_int64, _P, ctypes.c_int64, _P,
                             ctypes.c_double, ctypes.c_int32, _P, _P], ctypes.c_int),
+    "q8l_op_matmul_q5_0": ([_P, ctypes.c_int64, ctypes.c_int64, _P, ctypes.c_int64, ctypes.c_int32, _P, _P],
+                           ctypes.c_int),
     "q8l_op_matmul_kq": ([_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _P, ctypes.c_int64,
                           ctypes.c_int32, _P, _P], ctypes.c_int),
     "q8l_op_attention": ([_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -215,6 +218,10 @@ def q8l_op_matmul_q8_0(W, N: int, K: int, X, T: int, norm_w, eps: float, accumul
                        stream=None) -> int:
     return lib().q8l_op_matmul_q8_0(_ptr(W), N, K, _ptr(X), T, _ptr(norm_w), eps, accumulate,
                                     _ptr(Y), _stream(stream))
+
+
+def q8l_op_matmul_q5_0(W, N: int, K: int, X, T: int, accumulate: int, Y, stream=None) -> int:
+    return lib().q8l_op_matmul_q5_0(_ptr(W), N, K, _ptr(X), T, accumulate, _ptr(Y), _stream(stream))
 
 
 def q8l_op_matmul_kq(W, dtype: int, N: int, K: int, X, T: int, accumulate: int, Y, stream=None) -> int:

@@ -167,7 +167,7 @@ def pack_q8_0(scales: np.ndarray, q: np.ndarray) -> np.ndarray:
 @dataclasses.dataclass
 class Tensor:
     name: str
-    dtype: str          # 'q8_0', 'q4_k', 'q6_k' or 'f32'
+    dtype: str          # 'q8_0', 'q5_0', 'q4_k', 'q6_k' or 'f32'
     rows: int
     cols: int
     data: np.ndarray    # block formats: uint8 [rows, row bytes]; f32: float32 [cols]
@@ -255,23 +255,64 @@ def draw_k_quant(rng: np.random.Generator, rows: int, cols: int, fmt: str,
     return body.reshape(rows, nb * size)
 
 
-def with_k_quants(model: Model, o_fmts, d_fmts, seed: int = 7) -> Model:
-    """A copy of ``model`` whose per-layer attn_output / ffn_down matrices are
-    redrawn in the given formats ('q8_0' keeps the original tensor)."""
+# ---- Q5_0 (public GGUF block definition) ------------------------------------
+# 22 bytes per 32 weights: f16 d, a little-endian 32-bit word of fifth bits,
+# 16 bytes of nibbles (low nibbles weights 0..15, high nibbles 16..31).
+Q5_0_BLOCK_BYTES = 22
+
+
+def draw_q5_0(rng: np.random.Generator, rows: int, cols: int, scale_std: float = 0.02) -> np.ndarray:
+    """Random Q5_0 bytes [rows, cols/32 * 22]: f16 scales |z| * scale_std / 15
+    (weights near the Q8_0 draw's magnitude), uniform random fifth-bit words
+    and nibble bytes."""
+    if cols % QK8_0:
+        raise ValueError(f"Q5_0 rows must hold whole 32-weight blocks, got cols={cols}")
+    nb = cols // QK8_0
+    body = rng.integers(0, 256, size=(rows, nb, Q5_0_BLOCK_BYTES), dtype=np.uint8)
+    d = (np.abs(rng.standard_normal((rows, nb))) * (scale_std / 15.0)).astype("<f2")
+    body[:, :, 0:2] = d.view(np.uint8).reshape(rows, nb, 2)
+    return body.reshape(rows, nb * Q5_0_BLOCK_BYTES)
+
+
+def with_formats(model: Model, want: Dict[str, str], seed: int = 7) -> Model:
+    """A copy of ``model`` whose tensors named in ``want`` are redrawn in the
+    given block format ('q5_0', 'q4_k', 'q6_k'; 'q8_0' keeps the original),
+    drawn in canonical tensor order from one stream."""
     rng = np.random.default_rng(seed)
-    L = model.shape.n_layer
-    want = {}
-    for l in range(L):
-        want[f"blk.{l}.attn_output.weight"] = o_fmts[l]
-        want[f"blk.{l}.ffn_down.weight"] = d_fmts[l]
     ts = []
     for t in model.tensors:
         f = want.get(t.name, "q8_0")
-        if t.dtype == "q8_0" and f != "q8_0":
+        if t.dtype == "q8_0" and f == "q5_0":
+            ts.append(Tensor(t.name, f, t.rows, t.cols, draw_q5_0(rng, t.rows, t.cols)))
+        elif t.dtype == "q8_0" and f != "q8_0":
             ts.append(Tensor(t.name, f, t.rows, t.cols, draw_k_quant(rng, t.rows, t.cols, f)))
         else:
             ts.append(t)
     return Model(model.shape, ts)
+
+
+def with_k_quants(model: Model, o_fmts, d_fmts, seed: int = 7) -> Model:
+    """A copy of ``model`` whose per-layer attn_output / ffn_down matrices are
+    redrawn in the given formats ('q8_0' keeps the original tensor)."""
+    want = {}
+    for l in range(model.shape.n_layer):
+        want[f"blk.{l}.attn_output.weight"] = o_fmts[l]
+        want[f"blk.{l}.ffn_down.weight"] = d_fmts[l]
+    return with_formats(model, want, seed)
+
+
+# Per-layer formats of the seven projections, in the order q, k, v, o, gate,
+# up, down.
+LAYER_ROLES = ("attn_q", "attn_k", "attn_v", "attn_output", "ffn_gate", "ffn_up", "ffn_down")
+
+
+def with_layer_formats(model: Model, fmts, seed: int = 7) -> Model:
+    """``fmts[l]`` = seven formats for layer l (q, k, v, o, gate, up, down)."""
+    want = {}
+    for l in range(model.shape.n_layer):
+        for role, f in zip(LAYER_ROLES, fmts[l]):
+            want[f"blk.{l}.{role}.weight"] = f
+    return with_formats(model, want, seed)
 
 
 def prompt_ids(n_vocab: int, length: int, seed: int = 1) -> np.ndarray:
@@ -296,5 +337,6 @@ def shape_fields(shape: ModelShape) -> Dict[str, object]:
 
 __all__ = ["QK8_0", "Q8_0_BLOCK_BYTES", "LAYER_TENSORS", "ModelShape", "TINY", "SMOL135M",
            "BIG_GQA", "Workload", "WORKLOADS", "micro_shape", "draw_q8_0", "pack_q8_0",
-           "Tensor", "Model", "random_model", "K_BLOCK_BYTES", "draw_k_quant", "with_k_quants", "prompt_ids", "workload_inputs", "shape_fields"]
+           "Tensor", "Model", "random_model", "K_BLOCK_BYTES", "draw_k_quant", "with_k_quants", "Q5_0_BLOCK_BYTES", "draw_q5_0",
+           "with_formats", "LAYER_ROLES", "with_layer_formats", "prompt_ids", "workload_inputs", "shape_fields"]
 

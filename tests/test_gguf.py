@@ -237,14 +237,18 @@ def test_unsupported_tensor_type_is_reported_by_name(lib, tmp_path):
         C.q8l_gguf_close(g)
 
 
-@pytest.mark.parametrize("fmt,ftype", [("q5_0", W.TYPE_Q5_0), ("q4_0", W.TYPE_Q4_0)])
-def test_q4_0_and_q5_0_tensors_read_as_exact_q8_0(lib, tmp_path, fmt, ftype):
+@pytest.mark.parametrize("fmt,ftype,name", [("q5_0", W.TYPE_Q5_0, "output.weight"),
+                                            ("q4_0", W.TYPE_Q4_0, "blk.0.ffn_down.weight"),
+                                            ("q4_0", W.TYPE_Q4_0, "token_embd.weight")])
+def test_q4_0_and_q5_0_tensors_read_as_exact_q8_0(lib, tmp_path, fmt, ftype, name):
+    """Q4_0 anywhere, and Q5_0 outside the layers' projections, are read as
+    Q8_0 blocks with the same scale and the block's integers."""
     import oracle
     rng = np.random.default_rng(9)
     rows, cols = 40, 1536
     raw = W.random_blocks(rng, rows, cols, fmt)
     path = str(tmp_path / f"{fmt}.gguf")
-    W.write(path, W.llama_kv(synth.TINY), [("blk.0.ffn_down.weight", ftype, [cols, rows], raw.tobytes())])
+    W.write(path, W.llama_kv(synth.TINY), [(name, ftype, [cols, rows], raw.tobytes())])
     g = C.q8l_gguf_open(path)
     try:
         assert C.q8l_gguf_tensor_file_type(g, 0) == ftype
@@ -260,6 +264,30 @@ def test_q4_0_and_q5_0_tensors_read_as_exact_q8_0(lib, tmp_path, fmt, ftype):
     # ... and decode to the oracle's values of the original format exactly
     ref = oracle.dequant_q5_0(raw, rows, cols) if fmt == "q5_0" else oracle.dequant_q4_0(raw, rows, cols)
     assert np.array_equal(oracle.dequant_q8_0(buf, rows, cols), ref)
+
+
+@pytest.mark.parametrize("role", ["attn_q", "attn_k", "attn_v", "attn_output", "ffn_gate", "ffn_up",
+                                  "ffn_down"])
+def test_q5_0_projections_read_as_they_are(lib, tmp_path, role):
+    rng = np.random.default_rng(13)
+    rows, cols = 24, 576
+    raw = W.random_blocks(rng, rows, cols, "q5_0")
+    other = W.random_blocks(rng, 3, 64, "q5_0")          # 44-byte rows: a tensor not 16-byte sized
+    name = f"blk.2.{role}.weight"
+    path = str(tmp_path / "q5.gguf")
+    W.write(path, W.llama_kv(synth.TINY), [("blk.1.attn_q.weight", W.TYPE_Q5_0, [64, 3], other.tobytes()),
+                                           (name, W.TYPE_Q5_0, [cols, rows], raw.tobytes())])
+    g = C.q8l_gguf_open(path)
+    try:
+        idx = C.q8l_gguf_find_tensor(g, name)
+        st, info = C.q8l_gguf_tensor_info(g, idx)
+        assert st == C.Q8L_OK and info["dtype"] == C.Q8L_Q5_0
+        assert info["nbytes"] == rows * cols // 32 * 22 and (info["rows"], info["cols"]) == (rows, cols)
+        buf = np.empty(info["nbytes"], np.uint8)
+        assert C.q8l_gguf_read_tensor(g, idx, buf, buf.size) == C.Q8L_OK
+        assert np.array_equal(buf, raw.reshape(-1))
+    finally:
+        C.q8l_gguf_close(g)
 
 
 @pytest.mark.parametrize("fmt,ftype,size", [("q4_k", W.TYPE_Q4_K, 144), ("q6_k", W.TYPE_Q6_K, 210)])

@@ -81,7 +81,7 @@ def test_bind_accepts_k_formats_only_for_o_and_down(tiny_handle):
     assert C.q8l_bind_tensor(h, "blk.2.ffn_down.weight", C.Q8L_Q4_K, 576, 1536, FAKE, q6) == C.Q8L_E_SHAPE
     assert "497664 bytes" in C.q8l_last_error(h)
     assert C.q8l_bind_tensor(h, "blk.2.ffn_down.weight", C.Q8L_F32, 576, 1536, FAKE, q6) == C.Q8L_E_SHAPE
-    assert "Q8_0, Q4_K or Q6_K" in C.q8l_last_error(h)
+    assert "Q8_0, Q5_0, Q4_K or Q6_K" in C.q8l_last_error(h)
     assert C.q8l_bind_tensor(h, "blk.0.ffn_gate.weight", C.Q8L_Q4_K, 1536, 576, FAKE, 1536 * 576 // 256 * 144) \
         == C.Q8L_E_SHAPE
     assert C.q8l_bind_tensor(h, "blk.0.attn_output.weight", C.Q8L_Q4_K, 576, 576, FAKE, 576 * 576 // 256 * 144) \
@@ -97,6 +97,33 @@ def test_k_format_op_rejects_bad_arguments_before_device_work():
         a = {**ok, **bad}
         assert C.q8l_op_matmul_kq(a["W"], a["dtype"], a["N"], a["K"], a["X"], a["T"], a["accumulate"],
                                   a["Y"], stream=0) == C.Q8L_E_INVALID_ARG, bad
+
+
+def test_bind_accepts_q5_0_for_every_projection(tiny_handle):
+    """Q5_0 (22 bytes per 32 weights) binds for the seven projections of a
+    layer, not for the embedding, the norms or the output matrix."""
+    h = tiny_handle
+    s = synth.TINY
+    q5 = lambda r, c: r * c // 32 * 22
+    for role, r, c in (("attn_q", s.q_dim, 576), ("attn_k", s.kv_dim, 576), ("attn_v", s.kv_dim, 576),
+                       ("attn_output", 576, s.q_dim), ("ffn_gate", 1536, 576), ("ffn_up", 1536, 576),
+                       ("ffn_down", 576, 1536)):
+        assert C.q8l_bind_tensor(h, f"blk.1.{role}.weight", C.Q8L_Q5_0, r, c, FAKE, q5(r, c)) == C.Q8L_OK, role
+    assert C.q8l_bind_tensor(h, "blk.1.ffn_down.weight", C.Q8L_Q5_0, 576, 1536, FAKE, q5(576, 1536) + 22) \
+        == C.Q8L_E_SHAPE
+    assert "expected Q5_0 [576, 1536] (608256 bytes)" in C.q8l_last_error(h)
+    assert C.q8l_bind_tensor(h, "token_embd.weight", C.Q8L_Q5_0, s.n_vocab, 576, FAKE, q5(s.n_vocab, 576)) \
+        == C.Q8L_E_SHAPE
+    assert C.q8l_bind_tensor(h, "blk.0.attn_norm.weight", C.Q8L_Q5_0, 1, 576, FAKE, 576 * 4) == C.Q8L_E_SHAPE
+
+
+def test_q5_0_op_rejects_bad_arguments_before_device_work():
+    ok = dict(W=FAKE, N=576, K=576, X=FAKE, T=1, accumulate=0, Y=FAKE)
+    for bad in (dict(K=96), dict(K=0), dict(N=0), dict(T=0), dict(T=(1 << 20) + 1), dict(W=FAKE + 4),
+                dict(X=FAKE + 8), dict(W=None), dict(X=None), dict(Y=None)):
+        a = {**ok, **bad}
+        assert C.q8l_op_matmul_q5_0(a["W"], a["N"], a["K"], a["X"], a["T"], a["accumulate"], a["Y"],
+                                    stream=0) == C.Q8L_E_INVALID_ARG, bad
 
 
 def test_finalize_names_the_first_missing_tensor(tiny_handle):

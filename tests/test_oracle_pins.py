@@ -668,3 +668,71 @@ def test_k_quant_oracle_rejects_rows_without_whole_blocks():
           if t.name == "blk.0.ffn_down.weight" else t for t in m.tensors]
     with pytest.raises(ValueError):
         oracle.OracleModel(synth.Model(shape, ts))
+
+
+# ---- Q5_0 on every projection. The values are tied to Q8_0 as above: a
+# Q5_0 block holds d * (integer in [-16, 15]), the same numbers as a Q8_0
+# block with that d and those integers (unpacked here from the bit layout,
+# independently of the oracle's decoder).
+
+def _q5_0_integers(raw: np.ndarray, rows: int, cols: int):
+    """f16 scales [rows, cols/32] and integers [rows, cols] of Q5_0 bytes."""
+    blk = np.ascontiguousarray(raw, dtype=np.uint8).reshape(rows, cols // 32, 22)
+    d = blk[:, :, 0:2].copy().view("<f2").reshape(rows, cols // 32)
+    qh = blk[:, :, 2:6].copy().view("<u4").reshape(rows, cols // 32).astype(np.int64)
+    qs = blk[:, :, 6:22].astype(np.int64)
+    lo = (qs & 15) | (((qh[:, :, None] >> np.arange(16)) & 1) << 4)
+    hi = (qs >> 4) | (((qh[:, :, None] >> (np.arange(16) + 16)) & 1) << 4)
+    ints = np.concatenate([lo, hi], axis=2) - 16
+    return d, ints.reshape(rows, cols).astype(np.int8)
+
+
+def test_q5_0_matmul_equals_its_q8_0_twin():
+    rng = np.random.default_rng(41)
+    rows, cols = 5, 192
+    raw = synth.draw_q5_0(rng, rows, cols)
+    d, ints = _q5_0_integers(raw, rows, cols)
+    assert ints.min() == -16 and ints.max() == 15
+    twin = synth.pack_q8_0(d, ints)
+    x = rng.standard_normal((3, cols))
+    assert np.array_equal(oracle.dequant_q5_0(raw, rows, cols), oracle.dequant_q8_0(twin, rows, cols))
+    assert np.array_equal(oracle.matmul_fmt(raw, "q5_0", rows, cols, x),
+                          oracle.matmul_fmt(twin, "q8_0", rows, cols, x))
+
+
+@pytest.mark.parametrize("pattern", ["all_q5_0", "mixed"])
+def test_q5_0_model_matches_its_q8_0_twin(pattern):
+    """Every projection of a layer may be Q5_0: the logits equal bitwise those
+    of the model with the same matrices stored as Q8_0 (each matrix's format
+    reaches that matrix: a mixed pattern differs per layer and per role)."""
+    shape = synth.micro_shape(n_layer=2, n_embd=64, n_head=4, n_head_kv=2, head_dim=16, n_ff=128)
+    base = synth.random_model(shape, 3)
+    if pattern == "all_q5_0":
+        fmts = [["q5_0"] * 7 for _ in range(shape.n_layer)]
+    else:
+        fmts = [["q5_0", "q8_0", "q5_0", "q8_0", "q5_0", "q5_0", "q8_0"],
+                ["q8_0", "q5_0", "q8_0", "q5_0", "q8_0", "q8_0", "q5_0"]]
+    m5 = synth.with_layer_formats(base, fmts, seed=9)
+    twins = []
+    for t in m5.tensors:
+        if t.dtype == "q5_0":
+            d, ints = _q5_0_integers(t.data, t.rows, t.cols)
+            twins.append(synth.Tensor(t.name, "q8_0", t.rows, t.cols, synth.pack_q8_0(d, ints)))
+        else:
+            twins.append(t)
+    mq = synth.Model(shape, twins)
+    assert sum(t.dtype == "q5_0" for t in m5.tensors) == sum(f == "q5_0" for r in fmts for f in r)
+    toks = synth.prompt_ids(shape.n_vocab, 6, seed=2)
+    a = oracle.OracleModel(m5).forward(toks, 0)[2]
+    b = oracle.OracleModel(mq).forward(toks, 0)[2]
+    assert np.array_equal(a, b)
+    # and the Q5_0 matrices matter: the base model's logits differ
+    assert not np.array_equal(a, oracle.OracleModel(base).forward(toks, 0)[2])
+
+
+def test_k_formats_only_for_o_and_down():
+    shape = synth.micro_shape(n_embd=256, n_ff=256)
+    m = synth.random_model(shape, 0)
+    bad = synth.with_formats(m, {"blk.0.attn_q.weight": "q4_k"})
+    with pytest.raises(ValueError):
+        oracle.OracleModel(bad)
