@@ -58,7 +58,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-FORMAT_BYTES = {"q8_0": (32, 34), "q4_k": (256, 144), "q6_k": (256, 210)}   # (weights, bytes) per block
+FORMAT_BYTES = {"q8_0": (32, 34), "q5_0": (32, 22), "q4_k": (256, 144), "q6_k": (256, 210)}  # (weights, bytes)
 # The pages' Metal figures for these workloads, on an Apple M2 Max -- another
 # machine, quoted as context:
 #   C2: 20 decode steps after a 13-token prompt, 2.6 ms mean per step incl. the
@@ -92,10 +92,10 @@ def decode_fused(s, kv_len, o_fmt="q8_0"):
     """Whether a decode step at this cache length runs the attention and the
     o-projection as one kernel (the runtime's rule: one attention split, the
     group's columns in whole 64-weight pairs, at most 16 KB of per-group
-    partial rows, a Q8_0 o-projection)."""
+    partial rows, a Q8_0 or Q5_0 o-projection)."""
     G = s.n_head // s.n_head_kv
     return (kv_len <= attn_chunk(s.head_dim) and (G * s.head_dim) % 64 == 0 and G * s.head_dim // 64 <= 256
-            and s.n_head_kv * s.n_embd * 4 <= 16 * 1024 and o_fmt == "q8_0")
+            and s.n_head_kv * s.n_embd * 4 <= 16 * 1024 and o_fmt in ("q8_0", "q5_0"))
 
 
 def kernel_symbols(s, down_fmt="q8_0", kv_len=1):
@@ -630,6 +630,76 @@ def measure_config(key, cpu_seconds, with_cpu):
     return out
 
 
+def q5_0_as_q8_0(raw, rows, cols):
+    """Q5_0 blocks rewritten as Q8_0 blocks with the same scale and the
+    block's integers (nibble | fifth bit << 4) - 16: the same weights, the
+    layout the library used before it streamed Q5_0 as it is."""
+    import numpy as np
+
+    import synth
+    nb = cols // 32
+    blk = raw.reshape(rows, nb, 22)
+    d = blk[:, :, 0:2].copy().view("<f2").reshape(rows, nb)
+    qh = blk[:, :, 2:6].copy().view("<u4").reshape(rows, nb)
+    qs = blk[:, :, 6:22]
+    bits = lambda first: (((qh[:, :, None] >> (np.arange(16, dtype=np.uint32) + first)) & 1) << 4).astype(np.uint8)
+    q = np.concatenate([(qs & 15) | bits(0), (qs >> 4) | bits(16)], axis=2).astype(np.int16) - 16
+    return synth.pack_q8_0(d, q.reshape(rows, cols).astype(np.int8))
+
+
+# The pages' 4-bit file of the 135M model, per layer: q, k, o, gate and up in
+# Q5_0, v in Q5_0 in every other layer (Q8_0 otherwise), down in Q4_K and Q6_K
+# in alternate layers ("速度", section "CPU GGUF").
+def q4_k_m_layer(l):
+    return ["q5_0", "q5_0", "q5_0" if l % 2 else "q8_0", "q5_0", "q5_0", "q5_0", "q4_k" if l % 2 == 0 else "q6_k"]
+
+
+def q5_compare(reps=5):
+    """Decode with Q5_0 weights streamed as they are against the same
+    weights expanded to Q8_0, at the 135M shape (13-token prompt, 20 steps)
+    and the 7B-class one (128 + 32): every projection in Q5_0, and the pages'
+    4-bit mix. One JSON line per (shape, mix, layout): weight and cache bytes
+    per token, device-loop us/token (q8l_generate, HIP events; median of
+    `reps` fresh-cache reps) and the HBM rate it implies."""
+    import torch
+
+    import synth
+    from quantized_q8_gemv_amd.model import Q8Model
+
+    for key in ("C2", "C5"):
+        w = synth.WORKLOADS[key]
+        s = w.model
+        prompt = synth.prompt_ids(s.n_vocab, w.prompt_len, w.prompt_seed)
+        steps = w.decode_steps
+        for mix in ("all_q5_0", "q4_k_m"):
+            fmts = [["q5_0"] * 7 if mix == "all_q5_0" else q4_k_m_layer(l) for l in range(s.n_layer)]
+            t0 = time.perf_counter()
+            native = synth.random_model_formats(s, w.seed, fmts)
+            expanded = synth.Model(s, [synth.Tensor(t.name, "q8_0", t.rows, t.cols,
+                                                    q5_0_as_q8_0(t.data, t.rows, t.cols))
+                                       if t.dtype == "q5_0" else t for t in native.tensors])
+            eprint(f"[bench] {key} {mix}: models drawn in {time.perf_counter() - t0:.1f} s")
+            for layout, model in (("q5_0 native", native), ("q5_0 expanded to q8_0", expanded)):
+                gm = Q8Model(synth.shape_fields(s), model.tensors, device="cuda:0")
+                torch.cuda.synchronize()
+                device_loop(gm, prompt, steps, 1)   # warm-up: builds the decode graphs
+                per_tok = [r[0] for r in device_loop(gm, prompt, steps, reps)]
+                ms = statistics.median(per_tok)
+                W = per_token_weight_bytes(model)
+                b_tok = W + kv_bytes_per_position(s) * (len(prompt) + (steps + 1) / 2.0)
+                line = {"mode": "q5_compare", "model": s.name, "mix": mix, "layout": layout,
+                        "prompt_len": len(prompt), "decode_steps": steps, "reps": reps,
+                        "weight_bytes_per_token": int(W), "bytes_per_token": int(b_tok),
+                        "us_per_token": round(ms * 1e3, 2), "us_per_token_min": round(min(per_tok) * 1e3, 2),
+                        "hbm_gbs": round(b_tok / (ms * 1e-3) / 1e9, 1),
+                        "step_frac": round(b_tok / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                print(json.dumps(line), flush=True)
+                del gm
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+            del native, expanded
+
+
 KV_SWEEP = [16, 64, 256, 1024, 2048, 4000]
 
 
@@ -704,6 +774,9 @@ def main():
                     help="measure only the --config workload (no per-workload block for the others)")
     ap.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
                     help="print the profiles/ table of a rocprofv3 kernel_stats.csv; no GPU use")
+    ap.add_argument("--q5-compare", action="store_true",
+                    help="decode with Q5_0 weights as they are against the same weights expanded to Q8_0, "
+                         "at the 135M and 7B-class shapes, instead (one JSON line per case)")
     ap.add_argument("--kv-sweep", action="store_true",
                     help="decode cost against cache length on the 135M-shaped model instead "
                          "(one JSON line per length)")
@@ -719,6 +792,9 @@ def main():
         return
     if args.kv_sweep:
         kv_sweep(args.kernel_reps)
+        return
+    if args.q5_compare:
+        q5_compare()
         return
     if args.formats:
         import torch

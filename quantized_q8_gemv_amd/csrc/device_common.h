@@ -140,15 +140,39 @@ __device__ __forceinline__ float block_dot(const float *q, const float *x) {
     return (s0 + s1) + (s2 + s3);
 }
 
-// pair_dot1 for a Q5_0 pair: decode the pair, then block_dot per block.
+// One Q5_0 pair against one activation row, decoding on the fly (as
+// pair_dot1; same values and summation order as decode_pair_q5 + block_dot:
+// weights 0..15 of a block are the low nibbles, 16..31 the high ones).
+__device__ __forceinline__ float q5_block_dot(const uint32_t qs[4], uint32_t qh, const float *x) {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t u = q5_bytes(qs[j], qh, j, h != 0);
+            const float4 xv = *reinterpret_cast<const float4 *>(x + 16 * h + 4 * j);
+            s0 = fmaf(ubyte_f(u, 0) - 16.0f, xv.x, s0);
+            s1 = fmaf(ubyte_f(u, 1) - 16.0f, xv.y, s1);
+            s2 = fmaf(ubyte_f(u, 2) - 16.0f, xv.z, s2);
+            s3 = fmaf(ubyte_f(u, 3) - 16.0f, xv.w, s3);
+        }
+    return (s0 + s1) + (s2 + s3);
+}
+
 __device__ __forceinline__ void pair_dot1_q5(const uint32_t *w, const float *x, float &dA, float &sA, float &dB,
                                              float &sB) {
-    PairQ pq;
-    decode_pair_q5(w, pq);
-    dA = pq.dA;
-    dB = pq.dB;
-    sA = block_dot(pq.q, x);
-    sB = block_dot(pq.q + 32, x + 32);
+    const uint32_t r0 = w[0], r1 = w[1];
+    dA = half_bits_to_float(r0);
+    uint32_t qa[4];
+    qa[0] = __builtin_amdgcn_alignbyte(w[2], r1, 2);
+#pragma unroll
+    for (int j = 1; j < 4; ++j) qa[j] = __builtin_amdgcn_alignbyte(w[j + 2], w[j + 1], 2);
+    sA = q5_block_dot(qa, __builtin_amdgcn_alignbyte(r1, r0, 2), x);
+    dB = half_bits_to_float(w[5] >> 16);
+    uint32_t qb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qb[j] = w[7 + j];
+    sB = q5_block_dot(qb, w[6], x + 32);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

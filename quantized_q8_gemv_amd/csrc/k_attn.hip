@@ -179,8 +179,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_decode(AttnDecodeArgs a) {
 // sum_g part[g] is the prologue of the next kernel with a norm in front. Every
 // workgroup of a group recomputes the same attention (at most one split of
 // keys: a few KB of K/V from L2); the workgroup's W_o pairs are loaded into
-// registers first and are in flight during the attention.
-__global__ __launch_bounds__(kThreads) void k_attn_o1(AttnODecodeArgs b) {
+// registers first and are in flight during the attention. FMT: W_o's block
+// format (Q8_0 or Q5_0 pairs).
+template <int FMT>
+__device__ __forceinline__ void attn_o_body(const AttnODecodeArgs &b) {
+    constexpr int PB = FMT == F_Q5_0 ? kQ5PairBytes : kPairBytes;
     extern __shared__ __align__(16) uint8_t smem[];
     const AttnDecodeArgs &a = b.at;
     const int tid = threadIdx.x;
@@ -190,13 +193,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_o1(AttnODecodeArgs b) {
     const int P = a.nh * hd / kPairWeights; // pairs per row
     const int nr = min(b.rows, b.N - r0);
     const int units = nr * Pg;              // <= kThreads (host-checked)
-    uint32_t w[kPairBytes / 4];
+    uint32_t w[PB / 4];
     if (tid < units) {
         const int r = tid / Pg, p = tid - r * Pg;
         const uint32_t *src =
-            reinterpret_cast<const uint32_t *>(b.wo + (size_t(r0 + r) * P + size_t(g) * Pg + p) * kPairBytes);
+            reinterpret_cast<const uint32_t *>(b.wo + (size_t(r0 + r) * P + size_t(g) * Pg + p) * PB);
 #pragma unroll
-        for (int i = 0; i < kPairBytes / 4; ++i) w[i] = src[i];
+        for (int i = 0; i < PB / 4; ++i) w[i] = src[i];
     }
     const DecodeLds L = carve_decode(smem, G, hd);
     float *xs = reinterpret_cast<float *>(smem + attn_o_xs_offset(G, hd));  // Pg * kOPad: the group's output
@@ -209,7 +212,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_o1(AttnODecodeArgs b) {
     __syncthreads();
     if (tid < units) {
         float dA, sA, dB, sB;
-        pair_dot1(w, xs + (tid % Pg) * kOPad, dA, sA, dB, sB);
+        if (FMT == F_Q5_0)
+            pair_dot1_q5(w, xs + (tid % Pg) * kOPad, dA, sA, dB, sB);
+        else
+            pair_dot1(w, xs + (tid % Pg) * kOPad, dA, sA, dB, sB);
         red[tid] = fmaf(dB, sB, dA * sA);
     }
     __syncthreads();
@@ -219,6 +225,9 @@ __global__ __launch_bounds__(kThreads) void k_attn_o1(AttnODecodeArgs b) {
         b.part[size_t(g) * b.N + r0 + r] = v;
     }
 }
+
+__global__ __launch_bounds__(kThreads) void k_attn_o1(AttnODecodeArgs b) { attn_o_body<F_Q8_0>(b); }
+__global__ __launch_bounds__(kThreads) void k_attn_o1_q5(AttnODecodeArgs b) { attn_o_body<F_Q5_0>(b); }
 
 // Merge the split partials of the decode attention into O: one workgroup per
 // query head. The split weights w_s = exp(m_s - M) (M = max over splits) are
@@ -668,17 +677,18 @@ int attn_o_rows(const Dims &d) {
     return std::max(1, std::min(rows, kThreads / Pg));
 }
 
-hipError_t launch_attn_o(const AttnDecodeArgs &a, const uint8_t *wo, int N, float *part, hipStream_t s) {
+hipError_t launch_attn_o(const AttnDecodeArgs &a, const uint8_t *wo, int N, float *part, hipStream_t s, int fmt) {
     Dims d{};
     d.H = N; d.nh = a.nh; d.nkv = a.nkv; d.hd = a.hd;
-    if (!attn_o_fits(d)) return hipErrorInvalidValue;
+    if (!attn_o_fits(d) || (fmt != F_Q8_0 && fmt != F_Q5_0)) return hipErrorInvalidValue;
     AttnODecodeArgs b;
     b.at = a;
     b.wo = wo; b.N = N; b.part = part;
 
     b.rows = attn_o_rows(d);
     const int chunks = (N + b.rows - 1) / b.rows;
-    hipLaunchKernelGGL(k_attn_o1, dim3(chunks * a.nkv), dim3(kThreads), attn_o_lds(a.nh / a.nkv, a.hd, b.rows), s, b);
+    hipLaunchKernelGGL(fmt == F_Q5_0 ? k_attn_o1_q5 : k_attn_o1, dim3(chunks * a.nkv), dim3(kThreads),
+                       attn_o_lds(a.nh / a.nkv, a.hd, b.rows), s, b);
     return hipGetLastError();
 }
 

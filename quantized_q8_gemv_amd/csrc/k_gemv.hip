@@ -104,6 +104,21 @@ struct WStage {
     u32x4 v[kMaxV4];
 };
 
+// Block format of the pairs a kernel instance decodes (PairMode): fixed for
+// PM_Q8 / PM_Q5, the tile's own (sh.pb) for PM_MIXED.
+template <int PM>
+__device__ __forceinline__ bool pm_q5(const GemvShape &sh) {
+    return PM == PM_Q5 || (PM == PM_MIXED && sh.pb == kQ5PairBytes);
+}
+template <int PM>
+__device__ __forceinline__ int pm_pair_bytes(const GemvShape &sh) {
+    return PM == PM_Q8 ? kPairBytes : PM == PM_Q5 ? kQ5PairBytes : sh.pb;
+}
+template <int PM>
+__device__ __forceinline__ int pm_pair_dwords(const GemvShape &sh) {
+    return pm_pair_bytes<PM>(sh) / 4;
+}
+
 // Whether chunk tiles can be moved with 16-byte loads (all pieces 16-byte
 // aligned and whole). Otherwise (only ragged edge tiles of some shapes) the
 // tile is copied with 4-byte loads at store time (pairs are 4-byte aligned).
@@ -113,6 +128,7 @@ __device__ inline bool tile_vec(const CoreArgs &a, int nrows) {
     return (sh.PC % 4 == 0) && (sh.P % 4 == 0);
 }
 
+template <int PM>
 __device__ inline const uint8_t *tile_src(const CoreArgs &a, int nrows, int c, int i, int unit) {
     // i indexes `unit`-byte pieces of the flat tile
     const GemvShape &sh = a.sh;
@@ -121,30 +137,33 @@ __device__ inline const uint8_t *tile_src(const CoreArgs &a, int nrows, int c, i
         const int m = i >= per_mat ? 1 : 0;
         return a.W[m] + size_t(a.row0) * sh.rowbytes + size_t(i - m * per_mat) * unit;
     }
-    const int per_row = sh.PC * sh.pb / unit;
+    const int pb = pm_pair_bytes<PM>(sh);
+    const int per_row = sh.PC * pb / unit;
     const int per_mat = nrows * per_row;
     const int m = i >= per_mat ? 1 : 0;
     const int ii = i - m * per_mat;
     const int r = ii / per_row, j = ii - r * per_row;
-    return a.W[m] + size_t(a.row0 + r) * sh.rowbytes + size_t(c) * sh.PC * sh.pb + size_t(j) * unit;
+    return a.W[m] + size_t(a.row0 + r) * sh.rowbytes + size_t(c) * sh.PC * pb + size_t(j) * unit;
 }
 
+template <int PM>
 __device__ inline void stage_issue(const CoreArgs &a, int nrows, int c, bool vec, WStage &st) {
     if (!vec) return;
     const int tid = threadIdx.x;
-    const int n16 = a.nmat * nrows * a.sh.PC * a.sh.pb / 16;
+    const int n16 = a.nmat * nrows * a.sh.PC * pm_pair_bytes<PM>(a.sh) / 16;
 #pragma unroll
     for (int k = 0; k < kMaxV4; ++k) {
         const int i = tid + k * kThreads;
         if (i < n16)
-            st.v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(tile_src(a, nrows, c, i, 16)));
+            st.v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(tile_src<PM>(a, nrows, c, i, 16)));
     }
 }
 
+template <int PM>
 __device__ inline void stage_store(const CoreArgs &a, int nrows, int c, bool vec, const WStage &st,
                                    uint32_t *wt) {
     const int tid = threadIdx.x;
-    const int bytes = a.nmat * nrows * a.sh.PC * a.sh.pb;
+    const int bytes = a.nmat * nrows * a.sh.PC * pm_pair_bytes<PM>(a.sh);
     if (vec) {
         u32x4 *d = reinterpret_cast<u32x4 *>(wt);
 #pragma unroll
@@ -155,7 +174,7 @@ __device__ inline void stage_store(const CoreArgs &a, int nrows, int c, bool vec
     } else {
 #pragma unroll 1
         for (int i = tid; i < bytes / 4; i += kThreads)
-            wt[i] = *reinterpret_cast<const uint32_t *>(tile_src(a, nrows, c, i, 4));
+            wt[i] = *reinterpret_cast<const uint32_t *>(tile_src<PM>(a, nrows, c, i, 4));
     }
 }
 
@@ -164,7 +183,7 @@ __device__ inline void stage_store(const CoreArgs &a, int nrows, int c, bool vec
 // Timeline: chunk-0 weight loads are issued first; the activation row is
 // read (and its norm computed) while they are in flight; chunk c+1's loads
 // are issued before chunk c is computed.
-template <int MAXT, bool MULTI = true>
+template <int MAXT, bool MULTI, int PM>
 __device__ void gemv_core(const CoreArgs &a, const Lds &l) {
     const int tid = threadIdx.x;
     const GemvShape &sh = a.sh;
@@ -176,7 +195,7 @@ __device__ void gemv_core(const CoreArgs &a, const Lds &l) {
     const bool vec = tile_vec(a, nrows);
 
     WStage st;
-    stage_issue(a, nrows, 0, vec, st);
+    stage_issue<PM>(a, nrows, 0, vec, st);
 
     // Stage x for chunk c (all of K when x_full); rinv must be ready if norm.
     auto stage_x = [&](int c, bool normalize) {
@@ -265,12 +284,12 @@ __device__ void gemv_core(const CoreArgs &a, const Lds &l) {
 
     for (int c = 0; c < nchunks; ++c) {
         if (!x_full) stage_x(c, a.norm_w != nullptr);
-        stage_store(a, nrows, c, vec, st, l.wt);
-        if (MULTI && c + 1 < nchunks) stage_issue(a, nrows, c + 1, vec, st);
+        stage_store<PM>(a, nrows, c, vec, st, l.wt);
+        if (MULTI && c + 1 < nchunks) stage_issue<PM>(a, nrows, c + 1, vec, st);
         __syncthreads();
         if (tid < units) {
-            const uint32_t *wp = l.wt + size_t(tid) * (sh.pb / 4);
-            const bool q5 = sh.pb == kQ5PairBytes;
+            const uint32_t *wp = l.wt + size_t(tid) * pm_pair_dwords<PM>(sh);
+            const bool q5 = pm_q5<PM>(sh);
             if constexpr (MAXT == 1) {
                 float dA, sA, dB, sB;
                 if (q5)
@@ -351,8 +370,8 @@ struct QkvArgs {
     uint32_t *range_flag;
 };
 
-template <int MAXT, bool MULTI>
-__global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
+template <int MAXT, bool MULTI, int PM>
+__device__ __forceinline__ void qkv_multi(QkvArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds l = carve(smem, a.sh, 1, MAXT);
     int tile = blockIdx.x, kind;
@@ -372,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
     c.sh.rowbytes = a.sh.P * (kind == 0 ? a.pb[0] : kind == 1 ? a.pb[1] : a.pb[2]);
     c.row0 = tile * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<MAXT, MULTI>(c, l);
+    gemv_core<MAXT, MULTI, PM>(c, l);
 
     const int nrows = min(a.sh.NR, N - c.row0);
     const int half = nrows >> 1;
@@ -406,6 +425,14 @@ __global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) {
     if (bad && a.range_flag) *a.range_flag = 1u;
 }
 
+// One kernel per block-format mode (PairMode) of each body below.
+template <int MAXT, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_qkv(QkvArgs a) { qkv_multi<MAXT, MULTI, PM_Q8>(a); }
+template <int MAXT, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_qkv_q5(QkvArgs a) { qkv_multi<MAXT, MULTI, PM_Q5>(a); }
+template <int MAXT, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_qkv_mixed(QkvArgs a) { qkv_multi<MAXT, MULTI, PM_MIXED>(a); }
+
 // ---------------------------------------------------------------- gate/up
 
 struct GateUpArgs {
@@ -419,8 +446,8 @@ struct GateUpArgs {
     PartSrc ps;  // decode: split-K partials added to x first (n = 0: none)
 };
 
-template <int MAXT, bool MULTI>
-__global__ __launch_bounds__(kThreads) void k_gateup(GateUpArgs a) {
+template <int MAXT, bool MULTI, int PM>
+__device__ __forceinline__ void gateup_multi(const GateUpArgs &a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds l = carve(smem, a.sh, 2, MAXT);
     const int t0 = blockIdx.y * MAXT;
@@ -428,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void k_gateup(GateUpArgs a) {
     c.W[0] = a.wg; c.W[1] = a.wu; c.nmat = 2; c.sh = a.sh; c.N = a.F;
     c.row0 = blockIdx.x * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<MAXT, MULTI>(c, l);
+    gemv_core<MAXT, MULTI, PM>(c, l);
     const int nrows = min(a.sh.NR, a.F - c.row0);
     for (int e = threadIdx.x; e < c.Tc * nrows; e += kThreads) {
         const int t = e / nrows, r = e - t * nrows;
@@ -437,6 +464,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup(GateUpArgs a) {
         a.h[size_t(t0 + t) * a.F + c.row0 + r] = silu(g) * u;
     }
 }
+
+template <int MAXT, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_gateup(GateUpArgs a) { gateup_multi<MAXT, MULTI, PM_Q8>(a); }
+template <int MAXT, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_gateup_q5(GateUpArgs a) { gateup_multi<MAXT, MULTI, PM_Q5>(a); }
 
 // ---------------------------------------------------------------- generic (o, down, op)
 
@@ -453,8 +485,8 @@ struct MatmulArgs {
     const StepState *mst;
 };
 
-template <int MAXT, bool MULTI>
-__global__ __launch_bounds__(kThreads) void k_matmul(MatmulArgs a) {
+template <int MAXT, bool MULTI, int PM>
+__device__ __forceinline__ void matmul_multi(const MatmulArgs &a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds l = carve(smem, a.sh, 1, MAXT);
     const int t0 = blockIdx.y * MAXT;
@@ -462,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void k_matmul(MatmulArgs a) {
     c.W[0] = a.W; c.W[1] = nullptr; c.nmat = 1; c.sh = a.sh; c.N = a.N;
     c.row0 = blockIdx.x * a.sh.NR; c.Tc = min(MAXT, a.T - t0);
     c.X = a.x + size_t(t0) * a.sh.K; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    gemv_core<MAXT, MULTI>(c, l);
+    gemv_core<MAXT, MULTI, PM>(c, l);
     const int nrows = min(a.sh.NR, a.N - c.row0);
     for (int e = threadIdx.x; e < c.Tc * nrows; e += kThreads) {
         const int t = e / nrows, r = e - t * nrows;
@@ -471,6 +503,11 @@ __global__ __launch_bounds__(kThreads) void k_matmul(MatmulArgs a) {
         *dst = a.accumulate ? *dst + v : v;
     }
 }
+
+template <int MAXT, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_matmul(MatmulArgs a) { matmul_multi<MAXT, MULTI, PM_Q8>(a); }
+template <int MAXT, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_matmul_q5(MatmulArgs a) { matmul_multi<MAXT, MULTI, PM_Q5>(a); }
 
 // ---------------------------------------------------------------- output layer + argmax
 
@@ -782,6 +819,7 @@ __device__ void stage_row1(const CoreArgs &a, const Lds1 &l, PartSrc ps = PartSr
 // (d * q) * u (d * q is exact in f32) in pair order; the lanes are summed
 // by wave_sum_dpp. Fewer barriers and a short chain per lane, for tiles that
 // would leave most threads idle one pair per thread.
+template <int PM>
 __device__ __forceinline__ void rows_dot1(const CoreArgs &c, const Lds1 &l, int nrows) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const GemvShape &sh = c.sh;
@@ -793,7 +831,7 @@ __device__ __forceinline__ void rows_dot1(const CoreArgs &c, const Lds1 &l, int 
             l.outv[m * sh.NR + r] = v;
         }
     };
-    if (sh.pb == kQ5PairBytes) {
+    if (pm_q5<PM>(sh)) {
         // Q5_0: weight j = lane % 32 of block 2i + lane / 32 (nibble j / 16 of
         // byte 6 + j % 16, fifth bit j of the word at byte 2)
         const uint8_t *wt = reinterpret_cast<const uint8_t *>(l.wt) + (lane >> 5) * kQ5Bytes;
@@ -851,7 +889,7 @@ __device__ __forceinline__ void rows_dot1(const CoreArgs &c, const Lds1 &l, int 
 // One row tile: outv[m*NR + r] = sum_k W_m[row0+r][k] * u[k]. Chunk 0 of this
 // tile is already in `st`; the next tile's chunk 0 is issued during the last
 // chunk (when has_next).
-template <bool MULTI>
+template <bool MULTI, int PM>
 __device__ void tile_run1(const CoreArgs &c, const Lds1 &l, int nrows, bool vec, WStage &st,
                           const CoreArgs &n, int nn, bool nvec, bool has_next) {
     const int tid = threadIdx.x;
@@ -860,10 +898,10 @@ __device__ void tile_run1(const CoreArgs &c, const Lds1 &l, int nrows, bool vec,
     const int units = c.nmat * per_mat;
     if constexpr (!MULTI) {
         if (2 * units <= kThreads) {
-            stage_store(c, nrows, 0, vec, st, l.wt);
-            if (has_next) stage_issue(n, nn, 0, nvec, st);
+            stage_store<PM>(c, nrows, 0, vec, st, l.wt);
+            if (has_next) stage_issue<PM>(n, nn, 0, nvec, st);
             __syncthreads();
-            rows_dot1(c, l, nrows);
+            rows_dot1<PM>(c, l, nrows);
             __syncthreads();
             return;
         }
@@ -872,17 +910,17 @@ __device__ void tile_run1(const CoreArgs &c, const Lds1 &l, int nrows, bool vec,
     const int up = tid < units ? (tid % per_mat) % sh.PC : 0;
     float acc = 0.f;
     for (int ch = 0; ch < nchunks; ++ch) {
-        stage_store(c, nrows, ch, vec, st, l.wt);
+        stage_store<PM>(c, nrows, ch, vec, st, l.wt);
         if (MULTI && ch + 1 < nchunks)
-            stage_issue(c, nrows, ch + 1, vec, st);
+            stage_issue<PM>(c, nrows, ch + 1, vec, st);
         else if (has_next)
-            stage_issue(n, nn, 0, nvec, st);
+            stage_issue<PM>(n, nn, 0, nvec, st);
         __syncthreads();
         if (tid < units) {
             float dA, sA, dB, sB;
-            const uint32_t *wp = l.wt + size_t(tid) * (sh.pb / 4);
+            const uint32_t *wp = l.wt + size_t(tid) * pm_pair_dwords<PM>(sh);
             const float *xp = l.xs + size_t(ch * sh.PC + up) * kXPad;
-            if (sh.pb == kQ5PairBytes)
+            if (pm_q5<PM>(sh))
                 pair_dot1_q5(wp, xp, dA, sA, dB, sB);
             else
                 pair_dot1(wp, xp, dA, sA, dB, sB);
@@ -916,7 +954,7 @@ __device__ inline int tile_rows(const CoreArgs &c) { return min(c.sh.NR, c.N - c
 // weights are in LDS, into the registers tile t used (two register stages,
 // alternating). The activation row is staged while the first two tiles load.
 // epi(tile, rows) consumes outv after each tile.
-template <bool MULTI, bool MERGE = false, class Epi>
+template <bool MULTI, bool MERGE, int PM, class Epi>
 __device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, int ntiles, Epi &&epi,
                                             const MergeSrc *ms = nullptr, PartSrc ps = PartSrc{}) {
     const int G = int(gridDim.x);
@@ -933,21 +971,21 @@ __device__ __forceinline__ void walk_tiles2(const CoreArgs &c, const Lds1 &l, in
     at(t, ca, na, va);
     at(t + G, cb, nb, vb);
     WStage sa, sb;
-    if (na > 0) stage_issue(ca, na, 0, va, sa);
-    if (nb > 0) stage_issue(cb, nb, 0, vb, sb);
+    if (na > 0) stage_issue<PM>(ca, na, 0, va, sa);
+    if (nb > 0) stage_issue<PM>(cb, nb, 0, vb, sb);
     if constexpr (MERGE)
         stage_merged1(c, *ms, l);
     else
         stage_row1(c, l, ps);
     while (t < ntiles) {
         at(t + 2 * G, n, nn, nv);
-        tile_run1<MULTI>(ca, l, na, va, sa, n, nn, nv, nn > 0);
+        tile_run1<MULTI, PM>(ca, l, na, va, sa, n, nn, nv, nn > 0);
         epi(ca, na);
         ca = n; na = nn; va = nv;
         t += G;
         if (t >= ntiles) break;
         at(t + 2 * G, n, nn, nv);
-        tile_run1<MULTI>(cb, l, nb, vb, sb, n, nn, nv, nn > 0);
+        tile_run1<MULTI, PM>(cb, l, nb, vb, sb, n, nn, nv, nn > 0);
         epi(cb, nb);
         cb = n; nb = nn; vb = nv;
         t += G;
@@ -997,8 +1035,8 @@ __device__ void stage_embed1(const QkvArgs &a, const CoreArgs &c, const Lds1 &l)
     }
 }
 
-template <bool MULTI>
-__global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
+template <bool MULTI, int PM>
+__device__ __forceinline__ void qkv_one(const QkvArgs &a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds1 l = carve1(smem, a.sh, 1);
     const int ntiles = a.tq + 2 * a.tk;
@@ -1022,7 +1060,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
     int nrows = tile_rows(c);
     bool vec = tile_vec(c, nrows);
     WStage st;
-    stage_issue(c, nrows, 0, vec, st);
+    stage_issue<PM>(c, nrows, 0, vec, st);
     const int pos = a.st->pos, slot = a.st->slot;   // in flight with the weights and the row
     if (a.embed)
         stage_embed1(a, c, l);
@@ -1041,7 +1079,7 @@ __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
         const bool rot = kind != 2 && !a.rope_neox;
         float2 cs = make_float2(1.f, 0.f);
         if (rot && e < nrows / 2) cs = a.rope[size_t(pos) * (a.hd / 2) + (((c.row0 + 2 * e) % a.hd) >> 1)];
-        tile_run1<MULTI>(c, l, nrows, vec, st, n, nn, nvec, has_next);
+        tile_run1<MULTI, PM>(c, l, nrows, vec, st, n, nn, nvec, has_next);
         if (e < nrows / 2) {
             const int r = 2 * e;
             const float a0 = l.outv[r], a1 = l.outv[r + 1];
@@ -1067,14 +1105,21 @@ __global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) {
 }
 
 template <bool MULTI>
-__global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) {
+__global__ __launch_bounds__(kThreads) void k_qkv1(QkvArgs a) { qkv_one<MULTI, PM_Q8>(a); }
+template <bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_qkv1_q5(QkvArgs a) { qkv_one<MULTI, PM_Q5>(a); }
+template <bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_qkv1_mixed(QkvArgs a) { qkv_one<MULTI, PM_MIXED>(a); }
+
+template <bool MULTI, int PM>
+__device__ __forceinline__ void gateup_one(const GateUpArgs &a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds1 l = carve1(smem, a.sh, 2);
     const int ntiles = (a.F + a.sh.NR - 1) / a.sh.NR;
     CoreArgs c{};
     c.W[0] = a.wg; c.W[1] = a.wu; c.nmat = 2; c.sh = a.sh; c.N = a.F; c.Tc = 1;
     c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
-    walk_tiles2<MULTI>(
+    walk_tiles2<MULTI, false, PM>(
         c, l, ntiles,
         [&](const CoreArgs &t, int nrows) {
             for (int r = threadIdx.x; r < nrows; r += kThreads)
@@ -1082,6 +1127,11 @@ __global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) {
         },
         nullptr, a.ps);
 }
+
+template <bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_gateup1(GateUpArgs a) { gateup_one<MULTI, PM_Q8>(a); }
+template <bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_gateup1_q5(GateUpArgs a) { gateup_one<MULTI, PM_Q5>(a); }
 
 // Large K (several chunks), no norm: chunk-outer, tile-inner. Only one
 // activation chunk is in LDS at a time (so more workgroups fit per CU); each
@@ -1097,47 +1147,54 @@ constexpr int kMaxX4 = 10;   // float4 of one activation chunk per thread (chunk
 __device__ inline int chunk_pairs(const GemvShape &sh, int c) { return min(sh.PC, sh.P - c * sh.PC); }
 
 // Piece i (of `unit` bytes) of chunk c's tile: source address and LDS byte offset.
+template <int PM>
 __device__ inline const uint8_t *ctile_src(const uint8_t *W, const GemvShape &sh, int row0, int pcc, int c, int i,
                                            int unit) {
-    const int per_row = pcc * sh.pb / unit;
+    const int pb = pm_pair_bytes<PM>(sh);
+    const int per_row = pcc * pb / unit;
     const int r = i / per_row, j = i - r * per_row;
-    return W + size_t(row0 + r) * sh.rowbytes + size_t(c) * sh.PC * sh.pb + size_t(j) * unit;
+    return W + size_t(row0 + r) * sh.rowbytes + size_t(c) * sh.PC * pb + size_t(j) * unit;
 }
+template <int PM>
 __device__ inline int ctile_dst(const GemvShape &sh, int pcc, int i, int unit) {
-    const int per_row = pcc * sh.pb / unit;
+    const int pb = pm_pair_bytes<PM>(sh);
+    const int per_row = pcc * pb / unit;
     const int r = i / per_row, j = i - r * per_row;
-    return r * sh.PC * sh.pb + j * unit;
+    return r * sh.PC * pb + j * unit;
 }
 __device__ inline bool ctile_vec(const GemvShape &sh, int pcc) {
     return (pcc % 4 == 0) && (sh.PC % 4 == 0) && (sh.P % 4 == 0);
 }
+template <int PM>
 __device__ inline void ctile_issue(const uint8_t *W, const GemvShape &sh, int row0, int nrows, int c, WStage &st) {
     const int pcc = chunk_pairs(sh, c);
     if (!ctile_vec(sh, pcc)) return;
-    const int n16 = nrows * pcc * sh.pb / 16;
+    const int n16 = nrows * pcc * pm_pair_bytes<PM>(sh) / 16;
 #pragma unroll
     for (int k = 0; k < kMaxV4; ++k) {
         const int i = threadIdx.x + k * kThreads;
         if (i < n16)
-            st.v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ctile_src(W, sh, row0, pcc, c, i, 16)));
+            st.v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ctile_src<PM>(W, sh, row0, pcc, c, i, 16)));
     }
 }
+template <int PM>
 __device__ inline void ctile_store(const uint8_t *W, const GemvShape &sh, int row0, int nrows, int c,
                                    const WStage &st, uint32_t *wt) {
     const int pcc = chunk_pairs(sh, c);
+    const int pb = pm_pair_bytes<PM>(sh);
     uint8_t *base = reinterpret_cast<uint8_t *>(wt);
     if (ctile_vec(sh, pcc)) {
-        const int n16 = nrows * pcc * sh.pb / 16;
+        const int n16 = nrows * pcc * pb / 16;
 #pragma unroll
         for (int k = 0; k < kMaxV4; ++k) {
             const int i = threadIdx.x + k * kThreads;
-            if (i < n16) *reinterpret_cast<u32x4 *>(base + ctile_dst(sh, pcc, i, 16)) = st.v[k];
+            if (i < n16) *reinterpret_cast<u32x4 *>(base + ctile_dst<PM>(sh, pcc, i, 16)) = st.v[k];
         }
     } else {
 #pragma unroll 1
-        for (int i = threadIdx.x; i < nrows * pcc * sh.pb / 4; i += kThreads)
-            *reinterpret_cast<uint32_t *>(base + ctile_dst(sh, pcc, i, 4)) =
-                *reinterpret_cast<const uint32_t *>(ctile_src(W, sh, row0, pcc, c, i, 4));
+        for (int i = threadIdx.x; i < nrows * pcc * pb / 4; i += kThreads)
+            *reinterpret_cast<uint32_t *>(base + ctile_dst<PM>(sh, pcc, i, 4)) =
+                *reinterpret_cast<const uint32_t *>(ctile_src<PM>(W, sh, row0, pcc, c, i, 4));
     }
 }
 
@@ -1146,16 +1203,18 @@ __host__ __device__ inline size_t lds1c_bytes(const GemvShape &sh) {
            align16(size_t(sh.NR > 4 ? sh.NR : 4) * 4) + 16;
 }
 
+template <bool Q5>
 __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
+    constexpr int PM = Q5 ? PM_Q5 : PM_Q8;
     extern __shared__ __align__(16) uint8_t smem[];
     const GemvShape &sh = a.sh;
     uint32_t *wt = reinterpret_cast<uint32_t *>(smem);
-    float *xs = reinterpret_cast<float *>(smem + align16(size_t(sh.NR) * sh.PC * sh.pb));
+    float *xs = reinterpret_cast<float *>(smem + align16(size_t(sh.NR) * sh.PC * pm_pair_bytes<PM>(sh)));
     float *outv = xs + align16(size_t(sh.PC) * kXPad * 4) / 4;
     const int tid = threadIdx.x;
     const int ntiles = (a.N + sh.NR - 1) / sh.NR;
     const int nchunks = (sh.P + sh.PC - 1) / sh.PC;
-    const bool q5 = sh.pb == kQ5PairBytes;
+    const bool q5 = pm_q5<PM>(sh);
     int my_tiles = 0;
     for (int k = 0; k < kTilesPerWg; ++k) my_tiles += (int(blockIdx.x) + k * int(gridDim.x) < ntiles) ? 1 : 0;
     float acc[kTilesPerWg];
@@ -1176,7 +1235,7 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
 #pragma unroll
         for (int i = 0; i < kMaxX4; ++i) xr[i] = src[min(tid + i * kThreads, last)];
     }
-    ctile_issue(a.W, sh, row0, nrows, 0, st);
+    ctile_issue<PM>(a.W, sh, row0, nrows, 0, st);
     for (int ch = 0; ch < nchunks; ++ch) {
         const int pcc = chunk_pairs(sh, ch);
         __syncthreads();  // the previous chunk's activations are no longer read
@@ -1201,8 +1260,8 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
                 const bool has_next = nch < nchunks;
                 const int nrow0 = (int(blockIdx.x) + nk * int(gridDim.x)) * sh.NR;
                 const int nn = has_next ? min(sh.NR, a.N - nrow0) : 0;
-                ctile_store(a.W, sh, row0, nrows, ch, st, wt);
-                if (has_next) ctile_issue(a.W, sh, nrow0, nn, nch, st);
+                ctile_store<PM>(a.W, sh, row0, nrows, ch, st, wt);
+                if (has_next) ctile_issue<PM>(a.W, sh, nrow0, nn, nch, st);
                 __syncthreads();
                 const int r = tid / sh.PC, p = tid - r * sh.PC;
                 if (r < nrows && p < pcc) {
@@ -1245,8 +1304,9 @@ __global__ __launch_bounds__(kThreads) void k_matmul1_chunked(MatmulArgs a) {
     }
 }
 
-template <bool MULTI, bool MERGE = false>
-__global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
+
+template <bool MULTI, bool MERGE, int PM>
+__device__ __forceinline__ void matmul_one(const MatmulArgs &a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const Lds1 l = carve1(smem, a.sh, 1);
     const int ntiles = (a.N + a.sh.NR - 1) / a.sh.NR;
@@ -1254,7 +1314,7 @@ __global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
     c.W[0] = a.W; c.nmat = 1; c.sh = a.sh; c.N = a.N; c.Tc = 1;
     c.X = a.x; c.ldx = a.sh.K; c.norm_w = a.norm_w; c.eps = a.eps;
     const MergeSrc ms{a.mpart, a.msplits, a.mhd, a.mst};
-    walk_tiles2<MULTI, MERGE>(
+    walk_tiles2<MULTI, MERGE, PM>(
         c, l, ntiles,
         [&](const CoreArgs &t, int nrows) {
             for (int r = threadIdx.x; r < nrows; r += kThreads) {
@@ -1264,6 +1324,11 @@ __global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) {
         },
         &ms);
 }
+
+template <bool MULTI, bool MERGE = false>
+__global__ __launch_bounds__(kThreads) void k_matmul1(MatmulArgs a) { matmul_one<MULTI, MERGE, PM_Q8>(a); }
+template <bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_matmul1_q5(MatmulArgs a) { matmul_one<MULTI, false, PM_Q5>(a); }
 
 template <bool MULTI>
 __global__ __launch_bounds__(kThreads) void k_lmhead1(LmHeadArgs a) {
@@ -1280,7 +1345,7 @@ __global__ __launch_bounds__(kThreads) void k_lmhead1(LmHeadArgs a) {
     int nrows = tile_rows(c);
     bool vec = tile_vec(c, nrows);
     WStage st;
-    stage_issue(c, nrows, 0, vec, st);
+    stage_issue<PM_Q8>(c, nrows, 0, vec, st);
     stage_row1(c, l, a.ps);
     float *logits = a.st->logits_out;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -1292,7 +1357,7 @@ __global__ __launch_bounds__(kThreads) void k_lmhead1(LmHeadArgs a) {
         n.row0 = (tile + gridDim.x) * a.sh.NR;
         const int nn = has_next ? tile_rows(n) : 0;
         const bool nvec = has_next ? tile_vec(n, nn) : false;
-        tile_run1<MULTI>(c, l, nrows, vec, st, n, nn, nvec, has_next);
+        tile_run1<MULTI, PM_Q8>(c, l, nrows, vec, st, n, nn, nvec, has_next);
         for (int r = tid; r < nrows; r += kThreads) {
             const float v = l.outv[r];
             logits[c.row0 + r] = v;
@@ -1413,20 +1478,23 @@ hipError_t launch_qkv(const Dims &d, const LayerPtrs &w, const float *x, const S
     a.pb[2] = w.fv == F_Q5_0 ? kQ5PairBytes : kPairBytes;
     a.tq = (a.QD + a.sh.NR - 1) / a.sh.NR;
     a.tk = (a.KVD + a.sh.NR - 1) / a.sh.NR;
+    const int pm = pair_mode(w.fq, w.fk, w.fv);
+    const bool multi = a.sh.PC != a.sh.P;
     if (T == 1) {  // decode: row-looping kernel
         const size_t lds = lds1_bytes(a.sh, 1);
         const int g = grid1(a.tq + 2 * a.tk, lds);
-        if (a.sh.PC != a.sh.P)
-            hipLaunchKernelGGL(k_qkv1<true>, dim3(g), dim3(kThreads), lds, s, a);
-        else
-            hipLaunchKernelGGL(k_qkv1<false>, dim3(g), dim3(kThreads), lds, s, a);
+        auto kern = pm == PM_Q8 ? (multi ? k_qkv1<true> : k_qkv1<false>)
+                  : pm == PM_Q5 ? (multi ? k_qkv1_q5<true> : k_qkv1_q5<false>)
+                                : (multi ? k_qkv1_mixed<true> : k_qkv1_mixed<false>);
+        hipLaunchKernelGGL(kern, dim3(g), dim3(kThreads), lds, s, a);
         return hipGetLastError();
     }
     dim3 grid(a.tq + 2 * a.tk, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 1, maxt);
-    const bool multi = a.sh.PC != a.sh.P;
-    if (multi) hipLaunchKernelGGL((k_qkv<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
-    else hipLaunchKernelGGL((k_qkv<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
+    auto kern = pm == PM_Q8 ? (multi ? k_qkv<kMaxTokChunk, true> : k_qkv<kMaxTokChunk, false>)
+              : pm == PM_Q5 ? (multi ? k_qkv_q5<kMaxTokChunk, true> : k_qkv_q5<kMaxTokChunk, false>)
+                            : (multi ? k_qkv_mixed<kMaxTokChunk, true> : k_qkv_mixed<kMaxTokChunk, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -1440,20 +1508,21 @@ hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, floa
     a.wg = w.wg; a.wu = w.wu; a.norm_w = w.ffn_norm; a.x = x; a.h = h; a.F = d.F; a.T = T;
     a.eps = d.eps;
     a.sh = choose_shape(d.F, d.H, maxt, 2, 512, 1, w.fg);
+    const bool q5 = w.fg == F_Q5_0;
+    const bool multi = a.sh.PC != a.sh.P;
     if (T == 1) {
         const size_t lds = lds1_bytes(a.sh, 2);
         const int g = grid1((d.F + a.sh.NR - 1) / a.sh.NR, lds);
-        if (a.sh.PC != a.sh.P)
-            hipLaunchKernelGGL(k_gateup1<true>, dim3(g), dim3(kThreads), lds, s, a);
-        else
-            hipLaunchKernelGGL(k_gateup1<false>, dim3(g), dim3(kThreads), lds, s, a);
+        auto kern = q5 ? (multi ? k_gateup1_q5<true> : k_gateup1_q5<false>)
+                       : (multi ? k_gateup1<true> : k_gateup1<false>);
+        hipLaunchKernelGGL(kern, dim3(g), dim3(kThreads), lds, s, a);
         return hipGetLastError();
     }
     dim3 grid((d.F + a.sh.NR - 1) / a.sh.NR, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 2, maxt);
-    const bool multi = a.sh.PC != a.sh.P;
-    if (multi) hipLaunchKernelGGL((k_gateup<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
-    else hipLaunchKernelGGL((k_gateup<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
+    auto kern = q5 ? (multi ? k_gateup_q5<kMaxTokChunk, true> : k_gateup_q5<kMaxTokChunk, false>)
+                   : (multi ? k_gateup<kMaxTokChunk, true> : k_gateup<kMaxTokChunk, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -1467,6 +1536,8 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
     a.eps = eps;
     a.sh = choose_shape(N, K, maxt, 1, 512, 1, fmt);
     if (T == 1 && !norm_w && wgemv_fits(K)) return launch_wmatmul(W, N, K, X, accumulate, Y, s, fmt);
+    const bool q5 = fmt == F_Q5_0;
+    const bool multi = a.sh.PC != a.sh.P;
     if (T == 1) {
         if (a.sh.PC != a.sh.P && !norm_w) {  // large K: chunk-outer walk
             a.sh = chunked_shape(a.sh);
@@ -1474,22 +1545,22 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
             const size_t lds = lds1c_bytes(a.sh);
             const int ntiles = (N + a.sh.NR - 1) / a.sh.NR;
             const int g = std::max(grid1(ntiles, lds), (ntiles + kTilesPerWg - 1) / kTilesPerWg);
-            hipLaunchKernelGGL(k_matmul1_chunked, dim3(g), dim3(kThreads), lds, s, a);
+            hipLaunchKernelGGL(q5 ? k_matmul1_chunked<true> : k_matmul1_chunked<false>, dim3(g), dim3(kThreads), lds,
+                               s, a);
             return hipGetLastError();
         }
         const size_t lds = lds1_bytes(a.sh, 1);
         const int g = grid1((N + a.sh.NR - 1) / a.sh.NR, lds);
-        if (a.sh.PC != a.sh.P)
-            hipLaunchKernelGGL((k_matmul1<true>), dim3(g), dim3(kThreads), lds, s, a);
-        else
-            hipLaunchKernelGGL((k_matmul1<false>), dim3(g), dim3(kThreads), lds, s, a);
+        auto kern = q5 ? (multi ? k_matmul1_q5<true> : k_matmul1_q5<false>)
+                       : (multi ? k_matmul1<true> : k_matmul1<false>);
+        hipLaunchKernelGGL(kern, dim3(g), dim3(kThreads), lds, s, a);
         return hipGetLastError();
     }
     dim3 grid((N + a.sh.NR - 1) / a.sh.NR, (T + maxt - 1) / maxt);
     const size_t lds = lds_bytes(a.sh, 1, maxt);
-    const bool multi = a.sh.PC != a.sh.P;
-    if (multi) hipLaunchKernelGGL((k_matmul<kMaxTokChunk, true>), grid, dim3(kThreads), lds, s, a);
-    else hipLaunchKernelGGL((k_matmul<kMaxTokChunk, false>), grid, dim3(kThreads), lds, s, a);
+    auto kern = q5 ? (multi ? k_matmul_q5<kMaxTokChunk, true> : k_matmul_q5<kMaxTokChunk, false>)
+                   : (multi ? k_matmul<kMaxTokChunk, true> : k_matmul<kMaxTokChunk, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 

@@ -237,19 +237,30 @@ __device__ __forceinline__ void wqkv_body(const WQkvArgs &a, int kind, int lrow)
     }
 }
 
-template <int P>
-__global__ __launch_bounds__(kThreads) void k_wqkv1(WQkvArgs a) {
+template <int P, int PM>
+__device__ __forceinline__ void wqkv_kernel(WQkvArgs a) {
     const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
     const int N = a.QD + 2 * a.KVD;
     if (2 * e >= N) return;   // (no barriers in this kernel)
     const int row = 2 * e;
     const int kind = row < a.QD ? 0 : row < a.QD + a.KVD ? 1 : 2;
     const int lrow = kind == 0 ? row : kind == 1 ? row - a.QD : row - a.QD - a.KVD;
-    if ((kind == 0 ? a.fmt[0] : kind == 1 ? a.fmt[1] : a.fmt[2]) == F_Q5_0)
+    const bool q5 = PM == PM_Q5 || (PM == PM_MIXED && (kind == 0 ? a.fmt[0] == F_Q5_0
+                                                        : kind == 1 ? a.fmt[1] == F_Q5_0
+                                                                    : a.fmt[2] == F_Q5_0));
+    if (q5)
         wqkv_body<P, F_Q5_0>(a, kind, lrow);
     else
         wqkv_body<P, F_Q8_0>(a, kind, lrow);
 }
+
+// One kernel per block-format mode (PairMode).
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wqkv1(WQkvArgs a) { wqkv_kernel<P, PM_Q8>(a); }
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wqkv1_q5(WQkvArgs a) { wqkv_kernel<P, PM_Q5>(a); }
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wqkv1_mixed(WQkvArgs a) { wqkv_kernel<P, PM_MIXED>(a); }
 
 // ---------------------------------------------------------------- gate/up
 
@@ -261,7 +272,6 @@ struct WGateUpArgs {
     int F;
     float eps;
     PartSrc ps;
-    int fmt;   // WFmt of gate and up (one format)
 };
 
 // Wave w of workgroup b: row f = 4 b + w of gate and of up; h[f] = SiLU(g) * u.
@@ -283,15 +293,17 @@ __device__ __forceinline__ void wgateup_body(const WGateUpArgs &a, int f) {
     if (lane == 0) a.h[f] = silu(g) * u;
 }
 
-template <int P>
-__global__ __launch_bounds__(kThreads) void k_wgateup1(WGateUpArgs a) {
+template <int P, int FMT>
+__device__ __forceinline__ void wgateup_kernel(const WGateUpArgs &a) {
     const int f = blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (f >= a.F) return;
-    if (a.fmt == F_Q5_0)
-        wgateup_body<P, F_Q5_0>(a, f);
-    else
-        wgateup_body<P, F_Q8_0>(a, f);
+    wgateup_body<P, FMT>(a, f);
 }
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wgateup1(WGateUpArgs a) { wgateup_kernel<P, F_Q8_0>(a); }
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wgateup1_q5(WGateUpArgs a) { wgateup_kernel<P, F_Q5_0>(a); }
 
 // ---------------------------------------------------------------- o, down
 
@@ -300,7 +312,6 @@ struct WMatmulArgs {
     const float *x;
     float *y;
     int N, accumulate;
-    int fmt;   // WFmt of W (Q8_0 or Q5_0)
 };
 
 // Wave w of workgroup b: rows 2e, 2e + 1 (e = 4 b + w); y[row] (+)= W[row] . x.
@@ -325,16 +336,18 @@ __device__ __forceinline__ void wmatmul_body(const WMatmulArgs &a, int row) {
     }
 }
 
-template <int P>
-__global__ __launch_bounds__(kThreads) void k_wmatmul1(WMatmulArgs a) {
+template <int P, int FMT>
+__device__ __forceinline__ void wmatmul_kernel(const WMatmulArgs &a) {
     const int e = blockIdx.x * kWaves + (threadIdx.x >> 6);
     const int row = 2 * e;
     if (row >= a.N) return;
-    if (a.fmt == F_Q5_0)
-        wmatmul_body<P, F_Q5_0>(a, row);
-    else
-        wmatmul_body<P, F_Q8_0>(a, row);
+    wmatmul_body<P, FMT>(a, row);
 }
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wmatmul1(WMatmulArgs a) { wmatmul_kernel<P, F_Q8_0>(a); }
+template <int P>
+__global__ __launch_bounds__(kThreads) void k_wmatmul1_q5(WMatmulArgs a) { wmatmul_kernel<P, F_Q5_0>(a); }
 
 template <class F>
 bool dispatch_p(int P, F &&f) {
@@ -370,8 +383,12 @@ hipError_t launch_wqkv(const Dims &dm, const LayerPtrs &w, const float *x, const
     a.fmt[0] = w.fq; a.fmt[1] = w.fk; a.fmt[2] = w.fv;
     const int pairs = (a.QD + 2 * a.KVD) / 2;
     const int grid = (pairs + kWaves - 1) / kWaves;
+    const int pm = pair_mode(w.fq, w.fk, w.fv);
     if (!dispatch_p(dm.H / kPairWeights, [&](auto p) {
-            hipLaunchKernelGGL(k_wqkv1<decltype(p)::value>, dim3(grid), dim3(kThreads), 0, s, a);
+            constexpr int P = decltype(p)::value;
+            if (pm == PM_Q8) hipLaunchKernelGGL(k_wqkv1<P>, dim3(grid), dim3(kThreads), 0, s, a);
+            else if (pm == PM_Q5) hipLaunchKernelGGL(k_wqkv1_q5<P>, dim3(grid), dim3(kThreads), 0, s, a);
+            else hipLaunchKernelGGL(k_wqkv1_mixed<P>, dim3(grid), dim3(kThreads), 0, s, a);
         }))
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -381,10 +398,11 @@ hipError_t launch_wgateup(const Dims &dm, const LayerPtrs &w, const float *x, fl
                           const PartSrc &ps) {
     WGateUpArgs a;
     a.wg = w.wg; a.wu = w.wu; a.norm_w = w.ffn_norm; a.x = x; a.h = h; a.F = dm.F; a.eps = dm.eps; a.ps = ps;
-    a.fmt = w.fg;
     const int grid = (dm.F + kWaves - 1) / kWaves;
     if (!dispatch_p(dm.H / kPairWeights, [&](auto p) {
-            hipLaunchKernelGGL(k_wgateup1<decltype(p)::value>, dim3(grid), dim3(kThreads), 0, s, a);
+            constexpr int P = decltype(p)::value;
+            if (w.fg == F_Q5_0) hipLaunchKernelGGL(k_wgateup1_q5<P>, dim3(grid), dim3(kThreads), 0, s, a);
+            else hipLaunchKernelGGL(k_wgateup1<P>, dim3(grid), dim3(kThreads), 0, s, a);
         }))
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -393,10 +411,12 @@ hipError_t launch_wgateup(const Dims &dm, const LayerPtrs &w, const float *x, fl
 hipError_t launch_wmatmul(const uint8_t *W, int N, int K, const float *x, int accumulate, float *y, hipStream_t s,
                           int fmt) {
     WMatmulArgs a;
-    a.W = W; a.x = x; a.y = y; a.N = N; a.accumulate = accumulate; a.fmt = fmt;
+    a.W = W; a.x = x; a.y = y; a.N = N; a.accumulate = accumulate;
     const int grid = ((N + 1) / 2 + kWaves - 1) / kWaves;
     if (!dispatch_p(K / kPairWeights, [&](auto p) {
-            hipLaunchKernelGGL(k_wmatmul1<decltype(p)::value>, dim3(grid), dim3(kThreads), 0, s, a);
+            constexpr int P = decltype(p)::value;
+            if (fmt == F_Q5_0) hipLaunchKernelGGL(k_wmatmul1_q5<P>, dim3(grid), dim3(kThreads), 0, s, a);
+            else hipLaunchKernelGGL(k_wmatmul1<P>, dim3(grid), dim3(kThreads), 0, s, a);
         }))
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -78,6 +78,16 @@ constexpr int kQKK = 256;            // weights per Q4_K / Q6_K block
 constexpr int kQ4KBytes = 144;       // f16 d, f16 dmin, 12 scale/min bytes, 128 nibble bytes
 constexpr int kQ6KBytes = 210;       // 128 low-nibble bytes, 64 high-bit bytes, 16 int8 scales, f16 d
 
+// Block formats a GEMV kernel instance decodes: each kernel is built once
+// per mode, so the Q8_0 instances carry no Q5_0 decoding (its registers would
+// lower their occupancy). PM_MIXED picks per matrix at run time (q, k and v
+// of one layer in different formats).
+enum PairMode { PM_Q8 = 0, PM_Q5 = 1, PM_MIXED = 2 };
+inline int pair_mode(int f0, int f1, int f2) {
+    if (f0 == f1 && f1 == f2) return f0 == F_Q5_0 ? PM_Q5 : PM_Q8;
+    return PM_MIXED;
+}
+
 // 256-weight block formats: the K-format GEMV and GEMM kernels.
 __host__ __device__ inline bool kq_format(int fmt) { return fmt == F_Q4_K || fmt == F_Q6_K; }
 
@@ -202,7 +212,8 @@ constexpr int kAttnOWgs = 64;  // workgroups the fused attention + o-projection 
 constexpr size_t kFuseAttnOMaxBytes = 16 * 1024;  // largest n_head_kv * width * 4 fused
 bool attn_o_fits(const Dims &d);  // whole 64-column pairs per group, at most kThreads per row
 int attn_o_rows(const Dims &d);
-hipError_t launch_attn_o(const AttnDecodeArgs &a, const uint8_t *wo, int N, float *part, hipStream_t s);
+hipError_t launch_attn_o(const AttnDecodeArgs &a, const uint8_t *wo, int N, float *part, hipStream_t s,
+                         int fmt = F_Q8_0);
 
 // Merge split partials into o; with st set, kv_len is read from st->slot + 1.
 hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int nh, int hd,

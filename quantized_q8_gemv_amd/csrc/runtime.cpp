@@ -271,10 +271,10 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.n_splits = decode_splits;
             a.scale = 1.0f / sqrtf(float(d.hd));
             a.o = decode_splits == 1 ? att : nullptr;  // one split: the attention kernel normalises
-            if (decode_splits == 1 && w.fo == F_Q8_0 && m->fuse_attn_o) {
+            if (decode_splits == 1 && !kq_format(w.fo) && m->fuse_attn_o) {
                 // one kernel; its partial sums wait for the gate/up kernel's prologue
                 float *part_o = m->at<float>(m->lay.part_o);
-                if ((e = launch_attn_o(a, w.wo, d.H, part_o, s)) != hipSuccess) return e;
+                if ((e = launch_attn_o(a, w.wo, d.H, part_o, s, w.fo)) != hipSuccess) return e;
                 dpend.part = part_o;
                 dpend.n = d.nkv;
                 dpend.stride = d.H;
@@ -688,7 +688,7 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
     const int n_splits = split_bucket(m, kv_len);
     // as in the step: with one split the attention and the o-projection are
     // one kernel, and gate/up adds its partial sums to the residual first
-    const bool fused = n_splits == 1 && m->fuse_attn_o && m->layer(0).fo == F_Q8_0;
+    const bool fused = n_splits == 1 && m->fuse_attn_o && !kq_format(m->layer(0).fo);
     PartSrc ps_gu;
     if (fused) {
         ps_gu.part = m->at<float>(m->lay.part_o);
@@ -714,7 +714,8 @@ q8l_status q8l_time_decode_kernels(q8l_model *m, int32_t reps, float *ms_out, vo
             case 1:  // q/k/v as every layer but the first runs it (that one also reads the embedding)
                 return launch_qkv(d, w, x, S, m->at<float2>(m->lay.rope), q, m->kc(l), m->vc(l), 1, s);
             case 2:
-                if (fused && w.fo == F_Q8_0) return launch_attn_o(a, w.wo, d.H, m->at<float>(m->lay.part_o), s);
+                if (fused && !kq_format(w.fo))
+                    return launch_attn_o(a, w.wo, d.H, m->at<float>(m->lay.part_o), s, w.fo);
                 return launch_attn_decode(a, s);
             case 3:
                 if (kq_format(w.fo)) return launch_kq_gemv(w.fo, w.wo, d.H, QD, m->at<float>(m->lay.att), 1, x, s);
