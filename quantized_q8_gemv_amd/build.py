@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq8l.so")
-SOURCES = ["k_gemv.hip", "k_wgemv.hip", "k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_kquant.hip", "noalloc.hip", "runtime.cpp", "gguf.cpp"]
+SOURCES = ["k_gemv.hip", "k_wgemv.hip", "k_xgemv.hip", "k_gemm.hip", "k_attn.hip", "k_misc.hip", "k_kquant.hip", "noalloc.hip", "runtime.cpp", "gguf.cpp"]
 ARCH = os.environ.get("Q8L_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -175,6 +175,94 @@ __device__ __forceinline__ void pair_dot1_q5(const uint32_t *w, const float *x, 
     sB = q5_block_dot(qb, w[6], x + 32);
 }
 
+// The same pair products with the pair's 64 activations in registers
+// (x[i] = activation i of the pair): returns dA * sA + dB * sB, with sA, sB
+// summed as in pair_dot1 / pair_dot1_q5.
+__device__ __forceinline__ float xpair_dot_q8(const uint32_t (&w)[17], const float (&x)[64]) {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t q = __builtin_amdgcn_alignbyte(w[j + 1], w[j], 2);
+        s0 = fmaf(sbyte(q, 0), x[4 * j], s0);
+        s1 = fmaf(sbyte(q, 1), x[4 * j + 1], s1);
+        s2 = fmaf(sbyte(q, 2), x[4 * j + 2], s2);
+        s3 = fmaf(sbyte(q, 3), x[4 * j + 3], s3);
+    }
+    const float sA = (s0 + s1) + (s2 + s3);
+    s0 = s1 = s2 = s3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t q = w[9 + j];
+        s0 = fmaf(sbyte(q, 0), x[32 + 4 * j], s0);
+        s1 = fmaf(sbyte(q, 1), x[33 + 4 * j], s1);
+        s2 = fmaf(sbyte(q, 2), x[34 + 4 * j], s2);
+        s3 = fmaf(sbyte(q, 3), x[35 + 4 * j], s3);
+    }
+    const float sB = (s0 + s1) + (s2 + s3);
+    return fmaf(half_bits_to_float(w[8] >> 16), sB, half_bits_to_float(w[0]) * sA);
+}
+
+__device__ __forceinline__ float xblock_dot_q5(const uint32_t (&qs)[4], uint32_t qh, const float (&x)[64], int x0) {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t u = q5_bytes(qs[j], qh, j, h != 0);
+            const int i = x0 + 16 * h + 4 * j;
+            s0 = fmaf(ubyte_f(u, 0) - 16.0f, x[i], s0);
+            s1 = fmaf(ubyte_f(u, 1) - 16.0f, x[i + 1], s1);
+            s2 = fmaf(ubyte_f(u, 2) - 16.0f, x[i + 2], s2);
+            s3 = fmaf(ubyte_f(u, 3) - 16.0f, x[i + 3], s3);
+        }
+    return (s0 + s1) + (s2 + s3);
+}
+
+// The same with the activation block sums xs = sum x[0..31], sum x[32..63]
+// taken once (the activations stay while the rows change): sum (u - 16) x =
+// sum u x - 16 xs, one conversion and one FMA per weight (u the 5-bit code;
+// the rounding differs from the form above by the order of the terms only).
+__device__ __forceinline__ float xblock_dot_q5u(const uint32_t (&qs)[4], uint32_t qh, const float (&x)[64], int x0,
+                                                float xs) {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t u = q5_bytes(qs[j], qh, j, h != 0);
+            const int i = x0 + 16 * h + 4 * j;
+            s0 = fmaf(ubyte_f(u, 0), x[i], s0);
+            s1 = fmaf(ubyte_f(u, 1), x[i + 1], s1);
+            s2 = fmaf(ubyte_f(u, 2), x[i + 2], s2);
+            s3 = fmaf(ubyte_f(u, 3), x[i + 3], s3);
+        }
+    return fmaf(-16.0f, xs, (s0 + s1) + (s2 + s3));
+}
+
+__device__ __forceinline__ float xpair_dot_q5s(const uint32_t (&w)[11], const float (&x)[64], float xsA, float xsB) {
+    uint32_t qa[4], qb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        qa[j] = __builtin_amdgcn_alignbyte(w[j + 2], w[j + 1], 2);
+        qb[j] = w[7 + j];
+    }
+    const float sA = xblock_dot_q5u(qa, __builtin_amdgcn_alignbyte(w[1], w[0], 2), x, 0, xsA);
+    const float sB = xblock_dot_q5u(qb, w[6], x, 32, xsB);
+    return fmaf(half_bits_to_float(w[5] >> 16), sB, half_bits_to_float(w[0]) * sA);
+}
+
+__device__ __forceinline__ float xpair_dot_q5(const uint32_t (&w)[11], const float (&x)[64]) {
+    uint32_t qa[4], qb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        qa[j] = __builtin_amdgcn_alignbyte(w[j + 2], w[j + 1], 2);
+        qb[j] = w[7 + j];
+    }
+    const float sA = xblock_dot_q5(qa, __builtin_amdgcn_alignbyte(w[1], w[0], 2), x, 0);
+    const float sB = xblock_dot_q5(qb, w[6], x, 32);
+    return fmaf(half_bits_to_float(w[5] >> 16), sB, half_bits_to_float(w[0]) * sA);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -1503,6 +1503,10 @@ hipError_t launch_gateup(const Dims &d, const LayerPtrs &w, const float *x, floa
     const int maxt = T == 1 ? 1 : kMaxTokChunk;
     if (ps.n > 0 && T != 1) return hipErrorInvalidValue;
     if (T == 1 && wgemv_fits(d.H)) return launch_wgateup(d, w, x, h, s, ps);
+    if (T == 1 && ps.n == 0) {
+        const hipError_t e = launch_xgateup(d, w, x, h, s);
+        if (e != hipErrorNotSupported) return e;
+    }
     GateUpArgs a;
     a.ps = ps;
     a.wg = w.wg; a.wu = w.wu; a.norm_w = w.ffn_norm; a.x = x; a.h = h; a.F = d.F; a.T = T;
@@ -1536,6 +1540,10 @@ hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
     a.eps = eps;
     a.sh = choose_shape(N, K, maxt, 1, 512, 1, fmt);
     if (T == 1 && !norm_w && wgemv_fits(K)) return launch_wmatmul(W, N, K, X, accumulate, Y, s, fmt);
+    if (T == 1 && !norm_w) {
+        const hipError_t e = launch_xmatmul(W, N, K, X, accumulate, Y, s, fmt);
+        if (e != hipErrorNotSupported) return e;
+    }
     const bool q5 = fmt == F_Q5_0;
     const bool multi = a.sh.PC != a.sh.P;
     if (T == 1) {
@@ -1593,6 +1601,10 @@ hipError_t launch_lmhead(const Dims &d, const uint8_t *Wout, const float *out_no
     a.V = d.V; a.eps = d.eps;
     a.sh = choose_shape(d.V, d.H, 1, 1, 1024, 1);
     const int nb = lmhead_blocks(d.V, d.H);
+    if (ps.n == 0) {
+        const hipError_t e = launch_xlmhead(d, Wout, out_norm, x_last, st, partials, nb, s);
+        if (e != hipErrorNotSupported) return e;
+    }
     const size_t lds = lds1_bytes(a.sh, 1);
     if (a.sh.PC != a.sh.P)
         hipLaunchKernelGGL(k_lmhead1<true>, dim3(nb), dim3(kThreads), lds, s, a);

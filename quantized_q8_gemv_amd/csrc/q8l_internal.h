@@ -147,6 +147,21 @@ hipError_t launch_wgateup(const Dims &d, const LayerPtrs &w, const float *x, flo
                           const PartSrc &ps);
 hipError_t launch_wmatmul(const uint8_t *W, int N, int K, const float *x, int accumulate, float *y, hipStream_t s,
                           int fmt = F_Q8_0);
+// Single-token products of rows of kXMinPairs .. 64 pairs with the
+// activations in registers (k_xgemv.hip; PartSrc not taken: callers use the
+// LDS kernels when partial sums are pending). xgemv_slices: 1 for such rows,
+// 2 or 4 for rows of up to 128 or 256 pairs (the plain product only), 0
+// otherwise. launch_xlmhead writes n_partials argmax partials. Each returns
+// hipErrorNotSupported, launching nothing, for shapes or formats it does not
+// take (the caller then uses the LDS kernels).
+constexpr int kXMinPairs = 32;
+bool xgemv_fits(int K);
+int xgemv_slices(int K);
+hipError_t launch_xmatmul(const uint8_t *W, int N, int K, const float *x, int accumulate, float *y, hipStream_t s,
+                          int fmt);
+hipError_t launch_xgateup(const Dims &dm, const LayerPtrs &w, const float *x, float *h, hipStream_t s);
+hipError_t launch_xlmhead(const Dims &dm, const uint8_t *Wout, const float *out_norm, const float *x_last,
+                          StepState *st, float *partials, int n_partials, hipStream_t s);
 // Y[t] (+)= W U[t] for generic use (o-proj / down with accumulate = 1).
 // fmt: Q8_0 or Q5_0.
 hipError_t launch_matmul(const uint8_t *W, int N, int K, const float *X, int T,
