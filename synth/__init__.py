@@ -306,6 +306,31 @@ def with_k_quants(model: Model, o_fmts, d_fmts, seed: int = 7) -> Model:
 LAYER_ROLES = ("attn_q", "attn_k", "attn_v", "attn_output", "ffn_gate", "ffn_up", "ffn_down")
 
 
+def random_model_formats(shape: ModelShape, seed: int, fmts) -> Model:
+    """A model drawn with each projection directly in its block format
+    (``fmts[l]`` = seven formats for layer l, q .. down): Q8_0 tensors and
+    norms as in ``random_model``, Q5_0 / K-format tensors by ``draw_q5_0`` /
+    ``draw_k_quant``, all from one stream in canonical order. (Not the same
+    values as ``with_layer_formats``, which redraws on top of a Q8_0 model.)"""
+    rng = np.random.default_rng(seed)
+    want = {}
+    for l in range(shape.n_layer):
+        for role, f in zip(LAYER_ROLES, fmts[l]):
+            want[f"blk.{l}.{role}.weight"] = f
+    tensors = []
+    for name, dtype, rows, cols in shape.tensor_specs():
+        f = want.get(name, dtype)
+        if f == "q8_0":
+            tensors.append(Tensor(name, f, rows, cols, pack_q8_0(*draw_q8_0(rng, rows, cols))))
+        elif f == "q5_0":
+            tensors.append(Tensor(name, f, rows, cols, draw_q5_0(rng, rows, cols)))
+        elif f in K_BLOCK_BYTES:
+            tensors.append(Tensor(name, f, rows, cols, draw_k_quant(rng, rows, cols, f)))
+        else:
+            tensors.append(Tensor(name, f, rows, cols, rng.normal(1.0, 0.1, size=cols).astype(np.float32)))
+    return Model(shape, tensors)
+
+
 def with_layer_formats(model: Model, fmts, seed: int = 7) -> Model:
     """``fmts[l]`` = seven formats for layer l (q, k, v, o, gate, up, down)."""
     want = {}
@@ -338,5 +363,5 @@ def shape_fields(shape: ModelShape) -> Dict[str, object]:
 __all__ = ["QK8_0", "Q8_0_BLOCK_BYTES", "LAYER_TENSORS", "ModelShape", "TINY", "SMOL135M",
            "BIG_GQA", "Workload", "WORKLOADS", "micro_shape", "draw_q8_0", "pack_q8_0",
            "Tensor", "Model", "random_model", "K_BLOCK_BYTES", "draw_k_quant", "with_k_quants", "Q5_0_BLOCK_BYTES", "draw_q5_0",
-           "with_formats", "LAYER_ROLES", "with_layer_formats", "prompt_ids", "workload_inputs", "shape_fields"]
+           "with_formats", "LAYER_ROLES", "with_layer_formats", "random_model_formats", "prompt_ids", "workload_inputs", "shape_fields"]
 

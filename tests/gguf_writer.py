@@ -101,8 +101,8 @@ def model_tensors(model) -> List[TensorEntry]:
     out = []
     for t in model.tensors:
         data = np.ascontiguousarray(t.data).tobytes()
-        if t.dtype in ("q8_0", "q4_k", "q6_k"):
-            ty = {"q8_0": TYPE_Q8_0, "q4_k": TYPE_Q4_K, "q6_k": TYPE_Q6_K}[t.dtype]
+        if t.dtype in ("q8_0", "q5_0", "q4_k", "q6_k"):
+            ty = {"q8_0": TYPE_Q8_0, "q5_0": TYPE_Q5_0, "q4_k": TYPE_Q4_K, "q6_k": TYPE_Q6_K}[t.dtype]
             out.append((t.name, ty, [t.cols, t.rows], data))
         else:
             out.append((t.name, TYPE_F32, [t.cols] if t.rows == 1 else [t.cols, t.rows], data))

@@ -8,8 +8,9 @@ here: the single-op entry at the 135M projection shapes for 1 to 203 tokens
 chunk-outer GEMV of long rows (K = 11008, 14336, 17152) and 7B-sized matrices
 on sampled rows; whole models whose layers mix Q5_0 and Q8_0 per matrix at
 the 135M widths (prompts through the GEMM, the small multi-token path, and a
-cache past one attention split) and at the 7B-class widths; and the captured
-decode graphs.
+cache past one attention split) and at the 7B-class widths; the captured
+decode graphs; and GGUF files in the pages' 4-bit mix at both widths, every
+block format read as it is.
 
 Op tolerance: |gpu - oracle| <= 1e-4 * sqrt(K) * rms(w_row) * rms(x_t), as for
 the K formats (f32 accumulation and the f16 hi + lo activation split stay
@@ -163,3 +164,44 @@ def test_7b_width_q5_0_model_two_layers():
     for i, t in enumerate(prompt):
         step, _ = gm.forward([t], i)
     assert_logits_close(step, full, "7b-width q5_0: prefill 40 vs 40 single-token steps")
+
+
+def _q4_k_m_layer(l):
+    """The pages' 4-bit file of the 135M model, per layer ("速度", section
+    "CPU GGUF"): q, k, o, gate and up in Q5_0, v in Q5_0 in every other layer
+    (Q8_0 otherwise), down in Q4_K and Q6_K in alternate layers."""
+    return ["q5_0", "q5_0", "q5_0" if l % 2 else "q8_0", "q5_0", "q5_0", "q5_0", "q4_k" if l % 2 == 0 else "q6_k"]
+
+
+@pytest.mark.parametrize("width", ["135m", "7b"])
+def test_gguf_in_the_pages_4bit_mix_read_natively(tmp_path, width):
+    """A GGUF file in the pages' 4-bit mix read by Q8Model.from_gguf: every
+    format streamed as it is (Q5_0 included), against the oracle on the same
+    blocks. At the 135M widths (4 layers) and the 7B-class ones (2 layers,
+    hidden 4096, FFN 14336, untied vocab 32000)."""
+    import gguf_writer as W
+    from quantized_q8_gemv_amd import q8l as C
+    from quantized_q8_gemv_amd.model import Q8Model
+    if width == "135m":
+        s, plen = synth.TINY, 13
+    else:
+        s = synth.ModelShape("7b-width-2layer", n_layer=2, n_embd=4096, n_head=32, n_head_kv=8,
+                             head_dim=128, n_ff=14336, n_vocab=32000, tied_output=False)
+        plen = 24
+    m = synth.random_model_formats(s, 21, [_q4_k_m_layer(l) for l in range(s.n_layer)])
+    path = str(tmp_path / f"q4_k_m-{width}.gguf")
+    W.write(path, W.llama_kv(s), W.model_tensors(m))
+    g = C.q8l_gguf_open(path)
+    try:
+        for t in m.tensors:
+            st, info = C.q8l_gguf_tensor_info(g, C.q8l_gguf_find_tensor(g, t.name))
+            want = {"q8_0": C.Q8L_Q8_0, "q5_0": C.Q8L_Q5_0, "q4_k": C.Q8L_Q4_K, "q6_k": C.Q8L_Q6_K,
+                    "f32": C.Q8L_F32}[t.dtype]
+            assert st == C.Q8L_OK and info["dtype"] == want and info["nbytes"] == t.nbytes, t.name
+    finally:
+        C.q8l_gguf_close(g)
+    prompt = synth.prompt_ids(s.n_vocab, plen, 8)
+    ids, err, ties = compare_generation(Q8Model.from_gguf(path), oracle.OracleModel(m), prompt, 6,
+                                        f"gguf 4-bit mix {width} {plen}+6")
+    log(f"gguf 4-bit mix {width}: max abs err {err:.3g}")
+    assert ties <= 1
