@@ -98,11 +98,21 @@ def decode_fused(s, kv_len, o_fmt="q8_0"):
             and s.n_head_kv * s.n_embd * 4 <= 16 * 1024 and o_fmt in ("q8_0", "q5_0"))
 
 
+def x_slices(pairs):
+    """Slices of a row the register-activation GEMVs (k_x*) take it in: 1 for
+    32..64 pairs, 2 up to 128, 4 up to 256; 0 when they do not take it."""
+    if pairs < 32:
+        return 0
+    return 1 if pairs <= 64 else 2 if pairs <= 128 else 4 if pairs <= 256 else 0
+
+
 def kernel_symbols(s, down_fmt="q8_0", kv_len=1):
     """Device symbol of each decode kernel kind at this shape (T = 1) and
     cache length. Rows of a few pairs run the wave-per-row kernels
-    (k_w*<pairs>); longer rows the LDS-staged ones. A Q4_K / Q6_K down
-    projection runs k_kq_gemv<format, rows per wave>. With the attention
+    (k_w*<pairs>); rows of 32 to 64 pairs the register-activation ones
+    (k_x*; longer plain products in 2 or 4 slices, k_xmatmul1<slices>),
+    q/k/v of such rows and other lengths the LDS-staged ones. A Q4_K / Q6_K
+    down projection runs k_kq_gemv<format, rows per wave>. With the attention
     fused into the o-projection, the o-projection has no kernel of its own
     (None)."""
     multi = (s.n_embd // 64) * 272 > 40 * 1024  # rows longer than one LDS chunk
@@ -110,18 +120,25 @@ def kernel_symbols(s, down_fmt="q8_0", kv_len=1):
     down_multi = (s.n_ff // 64) * 272 > 40 * 1024
     ph, pq, pf = s.n_embd // 64, s.q_dim // 64, s.n_ff // 64
     wave_h = ph in WAVE_GEMV_PAIRS
+    x_h = not wave_h and x_slices(ph) == 1
+
+    def plain(pairs, lds_multi):
+        if pairs in WAVE_GEMV_PAIRS:
+            return f"k_wmatmul1<{pairs}>"
+        if x_slices(pairs):
+            return f"k_xmatmul1<{x_slices(pairs)}>"
+        return "k_matmul1_chunked<false>" if lds_multi else "k_matmul1<false, false>"
+
     if down_fmt == "q8_0":
-        down = (f"k_wmatmul1<{pf}>" if pf in WAVE_GEMV_PAIRS
-                else "k_matmul1_chunked" if down_multi else "k_matmul1<false, false>")
+        down = plain(pf, down_multi)
     else:
         down = f"k_kq_gemv<{1 if down_fmt == 'q4_k' else 2}, {2 if s.n_embd >= 4096 else 1}>"
     fused = decode_fused(s, kv_len)
-    oproj = (None if fused else f"k_wmatmul1<{pq}>" if pq in WAVE_GEMV_PAIRS
-             else "k_matmul1_chunked" if o_multi else "k_matmul1<false, false>")
+    oproj = None if fused else plain(pq, o_multi)
     return ["k_embed", f"k_wqkv1<{ph}>" if wave_h else f"k_qkv1<{str(multi).lower()}>",
             "k_attn_o1" if fused else "k_attn_decode", oproj,
-            f"k_wgateup1<{ph}>" if wave_h else f"k_gateup1<{str(multi).lower()}>",
-            down, f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
+            f"k_wgateup1<{ph}>" if wave_h else "k_xgateup1" if x_h else f"k_gateup1<{str(multi).lower()}>",
+            down, "k_xlmhead1" if x_h else f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
 
 
 def source_digest(path):
@@ -152,7 +169,8 @@ def measured_traffic(config, kind):
 # a summary's figures count only while the sources it lists are unchanged.
 STATS_FILES = {"C2": "profiles/decode_prefill_135m_13+20_kernel_stats.md"}
 STATS_SOURCES = ["quantized_q8_gemv_amd/csrc/k_gemv.hip", "quantized_q8_gemv_amd/csrc/k_wgemv.hip",
-                 "quantized_q8_gemv_amd/csrc/k_attn.hip", "quantized_q8_gemv_amd/csrc/runtime.cpp"]
+                 "quantized_q8_gemv_amd/csrc/k_xgemv.hip", "quantized_q8_gemv_amd/csrc/k_attn.hip",
+                 "quantized_q8_gemv_amd/csrc/runtime.cpp"]
 
 
 def short_symbol(name):
