@@ -271,6 +271,14 @@ def pmc_summary(fetch_dir, write_dir, config="C2"):
         for kind, (short, vals) in acc.items():
             res.setdefault(kind, {"symbol": short})[counter] = (len(vals), statistics.mean(vals))
     print(f"scale FETCH_SIZE {scale['FETCH_SIZE']:.4f}, WRITE_SIZE {scale['WRITE_SIZE']:.4f}")
+    # the read-only check: the 1 GiB f32 sums of copy_bandwidth(), the largest
+    # reduction dispatches of the FETCH_SIZE run
+    sums = sorted(v for _, n, v in load(fetch_dir, "FETCH_SIZE") if "reduce" in n)
+    if sums:
+        big = [v for v in sums if v >= 0.9 * sums[-1]]
+        read = statistics.mean(big) * 1024 * scale["FETCH_SIZE"]
+        print(f"read-only check: a 1 GiB f32 sum reads {read:,.0f} bytes by the scaled FETCH_SIZE "
+              f"({read / (1 << 30):.4f} of 1 GiB, {len(big)} dispatches)")
     print("| kind | symbol | dispatches | FETCH KiB | WRITE KiB | scaled bytes | algorithmic bytes | ratio |")
     print("|---|---|---:|---:|---:|---:|---:|---:|")
     lines = []
@@ -307,6 +315,14 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     del a, b
+    # A read-only reference for the FETCH_SIZE scale: a sum over `nbytes` of
+    # f32 (16-byte vector loads, nothing written but the result), checked
+    # against the copy's scale by pmc_summary().
+    c = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    for _ in range(2):
+        c.sum()
+    torch.cuda.synchronize()
+    del c
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 

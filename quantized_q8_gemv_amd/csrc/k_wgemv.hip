@@ -119,15 +119,19 @@ template <int P, int FMT>
 __device__ __forceinline__ void load_weights(const uint8_t *row, RowRegs<P, FMT> &r) {
     const int lane = threadIdx.x & 63;
     if (FMT == F_Q5_0) {
-        const uint8_t *b = row + (lane >> 5) * kQ5Bytes;
-        const int j = lane & 31;
+        // d and the fifth-bit word from the two dwords at the block's dword
+        // floor (block 0 of a pair: d = bytes 0..1, word = bytes 2..5; block
+        // 1, bytes 22..43: d = bytes 22..23, word = bytes 24..27): two dword
+        // loads and the value byte, where three 16-bit loads took longer
+        const int b1 = lane >> 5, j = lane & 31;
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(row) + b1 * 5;
+        const uint8_t *qb = row + b1 * kQ5Bytes + 6 + (j & 15);
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-            const uint8_t *blk = b + i * kQ5PairBytes;
-            r.d[i] = *reinterpret_cast<const uint16_t *>(blk);
-            r.h[i] = uint32_t(*reinterpret_cast<const uint16_t *>(blk + 2)) |
-                     (uint32_t(*reinterpret_cast<const uint16_t *>(blk + 4)) << 16);
-            r.q[i] = blk[6 + (j & 15)];
+            const uint32_t lo = w[i * (kQ5PairBytes / 4)], hi = w[i * (kQ5PairBytes / 4) + 1];
+            r.d[i] = b1 ? lo >> 16 : lo & 0xffffu;
+            r.h[i] = b1 ? hi : __builtin_amdgcn_alignbyte(hi, lo, 2);
+            r.q[i] = qb[i * kQ5PairBytes];
         }
     } else {
         const uint8_t *b = row + (lane >> 5) * kQBytes;
@@ -143,9 +147,12 @@ __device__ __forceinline__ void load_weights(const uint8_t *row, RowRegs<P, FMT>
 template <int P, int FMT>
 __device__ __forceinline__ float weight(const RowRegs<P, FMT> &r, int i) {
     if (FMT == F_Q5_0) {
-        const int j = threadIdx.x & 31;
-        const int q5 = ((r.q[i] >> (4 * (j >> 4))) & 15) | int(((r.h[i] >> j) & 1u) << 4);
-        return half_bits_to_float(r.d[i]) * static_cast<float>(q5 - 16);
+        // d * (u - 16) as one FMA, u the 5-bit code: exact (an f16 times an
+        // integer below 2^5 needs 16 bits)
+        const uint32_t j = threadIdx.x & 31;
+        const uint32_t u = (__builtin_amdgcn_ubfe(r.h[i], j, 1) << 4) | __builtin_amdgcn_ubfe(uint32_t(r.q[i]), 4 * (j >> 4), 4);
+        const float d = half_bits_to_float(r.d[i]);
+        return fmaf(static_cast<float>(u), d, -16.0f * d);
     }
     return half_bits_to_float(r.d[i]) * static_cast<float>(r.q[i]);
 }

@@ -34,11 +34,13 @@ def _dispatches(values, names):
     seq += [("__amd_rocclr_copyBuffer", values["copy"]),
             ("__amd_rocclr_copyBuffer", values["copy"] / 2),  # a 512 MiB cache-flush copy: not a reference
             ("__amd_rocclr_copyBuffer", 3.0)]  # a small upload copy: not a reference dispatch
+    if "sum" in values:  # the read-only reference: a 1 GiB f32 sum
+        seq += [("void at::native::reduce_kernel<512, 1>(at::native::ReduceOp<float>)", values["sum"])]
     return seq
 
 
 NS = "void q8l::(anonymous namespace)::"
-FETCH = {"copy": 524288.0, "embed": 2.0, "qkv": 400.0, "attn": 30.0, "o": 280.0, "gateup": 1000.0,
+FETCH = {"copy": 524288.0, "sum": 524800.0, "embed": 2.0, "qkv": 400.0, "attn": 30.0, "o": 280.0, "gateup": 1000.0,
          "down": 570.0, "lm": 15000.0}
 WRITE = {"copy": 1048576.0, "embed": 1.0, "qkv": 8.0, "attn": 2.0, "o": 4.0, "gateup": 12.0,
          "down": 9.0, "lm": 270.0}
@@ -52,6 +54,8 @@ def _summary(tmp_path, names):
         bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), config="C2")
     out = buf.getvalue()
     assert "scale FETCH_SIZE 2.0000, WRITE_SIZE 1.0000" in out
+    # 524800 KiB * 2 = 1.00098 GiB
+    assert "read-only check: a 1 GiB f32 sum reads 1,074,790,400 bytes by the scaled FETCH_SIZE (1.0010 of 1 GiB" in out
     return {l.split()[1].split("=")[1]: l for l in out.splitlines() if l.startswith("traffic:")}
 
 
