@@ -167,7 +167,8 @@ def measured_traffic(config, kind):
 
 # rocprofv3 --kernel-trace --stats summaries of the bench command per workload;
 # a summary's figures count only while the sources it lists are unchanged.
-STATS_FILES = {"C2": "profiles/decode_prefill_135m_13+20_kernel_stats.md"}
+STATS_FILES = {"C2": "profiles/decode_prefill_135m_13+20_kernel_stats.md",
+               "C5": "profiles/decode_prefill_7b-gqa_512+128_kernel_stats.md"}
 STATS_SOURCES = ["quantized_q8_gemv_amd/csrc/k_gemv.hip", "quantized_q8_gemv_amd/csrc/k_wgemv.hip",
                  "quantized_q8_gemv_amd/csrc/k_xgemv.hip", "quantized_q8_gemv_amd/csrc/k_attn.hip",
                  "quantized_q8_gemv_amd/csrc/runtime.cpp"]
