@@ -74,10 +74,17 @@ struct Cfg {
     static constexpr int A_HALVES = TM * LPAD;
     static constexpr int B_HALVES = TN * LPAD;
     static constexpr size_t BUF = sizeof(_Float16) * (2 * A_HALVES + B_HALVES) + sizeof(float) * TN * 2;
-    static constexpr size_t LDS = 2 * BUF;
+    // LDS buffers: one when a single K step of loads is in flight (grids
+    // that fill the chip: a second barrier per step, but half the LDS, so
+    // more workgroups per CU; 7B-class 512-token prefill 28.2 -> 27.1 ms,
+    // 135M 4000-token 11.9 -> 11.0 ms, 203-token 1.84 -> 1.86 ms; with one
+    // buffer for the large tile only, 27.3 and 11.4 ms), two for the
+    // small-grid walk that keeps several steps in flight
+    static constexpr bool one_buffer(int st) { return st == 1; }
+    static constexpr size_t lds(int st) { return (one_buffer(st) ? 1 : 2) * BUF; }
     static_assert(AP >= 1 && BU >= 1 && MS >= 1 && NS >= 1, "tile too small");
     static_assert(BUF % 16 == 0, "LDS buffer alignment");
-    static_assert(size_t(TM) * WN * sizeof(float) <= LDS, "gate/up exchange fits");
+    static_assert(size_t(TM) * WN * sizeof(float) <= BUF, "gate/up exchange fits");
 };
 
 struct GBuf {
@@ -422,7 +429,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
         for (int j = 0; j < S; ++j) {
             const int ks = k0 + j;
             if (ks >= nsteps) break;
-            const GBuf bf = gbuf<TM, TN>(smem, ks & 1);
+            constexpr bool kOne = C::one_buffer(S);
+            const GBuf bf = gbuf<TM, TN>(smem, kOne ? 0 : (ks & 1));
+            if (kOne) __syncthreads();   // (one buffer) every wave is done with the previous step
             g_store<A32, TM, TN, FMT>(regs[j], bf, a, m0, kfirst + ks, resc);
             __syncthreads();
             if (S == 1) {
@@ -941,12 +950,13 @@ constexpr int kSmallGridStages = 4;
 template <int FMT, int EPI, int TM, int TN, bool A32, int ST>
 hipError_t launch_st(const GemmArgs &a, dim3 grid, hipStream_t s) {
     using C = Cfg<TM, TN>;
-    if (C::LDS > 64 * 1024) {
+    constexpr size_t lds = C::lds(ST);
+    if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm_q8<FMT, EPI, TM, TN, A32, ST>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(C::LDS));
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_gemm_q8<FMT, EPI, TM, TN, A32, ST>), grid, dim3(kThreads), C::LDS, s, a);
+    hipLaunchKernelGGL((k_gemm_q8<FMT, EPI, TM, TN, A32, ST>), grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
