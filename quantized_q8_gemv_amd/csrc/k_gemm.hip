@@ -366,8 +366,19 @@ __device__ inline void g_store(const GRegs<TM, TN, FMT> &r, const GBuf &bf, cons
 
 // FMT: the weights' block format, Q8_0 or Q5_0 (a pair of 64 weights per K
 // step either way; only the B tile's load and decode differ).
+//
+// The large-tile Q8_0 q/k/v and gate/up kernels of grids that fill the chip
+// are held to 128 VGPRs (4 waves per SIMD instead of 3, with the row factors
+// loaded in the epilogue instead of at the start: 7B-class 512-token prefill
+// 27.5 -> 26.9 ms); the accumulating and the Q5_0 kernels would spill there.
+template <int FMT, int EPI, int TM, int ST>
+constexpr bool gemm_four_waves() {
+    return FMT == F_Q8_0 && ST == 1 && TM == 64 && (EPI == G_QKV || EPI == G_GATEUP);
+}
+
 template <int FMT, int EPI, int TM, int TN, bool A32, int ST>
-__global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(gemm_four_waves<FMT, EPI, TM, ST>() ? 4 : 1)))
+void k_gemm_q8(GemmArgs a) {
     using C = Cfg<TM, TN>;
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -415,8 +426,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
     // exponents; q/k/v and gate/up read the normalised rows (row factors only)
     constexpr bool kResc = !A32 && EPI != G_QKV && EPI != G_GATEUP;
     const bool resc = kResc ? tile_rescales<TM>(a, m0) : false;
+    constexpr bool kLateRows = gemm_four_waves<FMT, EPI, TM, ST>();
     RowFactors<TM, TN> rf;
-    rf.load(a, m0, wm, lane);
+    if (!kLateRows) rf.load(a, m0, wm, lane);
     // Every stage issues its loads unconditionally (steps past the end
     // re-read the last step, whose registers are never stored): with no
     // branch around them the compiler can wait for the oldest stage alone
@@ -466,6 +478,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs a) {
         }
     }
 
+    if (kLateRows) rf.load(a, m0, wm, lane);
     // ---- epilogue: acc[ms][ns][i] is (m, c) with
     //      m = wm*WM + ms*16 + 4*(lane/16) + i, c = wn*WN + ns*16 + lane%16
     if (EPI == G_GATEUP) {
