@@ -1589,6 +1589,7 @@ hipError_t launch_oproj_merged(const uint8_t *W, int N, int K, const float *part
 }
 
 static int lmhead_blocks(int V, int K) {
+    if (const int xs = xlmhead_short_blocks(V, K)) return xs;
     const GemvShape sh = choose_shape(V, K, 1, 1, 1024, 1);
     return grid1((V + sh.NR - 1) / sh.NR, lds1_bytes(sh, 1));
 }

@@ -20,7 +20,9 @@
 // 64 pairs, taken by S waves of one workgroup; their sums meet in LDS and are
 // added in slice order.
 //
-// Used for the o, gate/up, down and output products of a decode step. The
+// Output rows shorter than 32 pairs take the same per-lane pair layout with
+// several rows per wave (k_xlmhead_short). Used for the o, gate/up, down and
+// output products of a decode step. The
 // q/k/v product stays on the LDS-staged kernel, which measured faster at the
 // 7B-class shape (10.0 us against 11.1 for a version of this design with the
 // rope and cache-write epilogue).
@@ -112,8 +114,9 @@ __device__ __forceinline__ void xl_load(const float *x, int p, bool on, float (&
 // (f32 x, or the token's Q8_0 embedding row dequantized as d * q; workgroup
 // 0 then writes that row to xres) with coalesced 16-byte loads, take the
 // RMSNorm when norm_w is set (sum of squares per thread in element order,
-// then the waves in order), and leave u in LDS; each lane then reads its
-// pair's 64 values. One read of the row per workgroup instead of per wave.
+// then the waves in order), and leave u in LDS; each lane then reads the 64
+// values of pair `pair` (zeros when !on). One read of the row per workgroup
+// instead of per wave.
 constexpr int kXPad = 68;  // floats per staged pair (the pair stride spreads the lanes over the LDS banks)
 
 struct XStage {
@@ -121,8 +124,21 @@ struct XStage {
     float red[kWavesX];
 };
 
+// The 64 staged values of pair p (zeros when !on).
+__device__ __forceinline__ void xl_take(const XStage &L, int p, bool on, float (&v)[64]) {
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(L.u + (on ? p : 0) * kXPad);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const f32x4 t = src[i];
+        v[4 * i] = on ? t.x : 0.f;
+        v[4 * i + 1] = on ? t.y : 0.f;
+        v[4 * i + 2] = on ? t.z : 0.f;
+        v[4 * i + 3] = on ? t.w : 0.f;
+    }
+}
+
 __device__ __forceinline__ void xl_stage(XStage &L, const float *x, const uint8_t *erow, bool evalid, float *xres,
-                                         const float *norm_w, int P, float eps, float (&v)[64]) {
+                                         const float *norm_w, int P, float eps, float (&v)[64], int pair, bool on) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n4 = P * 16;
     float ss = 0.f;
@@ -172,16 +188,7 @@ __device__ __forceinline__ void xl_stage(XStage &L, const float *x, const uint8_
         }
     }
     __syncthreads();
-    const bool on = lane < P;
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(L.u + (on ? lane : 0) * kXPad);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const f32x4 t = src[i];
-        v[4 * i] = on ? t.x : 0.f;
-        v[4 * i + 1] = on ? t.y : 0.f;
-        v[4 * i + 2] = on ? t.z : 0.f;
-        v[4 * i + 3] = on ? t.w : 0.f;
-    }
+    xl_take(L, pair, on, v);
 }
 
 // ---------------------------------------------------------------- o, down, op
@@ -222,7 +229,7 @@ __device__ __forceinline__ void xmatmul_body(XMatmulArgs a) {
     XAct v;
     if constexpr (S == 1) {
         __shared__ XStage L;
-        xl_stage(L, a.x, nullptr, false, nullptr, nullptr, a.P, 0.f, v.v);
+        xl_stage(L, a.x, nullptr, false, nullptr, nullptr, a.P, 0.f, v.v, lane, lane < a.P);
     } else {
         xl_load(a.x, p, on, v.v);
     }
@@ -295,7 +302,7 @@ __device__ __forceinline__ void xgateup_body(XGateUpArgs a) {
     }
     XAct v;
     __shared__ XStage L;
-    xl_stage(L, a.x, nullptr, false, nullptr, a.norm_w, a.P, a.eps, v.v);
+    xl_stage(L, a.x, nullptr, false, nullptr, a.norm_w, a.P, a.eps, v.v, lane, lane < a.P);
     if (FMT == F_Q5_0) v.sums();
     for (int k0 = 0; g + k0 * nw < a.F; k0 += D) {
 #pragma unroll
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void k_xlmhead1(XLmHeadArgs a) {
     for (int k = 0; k < D; ++k) lp_load<F_Q8_0>(rs, off(g + k * nw), w[k]);
     XAct v;
     __shared__ XStage L;
-    xl_stage(L, a.x, nullptr, false, nullptr, a.norm_w, a.P, a.eps, v.v);
+    xl_stage(L, a.x, nullptr, false, nullptr, a.norm_w, a.P, a.eps, v.v, lane, lane < a.P);
     float *logits = a.st->logits_out;
     float bv = -INFINITY;
     uint32_t bi = uint32_t(g);
@@ -362,6 +369,77 @@ __global__ __launch_bounds__(kThreads) void k_xlmhead1(XLmHeadArgs a) {
             argmax_merge(bv, bi, s, uint32_t(r));
         }
     }
+    if (lane == 0) {
+        s_v[wv] = bv;
+        s_i[wv] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float v0 = s_v[0];
+        uint32_t i0 = s_i[0];
+        for (int w2 = 1; w2 < kWavesX; ++w2) argmax_merge(v0, i0, s_v[w2], s_i[w2]);
+        a.partials[2 * blockIdx.x] = v0;
+        a.partials[2 * blockIdx.x + 1] = __uint_as_float(i0);
+    }
+}
+
+// Rows of P < 32 pairs: a wave takes R = 64 / P rows at a time, lane
+// l = P * rr + i holding pair i of row rr (lanes from R * P on idle), so each
+// 16-byte load moves a whole pair per lane (Q8_0: 17 dwords of 64 weights)
+// instead of a byte. Each lane's pair product goes to the wave's row of LDS;
+// lane rr < R then adds its row's P products in pair order. A wave takes the
+// row groups g, g + waves, ..., kXsGroups of them at most, all loaded before
+// the first is computed.
+constexpr int kXsGroups = 2;
+
+__global__ __launch_bounds__(kThreads) void k_xlmhead_short(XLmHeadArgs a) {
+    constexpr int D = kXsGroups;
+    __shared__ float s_v[kWavesX];
+    __shared__ uint32_t s_i[kWavesX];
+    __shared__ float s_part[kWavesX][64];
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+    const int P = a.P, R = 64 / P;
+    const int nw = int(gridDim.x) * kWavesX;
+    const int g = int(blockIdx.x) * kWavesX + wv;
+    const int rr = lane / P, pi = lane - rr * P;
+    const bool on = rr < R;
+    const int ngroups = (a.V + R - 1) / R;
+    const uint32_t rowbytes = uint32_t(P) * kPairBytes;
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(a.W, a.V, rowbytes);
+    auto off = [&](int grp) {
+        const int r = grp * R + rr;
+        return (on && r < a.V) ? uint32_t(r) * rowbytes + uint32_t(pi) * kPairBytes : kNoRow;
+    };
+    LPair<F_Q8_0> w[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) lp_load<F_Q8_0>(rs, off(g + k * nw), w[k]);
+    XAct v;
+    __shared__ XStage L;
+    xl_stage(L, a.x, nullptr, false, nullptr, a.norm_w, P, a.eps, v.v, pi, on);
+    float *logits = a.st->logits_out;
+    float *pw = s_part[wv];
+    float bv = -INFINITY;
+    uint32_t bi = uint32_t(min(g * R, a.V - 1));   // a valid row even if every logit is NaN
+    for (int k0 = 0; g + k0 * nw < ngroups; k0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            const int k = k0 + j, grp = g + k * nw;
+            if (grp >= ngroups) break;
+            const float part = lp_dot<F_Q8_0>(w[j], v);
+            lp_load<F_Q8_0>(rs, off(g + (k + D) * nw), w[j]);
+            pw[lane] = part;
+            __builtin_amdgcn_wave_barrier();
+            const int r = grp * R + lane;
+            if (lane < R && r < a.V) {
+                float sum = pw[lane * P];
+                for (int i = 1; i < P; ++i) sum += pw[lane * P + i];
+                logits[r] = sum;
+                argmax_merge(bv, bi, sum, uint32_t(r));
+            }
+            __builtin_amdgcn_wave_barrier();   // the row is rewritten for the next group
+        }
+    }
+    wave_argmax(bv, bi);
     if (lane == 0) {
         s_v[wv] = bv;
         s_i[wv] = bi;
@@ -428,14 +506,24 @@ hipError_t launch_xgateup(const Dims &dm, const LayerPtrs &w, const float *x, fl
     return hipGetLastError();
 }
 
+int xlmhead_short_blocks(int V, int K) {
+    if (K % kPairWeights) return 0;
+    const int P = K / kPairWeights;
+    if (P < 1 || P >= kXMinPairs || !rows_fit(V, P, F_Q8_0)) return 0;
+    const int ngroups = (V + 64 / P - 1) / (64 / P);
+    return std::max(1, (ngroups + kWavesX * kXsGroups - 1) / (kWavesX * kXsGroups));
+}
+
 hipError_t launch_xlmhead(const Dims &dm, const uint8_t *Wout, const float *out_norm, const float *x_last,
                           StepState *st, float *partials, int n_partials, hipStream_t s) {
     const int P = dm.H / kPairWeights;
-    if (!xgemv_fits(dm.H) || !rows_fit(dm.V, P, F_Q8_0) || n_partials < 1) return hipErrorNotSupported;
+    const bool short_rows = xlmhead_short_blocks(dm.V, dm.H) > 0;
+    if ((!short_rows && !xgemv_fits(dm.H)) || !rows_fit(dm.V, P, F_Q8_0) || n_partials < 1)
+        return hipErrorNotSupported;
     XLmHeadArgs a;
     a.W = Wout; a.norm_w = out_norm; a.x = x_last; a.st = st; a.partials = partials;
     a.V = dm.V; a.P = P; a.eps = dm.eps;
-    hipLaunchKernelGGL(k_xlmhead1, dim3(n_partials), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(short_rows ? k_xlmhead_short : k_xlmhead1, dim3(n_partials), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -160,6 +160,9 @@ int xgemv_slices(int K);
 hipError_t launch_xmatmul(const uint8_t *W, int N, int K, const float *x, int accumulate, float *y, hipStream_t s,
                           int fmt);
 hipError_t launch_xgateup(const Dims &dm, const LayerPtrs &w, const float *x, float *h, hipStream_t s);
+// Grid of the output layer for rows under kXMinPairs pairs (several rows per
+// wave; also its partials count); 0 when such rows do not fit it.
+int xlmhead_short_blocks(int V, int K);
 hipError_t launch_xlmhead(const Dims &dm, const uint8_t *Wout, const float *out_norm, const float *x_last,
                           StepState *st, float *partials, int n_partials, hipStream_t s);
 // Y[t] (+)= W U[t] for generic use (o-proj / down with accumulate = 1).

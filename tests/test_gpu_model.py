@@ -60,6 +60,21 @@ def test_neox_rope_generation_matches_oracle(plen):
     assert ties <= 1
 
 
+@pytest.mark.parametrize("n_embd,n_head,n_head_kv,n_vocab", [(1536, 24, 8, 1001), (1984, 31, 31, 999),
+                                                             (256, 4, 2, 777)])
+def test_output_layer_of_short_rows(n_embd, n_head, n_head_kv, n_vocab):
+    """Output rows of 24, 31 and 4 pairs: the output layer takes 64 / P rows
+    per wave (2, 2 and 16; 48, 62 and 64 lanes busy) with a vocabulary that
+    leaves a partial last group; logits and greedy ids against the oracle."""
+    s = synth.micro_shape(n_layer=1, n_embd=n_embd, n_head=n_head, n_head_kv=n_head_kv, head_dim=64,
+                          n_ff=512, n_vocab=n_vocab, name=f"w{n_embd}")
+    m = synth.random_model(s, n_embd)
+    prompt = synth.prompt_ids(n_vocab, 5, 2)
+    ids, err, ties = compare_generation(gpu_model(m), oracle.OracleModel(m), prompt, 4, f"width {n_embd} 5+4")
+    log(f"width {n_embd}, vocab {n_vocab}: max abs err {err:.3g}, near ties {ties}")
+    assert ties <= 1
+
+
 def test_neox_rope_head_dim_128():
     s = synth.ModelShape("neox-hd128", n_layer=2, n_embd=1024, n_head=8, n_head_kv=2, head_dim=128,
                          n_ff=1024, n_vocab=2048, rope_neox=True)
