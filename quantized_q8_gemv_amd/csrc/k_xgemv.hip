@@ -501,7 +501,9 @@ hipError_t launch_xgateup(const Dims &dm, const LayerPtrs &w, const float *x, fl
         return hipErrorNotSupported;
     XGateUpArgs a;
     a.wg = w.wg; a.wu = w.wu; a.norm_w = w.ffn_norm; a.x = x; a.h = h; a.F = dm.F; a.P = P; a.eps = dm.eps;
-    const int grid = xgrid(dm.F, 1, 2);
+    // four workgroups per CU: one resident round at this kernel's register
+    // use (7B-class gate/up 26.0 -> 25.0 us; 2, 3, 5, 6 and 7 measured slower)
+    const int grid = xgrid(dm.F, 1, 4);
     hipLaunchKernelGGL(w.fg == F_Q5_0 ? k_xgateup1_q5 : k_xgateup1, dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
