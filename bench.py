@@ -72,7 +72,7 @@ KIND_NAMES = ["embed", "qkv_rope_kv", "attn_decode", "oproj_residual", "gateup_s
 NKINDS = len(KIND_NAMES)
 # source of each kind's kernel on the 135M shape, whose PMC summary is committed
 KIND_SOURCES = {"embed": "quantized_q8_gemv_amd/csrc/k_misc.hip", "attn_decode": "quantized_q8_gemv_amd/csrc/k_attn.hip",
-                "lmhead": "quantized_q8_gemv_amd/csrc/k_gemv.hip", "argmax_finish": "quantized_q8_gemv_amd/csrc/k_gemv.hip"}
+                "lmhead": "quantized_q8_gemv_amd/csrc/k_xgemv.hip", "argmax_finish": "quantized_q8_gemv_amd/csrc/k_gemv.hip"}
 for _k in KIND_NAMES:
     KIND_SOURCES.setdefault(_k, "quantized_q8_gemv_amd/csrc/k_wgemv.hip")
 # rocprofv3 PMC summaries of the decode kernels (FETCH_SIZE and WRITE_SIZE per
@@ -109,7 +109,8 @@ def x_slices(pairs):
 def kernel_symbols(s, down_fmt="q8_0", kv_len=1):
     """Device symbol of each decode kernel kind at this shape (T = 1) and
     cache length. Rows of a few pairs run the wave-per-row kernels
-    (k_w*<pairs>); rows of 32 to 64 pairs the register-activation ones
+    (k_w*<pairs>; their output layer several rows per wave,
+    k_xlmhead_short); rows of 32 to 64 pairs the register-activation ones
     (k_x*; longer plain products in 2 or 4 slices, k_xmatmul1<slices>),
     q/k/v of such rows and other lengths the LDS-staged ones. A Q4_K / Q6_K
     down projection runs k_kq_gemv<format, rows per wave>. With the attention
@@ -138,7 +139,8 @@ def kernel_symbols(s, down_fmt="q8_0", kv_len=1):
     return ["k_embed", f"k_wqkv1<{ph}>" if wave_h else f"k_qkv1<{str(multi).lower()}>",
             "k_attn_o1" if fused else "k_attn_decode", oproj,
             f"k_wgateup1<{ph}>" if wave_h else "k_xgateup1" if x_h else f"k_gateup1<{str(multi).lower()}>",
-            down, "k_xlmhead1" if x_h else f"k_lmhead1<{str(multi).lower()}>", "k_argmax_finish"]
+            down, "k_xlmhead1" if x_h else "k_xlmhead_short" if ph < 32 else f"k_lmhead1<{str(multi).lower()}>",
+            "k_argmax_finish"]
 
 
 def source_digest(path):

@@ -61,13 +61,14 @@ def _summary(tmp_path, names):
 
 def test_pmc_summary_scales_by_the_copy(tmp_path):
     """The 135M decode layer as it runs: wave-per-row q/k/v, gate/up and down,
-    the attention fused with the o-projection."""
+    the attention fused with the o-projection, the output layer several rows
+    per wave."""
     names = {"embed": NS + "k_embed(unsigned char const*, int)",
              "qkv": NS + "k_wqkv1<9>(q8l::(anonymous namespace)::WQkvArgs)",
              "attn": "q8l::(anonymous namespace)::k_attn_o1(q8l::AttnODecodeArgs)",
              "gateup": NS + "k_wgateup1<9>(q8l::(anonymous namespace)::WGateUpArgs)",
              "down": NS + "k_wmatmul1<24>(q8l::(anonymous namespace)::WMatmulArgs)",
-             "lm": NS + "k_lmhead1<false>(q8l::(anonymous namespace)::LmHeadArgs)"}
+             "lm": NS + "k_xlmhead_short(q8l::(anonymous namespace)::XLmHeadArgs)"}
     lines = _summary(tmp_path, names)
     # bytes = (FETCH KiB * 2 + WRITE KiB * 1) * 1024
     for kind, key in [("qkv_rope_kv", "qkv"), ("attn_decode", "attn"), ("gateup_silu", "gateup"),
