@@ -134,7 +134,7 @@ struct q8l_model {
     bool finalized = false;
     int32_t len = 0;
     std::string err;
-    std::map<int, hipGraphExec_t> graphs;  // by split bucket
+    std::map<int, hipGraphExec_t> graphs;  // by (split bucket, steps): graph_key
     std::map<int, hipGraph_t> graph_defs;
     hipStream_t cap = nullptr;
     uint32_t *range_host = nullptr;  // pinned: set by a kernel whose f16-pair split saw a value out of range
@@ -351,8 +351,15 @@ int split_bucket(const q8l_model *m, int kv_len) {
     return std::min(b, m->lay.max_splits);
 }
 
-q8l_status decode_graph(q8l_model *m, int bucket, hipGraphExec_t *out) {
-    auto it = m->graphs.find(bucket);
+// Decode graphs hold 1, 2, 4, ... kMaxGraphSteps consecutive steps of one
+// split bucket (each step's kernels read the position, slot and token that
+// the previous step's argmax kernel advanced on the device).
+constexpr int kMaxGraphSteps = 16;
+int graph_key(int bucket, int steps) { return bucket * 64 + steps; }
+
+q8l_status decode_graph(q8l_model *m, int bucket, hipGraphExec_t *out, int steps = 1) {
+    const int key = graph_key(bucket, steps);
+    auto it = m->graphs.find(key);
     if (it != m->graphs.end()) {
         *out = it->second;
         return Q8L_OK;
@@ -360,7 +367,8 @@ q8l_status decode_graph(q8l_model *m, int bucket, hipGraphExec_t *out) {
     if (!m->cap) Q8L_HIP(m, hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking), "hipStreamCreate");
     Q8L_HIP(m, hipStreamBeginCapture(m->cap, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
     // (no embedding kernel: the first layer's q/k/v kernel reads the embedding)
-    hipError_t e = enqueue_layers(m, 1, -1, bucket, m->cap);
+    hipError_t e = hipSuccess;
+    for (int k = 0; k < steps && e == hipSuccess; ++k) e = enqueue_layers(m, 1, -1, bucket, m->cap);
     hipGraph_t g = nullptr;
     hipError_t e2 = hipStreamEndCapture(m->cap, &g);
     if (e != hipSuccess) {
@@ -374,8 +382,8 @@ q8l_status decode_graph(q8l_model *m, int bucket, hipGraphExec_t *out) {
         hipGraphDestroy(g);
         return hip_fail(m, e, "hipGraphInstantiate");
     }
-    m->graphs[bucket] = ex;
-    m->graph_defs[bucket] = g;
+    m->graphs[key] = ex;
+    m->graph_defs[key] = g;
     *out = ex;
     return Q8L_OK;
 }
@@ -653,17 +661,26 @@ q8l_status q8l_generate(q8l_model *m, const uint32_t *token_dev, int32_t index_p
     if (q8l_status rc = range_check(m); rc != Q8L_OK) return rc;
     m->kv_checked = std::min(m->kv_checked, len);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    std::vector<hipGraphExec_t> gs(n_steps);
-    for (int k = 0; k < n_steps; ++k) {
-        q8l_status st = decode_graph(m, split_bucket(m, len + k + 1), &gs[k]);
+    // runs of steps in one split bucket, as graphs of power-of-two step counts
+    std::vector<hipGraphExec_t> gs;
+    for (int k = 0; k < n_steps;) {
+        const int b = split_bucket(m, len + k + 1);
+        int run = 1;
+        while (k + run < n_steps && run < kMaxGraphSteps && split_bucket(m, len + k + run + 1) == b) ++run;
+        int p = 1;
+        while (p * 2 <= run) p *= 2;
+        hipGraphExec_t g = nullptr;
+        q8l_status st = decode_graph(m, b, &g, p);
         if (st != Q8L_OK) return st;
+        gs.push_back(g);
+        k += p;
     }
     float *lg = logits_dev ? logits_dev : m->at<float>(m->lay.logits);
     q8l_status st = set_state(m, index_pos, len, 1, 1, lg, nullptr, ids_dev, nullptr, s);
     if (st != Q8L_OK) return st;
     Q8L_HIP(m, hipMemcpyAsync(&m->state()->token, token_dev, sizeof(uint32_t), hipMemcpyDeviceToDevice, s),
             "token copy");
-    for (int k = 0; k < n_steps; ++k) Q8L_HIP(m, hipGraphLaunch(gs[k], s), "hipGraphLaunch");
+    for (hipGraphExec_t g : gs) Q8L_HIP(m, hipGraphLaunch(g, s), "hipGraphLaunch");
     m->len = len + n_steps;
     m->err.clear();
     return Q8L_OK;
