@@ -6,6 +6,7 @@ Argument marshalling only: the forward pass runs in libq8l.so's kernels.
 from __future__ import annotations
 
 import ctypes
+import os
 from typing import Iterable, Optional, Sequence, Tuple
 
 import numpy as np
@@ -113,6 +114,19 @@ class Q8Model:
             pass
 
 
+def _loaded_hip_runtime() -> str:
+    """Path of the HIP runtime this process has already loaded (torch's, which
+    libq8l.so shares): opening that same file returns the loaded library
+    instead of starting a second runtime under another soname."""
+    C.lib()  # libq8l.so links the runtime: it is mapped from here on
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1] if line.strip() else ""
+            if os.path.basename(path).startswith("libamdhip64.so"):
+                return path
+    raise RuntimeError("no HIP runtime (libamdhip64.so) is loaded in this process")
+
+
 def host_mapped_u32():
     """A pinned host int32 tensor of one element and its device address.
 
@@ -122,7 +136,7 @@ def host_mapped_u32():
     import torch
 
     t = torch.zeros(1, dtype=torch.int32, pin_memory=True)
-    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded (same soname)
+    hip = ctypes.CDLL(_loaded_hip_runtime())
     dptr = ctypes.c_void_p()
     err = hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
     if err != 0 or not dptr.value:
