@@ -233,6 +233,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_o1_q5(AttnODecodeArgs b) { at
 // query head. The split weights w_s = exp(m_s - M) (M = max over splits) are
 // computed once per split into LDS; then o[d] = sum_s w_s o_s[d] / sum_s w_s l_s,
 // every sum in split order (the result does not depend on timing).
+constexpr int kCombinePre = 32;   // partial outputs per thread loaded before the weights are known
+
 __global__ __launch_bounds__(kThreads) void k_attn_combine(const float *part, int n_splits,
                                                           int active, int hd, float *o,
                                                           const StepState *st) {
@@ -245,6 +247,21 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(const float *part, in
         active = min((st->slot + 1 + C - 1) / C, n_splits);
     }
     const float *pb = part + size_t(h) * n_splits * (hd + 2);
+    // Many splits: kThreads / hd interleaved slices of the splits (slice j:
+    // splits j, j + P, ...), each summed in split order, then the slices in
+    // order -- P shorter dependent chains instead of one of `active` steps
+    // (135M, 63 splits: 997 -> 979 us/token; with 17 splits the extra
+    // exchange cost more than it saved). Otherwise thread d sums every split.
+    const bool sliced = active > 32 && hd <= kThreads && kThreads % hd == 0;
+    const int P = sliced ? kThreads / hd : 1;
+    const int j = sliced ? tid / hd : 0, d = sliced ? tid - j * hd : tid;
+    const bool outs = d < hd && j < P;
+    // This thread's first kCombinePre partial outputs, requested now so that
+    // they arrive while the split weights are computed (in bounds: clamped)
+    float pre[kCombinePre];
+#pragma unroll
+    for (int k = 0; k < kCombinePre; ++k)
+        pre[k] = pb[size_t(min(j + k * P, active - 1)) * (hd + 2) + 2 + min(d, hd - 1)];
     float mx = -INFINITY;
     for (int t = tid; t < active; t += kThreads) mx = fmaxf(mx, pb[size_t(t) * (hd + 2)]);
     mx = wave_max(mx);
@@ -259,16 +276,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(const float *part, in
     }
     ls = block_sum(ls, red);  // its barriers also publish w[]
     const float inv = 1.0f / ls;
-    if (active > 32 && hd <= kThreads && kThreads % hd == 0) {
-        // Many splits: kThreads / hd interleaved slices of the splits (slice
-        // j: splits j, j + P, ...), each summed in split order, then the
-        // slices in order -- P shorter dependent chains instead of one of
-        // `active` steps (135M, 63 splits: 997 -> 979 us/token; with 17
-        // splits the extra exchange cost more than it saved).
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kCombinePre; ++k)
+        if (j + k * P < active) acc = fmaf(w[j + k * P], pre[k], acc);
+    for (int t = j + kCombinePre * P; t < active; t += P) acc = fmaf(w[t], pb[size_t(t) * (hd + 2) + 2 + d], acc);
+    if (sliced) {
         __shared__ float acc_s[kThreads];
-        const int P = kThreads / hd, j = tid / hd, d = tid - j * hd;
-        float acc = 0.f;
-        for (int t = j; t < active; t += P) acc = fmaf(w[t], pb[size_t(t) * (hd + 2) + 2 + d], acc);
         acc_s[tid] = acc;
         __syncthreads();
         if (j == 0) {
@@ -278,11 +292,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(const float *part, in
         }
         return;
     }
-    for (int d = tid; d < hd; d += kThreads) {
-        float acc = 0.f;
-        for (int t = 0; t < active; ++t) acc = fmaf(w[t], pb[size_t(t) * (hd + 2) + 2 + d], acc);
-        o[size_t(h) * hd + d] = acc * inv;
-    }
+    if (outs) o[size_t(h) * hd + d] = acc * inv;
 }
 
 constexpr int kQB = 32;   // queries per prefill workgroup
