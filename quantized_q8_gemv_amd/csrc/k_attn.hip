@@ -418,6 +418,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int FQ = 64;    // queries per workgroup
+constexpr int kPfMinChunk = 4;   // key blocks per range at least (shorter prompts are not split)
 constexpr int FK = 64;    // keys per block
 
 template <int HD>
@@ -507,6 +508,11 @@ __device__ __forceinline__ void kv_store(const KvRegs<HD> &r, FlashLds<HD> &L) {
     }
 }
 
+// Key blocks of FK that query block qb (queries qb * FQ ..) reaches.
+__host__ __device__ inline int prefix_blocks(int prefix, int qb, int T) {
+    return (prefix + min((qb + 1) * FQ, T) - 1) / FK + 1;
+}
+
 template <int HD>
 __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs a) {
     __shared__ __align__(16) FlashLds<HD> L;
@@ -514,9 +520,23 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = a.nh / a.nkv;
     const int h = blockIdx.y, g = h / G;
-    // causal work grows with the query block: start the longest blocks first
-    const int q0 = (gridDim.x - 1 - blockIdx.x) * FQ;
     const int prefix = a.kv_len - a.T;
+    // causal work grows with the query block: start the longest blocks first.
+    // With key splits, workgroup x takes key range sp of the query blocks
+    // taken from the last one down (ns ranges of pf_chunk key blocks each).
+    const int nqb = (a.T + FQ - 1) / FQ;
+    int qb = nqb - 1 - int(blockIdx.x), sp = 0, ns = 1;
+    if (a.pf_chunk > 0) {
+        int w = blockIdx.x;
+        for (qb = nqb - 1;; --qb) {
+            ns = (prefix_blocks(prefix, qb, a.T) + a.pf_chunk - 1) / a.pf_chunk;
+            if (w < ns || qb == 0) break;
+            w -= ns;
+        }
+        if (w >= ns) return;   // (past the work: the grid is sized to it)
+        sp = w;
+    }
+    const int q0 = qb * FQ;
     const int row_stride = a.nh * HD;
     const int qi = q0 + wave * 16 + (lane & 15);   // this lane's query
     const int grp = lane >> 4;
@@ -545,13 +565,17 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
     const float *kb = a.kc + size_t(g) * a.kv_stride * HD;
     const float *vb = a.vc + size_t(g) * a.kv_stride * HD;
 
+    // this workgroup's keys: all of the block's, or key blocks
+    // [sp * pf_chunk, (sp + 1) * pf_chunk)
+    const int j_first = ns > 1 ? sp * a.pf_chunk * FK : 0;
+    const int j_last = ns > 1 ? min(blk_last, (sp + 1) * a.pf_chunk * FK - 1) : blk_last;
     KvRegs<HD> kv;
-    kv_load<HD>(kb, vb, 0, blk_last, kv);
-    for (int j0 = 0; j0 <= blk_last; j0 += FK) {
+    kv_load<HD>(kb, vb, j_first, j_last, kv);
+    for (int j0 = j_first; j0 <= j_last; j0 += FK) {
         __syncthreads();  // the previous block's LDS tiles are no longer read
         kv_store<HD>(kv, L);
         __syncthreads();
-        if (j0 + FK <= blk_last) kv_load<HD>(kb, vb, j0 + FK, blk_last, kv);
+        if (j0 + FK <= j_last) kv_load<HD>(kb, vb, j0 + FK, j_last, kv);
         // S^T for 4 key tiles of 16
         f32x4 st[4];
 #pragma unroll
@@ -588,16 +612,19 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
         bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
         bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
         // Scores are in log2 units (Q carries log2(e)). Key 0 is visible to
-        // every query, so m_new is finite and exp2(-inf) = 0 handles masked
-        // keys and the first block's alpha.
+        // every query, so with the whole key range m_new is finite and
+        // exp2(-inf) = 0 handles masked keys and the first block's alpha. A
+        // later key range can hold no visible key of a query yet (m_new still
+        // -inf): its exponentials are taken against 0 instead and give 0.
         const float m_new = fmaxf(m, bmax);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
         float psum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(st[kt][i] - m_new);
+                const float p = __builtin_amdgcn_exp2f(st[kt][i] - m_ref);
                 st[kt][i] = p;
                 psum += p;
             }
@@ -632,6 +659,20 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
             o[t] = acc;
         }
     }
+    if (ns > 1) {   // one key range of several: (max in log2 units, sum, unnormalised o)
+        if (qi < a.T) {
+            float *pp = a.pf_part + ((size_t(h) * a.T + qi) * kMaxPfSplits + sp) * (HD + 2);
+#pragma unroll
+            for (int t = 0; t < HD / 16; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pp[2 + t * 16 + 4 * grp + i] = o[t][i];
+            if (grp == 0) {
+                pp[0] = m;
+                pp[1] = lsum;
+            }
+        }
+        return;
+    }
     if (qi < a.T) {
         const float inv = 1.0f / lsum;
         const size_t base = size_t(qi) * row_stride + h * HD;
@@ -657,7 +698,73 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
     }
 }
 
+// Merge of the key ranges of the query blocks that were split: one wave per
+// (query, head), queries from q_begin; lane d (and d + 64) of the output.
+// o = sum_s w_s o_s / sum_s w_s l_s, w_s = exp2(m_s - M), M the largest m_s,
+// sums in range order (the result does not depend on timing). Written as the
+// attention kernel writes an unsplit block (f32, or the f16 pair planes with
+// the range check).
+template <int HD>
+__global__ __launch_bounds__(kThreads) void k_attn_prefill_merge(AttnPrefillArgs a, int q_begin) {
+    constexpr int DL = HD / 64;   // output values per lane
+    const int lane = threadIdx.x & 63;
+    const int qi = q_begin + int(blockIdx.x) * (kThreads / 64) + int(threadIdx.x >> 6), h = blockIdx.y;
+    if (qi >= a.T) return;   // (no barriers in this kernel)
+    const int prefix = a.kv_len - a.T;
+    const int ns = (prefix_blocks(prefix, qi / FQ, a.T) + a.pf_chunk - 1) / a.pf_chunk;
+    if (ns <= 1) return;     // written by the attention kernel itself
+    const float *pp = a.pf_part + (size_t(h) * a.T + qi) * kMaxPfSplits * (HD + 2);
+    float ms[kMaxPfSplits], ls[kMaxPfSplits], ov[kMaxPfSplits][DL];
+#pragma unroll
+    for (int s = 0; s < kMaxPfSplits; ++s) {
+        const float *ps = pp + size_t(min(s, ns - 1)) * (HD + 2);
+        ms[s] = ps[0];
+        ls[s] = ps[1];
+#pragma unroll
+        for (int j = 0; j < DL; ++j) ov[s][j] = ps[2 + lane + 64 * j];
+    }
+    float M = ms[0];
+#pragma unroll
+    for (int s = 1; s < kMaxPfSplits; ++s)
+        if (s < ns) M = fmaxf(M, ms[s]);
+    float L = 0.f, acc[DL];
+#pragma unroll
+    for (int j = 0; j < DL; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxPfSplits; ++s) {
+        if (s < ns) {
+            const float w = __builtin_amdgcn_exp2f(ms[s] - M);
+            L = fmaf(w, ls[s], L);
+#pragma unroll
+            for (int j = 0; j < DL; ++j) acc[j] = fmaf(w, ov[s][j], acc[j]);
+        }
+    }
+    const float inv = 1.0f / L;
+    const int row_stride = a.nh * HD;
+    const size_t base = size_t(qi) * row_stride + h * HD;
+    if (a.o_split) {
+        const size_t plane = size_t(a.T) * row_stride;
+        bool bad = false;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) {
+            const float v = acc[j] * inv;
+            bad |= !(fabsf(v) < kPairRange);
+            store_hilo(a.o_split, plane, base + lane + 64 * j, v);
+        }
+        if (bad && a.range_flag) *a.range_flag = 1u;
+    } else {
+#pragma unroll
+        for (int j = 0; j < DL; ++j) a.o[base + lane + 64 * j] = acc[j] * inv;
+    }
+}
+
 }  // namespace
+
+int attn_prefill_chunk(int kv_len) {
+    const int nb = (kv_len + FK - 1) / FK;
+    const int c = (nb + kMaxPfSplits - 1) / kMaxPfSplits;
+    return c >= kPfMinChunk ? c : 0;
+}
 
 int attn_decode_splits(int kv_len, int hd) {
     const int C = attn_chunk(hd);
@@ -713,11 +820,33 @@ hipError_t launch_attn_combine(const float *part, int n_splits, int kv_len, int 
 
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t s) {
     if (a.hd == 64 || a.hd == 128) {
-        dim3 grid((a.T + FQ - 1) / FQ, a.nh);
+        const int nqb = (a.T + FQ - 1) / FQ, prefix = a.kv_len - a.T;
+        // key splits: the workgroups of every query block, and the first
+        // query whose block is split
+        int wgs = nqb, q_split = a.T;
+        if (a.pf_part && a.pf_chunk > 0) {
+            if (a.pf_chunk * kMaxPfSplits < prefix_blocks(prefix, nqb - 1, a.T)) return hipErrorInvalidValue;
+            wgs = 0;
+            for (int qb = 0; qb < nqb; ++qb) {
+                const int ns = (prefix_blocks(prefix, qb, a.T) + a.pf_chunk - 1) / a.pf_chunk;
+                wgs += ns;
+                if (ns > 1 && q_split == a.T) q_split = qb * FQ;
+            }
+        }
+        AttnPrefillArgs b = a;
+        if (!a.pf_part) b.pf_chunk = 0;
+        dim3 grid(wgs, a.nh);
         if (a.hd == 64)
-            hipLaunchKernelGGL(k_attn_prefill_mfma<64>, grid, dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL(k_attn_prefill_mfma<64>, grid, dim3(kThreads), 0, s, b);
         else
-            hipLaunchKernelGGL(k_attn_prefill_mfma<128>, grid, dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL(k_attn_prefill_mfma<128>, grid, dim3(kThreads), 0, s, b);
+        if (q_split < a.T) {
+            const dim3 mgrid((a.T - q_split + kThreads / 64 - 1) / (kThreads / 64), a.nh);
+            if (a.hd == 64)
+                hipLaunchKernelGGL(k_attn_prefill_merge<64>, mgrid, dim3(kThreads), 0, s, b, q_split);
+            else
+                hipLaunchKernelGGL(k_attn_prefill_merge<128>, mgrid, dim3(kThreads), 0, s, b, q_split);
+        }
         return hipGetLastError();
     }
     const size_t lds = sizeof(float) * (size_t(kQB) * (a.hd + 1) + size_t(kKT) * (a.hd + 1) +

@@ -323,7 +323,17 @@ struct AttnPrefillArgs {
     int T, kv_len, kv_stride, nh, nkv, hd;
     float scale;
     uint32_t *range_flag = nullptr;  // set to 1 when a value split into an f16 pair is out of its range
+    // Key-split partials (NULL: every query block's keys in one workgroup).
+    // With it, query blocks with more than pf_chunk key blocks of 64 are cut
+    // into key ranges of pf_chunk blocks, each a workgroup writing (max,
+    // sum, unnormalised o) per query to pf_part [nh][T][kMaxPfSplits][hd + 2];
+    // a merge kernel then writes o.
+    float *pf_part = nullptr;
+    int pf_chunk = 0;
 };
+constexpr int kMaxPfSplits = 4;   // key ranges per query block at most
+// Key blocks per range for a prefill of kv_len keys (0: no split).
+int attn_prefill_chunk(int kv_len);
 hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t s);
 
 }  // namespace q8l

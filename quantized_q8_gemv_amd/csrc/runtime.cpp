@@ -47,6 +47,7 @@ struct Layout {
     size_t state, counters, rope, tok, kc, vc, x, q, att, h, u, logits, lm_part, attn_part, kpart, total;
     size_t rs, eg_h, el_h;  // prefill activation scaling: row factors, h row / block exponents
     size_t x_alt, part_o;   // decode: second residual row, split-K partials of the fused attention + o
+    size_t pf_part;         // prefill attention: partials of key-split query blocks
     int el_stride;          // 32-wide blocks per h row
     size_t kv_layer;  // floats per layer in kc (and vc)
     int max_splits;
@@ -109,6 +110,8 @@ Layout make_layout(const q8l_config *c) {
     L.el_h = take(S * size_t(L.el_stride));
     L.x_alt = take(H * 4);
     L.part_o = take(size_t(c->n_head_kv) * H * 4);
+    // prefill attention key ranges: [n_head][max_seq][kMaxPfSplits][hd + 2]
+    L.pf_part = take(attn_prefill_chunk(int(S)) > 0 ? size_t(c->n_head) * S * kMaxPfSplits * (hd + 2) * 4 : 0);
     L.total = off;
     return L;
 }
@@ -300,6 +303,8 @@ hipError_t enqueue_layers(q8l_model *m, int T, int kv_len_prefill, int decode_sp
             a.T = T; a.kv_len = kv_len_prefill; a.kv_stride = d.max_seq;
             a.nh = d.nh; a.nkv = d.nkv; a.hd = d.hd; a.scale = 1.0f / sqrtf(float(d.hd));
             a.range_flag = m->range_dev;
+            a.pf_chunk = attn_prefill_chunk(kv_len_prefill);   // long prompts: key ranges in parallel
+            a.pf_part = a.pf_chunk > 0 ? m->at<float>(m->lay.pf_part) : nullptr;
             if ((e = launch_attn_prefill(a, s)) != hipSuccess) return e;
             if (kq_format(w.fo))
                 e = gemm ? launch_gemm_kq(w.fo, w.wo, d.H, QD, att_s, true, T, 1, x, s, sc_o)

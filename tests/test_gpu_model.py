@@ -195,6 +195,21 @@ def test_long_context_prefill_and_decode_to_the_table_end():
     assert gm.forward_async([tok], 4096) == C.Q8L_E_POS_RANGE
 
 
+@pytest.mark.parametrize("plen", [200, 1023, 1100])
+def test_long_prompt_head_dim_128(plen):
+    """Prefill attention with the key ranges of long query blocks split over
+    workgroups and merged (1023 and 1100 tokens: 16 and 18 key blocks of 64
+    in ranges of 4 and 5; 200 tokens: no split), head size 128, 4 query heads
+    per KV head, then decode steps."""
+    s = synth.micro_shape(n_layer=1, n_embd=512, n_head=4, n_head_kv=1, head_dim=128, n_ff=512,
+                          n_vocab=1000, max_seq_len=1200, name="hd128-long")
+    m = synth.random_model(s, plen)
+    prompt = synth.prompt_ids(s.n_vocab, plen, 9)
+    ids, err, ties = compare_generation(gpu_model(m), oracle.OracleModel(m), prompt, 3, f"hd128 {plen}+3")
+    log(f"hd128 {plen}+3: max abs err {err:.3g}, near ties {ties}")
+    assert ties <= 1
+
+
 def test_big_gqa_shape_two_layers():
     """hidden 4096, 32/8 heads, head_dim 128, FFN 14336, vocab 32000 untied (2 layers)."""
     s = synth.ModelShape("7b-width-2layer", n_layer=2, n_embd=4096, n_head=32, n_head_kv=8,
