@@ -513,7 +513,9 @@ __host__ __device__ inline int prefix_blocks(int prefix, int qb, int T) {
     return (prefix + min((qb + 1) * FQ, T) - 1) / FK + 1;
 }
 
-template <int HD>
+// KS: query blocks may split their key range (a.pf_chunk > 0); without it
+// every workgroup takes a whole query block.
+template <int HD, bool KS>
 __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs a) {
     __shared__ __align__(16) FlashLds<HD> L;
     constexpr int LD = HD + 8, LV = FK + 8;
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
     // taken from the last one down (ns ranges of pf_chunk key blocks each).
     const int nqb = (a.T + FQ - 1) / FQ;
     int qb = nqb - 1 - int(blockIdx.x), sp = 0, ns = 1;
-    if (a.pf_chunk > 0) {
+    if constexpr (KS) {
         int w = blockIdx.x;
         for (qb = nqb - 1;; --qb) {
             ns = (prefix_blocks(prefix, qb, a.T) + a.pf_chunk - 1) / a.pf_chunk;
@@ -617,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
         // later key range can hold no visible key of a query yet (m_new still
         // -inf): its exponentials are taken against 0 instead and give 0.
         const float m_new = fmaxf(m, bmax);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float m_ref = KS && m_new == -INFINITY ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
         float psum = 0.f;
 #pragma unroll
@@ -659,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_prefill_mfma(AttnPrefillArgs 
             o[t] = acc;
         }
     }
-    if (ns > 1) {   // one key range of several: (max in log2 units, sum, unnormalised o)
+    if (KS && ns > 1) {   // one key range of several: (max in log2 units, sum, unnormalised o)
         if (qi < a.T) {
             float *pp = a.pf_part + ((size_t(h) * a.T + qi) * kMaxPfSplits + sp) * (HD + 2);
 #pragma unroll
@@ -834,12 +836,15 @@ hipError_t launch_attn_prefill(const AttnPrefillArgs &a, hipStream_t s) {
             }
         }
         AttnPrefillArgs b = a;
-        if (!a.pf_part) b.pf_chunk = 0;
+        const bool ks = a.pf_part && a.pf_chunk > 0;
+        if (!ks) b.pf_chunk = 0;
         dim3 grid(wgs, a.nh);
+        void (*kern)(AttnPrefillArgs);
         if (a.hd == 64)
-            hipLaunchKernelGGL(k_attn_prefill_mfma<64>, grid, dim3(kThreads), 0, s, b);
+            kern = ks ? k_attn_prefill_mfma<64, true> : k_attn_prefill_mfma<64, false>;
         else
-            hipLaunchKernelGGL(k_attn_prefill_mfma<128>, grid, dim3(kThreads), 0, s, b);
+            kern = ks ? k_attn_prefill_mfma<128, true> : k_attn_prefill_mfma<128, false>;
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, b);
         if (q_split < a.T) {
             const dim3 mgrid((a.T - q_split + kThreads / 64 - 1) / (kThreads / 64), a.nh);
             if (a.hd == 64)
