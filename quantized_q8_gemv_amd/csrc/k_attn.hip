@@ -18,8 +18,12 @@
 // when the cache fits one split, the workgroup writes the normalised output
 // itself (the merge of one split is that division).
 //
-// Prefill: one workgroup per (32 queries, head); key tiles staged in LDS,
-// online softmax in f32 per query row.
+// Prefill (head size 64 or 128): one workgroup per (64 queries, head) on
+// MFMA, key blocks of 64 staged in LDS as f16 pairs, online softmax per
+// query; long prompts cut each query block's keys into up to kMaxPfSplits
+// ranges on separate workgroups, merged in range order by
+// k_attn_prefill_merge. Other head sizes: one workgroup per (32 queries,
+// head) in f32 (k_attn_prefill).
 
 #include <algorithm>
 
