@@ -39,7 +39,29 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int GK = 64;     // weights per K step (two Q8_0 blocks)
-constexpr int LPAD = 72;   // halves per LDS row (64 + 8)
+constexpr int LPAD = 64;   // halves per LDS row of a tile (64 weights of K, 8 chunks of 16 bytes)
+
+// Half offset of (row, col) in an LDS tile, col inside one 16-byte chunk
+// (col % 8 + the access width <= 8). Chunk c of row r is stored at chunk
+// c ^ ((r >> 1) & 7): the 16 rows a fragment read takes (16-byte lanes, one
+// chunk each) and the rows a store covers then fall on distinct bank groups,
+// with no padding.
+__device__ __forceinline__ int lds_h(int row, int col) {
+    return row * LPAD + ((((col >> 3) ^ (row >> 1)) & 7) << 3) + (col & 7);
+}
+
+// The same with the row's key (row >> 1) & 7 given: a thread's store rows
+// differ by multiples of 16, so its key is fixed and kept in one register.
+__device__ __forceinline__ int lds_hk(int row, int col, int key) {
+    return row * LPAD + ((((col >> 3) ^ key) & 7) << 3) + (col & 7);
+}
+
+// Column offset of a lane's fragment chunk (half-block hb, lane group
+// lane / 16) in tile rows of the form 16 i + lane % 16: their swizzle key is
+// (lane % 16) / 2 for every i.
+__device__ __forceinline__ int frag_col(int hb, int lane) {
+    return ((((hb * 4 + (lane >> 4)) ^ ((lane & 15) >> 1)) & 7) << 3);
+}
 
 enum GemmEpi { G_STORE = 0, G_ACCUM = 1, G_QKV = 2, G_GATEUP = 3, G_PART = 4 };
 
@@ -248,6 +270,9 @@ __device__ inline void a_store(const u32x4 *ra, _Float16 *ahi, _Float16 *alo, co
                                bool resc) {
     using C = Cfg<TM, TN>;
     const int tid = threadIdx.x;
+    // row keys: A32 rows tid / 16 + 16 i, else tid / 8 + (0 or 32)
+    static_assert(kThreads % 256 == 0 && (TM * 8) % 256 == 0, "store rows differ by multiples of 16");
+    const int key = A32 ? (tid >> 5) & 7 : (tid >> 4) & 7;
 #pragma unroll
     for (int i = 0; i < C::AP; ++i) {
         const int c = tid + i * kThreads;
@@ -264,11 +289,14 @@ __device__ inline void a_store(const u32x4 *ra, _Float16 *ahi, _Float16 *alo, co
                 lo[k] = static_cast<_Float16>(vv[k] - static_cast<float>(hi[k]));
             }
             if (bad && a.sc.range_flag) *a.sc.range_flag = 1u;
-            *reinterpret_cast<uint2 *>(ahi + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, hi);
-            *reinterpret_cast<uint2 *>(alo + m * LPAD + c4 * 4) = __builtin_bit_cast(uint2, lo);
+            *reinterpret_cast<uint2 *>(ahi + lds_hk(m, c4 * 4, key)) = __builtin_bit_cast(uint2, hi);
+            *reinterpret_cast<uint2 *>(alo + lds_hk(m, c4 * 4, key)) = __builtin_bit_cast(uint2, lo);
         } else {
-            const int plane = c / (TM * 8), rr = c - plane * (TM * 8);
-            const int m = rr >> 3, p = rr & 7;
+            // thread tid stores chunk tid % 8 of rows tid / 8 + a multiple of 32
+            // (per i, known at compile time) of the hi or the lo plane
+            constexpr int kPlaneRows = TM * 8;
+            const int plane = (i * kThreads) / kPlaneRows;
+            const int m = (tid >> 3) + ((i * kThreads) % kPlaneRows) / 8, p = tid & 7;
             u32x4 v = ra[i];
             if (resc && m0 + m < a.T) {
                 const int t = m0 + m;
@@ -280,7 +308,8 @@ __device__ inline void a_store(const u32x4 *ra, _Float16 *ahi, _Float16 *alo, co
                     v = __builtin_bit_cast(u32x4, h);
                 }
             }
-            *reinterpret_cast<u32x4 *>((plane ? alo : ahi) + m * LPAD + p * 8) = v;
+            const int off = (tid >> 3) * LPAD + (((p ^ key) & 7) << 3);   // this thread's chunk in row tid / 8
+            *reinterpret_cast<u32x4 *>((plane ? alo : ahi) + off + ((i * kThreads) % kPlaneRows) / 8 * LPAD) = v;
         }
     }
 }
@@ -351,9 +380,12 @@ __device__ inline void g_store(const GRegs<TM, TN, FMT> &r, const GBuf &bf, cons
                                __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
         const u32x4 s1 = u32x4{__builtin_bit_cast(uint32_t, v[4]), __builtin_bit_cast(uint32_t, v[5]),
                                __builtin_bit_cast(uint32_t, v[6]), __builtin_bit_cast(uint32_t, v[7])};
-        _Float16 *dst = bf.bq + b * LPAD + (qd >> 1) * 32 + (qd & 1) * 16;
-        *reinterpret_cast<u32x4 *>(dst) = s0;
-        *reinterpret_cast<u32x4 *>(dst + 8) = s1;
+        // rows tid / 4 + 64 i: this thread's two chunks in row tid / 4, plus
+        // i * 64 rows
+        const int col = (tid & 2) * 16 + (tid & 1) * 16, key = (tid >> 3) & 7;
+        const int rofs = i * (kThreads / 4) * LPAD;
+        *reinterpret_cast<u32x4 *>(bf.bq + lds_hk(tid >> 2, col, key) + rofs) = s0;
+        *reinterpret_cast<u32x4 *>(bf.bq + lds_hk(tid >> 2, col + 8, key) + rofs) = s1;
         if (FMT == F_Q5_0) {
             if (qd == 0) bf.bd[b * 2 + 0] = half_bits_to_float(w[0] & 0xffffu);
             if (qd == 2) bf.bd[b * 2 + 1] = half_bits_to_float(w[0] >> 16);
@@ -455,17 +487,18 @@ void k_gemm_q8(GemmArgs a) {
             for (int hb = 0; hb < 2; ++hb) {
                 half8 bfr[C::NS];
                 float dsc[C::NS];
+                const int fc = frag_col(hb, lane);
 #pragma unroll
                 for (int ns = 0; ns < C::NS; ++ns) {
                     const int col = wn * C::WN + ns * 16 + (lane & 15);
-                    bfr[ns] = *reinterpret_cast<const half8 *>(bf.bq + col * LPAD + hb * 32 + 8 * (lane >> 4));
+                    bfr[ns] = *reinterpret_cast<const half8 *>(bf.bq + col * LPAD + fc);
                     dsc[ns] = bf.bd[col * 2 + hb];
                 }
 #pragma unroll
                 for (int ms = 0; ms < C::MS; ++ms) {
                     const int row = wm * C::WM + ms * 16 + (lane & 15);
-                    const half8 ah = *reinterpret_cast<const half8 *>(bf.ahi + row * LPAD + hb * 32 + 8 * (lane >> 4));
-                    const half8 al = *reinterpret_cast<const half8 *>(bf.alo + row * LPAD + hb * 32 + 8 * (lane >> 4));
+                    const half8 ah = *reinterpret_cast<const half8 *>(bf.ahi + row * LPAD + fc);
+                    const half8 al = *reinterpret_cast<const half8 *>(bf.alo + row * LPAD + fc);
 #pragma unroll
                     for (int ns = 0; ns < C::NS; ++ns) {
                         f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bfr[ns], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -686,7 +719,7 @@ __device__ inline void bytes_to_half_biased(uint32_t w, half2v &lo, half2v &hi) 
 }
 
 // 16 small unsigned values (4 dwords of bytes) minus `bias` + 1024, as f16, to LDS.
-__device__ inline void store16(const uint32_t *v, float bias, _Float16 *dst) {
+__device__ inline void store16(const uint32_t *v, float bias, _Float16 *bq, int row, int col) {
     const half2v b = {static_cast<_Float16>(1024.0f + bias), static_cast<_Float16>(1024.0f + bias)};
     half2v o[8];
 #pragma unroll
@@ -695,10 +728,12 @@ __device__ inline void store16(const uint32_t *v, float bias, _Float16 *dst) {
         o[2 * k] = o[2 * k] - b;
         o[2 * k + 1] = o[2 * k + 1] - b;
     }
-    *reinterpret_cast<u32x4 *>(dst) = u32x4{__builtin_bit_cast(uint32_t, o[0]), __builtin_bit_cast(uint32_t, o[1]),
-                                            __builtin_bit_cast(uint32_t, o[2]), __builtin_bit_cast(uint32_t, o[3])};
-    *reinterpret_cast<u32x4 *>(dst + 8) = u32x4{__builtin_bit_cast(uint32_t, o[4]), __builtin_bit_cast(uint32_t, o[5]),
-                                                __builtin_bit_cast(uint32_t, o[6]), __builtin_bit_cast(uint32_t, o[7])};
+    *reinterpret_cast<u32x4 *>(bq + lds_h(row, col)) =
+        u32x4{__builtin_bit_cast(uint32_t, o[0]), __builtin_bit_cast(uint32_t, o[1]), __builtin_bit_cast(uint32_t, o[2]),
+              __builtin_bit_cast(uint32_t, o[3])};
+    *reinterpret_cast<u32x4 *>(bq + lds_h(row, col + 8)) =
+        u32x4{__builtin_bit_cast(uint32_t, o[4]), __builtin_bit_cast(uint32_t, o[5]), __builtin_bit_cast(uint32_t, o[6]),
+              __builtin_bit_cast(uint32_t, o[7])};
 }
 
 template <int FMT, int TM, int TN>
@@ -719,8 +754,8 @@ __device__ inline void kb_store(const KSrc<FMT, TM, TN> &g, int ks, const KRegs<
                 lo[e] = w[4 + e] & 0x0f0f0f0fu;
                 hi[e] = (w[4 + e] >> 4) & 0x0f0f0f0fu;
             }
-            store16(lo, 0.f, bq + b * LPAD + 16 * part);
-            store16(hi, 0.f, bq + b * LPAD + 32 + 16 * part);
+            store16(lo, 0.f, bq, b, 16 * part);
+            store16(hi, 0.f, bq, b, 32 + 16 * part);
             if (part == 0) {
                 const int c = ks & 3;
                 const float d = half_bits_to_float(w[0]), dmin = half_bits_to_float(w[0] >> 16);
@@ -743,7 +778,7 @@ __device__ inline void kb_store(const KSrc<FMT, TM, TN> &g, int ks, const KRegs<
                 const uint32_t nib = (kk ? (l >> 4) : l) & 0x0f0f0f0fu;
                 q6[e] = nib | (((h >> hshift) & 0x03030303u) << 4);
             }
-            store16(q6, 32.f, bq + b * LPAD + 16 * part);
+            store16(q6, 32.f, bq, b, 16 * part);
             const int scv = static_cast<int8_t>((w[10] >> (8 * (p.sc & 3u))) & 0xffu);
             const float d = half_bits_to_float(w[11]);
             bd[b * 4 + part] = d * float(scv);
@@ -805,10 +840,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
         for (int hb = 0; hb < 2; ++hb) {
             half8 bfr[C::NS], bfr1[C::NS];
             float s0[C::NS], s1[C::NS];
+            const int fc = frag_col(hb, lane);
 #pragma unroll
             for (int ns = 0; ns < C::NS; ++ns) {
                 const int col = wn * C::WN + ns * 16 + (lane & 15);
-                const half8 v = *reinterpret_cast<const half8 *>(bq + col * LPAD + hb * 32 + 8 * (lane >> 4));
+                const half8 v = *reinterpret_cast<const half8 *>(bq + col * LPAD + fc);
                 if (FMT == F_Q4_K) {
                     bfr[ns] = v;
                     s0[ns] = bd[col * 4 + hb];          // d * s
@@ -823,8 +859,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_kq(GemmArgs a) {
 #pragma unroll
             for (int ms = 0; ms < C::MS; ++ms) {
                 const int row = wm * C::WM + ms * 16 + (lane & 15);
-                const half8 ah = *reinterpret_cast<const half8 *>(ahi + row * LPAD + hb * 32 + 8 * (lane >> 4));
-                const half8 al = *reinterpret_cast<const half8 *>(alo + row * LPAD + hb * 32 + 8 * (lane >> 4));
+                const half8 ah = *reinterpret_cast<const half8 *>(ahi + row * LPAD + fc);
+                const half8 al = *reinterpret_cast<const half8 *>(alo + row * LPAD + fc);
                 if (FMT == F_Q4_K) {
                     f32x4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, ones, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, ones, sx, 0, 0, 0);
