@@ -1086,7 +1086,20 @@ int gemm_splitk_max_tokens(int N) {
     return std::min(kSplitKMaxTokens, 32 * ((kSplitKWgs - 1) / row_tiles(N, 64)));
 }
 
+// Wide matrices (N >= 2048) at 256 tokens and more whose 64 x 128 grid is
+// still short of the large-tile threshold: large tiles split over K instead
+// of small tiles (their LDS traffic per MFMA is half), 2 to 8 slices towards
+// kSplitKWgs workgroups, as many as the partials buffer holds.
+bool splitk_large(int N, int T) { return N >= 2048 && T >= 256 && !large_tiles(T, row_tiles(N, 128)); }
+
 int gemm_splitk(int N, int K, int T) {
+    if (splitk_large(N, T)) {
+        const long wgs = long(row_tiles(T, 64)) * row_tiles(N, 128);
+        const long want = std::max(2L, (kSplitKWgs + wgs - 1) / wgs);
+        const long fit = long(kSplitKMax) * gemm_splitk_max_tokens(N) / T;
+        const long sk = std::min<long>({want, long(kSplitKMax), long(K / GK), fit});
+        return sk >= 2 ? int(sk) : 1;
+    }
     if (T > gemm_splitk_max_tokens(N)) return 1;
     const long wgs = long(row_tiles(T, 32)) * row_tiles(N, 64);
     if (wgs >= kSplitKWgs || large_tiles(T, row_tiles(N, 128))) return 1;
@@ -1097,10 +1110,16 @@ int gemm_splitk(int N, int K, int T) {
 
 hipError_t launch_gemm_part(const uint8_t *W, int N, int K, const _Float16 *A, int T, int splits, float *part,
                             hipStream_t s, const ActScale &sc, int fmt) {
-    if (splits < 1 || splits > kSplitKMax || splits > K / GK || T > gemm_splitk_max_tokens(N) || !pair_format(fmt))
+    // (the partials part[splits][T][N] must fit the buffer sized for
+    // kSplitKMax slices of gemm_splitk_max_tokens(N) rows)
+    if (splits < 1 || splits > kSplitKMax || splits > K / GK ||
+        long(splits) * T > long(kSplitKMax) * gemm_splitk_max_tokens(N) || !pair_format(fmt))
         return hipErrorInvalidValue;
     GemmArgs a = gemm_base(A, T, K, fmt);
     a.W[0] = W; a.Nm[0] = N; a.part = part; a.splits = splits; a.sc = sc;
+    if (splitk_large(N, T))
+        return fmt == F_Q5_0 ? launch_cfg<G_PART, 64, 128, false, F_Q5_0>(a, row_tiles(N, 128), s)
+                             : launch_cfg<G_PART, 64, 128, false>(a, row_tiles(N, 128), s);
     return fmt == F_Q5_0 ? launch_cfg<G_PART, 32, 64, false, F_Q5_0>(a, row_tiles(N, 64), s)
                          : launch_cfg<G_PART, 32, 64, false>(a, row_tiles(N, 64), s);
 }
