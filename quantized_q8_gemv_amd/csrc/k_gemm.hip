@@ -1086,11 +1086,11 @@ int gemm_splitk_max_tokens(int N) {
     return std::min(kSplitKMaxTokens, 32 * ((kSplitKWgs - 1) / row_tiles(N, 64)));
 }
 
-// Wide matrices (N >= 2048) at 256 tokens and more whose 64 x 128 grid is
+// Wide matrices (N >= 2048) past 64 tokens (two tile rows) whose 64 x 128 grid is
 // still short of the large-tile threshold: large tiles split over K instead
 // of small tiles (their LDS traffic per MFMA is half), 2 to 8 slices towards
 // kSplitKWgs workgroups, as many as the partials buffer holds.
-bool splitk_large(int N, int T) { return N >= 2048 && T >= 256 && !large_tiles(T, row_tiles(N, 128)); }
+bool splitk_large(int N, int T) { return N >= 2048 && T > 64 && !large_tiles(T, row_tiles(N, 128)); }
 
 int gemm_splitk(int N, int K, int T) {
     if (splitk_large(N, T)) {

@@ -210,15 +210,19 @@ def test_long_prompt_head_dim_128(plen):
     assert ties <= 1
 
 
-def test_big_gqa_shape_two_layers():
-    """hidden 4096, 32/8 heads, head_dim 128, FFN 14336, vocab 32000 untied (2 layers)."""
+@pytest.mark.parametrize("plen", [64, 97])
+def test_big_gqa_shape_two_layers(plen):
+    """hidden 4096, 32/8 heads, head_dim 128, FFN 14336, vocab 32000 untied (2
+    layers). 64 tokens: the o and down projections on 32x64 tiles split over
+    K; 97 tokens: on 64x128 tiles split over K (8 slices)."""
     s = synth.ModelShape("7b-width-2layer", n_layer=2, n_embd=4096, n_head=32, n_head_kv=8,
                          head_dim=128, n_ff=14336, n_vocab=32000, tied_output=False)
     m = synth.random_model(s, 6)
-    prompt = synth.prompt_ids(s.n_vocab, 64, 7)
+    prompt = synth.prompt_ids(s.n_vocab, plen, 7)
     gm = gpu_model(m)
-    ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 4, "7b-width 64+4")
-    log(f"7b-width: max abs err {err:.3g}")
+    ids, err, ties = compare_generation(gm, oracle.OracleModel(m), prompt, 4, f"7b-width {plen}+4")
+    log(f"7b-width {plen}: max abs err {err:.3g}")
+    assert ties <= 1
 
 
 @pytest.fixture(scope="module")
