@@ -1151,9 +1151,13 @@ hipError_t launch_gemm_kq(int fmt, const uint8_t *W, int N, int K, const void *A
                          : launch_kq_fmt<F_Q6_K>(a, a_split, accumulate, s);
 }
 
+constexpr long kQkvLargeWgs = 512;   // (768 measured slower at 700 and 900 tokens)
+
 template <int FMT>
-hipError_t launch_qkv_fmt(const GemmArgs &a, bool large, int yt, hipStream_t s) {
-    return large ? launch_cfg<G_QKV, 64, 128, false, FMT>(a, yt, s) : launch_cfg<G_QKV, 32, 64, false, FMT>(a, yt, s);
+hipError_t launch_qkv_fmt(const GemmArgs &a, int tiles, int yt, hipStream_t s) {
+    if (tiles == 2) return launch_cfg<G_QKV, 64, 128, false, FMT>(a, yt, s);
+    if (tiles == 1) return launch_cfg<G_QKV, 64, 64, false, FMT>(a, yt, s);
+    return launch_cfg<G_QKV, 32, 64, false, FMT>(a, yt, s);
 }
 
 // q, k and v in one launch when they share a block format; otherwise one
@@ -1166,8 +1170,11 @@ hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u,
     const int fm[3] = {w.fq, w.fk, w.fv};
     for (int i = 0; i < 3; ++i)
         if (!pair_format(fm[i])) return hipErrorInvalidValue;
-    const bool large = large_tiles(T, row_tiles(QD, 128) + 2 * row_tiles(KVD, 128));
-    const int tn = large ? 128 : 64;
+    const int n128 = row_tiles(QD, 128) + 2 * row_tiles(KVD, 128);
+    // 64 x 128 tiles from 2 workgroups per CU; 64 x 64 between the
+    // large-tile threshold and that
+    const int tiles = !large_tiles(T, n128) ? 0 : long((T + 63) / 64) * n128 >= kQkvLargeWgs ? 2 : 1;
+    const int tn = tiles == 2 ? 128 : 64;
     for (int first = 0; first < 3;) {
         int last = first;
         while (last + 1 < 3 && fm[last + 1] == fm[first]) ++last;
@@ -1183,8 +1190,8 @@ hipError_t launch_gemm_qkv(const Dims &d, const LayerPtrs &w, const _Float16 *u,
             if (!a.tiles[i]) a.W[i] = nullptr;
             yt += a.tiles[i];
         }
-        const hipError_t e = fm[first] == F_Q5_0 ? launch_qkv_fmt<F_Q5_0>(a, large, yt, s)
-                                                 : launch_qkv_fmt<F_Q8_0>(a, large, yt, s);
+        const hipError_t e = fm[first] == F_Q5_0 ? launch_qkv_fmt<F_Q5_0>(a, tiles, yt, s)
+                                                 : launch_qkv_fmt<F_Q8_0>(a, tiles, yt, s);
         if (e != hipSuccess) return e;
         first = last + 1;
     }
