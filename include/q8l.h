@@ -103,8 +103,9 @@ typedef struct q8l_model q8l_model;
 
 /* Bytes of device workspace the model needs: KV cache
  * [n_layer][2][n_head_kv][max_seq_len][head_dim] f32, the rope table,
- * activations for up to max_seq_len tokens, attention partials, split-K
- * partial sums for short prompts and counters.
+ * activations for up to max_seq_len tokens, attention partials (decode
+ * splits; the key ranges of long prefills), split-K partial sums of the
+ * prefill o and down projections, and counters.
  * Returns 0 for an invalid config. */
 size_t q8l_workspace_bytes(const q8l_config *cfg);
 
