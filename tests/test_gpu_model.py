@@ -210,6 +210,31 @@ def test_long_prompt_head_dim_128(plen):
     assert ties <= 1
 
 
+@pytest.mark.parametrize("hd", [64, 128])
+def test_key_split_prefill_after_a_cached_prefix(hd):
+    """A 1100-token prefill behind 10 cached positions: its query blocks
+    straddle key blocks, so some key ranges hold no visible key for the first
+    queries of a block (those ranges must weigh nothing in the merge); logits
+    of the chunked prefill and the decode steps after it against the oracle."""
+    s = synth.micro_shape(n_layer=1, n_embd=2 * hd, n_head=2, n_head_kv=1, head_dim=hd, n_ff=256,
+                          n_vocab=500, max_seq_len=1200, name=f"prefix-split-{hd}")
+    m = synth.random_model(s, hd + 3)
+    prompt = synth.prompt_ids(s.n_vocab, 1110, 11)
+    gm, om = gpu_model(m), oracle.OracleModel(m)
+    gm.forward(prompt[:10], 0)
+    om.forward(prompt[:10], 0)
+    g, gid = gm.forward(prompt[10:], 10)
+    st, ref, _ = om.forward(prompt[10:], 10)
+    assert st == oracle.OK
+    assert_logits_close(g, ref, f"hd {hd}: 1100 tokens after 10")
+    tok = oracle.argmax(ref)
+    for p in range(1110, 1113):
+        g, _ = gm.forward([tok], p)
+        _, ref, _ = om.forward([tok], p)
+        assert_logits_close(g, ref, f"hd {hd}: decode at {p}")
+        tok = oracle.argmax(ref)
+
+
 @pytest.mark.parametrize("plen", [64, 97])
 def test_big_gqa_shape_two_layers(plen):
     """hidden 4096, 32/8 heads, head_dim 128, FFN 14336, vocab 32000 untied (2
