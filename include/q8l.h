@@ -420,9 +420,11 @@ int64_t q8l_gguf_find_tensor(const q8l_gguf *g, const char *name);
 /* Tensor `index`: name (valid while the handle is open), dtype (a q8l_dtype, or
  * -1 with Q8L_E_FORMAT for other types), rows x cols (cols = the innermost
  * dimension), absolute file offset and byte size as read. Any output may be
- * NULL. Q5_0 tensors of the seven blk.{i} projections are read as they are
- * (dtype Q8L_Q5_0, 22 bytes per 32 weights). Q4_0 tensors, and Q5_0 tensors
- * of the other roles (token_embd, output), are read as Q8_0
+ * NULL. Q5_0 tensors of the seven blk.{i} projections with rows of at least
+ * 2048 weights are read as they are (dtype Q8L_Q5_0, 22 bytes per 32
+ * weights). Q4_0 tensors, Q5_0 tensors of shorter rows (whose single-token
+ * products are faster in Q8_0) and Q5_0 tensors of the other roles
+ * (token_embd, output) are read as Q8_0
  * (32-weight blocks of an f16 scale times 4- or 5-bit integers; sizes pinned
  * by "速度", section "CPU GGUF"): dtype Q8L_Q8_0, size rows*cols/32*34, each
  * block converted exactly (same scale, int8 = the block's integer). Q4_K and

@@ -79,8 +79,15 @@ bool k_family(uint32_t t) { return t == kTypeQ4_K || t == kTypeQ6_K; }
 uint64_t block_bytes(uint32_t t) { return t == kTypeQ4_0 ? 18 : t == kTypeQ5_0 ? 22 : 34; }
 
 // Q5_0 tensors that the model binds in their own format: the seven
-// projections of a layer ("blk.<n>.<role>.weight"). Others (the embedding,
-// the output matrix) are read as Q8_0.
+// projections of a layer ("blk.<n>.<role>.weight") with rows of at least
+// kQ5NativeMinCols weights. Others (the embedding, the output matrix, and
+// shorter rows) are read as Q8_0: rows under 2048 weights take the
+// latency-bound wave-per-row decode kernels, where unpacking the fifth bits
+// costs more than the bytes it saves (135M shape, every projection Q5_0:
+// 567 us/token streamed as Q5_0 against 469 as Q8_0; the 7B-class shape,
+// rows of 4096: 2000 against 2206).
+constexpr uint64_t kQ5NativeMinCols = 2048;
+
 bool q5_native_role(const std::string &name) {
     if (name.compare(0, 4, "blk.") != 0) return false;
     size_t p = 4;
@@ -290,7 +297,7 @@ q8l_status parse(q8l_gguf *g) {
         } else if (q8_family(t.type)) {
             if (t.dims[0] % 32) return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " rows are not whole blocks");
             t.file_bytes = n / 32 * block_bytes(t.type);
-            t.native = t.type == kTypeQ5_0 && q5_native_role(t.name);
+            t.native = t.type == kTypeQ5_0 && q5_native_role(t.name) && t.dims[0] >= kQ5NativeMinCols;
             t.nbytes = t.native ? t.file_bytes : n / 32 * 34;
         } else if (k_family(t.type)) {
             if (t.dims[0] % 256) return fail(g, Q8L_E_FORMAT, "tensor " + t.name + " rows are not whole blocks");

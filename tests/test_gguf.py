@@ -269,8 +269,9 @@ def test_q4_0_and_q5_0_tensors_read_as_exact_q8_0(lib, tmp_path, fmt, ftype, nam
 @pytest.mark.parametrize("role", ["attn_q", "attn_k", "attn_v", "attn_output", "ffn_gate", "ffn_up",
                                   "ffn_down"])
 def test_q5_0_projections_read_as_they_are(lib, tmp_path, role):
+    """Rows of 2048 weights and more: the 22-byte blocks as they are."""
     rng = np.random.default_rng(13)
-    rows, cols = 24, 576
+    rows, cols = 24, 2048
     raw = W.random_blocks(rng, rows, cols, "q5_0")
     other = W.random_blocks(rng, 3, 64, "q5_0")          # 44-byte rows: a tensor not 16-byte sized
     name = f"blk.2.{role}.weight"
@@ -286,6 +287,29 @@ def test_q5_0_projections_read_as_they_are(lib, tmp_path, role):
         buf = np.empty(info["nbytes"], np.uint8)
         assert C.q8l_gguf_read_tensor(g, idx, buf, buf.size) == C.Q8L_OK
         assert np.array_equal(buf, raw.reshape(-1))
+    finally:
+        C.q8l_gguf_close(g)
+
+
+@pytest.mark.parametrize("cols", [576, 1536, 2016])
+def test_q5_0_projections_of_short_rows_read_as_exact_q8_0(lib, tmp_path, cols):
+    """Rows under 2048 weights (the wave-per-row decode kernels' lengths) are
+    read as Q8_0: the same values, each block's scale and integer."""
+    import oracle
+    rng = np.random.default_rng(cols)
+    rows = 5
+    raw = W.random_blocks(rng, rows, cols, "q5_0")
+    name = "blk.0.ffn_up.weight"
+    path = str(tmp_path / "q5s.gguf")
+    W.write(path, W.llama_kv(synth.TINY), [(name, W.TYPE_Q5_0, [cols, rows], raw.tobytes())])
+    g = C.q8l_gguf_open(path)
+    try:
+        idx = C.q8l_gguf_find_tensor(g, name)
+        st, info = C.q8l_gguf_tensor_info(g, idx)
+        assert st == C.Q8L_OK and info["dtype"] == C.Q8L_Q8_0 and info["nbytes"] == rows * cols // 32 * 34
+        buf = np.empty(info["nbytes"], np.uint8)
+        assert C.q8l_gguf_read_tensor(g, idx, buf, buf.size) == C.Q8L_OK
+        assert np.array_equal(oracle.dequant_q8_0(buf, rows, cols), oracle.dequant_q5_0(raw, rows, cols))
     finally:
         C.q8l_gguf_close(g)
 

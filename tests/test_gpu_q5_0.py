@@ -175,10 +175,12 @@ def _q4_k_m_layer(l):
 
 @pytest.mark.parametrize("width", ["135m", "7b"])
 def test_gguf_in_the_pages_4bit_mix_read_natively(tmp_path, width):
-    """A GGUF file in the pages' 4-bit mix read by Q8Model.from_gguf: every
-    format streamed as it is (Q5_0 included), against the oracle on the same
-    blocks. At the 135M widths (4 layers) and the 7B-class ones (2 layers,
-    hidden 4096, FFN 14336, untied vocab 32000)."""
+    """A GGUF file in the pages' 4-bit mix read by Q8Model.from_gguf: K
+    formats streamed as they are, Q5_0 as it is in rows of 2048 weights and
+    more (the 7B-class widths) and as the same values in Q8_0 in shorter ones
+    (the 135M widths), against the oracle on the same blocks. At the 135M
+    widths (4 layers) and the 7B-class ones (2 layers, hidden 4096, FFN 14336,
+    untied vocab 32000)."""
     import gguf_writer as W
     from quantized_q8_gemv_amd import q8l as C
     from quantized_q8_gemv_amd.model import Q8Model
@@ -195,9 +197,11 @@ def test_gguf_in_the_pages_4bit_mix_read_natively(tmp_path, width):
     try:
         for t in m.tensors:
             st, info = C.q8l_gguf_tensor_info(g, C.q8l_gguf_find_tensor(g, t.name))
-            want = {"q8_0": C.Q8L_Q8_0, "q5_0": C.Q8L_Q5_0, "q4_k": C.Q8L_Q4_K, "q6_k": C.Q8L_Q6_K,
+            q5 = C.Q8L_Q5_0 if t.cols >= 2048 else C.Q8L_Q8_0
+            want = {"q8_0": C.Q8L_Q8_0, "q5_0": q5, "q4_k": C.Q8L_Q4_K, "q6_k": C.Q8L_Q6_K,
                     "f32": C.Q8L_F32}[t.dtype]
-            assert st == C.Q8L_OK and info["dtype"] == want and info["nbytes"] == t.nbytes, t.name
+            nbytes = t.rows * t.cols // 32 * 34 if (t.dtype == "q5_0" and q5 == C.Q8L_Q8_0) else t.nbytes
+            assert st == C.Q8L_OK and info["dtype"] == want and info["nbytes"] == nbytes, t.name
     finally:
         C.q8l_gguf_close(g)
     prompt = synth.prompt_ids(s.n_vocab, plen, 8)
