@@ -99,6 +99,23 @@ def test_generate_crosses_attention_split_buckets():
     assert gm.cache_len == 140
 
 
+def test_generate_head_dim_128_crosses_split_buckets():
+    """Head size 128 (32-key attention splits), rows of 2048 weights (the
+    register-activation decode kernels): one q8l_generate call from 20 cached
+    keys to 80 crosses 32 -> 33 keys (one split, normalised by the attention
+    kernel, to two, merged in the o-projection's prologue) and 64 -> 65 (to
+    three and more, 33 KB of partials: merged by the combine kernel)."""
+    s = synth.ModelShape("hd128-gen", n_layer=2, n_embd=2048, n_head=16, n_head_kv=4, head_dim=128,
+                         n_ff=2048, n_vocab=500, tied_output=False, max_seq_len=256)
+    m = synth.random_model(s, 12)
+    prompt = synth.prompt_ids(s.n_vocab, 20, 10)
+    gm = gpu_model(m)
+    first, ids, last = device_generate(gm, prompt, 60)
+    ties = check_against_oracle(oracle.OracleModel(m), prompt, first, ids, last, "hd128 generate 20+60")
+    assert ties <= 1
+    assert gm.cache_len == 80
+
+
 def test_generate_135m_203_prompt_128_steps_crosses_257_keys():
     """The 203 + 128 workload as one q8l_generate call: the cache grows from
     204 to 331 keys, crossing the 4 -> 8 split bucket at 257."""
