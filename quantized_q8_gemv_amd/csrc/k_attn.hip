@@ -246,34 +246,47 @@ __global__ __launch_bounds__(kThreads) void k_attn_combine(const float *part, in
     __shared__ float red[4];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int h = blockIdx.x;
-    if (st) {  // graph replay: the cache length comes from the step state
-        const int C = attn_chunk(hd);
-        active = min((st->slot + 1 + C - 1) / C, n_splits);
-    }
     const float *pb = part + size_t(h) * n_splits * (hd + 2);
     // Many splits: kThreads / hd interleaved slices of the splits (slice j:
     // splits j, j + P, ...), each summed in split order, then the slices in
     // order -- P shorter dependent chains instead of one of `active` steps
     // (135M, 63 splits: 997 -> 979 us/token; with 17 splits the extra
     // exchange cost more than it saved). Otherwise thread d sums every split.
-    const bool sliced = active > 32 && hd <= kThreads && kThreads % hd == 0;
+    // In graph replay (st set) the choice follows the launch's split count,
+    // a power of two of which more than half are in use, so it is the same
+    // as from the count in use without waiting for it.
+    const bool sliced = (st ? n_splits > 32 : active > 32) && hd <= kThreads && kThreads % hd == 0;
     const int P = sliced ? kThreads / hd : 1;
     const int j = sliced ? tid / hd : 0, d = sliced ? tid - j * hd : tid;
     const bool outs = d < hd && j < P;
-    // This thread's first kCombinePre partial outputs, requested now so that
-    // they arrive while the split weights are computed (in bounds: clamped)
+    // This thread's first kCombinePre partial outputs and its first split's
+    // (max, sum), requested before the count in use is known (a read of the
+    // step state: a round trip of its own), so that they arrive together
+    // (in bounds: clamped to the launch's splits; those past the count in
+    // use are never summed)
     float pre[kCombinePre];
 #pragma unroll
     for (int k = 0; k < kCombinePre; ++k)
-        pre[k] = pb[size_t(min(j + k * P, active - 1)) * (hd + 2) + 2 + min(d, hd - 1)];
-    float mx = -INFINITY;
-    for (int t = tid; t < active; t += kThreads) mx = fmaxf(mx, pb[size_t(t) * (hd + 2)]);
+        pre[k] = pb[size_t(min(j + k * P, n_splits - 1)) * (hd + 2) + 2 + min(d, hd - 1)];
+    const int t0 = min(tid, n_splits - 1);
+    const float m0 = pb[size_t(t0) * (hd + 2)], l0 = pb[size_t(t0) * (hd + 2) + 1];
+    if (st) {  // graph replay: the cache length comes from the step state
+        const int C = attn_chunk(hd);
+        active = min((st->slot + 1 + C - 1) / C, n_splits);
+    }
+    float mx = tid < active ? m0 : -INFINITY;
+    for (int t = tid + kThreads; t < active; t += kThreads) mx = fmaxf(mx, pb[size_t(t) * (hd + 2)]);
     mx = wave_max(mx);
     if (lane == 0) red[wid] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     float ls = 0.f;
-    for (int t = tid; t < active; t += kThreads) {
+    if (tid < active) {
+        const float wt = expf(m0 - mx);
+        w[tid] = wt;
+        ls = fmaf(wt, l0, ls);
+    }
+    for (int t = tid + kThreads; t < active; t += kThreads) {
         const float wt = expf(pb[size_t(t) * (hd + 2)] - mx);
         w[t] = wt;
         ls = fmaf(wt, pb[size_t(t) * (hd + 2) + 1], ls);

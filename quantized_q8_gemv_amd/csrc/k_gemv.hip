@@ -635,12 +635,13 @@ __device__ inline Lds1 carve1(uint8_t *smem, const GemvShape &sh, int nmat) {
 // attention, into xs in pair layout: for head h and split s with (m_s, l_s,
 // o_s), o[d] = sum_s w_s o_s[d] / sum_s w_s l_s with w_s = exp(m_s - M), M the
 // largest m_s, sums in split order (what k_attn_combine computes). Every
-// split's values are loaded before any is used (splits past the active ones
-// re-read the last active split and are not summed).
+// split's values are loaded before any is used, and before the number of
+// splits in use (from the step state) is known: indexes past the launch's
+// splits re-read its last one, and splits past the ones in use are not
+// summed.
 __device__ void stage_merged1(const CoreArgs &a, const MergeSrc &ms, const Lds1 &l) {
     const int hd = ms.hd, S = ms.splits;
     const int C = attn_chunk(hd);
-    const int active = min((ms.st->slot + 1 + C - 1) / C, S);
     const int n4 = a.sh.P * 16;
     for (int e = threadIdx.x; e < n4; e += kThreads) {
         const int k = 4 * e, h = k / hd, d = k - h * hd;
@@ -648,12 +649,13 @@ __device__ void stage_merged1(const CoreArgs &a, const MergeSrc &ms, const Lds1 
         float m[kMergeMaxSplits], ls[kMergeMaxSplits], o[kMergeMaxSplits][4];
 #pragma unroll
         for (int s = 0; s < kMergeMaxSplits; ++s) {
-            const float *ps = pb + size_t(min(s, active - 1)) * (hd + 2);
+            const float *ps = pb + size_t(min(s, S - 1)) * (hd + 2);
             m[s] = ps[0];
             ls[s] = ps[1];
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[s][i] = ps[2 + d + i];
         }
+        const int active = min((ms.st->slot + 1 + C - 1) / C, S);
         float M = m[0];
 #pragma unroll
         for (int s = 1; s < kMergeMaxSplits; ++s)
